@@ -1,0 +1,265 @@
+/*
+ * pa.h — C ABI of libpa.so: decode-step paged attention on a block-paged KV cache, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; cited by title and section):
+ *   [Visualized] "PagedAttention, Visualized" (penny-xu.github.io), Parts 2-3.
+ *   [Digest]     "PagedAttention" (devoured.fyi digest), sections "PagedAttention in one picture",
+ *                "Copy-on-write: when two requests share a prefix", "Why the attention kernel works
+ *                at all", "Misconceptions".
+ *   [Lesson06]   "LLM Inference Visualizer, Lesson 06: PagedAttention" (vivekgupta.ai), live
+ *                diagram "How paging grows".
+ *
+ * What the library computes.  The KV cache of every running sequence lives in a shared pool of
+ * fixed-size physical blocks of 16 token positions ([Digest] "PagedAttention in one picture";
+ * [Visualized] Part 3 table, "Block (16 tokens)").  A per-sequence block table maps logical block
+ * j (token positions 16j .. 16j+15) to a physical block id ([Digest] same section: an entry 7 at
+ * index 0 puts the first 16 positions of that sequence in physical block 7).  Decode attention walks that table and
+ * gathers K and V from wherever the blocks landed; the result is exactly ordinary attention on the
+ * de-paged sequence ([Digest] "Misconceptions": the math is untouched).
+ *
+ * Conventions for every entry point below.
+ *  - All device memory is owned by the caller.  The library never allocates, frees or
+ *    synchronises device memory; it only enqueues kernels on `stream` (a hipStream_t passed as
+ *    void*; NULL is the default stream).  Every call returns before the work has run.
+ *  - Host-side validation runs before any launch; on failure nothing is enqueued and the call
+ *    returns a negative pa_status; pa_last_error() then holds a thread-local description.
+ *  - After a launch, a HIP launch error is returned as PA_ERR_LAUNCH.
+ *  - Functions are re-entrant; the only global state is the thread-local error text.
+ *  - Calls that touch the same device buffers on different streams race; order them yourself.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                                        */
+  PA_ERR_SHAPE = -2,       /* sizes are negative or inconsistent with each other                */
+  PA_ERR_UNSUPPORTED = -3, /* a valid request this build does not implement (dtype, head_dim...) */
+  PA_ERR_WORKSPACE = -4,   /* the workspace is smaller than pa_decode_workspace_bytes()         */
+  PA_ERR_ALIAS = -5,       /* copy pairs overlap (a destination repeats or is also a source)    */
+  PA_ERR_LAUNCH = -6,      /* HIP reported an error when the kernels were enqueued              */
+  PA_ERR_NO_BLOCKS = -7,   /* block manager: the free list is empty                             */
+  PA_ERR_STATE = -8        /* block manager: unknown sequence or block id                       */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,      /* IEEE binary32                                                          */
+  PA_F16 = 1,      /* IEEE binary16                                                          */
+  PA_BF16 = 2,     /* bfloat16 (upper half of binary32)                                      */
+  PA_FP8_E4M3 = 3  /* OCP FP8 E4M3FN: bias 7, no infinities, NaN = S.1111.111, max +-448;
+                      cache storage only, always with one fp32 scale per KV head             */
+} pa_dtype;
+
+/* The only block size this build supports: 16 token positions per block, the default the pages
+ * give ([Digest] "PagedAttention in one picture" and "Misconceptions"). */
+#define PA_BLOCK_SIZE 16
+
+/*
+ * One layer's KV cache.  k_pool and v_pool are device buffers of pa_pool_bytes() bytes each.
+ *
+ * Pool layout (owned by the library; described here so that independent code can read it).
+ * Let e be the element size of cache_dtype in bytes (f32 4, f16 2, bf16 2, fp8 1), E = 16 / e the
+ * number of elements in one 16-byte vector, B = block_size = 16, D = head_dim, H = num_kv_heads.
+ * Both pools are block-major and then head-major: block b holds H consecutive tiles, one per KV
+ * head, each of B*D elements (B*D*e bytes: 4 KiB for f16/bf16 at D = 128, always a whole number
+ * of 128-byte lines).  Tile (b, h) starts at element (b*H + h) * B*D.  Inside a tile:
+ *
+ *   K tile: the head dimension is cut into D/E vectors of E elements (16 bytes).  Vector c of token
+ *           slot t is stored at vector index c*B + t, so element (t, i) sits at element offset
+ *           ((i / E) * B + t) * E + (i % E) within the tile.  One 16-byte vector per token, for all
+ *           16 tokens, forms 256 contiguous bytes.
+ *   V tile: stored transposed: the B values of head-dimension index i are contiguous, so element
+ *           (t, i) sits at element offset i * B + t within the tile.
+ *
+ * Token position p of a sequence with block table `bt` lives in block bt[p / B] at slot t = p % B;
+ * its global slot number is bt[p / B] * B + p % B (the slot_mapping value used by
+ * pa_reshape_and_cache).
+ *
+ * fp8: an element stored as byte c represents decode(c) * scale[h], where decode is the E4M3FN value
+ * of c and scale = k_scale for the K pool, v_scale for the V pool (device arrays of num_kv_heads
+ * fp32 values, one per KV head of this layer).  For the other dtypes the scale pointers must be NULL.
+ */
+typedef struct pa_cache {
+  void *k_pool;            /* device, pa_pool_bytes() bytes                       */
+  void *v_pool;            /* device, pa_pool_bytes() bytes                       */
+  const float *k_scale;    /* device [num_kv_heads] fp32, fp8 only, else NULL      */
+  const float *v_scale;    /* device [num_kv_heads] fp32, fp8 only, else NULL      */
+  int32_t num_blocks;      /* physical blocks in this pool                        */
+  int32_t block_size;      /* must be PA_BLOCK_SIZE                               */
+  int32_t num_kv_heads;    /* 1 .. 16                                             */
+  int32_t head_dim;        /* 64 or 128                                           */
+  int32_t cache_dtype;     /* a pa_dtype                                          */
+} pa_cache;
+
+/* Bytes of ONE of k_pool / v_pool: num_blocks * num_kv_heads * block_size * head_dim * e.
+ * Returns 0 for an invalid description.  For Qwen2.5-7B-shaped layers (4 KV heads, head_dim 128,
+ * f16) 2 * pa_pool_bytes / (num_blocks * 16) is 2,048 bytes per token per layer, i.e. 57,344 bytes
+ * per token over 28 layers ([Visualized] Part 2). */
+size_t pa_pool_bytes(const pa_cache *cache);
+
+/*
+ * pa_reshape_and_cache — write each new token's K and V into its slot.
+ * Each new token appends one KV entry inside the current logical block of its sequence
+ * ([Lesson06] "How paging grows"); K and V are kept for every later token ([Visualized] Part 2).
+ *
+ *   key, value    device [num_tokens] rows; row t holds num_kv_heads * head_dim elements of
+ *                 `in_dtype` laid out [kv_head][head_dim]; consecutive rows are key_stride /
+ *                 value_stride ELEMENTS apart (>= num_kv_heads * head_dim).
+ *   slot_mapping  device int64 [num_tokens]: token t goes to block slot_mapping[t] / 16, slot
+ *                 slot_mapping[t] % 16.  A negative value skips the token (padding); a value
+ *                 >= num_blocks * 16 is also skipped and never written.
+ *   in_dtype      f32/f16/bf16.  For an f32/f16/bf16 cache it must equal cache_dtype and the
+ *                 element is copied bit for bit.  For an fp8 cache each element x becomes
+ *                 E4M3FN(round-to-nearest-even, saturating at +-448)(float(x) / scale[h]), the
+ *                 division done in IEEE fp32; NaN becomes 0x7F with the sign of x.
+ * Two tokens with the same slot in one call race; callers must not do that.
+ */
+pa_status pa_reshape_and_cache(const pa_cache *cache, const void *key, const void *value,
+                               int32_t in_dtype, int64_t key_stride, int64_t value_stride,
+                               const int64_t *slot_mapping, int32_t num_tokens, void *stream);
+
+/* Partition size used when pa_decode_attention is given partition_size = 0 for these sizes. */
+int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len);
+
+/* Device workspace bytes pa_decode_attention needs for these sizes (0 is a valid answer when the
+ * work fits one partition per sequence).  partition_size = 0 means the automatic choice. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size);
+
+/* Flags for pa_decode_attention. */
+#define PA_DECODE_DEFAULT 0u
+#define PA_DECODE_FORCE_VALU 1u  /* use the vector-ALU kernel even where the matrix-core one applies */
+
+/*
+ * pa_decode_attention — one decode step of paged attention for a batch of sequences.
+ * The kernel walks each sequence's block table and gathers K and V block by block ([Digest]
+ * "PagedAttention in one picture", "Why the attention kernel works at all"); the result is the
+ * ordinary attention of the de-paged sequence ([Digest] "Misconceptions"):
+ *
+ *   for sequence s with L = context_lens[s] and query head q (KV head h = q / (num_q_heads /
+ *   num_kv_heads)):  z_p = scale * <query[s][q], K_s[p][h]> for p in [0, L);
+ *   out[s][q] = sum_p exp(z_p - max z) * V_s[p][h] / sum_p exp(z_p - max z);   out = 0 when L == 0,
+ *   where K_s[p][h] is element (slot p % 16) of tile (block_tables[s][p / 16], h) of the K pool.
+ *
+ *   out           device [num_seqs][num_q_heads][head_dim] in q_dtype, written in full.
+ *   query         device rows of num_q_heads * head_dim elements of q_dtype; sequence s starts at
+ *                 element s * q_stride (q_stride 0 means num_q_heads * head_dim).
+ *   q_dtype       f32 with an f32 cache; f16 with an f16 cache; bf16 with a bf16 cache; f16 or
+ *                 bf16 with an fp8 cache.
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq].  Only the first ceil(L / 16)
+ *                 entries of row s are read; the rest may hold anything.  An entry outside
+ *                 [0, num_blocks) is never dereferenced: the 16 positions it covers are left out.
+ *   context_lens  device int32 [num_seqs]; L includes the token written this step.  Values are
+ *                 clamped to [0, min(max_context_len, 16 * max_blocks_per_seq)].
+ *   max_context_len  host upper bound of context_lens, used to size the launch without reading
+ *                 the device.
+ *   scale         softmax scale, normally 1 / sqrt(head_dim).
+ *   partition_size  tokens per split-K partition: 0 = pa_decode_auto_partition(), otherwise a
+ *                 positive multiple of 16.  A sequence longer than one partition is computed as
+ *                 independent partitions (running max, running sum, unnormalised output) merged
+ *                 by a second kernel.
+ *   workspace     device scratch of at least pa_decode_workspace_bytes() bytes (NULL if 0).
+ * Supported: block_size 16, head_dim 64 or 128, num_q_heads a multiple of num_kv_heads with at
+ * most 16 query heads per KV head.
+ */
+pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int64_t q_stride,
+                              const pa_cache *cache, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                              float scale, int32_t partition_size, void *workspace,
+                              size_t workspace_bytes, uint32_t flags, void *stream);
+
+/*
+ * pa_copy_blocks — the clone step of copy-on-write.  When a sequence must write into a block
+ * whose reference count is above 1, the engine clones that block, drops the original's count by
+ * one and points the writer's table at the clone ([Digest] "Copy-on-write: when two requests share
+ * a prefix"; [Visualized] Part 3, "Copy-on-write after fork()").  For every (src, dst) pair and
+ * every layer this copies all KV heads of block src to block dst in both pools, bit for bit.
+ *
+ *   layers        HOST array of num_layers pa_cache descriptions with identical shape and dtype.
+ *   block_pairs   device int32 [num_pairs][2] = {src, dst}.  Destinations must be distinct and no
+ *                 destination may also be a source in the same call (a fresh clone target);
+ *                 pairs with an id outside [0, num_blocks) are skipped.
+ */
+pa_status pa_copy_blocks(const pa_cache *layers, int32_t num_layers, const int32_t *block_pairs,
+                         int32_t num_pairs, void *stream);
+
+/* Host-side check of the copy-pair rules above on a HOST copy of block_pairs: PA_ERR_ALIAS when a
+ * destination repeats or is also a source, PA_ERR_SHAPE when an id is out of range. */
+pa_status pa_check_copy_pairs(const int32_t *block_pairs_host, int32_t num_pairs,
+                              int32_t num_blocks);
+
+const char *pa_status_string(pa_status status);
+const char *pa_last_error(void); /* thread-local text of the last failure on this thread */
+
+/* ------------------------------------------------------------------------------------------
+ * Host block manager (no GPU calls).  It owns the free list, per-block reference counts and the
+ * per-sequence block tables, and produces the step metadata the kernels consume: slot numbers,
+ * block tables, context lengths and copy-on-write pairs.
+ *   - Blocks are handed out one at a time, only when a sequence's last block is full
+ *     ([Lesson06] "How paging grows"; [Digest] table row "page fault / alloc").
+ *   - A finished sequence's blocks go back to the pool ([Digest] "PagedAttention in one picture").
+ *   - fork() makes a child whose table points at all of the parent's blocks, each reference count
+ *     +1 ([Visualized] Part 3 shared prefix blocks; [Digest] copy-on-write section).
+ *   - append() into a block whose count is above 1 clones it first ([Digest] copy-on-write).
+ * Free list: a stack.  The initial order is given by the caller (free_order[0] is handed out
+ * first); a freed block is pushed on top and is the next one handed out.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct pa_bm pa_bm;
+
+/* free_order: HOST int32 [num_blocks], a permutation of 0..num_blocks-1 (NULL = 0, 1, 2, ...).
+ * Returns NULL on invalid arguments or allocation failure. */
+pa_bm *pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t *free_order);
+void pa_bm_destroy(pa_bm *bm);
+
+/* New empty sequence; ids are 0, 1, 2, ... in creation order and are never reused. */
+pa_status pa_bm_add_seq(pa_bm *bm, int32_t *seq_id);
+
+/* New sequence sharing every block of `parent` (each block's count +1), same context length. */
+pa_status pa_bm_fork(pa_bm *bm, int32_t parent, int32_t *child);
+
+/* Append one token position to `seq`.  If its length L is a multiple of block_size a fresh block
+ * is taken from the free list.  Otherwise, if the last block's count is above 1, a fresh block is
+ * taken, (*cow_src, *cow_dst) = (old, fresh) is reported, the old block's count drops by one and
+ * the table points at the fresh block; else *cow_src = *cow_dst = -1.  *slot receives
+ * table[L / block_size] * block_size + L % block_size, then L grows by one.  On
+ * PA_ERR_NO_BLOCKS nothing changes. */
+pa_status pa_bm_append(pa_bm *bm, int32_t seq, int64_t *slot, int32_t *cow_src, int32_t *cow_dst);
+
+/* pa_bm_append for seqs[0..n) in order.  slots[i] is seqs[i]'s slot; the copy pairs are written
+ * to cow_pairs as {src, dst} rows in order of occurrence, *num_pairs of them (cow_pairs must hold
+ * n rows).  Stops at the first failure; the appends before it stay done. */
+pa_status pa_bm_append_batch(pa_bm *bm, const int32_t *seqs, int32_t n, int64_t *slots,
+                             int32_t *cow_pairs, int32_t *num_pairs);
+
+/* Release a sequence: every block's count drops by one; blocks reaching 0 return to the pool. */
+pa_status pa_bm_free_seq(pa_bm *bm, int32_t seq);
+
+int32_t pa_bm_refcount(const pa_bm *bm, int32_t block); /* -1 for a bad id */
+int32_t pa_bm_num_free(const pa_bm *bm);
+int32_t pa_bm_seq_len(const pa_bm *bm, int32_t seq);    /* context length, -1 for a bad id */
+
+/* Copy seq's table into out[0..cap); *num_blocks = its length in blocks (may exceed cap; only
+ * min(cap, length) entries are written). */
+pa_status pa_bm_block_table(const pa_bm *bm, int32_t seq, int32_t *out, int32_t cap,
+                            int32_t *num_blocks);
+
+/* Rows of the kernels' block_tables / context_lens for seqs[0..n): tables is HOST int32
+ * [n][max_blocks_per_seq], entries past a sequence's length set to pad_value; PA_ERR_SHAPE if a
+ * table is longer than max_blocks_per_seq. */
+pa_status pa_bm_export(const pa_bm *bm, const int32_t *seqs, int32_t n, int32_t *tables,
+                       int32_t max_blocks_per_seq, int32_t pad_value, int32_t *context_lens);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */
