@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of decode-step paged attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the copy-on-write clone (when the step has
+pairs), then for every layer reshape_and_cache of the new token and the split-K decode with its
+partition reduce.  The step's metadata (slots, tables, lengths, copy pairs) comes from the host
+block manager before timing and is resident in HBM when the timed region starts.
+
+Prints ONE JSON line:
+  value        KV GB/s of the step: algorithmic (logical) KV bytes read per step / step time;
+  roofline     for pa_decode_attention (the dominant call: split-K kernel + partition reduce):
+               algorithmic bytes per call (unique physical KV slots + tables + lengths + Q + out)
+               / its mean duration from HIP events on the launch stream, against 8 TB/s;
+  cpu_baseline the CPU oracle (fp64) timed on the host's cores on a bounded sample of set 0.
+
+Timing loops rotate between `--sets` independent batches of the workload placed in the same pool
+(distinct blocks and values), so each step reads KV that the 256 MB MALL and the L2s do not already
+hold, as the successive layers of a model would.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "paged decode attention KV GB/s (% of HBM peak) + sequences/s per layer"
+DEFAULT_SETS = {"c1": 1, "c2": 16, "c3": 3, "c4": 4, "c5": 1}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(batch, unique: bool) -> int:
+    """Bytes one pa_decode_attention call must move at minimum: the KV rows of every context
+    position (each distinct physical slot once when unique), the block-table entries and lengths
+    it reads, the queries it reads and the outputs it writes (fp8: plus the per-head scales)."""
+    w = batch.w
+    kv = batch.kv_bytes_per_layer(unique=unique)
+    tables = int(sum(math.ceil(int(L) / 16) for L in batch.lengths)) * 4
+    lens = w.num_seqs * 4
+    qe = 4 if w.q_dtype == "f32" else 2
+    qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * qe
+    sc = 2 * w.num_kv_heads * 4 if w.cache_dtype == "fp8" else 0
+    return kv + tables + lens + qo + sc
+
+
+def cpu_baseline(batch, budget_s: float) -> dict:
+    """The CPU oracle, as it stands, on a bounded sample of set 0 of layer 0: whole sequences (all
+    query heads) taken in order until the estimated work fits the budget; repeated until at least
+    a few seconds have been measured."""
+    import oracle
+    from oracle.batch import OracleBatch
+
+    w = batch.w
+    L = batch.lengths.astype(np.int64)
+    # estimate: ~4 ns per (position, head-dim, query head) on one core for de-page + dot products
+    threads = oracle.max_threads()
+    per_seq = L * w.num_q_heads * w.head_dim * 4e-9 * 2 / max(threads, 1)
+    take, acc = [], 0.0
+    for s in range(w.num_seqs):
+        if take and acc + per_seq[s] > budget_s:
+            break
+        take.append(s)
+        acc += per_seq[s]
+    layer = batch.layers[0]
+    ob = OracleBatch(batch, pad_block=0)
+    ob.metadata_matches(batch)
+    ob.build_pools(batch, layer, owners=set(take))
+    sel = (np.repeat(take, w.num_q_heads), np.tile(np.arange(w.num_q_heads), len(take)))
+    e = 1 if w.cache_dtype == "fp8" else (4 if w.cache_dtype == "f32" else 2)
+    row = 2 * w.num_kv_heads * w.head_dim * e
+    # per query head the oracle de-pages its KV head's rows: count the logical bytes of the sample
+    sample_bytes = int(L[take].sum()) * row
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        ob.attention(batch, layer, sel=sel, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min(3.0, budget_s) or reps >= 50:
+            break
+    gbps = sample_bytes * reps / el / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"layer {layer}, set 0: {len(take)} of {w.num_seqs} sequences x all "
+                      f"{w.num_q_heads} query heads ({int(L[take].sum())} positions), fp64, "
+                      f"{reps} pass(es) in {el:.2f} s; seqs/s = "
+                      f"{len(take) * reps / el:.3f}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--sets", type=int, default=0, help="independent batches rotated (0 = default)")
+    ap.add_argument("--valu", action="store_true", help="force the vector-ALU decode kernel")
+    ap.add_argument("--partition", type=int, default=-1, help="partition size (-1 = workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode path here runs on a single MI355X and "
+              "has no multi-GPU mode (sharding would split sequences, KV heads or context "
+              "partitions across GPUs; it is not built).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from paged_kv_cache_356_amd import api
+    from paged_kv_cache_356_amd import workloads as wl
+    from paged_kv_cache_356_amd.decode_batch import DecodeBatch
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        return 1
+    api.lib()
+    w = wl.WORKLOADS[args.workload]
+    sets = args.sets or DEFAULT_SETS[w.name]
+    flags = api.PA_DECODE_FORCE_VALU if args.valu else api.PA_DECODE_DEFAULT
+    t_build = time.perf_counter()
+    batch = DecodeBatch(w, device="cuda", num_sets=sets,
+                        keep_values=not args.no_cpu_baseline,
+                        partition_size=None if args.partition < 0 else args.partition,
+                        keep_layers=[0])
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: built {sets} set(s), {len(batch.layers)} layer(s) in "
+        f"{time.perf_counter() - t_build:.1f} s; lengths {wl.lengths_summary(batch.lengths)}")
+
+    stream = torch.cuda.current_stream()
+    caches = [batch.caches[l] for l in batch.layers]
+    n_dec = args.steps * len(batch.layers)
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_dec)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_dec)]
+
+    def step(k: int, timed: bool):
+        r = k % sets
+        st = batch.sets[r]
+        if st.pairs.shape[0]:
+            api.pa_copy_blocks(caches, st.d_pairs, stream)
+        for li, l in enumerate(batch.layers):
+            cache = batch.caches[l]
+            api.pa_reshape_and_cache(cache, st.new_k[l], st.new_v[l], st.d_slots, stream)
+            if timed:
+                ev0[k * len(batch.layers) + li].record(stream)
+            api.pa_decode_attention(st.out[l], st.q[l], cache, st.d_tables, st.d_ctx,
+                                    batch.max_context_len, w.scale, batch.partition_size,
+                                    batch.workspace, flags, stream)
+            if timed:
+                ev1[k * len(batch.layers) + li].record(stream)
+
+    for k in range(args.warmup):
+        step(k, False)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} step(s) done")
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"[bench] timed {args.steps} step(s) in {elapsed * 1e3:.2f} ms")
+
+    dec_ms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
+    dec_mean_s = float(np.mean(dec_ms)) / 1e3
+    ms_per_step = elapsed * 1e3 / args.steps
+    layers = len(batch.layers)
+    kv_logical = batch.kv_bytes_per_layer(unique=False)
+    unique = w.prefix_len > 0
+    alg = algorithmic_bytes(batch, unique=unique)
+    achieved = alg / dec_mean_s / 1e9
+    value = kv_logical * layers / (ms_per_step / 1e3) / 1e9
+    seqs_per_s_layer = w.num_seqs / (ms_per_step / 1e3 / layers)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.cache_dtype if w.cache_dtype != "fp8" else "fp8-e4m3 KV, f16 q",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.description}",
+            "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": 16, "layers": layers,
+            "num_blocks_per_layer": w.num_blocks, "context_lens": wl.lengths_summary(batch.lengths),
+            "partition_size": batch.partition_size or api.pa_decode_auto_partition(
+                w.num_seqs, w.num_kv_heads, batch.max_context_len),
+            "kernel": "valu" if args.valu else "default",
+            "sets_rotated": sets,
+            "kv_bytes_per_step_logical": kv_logical * layers,
+            "kv_bytes_per_layer_unique": batch.kv_bytes_per_layer(unique=True) if unique else
+            kv_logical,
+            "copy_pairs_per_step": int(batch.sets[0].pairs.shape[0]),
+        },
+        "hbm_fraction_of_step": round(value / HBM_PEAK_GBPS, 4),
+        "seqs_per_s_per_layer": round(seqs_per_s_layer, 1),
+        "decode_call_us_mean": round(dec_mean_s * 1e6, 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "kernel": "pa_decode_attention (split-K decode + partition reduce)",
+            "bytes_per_call": alg,
+            "bytes_kind": "unique physical KV slots" if unique else "logical KV",
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,118 @@
+// cache_kernels.hip — reshape_and_cache (write each new token's K/V into its slot) and
+// copy_blocks (the clone step of copy-on-write) for gfx950.
+//
+// reshape_and_cache: each generated token appends one K/V entry inside the current block of its
+// sequence ("LLM Inference Visualizer, Lesson 06", "How paging grows"); K and V are what every
+// later token reads ("PagedAttention, Visualized", Part 2).
+// copy_blocks: a writer into a shared block gets a clone of that one block ("PagedAttention"
+// (devoured.fyi), "Copy-on-write: when two requests share a prefix").
+#include <type_traits>
+
+#include "pa_device.h"
+#include "pa_kernels.h"
+
+namespace pa {
+namespace {
+
+// One workgroup per token.  Thread v handles K vector c (E elements of head h) of that token:
+// it writes the 16-byte K vector in one store and the E transposed V elements one by one.
+template <class CT, class IT>
+__global__ __launch_bounds__(128) void reshape_and_cache_kernel(ReshapeArgs a) {
+  const int t = blockIdx.x;
+  const int64_t slot = a.slots[t];
+  const CacheArgs &c = a.cache;
+  if (slot < 0 || slot >= (int64_t)c.num_blocks * kBlock) return;  // padding / out of range
+  const int64_t blk = slot / kBlock;
+  const int off = (int)(slot % kBlock);
+  const int H = c.num_kv_heads, D = c.head_dim;
+  using L = Layout<CT::bytes>;
+  constexpr int E = L::E;
+  const int vec_per_head = D / E;
+  const auto *key = static_cast<const typename IT::raw *>(a.key) + (size_t)t * a.key_stride;
+  const auto *val = static_cast<const typename IT::raw *>(a.value) + (size_t)t * a.value_stride;
+  auto *kp = static_cast<typename CT::raw *>(c.k_pool);
+  auto *vp = static_cast<typename CT::raw *>(c.v_pool);
+  for (int v = threadIdx.x; v < H * vec_per_head; v += blockDim.x) {
+    const int h = v / vec_per_head, cv = v % vec_per_head;
+    const size_t tile = L::tile(blk, h, H, D);
+    const int i0 = cv * E;
+    union {
+      uint4 v;
+      typename CT::raw e[E];
+    } kv, vv;
+    if constexpr (std::is_same<CT, fp8_t>::value) {
+      const float ks = c.k_scale[h], vs = c.v_scale[h];
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        kv.e[j] = f32_to_e4m3(__fdiv_rn(load_f32<IT>(key, (size_t)h * D + i0 + j), ks));
+        vv.e[j] = f32_to_e4m3(__fdiv_rn(load_f32<IT>(val, (size_t)h * D + i0 + j), vs));
+      }
+    } else {
+      static_assert(std::is_same<CT, IT>::value, "non-fp8 caches take rows of their own dtype");
+#pragma unroll
+      for (int j = 0; j < E; ++j) {  // same dtype: bit copy
+        kv.e[j] = key[(size_t)h * D + i0 + j];
+        vv.e[j] = val[(size_t)h * D + i0 + j];
+      }
+    }
+    // K: the E elements are one contiguous 16-byte vector of the tile.
+    auto *kdst = kp + tile + L::k_off(off, i0);
+    *reinterpret_cast<uint4 *>(kdst) = kv.v;
+    // V: transposed tile, element (off, i) at i * 16 + off.
+#pragma unroll
+    for (int j = 0; j < E; ++j) vp[tile + L::v_off(off, i0 + j)] = vv.e[j];
+  }
+}
+
+template <class CT, class IT>
+hipError_t reshape_launch(const ReshapeArgs &a, hipStream_t s) {
+  reshape_and_cache_kernel<CT, IT><<<dim3(a.num_tokens), dim3(128), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// One workgroup per (pair, layer); 16-byte vector copies of the block's span in both pools.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
+  const int p = blockIdx.x, layer = blockIdx.y;
+  const int src = a.pairs[2 * p], dst = a.pairs[2 * p + 1];
+  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
+  const int64_t nvec = a.block_bytes / 16;
+  const uint4 *ks = reinterpret_cast<const uint4 *>(static_cast<const char *>(a.k_pools[layer]) +
+                                                    (size_t)src * a.block_bytes);
+  const uint4 *vs = reinterpret_cast<const uint4 *>(static_cast<const char *>(a.v_pools[layer]) +
+                                                    (size_t)src * a.block_bytes);
+  uint4 *kd = reinterpret_cast<uint4 *>(static_cast<char *>(a.k_pools[layer]) +
+                                        (size_t)dst * a.block_bytes);
+  uint4 *vd = reinterpret_cast<uint4 *>(static_cast<char *>(a.v_pools[layer]) +
+                                        (size_t)dst * a.block_bytes);
+  for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const ReshapeArgs &a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  switch (a.cache.dtype) {
+    case kF32: return reshape_launch<f32_t, f32_t>(a, s);
+    case kF16: return reshape_launch<f16_t, f16_t>(a, s);
+    case kBF16: return reshape_launch<bf16_t, bf16_t>(a, s);
+    case kFP8:
+      switch (a.in_dtype) {
+        case kF32: return reshape_launch<fp8_t, f32_t>(a, s);
+        case kF16: return reshape_launch<fp8_t, f16_t>(a, s);
+        case kBF16: return reshape_launch<fp8_t, bf16_t>(a, s);
+        default: return hipErrorInvalidValue;
+      }
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_copy_blocks(const CopyArgs &a, hipStream_t s) {
+  if (a.num_pairs == 0 || a.num_layers == 0) return hipSuccess;
+  copy_blocks_kernel<<<dim3(a.num_pairs, a.num_layers), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

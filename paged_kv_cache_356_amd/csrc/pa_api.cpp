@@ -1,0 +1,300 @@
+// pa_api.cpp — the C ABI of libpa.so (include/pa.h): argument validation, partition sizing and
+// dispatch to the gfx950 kernels.  Nothing here allocates or synchronises device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "pa.h"
+#include "pa_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status ok() { return PA_OK; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pa_status check_cache(const pa_cache *c, const char *who) {
+  if (!c) return fail(PA_ERR_NULL, "%s: cache is NULL", who);
+  if (c->block_size != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only %d is supported)", who, c->block_size,
+                PA_BLOCK_SIZE);
+  if (c->num_blocks < 0) return fail(PA_ERR_SHAPE, "%s: num_blocks %d < 0", who, c->num_blocks);
+  if (c->num_kv_heads < 1 || c->num_kv_heads > 16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: num_kv_heads %d outside 1..16", who, c->num_kv_heads);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128 supported)", who, c->head_dim);
+  if (c->cache_dtype < PA_F32 || c->cache_dtype > PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "%s: cache_dtype %d unknown", who, c->cache_dtype);
+  if (!c->k_pool || !c->v_pool) return fail(PA_ERR_NULL, "%s: k_pool / v_pool is NULL", who);
+  if (!aligned16(c->k_pool) || !aligned16(c->v_pool))
+    return fail(PA_ERR_SHAPE, "%s: pools must be 16-byte aligned", who);
+  const bool fp8 = c->cache_dtype == PA_FP8_E4M3;
+  if (fp8 && (!c->k_scale || !c->v_scale))
+    return fail(PA_ERR_NULL, "%s: an fp8 cache needs k_scale and v_scale", who);
+  if (!fp8 && (c->k_scale || c->v_scale))
+    return fail(PA_ERR_SHAPE, "%s: scales are only meaningful for an fp8 cache", who);
+  return PA_OK;
+}
+
+pa::CacheArgs cache_args(const pa_cache *c) {
+  pa::CacheArgs a;
+  a.k_pool = c->k_pool;
+  a.v_pool = c->v_pool;
+  a.k_scale = c->k_scale;
+  a.v_scale = c->v_scale;
+  a.num_blocks = c->num_blocks;
+  a.num_kv_heads = c->num_kv_heads;
+  a.head_dim = c->head_dim;
+  a.dtype = c->cache_dtype;
+  return a;
+}
+
+pa_status launch_status(hipError_t e, const char *who) {
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "%s: %s", who, hipGetErrorString(e));
+  return PA_OK;
+}
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                          int32_t partition_size) {
+  return partition_size > 0 ? partition_size
+                            : pa_decode_auto_partition(num_seqs, num_kv_heads, max_context_len);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_pool_bytes(const pa_cache *c) {
+  if (!c || c->block_size != PA_BLOCK_SIZE || c->num_blocks < 0 || c->num_kv_heads < 1 ||
+      c->head_dim < 1)
+    return 0;
+  const int e = pa::dtype_bytes(c->cache_dtype);
+  if (!e) return 0;
+  return (size_t)c->num_blocks * c->num_kv_heads * c->block_size * c->head_dim * e;
+}
+
+pa_status pa_reshape_and_cache(const pa_cache *cache, const void *key, const void *value,
+                               int32_t in_dtype, int64_t key_stride, int64_t value_stride,
+                               const int64_t *slot_mapping, int32_t num_tokens, void *stream) {
+  const char *who = "pa_reshape_and_cache";
+  pa_status st = check_cache(cache, who);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "%s: num_tokens %d < 0", who, num_tokens);
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !slot_mapping) return fail(PA_ERR_NULL, "%s: NULL key/value/slots", who);
+  if (in_dtype < PA_F32 || in_dtype > PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: in_dtype %d (f32/f16/bf16 rows only)", who, in_dtype);
+  if (cache->cache_dtype != PA_FP8_E4M3 && in_dtype != cache->cache_dtype)
+    return fail(PA_ERR_UNSUPPORTED, "%s: rows of dtype %d into a cache of dtype %d", who, in_dtype,
+                cache->cache_dtype);
+  const int64_t row = (int64_t)cache->num_kv_heads * cache->head_dim;
+  if (key_stride == 0) key_stride = row;
+  if (value_stride == 0) value_stride = row;
+  if (key_stride < row || value_stride < row)
+    return fail(PA_ERR_SHAPE, "%s: strides %lld/%lld below a row of %lld elements", who,
+                (long long)key_stride, (long long)value_stride, (long long)row);
+  pa::ReshapeArgs a;
+  a.cache = cache_args(cache);
+  a.key = key;
+  a.value = value;
+  a.in_dtype = in_dtype;
+  a.key_stride = key_stride;
+  a.value_stride = value_stride;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  return launch_status(pa::launch_reshape_and_cache(a, static_cast<hipStream_t>(stream)), who);
+}
+
+int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+  // Split long contexts into 512-token partitions; when that leaves too few workgroups to cover
+  // 256 compute units several times over, halve the partition (not below 128 tokens).
+  int32_t pt = 512;
+  const int64_t rows = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
+  const int32_t L = max_context_len > 0 ? max_context_len : 1;
+  while (pt > 128 && rows * ceil_div(L, pt) < 2048) pt /= 2;
+  return pt;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const int32_t pt = resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+  if (pt <= 0) return 0;
+  const int64_t np = ceil_div(max_context_len, pt);
+  if (np <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)np;
+  return align256(rows * head_dim * sizeof(float)) + align256(rows * 2 * sizeof(float));
+}
+
+pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int64_t q_stride,
+                              const pa_cache *cache, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                              float scale, int32_t partition_size, void *workspace,
+                              size_t workspace_bytes, uint32_t flags, void *stream) {
+  const char *who = "pa_decode_attention";
+  pa_status st = check_cache(cache, who);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_seqs > 65535)
+    return fail(PA_ERR_SHAPE, "%s: num_seqs %d outside 0..65535", who, num_seqs);
+  if (num_seqs == 0) return ok();
+  if (!out || !query || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL, "%s: NULL out/query/block_tables/context_lens", who);
+  const int H = cache->num_kv_heads, D = cache->head_dim;
+  if (num_q_heads < 1 || num_q_heads % H != 0)
+    return fail(PA_ERR_SHAPE, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", who,
+                num_q_heads, H);
+  if (num_q_heads / H > 16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most 16)", who,
+                num_q_heads / H);
+  const int cdt = cache->cache_dtype;
+  const bool combo_ok = (cdt == PA_FP8_E4M3) ? (q_dtype == PA_F16 || q_dtype == PA_BF16)
+                                             : (q_dtype == cdt);
+  if (!combo_ok)
+    return fail(PA_ERR_UNSUPPORTED, "%s: query dtype %d with cache dtype %d", who, q_dtype, cdt);
+  if (max_blocks_per_seq < 1)
+    return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq %d < 1", who, max_blocks_per_seq);
+  if (max_context_len < 0) return fail(PA_ERR_SHAPE, "%s: max_context_len < 0", who);
+  if (partition_size < 0 || partition_size % PA_BLOCK_SIZE != 0)
+    return fail(PA_ERR_SHAPE, "%s: partition_size %d is not a non-negative multiple of 16", who,
+                partition_size);
+  if (q_stride == 0) q_stride = (int64_t)num_q_heads * D;
+  if (q_stride < (int64_t)num_q_heads * D)
+    return fail(PA_ERR_SHAPE, "%s: q_stride %lld below a row", who, (long long)q_stride);
+  if ((flags & ~PA_DECODE_FORCE_VALU) != 0) return fail(PA_ERR_SHAPE, "%s: unknown flags", who);
+
+  const int64_t cap = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
+  const int32_t max_len = (int32_t)(max_context_len < cap ? max_context_len : cap);
+  const int32_t pt = resolve_partition(num_seqs, H, max_len, partition_size);
+  const int32_t np = max_len > 0 ? ceil_div(max_len, pt) : 1;
+  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, H, D, max_len, pt);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
+                need);
+  if (need > 0 && !aligned16(workspace))
+    return fail(PA_ERR_SHAPE, "%s: workspace must be 16-byte aligned", who);
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.q = query;
+  a.q_stride = q_stride;
+  a.q_dtype = q_dtype;
+  a.cache = cache_args(cache);
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.max_context_len = max_len;
+  a.scale = scale;
+  a.partition_size = pt;
+  a.num_partitions = np;
+  a.part_out = nullptr;
+  a.part_ml = nullptr;
+  if (np > 1) {
+    const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)np;
+    a.part_out = static_cast<float *>(workspace);
+    a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                          align256(rows * D * sizeof(float)));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool use_mfma = !(flags & PA_DECODE_FORCE_VALU) && pa::decode_mfma_supports(a);
+  hipError_t e = use_mfma ? pa::launch_decode_mfma(a, s) : pa::launch_decode_valu(a, s);
+  if (e == hipSuccess) e = pa::launch_partition_reduce(a, s);
+  return launch_status(e, who);
+}
+
+pa_status pa_check_copy_pairs(const int32_t *pairs, int32_t num_pairs, int32_t num_blocks) {
+  const char *who = "pa_check_copy_pairs";
+  if (num_pairs < 0) return fail(PA_ERR_SHAPE, "%s: num_pairs < 0", who);
+  if (num_pairs > 0 && !pairs) return fail(PA_ERR_NULL, "%s: pairs is NULL", who);
+  if (num_blocks < 0) return fail(PA_ERR_SHAPE, "%s: num_blocks < 0", who);
+  std::vector<char> is_dst((size_t)num_blocks, 0), is_src((size_t)num_blocks, 0);
+  for (int32_t k = 0; k < num_pairs; ++k) {
+    const int32_t s = pairs[2 * k], d = pairs[2 * k + 1];
+    if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
+      return fail(PA_ERR_SHAPE, "%s: pair %d = (%d, %d) outside the pool", who, k, s, d);
+    is_src[(size_t)s] = 1;
+  }
+  for (int32_t k = 0; k < num_pairs; ++k) {
+    const int32_t d = pairs[2 * k + 1];
+    if (is_dst[(size_t)d]) return fail(PA_ERR_ALIAS, "%s: destination %d repeats", who, d);
+    if (is_src[(size_t)d]) return fail(PA_ERR_ALIAS, "%s: destination %d is also a source", who, d);
+    is_dst[(size_t)d] = 1;
+  }
+  return PA_OK;
+}
+
+pa_status pa_copy_blocks(const pa_cache *layers, int32_t num_layers, const int32_t *block_pairs,
+                         int32_t num_pairs, void *stream) {
+  const char *who = "pa_copy_blocks";
+  if (num_layers < 0 || num_pairs < 0) return fail(PA_ERR_SHAPE, "%s: negative count", who);
+  if (num_layers == 0 || num_pairs == 0) return ok();
+  if (!layers || !block_pairs) return fail(PA_ERR_NULL, "%s: NULL layers / block_pairs", who);
+  for (int32_t l = 0; l < num_layers; ++l) {
+    pa_status st = check_cache(&layers[l], who);
+    if (st != PA_OK) return st;
+    if (layers[l].num_blocks != layers[0].num_blocks ||
+        layers[l].num_kv_heads != layers[0].num_kv_heads ||
+        layers[l].head_dim != layers[0].head_dim || layers[l].cache_dtype != layers[0].cache_dtype)
+      return fail(PA_ERR_SHAPE, "%s: layer %d differs in shape or dtype from layer 0", who, l);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t block_bytes = (int64_t)layers[0].num_kv_heads * PA_BLOCK_SIZE * layers[0].head_dim *
+                              pa::dtype_bytes(layers[0].cache_dtype);
+  for (int32_t l0 = 0; l0 < num_layers; l0 += pa::CopyArgs::kMaxLayers) {
+    pa::CopyArgs a;
+    a.num_layers = num_layers - l0 < pa::CopyArgs::kMaxLayers ? num_layers - l0
+                                                              : pa::CopyArgs::kMaxLayers;
+    for (int32_t l = 0; l < a.num_layers; ++l) {
+      a.k_pools[l] = layers[l0 + l].k_pool;
+      a.v_pools[l] = layers[l0 + l].v_pool;
+    }
+    a.block_bytes = block_bytes;
+    a.num_blocks = layers[0].num_blocks;
+    a.pairs = block_pairs;
+    a.num_pairs = num_pairs;
+    pa_status st = launch_status(pa::launch_copy_blocks(a, s), who);
+    if (st != PA_OK) return st;
+  }
+  return PA_OK;
+}
+
+const char *pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "null pointer";
+    case PA_ERR_SHAPE: return "bad shape or size";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_ALIAS: return "overlapping copy pairs";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_NO_BLOCKS: return "no free blocks";
+    case PA_ERR_STATE: return "bad sequence or block id";
+  }
+  return "unknown status";
+}
+
+const char *pa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// pa_kernels.h — host-side launch interface between the C ABI layer (pa_api.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by pa_api.cpp and only enqueues work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };
+
+inline int dtype_bytes(int dt) {
+  return dt == kF32 ? 4 : (dt == kF16 || dt == kBF16) ? 2 : dt == kFP8 ? 1 : 0;
+}
+
+struct CacheArgs {
+  void *k_pool;
+  void *v_pool;
+  const float *k_scale;
+  const float *v_scale;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+};
+
+struct ReshapeArgs {
+  CacheArgs cache;
+  const void *key;
+  const void *value;
+  int32_t in_dtype;
+  int64_t key_stride;    // elements between token rows
+  int64_t value_stride;  // elements between token rows
+  const int64_t *slots;
+  int32_t num_tokens;
+};
+
+// Per-partition results of the split-K decode, owned by the caller's workspace:
+//   part_out [S][Hq][P][D] fp32, normalised partial outputs
+//   part_ml  [S][Hq][P][2] fp32, (running max, running sum) of each partition
+struct DecodeArgs {
+  void *out;
+  const void *q;
+  int64_t q_stride;
+  int32_t q_dtype;
+  CacheArgs cache;
+  const int32_t *block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t *context_lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t max_context_len;  // already clamped to 16 * max_blocks_per_seq
+  float scale;
+  int32_t partition_size;   // tokens per partition, multiple of 16
+  int32_t num_partitions;   // ceil(max_context_len / partition_size)
+  float *part_out;          // NULL when num_partitions == 1
+  float *part_ml;
+};
+
+struct CopyArgs {
+  static constexpr int kMaxLayers = 32;
+  void *k_pools[kMaxLayers];
+  void *v_pools[kMaxLayers];
+  int32_t num_layers;
+  int64_t block_bytes;  // bytes of one block in one pool (all KV heads)
+  int32_t num_blocks;
+  const int32_t *pairs;
+  int32_t num_pairs;
+};
+
+hipError_t launch_reshape_and_cache(const ReshapeArgs &a, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyArgs &a, hipStream_t stream);
+hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
+bool decode_mfma_supports(const DecodeArgs &a);
+hipError_t launch_partition_reduce(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace pa

@@ -136,3 +136,34 @@ def normal(shape, dtype: str, gen: torch.Generator, device="cpu") -> torch.Tenso
 
 def lengths_summary(L: np.ndarray) -> dict:
     return {"min": int(L.min()), "max": int(L.max()), "mean": float(L.mean()), "sum": int(L.sum())}
+
+
+def build_history(bm, lengths, prefix_len: int = 0, twins: bool = False):
+    """The workload's recipe of block-manager operations, run on whichever manager it is given.
+
+    Each batch sequence s ends up holding lengths[s] - 1 positions, so this step's append brings it
+    to lengths[s].  With prefix_len > 0 a prefix sequence of prefix_len positions is built first,
+    every batch sequence is forked from it, and the prefix's owner is released (the batch's tables
+    share its blocks).  With twins, every batch sequence is forked once more after its history is
+    written and the fork is kept aside, so the block this step writes into is shared and must be
+    cloned first.
+
+    Returns (seqs, history, twin_ids); history lists (owner, slots) in write order, owner "prefix"
+    or the batch index, with the slots of the positions written for that owner.
+    """
+    history = []
+    seqs = []
+    if prefix_len:
+        p = bm.add_seq()
+        history.append(("prefix", [bm.append(p)[0] for _ in range(prefix_len)]))
+        seqs = [bm.fork(p) for _ in lengths]
+        bm.free_seq(p)
+    else:
+        seqs = [bm.add_seq() for _ in lengths]
+    for i, (s, L) in enumerate(zip(seqs, lengths)):
+        n = int(L) - 1 - prefix_len
+        if n < 0:
+            raise ValueError(f"length {int(L)} does not cover the {prefix_len}-token prefix + 1")
+        history.append((i, [bm.append(s)[0] for _ in range(n)]))
+    twin_ids = [bm.fork(s) for s in seqs] if twins else []
+    return seqs, history, twin_ids

@@ -47,36 +47,3 @@ def max_abs_err(a, b) -> float:
 
 
 TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2, "fp8": 3e-2}
-
-
-def build_history(bm, lengths, prefix_len: int = 0, twins: bool = False):
-    """Drive a block manager (oracle model or product) through the setup of a decode batch.
-
-    Each sequence s ends up holding lengths[s] - 1 history positions, so that this step's append
-    brings it to lengths[s].  With prefix_len > 0 a prefix sequence of prefix_len positions is
-    built first, every batch sequence is forked from it and the prefix owner is then released (the
-    batch's tables share its blocks).  With twins, every batch sequence is forked once more after
-    its history is written and the fork is kept aside, so the block the step writes into is shared
-    and the step's append must clone it.
-
-    Returns (seqs, history) where history is a list of (owner_tag, slots) in write order: owner
-    "prefix" or the batch index, with the slots its history positions were written to.
-    """
-    history = []
-    seqs = []
-    if prefix_len:
-        p = bm.add_seq()
-        slots = [bm.append(p)[0] for _ in range(prefix_len)]
-        history.append(("prefix", slots))
-        for _ in lengths:
-            seqs.append(bm.fork(p))
-        bm.free_seq(p)
-    else:
-        for _ in lengths:
-            seqs.append(bm.add_seq())
-    for i, (s, L) in enumerate(zip(seqs, lengths)):
-        n = int(L) - 1 - prefix_len
-        slots = [bm.append(s)[0] for _ in range(n)]
-        history.append((i, slots))
-    twin_ids = [bm.fork(s) for s in seqs] if twins else []
-    return seqs, history, twin_ids

@@ -1,0 +1,224 @@
+"""CPU tests of the product's host side: libpa.so loads and exports every symbol include/pa.h
+declares, argument validation rejects bad calls before any launch, the C++ block manager agrees
+bit for bit with the oracle's model, and the pages' per-token KV arithmetic holds for
+pa_pool_bytes.  No kernel is launched here."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle.bm_model import BlockManagerModel, NoBlocks
+from paged_kv_cache_356_amd import api
+from paged_kv_cache_356_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    declared = _header_functions()
+    assert len(declared) >= 21
+    assert sorted(api.EXPORTS) == declared
+    L = api.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = api.lib()
+    for code in api.STATUS:
+        assert L.pa_status_string(code)
+
+
+def _cache(**kw):
+    d = dict(k_pool=16, v_pool=32, k_scale=None, v_scale=None, num_blocks=8, block_size=16,
+             num_kv_heads=4, head_dim=128, cache_dtype=api.PA_F16)
+    d.update(kw)
+    return api.pa_cache(d["k_pool"], d["v_pool"], d["k_scale"], d["v_scale"], d["num_blocks"],
+                        d["block_size"], d["num_kv_heads"], d["head_dim"], d["cache_dtype"])
+
+
+def _decode(cache, **kw):
+    a = dict(out=64, query=128, q_dtype=api.PA_F16, q_stride=0, tables=256, max_blocks=4, ctx=512,
+             S=2, Hq=28, max_ctx=64, scale=0.1, ps=0, ws=None, ws_bytes=0, flags=0)
+    a.update(kw)
+    return api.lib().pa_decode_attention(a["out"], a["query"], a["q_dtype"], a["q_stride"],
+                                         ctypes.byref(cache), a["tables"], a["max_blocks"], a["ctx"],
+                                         a["S"], a["Hq"], a["max_ctx"], a["scale"], a["ps"], a["ws"],
+                                         a["ws_bytes"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_size=8), -3), (dict(head_dim=96), -3), (dict(num_kv_heads=0), -3),
+    (dict(cache_dtype=9), -3), (dict(k_pool=None), -1), (dict(k_pool=17), -2),
+    (dict(cache_dtype=api.PA_FP8_E4M3), -1), (dict(k_scale=64), -2),
+])
+def test_cache_validation(kw, status):
+    assert _decode(_cache(**kw)) == status
+    assert api.lib().pa_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=30), -2), (dict(Hq=4 * 17), -3), (dict(q_dtype=api.PA_BF16), -3),
+    (dict(out=None), -1), (dict(max_blocks=0), -2), (dict(ps=24), -2), (dict(ps=-16), -2),
+    (dict(q_stride=100), -2), (dict(flags=8), -2), (dict(S=70000), -2), (dict(max_ctx=-1), -2),
+    (dict(max_ctx=4096, ps=16), -4),
+])
+def test_decode_validation(kw, status):
+    assert _decode(_cache(), **kw) == status
+
+
+def test_zero_sequences_is_a_no_op():
+    assert _decode(_cache(), S=0, out=None, query=None) == 0
+
+
+def test_workspace_sizing():
+    ws = api.pa_decode_workspace_bytes
+    assert ws(8, 28, 4, 128, 512, 512) == 0                 # one partition: no workspace
+    rows = 8 * 28 * 64
+    need = ws(8, 28, 4, 128, 32768, 512)
+    assert need >= rows * 128 * 4 + rows * 2 * 4
+    assert api.pa_decode_auto_partition(8, 4, 32768) == 512
+    assert api.pa_decode_auto_partition(32, 4, 2048) in (128, 256)
+    assert api.pa_decode_auto_partition(1, 1, 100) == 128
+
+
+def test_reshape_validation():
+    L = api.lib()
+    c = _cache()
+    f = L.pa_reshape_and_cache
+    assert f(ctypes.byref(c), 64, 64, api.PA_F16, 0, 0, 128, 0, None) == 0
+    assert f(ctypes.byref(c), 64, 64, api.PA_BF16, 0, 0, 128, 3, None) == -3
+    assert f(ctypes.byref(c), None, 64, api.PA_F16, 0, 0, 128, 3, None) == -1
+    assert f(ctypes.byref(c), 64, 64, api.PA_F16, 100, 0, 128, 3, None) == -2
+    assert f(ctypes.byref(c), 64, 64, api.PA_F16, 0, 0, 128, -1, None) == -2
+
+
+def test_copy_pair_checks():
+    api.pa_check_copy_pairs(np.array([[1, 2], [1, 3], [4, 5]]), 8)
+    with pytest.raises(api.PaError) as e:
+        api.pa_check_copy_pairs(np.array([[1, 2], [3, 2]]), 8)
+    assert e.value.status == -5
+    with pytest.raises(api.PaError) as e:
+        api.pa_check_copy_pairs(np.array([[1, 2], [2, 3]]), 8)
+    assert e.value.status == -5
+    with pytest.raises(api.PaError) as e:
+        api.pa_check_copy_pairs(np.array([[1, 8]]), 8)
+    assert e.value.status == -2
+
+
+# ------------------------------------------------------------------ block manager vs the model
+@pytest.mark.parametrize("seed", range(8))
+def test_block_manager_matches_model(seed):
+    g = np.random.default_rng(100 + seed)
+    nb, B = 96, int(g.choice([1, 4, 16]))
+    order = g.permutation(nb)
+    prod = api.BlockManager(nb, B, order)
+    model = BlockManagerModel(nb, B, order)
+    live = []
+    for step in range(800):
+        op = int(g.integers(0, 10))
+        if op == 0 or not live:
+            a, b = prod.add_seq(), model.add_seq()
+            assert a == b
+            live.append(a)
+        elif op == 1:
+            p = live[int(g.integers(len(live)))]
+            a, b = prod.fork(p), model.fork(p)
+            assert a == b
+            live.append(a)
+        elif op == 2 and len(live) > 1:
+            s = live.pop(int(g.integers(len(live))))
+            prod.free_seq(s)
+            model.free_seq(s)
+        elif op == 3:
+            seqs = [live[i] for i in g.integers(0, len(live), 5)]
+            seqs = list(dict.fromkeys(seqs))
+            try:
+                want = model.append_batch(seqs)
+            except NoBlocks:
+                # both stop at the first failure and keep the appends made before it
+                with pytest.raises(api.PaError) as e:
+                    prod.append_batch(seqs)
+                assert e.value.status == -7
+                continue
+            slots, pairs = prod.append_batch(seqs)
+            assert list(slots) == want[0]
+            assert [tuple(p) for p in pairs.tolist()] == want[1]
+        else:
+            s = live[int(g.integers(len(live)))]
+            try:
+                want = model.append(s)
+            except NoBlocks:
+                with pytest.raises(api.PaError) as e:
+                    prod.append(s)
+                assert e.value.status == -7
+                continue
+            assert prod.append(s) == want
+        assert prod.num_free() == len(model.free)
+    for s in live:
+        assert prod.table(s) == model.table(s)
+        assert prod.seq_len(s) == model.lens[s]
+    for b in range(nb):
+        assert prod.refcount(b) == model.ref[b]
+    M = max(len(model.table(s)) for s in live) + 2
+    t, lens = prod.export(live, M, pad=-3)
+    rows, mlens = model.export(live, M, -3)
+    assert t.tolist() == rows and lens.tolist() == mlens
+
+
+def test_block_manager_workload_recipe_matches_model():
+    w = wl.WORKLOADS["c4"].replace(num_seqs=12, num_blocks=2048, prefix_len=64)
+    L = 64 + wl.suffix_lengths(w.replace(num_seqs=256))[:12]
+    fo = wl.free_order(w)
+    prod, model = api.BlockManager(w.num_blocks, 16, fo), BlockManagerModel(w.num_blocks, 16, fo)
+    a = wl.build_history(prod, L, w.prefix_len, twins=True)
+    b = wl.build_history(model, L, w.prefix_len, twins=True)
+    assert a == b
+    sa, pa = prod.append_batch(a[0])
+    sb, pb = model.append_batch(b[0])
+    assert list(sa) == sb and [tuple(p) for p in pa.tolist()] == pb
+    assert len(pb) == sum(1 for x in L if (x - 1) % 16 != 0)
+    # the prefix's blocks are referenced by every batch table and every parked twin
+    for blk in prod.table(a[0][0])[:4]:
+        assert prod.refcount(blk) == 2 * 12
+
+
+def test_bad_block_manager_arguments():
+    with pytest.raises(api.PaError):
+        api.BlockManager(4, 16, [0, 1, 1, 2])
+    bm = api.BlockManager(4, 16)
+    with pytest.raises(api.PaError) as e:
+        bm.append(3)
+    assert e.value.status == -8
+    assert bm.refcount(9) == -1 and bm.seq_len(0) == -1
+
+
+# ------------------------------------------------------------------ the pages' arithmetic
+def test_per_token_kv_bytes_of_qwen25_7b():
+    # "PagedAttention, Visualized", Part 2: 2 (K and V) x 512 x 28 layers x 2 bytes = 57,344 bytes
+    nb = 1000
+    per_layer = 2 * api.pool_bytes(nb, 4, 128, api.PA_F16) / (nb * 16)
+    assert per_layer * 28 == 57344
+    fp8 = 2 * api.pool_bytes(nb, 4, 128, api.PA_FP8_E4M3) / (nb * 16)
+    assert fp8 * 28 == 57344 // 2
+    # the A40 figure on the same page: 447,168 tokens of KV; 23.88 GiB is its rounded size
+    total = 447168 * 57344
+    assert total == 25_642_401_792 and round(total / 2 ** 30, 2) == 23.88
+    # the page's "about 57,335 bytes" comes from the rounded 23.88 GiB; the exact rate is 57,344
+    assert abs(23.88 * 2 ** 30 / 447168 - 57344) < 10
+    # a 32,000-token conversation: about 1.8 GB
+    assert 32000 * 57344 == 1_835_008_000
+    # concurrency ceiling at a 32,768-token maximum context: 13.65x
+    assert round(447168 / 32768, 2) == 13.65
+    # reserving 32,768 slots for a 500-token conversation wastes about 98%
+    assert round(1 - 500 / 32768, 2) == 0.98
