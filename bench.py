@@ -107,8 +107,13 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=0, help="independent batches rotated (0 = default)")
     ap.add_argument("--valu", action="store_true", help="force the vector-ALU decode kernel")
     ap.add_argument("--partition", type=int, default=-1, help="partition size (-1 = workload's)")
+    ap.add_argument("--num-blocks", type=int, default=0,
+                    help="physical blocks per layer pool (0 = the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB a few times (the "
+                         "reference kernel for scaling HBM byte counters) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -127,8 +132,20 @@ def main() -> int:
     if not torch.cuda.is_available():
         log("bench.py needs a GPU")
         return 1
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n,
+                          "copies": 3}), flush=True)
+        return 0
     api.lib()
     w = wl.WORKLOADS[args.workload]
+    if args.num_blocks:
+        w = w.replace(num_blocks=args.num_blocks)
     sets = args.sets or DEFAULT_SETS[w.name]
     flags = api.PA_DECODE_FORCE_VALU if args.valu else api.PA_DECODE_DEFAULT
     t_build = time.perf_counter()

@@ -70,23 +70,43 @@ hipError_t reshape_launch(const ReshapeArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One workgroup per (pair, layer); 16-byte vector copies of the block's span in both pools.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
+// One workgroup per (pair, layer, chunk of 64 KiB of the block's span in both pools).  Every
+// thread issues all of its 16-byte loads before its first store (the source and destination blocks
+// are distinct, which the restrict qualifiers state), so a copy costs one memory round trip.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyVecs = 8;  // 16-byte vectors per thread and pool in one chunk
+constexpr int64_t kCopyChunk = (int64_t)kCopyThreads * kCopyVecs;  // vectors per chunk and pool
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs a) {
   const int p = blockIdx.x, layer = blockIdx.y;
   const int src = a.pairs[2 * p], dst = a.pairs[2 * p + 1];
   if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
   const int64_t nvec = a.block_bytes / 16;
-  const uint4 *ks = reinterpret_cast<const uint4 *>(static_cast<const char *>(a.k_pools[layer]) +
-                                                    (size_t)src * a.block_bytes);
-  const uint4 *vs = reinterpret_cast<const uint4 *>(static_cast<const char *>(a.v_pools[layer]) +
-                                                    (size_t)src * a.block_bytes);
-  uint4 *kd = reinterpret_cast<uint4 *>(static_cast<char *>(a.k_pools[layer]) +
-                                        (size_t)dst * a.block_bytes);
-  uint4 *vd = reinterpret_cast<uint4 *>(static_cast<char *>(a.v_pools[layer]) +
-                                        (size_t)dst * a.block_bytes);
-  for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) {
-    kd[i] = ks[i];
-    vd[i] = vs[i];
+  const int64_t v0 = (int64_t)blockIdx.z * kCopyChunk;
+  const uint4 *__restrict__ ks = reinterpret_cast<const uint4 *>(
+      static_cast<const char *>(a.k_pools[layer]) + (size_t)src * a.block_bytes);
+  const uint4 *__restrict__ vs = reinterpret_cast<const uint4 *>(
+      static_cast<const char *>(a.v_pools[layer]) + (size_t)src * a.block_bytes);
+  uint4 *__restrict__ kd = reinterpret_cast<uint4 *>(static_cast<char *>(a.k_pools[layer]) +
+                                                     (size_t)dst * a.block_bytes);
+  uint4 *__restrict__ vd = reinterpret_cast<uint4 *>(static_cast<char *>(a.v_pools[layer]) +
+                                                     (size_t)dst * a.block_bytes);
+  uint4 kx[kCopyVecs], vx[kCopyVecs];
+#pragma unroll
+  for (int k = 0; k < kCopyVecs; ++k) {
+    const int64_t i = v0 + threadIdx.x + (int64_t)k * kCopyThreads;
+    if (i < nvec) {
+      kx[k] = ks[i];
+      vx[k] = vs[i];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kCopyVecs; ++k) {
+    const int64_t i = v0 + threadIdx.x + (int64_t)k * kCopyThreads;
+    if (i < nvec) {
+      kd[i] = kx[k];
+      vd[i] = vx[k];
+    }
   }
 }
 
@@ -111,7 +131,9 @@ hipError_t launch_reshape_and_cache(const ReshapeArgs &a, hipStream_t s) {
 
 hipError_t launch_copy_blocks(const CopyArgs &a, hipStream_t s) {
   if (a.num_pairs == 0 || a.num_layers == 0) return hipSuccess;
-  copy_blocks_kernel<<<dim3(a.num_pairs, a.num_layers), dim3(256), 0, s>>>(a);
+  const int64_t nvec = a.block_bytes / 16;
+  const unsigned chunks = (unsigned)((nvec + kCopyChunk - 1) / kCopyChunk);
+  copy_blocks_kernel<<<dim3(a.num_pairs, a.num_layers, chunks), dim3(kCopyThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 

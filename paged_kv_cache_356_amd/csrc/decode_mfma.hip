@@ -39,6 +39,8 @@
 // Workgroup = 4 wavefronts for one (partition, KV head, sequence); wavefront w takes the
 // partition's blocks w, w+4, ... and keeps the loads of its next blocks in flight while it computes
 // the current one.  The four partial states are merged through LDS.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -48,6 +50,7 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kMaxScanSeqs = 4096;  // persistent grid: sequences whose item prefix fits in LDS
 #ifndef PA_DECODE_BUFS
 #define PA_DECODE_BUFS 2
 #endif
@@ -74,6 +77,8 @@ __device__ __forceinline__ T load_kv(const char *p) {
   else return *reinterpret_cast<const T *>(p);
 }
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNoMax = -3.0e38f;  // running-maximum floor (finite)
+constexpr float kSlack = 8.0f;  // base-2 headroom of the lazily rescaled running maximum
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
@@ -124,8 +129,22 @@ __device__ __forceinline__ float unpack_hi(uint32_t v) {
   else return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
-// Four E4M3FN bytes (byte 0 first) -> four binary16 values equal to decode(byte) * 2^-8.
+#ifndef PA_FP8_HWCVT
+#define PA_FP8_HWCVT 1
+#endif
+// Scale that the f16 values produced from fp8 codes carry: 2^-8 for the bit mapping below, 1 for
+// the hardware conversion.
+constexpr float kFp8Unscale = PA_FP8_HWCVT ? 1.0f : 256.0f;
+
+// Four E4M3FN bytes (byte 0 first) -> four binary16 values equal to decode(byte) * 2^-8, or, with
+// the hardware conversion (v_cvt_scalef32_pk_f16_fp8 at scale 1), equal to decode(byte).
 __device__ __forceinline__ uint2 e4m3x4_to_f16x4(uint32_t x) {
+#if PA_FP8_HWCVT
+  uint2 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true));
+  return r;
+#else
   const uint32_t t01 = ((x & 0xffu) << 8) | ((x & 0xff00u) << 16);
   const uint32_t t23 = ((x >> 8) & 0xff00u) | (x & 0xff000000u);
   uint2 r;
@@ -140,6 +159,7 @@ __device__ __forceinline__ uint2 e4m3x4_to_f16x4(uint32_t x) {
     if ((y & 0x7f000000u) == 0x7f000000u) r.y |= 0x7e000000u;
   }
   return r;
+#endif
 }
 
 template <class CT, int D>
@@ -152,22 +172,32 @@ struct Frag {
   VRaw v[kNT];
 };
 
+template <int D>
+struct DecodeLds {
+  float o[kWaves][D][17];  // each wavefront's unnormalised output, [head-dim][head] (+1 pad)
+  float m[kWaves][16];
+  float l[kWaves][16];
+};
+
+// One work item: partition `part` of sequence s for KV head h, computed by the whole workgroup.
 template <class CT, class QT, int D>
-__global__ __launch_bounds__(256)
-#if PA_DECODE_OCC
-__attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC, PA_DECODE_OCC)))
-#endif
-void decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_item(const DecodeArgs &a, int s_in, int h_in, int part_in,
+                                            DecodeLds<D> &lds) {
+  // The item is the same for the whole workgroup: keep its coordinates (and so the block-table
+  // row and the tile addresses) in scalar registers, which makes the table reads scalar loads.
+  const int s = __builtin_amdgcn_readfirstlane(s_in);
+  const int h = __builtin_amdgcn_readfirstlane(h_in);
+  const int part = __builtin_amdgcn_readfirstlane(part_in);
   constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
   constexpr bool kBF = std::is_same<CT, bf16_t>::value;  // fp8 and f16 caches compute in f16
   constexpr int KK = D / 32;                              // QK^T products per block
   using F = Frag<CT, D>;
   constexpr int NT = F::kNT;
   constexpr int kTileBytes = kBlock * D * CT::bytes;
-  __shared__ float o_s[kWaves][D][17];
-  __shared__ float m_s[kWaves][16], l_s[kWaves][16];
+  auto &o_s = lds.o;
+  auto &m_s = lds.m;
+  auto &l_s = lds.l;
 
-  const int s = blockIdx.z, h = blockIdx.y, part = blockIdx.x;
   const int H = a.cache.num_kv_heads, Hq = a.num_q_heads, g = Hq / H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -203,8 +233,8 @@ void decode_mfma_kernel(DecodeArgs a) {
 
   float kscale = a.scale * kLog2e, vscale = 1.0f;
   if constexpr (kFP8) {
-    kscale *= a.cache.k_scale[h] * 256.0f;
-    vscale = a.cache.v_scale[h] * 256.0f;
+    kscale *= a.cache.k_scale[h] * kFp8Unscale;
+    vscale = a.cache.v_scale[h] * kFp8Unscale;
   }
   const char *kpool = static_cast<const char *>(a.cache.k_pool);
   const char *vpool = static_cast<const char *>(a.cache.v_pool);
@@ -223,12 +253,16 @@ void decode_mfma_kernel(DecodeArgs a) {
       f.v[nt] = load_kv<typename F::VRaw>(vt + (size_t)((16 * nt + col) * kBlock + 4 * grp) * CT::bytes);
   };
 
-  float m = -INFINITY, l = 0.0f;
+  // Running maximum (base-2 logits) per head; it starts at a finite floor so that a block whose
+  // tokens are all masked gives probabilities exp2(-inf - m) = 0 rather than NaN.
+  float m = kNoMax, l = 0.0f;
   f4_t acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](const F &f, int tok0) {
+  // Block at token tok0; tokens at or past `lim` are masked (lim = tok0 masks the whole block, for
+  // a ring slot that holds no block of this partition).
+  auto compute = [&](const F &f, int tok0, int lim) {
     // ---- S^T = K Q^T: lane holds the scores of tokens tok0 + 4 grp + i for head col
     f4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (kFP8) {
@@ -248,18 +282,27 @@ void decode_mfma_kernel(DecodeArgs a) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      z[i] = t0 + i < end ? st[i] * kscale : -INFINITY;  // select: tail slots never leak
+      z[i] = t0 + i < lim ? st[i] * kscale : -INFINITY;  // select: tail slots never leak
       mx = fmaxf(mx, z[i]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);  // finite: every block has a token before `end`
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    // Lazy rescaling: the running maximum of a head moves only when a block's maximum exceeds it
+    // by more than kSlack (base 2), so probabilities stay below 2^kSlack and the accumulator is
+    // rescaled on a few blocks instead of every one.  The first block always moves it (m = -inf).
+    const bool grow = mx > m + kSlack;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
+      const float mn = grow ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first block, else <= 1
+      l *= alpha;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
+      m = mn;
+    }
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - mn);
-    l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    m = mn;
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - m);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
     uint2 phi, plo;
     phi.x = pack2<kBF>(p[0], p[1]);
     phi.y = pack2<kBF>(p[2], p[3]);
@@ -267,9 +310,9 @@ void decode_mfma_kernel(DecodeArgs a) {
     plo.y = pack2<kBF>(p[2] - unpack_lo<kBF>(phi.y), p[3] - unpack_hi<kBF>(phi.y));
 
     // ---- O^T += V^T P^T; V elements of tail tokens are zeroed (select), so NaN there cannot leak
-    const bool tail = tok0 + kBlock > end;  // wave-uniform
-    const uint32_t keep0 = (t0 + 0 < end ? 0xffffu : 0u) | (t0 + 1 < end ? 0xffff0000u : 0u);
-    const uint32_t keep1 = (t0 + 2 < end ? 0xffffu : 0u) | (t0 + 3 < end ? 0xffff0000u : 0u);
+    const bool tail = tok0 + kBlock > lim;  // wave-uniform
+    const uint32_t keep0 = (t0 + 0 < lim ? 0xffffu : 0u) | (t0 + 1 < lim ? 0xffff0000u : 0u);
+    const uint32_t keep1 = (t0 + 2 < lim ? 0xffffu : 0u) | (t0 + 3 < lim ? 0xffff0000u : 0u);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       uint2 vop;
@@ -279,8 +322,7 @@ void decode_mfma_kernel(DecodeArgs a) {
         vop.x &= keep0;
         vop.y &= keep1;
       }
-      f4_t c = acc[nt] * alpha;
-      c = mma_k16<kBF>(vop, phi, c);
+      const f4_t c = mma_k16<kBF>(vop, phi, acc[nt]);
       acc[nt] = mma_k16<kBF>(vop, plo, c);
     }
   };
@@ -288,9 +330,11 @@ void decode_mfma_kernel(DecodeArgs a) {
   // ---- the partition's blocks w, w + 4, ... through a ring of kBufs fragments: while one block
   // is computed, the loads of the next kBufs - 1 blocks of this wavefront are in flight.  Buffer
   // indices are compile-time constants (the inner loop is unrolled), so the ring needs no copies.
-  // Every ring slot is loaded on every round, with no branch around the loads, so each compute
-  // waits only for its own slot: a slot past the end of the range, or whose table entry lies
-  // outside the pool, reads tile (0, h) instead (a few L2-resident lines) and is not computed.
+  // Every ring slot is loaded and computed on every round, with no branch around either, so each
+  // compute waits only for its own slot and the accumulators stay in place: a slot past the end of
+  // the range, or whose table entry lies outside the pool, reads tile (0, h) instead (a few
+  // L2-resident lines) and is computed with all of its tokens masked, which leaves the state
+  // unchanged (its V elements are zeroed by selection, its probabilities are 0).
   const int jb0 = start / kBlock, jb1 = (end + kBlock - 1) / kBlock;
   F buf[kBufs];
   bool ok[kBufs];
@@ -305,7 +349,7 @@ void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int b = 0; b < kBufs; ++b) {
       const int j = jr + b * kWaves;
-      if (ok[b]) compute(buf[b], j * kBlock);
+      compute(buf[b], j * kBlock, ok[b] ? end : j * kBlock);  // branch-free: see the ring note
       const int jn = j + kBufs * kWaves;
       const int bid = jn < jb1 ? table[jn] : -1;
       ok[b] = (unsigned)bid < (unsigned)nb;
@@ -329,19 +373,17 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int hq0 = h * g;
   for (int x = tid; x < g * D; x += blockDim.x) {
     const int i = x / D, d = x % D;
-    float M = -INFINITY;
+    float M = kNoMax;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) M = fmaxf(M, m_s[v][i]);
     float lsum = 0.0f, o = 0.0f;
-    if (M != -INFINITY) {
 #pragma unroll
-      for (int v = 0; v < kWaves; ++v) {
-        const float c = __builtin_amdgcn_exp2f(m_s[v][i] - M);  // 0 for an idle wavefront
-        lsum += c * l_s[v][i];
-        o += c * o_s[v][d][i];
-      }
-      o = o / lsum * vscale;
+    for (int v = 0; v < kWaves; ++v) {
+      const float c = __builtin_amdgcn_exp2f(m_s[v][i] - M);  // an idle wavefront has l = 0
+      lsum += c * l_s[v][i];
+      o += c * o_s[v][d][i];
     }
+    o = lsum > 0.0f ? o / lsum * vscale : 0.0f;  // no position at all: zero
     if (nparts == 1) {
       out[((size_t)s * Hq + hq0 + i) * D + d] = from_f32<QT>(o);
     } else {
@@ -355,12 +397,113 @@ void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
+// Grid modes.  Direct: one workgroup per (partition, KV head, sequence) of the launch bounds, the
+// ones past a sequence's end returning at once.  Persistent: as many workgroups as fit on the
+// device at once, each taking items f = blockIdx.x, + gridDim.x, ... of the flat list of the
+// batch's real items, ordered (sequence, partition, KV head) with the KV head fastest; the list
+// is the prefix sum of the sequences' partition counts, computed by every workgroup in LDS (an
+// empty sequence counts one item, which writes its zero output).  Item sizes are all one
+// partition except each sequence's last, so the round-robin split stays balanced without the
+// idle workgroups of the direct grid.
+template <class CT, class QT, int D>
+__global__ __launch_bounds__(256)
+#if PA_DECODE_OCC
+__attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC, PA_DECODE_OCC)))
+#endif
+void decode_mfma_kernel(DecodeArgs a) {
+  __shared__ DecodeLds<D> lds;
+  if (!a.persistent) {
+    decode_item<CT, QT, D>(a, blockIdx.z, blockIdx.y, blockIdx.x, lds);
+    return;
+  }
+  __shared__ int prefix[kMaxScanSeqs + 1];
+  __shared__ int wave_tot[kWaves];
+  const int S = a.num_seqs, H = a.cache.num_kv_heads, PT = a.partition_size;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // thread t counts the items of sequences [t * per, (t + 1) * per)
+  const int per = (S + 255) / 256;
+  const int s0 = tid * per;
+  int mine = 0;
+  for (int i = 0; i < per; ++i) {
+    const int s = s0 + i;
+    if (s < S) {
+      int L = a.context_lens[s];
+      L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
+      mine += L > 0 ? (L + PT - 1) / PT : 1;
+    }
+  }
+  int incl = mine;  // inclusive scan over the wavefront
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wave_tot[wv] = incl;
+  __syncthreads();
+  int run = incl - mine;
+  for (int v = 0; v < wv; ++v) run += wave_tot[v];
+  for (int i = 0; i < per; ++i) {
+    const int s = s0 + i;
+    if (s < S) {
+      prefix[s] = run;
+      int L = a.context_lens[s];
+      L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
+      run += L > 0 ? (L + PT - 1) / PT : 1;
+    }
+  }
+  if (tid == 255) prefix[S] = run;  // thread 255 holds the grand total (its chunk ends at S or later)
+  __syncthreads();
+  const int total = prefix[S] * H;
+  for (int f = blockIdx.x; f < total; f += gridDim.x) {
+    const int pf = f / H, h = f - pf * H;
+    int lo = 0, hi = S - 1;  // largest s with prefix[s] <= pf
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (prefix[mid] <= pf) lo = mid;
+      else hi = mid - 1;
+    }
+    decode_item<CT, QT, D>(a, lo, h, pf - prefix[lo], lds);
+    __syncthreads();  // the next item reuses the LDS merge buffers
+  }
+}
+
+// Workgroups of one instantiation that fit on the device at once (occupancy x compute units),
+// looked up once per device.
+template <class CT, class QT, int D>
+int resident_groups() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = -1;
+  if (dev >= 0) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int occ = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_mfma_kernel<CT, QT, D>, 256, 0) !=
+          hipSuccess || occ < 1)
+    occ = 1;
+  if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                     hipSuccess || cus < 1)
+    cus = 1;
+  const int n = occ * cus;
+  if (dev >= 0) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <class CT, class QT, int D>
+hipError_t launch_dd(DecodeArgs a, hipStream_t s) {
+  const int64_t direct = (int64_t)a.num_partitions * a.cache.num_kv_heads * a.num_seqs;
+  a.persistent = a.num_seqs <= kMaxScanSeqs;
+  dim3 grid(a.num_partitions, a.cache.num_kv_heads, a.num_seqs);
+  if (a.persistent) grid = dim3((unsigned)std::min<int64_t>(direct, resident_groups<CT, QT, D>()));
+  decode_mfma_kernel<CT, QT, D><<<grid, dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
 template <class CT, class QT>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
-  dim3 grid(a.num_partitions, a.cache.num_kv_heads, a.num_seqs), block(256);
-  if (a.cache.head_dim == 64) decode_mfma_kernel<CT, QT, 64><<<grid, block, 0, s>>>(a);
-  else decode_mfma_kernel<CT, QT, 128><<<grid, block, 0, s>>>(a);
-  return hipGetLastError();
+  return a.cache.head_dim == 64 ? launch_dd<CT, QT, 64>(a, s) : launch_dd<CT, QT, 128>(a, s);
 }
 
 }  // namespace

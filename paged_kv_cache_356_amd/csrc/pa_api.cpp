@@ -211,6 +211,7 @@ pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int
   a.num_partitions = np;
   a.part_out = nullptr;
   a.part_ml = nullptr;
+  a.persistent = 0;
   if (np > 1) {
     const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)np;
     a.part_out = static_cast<float *>(workspace);

@@ -56,6 +56,7 @@ struct DecodeArgs {
   int32_t num_partitions;   // ceil(max_context_len / partition_size)
   float *part_out;          // NULL when num_partitions == 1
   float *part_ml;
+  int32_t persistent;       // grid mode of the matrix-core kernel (set by its launcher)
 };
 
 struct CopyArgs {

@@ -7,106 +7,92 @@
 // the attention kernel works at all": attention walks K and V one chunk at a time).
 // Sequences that fit one partition were finished by the decode kernel and are skipped here.
 //
-// One workgroup of 256 threads per (sequence, query head) row.  The row's partials are read as
-// float4 columns: thread t owns column t % C (C = D / 4) and partitions t / C, t / C + G, ...
-// (G = 256 / C), so every load of a chunk of 256 partitions is issued before any is used; the G
-// per-thread sums are then combined through LDS.
+// One wavefront per (sequence, query head) row, four rows per workgroup, no barriers.  Each lane
+// owns one float4 column of the partial outputs (C = D / 4 columns) and the partitions
+// lane / C, lane / C + G, ... (G = 64 / C) of a chunk of 64; the weights of the chunk's partitions
+// sit one per lane and are fetched with lane shuffles, the loads of a sub-chunk of 8 G partitions
+// are all issued before any is used, and the G column groups are combined with shuffles at the end.
 #include "pa_device.h"
 #include "pa_kernels.h"
 
 namespace pa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kChunk = 256;  // partitions whose weights are staged in LDS at a time
+constexpr int kRowsPerGroup = 4;
 
 template <class QT, int D>
-__global__ __launch_bounds__(kThreads) void partition_reduce_kernel(DecodeArgs a) {
-  constexpr int C = D / 4;            // float4 columns of a partial output
-  constexpr int G = kThreads / C;     // partitions handled side by side
-  constexpr int kPer = kChunk / G;    // partitions per thread and chunk
-  __shared__ float w_s[kChunk];
-  __shared__ float red_s[kThreads / 64];
-  __shared__ float4 acc_s[G][C];
-
-  const int row = blockIdx.x;  // s * Hq + hq
+__global__ __launch_bounds__(64 * kRowsPerGroup) void partition_reduce_kernel(DecodeArgs a) {
+  constexpr int C = D / 4;   // float4 columns of a partial output
+  constexpr int G = 64 / C;  // partitions handled side by side in a wavefront
+  constexpr int kPer = 8;    // float4 loads in flight per lane (a sub-chunk of G * kPer partitions)
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerGroup + (threadIdx.x >> 6);  // s * Hq + hq
+  if (row >= a.num_seqs * a.num_q_heads) return;
   const int s = row / a.num_q_heads;
   int Ls = a.context_lens[s];
   Ls = Ls < 0 ? 0 : (Ls > a.max_context_len ? a.max_context_len : Ls);
   const int PT = a.partition_size;
   const int np = (Ls + PT - 1) / PT;
-  if (np <= 1) return;
+  if (np <= 1) return;  // finished by the decode kernel
   const size_t row0 = (size_t)row * a.num_partitions;
   const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml) + row0;
   const float4 *po = reinterpret_cast<const float4 *>(a.part_out) + row0 * C;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
-  // M = max over partitions
-  float M = -INFINITY;
-  for (int p = tid; p < np; p += kThreads) M = fmaxf(M, ml[p].x);
+  // M = max over partitions (the first chunk's pair stays in registers)
+  const float2 first = lane < np ? ml[lane] : make_float2(-INFINITY, 0.0f);
+  float M = first.x;
+  for (int p = lane + 64; p < np; p += 64) M = fmaxf(M, ml[p].x);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if (lane == 0) red_s[wv] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
 
-  const int c = tid % C, grp = tid / C;
+  const int c = lane % C, grp = lane / C;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float wsum = 0.0f;
-  for (int base = 0; base < np; base += kChunk) {
-    const int n = min(kChunk, np - base);
-    __syncthreads();  // previous chunk's weights are no longer read
-    if (tid < n) {
-      const float2 v = ml[base + tid];
-      const float wp = v.x == -INFINITY ? 0.0f : v.y * __builtin_amdgcn_exp2f(v.x - M);
-      w_s[tid] = wp;
-      wsum += wp;
-    }
-    __syncthreads();
-    float4 x[kPer];
+  for (int base = 0; base < np; base += 64) {
+    const int n = min(64, np - base);
+    const float2 v = base == 0 ? first : (lane < n ? ml[base + lane] : make_float2(-INFINITY, 0.0f));
+    const float wl = v.x == -INFINITY ? 0.0f : v.y * __builtin_amdgcn_exp2f(v.x - M);
+    wsum += wl;
+    for (int sub = 0; sub < n; sub += G * kPer) {
+      float4 x[kPer];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int p = grp + k * G;
-      x[k] = p < n ? po[(size_t)(base + p) * C + c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
+      for (int k = 0; k < kPer; ++k) {
+        const int q = sub + grp + k * G;
+        x[k] = q < n ? po[(size_t)(base + q) * C + c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int p = grp + k * G;
-      const float wp = p < n ? w_s[p] : 0.0f;
-      acc.x += wp * x[k].x;
-      acc.y += wp * x[k].y;
-      acc.z += wp * x[k].z;
-      acc.w += wp * x[k].w;
+      for (int k = 0; k < kPer; ++k) {
+        const float wq = __shfl(wl, (sub + grp + k * G) & 63);  // 0 for q >= n
+        acc.x += wq * x[k].x;
+        acc.y += wq * x[k].y;
+        acc.z += wq * x[k].z;
+        acc.w += wq * x[k].w;
+      }
     }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o);
-  __syncthreads();
-  if (lane == 0) red_s[wv] = wsum;
-  acc_s[grp][c] = acc;
-  __syncthreads();
-  if (tid < C) {
-    const float tot = (red_s[0] + red_s[1]) + (red_s[2] + red_s[3]);
-    const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
-    float4 r = acc_s[0][tid];
 #pragma unroll
-    for (int k = 1; k < G; ++k) {
-      r.x += acc_s[k][tid].x;
-      r.y += acc_s[k][tid].y;
-      r.z += acc_s[k][tid].z;
-      r.w += acc_s[k][tid].w;
-    }
-    auto *out = static_cast<typename QT::raw *>(a.out) + (size_t)row * D + 4 * tid;
-    out[0] = from_f32<QT>(r.x * inv);
-    out[1] = from_f32<QT>(r.y * inv);
-    out[2] = from_f32<QT>(r.z * inv);
-    out[3] = from_f32<QT>(r.w * inv);
+  for (int o = C; o < 64; o <<= 1) {
+    acc.x += __shfl_xor(acc.x, o);
+    acc.y += __shfl_xor(acc.y, o);
+    acc.z += __shfl_xor(acc.z, o);
+    acc.w += __shfl_xor(acc.w, o);
+  }
+  if (lane < C) {
+    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    auto *out = static_cast<typename QT::raw *>(a.out) + (size_t)row * D + 4 * lane;
+    out[0] = from_f32<QT>(acc.x * inv);
+    out[1] = from_f32<QT>(acc.y * inv);
+    out[2] = from_f32<QT>(acc.z * inv);
+    out[3] = from_f32<QT>(acc.w * inv);
   }
 }
 
 template <class QT>
 hipError_t launch_q(const DecodeArgs &a, hipStream_t s) {
-  dim3 grid(a.num_seqs * a.num_q_heads), block(kThreads);
+  const int rows = a.num_seqs * a.num_q_heads;
+  dim3 grid((rows + kRowsPerGroup - 1) / kRowsPerGroup), block(64 * kRowsPerGroup);
   if (a.cache.head_dim == 64) partition_reduce_kernel<QT, 64><<<grid, block, 0, s>>>(a);
   else partition_reduce_kernel<QT, 128><<<grid, block, 0, s>>>(a);
   return hipGetLastError();

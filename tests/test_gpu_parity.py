@@ -213,6 +213,24 @@ def test_partition_sizes_agree(ps):
     _check_batch(b, ob, 0, TOL["f16"])
 
 
+def test_many_sequences_direct_grid():
+    """More sequences than the persistent grid's prefix scan covers: the matrix-core kernel falls
+    back to one workgroup per (partition, KV head, sequence)."""
+    g = np.random.default_rng(41)
+    S = 4100
+    lengths = g.integers(1, 48, size=S)
+    lengths[:3] = [1, 16, 47]
+    w = wl.WORKLOADS["c2"].replace(num_seqs=S, num_blocks=16384)
+    _say(f"direct grid, {S} sequences")
+    pad = _pad_block(w)
+    b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON, lengths=lengths,
+                    partition_size=16)
+    ob = OracleBatch(b, pad, pool_fill=POISON)
+    sel_s = np.r_[0:8, S - 8:S]
+    sel = (np.repeat(sel_s, w.num_q_heads), np.tile(np.arange(w.num_q_heads), len(sel_s)))
+    _check_batch(b, ob, 0, TOL["f16"], sel=sel)
+
+
 # --------------------------------------------------------------------------- invariances
 def test_permutation_of_physical_blocks_is_bitwise_invisible():
     _say("permutation invariance")
