@@ -34,7 +34,10 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "paged decode attention KV GB/s (% of HBM peak) + sequences/s per layer"
-DEFAULT_SETS = {"c1": 1, "c2": 16, "c3": 3, "c4": 4, "c5": 1}
+# independent batches rotated by the timing loop, so that successive steps read KV that no cache
+# holds (the 256 MB MALL included); the 28-layer step reads ~14.5 GB by itself
+DEFAULT_SETS = {"tiny_f32": 1, "f16_batch32": 16, "bf16_32k_batch8": 3,
+                "f16_shared_prefix_batch256": 4, "fp8_28layer_batch512": 1}
 
 
 def log(*a):
@@ -103,7 +106,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="f16_batch32", choices=list(DEFAULT_SETS))
     ap.add_argument("--sets", type=int, default=0, help="independent batches rotated (0 = default)")
     ap.add_argument("--valu", action="store_true", help="force the vector-ALU decode kernel")
     ap.add_argument("--partition", type=int, default=-1, help="partition size (-1 = workload's)")

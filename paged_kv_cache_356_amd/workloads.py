@@ -10,18 +10,18 @@ model's hidden size 3584 and 4 x 128 = 512 is the per-layer K (or V) width, "Pag
 Visualized" Parts 1-2; block size 16, "PagedAttention" (devoured.fyi), "PagedAttention in one
 picture"):
 
-  c1  tiny fp32: 4 sequences, lengths {5, 16, 17, 40}, 4 query / 2 KV heads, head_dim 64, 32 blocks.
-  c2  fp16: 32 sequences, lengths uniform in [128, 2048], 65,536-block pool.
-  c3  bf16: 8 sequences of 32,768 tokens (2,048 blocks each), split-K partitions of 512.
-  c4  fp16: 256 sequences sharing a 1,024-token prefix (64 blocks) plus private suffixes of
+  tiny_f32                    4 sequences, lengths {5, 16, 17, 40}, 4 query / 2 KV heads, head_dim 64, 32 blocks.
+  f16_batch32                 32 sequences, lengths uniform in [128, 2048], 65,536-block pool.
+  bf16_32k_batch8             8 sequences of 32,768 tokens (2,048 blocks each), split-K partitions of 512.
+  f16_shared_prefix_batch256  256 sequences sharing a 1,024-token prefix (64 blocks) plus private suffixes of
       round(lognormal(ln 300, 0.8)) tokens clipped to [1, 2048].
-  c5  fp8 E4M3 cache with fp16 queries, 28 layers, 512 sequences, lengths round(lognormal(ln 600,
+  fp8_28layer_batch512        fp8 E4M3 cache with fp16 queries, 28 layers, 512 sequences, lengths round(lognormal(ln 600,
       1.0)) clipped to [1, 32768], 436,000 blocks per layer (about 200 GB of KV over 28 layers).
 
 The request-length traces used by the serving benchmarks the pages quote are not available here;
 the uniform and log-normal length mixes stand in for them.
 
-Seeds: every workload uses seed 356000 + its index (c1 -> 356001 ...).  numpy's PCG64 draws the
+Seeds: every workload uses seed 356000 + its index (tiny_f32 -> 356001 ...).  numpy's PCG64 draws the
 metadata; torch's generator draws the values.
 """
 from __future__ import annotations
@@ -50,7 +50,7 @@ class Workload:
     q_dtype: str             # f32 / f16 / bf16
     num_layers: int = 1
     partition_size: int = 0  # 0 = library default
-    prefix_len: int = 0      # shared prefix tokens (c4)
+    prefix_len: int = 0      # shared prefix tokens
     description: str = ""
 
     @property
@@ -75,15 +75,15 @@ class Workload:
 
 
 WORKLOADS = {
-    "c1": Workload("c1", 1, 4, 4, 2, 64, 32, "f32", "f32",
+    "tiny_f32": Workload("tiny_f32", 1, 4, 4, 2, 64, 32, "f32", "f32",
                    description="tiny fp32 paged decode, lengths {5,16,17,40}"),
-    "c2": Workload("c2", 2, 32, 28, 4, 128, 65536, "f16", "f16",
+    "f16_batch32": Workload("f16_batch32", 2, 32, 28, 4, 128, 65536, "f16", "f16",
                    description="Qwen2.5-7B-shaped single-layer fp16 decode, batch 32, L~U[128,2048]"),
-    "c3": Workload("c3", 3, 8, 28, 4, 128, 65536, "bf16", "bf16", partition_size=512,
+    "bf16_32k_batch8": Workload("bf16_32k_batch8", 3, 8, 28, 4, 128, 65536, "bf16", "bf16", partition_size=512,
                    description="long-context bf16 decode, batch 8 x 32,768 tokens, partitions of 512"),
-    "c4": Workload("c4", 4, 256, 28, 4, 128, 65536, "f16", "f16", prefix_len=1024,
+    "f16_shared_prefix_batch256": Workload("f16_shared_prefix_batch256", 4, 256, 28, 4, 128, 65536, "f16", "f16", prefix_len=1024,
                    description="shared-prefix fp16 decode, batch 256, 1,024-token shared prefix"),
-    "c5": Workload("c5", 5, 512, 28, 4, 128, 436000, "fp8", "f16", num_layers=28,
+    "fp8_28layer_batch512": Workload("fp8_28layer_batch512", 5, 512, 28, 4, 128, 436000, "fp8", "f16", num_layers=28,
                    description="28-layer fp8-E4M3 KV decode step, batch 512, L~lognormal(600,1)"),
 }
 
@@ -95,15 +95,15 @@ def rng(w: Workload, stream: int = 0) -> np.random.Generator:
 def context_lengths(w: Workload) -> np.ndarray:
     """Context length of every sequence AFTER this step's token is appended (int32 [S])."""
     r = rng(w, 1)
-    if w.name == "c1":
+    if w.name == "tiny_f32":
         L = np.array([5, 16, 17, 40])
-    elif w.name == "c2":
+    elif w.name == "f16_batch32":
         L = r.integers(128, 2048, size=w.num_seqs, endpoint=True)
-    elif w.name == "c3":
+    elif w.name == "bf16_32k_batch8":
         L = np.full(w.num_seqs, 32768)
-    elif w.name == "c4":
+    elif w.name == "f16_shared_prefix_batch256":
         L = w.prefix_len + suffix_lengths(w)
-    elif w.name == "c5":
+    elif w.name == "fp8_28layer_batch512":
         L = np.clip(np.rint(r.lognormal(np.log(600.0), 1.0, size=w.num_seqs)), 1, 32768)
     else:
         raise KeyError(w.name)
@@ -111,7 +111,7 @@ def context_lengths(w: Workload) -> np.ndarray:
 
 
 def suffix_lengths(w: Workload) -> np.ndarray:
-    """c4: private suffix lengths (including this step's token), clipped to [1, 2048]."""
+    """Shared-prefix workload: private suffix lengths (including this step's token), clipped to [1, 2048]."""
     r = rng(w, 2)
     s = np.clip(np.rint(r.lognormal(np.log(300.0), 0.8, size=w.num_seqs)), 1, 2048)
     return np.asarray(s, np.int32)

@@ -154,8 +154,8 @@ def test_copy_blocks_bit_exact_over_layers(dtype):
 
 # --------------------------------------------------------------------------- attention, small
 def test_c1_tiny_fp32_matches_oracle():
-    w = wl.WORKLOADS["c1"]
-    _say("c1 tiny fp32")
+    w = wl.WORKLOADS["tiny_f32"]
+    _say("tiny fp32")
     pad = _pad_block(w)
     for ps in (0, 16, 32):
         b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON, partition_size=ps)
@@ -171,30 +171,30 @@ def test_c1_tiny_fp32_matches_oracle():
 
 SMALL = {
     # reduced versions of the four large workloads: same dtypes, heads, block size and length mix
-    "c2": dict(num_seqs=6, num_blocks=1024),
-    "c3": dict(num_seqs=2, num_blocks=1024),
-    "c4": dict(num_seqs=6, num_blocks=1024, prefix_len=64),
-    "c5": dict(num_seqs=6, num_blocks=2048, num_layers=2),
+    "f16_batch32": dict(num_seqs=6, num_blocks=1024),
+    "bf16_32k_batch8": dict(num_seqs=2, num_blocks=1024),
+    "f16_shared_prefix_batch256": dict(num_seqs=6, num_blocks=1024, prefix_len=64),
+    "fp8_28layer_batch512": dict(num_seqs=6, num_blocks=2048, num_layers=2),
 }
 SMALL_LENGTHS = {
-    "c2": [128, 700, 2048, 1, 17, 1500],
-    "c3": [2048, 1999],
-    "c4": [64 + 1, 64 + 16, 64 + 17, 64 + 300, 64 + 2, 64 + 511],
-    "c5": [1, 600, 2500, 33, 4096, 16],
+    "f16_batch32": [128, 700, 2048, 1, 17, 1500],
+    "bf16_32k_batch8": [2048, 1999],
+    "f16_shared_prefix_batch256": [64 + 1, 64 + 16, 64 + 17, 64 + 300, 64 + 2, 64 + 511],
+    "fp8_28layer_batch512": [1, 600, 2500, 33, 4096, 16],
 }
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["f16_batch32", "bf16_32k_batch8", "f16_shared_prefix_batch256", "fp8_28layer_batch512"])
 @pytest.mark.parametrize("flags", [api.PA_DECODE_DEFAULT, api.PA_DECODE_FORCE_VALU])
 def test_small_workloads_match_oracle(name, flags):
     w = wl.WORKLOADS[name].replace(**SMALL[name])
     _say(f"{name} reduced, flags {flags}")
     pad = _pad_block(w)
     b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON,
-                    lengths=SMALL_LENGTHS[name], partition_size=0 if name != "c3" else 512)
+                    lengths=SMALL_LENGTHS[name], partition_size=0 if name != "bf16_32k_batch8" else 512)
     ob = OracleBatch(b, pad, pool_fill=POISON)
     ob.metadata_matches(b)
-    if name == "c4":
+    if name == "f16_shared_prefix_batch256":
         assert b.sets[0].pairs.shape[0] > 0  # the step clones shared write targets
     for l in b.layers:
         _check_batch(b, ob, l, TOL[w.cache_dtype], flags=flags)
@@ -205,7 +205,7 @@ def test_small_workloads_match_oracle(name, flags):
 
 @pytest.mark.parametrize("ps", [16, 64, 512])
 def test_partition_sizes_agree(ps):
-    w = wl.WORKLOADS["c2"].replace(num_seqs=3, num_blocks=512)
+    w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=3, num_blocks=512)
     _say(f"partition size {ps}")
     pad = _pad_block(w)
     b = DecodeBatch(w, keep_values=True, pad_block=pad, lengths=[1000, 513, 16], partition_size=ps)
@@ -220,7 +220,7 @@ def test_many_sequences_direct_grid():
     S = 4100
     lengths = g.integers(1, 48, size=S)
     lengths[:3] = [1, 16, 47]
-    w = wl.WORKLOADS["c2"].replace(num_seqs=S, num_blocks=16384)
+    w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=S, num_blocks=16384)
     _say(f"direct grid, {S} sequences")
     pad = _pad_block(w)
     b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON, lengths=lengths,
@@ -234,7 +234,7 @@ def test_many_sequences_direct_grid():
 # --------------------------------------------------------------------------- invariances
 def test_permutation_of_physical_blocks_is_bitwise_invisible():
     _say("permutation invariance")
-    w = wl.WORKLOADS["c2"].replace(num_seqs=4, num_blocks=512)
+    w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=4, num_blocks=512)
     base = DecodeBatch(w, lengths=[300, 1024, 17, 900])
     base.run_step(0)
     torch.cuda.synchronize()
@@ -256,7 +256,7 @@ def test_permutation_of_physical_blocks_is_bitwise_invisible():
 
 def test_shared_prefix_equals_duplicated_prefix_bitwise():
     _say("shared vs duplicated prefix")
-    w = wl.WORKLOADS["c4"].replace(num_seqs=5, num_blocks=1024, prefix_len=64)
+    w = wl.WORKLOADS["f16_shared_prefix_batch256"].replace(num_seqs=5, num_blocks=1024, prefix_len=64)
     lengths = [64 + 5, 64 + 40, 64 + 17, 64 + 200, 64 + 1]
     b = DecodeBatch(w, lengths=lengths)
     b.run_step(0)
@@ -281,7 +281,7 @@ def test_shared_prefix_equals_duplicated_prefix_bitwise():
 
 def test_poison_outside_the_context_never_leaks():
     _say("NaN poison")
-    w = wl.WORKLOADS["c2"].replace(num_seqs=5, num_blocks=512)
+    w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=5, num_blocks=512)
     lengths = [17, 1, 1023, 64, 250]
     pad = _pad_block(w)
     clean = DecodeBatch(w, lengths=lengths, pad_block=0)
@@ -295,7 +295,7 @@ def test_poison_outside_the_context_never_leaks():
 
 def test_empty_context_and_out_of_range_blocks():
     _say("edge cases")
-    w = wl.WORKLOADS["c2"].replace(num_seqs=3, num_blocks=256)
+    w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=3, num_blocks=256)
     lengths = [40, 1, 100]
     pad = _pad_block(w)
     b = DecodeBatch(w, keep_values=True, lengths=lengths, pad_block=pad)
@@ -329,7 +329,7 @@ def test_empty_context_and_out_of_range_blocks():
 
 
 def test_rejections_do_not_launch():
-    w = wl.WORKLOADS["c1"]
+    w = wl.WORKLOADS["tiny_f32"]
     b = DecodeBatch(w)
     st = b.sets[0]
     with pytest.raises(api.PaError) as e:
@@ -343,7 +343,7 @@ def test_rejections_do_not_launch():
 
 
 # --------------------------------------------------------------------------- full sizes, sampled
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["f16_batch32", "bf16_32k_batch8", "f16_shared_prefix_batch256", "fp8_28layer_batch512"])
 def test_full_size_workloads_sampled(name):
     w = wl.WORKLOADS[name]
     layers = [0, w.num_layers - 1] if w.num_layers > 1 else [0]

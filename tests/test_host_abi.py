@@ -177,7 +177,7 @@ def test_block_manager_matches_model(seed):
 
 
 def test_block_manager_workload_recipe_matches_model():
-    w = wl.WORKLOADS["c4"].replace(num_seqs=12, num_blocks=2048, prefix_len=64)
+    w = wl.WORKLOADS["f16_shared_prefix_batch256"].replace(num_seqs=12, num_blocks=2048, prefix_len=64)
     L = 64 + wl.suffix_lengths(w.replace(num_seqs=256))[:12]
     fo = wl.free_order(w)
     prod, model = api.BlockManager(w.num_blocks, 16, fo), BlockManagerModel(w.num_blocks, 16, fo)
