@@ -112,6 +112,8 @@ def main() -> int:
     ap.add_argument("--partition", type=int, default=-1, help="partition size (-1 = workload's)")
     ap.add_argument("--num-blocks", type=int, default=0,
                     help="physical blocks per layer pool (0 = the workload's own)")
+    ap.add_argument("--no-prefix", action="store_true",
+                    help="shared-prefix workload: use the plain decode instead of the shared-prefix one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -156,6 +158,7 @@ def main() -> int:
                         keep_values=not args.no_cpu_baseline,
                         partition_size=None if args.partition < 0 else args.partition,
                         keep_layers=[0])
+    batch.use_prefix = batch.use_prefix and not args.no_prefix
     torch.cuda.synchronize()
     log(f"[bench] {w.name}: built {sets} set(s), {len(batch.layers)} layer(s) in "
         f"{time.perf_counter() - t_build:.1f} s; lengths {wl.lengths_summary(batch.lengths)}")
@@ -176,9 +179,7 @@ def main() -> int:
             api.pa_reshape_and_cache(cache, st.new_k[l], st.new_v[l], st.d_slots, stream)
             if timed:
                 ev0[k * len(batch.layers) + li].record(stream)
-            api.pa_decode_attention(st.out[l], st.q[l], cache, st.d_tables, st.d_ctx,
-                                    batch.max_context_len, w.scale, batch.partition_size,
-                                    batch.workspace, flags, stream)
+            batch.decode(r, l, flags=flags, stream=stream)
             if timed:
                 ev1[k * len(batch.layers) + li].record(stream)
 
@@ -225,6 +226,7 @@ def main() -> int:
             "partition_size": batch.partition_size or api.pa_decode_auto_partition(
                 w.num_seqs, w.num_kv_heads, batch.max_context_len),
             "kernel": "valu" if args.valu else "default",
+            "shared_prefix_decode": bool(batch.use_prefix),
             "sets_rotated": sets,
             "kv_bytes_per_step_logical": kv_logical * layers,
             "kv_bytes_per_layer_unique": batch.kv_bytes_per_layer(unique=True) if unique else
@@ -241,7 +243,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": None,
-            "kernel": "pa_decode_attention (split-K decode + partition reduce)",
+            "kernel": ("pa_decode_attention_shared_prefix" if batch.use_prefix else
+                       "pa_decode_attention") + " (split-K decode + partition reduce)",
             "bytes_per_call": alg,
             "bytes_kind": "unique physical KV slots" if unique else "logical KV",
         },

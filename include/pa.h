@@ -179,6 +179,45 @@ pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int
                               size_t workspace_bytes, uint32_t flags, void *stream);
 
 /*
+ * pa_decode_attention_shared_prefix — pa_decode_attention for a batch whose sequences all begin
+ * with the same prefix_len positions stored in the same physical blocks: several requests share a
+ * prompt prefix and their block tables point at one copy of it ([Visualized] Part 3, shared
+ * prefix blocks with a reference count; [Digest] "Copy-on-write: when two requests share a
+ * prefix" and "Misconceptions", on system prompts shared by many users).  The result is the same
+ * attention as pa_decode_attention over each sequence's whole context (within floating-point
+ * rounding: the summation order differs); only the reading changes: each block of the prefix is
+ * read once for all sequences, with up to 16 (sequence, query head) rows per matrix-core product,
+ * instead of once per sequence.
+ *
+ *   prefix_table  device int32 [prefix_len / 16]: the prefix's physical block ids.  The first
+ *                 prefix_len / 16 entries of every block_tables row must hold the same ids (the
+ *                 caller's guarantee; they are what the sharing means).
+ *   prefix_len    shared positions, a non-negative multiple of 16 (0: plain decode).  A sequence
+ *                 whose context length is below prefix_len attends only to its first
+ *                 context_lens[s] positions, as in pa_decode_attention.
+ *   workspace     at least pa_decode_shared_prefix_workspace_bytes() bytes.
+ * All other arguments and rules are those of pa_decode_attention.  Batches the prefix path does not
+ * cover (more than 4096 sequences, the vector-ALU dtype pairs, PA_DECODE_FORCE_VALU) are computed
+ * by the plain decode, with the same result.
+ */
+pa_status pa_decode_attention_shared_prefix(void *out, const void *query, int32_t q_dtype,
+                                            int64_t q_stride, const pa_cache *cache,
+                                            const int32_t *block_tables,
+                                            int32_t max_blocks_per_seq,
+                                            const int32_t *context_lens, int32_t num_seqs,
+                                            int32_t num_q_heads, int32_t max_context_len,
+                                            float scale, const int32_t *prefix_table,
+                                            int32_t prefix_len, int32_t partition_size,
+                                            void *workspace, size_t workspace_bytes,
+                                            uint32_t flags, void *stream);
+
+/* Device workspace bytes pa_decode_attention_shared_prefix needs for these sizes. */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t max_context_len, int32_t prefix_len,
+                                               int32_t partition_size);
+
+/*
  * pa_copy_blocks — the clone step of copy-on-write.  When a sequence must write into a block
  * whose reference count is above 1, the engine clones that block, drops the original's count by
  * one and points the writer's table at the clone ([Digest] "Copy-on-write: when two requests share

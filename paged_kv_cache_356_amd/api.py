@@ -30,7 +30,8 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPO
 # Every symbol include/pa.h declares.
 EXPORTS = [
     "pa_pool_bytes", "pa_reshape_and_cache", "pa_decode_auto_partition",
-    "pa_decode_workspace_bytes", "pa_decode_attention", "pa_copy_blocks", "pa_check_copy_pairs",
+    "pa_decode_workspace_bytes", "pa_decode_attention", "pa_decode_attention_shared_prefix",
+    "pa_decode_shared_prefix_workspace_bytes", "pa_copy_blocks", "pa_check_copy_pairs",
     "pa_status_string", "pa_last_error", "pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq",
     "pa_bm_fork", "pa_bm_append", "pa_bm_append_batch", "pa_bm_free_seq", "pa_bm_refcount",
     "pa_bm_num_free", "pa_bm_seq_len", "pa_bm_block_table", "pa_bm_export",
@@ -71,6 +72,11 @@ def lib() -> ctypes.CDLL:
             "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
             "pa_decode_attention": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _i32, _vp, _i32, _i32,
                                            _i32, _f32, _i32, _vp, _sz, _u32, _vp]),
+            "pa_decode_attention_shared_prefix": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _i32, _vp,
+                                                          _i32, _i32, _i32, _f32, _vp, _i32, _i32,
+                                                          _vp, _sz, _u32, _vp]),
+            "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32,
+                                                              _i32]),
             "pa_copy_blocks": (_i32, [_cp, _i32, _vp, _i32, _vp]),
             "pa_check_copy_pairs": (_i32, [_vp, _i32, _i32]),
             "pa_status_string": (ctypes.c_char_p, [_i32]),
@@ -199,6 +205,38 @@ def pa_decode_attention(out: torch.Tensor, query: torch.Tensor, cache: KVCache,
                                      _ptr(context_lens), S, Hq, int(max_context_len), float(scale),
                                      int(partition_size), _ptr(workspace), ws_bytes, int(flags),
                                      _stream(stream)))
+
+
+def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            max_context_len, prefix_len,
+                                            partition_size=0) -> int:
+    return lib().pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                         head_dim, max_context_len, prefix_len,
+                                                         partition_size)
+
+
+def pa_decode_attention_shared_prefix(out: torch.Tensor, query: torch.Tensor, cache: KVCache,
+                                      block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                      max_context_len: int, scale: float,
+                                      prefix_table: torch.Tensor, prefix_len: int,
+                                      partition_size: int = 0,
+                                      workspace: torch.Tensor | None = None,
+                                      flags: int = PA_DECODE_DEFAULT, stream=None) -> None:
+    """pa_decode_attention for a batch sharing its first prefix_len positions (the blocks in
+    prefix_table, device int32 [prefix_len / 16])."""
+    S, Hq, D = query.shape
+    assert out.shape == query.shape and out.dtype == query.dtype and out.is_contiguous()
+    assert query[0].is_contiguous() if S else True
+    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous()
+    assert context_lens.dtype == torch.int32 and context_lens.is_contiguous()
+    assert prefix_table.dtype == torch.int32 and prefix_table.is_contiguous()
+    c = cache.struct()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_attention_shared_prefix(
+        _ptr(out), _ptr(query), TORCH_CODES[query.dtype], query.stride(0) if S else 0,
+        ctypes.byref(c), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, Hq,
+        int(max_context_len), float(scale), _ptr(prefix_table), int(prefix_len),
+        int(partition_size), _ptr(workspace), ws_bytes, int(flags), _stream(stream)))
 
 
 def pa_copy_blocks(caches: list[KVCache], block_pairs: torch.Tensor, stream=None) -> None:

@@ -59,7 +59,7 @@ constexpr int kBufs = PA_DECODE_BUFS;  // blocks per wavefront in the load ring
 #define PA_DECODE_NT 1
 #endif
 #ifndef PA_DECODE_OCC
-#define PA_DECODE_OCC 0
+#define PA_DECODE_OCC 3  // at least this many wavefronts per SIMD (caps registers at 168)
 #endif
 
 // K/V tiles are read once per decode step: optionally as non-temporal loads.
@@ -172,97 +172,71 @@ struct Frag {
   VRaw v[kNT];
 };
 
+
+// ---------------------------------------------------------------------------------------------
+// Per-wavefront pieces.  Lane l = 16 * grp + col: column col of the products is one query row.
+
 template <int D>
-struct DecodeLds {
-  float o[kWaves][D][17];  // each wavefront's unnormalised output, [head-dim][head] (+1 pad)
-  float m[kWaves][16];
-  float l[kWaves][16];
+struct RowState {
+  uint4 qop[D / 32];  // Q^T operand of this lane's query row
+  float m, l;         // running maximum (base-2 logits) and running sum of this lane's column
+  f4_t acc[D / 16];   // O^T accumulator: head-dim rows 16 nt + 4 grp + i of this lane's column
 };
 
-// One work item: partition `part` of sequence s for KV head h, computed by the whole workgroup.
-template <class CT, class QT, int D>
-__device__ __forceinline__ void decode_item(const DecodeArgs &a, int s_in, int h_in, int part_in,
-                                            DecodeLds<D> &lds) {
-  // The item is the same for the whole workgroup: keep its coordinates (and so the block-table
-  // row and the tile addresses) in scalar registers, which makes the table reads scalar loads.
-  const int s = __builtin_amdgcn_readfirstlane(s_in);
-  const int h = __builtin_amdgcn_readfirstlane(h_in);
-  const int part = __builtin_amdgcn_readfirstlane(part_in);
+// Q^T operand: lane l holds query row (rs, rhq), 8 dims per product kk, zeros for a padding
+// column.  The dims follow the K operand: f16/bf16 tiles give lane group grp dims 8 grp + 32 kk;
+// fp8 tiles give 16-byte vectors of 16 dims, split in two products, so 16 grp + 64 (kk/2) +
+// 8 (kk%2).
+template <class CT, int D>
+__device__ __forceinline__ void load_query(const DecodeArgs &a, int rs, int rhq, bool rvalid,
+                                           RowState<D> &st) {
+  constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
+  const int grp = (threadIdx.x & 63) >> 4;
+  const auto *q =
+      reinterpret_cast<const uint16_t *>(a.q) + (size_t)rs * a.q_stride + (size_t)rhq * D;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const int d0 = kFP8 ? 16 * grp + 64 * (kk >> 1) + 8 * (kk & 1) : 8 * grp + 32 * kk;
+    st.qop[kk] = rvalid ? *reinterpret_cast<const uint4 *>(q + d0) : make_uint4(0, 0, 0, 0);
+  }
+  st.m = kNoMax;  // a finite floor: a fully masked block gives exp2(-inf - m) = 0, not NaN
+  st.l = 0.0f;
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) st.acc[nt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+template <class CT, int D>
+__device__ __forceinline__ void load_block(const DecodeArgs &a, int bid, int h, Frag<CT, D> &f) {
+  using F = Frag<CT, D>;
+  constexpr int kTileBytes = kBlock * D * CT::bytes;
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  const size_t tile = ((size_t)bid * a.cache.num_kv_heads + h) * kTileBytes;
+  const char *kt = static_cast<const char *>(a.cache.k_pool) + tile;
+  const char *vt = static_cast<const char *>(a.cache.v_pool) + tile;
+#pragma unroll
+  for (int i = 0; i < F::kKLoads; ++i)
+    f.k[i] = load_kv<uint4>(kt + (size_t)(lane + 64 * i) * 16);
+#pragma unroll
+  for (int nt = 0; nt < F::kNT; ++nt)
+    f.v[nt] = load_kv<typename F::VRaw>(vt + (size_t)((16 * nt + col) * kBlock + 4 * grp) * CT::bytes);
+}
+
+// One 16-token block at token tok0 into the state.  Scores of positions at or past `zlim` (per
+// lane) are masked; V elements of positions at or past `vlim` (wave-uniform) are zeroed.  zlim =
+// vlim = tok0 masks the whole block, which leaves the state unchanged.
+template <class CT, int D>
+__device__ __forceinline__ void block_step(const Frag<CT, D> &f, float kscale, int tok0, int zlim,
+                                           int vlim, RowState<D> &rs_) {
   constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
   constexpr bool kBF = std::is_same<CT, bf16_t>::value;  // fp8 and f16 caches compute in f16
-  constexpr int KK = D / 32;                              // QK^T products per block
+  constexpr int KK = D / 32;
   using F = Frag<CT, D>;
   constexpr int NT = F::kNT;
-  constexpr int kTileBytes = kBlock * D * CT::bytes;
-  auto &o_s = lds.o;
-  auto &m_s = lds.m;
-  auto &l_s = lds.l;
-
-  const int H = a.cache.num_kv_heads, Hq = a.num_q_heads, g = Hq / H;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, grp = lane >> 4;
-  int Ls = a.context_lens[s];
-  Ls = Ls < 0 ? 0 : (Ls > a.max_context_len ? a.max_context_len : Ls);
-  const int PT = a.partition_size;
-  const int start = part * PT;
-  auto *out = static_cast<typename QT::raw *>(a.out);
-  if (start >= Ls) {
-    if (part == 0) {  // empty context: output is zero
-      for (int x = tid; x < g * D; x += blockDim.x)
-        out[((size_t)s * Hq + h * g) * D + x] = from_f32<QT>(0.0f);
-    }
-    return;
-  }
-  const int end = min(Ls, start + PT);
-  const int nparts = (Ls + PT - 1) / PT;
-
-  // Q^T operand: lane l holds head (h*g + col) (zero when col >= g), 8 dims per product kk.  The
-  // dims follow the K operand: f16/bf16 tiles give lane group r dims 8r + 32kk; fp8 tiles give
-  // 16-byte vectors of 16 dims, split in two products, so dims 16r + 64(kk/2) + 8(kk%2).
-  uint4 qop[KK];
-  {
-    const auto *q = reinterpret_cast<const uint16_t *>(a.q) + (size_t)s * a.q_stride +
-                    (size_t)(h * g + col) * D;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int d0 = kFP8 ? 16 * grp + 64 * (kk >> 1) + 8 * (kk & 1) : 8 * grp + 32 * kk;
-      qop[kk] = col < g ? *reinterpret_cast<const uint4 *>(q + d0) : make_uint4(0, 0, 0, 0);
-    }
-  }
-
-  float kscale = a.scale * kLog2e, vscale = 1.0f;
-  if constexpr (kFP8) {
-    kscale *= a.cache.k_scale[h] * kFp8Unscale;
-    vscale = a.cache.v_scale[h] * kFp8Unscale;
-  }
-  const char *kpool = static_cast<const char *>(a.cache.k_pool);
-  const char *vpool = static_cast<const char *>(a.cache.v_pool);
-  const int32_t *table = a.block_tables + (size_t)s * a.max_blocks_per_seq;
-  const int nb = a.cache.num_blocks;
-
-  auto load = [&](int bid, F &f) {
-    const size_t tile = ((size_t)bid * H + h) * kTileBytes;
-    const char *kt = kpool + tile;
-    const char *vt = vpool + tile;
-#pragma unroll
-    for (int i = 0; i < F::kKLoads; ++i)
-      f.k[i] = load_kv<uint4>(kt + (size_t)(lane + 64 * i) * 16);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      f.v[nt] = load_kv<typename F::VRaw>(vt + (size_t)((16 * nt + col) * kBlock + 4 * grp) * CT::bytes);
-  };
-
-  // Running maximum (base-2 logits) per head; it starts at a finite floor so that a block whose
-  // tokens are all masked gives probabilities exp2(-inf - m) = 0 rather than NaN.
-  float m = kNoMax, l = 0.0f;
-  f4_t acc[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  // Block at token tok0; tokens at or past `lim` are masked (lim = tok0 masks the whole block, for
-  // a ring slot that holds no block of this partition).
-  auto compute = [&](const F &f, int tok0, int lim) {
+  const int grp = (threadIdx.x & 63) >> 4;
+  const auto &qop = rs_.qop;
+  float &m = rs_.m;
+  float &l = rs_.l;
+  auto &acc = rs_.acc;
     // ---- S^T = K Q^T: lane holds the scores of tokens tok0 + 4 grp + i for head col
     f4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (kFP8) {
@@ -282,7 +256,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, int s_in, int h
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      z[i] = t0 + i < lim ? st[i] * kscale : -INFINITY;  // select: tail slots never leak
+      z[i] = t0 + i < zlim ? st[i] * kscale : -INFINITY;  // select: tail slots never leak
       mx = fmaxf(mx, z[i]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -310,9 +284,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, int s_in, int h
     plo.y = pack2<kBF>(p[2] - unpack_lo<kBF>(phi.y), p[3] - unpack_hi<kBF>(phi.y));
 
     // ---- O^T += V^T P^T; V elements of tail tokens are zeroed (select), so NaN there cannot leak
-    const bool tail = tok0 + kBlock > lim;  // wave-uniform
-    const uint32_t keep0 = (t0 + 0 < lim ? 0xffffu : 0u) | (t0 + 1 < lim ? 0xffff0000u : 0u);
-    const uint32_t keep1 = (t0 + 2 < lim ? 0xffffu : 0u) | (t0 + 3 < lim ? 0xffff0000u : 0u);
+    const bool tail = tok0 + kBlock > vlim;  // wave-uniform
+    const uint32_t keep0 = (t0 + 0 < vlim ? 0xffffu : 0u) | (t0 + 1 < vlim ? 0xffff0000u : 0u);
+    const uint32_t keep1 = (t0 + 2 < vlim ? 0xffffu : 0u) | (t0 + 3 < vlim ? 0xffff0000u : 0u);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       uint2 vop;
@@ -325,145 +299,332 @@ __device__ __forceinline__ void decode_item(const DecodeArgs &a, int s_in, int h
       const f4_t c = mma_k16<kBF>(vop, phi, acc[nt]);
       acc[nt] = mma_k16<kBF>(vop, plo, c);
     }
-  };
+}
 
-  // ---- the partition's blocks w, w + 4, ... through a ring of kBufs fragments: while one block
-  // is computed, the loads of the next kBufs - 1 blocks of this wavefront are in flight.  Buffer
-  // indices are compile-time constants (the inner loop is unrolled), so the ring needs no copies.
-  // Every ring slot is loaded and computed on every round, with no branch around either, so each
-  // compute waits only for its own slot and the accumulators stay in place: a slot past the end of
-  // the range, or whose table entry lies outside the pool, reads tile (0, h) instead (a few
-  // L2-resident lines) and is computed with all of its tokens masked, which leaves the state
-  // unchanged (its V elements are zeroed by selection, its probabilities are 0).
-  const int jb0 = start / kBlock, jb1 = (end + kBlock - 1) / kBlock;
-  F buf[kBufs];
-  bool ok[kBufs];
-#pragma unroll
-  for (int b = 0; b < kBufs; ++b) {
-    const int j = jb0 + w + b * kWaves;
-    const int bid = j < jb1 ? table[j] : -1;
-    ok[b] = (unsigned)bid < (unsigned)nb;  // an entry outside the pool is never dereferenced
-    load(ok[b] ? bid : 0, buf[b]);
-  }
-  for (int jr = jb0 + w; jr < jb1; jr += kBufs * kWaves) {
+// The ring: blocks j = jfirst, jfirst + jstride, ... < jb1 of table row `table`, KV head h, through
+// kBufs fragments.  While one block is computed, the loads of the next kBufs - 1 are in flight.
+// Buffer indices are compile-time constants (the inner loop is unrolled), so the ring needs no
+// copies.  Every slot is loaded and computed on every round, with no branch around either, so each
+// compute waits only for its own slot and the accumulators stay in place: a slot past the end of
+// the range, or whose table entry lies outside the pool, reads tile (0, h) instead (a few
+// L2-resident lines) and is computed fully masked.
+// The wavefront's table entries are fetched before its ring starts, one per lane, and read back with
+// v_readlane: a table read inside the ring would be a vector load whose result feeds the next
+// address, and waiting for it would drain every load in flight.  A wavefront with more than 64
+// blocks runs one ring per 64 of them.
+template <class CT, int D>
+__device__ __forceinline__ void stream_blocks(const DecodeArgs &a, const int32_t *table, int h,
+                                              int jfirst, int jstride, int jb1, int zlim, int vend,
+                                              float kscale, RowState<D> &st) {
+  using F = Frag<CT, D>;
+  const int nb = a.cache.num_blocks;
+  const int lane = threadIdx.x & 63;
+  const int nk = jfirst < jb1 ? (jb1 - jfirst + jstride - 1) / jstride : 0;  // this wave's blocks
+  for (int k0 = 0; k0 < nk; k0 += 64) {
+    const int kn = min(64, nk - k0);
+    const int jc = jfirst + k0 * jstride;  // the chunk's first block
+    const int tbl = lane < kn ? table[jc + lane * jstride] : -1;
+    // block id of the chunk's k-th block (-1 past the chunk); k is wave-uniform
+    auto entry = [&](int k) { return k < kn ? __builtin_amdgcn_readlane(tbl, k < 64 ? k : 63) : -1; };
+    F buf[kBufs];
+    bool ok[kBufs];
 #pragma unroll
     for (int b = 0; b < kBufs; ++b) {
-      const int j = jr + b * kWaves;
-      compute(buf[b], j * kBlock, ok[b] ? end : j * kBlock);  // branch-free: see the ring note
-      const int jn = j + kBufs * kWaves;
-      const int bid = jn < jb1 ? table[jn] : -1;
-      ok[b] = (unsigned)bid < (unsigned)nb;
-      load(ok[b] ? bid : 0, buf[b]);
+      const int bid = entry(b);
+      ok[b] = (unsigned)bid < (unsigned)nb;  // an entry outside the pool is never dereferenced
+      load_block<CT, D>(a, ok[b] ? bid : 0, h, buf[b]);
     }
-  }
-
-  // ---- merge the four wavefronts through LDS
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (grp == 0) {
-    m_s[w][col] = m;
-    l_s[w][col] = l;
-  }
+    for (int kr = 0; kr < kn; kr += kBufs) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o_s[w][16 * nt + 4 * grp + i][col] = acc[nt][i];
-  __syncthreads();
-
-  const int hq0 = h * g;
-  for (int x = tid; x < g * D; x += blockDim.x) {
-    const int i = x / D, d = x % D;
-    float M = kNoMax;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, m_s[v][i]);
-    float lsum = 0.0f, o = 0.0f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const float c = __builtin_amdgcn_exp2f(m_s[v][i] - M);  // an idle wavefront has l = 0
-      lsum += c * l_s[v][i];
-      o += c * o_s[v][d][i];
-    }
-    o = lsum > 0.0f ? o / lsum * vscale : 0.0f;  // no position at all: zero
-    if (nparts == 1) {
-      out[((size_t)s * Hq + hq0 + i) * D + d] = from_f32<QT>(o);
-    } else {
-      const size_t row = ((size_t)s * Hq + hq0 + i) * a.num_partitions + part;
-      a.part_out[row * D + d] = o;
-      if (d == 0) {
-        a.part_ml[row * 2] = M;
-        a.part_ml[row * 2 + 1] = lsum;
+      for (int b = 0; b < kBufs; ++b) {
+        const int t0 = (jc + (kr + b) * jstride) * kBlock;
+        block_step<CT, D>(buf[b], kscale, t0, ok[b] ? zlim : t0, ok[b] ? vend : t0, st);
+        const int bid = entry(kr + b + kBufs);
+        ok[b] = (unsigned)bid < (unsigned)nb;
+        load_block<CT, D>(a, ok[b] ? bid : 0, h, buf[b]);
       }
     }
   }
 }
 
-// Grid modes.  Direct: one workgroup per (partition, KV head, sequence) of the launch bounds, the
-// ones past a sequence's end returning at once.  Persistent: as many workgroups as fit on the
-// device at once, each taking items f = blockIdx.x, + gridDim.x, ... of the flat list of the
-// batch's real items, ordered (sequence, partition, KV head) with the KV head fastest; the list
-// is the prefix sum of the sequences' partition counts, computed by every workgroup in LDS (an
-// empty sequence counts one item, which writes its zero output).  Item sizes are all one
-// partition except each sequence's last, so the round-robin split stays balanced without the
-// idle workgroups of the direct grid.
+template <class CT>
+__device__ __forceinline__ void head_scales(const DecodeArgs &a, int h, float &kscale,
+                                            float &vscale) {
+  kscale = a.scale * kLog2e;
+  vscale = 1.0f;
+  if constexpr (std::is_same<CT, fp8_t>::value) {
+    kscale *= a.cache.k_scale[h] * kFp8Unscale;
+    vscale = a.cache.v_scale[h] * kFp8Unscale;
+  }
+}
+
+__device__ __forceinline__ int clamp_len(const DecodeArgs &a, int s) {
+  int L = a.context_lens[s];
+  return L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Wavefront item: one wavefront computes KV head h over positions [jb0 * 16, end) of one
+// block-table row, against up to 16 query rows (the 16 columns of the products), and writes the
+// rows' results itself (no merge with other wavefronts, no barrier):
+//  - sequence item (s >= 0): the rows are the g query heads of sequence s, on s's table row.
+//  - prefix tile (s < 0): the rows are flat rows row0 .. row0 + 15 of the batch (flat row r is
+//    query head h*g + r % g of sequence r / g), on the shared prefix's table; each row masks the
+//    positions at or past its own context length.
+// The result goes to workspace partition `slot`, or straight to the output when slot < 0.
+// Wavefronts of one workgroup run their items independently, so one wavefront's item prologue
+// (query, table fetch, first loads) and epilogue overlap the other wavefronts' block streams.
+template <class CT, class QT, int D>
+__device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int row0_in, int h_in,
+                                          int jb0_in, int jb1_in, int end_in, int slot_in) {
+  // The item is the same for the whole wavefront: keep its fields (and so the tile addresses) in
+  // scalar registers.
+  const int s = __builtin_amdgcn_readfirstlane(s_in);
+  const int row0 = __builtin_amdgcn_readfirstlane(row0_in);
+  const int h = __builtin_amdgcn_readfirstlane(h_in);
+  const int jb0 = __builtin_amdgcn_readfirstlane(jb0_in);
+  const int jb1 = __builtin_amdgcn_readfirstlane(jb1_in);
+  const int end = __builtin_amdgcn_readfirstlane(end_in);
+  const int slot = __builtin_amdgcn_readfirstlane(slot_in);
+  constexpr int NT = D / 16;
+  const int H = a.cache.num_kv_heads, Hq = a.num_q_heads, g = Hq / H;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const bool tile = s < 0;
+  const int nrows = tile ? min(16, a.num_seqs * g - row0) : g;
+  const bool rvalid = col < nrows;
+  const int rs = tile ? (rvalid ? (row0 + col) / g : 0) : s;
+  const int rhq = h * g + (rvalid ? (tile ? (row0 + col) % g : col) : 0);
+  const int lim = tile && rvalid ? min(end, clamp_len(a, rs)) : end;
+  const int32_t *table =
+      tile ? a.prefix_table : a.block_tables + (size_t)s * a.max_blocks_per_seq;
+
+  RowState<D> st;
+  load_query<CT, D>(a, rs, rhq, rvalid, st);
+  float kscale, vscale;
+  head_scales<CT>(a, h, kscale, vscale);
+  stream_blocks<CT, D>(a, table, h, jb0, 1, jb1, lim, end, kscale, st);
+
+  // the row's sum over the four lane groups; m is already uniform over them
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!rvalid) return;
+  const size_t orow = (size_t)rs * Hq + rhq;
+  const float inv = l > 0.0f ? vscale / l : 0.0f;  // no position at all: zero
+  if (slot < 0) {
+    auto *out = static_cast<typename QT::raw *>(a.out) + orow * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      typename QT::raw v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = from_f32<QT>(st.acc[nt][i] * inv);
+      *reinterpret_cast<uint2 *>(out + 16 * nt + 4 * grp) = *reinterpret_cast<const uint2 *>(v);
+    }
+  } else {
+    const size_t row = orow * a.num_partitions + slot;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float4 v;
+      v.x = st.acc[nt][0] * inv;
+      v.y = st.acc[nt][1] * inv;
+      v.z = st.acc[nt][2] * inv;
+      v.w = st.acc[nt][3] * inv;
+      *reinterpret_cast<float4 *>(a.part_out + row * D + 16 * nt + 4 * grp) = v;
+    }
+    if (grp == 0) {
+      a.part_ml[row * 2] = st.m;
+      a.part_ml[row * 2 + 1] = l;
+    }
+  }
+}
+
+// LDS of a workgroup prefix tile: each wavefront's unnormalised output [head-dim][row] (+1 pad)
+// and its (running max, running sum) per row.
+template <int D>
+struct TileLds {
+  float o[kWaves][D][17];
+  float m[kWaves][16];
+  float l[kWaves][16];
+};
+
+// Prefix tile, computed by the whole workgroup: flat rows row0 .. row0 + 15 of the batch (flat row
+// r is query head h*g + r % g of sequence r / g) against the shared prefix's blocks [jb0, jb1);
+// wavefront w takes blocks jb0 + w, + 4, ..., so the workgroup's four block streams run side by
+// side, and the four partial states are merged through LDS into workspace partition `slot`.
+// Each row masks the positions at or past its own context length.
+template <class CT, class QT, int D>
+__device__ __forceinline__ void prefix_tile(const DecodeArgs &a, int row0_in, int h_in, int jb0_in,
+                                            int jb1_in, int end_in, int slot_in,
+                                            TileLds<D> &lds) {
+  const int row0 = __builtin_amdgcn_readfirstlane(row0_in);
+  const int h = __builtin_amdgcn_readfirstlane(h_in);
+  const int jb0 = __builtin_amdgcn_readfirstlane(jb0_in);
+  const int jb1 = __builtin_amdgcn_readfirstlane(jb1_in);
+  const int end = __builtin_amdgcn_readfirstlane(end_in);
+  const int slot = __builtin_amdgcn_readfirstlane(slot_in);
+  constexpr int NT = D / 16;
+  const int H = a.cache.num_kv_heads, Hq = a.num_q_heads, g = Hq / H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int nrows = min(16, a.num_seqs * g - row0);
+  const bool rvalid = col < nrows;
+  const int rs = rvalid ? (row0 + col) / g : 0;
+  const int rhq = h * g + (rvalid ? (row0 + col) % g : 0);
+  const int lim = rvalid ? min(end, clamp_len(a, rs)) : end;
+
+  RowState<D> st;
+  load_query<CT, D>(a, rs, rhq, rvalid, st);
+  float kscale, vscale;
+  head_scales<CT>(a, h, kscale, vscale);
+  stream_blocks<CT, D>(a, a.prefix_table, h, jb0 + w, kWaves, jb1, lim, end, kscale, st);
+
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (grp == 0) {
+    lds.m[w][col] = st.m;
+    lds.l[w][col] = l;
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds.o[w][16 * nt + 4 * grp + i][col] = st.acc[nt][i];
+  __syncthreads();
+  for (int x = tid; x < nrows * D; x += blockDim.x) {
+    const int i = x / D, d = x % D;
+    float M = kNoMax;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, lds.m[v][i]);
+    float lsum = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const float c = __builtin_amdgcn_exp2f(lds.m[v][i] - M);  // an idle wavefront has l = 0
+      lsum += c * lds.l[v][i];
+      o += c * lds.o[v][d][i];
+    }
+    const int r = row0 + i;
+    const size_t row = ((size_t)(r / g) * Hq + h * g + r % g) * a.num_partitions + slot;
+    a.part_out[row * D + d] = lsum > 0.0f ? o / lsum * vscale : 0.0f;
+    if (d == 0) {
+      a.part_ml[row * 2] = M;
+      a.part_ml[row * 2 + 1] = lsum;
+    }
+  }
+  __syncthreads();  // the LDS buffers are free for the next tile
+}
+
+// Items of sequence s: plain decode, partitions of its context (an empty context counts one item,
+// which writes its zeros); shared-prefix decode, partitions of the positions after the prefix
+// (possibly none).
+__device__ __forceinline__ int seq_items(const DecodeArgs &a, int L) {
+  if (a.prefix_len > 0) return row_partitions(a, L) - a.prefix_chunks;
+  return L > 0 ? row_partitions(a, L) : 1;
+}
+
+template <class CT, class QT, int D>
+__device__ __forceinline__ void run_sequence_item(const DecodeArgs &a, int s, int part, int h) {
+  const int PT = a.partition_size;
+  const int L = clamp_len(a, s);
+  if (a.prefix_len > 0) {
+    const int start = a.prefix_len + part * PT;
+    const int end = min(L, start + PT);
+    wave_item<CT, QT, D>(a, s, 0, h, start / kBlock, (end + kBlock - 1) / kBlock, end,
+                         a.prefix_chunks + part);
+  } else {
+    const int start = part * PT;
+    const int end = min(L, start + PT);
+    const int n = L > 0 ? (L + PT - 1) / PT : 1;
+    wave_item<CT, QT, D>(a, s, 0, h, start / kBlock,
+                         L > start ? (end + kBlock - 1) / kBlock : start / kBlock, end,
+                         n > 1 ? part : -1);
+  }
+}
+
+// Grid modes.  Direct (plain decode only, more than kMaxScanSeqs sequences): wavefront
+// 4 blockIdx.x + w takes flat item (partition, KV head, sequence) of the launch bounds, the ones
+// past a sequence's end returning at once.  Persistent: as many workgroups as fit on the device
+// at once; with a shared prefix they first share out its tiles (a chunk being up to kPrefixChunk
+// positions), then every wavefront takes its share of the sequence items, located through the
+// prefix sum of the sequences' item counts that every workgroup computes in LDS.
 template <class CT, class QT, int D>
 __global__ __launch_bounds__(256)
 #if PA_DECODE_OCC
-__attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC, PA_DECODE_OCC)))
+__attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
 #endif
 void decode_mfma_kernel(DecodeArgs a) {
-  __shared__ DecodeLds<D> lds;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = a.num_seqs, H = a.cache.num_kv_heads, g = a.num_q_heads / H;
+  const int PT = a.partition_size;
   if (!a.persistent) {
-    decode_item<CT, QT, D>(a, blockIdx.z, blockIdx.y, blockIdx.x, lds);
+    const int64_t f = (int64_t)blockIdx.x * kWaves + w;
+    const int part = (int)(f % a.num_partitions);
+    const int h = (int)((f / a.num_partitions) % H);
+    const int64_t s = f / ((int64_t)a.num_partitions * H);
+    if (s >= S) return;
+    const int L = clamp_len(a, (int)s);
+    const int n = L > 0 ? (L + PT - 1) / PT : 1;
+    if (part < n) run_sequence_item<CT, QT, D>(a, (int)s, part, h);
     return;
   }
-  __shared__ int prefix[kMaxScanSeqs + 1];
+  __shared__ int prefix[kMaxScanSeqs + 1];  // items of the sequences before s
   __shared__ int wave_tot[kWaves];
-  const int S = a.num_seqs, H = a.cache.num_kv_heads, PT = a.partition_size;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   // thread t counts the items of sequences [t * per, (t + 1) * per)
   const int per = (S + 255) / 256;
   const int s0 = tid * per;
   int mine = 0;
-  for (int i = 0; i < per; ++i) {
-    const int s = s0 + i;
-    if (s < S) {
-      int L = a.context_lens[s];
-      L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
-      mine += L > 0 ? (L + PT - 1) / PT : 1;
-    }
-  }
+  for (int i = 0; i < per; ++i)
+    if (s0 + i < S) mine += seq_items(a, clamp_len(a, s0 + i));
   int incl = mine;  // inclusive scan over the wavefront
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(incl, o);
     if (lane >= o) incl += y;
   }
-  if (lane == 63) wave_tot[wv] = incl;
+  if (lane == 63) wave_tot[w] = incl;
   __syncthreads();
   int run = incl - mine;
-  for (int v = 0; v < wv; ++v) run += wave_tot[v];
+  for (int v = 0; v < w; ++v) run += wave_tot[v];
   for (int i = 0; i < per; ++i) {
     const int s = s0 + i;
     if (s < S) {
       prefix[s] = run;
-      int L = a.context_lens[s];
-      L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
-      run += L > 0 ? (L + PT - 1) / PT : 1;
+      run += seq_items(a, clamp_len(a, s));
     }
   }
   if (tid == 255) prefix[S] = run;  // thread 255 holds the grand total (its chunk ends at S or later)
   __syncthreads();
-  const int total = prefix[S] * H;
-  for (int f = blockIdx.x; f < total; f += gridDim.x) {
+
+  // Shared prefix first: workgroup b computes prefix tiles b, b + G, ... (all four wavefronts
+  // together), list order (chunk, 16-row tile, KV head) with the KV head fastest.
+  const int n_tiles = a.prefix_len > 0 ? (S * g + 15) / 16 : 0;
+  const int n_pre = n_tiles * a.prefix_chunks * H;
+  if (n_pre > 0) {
+    __shared__ TileLds<D> tlds;
+    for (int i = blockIdx.x; i < n_pre; i += gridDim.x) {
+      const int h = i % H, t = (i / H) % n_tiles, c = i / (H * n_tiles);
+      const int start = c * kPrefixChunk;
+      const int end = min(a.prefix_len, start + kPrefixChunk);
+      prefix_tile<CT, QT, D>(a, t * 16, h, start / kBlock, end / kBlock, end, c, tlds);
+    }
+  }
+  // Then the sequences' items, one per wavefront: wavefront gw of GW takes items gw, gw + GW, ...
+  // of the list (sequence, partition, KV head) with the KV head fastest, so the wavefronts running
+  // at the same time cover the H tiles (b, 0..H-1) of the same blocks, next to each other in the
+  // pool.
+  const int total = __builtin_amdgcn_readfirstlane(prefix[S]) * H;
+  const int GW = gridDim.x * kWaves;
+  for (int f = blockIdx.x * kWaves + w; f < total; f += GW) {
     const int pf = f / H, h = f - pf * H;
-    int lo = 0, hi = S - 1;  // largest s with prefix[s] <= pf
+    int lo = 0, hi = S - 1;  // largest s with prefix[s] <= pf (LDS values, made uniform)
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (prefix[mid] <= pf) lo = mid;
+      if (__builtin_amdgcn_readfirstlane(prefix[mid]) <= pf) lo = mid;
       else hi = mid - 1;
     }
-    decode_item<CT, QT, D>(a, lo, h, pf - prefix[lo], lds);
-    __syncthreads();  // the next item reuses the LDS merge buffers
+    run_sequence_item<CT, QT, D>(a, lo, pf - __builtin_amdgcn_readfirstlane(prefix[lo]), h);
   }
 }
 
@@ -493,9 +654,10 @@ int resident_groups() {
 
 template <class CT, class QT, int D>
 hipError_t launch_dd(DecodeArgs a, hipStream_t s) {
-  const int64_t direct = (int64_t)a.num_partitions * a.cache.num_kv_heads * a.num_seqs;
+  const int64_t items = (int64_t)a.num_partitions * a.cache.num_kv_heads * a.num_seqs;
+  const int64_t direct = (items + kWaves - 1) / kWaves;  // one wavefront per item
   a.persistent = a.num_seqs <= kMaxScanSeqs;
-  dim3 grid(a.num_partitions, a.cache.num_kv_heads, a.num_seqs);
+  dim3 grid((unsigned)direct);
   if (a.persistent) grid = dim3((unsigned)std::min<int64_t>(direct, resident_groups<CT, QT, D>()));
   decode_mfma_kernel<CT, QT, D><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
@@ -508,13 +670,19 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
 
 }  // namespace
 
+bool decode_mfma_supports_prefix(const DecodeArgs &a) {
+  // the prefix tiles exist only in the persistent grid
+  return decode_mfma_supports(a) && a.num_seqs <= kMaxScanSeqs;
+}
+
 bool decode_mfma_supports(const DecodeArgs &a) {
   const int cdt = a.cache.dtype, qdt = a.q_dtype;
   const bool types = (cdt == kF16 && qdt == kF16) || (cdt == kBF16 && qdt == kBF16) ||
                      (cdt == kFP8 && qdt == kF16);
   const int g = a.num_q_heads / a.cache.num_kv_heads;
-  // the Q^T operand is read as 16-byte vectors of 8 elements
-  const bool q_aligned = (reinterpret_cast<uintptr_t>(a.q) & 15u) == 0 && a.q_stride % 8 == 0;
+  // the Q^T operand is read as 16-byte vectors of 8 elements; outputs are stored 4 at a time
+  const bool q_aligned = (reinterpret_cast<uintptr_t>(a.q) & 15u) == 0 && a.q_stride % 8 == 0 &&
+                         (reinterpret_cast<uintptr_t>(a.out) & 7u) == 0;
   // an empty pool has no tile for the ring's idle slots to read
   return types && g >= 1 && g <= 16 && (a.cache.head_dim == 64 || a.cache.head_dim == 128) &&
          q_aligned && a.cache.num_blocks > 0;

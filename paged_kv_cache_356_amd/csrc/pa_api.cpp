@@ -79,6 +79,27 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_co
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Partition slots per row for these sizes (plain decode: prefix_len = 0).
+int64_t decode_slots(int32_t max_len, int32_t pt, int32_t prefix_len) {
+  if (max_len <= 0) return 1;
+  if (prefix_len <= 0) return ceil_div(max_len, pt);
+  return ceil_div(prefix_len, pa::kPrefixChunk) +
+         (max_len > prefix_len ? ceil_div(max_len - prefix_len, pt) : 0);
+}
+
+// Workspace: with more than one partition slot per row, or a shared prefix, the partials
+// [S][Hq][slots][D] and their (m, l) [S][Hq][slots][2], fp32; none otherwise.
+size_t partials_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int64_t slots) {
+  const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)slots;
+  return align256(rows * head_dim * sizeof(float)) + align256(rows * 2 * sizeof(float));
+}
+
+size_t ws_bytes_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int64_t slots,
+                    bool partials) {
+  return partials ? partials_bytes(num_seqs, num_q_heads, head_dim, slots) : 0;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -137,29 +158,36 @@ int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  if (max_context_len <= 0) return 0;
   const int32_t pt = resolve_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
   if (pt <= 0) return 0;
   const int64_t np = ceil_div(max_context_len, pt);
-  if (np <= 1) return 0;
-  const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)np;
-  return align256(rows * head_dim * sizeof(float)) + align256(rows * 2 * sizeof(float));
+  return ws_bytes_for(num_seqs, num_q_heads, head_dim, np, np > 1);
 }
 
-pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int64_t q_stride,
-                              const pa_cache *cache, const int32_t *block_tables,
-                              int32_t max_blocks_per_seq, const int32_t *context_lens,
-                              int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
-                              float scale, int32_t partition_size, void *workspace,
-                              size_t workspace_bytes, uint32_t flags, void *stream) {
-  const char *who = "pa_decode_attention";
+}  // extern "C"
+
+namespace {
+
+// Validation and dispatch shared by the plain and the shared-prefix decode.
+pa_status decode_common(const char *who, void *out, const void *query, int32_t q_dtype,
+                        int64_t q_stride, const pa_cache *cache, const int32_t *block_tables,
+                        int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                        int32_t num_q_heads, int32_t max_context_len, float scale,
+                        const int32_t *prefix_table, int32_t prefix_len, int32_t partition_size,
+                        void *workspace, size_t workspace_bytes, uint32_t flags, void *stream) {
   pa_status st = check_cache(cache, who);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_seqs > 65535)
     return fail(PA_ERR_SHAPE, "%s: num_seqs %d outside 0..65535", who, num_seqs);
+  if (prefix_len < 0 || prefix_len % PA_BLOCK_SIZE != 0)
+    return fail(PA_ERR_SHAPE, "%s: prefix_len %d is not a non-negative multiple of 16", who,
+                prefix_len);
   if (num_seqs == 0) return ok();
   if (!out || !query || !block_tables || !context_lens)
     return fail(PA_ERR_NULL, "%s: NULL out/query/block_tables/context_lens", who);
+  if (prefix_len > 0 && !prefix_table) return fail(PA_ERR_NULL, "%s: NULL prefix_table", who);
   const int H = cache->num_kv_heads, D = cache->head_dim;
   if (num_q_heads < 1 || num_q_heads % H != 0)
     return fail(PA_ERR_SHAPE, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", who,
@@ -185,15 +213,6 @@ pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int
 
   const int64_t cap = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
   const int32_t max_len = (int32_t)(max_context_len < cap ? max_context_len : cap);
-  const int32_t pt = resolve_partition(num_seqs, H, max_len, partition_size);
-  const int32_t np = max_len > 0 ? ceil_div(max_len, pt) : 1;
-  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, H, D, max_len, pt);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
-                need);
-  if (need > 0 && !aligned16(workspace))
-    return fail(PA_ERR_SHAPE, "%s: workspace must be 16-byte aligned", who);
-
   pa::DecodeArgs a;
   a.out = out;
   a.q = query;
@@ -207,22 +226,100 @@ pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int
   a.num_q_heads = num_q_heads;
   a.max_context_len = max_len;
   a.scale = scale;
-  a.partition_size = pt;
-  a.num_partitions = np;
+  a.persistent = 0;
+  a.prefix_table = nullptr;
+  a.prefix_len = 0;
+  a.prefix_chunks = 0;
+  a.partition_size = 0;
+  a.num_partitions = 1;
   a.part_out = nullptr;
   a.part_ml = nullptr;
-  a.persistent = 0;
-  if (np > 1) {
-    const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)np;
-    a.part_out = static_cast<float *>(workspace);
-    a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                          align256(rows * D * sizeof(float)));
+  const bool force_valu = (flags & PA_DECODE_FORCE_VALU) != 0;
+  // The prefix's tiles need the matrix-core kernel; elsewhere the plain decode gives the same result.
+  bool use_prefix = prefix_len > 0;
+  if (use_prefix) {
+    pa::DecodeArgs t = a;
+    t.prefix_len = prefix_len;
+    use_prefix = !force_valu && pa::decode_mfma_supports_prefix(t);
+  }
+  const int32_t pt = resolve_partition(num_seqs, H, use_prefix ? max_len - prefix_len : max_len,
+                                       partition_size);
+  const int64_t slots = decode_slots(max_len, pt, use_prefix ? prefix_len : 0);
+  const bool partials = use_prefix || slots > 1;
+  const size_t need = ws_bytes_for(num_seqs, num_q_heads, D, slots, partials);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
+                need);
+  if (need > 0 && !aligned16(workspace))
+    return fail(PA_ERR_SHAPE, "%s: workspace must be 16-byte aligned", who);
+  a.partition_size = pt;
+  a.num_partitions = (int32_t)slots;
+  if (use_prefix) {
+    a.prefix_table = prefix_table;
+    a.prefix_len = prefix_len;
+    a.prefix_chunks = ceil_div(prefix_len, pa::kPrefixChunk);
+  }
+  if (partials) {
+    char *ws = static_cast<char *>(workspace);
+    const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)slots;
+    a.part_out = reinterpret_cast<float *>(ws);
+    a.part_ml = reinterpret_cast<float *>(ws + align256(rows * D * sizeof(float)));
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool use_mfma = !(flags & PA_DECODE_FORCE_VALU) && pa::decode_mfma_supports(a);
+  const bool use_mfma = use_prefix || (!force_valu && pa::decode_mfma_supports(a));
   hipError_t e = use_mfma ? pa::launch_decode_mfma(a, s) : pa::launch_decode_valu(a, s);
   if (e == hipSuccess) e = pa::launch_partition_reduce(a, s);
   return launch_status(e, who);
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int64_t q_stride,
+                              const pa_cache *cache, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                              float scale, int32_t partition_size, void *workspace,
+                              size_t workspace_bytes, uint32_t flags, void *stream) {
+  return decode_common("pa_decode_attention", out, query, q_dtype, q_stride, cache, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, num_q_heads, max_context_len,
+                       scale, nullptr, 0, partition_size, workspace, workspace_bytes, flags,
+                       stream);
+}
+
+pa_status pa_decode_attention_shared_prefix(void *out, const void *query, int32_t q_dtype,
+                                            int64_t q_stride, const pa_cache *cache,
+                                            const int32_t *block_tables,
+                                            int32_t max_blocks_per_seq,
+                                            const int32_t *context_lens, int32_t num_seqs,
+                                            int32_t num_q_heads, int32_t max_context_len,
+                                            float scale, const int32_t *prefix_table,
+                                            int32_t prefix_len, int32_t partition_size,
+                                            void *workspace, size_t workspace_bytes,
+                                            uint32_t flags, void *stream) {
+  return decode_common("pa_decode_attention_shared_prefix", out, query, q_dtype, q_stride, cache,
+                       block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                       max_context_len, scale, prefix_table, prefix_len, partition_size,
+                       workspace, workspace_bytes, flags, stream);
+}
+
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t max_context_len, int32_t prefix_len,
+                                               int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || prefix_len < 0) return 0;
+  if (prefix_len == 0)
+    return pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                     max_context_len, partition_size);
+  const int32_t ml = max_context_len > 0 ? max_context_len : 0;
+  // enough for the prefix path and for the plain decode it falls back to
+  const int32_t pt = resolve_partition(num_seqs, num_kv_heads, ml - prefix_len, partition_size);
+  const size_t with_prefix = ws_bytes_for(num_seqs, num_q_heads, head_dim,
+                                          decode_slots(ml, pt, prefix_len), true);
+  const size_t plain = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                 ml, partition_size);
+  return with_prefix > plain ? with_prefix : plain;
 }
 
 pa_status pa_check_copy_pairs(const int32_t *pairs, int32_t num_pairs, int32_t num_blocks) {

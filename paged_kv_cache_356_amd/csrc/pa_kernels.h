@@ -10,6 +10,9 @@ namespace pa {
 
 enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };
 
+// Shared-prefix decode: prefix positions per prefix work item (and per workspace partition slot).
+constexpr int32_t kPrefixChunk = 512;
+
 inline int dtype_bytes(int dt) {
   return dt == kF32 ? 4 : (dt == kF16 || dt == kBF16) ? 2 : dt == kFP8 ? 1 : 0;
 }
@@ -57,7 +60,21 @@ struct DecodeArgs {
   float *part_out;          // NULL when num_partitions == 1
   float *part_ml;
   int32_t persistent;       // grid mode of the matrix-core kernel (set by its launcher)
+  // Shared-prefix decode (0 / NULL for the plain decode): every sequence's first prefix_len
+  // positions live in the blocks prefix_table[0 .. prefix_len / 16).  Workspace partition slots
+  // 0 .. prefix_chunks - 1 of every row hold the prefix's chunks, the suffix partitions follow.
+  const int32_t *prefix_table;
+  int32_t prefix_len;       // multiple of 16
+  int32_t prefix_chunks;    // ceil(prefix_len / kPrefixChunk)
 };
+
+// Workspace partition slots of a row whose context length is L (see DecodeArgs).
+inline __host__ __device__ int32_t row_partitions(const DecodeArgs &a, int32_t L) {
+  const int32_t PT = a.partition_size;
+  if (a.prefix_len > 0)
+    return a.prefix_chunks + (L > a.prefix_len ? (L - a.prefix_len + PT - 1) / PT : 0);
+  return (L + PT - 1) / PT;
+}
 
 struct CopyArgs {
   static constexpr int kMaxLayers = 32;
@@ -75,6 +92,7 @@ hipError_t launch_copy_blocks(const CopyArgs &a, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 bool decode_mfma_supports(const DecodeArgs &a);
+bool decode_mfma_supports_prefix(const DecodeArgs &a);
 hipError_t launch_partition_reduce(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace pa

@@ -5,7 +5,9 @@
 //   M = max_p m_p,  w_p = l_p * 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p,
 // the same online-softmax merge the partitions used inside ("PagedAttention" (devoured.fyi), "Why
 // the attention kernel works at all": attention walks K and V one chunk at a time).
-// Sequences that fit one partition were finished by the decode kernel and are skipped here.
+// Sequences that fit one partition of the plain decode were finished by the decode kernel and are
+// skipped here; with a shared prefix every row is merged (its prefix chunks and its suffix
+// partitions).
 //
 // One wavefront per (sequence, query head) row, four rows per workgroup, no barriers.  Each lane
 // owns one float4 column of the partial outputs (C = D / 4 columns) and the partitions
@@ -31,9 +33,8 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void partition_reduce_kernel(De
   const int s = row / a.num_q_heads;
   int Ls = a.context_lens[s];
   Ls = Ls < 0 ? 0 : (Ls > a.max_context_len ? a.max_context_len : Ls);
-  const int PT = a.partition_size;
-  const int np = (Ls + PT - 1) / PT;
-  if (np <= 1) return;  // finished by the decode kernel
+  const int np = row_partitions(a, Ls);
+  if (np <= 1 && a.prefix_len == 0) return;  // finished by the decode kernel
   const size_t row0 = (size_t)row * a.num_partitions;
   const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml) + row0;
   const float4 *po = reinterpret_cast<const float4 *>(a.part_out) + row0 * C;
@@ -101,7 +102,7 @@ hipError_t launch_q(const DecodeArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_partition_reduce(const DecodeArgs &a, hipStream_t s) {
-  if (a.num_partitions <= 1) return hipSuccess;
+  if (a.num_partitions <= 1 && a.prefix_len == 0) return hipSuccess;
   switch (a.q_dtype) {
     case kF32: return launch_q<f32_t>(a, s);
     case kF16: return launch_q<f16_t>(a, s);

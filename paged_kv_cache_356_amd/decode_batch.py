@@ -118,9 +118,24 @@ class DecodeBatch:
                     # set 0's history rows, kept for checks on the host
                     st.hist_k[l], st.hist_v[l] = hk, hv
                 del hk, hv
+        # the shared prefix's blocks: the first prefix_len / 16 entries of every table (all equal)
+        self.prefix_len = w.prefix_len
+        self.prefix_tables = []
+        if self.prefix_len:
+            nb = self.prefix_len // api.PA_BLOCK_SIZE
+            for st in self.sets:
+                first = st.tables[:, :nb]
+                assert (first == first[0]).all(), "the batch's tables do not share the prefix blocks"
+                self.prefix_tables.append(torch.from_numpy(first[0].copy()).to(device))
         ws = api.pa_decode_workspace_bytes(S, w.num_q_heads, H, D, self.max_context_len,
                                            self.partition_size)
+        if self.prefix_len:
+            ws = max(ws, api.pa_decode_shared_prefix_workspace_bytes(
+                S, w.num_q_heads, H, D, self.max_context_len, self.prefix_len,
+                self.partition_size))
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
+        # use the shared-prefix decode where the workload has a prefix (run_step / run_layer)
+        self.use_prefix = self.prefix_len > 0
 
     # ------------------------------------------------------------------ the step
     def run_step(self, set_index: int = 0, flags: int = api.PA_DECODE_DEFAULT, stream=None):
@@ -138,9 +153,23 @@ class DecodeBatch:
             api.pa_copy_blocks([cache], st.d_pairs, stream)
         if reshape:
             api.pa_reshape_and_cache(cache, st.new_k[layer], st.new_v[layer], st.d_slots, stream)
-        api.pa_decode_attention(st.out[layer], st.q[layer], cache, st.d_tables, st.d_ctx,
-                                self.max_context_len, self.w.scale, self.partition_size,
-                                self.workspace, flags, stream)
+        self.decode(set_index, layer, flags=flags, stream=stream)
+
+    def decode(self, set_index: int, layer: int, flags: int = api.PA_DECODE_DEFAULT, stream=None,
+               out: torch.Tensor | None = None):
+        """The step's attention call for one layer (shared-prefix decode when use_prefix)."""
+        st = self.sets[set_index]
+        cache = self.caches[layer]
+        out = st.out[layer] if out is None else out
+        if self.use_prefix:
+            api.pa_decode_attention_shared_prefix(
+                out, st.q[layer], cache, st.d_tables, st.d_ctx, self.max_context_len,
+                self.w.scale, self.prefix_tables[set_index], self.prefix_len,
+                self.partition_size, self.workspace, flags, stream)
+        else:
+            api.pa_decode_attention(out, st.q[layer], cache, st.d_tables, st.d_ctx,
+                                    self.max_context_len, self.w.scale, self.partition_size,
+                                    self.workspace, flags, stream)
 
     # ------------------------------------------------------------------ accounting
     def kv_bytes_per_layer(self, unique: bool = False) -> int:

@@ -77,6 +77,41 @@ def test_decode_validation(kw, status):
     assert _decode(_cache(), **kw) == status
 
 
+def _decode_prefix(cache, prefix_table=1024, prefix_len=64, **kw):
+    a = dict(out=64, query=128, q_dtype=api.PA_F16, q_stride=0, tables=256, max_blocks=8, ctx=512,
+             S=2, Hq=28, max_ctx=128, scale=0.1, ps=0, ws=None, ws_bytes=0, flags=0)
+    a.update(kw)
+    return api.lib().pa_decode_attention_shared_prefix(
+        a["out"], a["query"], a["q_dtype"], a["q_stride"], ctypes.byref(cache), a["tables"],
+        a["max_blocks"], a["ctx"], a["S"], a["Hq"], a["max_ctx"], a["scale"], prefix_table,
+        prefix_len, a["ps"], a["ws"], a["ws_bytes"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(prefix_len=24), -2), (dict(prefix_len=-16), -2), (dict(prefix_table=None), -1),
+    (dict(Hq=30), -2), (dict(ps=24), -2), (dict(out=None), -1),
+    (dict(ws=None, ws_bytes=0), -4),  # the prefix partials always need a workspace
+])
+def test_shared_prefix_decode_validation(kw, status):
+    assert _decode_prefix(_cache(), **kw) == status
+    assert api.lib().pa_last_error()
+
+
+def test_shared_prefix_workspace_sizing():
+    ws = api.pa_decode_shared_prefix_workspace_bytes
+    plain = api.pa_decode_workspace_bytes
+    # no prefix: the plain decode's workspace
+    assert ws(8, 28, 4, 128, 32768, 0, 512) == plain(8, 28, 4, 128, 32768, 512)
+    # 256 sequences, 1,024-position prefix, contexts up to 3,072, partitions of 512:
+    # 2 prefix chunks + 4 suffix partitions per row
+    rows = 256 * 28 * 6
+    need = ws(256, 28, 4, 128, 3072, 1024, 512)
+    assert need >= rows * 128 * 4 + rows * 2 * 4
+    assert need >= plain(256, 28, 4, 128, 3072, 512)
+    # even a context that fits one partition has a prefix partial to merge
+    assert ws(4, 28, 4, 128, 64, 64, 512) > 0
+
+
 def test_zero_sequences_is_a_no_op():
     assert _decode(_cache(), S=0, out=None, query=None) == 0
 
