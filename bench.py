@@ -15,7 +15,10 @@ Prints ONE JSON line:
 
 Timing loops rotate between `--sets` independent batches of the workload placed in the same pool
 (distinct blocks and values), so each step reads KV that the 256 MB MALL and the L2s do not already
-hold, as the successive layers of a model would.
+hold, as the successive layers of a model would.  Each set's step is captured once as a HIP graph
+and replayed (--eager launches every call from Python instead), so the timed loop measures the GPU
+rather than the host's per-call launch overhead; the decode-call duration comes from a captured run
+of back-to-back decode calls between two HIP events.
 """
 from __future__ import annotations
 
@@ -109,6 +112,8 @@ def main() -> int:
     ap.add_argument("--workload", default="f16_batch32", choices=list(DEFAULT_SETS))
     ap.add_argument("--sets", type=int, default=0, help="independent batches rotated (0 = default)")
     ap.add_argument("--valu", action="store_true", help="force the vector-ALU decode kernel")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every call from Python instead of replaying captured HIP graphs")
     ap.add_argument("--partition", type=int, default=-1, help="partition size (-1 = workload's)")
     ap.add_argument("--num-blocks", type=int, default=0,
                     help="physical blocks per layer pool (0 = the workload's own)")
@@ -163,39 +168,72 @@ def main() -> int:
     log(f"[bench] {w.name}: built {sets} set(s), {len(batch.layers)} layer(s) in "
         f"{time.perf_counter() - t_build:.1f} s; lengths {wl.lengths_summary(batch.lengths)}")
 
-    stream = torch.cuda.current_stream()
     caches = [batch.caches[l] for l in batch.layers]
-    n_dec = args.steps * len(batch.layers)
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_dec)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_dec)]
+    layers = batch.layers
 
-    def step(k: int, timed: bool):
-        r = k % sets
+    # Every library call enqueues on torch's current stream: the default stream when run eagerly,
+    # the capture stream while a graph is being captured.
+    def step(r: int):
+        """One step of set r: the copy-on-write clone, then per layer the new token's K/V write and
+        the decode attention."""
         st = batch.sets[r]
         if st.pairs.shape[0]:
-            api.pa_copy_blocks(caches, st.d_pairs, stream)
-        for li, l in enumerate(batch.layers):
-            cache = batch.caches[l]
-            api.pa_reshape_and_cache(cache, st.new_k[l], st.new_v[l], st.d_slots, stream)
-            if timed:
-                ev0[k * len(batch.layers) + li].record(stream)
-            batch.decode(r, l, flags=flags, stream=stream)
-            if timed:
-                ev1[k * len(batch.layers) + li].record(stream)
+            api.pa_copy_blocks(caches, st.d_pairs)
+        for l in layers:
+            api.pa_reshape_and_cache(batch.caches[l], st.new_k[l], st.new_v[l], st.d_slots)
+            batch.decode(r, l, flags=flags)
 
+    def decodes(n: int):
+        """n decode calls back to back, rotating over sets and layers (fresh KV for each)."""
+        for k in range(n):
+            batch.decode(k % sets, layers[(k // sets) % len(layers)], flags=flags)
+
+    n_dec = max(8, min(64, sets * len(layers)))
     for k in range(args.warmup):
-        step(k, False)
+        step(k % sets)
+    decodes(n_dec)  # eager pass: first-call set-up happens outside any capture
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} step(s) done")
+    if args.eager:
+        run_step = lambda k: step(k % sets)
+        run_decodes = lambda: decodes(n_dec)
+    else:
+        # The step's launches are replayed as one HIP graph per set: the timed loop measures the GPU,
+        # not the host's launch overhead.
+        graphs = []
+        for r in range(sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        g_dec = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_dec):
+            decodes(n_dec)
+        torch.cuda.synchronize()
+        for r in range(sets):  # one untimed replay of each
+            graphs[r].replay()
+        g_dec.replay()
+        torch.cuda.synchronize()
+        run_step = lambda k: graphs[k % sets].replay()
+        run_decodes = g_dec.replay
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(k, True)
+        run_step(k)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} step(s) in {elapsed * 1e3:.2f} ms")
 
-    dec_ms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
-    dec_mean_s = float(np.mean(dec_ms)) / 1e3
+    # Decode-call duration for the roofline: n_dec calls back to back between two HIP events on the
+    # stream they run on, a few times over.
+    reps = max(1, min(20, int(2e-3 / max(elapsed / args.steps / len(layers), 1e-6))))
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    ev0.record(stream)
+    for _ in range(reps):
+        run_decodes()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dec_mean_s = ev0.elapsed_time(ev1) / 1e3 / (reps * n_dec)
     ms_per_step = elapsed * 1e3 / args.steps
     layers = len(batch.layers)
     kv_logical = batch.kv_bytes_per_layer(unique=False)
@@ -228,6 +266,7 @@ def main() -> int:
             "kernel": "valu" if args.valu else "default",
             "shared_prefix_decode": bool(batch.use_prefix),
             "sets_rotated": sets,
+            "launch": "eager" if args.eager else "hip graph replay",
             "kv_bytes_per_step_logical": kv_logical * layers,
             "kv_bytes_per_layer_unique": batch.kv_bytes_per_layer(unique=True) if unique else
             kv_logical,
@@ -236,6 +275,7 @@ def main() -> int:
         "hbm_fraction_of_step": round(value / HBM_PEAK_GBPS, 4),
         "seqs_per_s_per_layer": round(seqs_per_s_layer, 1),
         "decode_call_us_mean": round(dec_mean_s * 1e6, 3),
+        "decode_calls_timed": reps * n_dec,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),

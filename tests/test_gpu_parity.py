@@ -365,6 +365,30 @@ def test_empty_context_and_out_of_range_blocks():
     assert max_abs_err(as_f64(out[2]), ref) <= TOL["f16"]
 
 
+@pytest.mark.parametrize("name", ["f16_batch32", "f16_shared_prefix_batch256"])
+def test_graph_replay_matches_eager(name):
+    """The library's calls captured as a HIP graph (no allocation, memset or synchronisation inside
+    them): every replay, with eager work and synchronisations between replays, gives the eager
+    result bit for bit."""
+    w = wl.WORKLOADS[name].replace(num_seqs=6, num_blocks=2048,
+                                   **({"prefix_len": 64} if name.startswith("f16_shared") else {}))
+    lengths = [100, 1500, 17, 640, 2048, 300] if w.prefix_len == 0 else [65, 80, 81, 400, 66, 575]
+    _say(f"graph replay, {name}")
+    b = DecodeBatch(w, lengths=lengths, partition_size=128)
+    b.run_step(0)
+    torch.cuda.synchronize()
+    ref = b.sets[0].out[0].clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        b.run_step(0)
+    for _ in range(3):
+        b.sets[0].out[0].fill_(7.0)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(b.sets[0].out[0], ref)
+
+
 def test_rejections_do_not_launch():
     w = wl.WORKLOADS["tiny_f32"]
     b = DecodeBatch(w)
