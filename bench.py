@@ -15,10 +15,10 @@ Prints ONE JSON line:
 
 Timing loops rotate between `--sets` independent batches of the workload placed in the same pool
 (distinct blocks and values), so each step reads KV that the 256 MB MALL and the L2s do not already
-hold, as the successive layers of a model would.  Each set's step is captured once as a HIP graph
-and replayed (--eager launches every call from Python instead), so the timed loop measures the GPU
-rather than the host's per-call launch overhead; the decode-call duration comes from a captured run
-of back-to-back decode calls between two HIP events.
+hold, as the successive layers of a model would.  Calls are launched from Python, which stays ahead
+of the GPU on every workload here (--graph replays each set's step as a captured HIP graph instead);
+the decode-call duration is the mean of back-to-back decode calls between two HIP events on the
+stream they run on.
 """
 from __future__ import annotations
 
@@ -59,6 +59,24 @@ def algorithmic_bytes(batch, unique: bool) -> int:
     qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * qe
     sc = 2 * w.num_kv_heads * 4 if w.cache_dtype == "fp8" else 0
     return kv + tables + lens + qo + sc
+
+
+def measured_traffic(w, default_run: bool):
+    """HBM bytes per decode call from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs summarised in
+    profiles/traffic.json (scaled by the reference copy), or None when this run is not the measured
+    configuration or the kernel sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not default_run or not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    h = hashlib.sha256()
+    for f in t["kernel_sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != t["sha256"] or w.name not in t["workloads"]:
+        return None
+    return int(t["workloads"][w.name]["bytes_per_call"])
 
 
 def cpu_baseline(batch, budget_s: float) -> dict:
@@ -112,8 +130,9 @@ def main() -> int:
     ap.add_argument("--workload", default="f16_batch32", choices=list(DEFAULT_SETS))
     ap.add_argument("--sets", type=int, default=0, help="independent batches rotated (0 = default)")
     ap.add_argument("--valu", action="store_true", help="force the vector-ALU decode kernel")
-    ap.add_argument("--eager", action="store_true",
-                    help="launch every call from Python instead of replaying captured HIP graphs")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step as a captured HIP graph instead of launching every call "
+                         "from Python")
     ap.add_argument("--partition", type=int, default=-1, help="partition size (-1 = workload's)")
     ap.add_argument("--num-blocks", type=int, default=0,
                     help="physical blocks per layer pool (0 = the workload's own)")
@@ -194,12 +213,11 @@ def main() -> int:
     decodes(n_dec)  # eager pass: first-call set-up happens outside any capture
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} step(s) done")
-    if args.eager:
+    if not args.graph:
         run_step = lambda k: step(k % sets)
         run_decodes = lambda: decodes(n_dec)
     else:
-        # The step's launches are replayed as one HIP graph per set: the timed loop measures the GPU,
-        # not the host's launch overhead.
+        # The step's launches replayed as one HIP graph per set.
         graphs = []
         for r in range(sets):
             g = torch.cuda.CUDAGraph()
@@ -266,7 +284,7 @@ def main() -> int:
             "kernel": "valu" if args.valu else "default",
             "shared_prefix_decode": bool(batch.use_prefix),
             "sets_rotated": sets,
-            "launch": "eager" if args.eager else "hip graph replay",
+            "launch": "hip graph replay" if args.graph else "eager (GPU-bound)",
             "kv_bytes_per_step_logical": kv_logical * layers,
             "kv_bytes_per_layer_unique": batch.kv_bytes_per_layer(unique=True) if unique else
             kv_logical,
@@ -282,7 +300,11 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w, args.partition < 0 and not args.valu and
+                                        not args.num_blocks and not args.no_prefix),
+            "traffic_note": "HBM bytes per call from rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE "
+                            "(decode + reduce kernels; profiles/traffic.json), null unless this run "
+                            "is the measured configuration of unchanged kernels",
             "kernel": ("pa_decode_attention_shared_prefix" if batch.use_prefix else
                        "pa_decode_attention") + " (split-K decode + partition reduce)",
             "bytes_per_call": alg,

@@ -122,9 +122,11 @@ def test_workspace_sizing():
     rows = 8 * 28 * 64
     need = ws(8, 28, 4, 128, 32768, 512)
     assert need >= rows * 128 * 4 + rows * 2 * 4
-    assert api.pa_decode_auto_partition(8, 4, 32768) == 512
-    assert api.pa_decode_auto_partition(32, 4, 2048) in (128, 256)
-    assert api.pa_decode_auto_partition(1, 1, 100) == 128
+    assert api.pa_decode_auto_partition(8, 4, 32768) == 1024    # few long rows
+    assert api.pa_decode_auto_partition(32, 4, 2048) == 256
+    assert api.pa_decode_auto_partition(512, 4, 13708) == 256
+    assert api.pa_decode_auto_partition(2, 2, 1000) == 64       # tiny batch: more, smaller items
+    assert api.pa_decode_auto_partition(1, 1, 100) == 64
 
 
 def test_reshape_validation():
