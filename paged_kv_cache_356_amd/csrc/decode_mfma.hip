@@ -610,13 +610,16 @@ void decode_mfma_kernel(DecodeArgs a) {
       prefix_tile<CT, QT, D>(a, t * 16, h, start / kBlock, end / kBlock, end, c, tlds);
     }
   }
-  // Then the sequences' items, one per wavefront: wavefront gw of GW takes items gw, gw + GW, ...
-  // of the list (sequence, partition, KV head) with the KV head fastest, so the wavefronts running
-  // at the same time cover the H tiles (b, 0..H-1) of the same blocks, next to each other in the
-  // pool.
+  // Then the sequences' items, one per wavefront, dealt wavefront-major: wavefront w of workgroup b
+  // takes items w G + b, w G + b + 4 G, ... (G workgroups), so the first G items go one to every
+  // workgroup (and so spread over all compute units) before any workgroup gets a second, and a
+  // batch with fewer items than wavefronts does not pile two busy workgroups onto some units
+  // while others idle.  The list is (sequence, partition, KV head) with the KV head fastest, so
+  // the wavefronts running at the same time cover the H tiles (b, 0..H-1) of the same blocks,
+  // next to each other in the pool.
   const int total = __builtin_amdgcn_readfirstlane(prefix[S]) * H;
   const int GW = gridDim.x * kWaves;
-  for (int f = blockIdx.x * kWaves + w; f < total; f += GW) {
+  for (int f = w * gridDim.x + blockIdx.x; f < total; f += GW) {
     const int pf = f / H, h = f - pf * H;
     int lo = 0, hi = S - 1;  // largest s with prefix[s] <= pf (LDS values, made uniform)
     while (lo < hi) {

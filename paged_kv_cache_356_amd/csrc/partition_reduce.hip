@@ -12,8 +12,9 @@
 // One wavefront per (sequence, query head) row, four rows per workgroup, no barriers.  Each lane
 // owns one float4 column of the partial outputs (C = D / 4 columns) and the partitions
 // lane / C, lane / C + G, ... (G = 64 / C) of a chunk of 64; the weights of the chunk's partitions
-// sit one per lane and are fetched with lane shuffles, the loads of a sub-chunk of 8 G partitions
-// are all issued before any is used, and the G column groups are combined with shuffles at the end.
+// sit one per lane and are fetched with lane shuffles, the loads of a sub-chunk of kPer * G
+// partitions are all issued before any is used, and the G column groups are combined with shuffles
+// at the end.
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -22,11 +23,13 @@ namespace {
 
 constexpr int kRowsPerGroup = 4;
 
-template <class QT, int D>
+// kPer: float4 loads in flight per lane (a sub-chunk of G * kPer partitions).  8 keeps the
+// registers low for batches of many rows; 32 takes 64 partitions of a row in one round trip when
+// rows are few (then occupancy does not matter).
+template <class QT, int D, int kPer>
 __global__ __launch_bounds__(64 * kRowsPerGroup) void partition_reduce_kernel(DecodeArgs a) {
   constexpr int C = D / 4;   // float4 columns of a partial output
   constexpr int G = 64 / C;  // partitions handled side by side in a wavefront
-  constexpr int kPer = 8;    // float4 loads in flight per lane (a sub-chunk of G * kPer partitions)
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerGroup + (threadIdx.x >> 6);  // s * Hq + hq
   if (row >= a.num_seqs * a.num_q_heads) return;
@@ -94,8 +97,14 @@ template <class QT>
 hipError_t launch_q(const DecodeArgs &a, hipStream_t s) {
   const int rows = a.num_seqs * a.num_q_heads;
   dim3 grid((rows + kRowsPerGroup - 1) / kRowsPerGroup), block(64 * kRowsPerGroup);
-  if (a.cache.head_dim == 64) partition_reduce_kernel<QT, 64><<<grid, block, 0, s>>>(a);
-  else partition_reduce_kernel<QT, 128><<<grid, block, 0, s>>>(a);
+  const bool wide = rows <= 2048 && a.num_partitions > 16;
+  if (a.cache.head_dim == 64) {
+    if (wide) partition_reduce_kernel<QT, 64, 16><<<grid, block, 0, s>>>(a);
+    else partition_reduce_kernel<QT, 64, 8><<<grid, block, 0, s>>>(a);
+  } else {
+    if (wide) partition_reduce_kernel<QT, 128, 32><<<grid, block, 0, s>>>(a);
+    else partition_reduce_kernel<QT, 128, 8><<<grid, block, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
