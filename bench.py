@@ -23,6 +23,7 @@ stream they run on.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -239,6 +240,10 @@ def main() -> int:
         torch.cuda.synchronize()
         run_step = lambda k: graphs[k % sets].replay()
         run_decodes = g_dec.replay
+    # Python's cyclic garbage collector is run before the timed region and kept off during it (as
+    # timeit does): a full collection takes tens of milliseconds, longer than many steps.
+    gc.collect()
+    gc.disable()
     t0 = time.perf_counter()
     for k in range(args.steps):
         run_step(k)
@@ -256,6 +261,7 @@ def main() -> int:
         run_decodes()
     ev1.record(stream)
     torch.cuda.synchronize()
+    gc.enable()
     dec_mean_s = ev0.elapsed_time(ev1) / 1e3 / (reps * n_dec)
     ms_per_step = elapsed * 1e3 / args.steps
     layers = len(batch.layers)

@@ -69,10 +69,10 @@ template <class T> struct NativeVec { using type = T; };
 template <> struct NativeVec<uint4> { using type = u32x4_t; };
 template <> struct NativeVec<uint2> { using type = u32x2_t; };
 
-template <class T>
+template <class T, bool kNT>
 __device__ __forceinline__ T load_kv(const char *p) {
   using N = typename NativeVec<T>::type;
-  if constexpr (PA_DECODE_NT)
+  if constexpr (kNT)
     return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const N *>(p)));
   else return *reinterpret_cast<const T *>(p);
 }
@@ -205,7 +205,7 @@ __device__ __forceinline__ void load_query(const DecodeArgs &a, int rs, int rhq,
   for (int nt = 0; nt < D / 16; ++nt) st.acc[nt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
-template <class CT, int D>
+template <class CT, int D, bool kNT>
 __device__ __forceinline__ void load_block(const DecodeArgs &a, int bid, int h, Frag<CT, D> &f) {
   using F = Frag<CT, D>;
   constexpr int kTileBytes = kBlock * D * CT::bytes;
@@ -215,10 +215,11 @@ __device__ __forceinline__ void load_block(const DecodeArgs &a, int bid, int h, 
   const char *vt = static_cast<const char *>(a.cache.v_pool) + tile;
 #pragma unroll
   for (int i = 0; i < F::kKLoads; ++i)
-    f.k[i] = load_kv<uint4>(kt + (size_t)(lane + 64 * i) * 16);
+    f.k[i] = load_kv<uint4, kNT>(kt + (size_t)(lane + 64 * i) * 16);
 #pragma unroll
   for (int nt = 0; nt < F::kNT; ++nt)
-    f.v[nt] = load_kv<typename F::VRaw>(vt + (size_t)((16 * nt + col) * kBlock + 4 * grp) * CT::bytes);
+    f.v[nt] = load_kv<typename F::VRaw, kNT>(
+        vt + (size_t)((16 * nt + col) * kBlock + 4 * grp) * CT::bytes);
 }
 
 // One 16-token block at token tok0 into the state.  Scores of positions at or past `zlim` (per
@@ -301,8 +302,8 @@ __device__ __forceinline__ void block_step(const Frag<CT, D> &f, float kscale, i
     }
 }
 
-// The ring: blocks j = jfirst, jfirst + jstride, ... < jb1 of table row `table`, KV head h, through
-// kBufs fragments.  While one block is computed, the loads of the next kBufs - 1 are in flight.
+// The ring: blocks j = jb0 .. jb1 - 1 of table row `table`, KV head h, through kBufs fragments.
+// While one block is computed, the loads of the next kBufs - 1 are in flight.
 // Buffer indices are compile-time constants (the inner loop is unrolled), so the ring needs no
 // copies.  Every slot is loaded and computed on every round, with no branch around either, so each
 // compute waits only for its own slot and the accumulators stay in place: a slot past the end of
@@ -312,18 +313,17 @@ __device__ __forceinline__ void block_step(const Frag<CT, D> &f, float kscale, i
 // v_readlane: a table read inside the ring would be a vector load whose result feeds the next
 // address, and waiting for it would drain every load in flight.  A wavefront with more than 64
 // blocks runs one ring per 64 of them.
-template <class CT, int D>
+template <class CT, int D, bool kNT>
 __device__ __forceinline__ void stream_blocks(const DecodeArgs &a, const int32_t *table, int h,
-                                              int jfirst, int jstride, int jb1, int zlim, int vend,
-                                              float kscale, RowState<D> &st) {
+                                              int jb0, int jb1, int zlim, int vend, float kscale,
+                                              RowState<D> &st) {
   using F = Frag<CT, D>;
   const int nb = a.cache.num_blocks;
   const int lane = threadIdx.x & 63;
-  const int nk = jfirst < jb1 ? (jb1 - jfirst + jstride - 1) / jstride : 0;  // this wave's blocks
+  const int nk = jb1 > jb0 ? jb1 - jb0 : 0;  // this wave's blocks
   for (int k0 = 0; k0 < nk; k0 += 64) {
     const int kn = min(64, nk - k0);
-    const int jc = jfirst + k0 * jstride;  // the chunk's first block
-    const int tbl = lane < kn ? table[jc + lane * jstride] : -1;
+    const int tbl = lane < kn ? table[jb0 + k0 + lane] : -1;
     // block id of the chunk's k-th block (-1 past the chunk); k is wave-uniform
     auto entry = [&](int k) { return k < kn ? __builtin_amdgcn_readlane(tbl, k < 64 ? k : 63) : -1; };
     F buf[kBufs];
@@ -332,16 +332,16 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs &a, const int32_t
     for (int b = 0; b < kBufs; ++b) {
       const int bid = entry(b);
       ok[b] = (unsigned)bid < (unsigned)nb;  // an entry outside the pool is never dereferenced
-      load_block<CT, D>(a, ok[b] ? bid : 0, h, buf[b]);
+      load_block<CT, D, kNT>(a, ok[b] ? bid : 0, h, buf[b]);
     }
     for (int kr = 0; kr < kn; kr += kBufs) {
 #pragma unroll
       for (int b = 0; b < kBufs; ++b) {
-        const int t0 = (jc + (kr + b) * jstride) * kBlock;
+        const int t0 = (jb0 + k0 + kr + b) * kBlock;
         block_step<CT, D>(buf[b], kscale, t0, ok[b] ? zlim : t0, ok[b] ? vend : t0, st);
         const int bid = entry(kr + b + kBufs);
         ok[b] = (unsigned)bid < (unsigned)nb;
-        load_block<CT, D>(a, ok[b] ? bid : 0, h, buf[b]);
+        load_block<CT, D, kNT>(a, ok[b] ? bid : 0, h, buf[b]);
       }
     }
   }
@@ -374,7 +374,9 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs &a, int s) {
 // The result goes to workspace partition `slot`, or straight to the output when slot < 0.
 // Wavefronts of one workgroup run their items independently, so one wavefront's item prologue
 // (query, table fetch, first loads) and epilogue overlap the other wavefronts' block streams.
-template <class CT, class QT, int D>
+// kNT: read K/V with non-temporal loads (each tile is read once per call), or with ordinary loads
+// (prefix tiles, whose blocks the other tiles of the batch read too).
+template <class CT, class QT, int D, bool kNT>
 __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int row0_in, int h_in,
                                           int jb0_in, int jb1_in, int end_in, int slot_in) {
   // The item is the same for the whole wavefront: keep its fields (and so the tile addresses) in
@@ -403,7 +405,7 @@ __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int row
   load_query<CT, D>(a, rs, rhq, rvalid, st);
   float kscale, vscale;
   head_scales<CT>(a, h, kscale, vscale);
-  stream_blocks<CT, D>(a, table, h, jb0, 1, jb1, lim, end, kscale, st);
+  stream_blocks<CT, D, kNT>(a, table, h, jb0, jb1, lim, end, kscale, st);
 
   // the row's sum over the four lane groups; m is already uniform over them
   float l = st.l;
@@ -439,82 +441,6 @@ __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int row
   }
 }
 
-// LDS of a workgroup prefix tile: each wavefront's unnormalised output [head-dim][row] (+1 pad)
-// and its (running max, running sum) per row.
-template <int D>
-struct TileLds {
-  float o[kWaves][D][17];
-  float m[kWaves][16];
-  float l[kWaves][16];
-};
-
-// Prefix tile, computed by the whole workgroup: flat rows row0 .. row0 + 15 of the batch (flat row
-// r is query head h*g + r % g of sequence r / g) against the shared prefix's blocks [jb0, jb1);
-// wavefront w takes blocks jb0 + w, + 4, ..., so the workgroup's four block streams run side by
-// side, and the four partial states are merged through LDS into workspace partition `slot`.
-// Each row masks the positions at or past its own context length.
-template <class CT, class QT, int D>
-__device__ __forceinline__ void prefix_tile(const DecodeArgs &a, int row0_in, int h_in, int jb0_in,
-                                            int jb1_in, int end_in, int slot_in,
-                                            TileLds<D> &lds) {
-  const int row0 = __builtin_amdgcn_readfirstlane(row0_in);
-  const int h = __builtin_amdgcn_readfirstlane(h_in);
-  const int jb0 = __builtin_amdgcn_readfirstlane(jb0_in);
-  const int jb1 = __builtin_amdgcn_readfirstlane(jb1_in);
-  const int end = __builtin_amdgcn_readfirstlane(end_in);
-  const int slot = __builtin_amdgcn_readfirstlane(slot_in);
-  constexpr int NT = D / 16;
-  const int H = a.cache.num_kv_heads, Hq = a.num_q_heads, g = Hq / H;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, grp = lane >> 4;
-  const int nrows = min(16, a.num_seqs * g - row0);
-  const bool rvalid = col < nrows;
-  const int rs = rvalid ? (row0 + col) / g : 0;
-  const int rhq = h * g + (rvalid ? (row0 + col) % g : 0);
-  const int lim = rvalid ? min(end, clamp_len(a, rs)) : end;
-
-  RowState<D> st;
-  load_query<CT, D>(a, rs, rhq, rvalid, st);
-  float kscale, vscale;
-  head_scales<CT>(a, h, kscale, vscale);
-  stream_blocks<CT, D>(a, a.prefix_table, h, jb0 + w, kWaves, jb1, lim, end, kscale, st);
-
-  float l = st.l;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (grp == 0) {
-    lds.m[w][col] = st.m;
-    lds.l[w][col] = l;
-  }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds.o[w][16 * nt + 4 * grp + i][col] = st.acc[nt][i];
-  __syncthreads();
-  for (int x = tid; x < nrows * D; x += blockDim.x) {
-    const int i = x / D, d = x % D;
-    float M = kNoMax;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, lds.m[v][i]);
-    float lsum = 0.0f, o = 0.0f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const float c = __builtin_amdgcn_exp2f(lds.m[v][i] - M);  // an idle wavefront has l = 0
-      lsum += c * lds.l[v][i];
-      o += c * lds.o[v][d][i];
-    }
-    const int r = row0 + i;
-    const size_t row = ((size_t)(r / g) * Hq + h * g + r % g) * a.num_partitions + slot;
-    a.part_out[row * D + d] = lsum > 0.0f ? o / lsum * vscale : 0.0f;
-    if (d == 0) {
-      a.part_ml[row * 2] = M;
-      a.part_ml[row * 2 + 1] = lsum;
-    }
-  }
-  __syncthreads();  // the LDS buffers are free for the next tile
-}
-
 // Items of sequence s: plain decode, partitions of its context (an empty context counts one item,
 // which writes its zeros); shared-prefix decode, partitions of the positions after the prefix
 // (possibly none).
@@ -530,24 +456,30 @@ __device__ __forceinline__ void run_sequence_item(const DecodeArgs &a, int s, in
   if (a.prefix_len > 0) {
     const int start = a.prefix_len + part * PT;
     const int end = min(L, start + PT);
-    wave_item<CT, QT, D>(a, s, 0, h, start / kBlock, (end + kBlock - 1) / kBlock, end,
-                         a.prefix_chunks + part);
+    wave_item<CT, QT, D, PA_DECODE_NT>(a, s, 0, h, start / kBlock, (end + kBlock - 1) / kBlock,
+                                       end, a.prefix_chunks + part);
   } else {
     const int start = part * PT;
     const int end = min(L, start + PT);
     const int n = L > 0 ? (L + PT - 1) / PT : 1;
-    wave_item<CT, QT, D>(a, s, 0, h, start / kBlock,
-                         L > start ? (end + kBlock - 1) / kBlock : start / kBlock, end,
-                         n > 1 ? part : -1);
+    wave_item<CT, QT, D, PA_DECODE_NT>(a, s, 0, h, start / kBlock,
+                                       L > start ? (end + kBlock - 1) / kBlock : start / kBlock,
+                                       end, n > 1 ? part : -1);
   }
 }
 
 // Grid modes.  Direct (plain decode only, more than kMaxScanSeqs sequences): wavefront
 // 4 blockIdx.x + w takes flat item (partition, KV head, sequence) of the launch bounds, the ones
 // past a sequence's end returning at once.  Persistent: as many workgroups as fit on the device
-// at once; with a shared prefix they first share out its tiles (a chunk being up to kPrefixChunk
-// positions), then every wavefront takes its share of the sequence items, located through the
-// prefix sum of the sequences' item counts that every workgroup computes in LDS.
+// at once, every wavefront taking its share of the sequence items, located through the prefix sum
+// of the sequences' item counts that every workgroup computes in LDS.
+// With a shared prefix, the prefix is cut into groups of 64 flat rows (sequence, query head) of
+// one KV head and chunks of up to kPrefixChunk positions; workgroup b takes groups b, b + G, ...
+// (G workgroups), its wavefront w the group's rows 16 w .. 16 w + 15.  The four wavefronts walk
+// the same blocks in the same order with ordinary loads, so the compute unit's cache serves the
+// same tile to all four and each block crosses from L2 about once per group instead of once per
+// 16 rows.  The sequence items go first to the wavefronts of workgroups without prefix work, so
+// the streaming of private blocks from HBM starts at once beside the prefix groups.
 template <class CT, class QT, int D>
 __global__ __launch_bounds__(256)
 #if PA_DECODE_OCC
@@ -597,29 +529,31 @@ void decode_mfma_kernel(DecodeArgs a) {
   if (tid == 255) prefix[S] = run;  // thread 255 holds the grand total (its chunk ends at S or later)
   __syncthreads();
 
-  // Shared prefix first: workgroup b computes prefix tiles b, b + G, ... (all four wavefronts
-  // together), list order (chunk, 16-row tile, KV head) with the KV head fastest.
-  const int n_tiles = a.prefix_len > 0 ? (S * g + 15) / 16 : 0;
-  const int n_pre = n_tiles * a.prefix_chunks * H;
-  if (n_pre > 0) {
-    __shared__ TileLds<D> tlds;
-    for (int i = blockIdx.x; i < n_pre; i += gridDim.x) {
-      const int h = i % H, t = (i / H) % n_tiles, c = i / (H * n_tiles);
-      const int start = c * kPrefixChunk;
-      const int end = min(a.prefix_len, start + kPrefixChunk);
-      prefix_tile<CT, QT, D>(a, t * 16, h, start / kBlock, end / kBlock, end, c, tlds);
-    }
+  // Prefix groups: list order (chunk, 64-row group, KV head) with the KV head fastest.
+  const int G = gridDim.x;
+  const int n_groups = a.prefix_len > 0 ? (S * g + 63) / 64 : 0;
+  const int n_pre = n_groups * a.prefix_chunks * H;
+  for (int i = blockIdx.x; i < n_pre; i += G) {
+    const int h = i % H, t = (i / H) % n_groups, c = i / (H * n_groups);
+    const int row0 = 64 * t + 16 * w;
+    if (row0 >= S * g) continue;  // the last group's unused tiles
+    const int start = c * kPrefixChunk;
+    const int end = min(a.prefix_len, start + kPrefixChunk);
+    wave_item<CT, QT, D, false>(a, -1, row0, h, start / kBlock, end / kBlock, end, c);
   }
-  // Then the sequences' items, one per wavefront, dealt wavefront-major: wavefront w of workgroup b
-  // takes items w G + b, w G + b + 4 G, ... (G workgroups), so the first G items go one to every
-  // workgroup (and so spread over all compute units) before any workgroup gets a second, and a
-  // batch with fewer items than wavefronts does not pile two busy workgroups onto some units
-  // while others idle.  The list is (sequence, partition, KV head) with the KV head fastest, so
-  // the wavefronts running at the same time cover the H tiles (b, 0..H-1) of the same blocks,
-  // next to each other in the pool.
+  // The sequences' items, one per wavefront.  Wavefronts are ranked so that those of workgroups
+  // without prefix work come first, each class wavefront-major (wavefront w of every workgroup
+  // before wavefront w + 1 of any): the first items go one to every workgroup, spread over all
+  // compute units, before any workgroup gets a second.  Item f goes to the wavefront of rank
+  // f mod 4G.  The list is (sequence, partition, KV head) with the KV head fastest, so the
+  // wavefronts running at the same time cover the H tiles (b, 0..H-1) of the same blocks, next to
+  // each other in the pool.
+  const int busy = min(n_pre, G);  // workgroups 0 .. busy - 1 have prefix work
+  const int rank = blockIdx.x < busy ? (G - busy) * kWaves + w * busy + blockIdx.x
+                                     : w * (G - busy) + (blockIdx.x - busy);
   const int total = __builtin_amdgcn_readfirstlane(prefix[S]) * H;
-  const int GW = gridDim.x * kWaves;
-  for (int f = w * gridDim.x + blockIdx.x; f < total; f += GW) {
+  const int GW = G * kWaves;
+  for (int f = rank; f < total; f += GW) {
     const int pf = f / H, h = f - pf * H;
     int lo = 0, hi = S - 1;  // largest s with prefix[s] <= pf (LDS values, made uniform)
     while (lo < hi) {

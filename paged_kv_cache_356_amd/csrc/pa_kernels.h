@@ -11,7 +11,10 @@ namespace pa {
 enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };
 
 // Shared-prefix decode: prefix positions per prefix work item (and per workspace partition slot).
-constexpr int32_t kPrefixChunk = 512;
+#ifndef PA_PREFIX_CHUNK
+#define PA_PREFIX_CHUNK 512
+#endif
+constexpr int32_t kPrefixChunk = PA_PREFIX_CHUNK;
 
 inline int dtype_bytes(int dt) {
   return dt == kF32 ? 4 : (dt == kF16 || dt == kBF16) ? 2 : dt == kFP8 ? 1 : 0;
