@@ -165,10 +165,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   max_context_len  host upper bound of context_lens, used to size the launch without reading
  *                 the device.
  *   scale         softmax scale, normally 1 / sqrt(head_dim).
- *   partition_size  tokens per split-K partition: 0 = pa_decode_auto_partition(), otherwise a
- *                 positive multiple of 16.  A sequence longer than one partition is computed as
- *                 independent partitions (running max, running sum, unnormalised output) merged
- *                 by a second kernel.
+ *   partition_size  most tokens per split-K partition: 0 = pa_decode_auto_partition(),
+ *                 otherwise a positive multiple of 16.  A context of L tokens is cut into
+ *                 ceil(L / partition_size) partitions of whole blocks, as equal as whole blocks
+ *                 allow; when there are several they are computed independently (running max,
+ *                 running sum, unnormalised output) and merged by a second kernel.
  *   workspace     device scratch of at least pa_decode_workspace_bytes() bytes (NULL if 0).
  * Supported: block_size 16, head_dim 64 or 128, num_q_heads a multiple of num_kv_heads with at
  * most 16 query heads per KV head.
@@ -198,6 +199,8 @@ pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int
  *                 whose context length is below prefix_len attends only to its first
  *                 context_lens[s] positions, as in pa_decode_attention.
  *   workspace     at least pa_decode_shared_prefix_workspace_bytes() bytes.
+ * The prefix is computed in chunks of 512 positions; the positions after it are cut into
+ * partitions as in pa_decode_attention (ceil((L - prefix_len) / partition_size) of them).
  * All other arguments and rules are those of pa_decode_attention.  Batches the prefix path does not
  * cover (more than 4096 sequences, the vector-ALU dtype pairs, PA_DECODE_FORCE_VALU) are computed
  * by the plain decode, with the same result.

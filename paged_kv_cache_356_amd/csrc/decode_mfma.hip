@@ -453,18 +453,17 @@ template <class CT, class QT, int D>
 __device__ __forceinline__ void run_sequence_item(const DecodeArgs &a, int s, int part, int h) {
   const int PT = a.partition_size;
   const int L = clamp_len(a, s);
+  int start, end;
   if (a.prefix_len > 0) {
-    const int start = a.prefix_len + part * PT;
-    const int end = min(L, start + PT);
+    partition_range(a.prefix_len, L, PT, part, &start, &end);
     wave_item<CT, QT, D, PA_DECODE_NT>(a, s, 0, h, start / kBlock, (end + kBlock - 1) / kBlock,
                                        end, a.prefix_chunks + part);
-  } else {
-    const int start = part * PT;
-    const int end = min(L, start + PT);
-    const int n = L > 0 ? (L + PT - 1) / PT : 1;
-    wave_item<CT, QT, D, PA_DECODE_NT>(a, s, 0, h, start / kBlock,
-                                       L > start ? (end + kBlock - 1) / kBlock : start / kBlock,
-                                       end, n > 1 ? part : -1);
+  } else if (L > 0) {
+    partition_range(0, L, PT, part, &start, &end);
+    wave_item<CT, QT, D, PA_DECODE_NT>(a, s, 0, h, start / kBlock, (end + kBlock - 1) / kBlock,
+                                       end, L > PT ? part : -1);
+  } else {  // empty context: no block, zeros written straight to the output
+    wave_item<CT, QT, D, PA_DECODE_NT>(a, s, 0, h, 0, 0, 0, -1);
   }
 }
 

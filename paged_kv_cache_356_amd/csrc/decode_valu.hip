@@ -40,17 +40,17 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   int Ls = a.context_lens[s];
   Ls = Ls < 0 ? 0 : (Ls > a.max_context_len ? a.max_context_len : Ls);
   const int PT = a.partition_size;
-  const int start = part * PT;
+  const int nparts = (Ls + PT - 1) / PT;
   auto *out = static_cast<typename QT::raw *>(a.out);
-  if (start >= Ls) {
+  if (part >= nparts) {
     if (part == 0) {  // empty context: output is zero
       for (int x = tid; x < g * D; x += blockDim.x)
         out[((size_t)s * Hq + h * g) * D + x] = from_f32<QT>(0.0f);
     }
     return;
   }
-  const int end = min(Ls, start + PT);
-  const int nparts = (Ls + PT - 1) / PT;
+  int start, end;
+  partition_range(0, Ls, PT, part, &start, &end);
 
   const auto *q = static_cast<const typename QT::raw *>(a.q) + (size_t)s * a.q_stride +
                   (size_t)h * g * D;

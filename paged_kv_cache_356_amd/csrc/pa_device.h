@@ -6,9 +6,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace pa {
+#include "pa_kernels.h"
 
-constexpr int kBlock = 16;  // token positions per KV block
+namespace pa {
 
 // Cache element tags.  bf16 and fp8 are carried as raw bits; conversions below are exact.
 struct f32_t { using raw = float; static constexpr int bytes = 4; };

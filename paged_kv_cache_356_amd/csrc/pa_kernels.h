@@ -10,6 +10,8 @@ namespace pa {
 
 enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };
 
+constexpr int kBlock = 16;  // token positions per KV block
+
 // Shared-prefix decode: prefix positions per prefix work item (and per workspace partition slot).
 #ifndef PA_PREFIX_CHUNK
 #define PA_PREFIX_CHUNK 512
@@ -70,6 +72,22 @@ struct DecodeArgs {
   int32_t prefix_len;       // multiple of 16
   int32_t prefix_chunks;    // ceil(prefix_len / kPrefixChunk)
 };
+
+// Partition `part` of positions [base, L) (base a multiple of the block size) cut into
+// n = ceil((L - base) / PT) partitions: the range's nb blocks are shared out as evenly as whole
+// blocks allow (the first nb mod n partitions take one block more), so no partition holds more than
+// PT positions and the partitions of one range differ by at most one block.  Sets [*start, *end).
+inline __host__ __device__ void partition_range(int32_t base, int32_t L, int32_t PT, int32_t part,
+                                                int32_t *start, int32_t *end) {
+  const int32_t len = L - base;
+  const int32_t n = (len + PT - 1) / PT;
+  const int32_t nb = (len + kBlock - 1) / kBlock;
+  const int32_t q = nb / n, r = nb % n;
+  const int32_t b0 = part * q + (part < r ? part : r);
+  const int32_t b1 = b0 + q + (part < r ? 1 : 0);
+  *start = base + b0 * kBlock;
+  *end = base + b1 * kBlock < L ? base + b1 * kBlock : L;
+}
 
 // Workspace partition slots of a row whose context length is L (see DecodeArgs).
 inline __host__ __device__ int32_t row_partitions(const DecodeArgs &a, int32_t L) {
