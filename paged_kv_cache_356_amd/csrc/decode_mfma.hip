@@ -58,6 +58,15 @@ constexpr int kBufs = PA_DECODE_BUFS;  // blocks per wavefront in the load ring
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1
 #endif
+#ifndef PA_SPREAD
+#define PA_SPREAD 0
+#endif
+#ifndef PA_PRIO
+#define PA_PRIO 1
+#endif
+#ifndef PA_PRIO_SHIFT
+#define PA_PRIO_SHIFT 3  // blocks per priority level
+#endif
 #ifndef PA_DECODE_OCC
 #define PA_DECODE_OCC 3  // at least this many wavefronts per SIMD (caps registers at 168)
 #endif
@@ -313,6 +322,22 @@ __device__ __forceinline__ void block_step(const Frag<CT, D> &f, float kscale, i
 // v_readlane: a table read inside the ring would be a vector load whose result feeds the next
 // address, and waiting for it would drain every load in flight.  A wavefront with more than 64
 // blocks runs one ring per 64 of them.
+// Wavefront priority from the blocks it still has to stream: waves sharing a SIMD otherwise
+// issue oldest first, and the youngest one of a compute unit can take half as long again as the
+// oldest over the same work, which sets the kernel's end.  Longest remaining work first evens
+// them out.  (s_setprio takes an immediate, hence the branches; the value is wave-uniform.)
+__device__ __forceinline__ void prio_for_remaining(int blocks_left) {
+#if PA_PRIO
+  const int p = blocks_left >> PA_PRIO_SHIFT;
+  if (p >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (p == 2) __builtin_amdgcn_s_setprio(2);
+  else if (p == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+#else
+  (void)blocks_left;
+#endif
+}
+
 template <class CT, int D, bool kNT>
 __device__ __forceinline__ void stream_blocks(const DecodeArgs &a, const int32_t *table, int h,
                                               int jb0, int jb1, int zlim, int vend, float kscale,
@@ -335,6 +360,7 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs &a, const int32_t
       load_block<CT, D, kNT>(a, ok[b] ? bid : 0, h, buf[b]);
     }
     for (int kr = 0; kr < kn; kr += kBufs) {
+      prio_for_remaining(nk - k0 - kr);
 #pragma unroll
       for (int b = 0; b < kBufs; ++b) {
         const int t0 = (jb0 + k0 + kr + b) * kBlock;
@@ -553,7 +579,8 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int total = __builtin_amdgcn_readfirstlane(prefix[S]) * H;
   const int GW = G * kWaves;
   for (int f = rank; f < total; f += GW) {
-    const int pf = f / H, h = f - pf * H;
+    const int pf = f / H;
+    const int h = f - pf * H;
     int lo = 0, hi = S - 1;  // largest s with prefix[s] <= pf (LDS values, made uniform)
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -594,7 +621,9 @@ hipError_t launch_dd(DecodeArgs a, hipStream_t s) {
   const int64_t direct = (items + kWaves - 1) / kWaves;  // one wavefront per item
   a.persistent = a.num_seqs <= kMaxScanSeqs;
   dim3 grid((unsigned)direct);
-  if (a.persistent) grid = dim3((unsigned)std::min<int64_t>(direct, resident_groups<CT, QT, D>()));
+  if (a.persistent)
+    grid = dim3((unsigned)(PA_SPREAD ? resident_groups<CT, QT, D>()
+                                     : std::min<int64_t>(direct, resident_groups<CT, QT, D>())));
   decode_mfma_kernel<CT, QT, D><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }

@@ -15,6 +15,10 @@
 // sit one per lane and are fetched with lane shuffles, the loads of a sub-chunk of kPer * G
 // partitions are all issued before any is used, and the G column groups are combined with shuffles
 // at the end.
+// The first chunk's (m, l) pairs and first sub-chunk of outputs are loaded together, as soon as the
+// row's partition count is known: the outputs do not wait for the maximum, so a row with few
+// partitions makes two round trips to memory (context length, then its partials), not three.
+// Slots past the row's partitions hold whatever earlier calls left there and are never read.
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -23,47 +27,60 @@ namespace {
 
 constexpr int kRowsPerGroup = 4;
 
-// kPer: float4 loads in flight per lane (a sub-chunk of G * kPer partitions).  8 keeps the
-// registers low for batches of many rows; 32 takes 64 partitions of a row in one round trip when
-// rows are few (then occupancy does not matter).
+// kPer: float4 loads in flight per lane (a sub-chunk of G * kPer partitions).  A few keep the
+// registers low, so that many rows are in flight, for batches of many rows; 32 takes 64
+// partitions of a row in one round trip when rows are few (then occupancy does not matter).
+#ifndef PA_REDUCE_WIDE
+#define PA_REDUCE_WIDE 1
+#endif
+#ifndef PA_REDUCE_PER
+#define PA_REDUCE_PER 4
+#endif
 template <class QT, int D, int kPer>
 __global__ __launch_bounds__(64 * kRowsPerGroup) void partition_reduce_kernel(DecodeArgs a) {
   constexpr int C = D / 4;   // float4 columns of a partial output
   constexpr int G = 64 / C;  // partitions handled side by side in a wavefront
+  constexpr int SUB = G * kPer;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerGroup + (threadIdx.x >> 6);  // s * Hq + hq
   if (row >= a.num_seqs * a.num_q_heads) return;
   const int s = row / a.num_q_heads;
+  const int NP = a.num_partitions;
+  const size_t row0 = (size_t)row * NP;
+  const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml) + row0;
+  const float4 *po = reinterpret_cast<const float4 *>(a.part_out) + row0 * C;
+  const int c = lane % C, grp = lane / C;
+
   int Ls = a.context_lens[s];
   Ls = Ls < 0 ? 0 : (Ls > a.max_context_len ? a.max_context_len : Ls);
   const int np = row_partitions(a, Ls);
   if (np <= 1 && a.prefix_len == 0) return;  // finished by the decode kernel
-  const size_t row0 = (size_t)row * a.num_partitions;
-  const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml) + row0;
-  const float4 *po = reinterpret_cast<const float4 *>(a.part_out) + row0 * C;
+  const float2 v0 = lane < np ? ml[lane] : make_float2(-INFINITY, 0.0f);
+  float4 x[kPer];  // one sub-chunk of partial outputs; the first is loaded beside v0
+  auto load_sub = [&](int base, int sub, int n) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int q = sub + grp + k * G;
+      x[k] = q < n ? po[(size_t)(base + q) * C + c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+  };
+  load_sub(0, 0, min(64, np));
 
-  // M = max over partitions (the first chunk's pair stays in registers)
-  const float2 first = lane < np ? ml[lane] : make_float2(-INFINITY, 0.0f);
-  float M = first.x;
+  // M = max over the row's partitions
+  float M = v0.x;
   for (int p = lane + 64; p < np; p += 64) M = fmaxf(M, ml[p].x);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
 
-  const int c = lane % C, grp = lane / C;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float wsum = 0.0f;
   for (int base = 0; base < np; base += 64) {
     const int n = min(64, np - base);
-    const float2 v = base == 0 ? first : (lane < n ? ml[base + lane] : make_float2(-INFINITY, 0.0f));
+    const float2 v = base == 0 ? v0 : (lane < n ? ml[base + lane] : make_float2(-INFINITY, 0.0f));
     const float wl = v.x == -INFINITY ? 0.0f : v.y * __builtin_amdgcn_exp2f(v.x - M);
     wsum += wl;
-    for (int sub = 0; sub < n; sub += G * kPer) {
-      float4 x[kPer];
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int q = sub + grp + k * G;
-        x[k] = q < n ? po[(size_t)(base + q) * C + c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      }
+    for (int sub = 0; sub < n; sub += SUB) {
+      if (base > 0 || sub > 0) load_sub(base, sub, n);
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
         const float wq = __shfl(wl, (sub + grp + k * G) & 63);  // 0 for q >= n
@@ -97,13 +114,13 @@ template <class QT>
 hipError_t launch_q(const DecodeArgs &a, hipStream_t s) {
   const int rows = a.num_seqs * a.num_q_heads;
   dim3 grid((rows + kRowsPerGroup - 1) / kRowsPerGroup), block(64 * kRowsPerGroup);
-  const bool wide = rows <= 2048 && a.num_partitions > 16;
+  const bool wide = PA_REDUCE_WIDE && rows <= 2048 && a.num_partitions > 16;
   if (a.cache.head_dim == 64) {
     if (wide) partition_reduce_kernel<QT, 64, 16><<<grid, block, 0, s>>>(a);
-    else partition_reduce_kernel<QT, 64, 8><<<grid, block, 0, s>>>(a);
+    else partition_reduce_kernel<QT, 64, 2><<<grid, block, 0, s>>>(a);
   } else {
     if (wide) partition_reduce_kernel<QT, 128, 32><<<grid, block, 0, s>>>(a);
-    else partition_reduce_kernel<QT, 128, 8><<<grid, block, 0, s>>>(a);
+    else partition_reduce_kernel<QT, 128, PA_REDUCE_PER><<<grid, block, 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -330,6 +330,31 @@ def test_poison_outside_the_context_never_leaks():
     assert torch.equal(clean.sets[0].out[0], dirty.sets[0].out[0])
 
 
+def test_stale_workspace_never_leaks():
+    """Workspace slots past a row's own partitions hold whatever earlier calls left there and must
+    never be read: a workspace full of NaN bytes gives the same bits as a zeroed one, for the plain
+    and the shared-prefix decode, with rows of 1, several and all the partitions."""
+    _say("NaN-filled workspace")
+    for name, lengths, ps in (("f16_batch32", [1000, 17, 513, 64, 250], 64),
+                              ("f16_shared_prefix_batch256", [64 + 1, 64 + 300, 64 + 17, 64 + 2],
+                               32)):
+        kw = dict(num_seqs=len(lengths), num_blocks=512)
+        if name == "f16_shared_prefix_batch256":
+            kw["prefix_len"] = 64
+        w = wl.WORKLOADS[name].replace(**kw)
+        b = DecodeBatch(w, lengths=lengths, pad_block=0, partition_size=ps)
+        outs = []
+        for fill in (0, POISON):
+            b.workspace.fill_(fill)
+            b.sets[0].out[0].fill_(0)
+            b.decode(0, 0)
+            torch.cuda.synchronize()
+            outs.append(b.sets[0].out[0].clone())
+        _say(f"  {name}: equal {torch.equal(outs[0], outs[1])}")
+        assert torch.isfinite(outs[1].float()).all()
+        assert torch.equal(outs[0], outs[1])
+
+
 def test_empty_context_and_out_of_range_blocks():
     _say("edge cases")
     w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=3, num_blocks=256)
