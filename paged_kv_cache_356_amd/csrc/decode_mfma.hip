@@ -54,36 +54,40 @@ constexpr int kMaxScanSeqs = 4096;  // persistent grid: sequences whose item pre
 #ifndef PA_DECODE_BUFS
 #define PA_DECODE_BUFS 2
 #endif
-constexpr int kBufs = PA_DECODE_BUFS;  // blocks per wavefront in the load ring
+#ifndef PA_FP8_BUFS
+#define PA_FP8_BUFS 3
+#endif
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1
 #endif
 #ifndef PA_SPREAD
 #define PA_SPREAD 0
 #endif
-#ifndef PA_PRIO
-#define PA_PRIO 1
-#endif
-#ifndef PA_PRIO_SHIFT
-#define PA_PRIO_SHIFT 3  // blocks per priority level
-#endif
 #ifndef PA_DECODE_OCC
 #define PA_DECODE_OCC 3  // at least this many wavefronts per SIMD (caps registers at 168)
 #endif
 
-// K/V tiles are read once per decode step: optionally as non-temporal loads.
+// K/V tiles are read with raw buffer loads through a descriptor per tile: a slot with no block
+// gets a descriptor of length 0, whose loads return zeros without touching memory (and still count
+// in vmcnt, so the ring's waits stay partial).  kNT adds the non-temporal hint (each tile is read
+// once per call).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-template <class T> struct NativeVec { using type = T; };
-template <> struct NativeVec<uint4> { using type = u32x4_t; };
-template <> struct NativeVec<uint2> { using type = u32x2_t; };
+constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, the value raw loads use on gfx9
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *tile, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(tile), (short)0, bytes, kRsrcWord3);
+}
 
 template <class T, bool kNT>
-__device__ __forceinline__ T load_kv(const char *p) {
-  using N = typename NativeVec<T>::type;
-  if constexpr (kNT)
-    return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const N *>(p)));
-  else return *reinterpret_cast<const T *>(p);
+__device__ __forceinline__ T load_kv(__amdgpu_buffer_rsrc_t r, int off) {
+  constexpr int aux = kNT ? 2 : 0;  // 2: nt
+  if constexpr (sizeof(T) == 16)
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, aux));
+  else if constexpr (sizeof(T) == 8)
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, aux));
+  else
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, aux));
 }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNoMax = -3.0e38f;  // running-maximum floor (finite)
@@ -214,21 +218,23 @@ __device__ __forceinline__ void load_query(const DecodeArgs &a, int rs, int rhq,
   for (int nt = 0; nt < D / 16; ++nt) st.acc[nt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
+// The K and V tiles of block bid, KV head h, into f; ok = false (no block in this slot) loads zeros
+// without reading memory.
 template <class CT, int D, bool kNT>
-__device__ __forceinline__ void load_block(const DecodeArgs &a, int bid, int h, Frag<CT, D> &f) {
+__device__ __forceinline__ void load_block(const DecodeArgs &a, int bid, bool ok, int h,
+                                           Frag<CT, D> &f) {
   using F = Frag<CT, D>;
   constexpr int kTileBytes = kBlock * D * CT::bytes;
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-  const size_t tile = ((size_t)bid * a.cache.num_kv_heads + h) * kTileBytes;
-  const char *kt = static_cast<const char *>(a.cache.k_pool) + tile;
-  const char *vt = static_cast<const char *>(a.cache.v_pool) + tile;
+  const size_t tile = ((size_t)(ok ? bid : 0) * a.cache.num_kv_heads + h) * kTileBytes;
+  const int n = ok ? kTileBytes : 0;
+  const auto rk = tile_rsrc(static_cast<const char *>(a.cache.k_pool) + tile, n);
+  const auto rv = tile_rsrc(static_cast<const char *>(a.cache.v_pool) + tile, n);
 #pragma unroll
-  for (int i = 0; i < F::kKLoads; ++i)
-    f.k[i] = load_kv<uint4, kNT>(kt + (size_t)(lane + 64 * i) * 16);
+  for (int i = 0; i < F::kKLoads; ++i) f.k[i] = load_kv<uint4, kNT>(rk, (lane + 64 * i) * 16);
 #pragma unroll
   for (int nt = 0; nt < F::kNT; ++nt)
-    f.v[nt] = load_kv<typename F::VRaw, kNT>(
-        vt + (size_t)((16 * nt + col) * kBlock + 4 * grp) * CT::bytes);
+    f.v[nt] = load_kv<typename F::VRaw, kNT>(rv, ((16 * nt + col) * kBlock + 4 * grp) * CT::bytes);
 }
 
 // One 16-token block at token tok0 into the state.  Scores of positions at or past `zlim` (per
@@ -311,76 +317,113 @@ __device__ __forceinline__ void block_step(const Frag<CT, D> &f, float kscale, i
     }
 }
 
-// The ring: blocks j = jb0 .. jb1 - 1 of table row `table`, KV head h, through kBufs fragments.
-// While one block is computed, the loads of the next kBufs - 1 are in flight.
-// Buffer indices are compile-time constants (the inner loop is unrolled), so the ring needs no
-// copies.  Every slot is loaded and computed on every round, with no branch around either, so each
-// compute waits only for its own slot and the accumulators stay in place: a slot past the end of
-// the range, or whose table entry lies outside the pool, reads tile (0, h) instead (a few
-// L2-resident lines) and is computed fully masked.
-// The wavefront's table entries are fetched before its ring starts, one per lane, and read back with
-// v_readlane: a table read inside the ring would be a vector load whose result feeds the next
-// address, and waiting for it would drain every load in flight.  A wavefront with more than 64
-// blocks runs one ring per 64 of them.
-// Wavefront priority from the blocks it still has to stream: waves sharing a SIMD otherwise
-// issue oldest first, and the youngest one of a compute unit can take half as long again as the
-// oldest over the same work, which sets the kernel's end.  Longest remaining work first evens
-// them out.  (s_setprio takes an immediate, hence the branches; the value is wave-uniform.)
-__device__ __forceinline__ void prio_for_remaining(int blocks_left) {
-#if PA_PRIO
-  const int p = blocks_left >> PA_PRIO_SHIFT;
-  if (p >= 3) __builtin_amdgcn_s_setprio(3);
-  else if (p == 2) __builtin_amdgcn_s_setprio(2);
-  else if (p == 1) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
-#else
-  (void)blocks_left;
-#endif
-}
-
-template <class CT, int D, bool kNT>
-__device__ __forceinline__ void stream_blocks(const DecodeArgs &a, const int32_t *table, int h,
-                                              int jb0, int jb1, int zlim, int vend, float kscale,
-                                              RowState<D> &st) {
-  using F = Frag<CT, D>;
-  const int nb = a.cache.num_blocks;
-  const int lane = threadIdx.x & 63;
-  const int nk = jb1 > jb0 ? jb1 - jb0 : 0;  // this wave's blocks
-  for (int k0 = 0; k0 < nk; k0 += 64) {
-    const int kn = min(64, nk - k0);
-    const int tbl = lane < kn ? table[jb0 + k0 + lane] : -1;
-    // block id of the chunk's k-th block (-1 past the chunk); k is wave-uniform
-    auto entry = [&](int k) { return k < kn ? __builtin_amdgcn_readlane(tbl, k < 64 ? k : 63) : -1; };
-    F buf[kBufs];
-    bool ok[kBufs];
+// An empty asm that reads and writes every register of a fragment: the compiler must wait for the
+// fragment's loads before it.
+template <class CT, int D>
+__device__ __forceinline__ void settle_frag(Frag<CT, D> &f) {
 #pragma unroll
-    for (int b = 0; b < kBufs; ++b) {
-      const int bid = entry(b);
-      ok[b] = (unsigned)bid < (unsigned)nb;  // an entry outside the pool is never dereferenced
-      load_block<CT, D, kNT>(a, ok[b] ? bid : 0, h, buf[b]);
-    }
-    for (int kr = 0; kr < kn; kr += kBufs) {
-      prio_for_remaining(nk - k0 - kr);
+  for (int i = 0; i < Frag<CT, D>::kKLoads; ++i)
+    asm volatile("" : "+v"(f.k[i].x), "+v"(f.k[i].y), "+v"(f.k[i].z), "+v"(f.k[i].w));
 #pragma unroll
-      for (int b = 0; b < kBufs; ++b) {
-        const int t0 = (jb0 + k0 + kr + b) * kBlock;
-        block_step<CT, D>(buf[b], kscale, t0, ok[b] ? zlim : t0, ok[b] ? vend : t0, st);
-        const int bid = entry(kr + b + kBufs);
-        ok[b] = (unsigned)bid < (unsigned)nb;
-        load_block<CT, D, kNT>(a, ok[b] ? bid : 0, h, buf[b]);
-      }
-    }
+  for (int nt = 0; nt < Frag<CT, D>::kNT; ++nt) {
+    if constexpr (sizeof(f.v[nt]) == 8) asm volatile("" : "+v"(f.v[nt].x), "+v"(f.v[nt].y));
+    else asm volatile("" : "+v"(f.v[nt]));
   }
 }
 
+// The ring: blocks j = jb0 .. jb1 - 1 of table row `table`, KV head h, through kBufs fragments.
+// While one block is computed, the loads of the next kBufs - 1 are in flight.
+// Buffer indices are compile-time constants (the inner loop is unrolled), so the ring needs no
+// copies.  The first kBufs slots are loaded unconditionally (a slot past the end through an empty
+// descriptor: zeros, no memory access), and in the full rounds every slot is computed and reloaded
+// with a real block, with no branch around either, so each compute waits only for its own slot
+// (partial s_waitcnt vmcnt) and the accumulators stay in place.  The last one or two rounds are
+// straight-line code that computes and reloads only the blocks that exist: a load issued past the
+// end would have to complete before its registers are reused after the ring, which costs the
+// wavefront a full memory round trip at the end of every item.  A table entry outside the pool is
+// loaded through an empty descriptor too and computed fully masked.
+// The wavefront's table entries are fetched before its ring starts, one per lane, and read back with
+// v_readlane: a table read inside the ring would be a vector load whose result feeds the next
+// address, and waiting for it would drain every load in flight.  A wavefront with more than 64
+// blocks runs one ring per 64 of them.  The first 64 entries (tbl0, from first_table_entries)
+// come from the caller, which can fetch them while the wavefront's previous item streams.
+template <class CT, int D, bool kNT>
+__device__ __forceinline__ void stream_blocks(const DecodeArgs &a, const int32_t *table, int h,
+                                              int jb0, int jb1, int tbl0, int zlim, int vend,
+                                              float kscale, RowState<D> &st) {
+  using F = Frag<CT, D>;
+  // blocks per wavefront in the load ring: fp8 fragments are half the registers of 16-bit ones
+  constexpr int kBufs = std::is_same<CT, fp8_t>::value ? PA_FP8_BUFS : PA_DECODE_BUFS;
+  const int nb = a.cache.num_blocks;
+  const int lane = threadIdx.x & 63;
+  const int nk = jb1 > jb0 ? jb1 - jb0 : 0;  // this wave's blocks
+  // One ring over the chunk of kn <= 64 blocks starting at block k0, with the chunk's table
+  // entries one per lane in tbl.  The first chunk is run on its own, outside the loop over the
+  // others, so that its entries (fetched by the caller) need no wait at a loop header.
+  auto chunk = [&](int k0, int kn, int tbl) {
+    // block id of the chunk's k-th block; k < kn is wave-uniform
+    auto entry = [&](int k) { return __builtin_amdgcn_readlane(tbl, k < 64 ? k : 63); };
+    F buf[kBufs];
+    bool ok[kBufs];
+    auto load = [&](int b, int k) {
+      const int bid = k < kn ? entry(k) : -1;
+      ok[b] = (unsigned)bid < (unsigned)nb;  // an entry outside the pool is never dereferenced
+      load_block<CT, D, kNT>(a, bid, ok[b], h, buf[b]);
+    };
+    auto compute = [&](int b, int k) {
+      const int t0 = (jb0 + k0 + k) * kBlock;
+      block_step<CT, D>(buf[b], kscale, t0, ok[b] ? zlim : t0, ok[b] ? vend : t0, st);
+    };
+#pragma unroll
+    for (int b = 0; b < kBufs; ++b) load(b, b);  // slots past the end: zeros, no memory access
+    int kr = 0;
+    for (; kr + 2 * kBufs <= kn; kr += kBufs) {  // full rounds
+#pragma unroll
+      for (int b = 0; b < kBufs; ++b) {
+        compute(b, kr + b);
+        load(b, kr + b + kBufs);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t, kr += kBufs) {  // what is left: fewer than 2 kBufs blocks
+#pragma unroll
+      for (int b = 0; b < kBufs; ++b) {
+        if (kr + b < kn) {
+          compute(b, kr + b);
+          if (kr + b + kBufs < kn) load(b, kr + b + kBufs);
+        }
+      }
+    }
+    // A slot the chunk never computed still has its (empty) first load pending: wait for it now,
+    // when it is long done, rather than at the next reuse of its registers, where the wait could
+    // not be told apart from one for every memory operation issued since.
+#pragma unroll
+    for (int b = 0; b < kBufs; ++b) settle_frag(buf[b]);
+  };
+  if (nk > 0) chunk(0, min(64, nk), tbl0);
+  for (int k0 = 64; k0 < nk; k0 += 64) {
+    const int kn = min(64, nk - k0);
+    chunk(k0, kn, lane < kn ? table[jb0 + k0 + lane] : -1);
+  }
+}
+
+// Lane i's entry of the first 64 blocks [jb0, jb1) of a table row (-1 past the range).
+__device__ __forceinline__ int first_table_entries(const int32_t *table, int jb0, int jb1) {
+  const int lane = threadIdx.x & 63;
+  return lane < min(64, jb1 - jb0) ? table[jb0 + lane] : -1;
+}
+
+// The per-head scales are read through the constant address space: the kernel never writes them,
+// and scalar loads keep them out of the vector memory counter the block ring waits on.
 template <class CT>
 __device__ __forceinline__ void head_scales(const DecodeArgs &a, int h, float &kscale,
                                             float &vscale) {
   kscale = a.scale * kLog2e;
   vscale = 1.0f;
   if constexpr (std::is_same<CT, fp8_t>::value) {
-    kscale *= a.cache.k_scale[h] * kFp8Unscale;
-    vscale = a.cache.v_scale[h] * kFp8Unscale;
+    using cfloat = const __attribute__((address_space(4))) float;
+    kscale *= ((cfloat *)(uintptr_t)a.cache.k_scale)[h] * kFp8Unscale;
+    vscale = ((cfloat *)(uintptr_t)a.cache.v_scale)[h] * kFp8Unscale;
   }
 }
 
@@ -401,10 +444,14 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs &a, int s) {
 // Wavefronts of one workgroup run their items independently, so one wavefront's item prologue
 // (query, table fetch, first loads) and epilogue overlap the other wavefronts' block streams.
 // kNT: read K/V with non-temporal loads (each tile is read once per call), or with ordinary loads
-// (prefix tiles, whose blocks the other tiles of the batch read too).
+// (prefix tiles, whose blocks the other tiles of the batch read too).  `lens`: the clamped context
+// lengths of the batch (in LDS), read by prefix tiles for their rows' masks.  tbl0: the item's
+// first table entries (first_table_entries of its table row).  settle: a value whose load is in
+// flight (the next item's first table entries), waited for once this item's blocks are done.
 template <class CT, class QT, int D, bool kNT>
 __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int row0_in, int h_in,
-                                          int jb0_in, int jb1_in, int end_in, int slot_in) {
+                                          int jb0_in, int jb1_in, int end_in, int slot_in,
+                                          const int *lens, int tbl0, int &settle) {
   // The item is the same for the whole wavefront: keep its fields (and so the tile addresses) in
   // scalar registers.
   const int s = __builtin_amdgcn_readfirstlane(s_in);
@@ -423,7 +470,7 @@ __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int row
   const bool rvalid = col < nrows;
   const int rs = tile ? (rvalid ? (row0 + col) / g : 0) : s;
   const int rhq = h * g + (rvalid ? (tile ? (row0 + col) % g : col) : 0);
-  const int lim = tile && rvalid ? min(end, clamp_len(a, rs)) : end;
+  const int lim = tile && rvalid ? min(end, lens[rs]) : end;
   const int32_t *table =
       tile ? a.prefix_table : a.block_tables + (size_t)s * a.max_blocks_per_seq;
 
@@ -431,7 +478,15 @@ __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int row
   load_query<CT, D>(a, rs, rhq, rvalid, st);
   float kscale, vscale;
   head_scales<CT>(a, h, kscale, vscale);
-  stream_blocks<CT, D, kNT>(a, table, h, jb0, jb1, lim, end, kscale, st);
+  stream_blocks<CT, D, kNT>(a, table, h, jb0, jb1, tbl0, lim, end, kscale, st);
+  // Wait here, where the ring has nothing left in flight, for every load this item started that its
+  // blocks may not have consumed (the query and table entries of an item without blocks) and for
+  // `settle` (the next item's table entries, fetched before this item started): later, behind this
+  // item's stores, such a wait could not be told apart from a wait for the stores themselves.
+  asm volatile("" : "+v"(settle), "+v"(tbl0));
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    asm volatile("" : "+v"(st.qop[kk].x), "+v"(st.qop[kk].y), "+v"(st.qop[kk].z), "+v"(st.qop[kk].w));
 
   // the row's sum over the four lane groups; m is already uniform over them
   float l = st.l;
@@ -475,22 +530,41 @@ __device__ __forceinline__ int seq_items(const DecodeArgs &a, int L) {
   return L > 0 ? row_partitions(a, L) : 1;
 }
 
-template <class CT, class QT, int D>
-__device__ __forceinline__ void run_sequence_item(const DecodeArgs &a, int s, int part, int h) {
+// Sequence item `part` of sequence s (context length L), KV head h: its blocks [jb0, jb1), the end
+// of its positions and its workspace slot (-1: the output itself).
+struct SeqItem {
+  int s, h, jb0, jb1, end, slot;
+};
+
+__device__ __forceinline__ SeqItem sequence_item(const DecodeArgs &a, int s, int L, int part,
+                                                 int h) {
   const int PT = a.partition_size;
-  const int L = clamp_len(a, s);
+  SeqItem it{s, h, 0, 0, 0, -1};
   int start, end;
   if (a.prefix_len > 0) {
     partition_range(a.prefix_len, L, PT, part, &start, &end);
-    wave_item<CT, QT, D, PA_DECODE_NT>(a, s, 0, h, start / kBlock, (end + kBlock - 1) / kBlock,
-                                       end, a.prefix_chunks + part);
+    it.slot = a.prefix_chunks + part;
   } else if (L > 0) {
     partition_range(0, L, PT, part, &start, &end);
-    wave_item<CT, QT, D, PA_DECODE_NT>(a, s, 0, h, start / kBlock, (end + kBlock - 1) / kBlock,
-                                       end, L > PT ? part : -1);
+    it.slot = L > PT ? part : -1;
   } else {  // empty context: no block, zeros written straight to the output
-    wave_item<CT, QT, D, PA_DECODE_NT>(a, s, 0, h, 0, 0, 0, -1);
+    start = end = 0;
   }
+  it.jb0 = start / kBlock;
+  it.jb1 = (end + kBlock - 1) / kBlock;
+  it.end = end;
+  return it;
+}
+
+__device__ __forceinline__ const int32_t *table_row(const DecodeArgs &a, int s) {
+  return a.block_tables + (size_t)s * a.max_blocks_per_seq;
+}
+
+template <class CT, class QT, int D>
+__device__ __forceinline__ void run_sequence_item(const DecodeArgs &a, const SeqItem &it, int tbl0,
+                                                  int &settle) {
+  wave_item<CT, QT, D, PA_DECODE_NT>(a, it.s, 0, it.h, it.jb0, it.jb1, it.end, it.slot, nullptr,
+                                     tbl0, settle);
 }
 
 // Grid modes.  Direct (plain decode only, more than kMaxScanSeqs sequences): wavefront
@@ -523,17 +597,27 @@ void decode_mfma_kernel(DecodeArgs a) {
     if (s >= S) return;
     const int L = clamp_len(a, (int)s);
     const int n = L > 0 ? (L + PT - 1) / PT : 1;
-    if (part < n) run_sequence_item<CT, QT, D>(a, (int)s, part, h);
+    if (part < n) {
+      const SeqItem it = sequence_item(a, (int)s, L, part, h);
+      int none = 0;
+      run_sequence_item<CT, QT, D>(a, it, first_table_entries(table_row(a, it.s), it.jb0, it.jb1),
+                                   none);
+    }
     return;
   }
   __shared__ int prefix[kMaxScanSeqs + 1];  // items of the sequences before s
+  __shared__ int lens[kMaxScanSeqs];        // clamped context lengths
   __shared__ int wave_tot[kWaves];
   // thread t counts the items of sequences [t * per, (t + 1) * per)
   const int per = (S + 255) / 256;
   const int s0 = tid * per;
   int mine = 0;
   for (int i = 0; i < per; ++i)
-    if (s0 + i < S) mine += seq_items(a, clamp_len(a, s0 + i));
+    if (s0 + i < S) {
+      const int L = clamp_len(a, s0 + i);
+      lens[s0 + i] = L;
+      mine += seq_items(a, L);
+    }
   int incl = mine;  // inclusive scan over the wavefront
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -548,7 +632,7 @@ void decode_mfma_kernel(DecodeArgs a) {
     const int s = s0 + i;
     if (s < S) {
       prefix[s] = run;
-      run += seq_items(a, clamp_len(a, s));
+      run += seq_items(a, lens[s]);
     }
   }
   if (tid == 255) prefix[S] = run;  // thread 255 holds the grand total (its chunk ends at S or later)
@@ -564,7 +648,10 @@ void decode_mfma_kernel(DecodeArgs a) {
     if (row0 >= S * g) continue;  // the last group's unused tiles
     const int start = c * kPrefixChunk;
     const int end = min(a.prefix_len, start + kPrefixChunk);
-    wave_item<CT, QT, D, false>(a, -1, row0, h, start / kBlock, end / kBlock, end, c);
+    int none = 0;
+    wave_item<CT, QT, D, false>(a, -1, row0, h, start / kBlock, end / kBlock, end, c, lens,
+                                first_table_entries(a.prefix_table, start / kBlock, end / kBlock),
+                                none);
   }
   // The sequences' items, one per wavefront.  Wavefronts are ranked so that those of workgroups
   // without prefix work come first, each class wavefront-major (wavefront w of every workgroup
@@ -578,7 +665,7 @@ void decode_mfma_kernel(DecodeArgs a) {
                                      : w * (G - busy) + (blockIdx.x - busy);
   const int total = __builtin_amdgcn_readfirstlane(prefix[S]) * H;
   const int GW = G * kWaves;
-  for (int f = rank; f < total; f += GW) {
+  auto item_of = [&](int f) {
     const int pf = f / H;
     const int h = f - pf * H;
     int lo = 0, hi = S - 1;  // largest s with prefix[s] <= pf (LDS values, made uniform)
@@ -587,7 +674,27 @@ void decode_mfma_kernel(DecodeArgs a) {
       if (__builtin_amdgcn_readfirstlane(prefix[mid]) <= pf) lo = mid;
       else hi = mid - 1;
     }
-    run_sequence_item<CT, QT, D>(a, lo, pf - __builtin_amdgcn_readfirstlane(prefix[lo]), h);
+    return sequence_item(a, lo, __builtin_amdgcn_readfirstlane(lens[lo]),
+                         pf - __builtin_amdgcn_readfirstlane(prefix[lo]), h);
+  };
+  // The next item's coordinates and first table entries are fetched before the current item
+  // streams, so an item starts with one round trip to memory (its first blocks, with its query)
+  // instead of three (context length, table, blocks).
+  if (rank < total) {
+    SeqItem it = item_of(rank);
+    int tbl = first_table_entries(table_row(a, it.s), it.jb0, it.jb1);
+    asm volatile("" : "+v"(tbl));  // waited for here, once, not at the loop header every item
+    for (int f = rank; f < total; f += GW) {
+      SeqItem next = it;
+      int tbl_next = -1;
+      if (f + GW < total) {
+        next = item_of(f + GW);
+        tbl_next = first_table_entries(table_row(a, next.s), next.jb0, next.jb1);
+      }
+      run_sequence_item<CT, QT, D>(a, it, tbl, tbl_next);
+      it = next;
+      tbl = tbl_next;
+    }
   }
 }
 
