@@ -188,7 +188,6 @@ def main() -> int:
     log(f"[bench] {w.name}: built {sets} set(s), {len(batch.layers)} layer(s) in "
         f"{time.perf_counter() - t_build:.1f} s; lengths {wl.lengths_summary(batch.lengths)}")
 
-    caches = [batch.caches[l] for l in batch.layers]
     layers = batch.layers
 
     # Every library call enqueues on torch's current stream: the default stream when run eagerly,
@@ -196,11 +195,9 @@ def main() -> int:
     def step(r: int):
         """One step of set r: the copy-on-write clone, then per layer the new token's K/V write and
         the decode attention."""
-        st = batch.sets[r]
-        if st.pairs.shape[0]:
-            api.pa_copy_blocks(caches, st.d_pairs)
+        batch.copy(r)
         for l in layers:
-            api.pa_reshape_and_cache(batch.caches[l], st.new_k[l], st.new_v[l], st.d_slots)
+            batch.reshape(r, l)
             batch.decode(r, l, flags=flags)
 
     def decodes(n: int):

@@ -117,9 +117,18 @@ def _ptr(t) -> int | None:
     return int(t)
 
 
+_have_gpu = None
+
+
 def _stream(stream) -> int | None:
+    """The hipStream_t to enqueue on: torch's current stream when `stream` is None."""
+    global _have_gpu
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+        if _have_gpu is None:
+            _have_gpu = torch.cuda.is_available()
+        if not _have_gpu:
+            return None
+        return torch._C._cuda_getCurrentRawStream(torch._C._cuda_getDevice())
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -146,9 +155,15 @@ class KVCache:
                        head_dim, code, k_scale, v_scale)
 
     def struct(self) -> pa_cache:
-        return pa_cache(_ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.k_scale),
-                        _ptr(self.v_scale), self.num_blocks, PA_BLOCK_SIZE, self.num_kv_heads,
-                        self.head_dim, self.cache_dtype)
+        """The pa_cache of this layer (built once; rebuilt if a pool tensor was replaced)."""
+        key = (_ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.k_scale), _ptr(self.v_scale),
+               self.num_blocks, self.num_kv_heads, self.head_dim, self.cache_dtype)
+        c = self.__dict__.get("_c")
+        if c is None or self.__dict__.get("_key") != key:
+            c = pa_cache(key[0], key[1], key[2], key[3], self.num_blocks, PA_BLOCK_SIZE,
+                         self.num_kv_heads, self.head_dim, self.cache_dtype)
+            self.__dict__["_c"], self.__dict__["_key"] = c, key
+        return c
 
 
 def pool_bytes(num_blocks, num_kv_heads, head_dim, cache_dtype) -> int:
@@ -161,18 +176,31 @@ def pool_bytes(num_blocks, num_kv_heads, head_dim, cache_dtype) -> int:
 
 
 # --------------------------------------------------------------------------- kernels
+class ReshapeCall:
+    """pa_reshape_and_cache with every argument but the stream fixed: the checks and conversions
+    are done once, when the call is made, for loops that repeat it."""
+
+    def __init__(self, cache: KVCache, key: torch.Tensor, value: torch.Tensor,
+                 slot_mapping: torch.Tensor):
+        assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
+        T = slot_mapping.shape[0]
+        assert key.dtype == value.dtype and key.shape[0] == T and value.shape[0] == T
+        for t in (key, value):  # rows [num_kv_heads, head_dim] contiguous, strided along T
+            assert t.dim() == 3 and t.stride(2) == 1 and t.stride(1) == t.shape[2]
+        self._keep = (cache, key, value, slot_mapping)
+        self._args = (ctypes.byref(cache.struct()), _ptr(key), _ptr(value),
+                      TORCH_CODES[key.dtype], key.stride(0) if T else 0,
+                      value.stride(0) if T else 0, _ptr(slot_mapping), T)
+        self._fn = lib().pa_reshape_and_cache
+
+    def __call__(self, stream=None) -> None:
+        _check(self._fn(*self._args, _stream(stream)))
+
+
 def pa_reshape_and_cache(cache: KVCache, key: torch.Tensor, value: torch.Tensor,
                          slot_mapping: torch.Tensor, stream=None) -> None:
     """key/value: [T, num_kv_heads, head_dim] (rows may be strided along T); slot_mapping int64 [T]."""
-    assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
-    T = slot_mapping.shape[0]
-    assert key.dtype == value.dtype and key.shape[0] == T and value.shape[0] == T
-    assert key[0].is_contiguous() and value[0].is_contiguous() if T else True
-    c = cache.struct()
-    _check(lib().pa_reshape_and_cache(ctypes.byref(c), _ptr(key), _ptr(value),
-                                      TORCH_CODES[key.dtype], key.stride(0) if T else 0,
-                                      value.stride(0) if T else 0, _ptr(slot_mapping), T,
-                                      _stream(stream)))
+    ReshapeCall(cache, key, value, slot_mapping)(stream)
 
 
 def pa_decode_auto_partition(num_seqs, num_kv_heads, max_context_len) -> int:
@@ -185,6 +213,39 @@ def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max
                                            max_context_len, partition_size)
 
 
+class DecodeCall:
+    """pa_decode_attention, or pa_decode_attention_shared_prefix when prefix_table is given, with
+    every argument but the stream fixed: the checks and conversions are done once, when the call is
+    made, for loops that repeat it (a decode step per layer)."""
+
+    def __init__(self, out: torch.Tensor, query: torch.Tensor, cache: KVCache,
+                 block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                 scale: float, partition_size: int = 0, workspace: torch.Tensor | None = None,
+                 flags: int = PA_DECODE_DEFAULT, prefix_table: torch.Tensor | None = None,
+                 prefix_len: int = 0):
+        S, Hq, D = query.shape
+        assert out.shape == query.shape and out.dtype == query.dtype and out.is_contiguous()
+        assert query.stride(2) == 1 and query.stride(1) == D  # rows contiguous, strided along S
+        assert block_tables.dtype == torch.int32 and block_tables.is_contiguous()
+        assert context_lens.dtype == torch.int32 and context_lens.is_contiguous()
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        head = (_ptr(out), _ptr(query), TORCH_CODES[query.dtype], query.stride(0) if S else 0,
+                ctypes.byref(cache.struct()), _ptr(block_tables), block_tables.shape[1],
+                _ptr(context_lens), S, Hq, int(max_context_len), float(scale))
+        tail = (int(partition_size), _ptr(workspace), ws_bytes, int(flags))
+        self._keep = (out, query, cache, block_tables, context_lens, workspace, prefix_table)
+        if prefix_table is None:
+            self._fn = lib().pa_decode_attention
+            self._args = head + tail
+        else:
+            assert prefix_table.dtype == torch.int32 and prefix_table.is_contiguous()
+            self._fn = lib().pa_decode_attention_shared_prefix
+            self._args = head + (_ptr(prefix_table), int(prefix_len)) + tail
+
+    def __call__(self, stream=None) -> None:
+        _check(self._fn(*self._args, _stream(stream)))
+
+
 def pa_decode_attention(out: torch.Tensor, query: torch.Tensor, cache: KVCache,
                         block_tables: torch.Tensor, context_lens: torch.Tensor,
                         max_context_len: int, scale: float, partition_size: int = 0,
@@ -192,19 +253,8 @@ def pa_decode_attention(out: torch.Tensor, query: torch.Tensor, cache: KVCache,
                         stream=None) -> None:
     """out, query: [S, num_q_heads, head_dim] (query rows may be strided along S);
     block_tables int32 [S, max_blocks_per_seq]; context_lens int32 [S]."""
-    S, Hq, D = query.shape
-    assert out.shape == query.shape and out.dtype == query.dtype and out.is_contiguous()
-    assert query[0].is_contiguous() if S else True
-    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous()
-    assert context_lens.dtype == torch.int32 and context_lens.is_contiguous()
-    c = cache.struct()
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pa_decode_attention(_ptr(out), _ptr(query), TORCH_CODES[query.dtype],
-                                     query.stride(0) if S else 0, ctypes.byref(c),
-                                     _ptr(block_tables), block_tables.shape[1],
-                                     _ptr(context_lens), S, Hq, int(max_context_len), float(scale),
-                                     int(partition_size), _ptr(workspace), ws_bytes, int(flags),
-                                     _stream(stream)))
+    DecodeCall(out, query, cache, block_tables, context_lens, max_context_len, scale,
+               partition_size, workspace, flags)(stream)
 
 
 def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
@@ -224,27 +274,27 @@ def pa_decode_attention_shared_prefix(out: torch.Tensor, query: torch.Tensor, ca
                                       flags: int = PA_DECODE_DEFAULT, stream=None) -> None:
     """pa_decode_attention for a batch sharing its first prefix_len positions (the blocks in
     prefix_table, device int32 [prefix_len / 16])."""
-    S, Hq, D = query.shape
-    assert out.shape == query.shape and out.dtype == query.dtype and out.is_contiguous()
-    assert query[0].is_contiguous() if S else True
-    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous()
-    assert context_lens.dtype == torch.int32 and context_lens.is_contiguous()
-    assert prefix_table.dtype == torch.int32 and prefix_table.is_contiguous()
-    c = cache.struct()
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pa_decode_attention_shared_prefix(
-        _ptr(out), _ptr(query), TORCH_CODES[query.dtype], query.stride(0) if S else 0,
-        ctypes.byref(c), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, Hq,
-        int(max_context_len), float(scale), _ptr(prefix_table), int(prefix_len),
-        int(partition_size), _ptr(workspace), ws_bytes, int(flags), _stream(stream)))
+    DecodeCall(out, query, cache, block_tables, context_lens, max_context_len, scale,
+               partition_size, workspace, flags, prefix_table, prefix_len)(stream)
+
+
+class CopyCall:
+    """pa_copy_blocks with every argument but the stream fixed (checks and conversions done once)."""
+
+    def __init__(self, caches: list[KVCache], block_pairs: torch.Tensor):
+        assert block_pairs.dtype == torch.int32 and block_pairs.is_contiguous()
+        arr = (pa_cache * len(caches))(*[c.struct() for c in caches])
+        self._keep = (caches, block_pairs, arr)
+        self._args = (arr, len(caches), _ptr(block_pairs), block_pairs.shape[0])
+        self._fn = lib().pa_copy_blocks
+
+    def __call__(self, stream=None) -> None:
+        _check(self._fn(*self._args, _stream(stream)))
 
 
 def pa_copy_blocks(caches: list[KVCache], block_pairs: torch.Tensor, stream=None) -> None:
     """block_pairs: device int32 [P, 2] of (src, dst); every layer in `caches` is copied."""
-    assert block_pairs.dtype == torch.int32 and block_pairs.is_contiguous()
-    P = block_pairs.shape[0]
-    arr = (pa_cache * len(caches))(*[c.struct() for c in caches])
-    _check(lib().pa_copy_blocks(arr, len(caches), _ptr(block_pairs), P, _stream(stream)))
+    CopyCall(caches, block_pairs)(stream)
 
 
 def pa_check_copy_pairs(pairs: np.ndarray, num_blocks: int) -> None:

@@ -138,38 +138,60 @@ class DecodeBatch:
         self.use_prefix = self.prefix_len > 0
 
     # ------------------------------------------------------------------ the step
-    def run_step(self, set_index: int = 0, flags: int = api.PA_DECODE_DEFAULT, stream=None):
+    # The library calls of a step are prepared once per (set, layer) and replayed (api.*Call): the
+    # tensors of a set never move, so only the stream is looked up per call.
+    def _call(self, key, make):
+        calls = self.__dict__.setdefault("_calls", {})
+        c = calls.get(key)
+        if c is None:
+            c = calls[key] = make()
+        return c
+
+    def copy(self, set_index: int, layers=None, stream=None):
+        """The step's copy-on-write clones (no call when the set has no pairs)."""
         st = self.sets[set_index]
-        if st.pairs.shape[0]:
-            api.pa_copy_blocks([self.caches[l] for l in self.layers], st.d_pairs, stream)
+        if not st.pairs.shape[0]:
+            return
+        ls = tuple(self.layers if layers is None else layers)
+        self._call(("copy", set_index, ls),
+                   lambda: api.CopyCall([self.caches[l] for l in ls], st.d_pairs))(stream)
+
+    def reshape(self, set_index: int, layer: int, stream=None):
+        """The step's reshape_and_cache of the new token's K/V for one layer."""
+        st = self.sets[set_index]
+        self._call(("reshape", set_index, layer),
+                   lambda: api.ReshapeCall(self.caches[layer], st.new_k[layer], st.new_v[layer],
+                                           st.d_slots))(stream)
+
+    def run_step(self, set_index: int = 0, flags: int = api.PA_DECODE_DEFAULT, stream=None):
+        self.copy(set_index, stream=stream)
         for l in self.layers:
             self.run_layer(set_index, l, flags=flags, stream=stream, copy=False)
 
     def run_layer(self, set_index: int, layer: int, flags: int = api.PA_DECODE_DEFAULT,
                   stream=None, copy: bool = True, reshape: bool = True):
-        st = self.sets[set_index]
-        cache = self.caches[layer]
-        if copy and st.pairs.shape[0]:
-            api.pa_copy_blocks([cache], st.d_pairs, stream)
+        if copy:
+            self.copy(set_index, [layer], stream)
         if reshape:
-            api.pa_reshape_and_cache(cache, st.new_k[layer], st.new_v[layer], st.d_slots, stream)
+            self.reshape(set_index, layer, stream)
         self.decode(set_index, layer, flags=flags, stream=stream)
 
     def decode(self, set_index: int, layer: int, flags: int = api.PA_DECODE_DEFAULT, stream=None,
                out: torch.Tensor | None = None):
         """The step's attention call for one layer (shared-prefix decode when use_prefix)."""
         st = self.sets[set_index]
-        cache = self.caches[layer]
-        out = st.out[layer] if out is None else out
-        if self.use_prefix:
-            api.pa_decode_attention_shared_prefix(
-                out, st.q[layer], cache, st.d_tables, st.d_ctx, self.max_context_len,
-                self.w.scale, self.prefix_tables[set_index], self.prefix_len,
-                self.partition_size, self.workspace, flags, stream)
-        else:
-            api.pa_decode_attention(out, st.q[layer], cache, st.d_tables, st.d_ctx,
-                                    self.max_context_len, self.w.scale, self.partition_size,
-                                    self.workspace, flags, stream)
+
+        def make(o):
+            pre = dict(prefix_table=self.prefix_tables[set_index], prefix_len=self.prefix_len) \
+                if self.use_prefix else {}
+            return api.DecodeCall(o, st.q[layer], self.caches[layer], st.d_tables, st.d_ctx,
+                                  self.max_context_len, self.w.scale, self.partition_size,
+                                  self.workspace, flags, **pre)
+        if out is not None:
+            make(out)(stream)
+            return
+        key = ("decode", set_index, layer, flags, self.use_prefix, self.partition_size)
+        self._call(key, lambda: make(st.out[layer]))(stream)
 
     # ------------------------------------------------------------------ accounting
     def kv_bytes_per_layer(self, unique: bool = False) -> int:
