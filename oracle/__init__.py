@@ -212,5 +212,25 @@ def copy_blocks(k_pools, v_pools, block_bytes, num_blocks, pairs):
     lib().orc_copy_blocks(kp, vp, n, block_bytes, num_blocks, _ptr(pairs), pairs.shape[0])
 
 
+def swap_blocks(dev_pools, host_pools, block_bytes: int, num_blocks: int, num_host: int, pairs,
+                to_host: bool) -> None:
+    """Evicting blocks to CPU memory and bringing them back ("PagedAttention, Visualized", Part 3,
+    the OS table: swapping to disk).  dev_pools / host_pools: per layer, per K and V, flat uint8
+    arrays of num_blocks / num_host blocks of block_bytes.  For each (device block, host slot) pair,
+    in order and for every pool, the block's bytes are copied to the slot (to_host) or back.
+    Pairs naming a block or slot outside its pool are skipped."""
+    pairs = np.asarray(pairs, np.int64).reshape(-1, 2)
+    for d, h in pairs:
+        if not (0 <= d < num_blocks and 0 <= h < num_host):
+            continue
+        for dev, host in zip(dev_pools, host_pools):
+            ds = slice(int(d) * block_bytes, (int(d) + 1) * block_bytes)
+            hs = slice(int(h) * block_bytes, (int(h) + 1) * block_bytes)
+            if to_host:
+                host[hs] = dev[ds]
+            else:
+                dev[ds] = host[hs]
+
+
 def max_threads() -> int:
     return lib().orc_max_threads()

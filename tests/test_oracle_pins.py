@@ -491,3 +491,25 @@ def test_copy_blocks_skips_out_of_range_pairs_and_touches_nothing_else():
     blk = H * 16 * D
     assert np.array_equal(kp[3 * blk:], k0[:blk]) and np.array_equal(vp[3 * blk:], v0[:blk])
     assert np.array_equal(kp[: 3 * blk], k0[: 3 * blk]) and np.array_equal(vp[: 3 * blk], v0[: 3 * blk])
+
+
+def test_swap_replay_copies_whole_blocks_both_ways():
+    """Swapping: a block's bytes go to its host slot and come back unchanged; other bytes of either
+    pool are untouched; pairs outside a pool are skipped."""
+    g = np.random.default_rng(7)
+    bb, nb, nh = 24, 6, 3
+    dev = [g.integers(0, 256, nb * bb).astype(np.uint8) for _ in range(4)]  # 2 layers x K, V
+    host = [np.zeros(nh * bb, np.uint8) for _ in range(4)]
+    orig = [x.copy() for x in dev]
+    oracle.swap_blocks(dev, host, bb, nb, nh, [(4, 2), (0, 0), (nb, 1), (1, nh)], True)
+    for x, hx in zip(orig, host):
+        assert np.array_equal(hx[2 * bb:3 * bb], x[4 * bb:5 * bb])
+        assert np.array_equal(hx[0:bb], x[0:bb])
+        assert not hx[bb:2 * bb].any()  # slot 1: its pair named a block outside the pool
+    for x in dev:
+        x[:] = 0
+    oracle.swap_blocks(dev, host, bb, nb, nh, [(5, 2), (3, 0)], False)
+    for x, o in zip(dev, orig):
+        assert np.array_equal(x[5 * bb:6 * bb], o[4 * bb:5 * bb])
+        assert np.array_equal(x[3 * bb:4 * bb], o[0:bb])
+        assert not x[:3 * bb].any() and not x[4 * bb:5 * bb].any()
