@@ -123,6 +123,50 @@ def cpu_baseline(batch, budget_s: float) -> dict:
                       f"{len(take) * reps / el:.3f}"}
 
 
+def swap_bench(args, torch, api, wl, DecodeBatch) -> int:
+    """Evict every other sequence of the workload's batch to pinned host memory and bring it back
+    (pa_bm_swap_out / pa_swap_blocks, then pa_bm_swap_in / pa_swap_blocks), timed with HIP events on
+    the launch stream.  Bytes = pairs x layers x 2 pools x block bytes."""
+    w = wl.WORKLOADS[args.workload]
+    if args.num_blocks:
+        w = w.replace(num_blocks=args.num_blocks)
+    b = DecodeBatch(w, device="cuda", num_sets=1)
+    torch.cuda.synchronize()
+    caches = [b.caches[l] for l in b.layers]
+    st = b.sets[0]
+    victims = st.seqs[::2]
+    need = sum(len(b.bm.table(s)) for s in victims)
+    host = api.HostPools(caches, need)
+    b.bm.set_host_blocks(need)
+    out_pairs = np.concatenate([b.bm.swap_out(s) for s in victims]).astype(np.int32)
+    in_pairs = np.concatenate([b.bm.swap_in(s) for s in victims]).astype(np.int32)
+    d_out, d_in = torch.from_numpy(out_pairs).cuda(), torch.from_numpy(in_pairs).cuda()
+    calls = {"out": api.SwapCall(caches, host, d_out, True),
+             "in": api.SwapCall(caches, host, d_in, False)}
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, call in calls.items():
+        call()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        ev0.record(stream)
+        for _ in range(reps):
+            call()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        sec = ev0.elapsed_time(ev1) / 1e3 / reps
+        npairs = len(out_pairs) if name == "out" else len(in_pairs)
+        nbytes = npairs * len(caches) * 2 * host.block_bytes
+        res[name] = {"pairs": npairs, "bytes": nbytes, "us": round(sec * 1e6, 2),
+                     "GB_per_s": round(nbytes / sec / 1e9, 2)}
+    print(json.dumps({"metric": "swap to/from pinned host memory (pa_swap_blocks)",
+                      "workload": f"{w.name}: every other sequence of the batch, unshared blocks",
+                      "layers": len(caches), "block_bytes": host.block_bytes,
+                      "swap_out": res["out"], "swap_in": res["in"]}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +185,9 @@ def main() -> int:
                     help="shared-prefix workload: use the plain decode instead of the shared-prefix one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--swap", action="store_true",
+                    help="measure swapping half of the workload's sequences to pinned host memory "
+                         "and back (pa_swap_blocks), print that line and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB a few times (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -173,6 +220,8 @@ def main() -> int:
                           "copies": 3}), flush=True)
         return 0
     api.lib()
+    if args.swap:
+        return swap_bench(args, torch, api, wl, DecodeBatch)
     w = wl.WORKLOADS[args.workload]
     if args.num_blocks:
         w = w.replace(num_blocks=args.num_blocks)

@@ -242,6 +242,29 @@ pa_status pa_copy_blocks(const pa_cache *layers, int32_t num_layers, const int32
 pa_status pa_check_copy_pairs(const int32_t *block_pairs_host, int32_t num_pairs,
                               int32_t num_blocks);
 
+/*
+ * pa_swap_blocks — evicting blocks to CPU memory and bringing them back, the KV cache's swapping
+ * to disk ([Visualized] Part 3, the OS-to-PagedAttention table and the paragraph after it).  For
+ * every (device block, host slot) pair and every layer, all KV heads of the device block are copied
+ * to the host slot (to_host != 0) or the host slot's bytes back to the device block (to_host == 0),
+ * in both pools, bit for bit.  The pairs come from pa_bm_swap_out / pa_bm_swap_in.
+ *
+ *   layers        HOST array of num_layers pa_cache descriptions with identical shape and dtype.
+ *   host_k, host_v  HOST arrays of num_layers pointers to pinned host memory (hipHostMalloc /
+ *                 torch pin_memory) of num_host_blocks * block bytes each, a block laid out as in
+ *                 the device pool (block bytes = pa_pool_bytes / num_blocks).  The library checks
+ *                 with hipPointerGetAttributes that the device can reach each one and refuses the
+ *                 call otherwise (PA_ERR_UNSUPPORTED).
+ *   block_pairs   int32 [num_pairs][2] = {device block, host slot} in device memory or pinned host
+ *                 memory; pairs with an id outside [0, num_blocks) or [0, num_host_blocks) are
+ *                 skipped.  Device blocks must be distinct, and host slots too (a race otherwise).
+ * The copy is enqueued on `stream` like every other call; the host side of a swap-out may be read
+ * only after the stream has reached it.
+ */
+pa_status pa_swap_blocks(const pa_cache *layers, int32_t num_layers, void *const *host_k,
+                         void *const *host_v, int32_t num_host_blocks, const int32_t *block_pairs,
+                         int32_t num_pairs, int32_t to_host, void *stream);
+
 const char *pa_status_string(pa_status status);
 const char *pa_last_error(void); /* thread-local text of the last failure on this thread */
 
@@ -255,8 +278,12 @@ const char *pa_last_error(void); /* thread-local text of the last failure on thi
  *   - fork() makes a child whose table points at all of the parent's blocks, each reference count
  *     +1 ([Visualized] Part 3 shared prefix blocks; [Digest] copy-on-write section).
  *   - append() into a block whose count is above 1 clones it first ([Digest] copy-on-write).
- * Free list: a stack.  The initial order is given by the caller (free_order[0] is handed out
- * first); a freed block is pushed on top and is the next one handed out.
+ *   - swap_out() evicts a sequence's blocks to host slots, except the shared ones, which stay on
+ *     the device because another sequence still needs them; swap_in() brings them back
+ *     ([Visualized] Part 3, OS table: swapping to disk is evicting blocks to CPU memory).
+ * Free lists: stacks.  The initial device order is given by the caller (free_order[0] is handed
+ * out first), host slots are handed out 0, 1, 2, ... at first; a freed entry is pushed on top and
+ * is the next one handed out.
  * ------------------------------------------------------------------------------------------ */
 typedef struct pa_bm pa_bm;
 
@@ -292,8 +319,29 @@ int32_t pa_bm_refcount(const pa_bm *bm, int32_t block); /* -1 for a bad id */
 int32_t pa_bm_num_free(const pa_bm *bm);
 int32_t pa_bm_seq_len(const pa_bm *bm, int32_t seq);    /* context length, -1 for a bad id */
 
+/* Host slots for swapped-out blocks: num_host_blocks of them, 0 handed out first.  PA_ERR_STATE
+ * while a sequence is swapped out. */
+pa_status pa_bm_set_host_blocks(pa_bm *bm, int32_t num_host_blocks);
+
+/* Evict `seq` (resident): each table entry whose block has count 1, in table order, gets a host
+ * slot; the pair {block, slot} is written to pairs (cap rows), the device block is freed and the
+ * entry becomes the slot.  Shared blocks stay on the device and keep seq's reference.  *num_pairs
+ * = the number of moves.  Nothing changes on PA_ERR_SHAPE (cap too small) or PA_ERR_NO_BLOCKS
+ * (too few free host slots).  A swapped-out sequence cannot append, fork or be exported until
+ * pa_bm_swap_in; pa_bm_free_seq returns its host slots. */
+pa_status pa_bm_swap_out(pa_bm *bm, int32_t seq, int32_t *pairs, int32_t cap, int32_t *num_pairs);
+
+/* Bring `seq` back: each host-slot entry, in table order, gets a fresh device block; the pair
+ * {block, slot} is written to pairs, the slot is freed and the entry becomes the block.  Nothing
+ * changes on PA_ERR_SHAPE (cap too small) or PA_ERR_NO_BLOCKS (too few free device blocks). */
+pa_status pa_bm_swap_in(pa_bm *bm, int32_t seq, int32_t *pairs, int32_t cap, int32_t *num_pairs);
+
+int32_t pa_bm_num_free_host(const pa_bm *bm);
+int32_t pa_bm_is_swapped(const pa_bm *bm, int32_t seq); /* 1 out, 0 resident, -1 bad id */
+
 /* Copy seq's table into out[0..cap); *num_blocks = its length in blocks (may exceed cap; only
- * min(cap, length) entries are written). */
+ * min(cap, length) entries are written).  For a swapped-out sequence, entries that were moved hold
+ * host slot ids. */
 pa_status pa_bm_block_table(const pa_bm *bm, int32_t seq, int32_t *out, int32_t cap,
                             int32_t *num_blocks);
 

@@ -32,6 +32,8 @@ EXPORTS = [
     "pa_pool_bytes", "pa_reshape_and_cache", "pa_decode_auto_partition",
     "pa_decode_workspace_bytes", "pa_decode_attention", "pa_decode_attention_shared_prefix",
     "pa_decode_shared_prefix_workspace_bytes", "pa_copy_blocks", "pa_check_copy_pairs",
+    "pa_swap_blocks", "pa_bm_set_host_blocks", "pa_bm_swap_out", "pa_bm_swap_in",
+    "pa_bm_num_free_host", "pa_bm_is_swapped",
     "pa_status_string", "pa_last_error", "pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq",
     "pa_bm_fork", "pa_bm_append", "pa_bm_append_batch", "pa_bm_free_seq", "pa_bm_refcount",
     "pa_bm_num_free", "pa_bm_seq_len", "pa_bm_block_table", "pa_bm_export",
@@ -79,6 +81,12 @@ def lib() -> ctypes.CDLL:
                                                               _i32]),
             "pa_copy_blocks": (_i32, [_cp, _i32, _vp, _i32, _vp]),
             "pa_check_copy_pairs": (_i32, [_vp, _i32, _i32]),
+            "pa_swap_blocks": (_i32, [_cp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp]),
+            "pa_bm_set_host_blocks": (_i32, [_vp, _i32]),
+            "pa_bm_swap_out": (_i32, [_vp, _i32, _vp, _i32, _vp]),
+            "pa_bm_swap_in": (_i32, [_vp, _i32, _vp, _i32, _vp]),
+            "pa_bm_num_free_host": (_i32, [_vp]),
+            "pa_bm_is_swapped": (_i32, [_vp, _i32]),
             "pa_status_string": (ctypes.c_char_p, [_i32]),
             "pa_last_error": (ctypes.c_char_p, []),
             "pa_bm_create": (_vp, [_i32, _i32, _vp]),
@@ -297,6 +305,46 @@ def pa_copy_blocks(caches: list[KVCache], block_pairs: torch.Tensor, stream=None
     CopyCall(caches, block_pairs)(stream)
 
 
+class HostPools:
+    """Pinned host memory for swapped-out blocks: per layer, a K and a V pool of num_host_blocks
+    blocks laid out as in the layer's device pool."""
+
+    def __init__(self, caches: list[KVCache], num_host_blocks: int):
+        c = caches[0]
+        self.num_host_blocks = num_host_blocks
+        self.block_bytes = pool_bytes(c.num_blocks, c.num_kv_heads, c.head_dim,
+                                      c.cache_dtype) // max(c.num_blocks, 1)
+        n = max(num_host_blocks * self.block_bytes, 1)
+        self.k = [torch.empty(n, dtype=torch.uint8, pin_memory=True) for _ in caches]
+        self.v = [torch.empty(n, dtype=torch.uint8, pin_memory=True) for _ in caches]
+
+
+class SwapCall:
+    """pa_swap_blocks with every argument but the stream fixed (checks and conversions done once)."""
+
+    def __init__(self, caches: list[KVCache], host: HostPools, block_pairs: torch.Tensor,
+                 to_host: bool):
+        assert block_pairs.dtype == torch.int32 and block_pairs.is_contiguous()
+        assert len(host.k) == len(caches)
+        arr = (pa_cache * len(caches))(*[c.struct() for c in caches])
+        hk = (ctypes.c_void_p * len(caches))(*[_ptr(t) for t in host.k])
+        hv = (ctypes.c_void_p * len(caches))(*[_ptr(t) for t in host.v])
+        self._keep = (caches, host, block_pairs, arr, hk, hv)
+        self._args = (arr, len(caches), hk, hv, host.num_host_blocks, _ptr(block_pairs),
+                      block_pairs.shape[0], int(bool(to_host)))
+        self._fn = lib().pa_swap_blocks
+
+    def __call__(self, stream=None) -> None:
+        _check(self._fn(*self._args, _stream(stream)))
+
+
+def pa_swap_blocks(caches: list[KVCache], host: HostPools, block_pairs: torch.Tensor,
+                   to_host: bool, stream=None) -> None:
+    """block_pairs: int32 [P, 2] of (device block, host slot) in device or pinned host memory; every
+    layer in `caches` is copied to its host pools (to_host) or back."""
+    SwapCall(caches, host, block_pairs, to_host)(stream)
+
+
 def pa_check_copy_pairs(pairs: np.ndarray, num_blocks: int) -> None:
     pairs = np.ascontiguousarray(pairs, np.int32).reshape(-1, 2)
     _check(lib().pa_check_copy_pairs(_ptr(pairs), pairs.shape[0], num_blocks))
@@ -354,6 +402,30 @@ class BlockManager:
 
     def free_seq(self, seq: int) -> None:
         _check(lib().pa_bm_free_seq(self._h, seq))
+
+    def set_host_blocks(self, n: int) -> None:
+        _check(lib().pa_bm_set_host_blocks(self._h, n))
+
+    def _swap(self, fn, seq: int) -> np.ndarray:
+        cap = max(self.seq_len(seq), 0) // self.block_size + 1
+        pairs = np.zeros((cap, 2), np.int32)
+        n = ctypes.c_int32()
+        _check(fn(self._h, seq, _ptr(pairs), cap, ctypes.byref(n)))
+        return pairs[: n.value].copy()
+
+    def swap_out(self, seq: int) -> np.ndarray:
+        """Evict seq's unshared blocks to host slots; returns the (device block, host slot) pairs."""
+        return self._swap(lib().pa_bm_swap_out, seq)
+
+    def swap_in(self, seq: int) -> np.ndarray:
+        """Bring seq back into fresh device blocks; returns the (device block, host slot) pairs."""
+        return self._swap(lib().pa_bm_swap_in, seq)
+
+    def num_free_host(self) -> int:
+        return lib().pa_bm_num_free_host(self._h)
+
+    def is_swapped(self, seq: int) -> int:
+        return lib().pa_bm_is_swapped(self._h, seq)
 
     def refcount(self, block: int) -> int:
         return lib().pa_bm_refcount(self._h, block)

@@ -74,31 +74,33 @@ hipError_t reshape_launch(const ReshapeArgs &a, hipStream_t s) {
 // thread issues all of its 16-byte loads before its first store (the source and destination blocks
 // are distinct, which the restrict qualifiers state), so a copy costs one memory round trip.
 constexpr int kCopyThreads = 256;
-constexpr int kCopyVecs = 8;  // 16-byte vectors per thread and pool in one chunk
+constexpr int kCopyVecs = 4;  // 16-byte vectors per thread and pool in one chunk (16 KiB)
 constexpr int64_t kCopyChunk = (int64_t)kCopyThreads * kCopyVecs;  // vectors per chunk and pool
 
-__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs a) {
-  const int p = blockIdx.x, layer = blockIdx.y;
-  const int src = a.pairs[2 * p], dst = a.pairs[2 * p + 1];
-  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
-  const int64_t nvec = a.block_bytes / 16;
+// The argument struct of a kernel as it sits in the kernel-argument segment.  Indexing its
+// per-layer pointer arrays with the (wave-uniform) layer through this pointer reads them with
+// scalar loads; indexing the by-value parameter would first copy the whole struct to per-lane
+// scratch memory.  The struct is the kernel's only parameter, at offset 0.
+template <class Args>
+__device__ __forceinline__ const __attribute__((address_space(4))) Args *kernel_args() {
+  return (const __attribute__((address_space(4))) Args *)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
+// Whole blocks from src to dst, one chunk of kCopyChunk 16-byte vectors per pool and workgroup:
+// every load of the chunk is issued before any store.  Loads past the block's end re-read its last
+// vector (always in bounds) and are not stored, so the staging registers are written on every path
+// and stay in registers.
+__device__ __forceinline__ void copy_chunk(const uint4 *__restrict__ ks, const uint4 *__restrict__ vs,
+                                           uint4 *__restrict__ kd, uint4 *__restrict__ vd,
+                                           int64_t nvec) {
   const int64_t v0 = (int64_t)blockIdx.z * kCopyChunk;
-  const uint4 *__restrict__ ks = reinterpret_cast<const uint4 *>(
-      static_cast<const char *>(a.k_pools[layer]) + (size_t)src * a.block_bytes);
-  const uint4 *__restrict__ vs = reinterpret_cast<const uint4 *>(
-      static_cast<const char *>(a.v_pools[layer]) + (size_t)src * a.block_bytes);
-  uint4 *__restrict__ kd = reinterpret_cast<uint4 *>(static_cast<char *>(a.k_pools[layer]) +
-                                                     (size_t)dst * a.block_bytes);
-  uint4 *__restrict__ vd = reinterpret_cast<uint4 *>(static_cast<char *>(a.v_pools[layer]) +
-                                                     (size_t)dst * a.block_bytes);
   uint4 kx[kCopyVecs], vx[kCopyVecs];
 #pragma unroll
   for (int k = 0; k < kCopyVecs; ++k) {
     const int64_t i = v0 + threadIdx.x + (int64_t)k * kCopyThreads;
-    if (i < nvec) {
-      kx[k] = ks[i];
-      vx[k] = vs[i];
-    }
+    const int64_t j = i < nvec ? i : nvec - 1;
+    kx[k] = ks[j];
+    vx[k] = vs[j];
   }
 #pragma unroll
   for (int k = 0; k < kCopyVecs; ++k) {
@@ -108,6 +110,43 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs a) {
       vd[i] = vx[k];
     }
   }
+}
+
+// Swapping: for pair p = {device block d, host slot h} and layer blockIdx.y, both pools' block d
+// to slot h of the pinned host pools (to_host) or back.
+__global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(SwapArgs) {
+  const auto *a = kernel_args<SwapArgs>();
+  const int p = blockIdx.x, layer = blockIdx.y;
+  const int d = a->pairs[2 * p], h = a->pairs[2 * p + 1];
+  if (d < 0 || d >= a->num_blocks || h < 0 || h >= a->num_host) return;
+  const int64_t bb = a->block_bytes;
+  char *dk = static_cast<char *>(a->dev_k[layer]) + (size_t)d * bb;
+  char *dv = static_cast<char *>(a->dev_v[layer]) + (size_t)d * bb;
+  char *hk = static_cast<char *>(a->host_k[layer]) + (size_t)h * bb;
+  char *hv = static_cast<char *>(a->host_v[layer]) + (size_t)h * bb;
+  if (a->to_host)
+    copy_chunk(reinterpret_cast<const uint4 *>(dk), reinterpret_cast<const uint4 *>(dv),
+               reinterpret_cast<uint4 *>(hk), reinterpret_cast<uint4 *>(hv), bb / 16);
+  else
+    copy_chunk(reinterpret_cast<const uint4 *>(hk), reinterpret_cast<const uint4 *>(hv),
+               reinterpret_cast<uint4 *>(dk), reinterpret_cast<uint4 *>(dv), bb / 16);
+}
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs) {
+  const auto *ap = kernel_args<CopyArgs>();
+  const auto &a = *ap;
+  const int p = blockIdx.x, layer = blockIdx.y;
+  const int src = a.pairs[2 * p], dst = a.pairs[2 * p + 1];
+  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
+  const uint4 *ks = reinterpret_cast<const uint4 *>(static_cast<const char *>(a.k_pools[layer]) +
+                                                    (size_t)src * a.block_bytes);
+  const uint4 *vs = reinterpret_cast<const uint4 *>(static_cast<const char *>(a.v_pools[layer]) +
+                                                    (size_t)src * a.block_bytes);
+  uint4 *kd = reinterpret_cast<uint4 *>(static_cast<char *>(a.k_pools[layer]) +
+                                        (size_t)dst * a.block_bytes);
+  uint4 *vd = reinterpret_cast<uint4 *>(static_cast<char *>(a.v_pools[layer]) +
+                                        (size_t)dst * a.block_bytes);
+  copy_chunk(ks, vs, kd, vd, a.block_bytes / 16);
 }
 
 }  // namespace
@@ -127,6 +166,14 @@ hipError_t launch_reshape_and_cache(const ReshapeArgs &a, hipStream_t s) {
       }
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_swap_blocks(const SwapArgs &a, hipStream_t s) {
+  if (a.num_pairs == 0 || a.num_layers == 0) return hipSuccess;
+  const int64_t nvec = a.block_bytes / 16;
+  const unsigned chunks = (unsigned)((nvec + kCopyChunk - 1) / kCopyChunk);
+  swap_blocks_kernel<<<dim3(a.num_pairs, a.num_layers, chunks), dim3(kCopyThreads), 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_copy_blocks(const CopyArgs &a, hipStream_t s) {

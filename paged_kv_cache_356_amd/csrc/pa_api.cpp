@@ -380,6 +380,70 @@ pa_status pa_copy_blocks(const pa_cache *layers, int32_t num_layers, const int32
   return PA_OK;
 }
 
+// The device-side address of memory the GPU can reach: device memory, or pinned host memory
+// (hipHostMalloc).  Pageable host memory, or a pointer HIP does not know, gives nullptr.
+static void *device_reachable(const void *p, bool host_only) {
+  hipPointerAttribute_t attr;
+  if (!p || hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of a failed query
+    return nullptr;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer) return attr.devicePointer;
+  if (!host_only && attr.type == hipMemoryTypeDevice) return const_cast<void *>(p);
+  return nullptr;
+}
+
+pa_status pa_swap_blocks(const pa_cache *layers, int32_t num_layers, void *const *host_k,
+                         void *const *host_v, int32_t num_host_blocks, const int32_t *block_pairs,
+                         int32_t num_pairs, int32_t to_host, void *stream) {
+  const char *who = "pa_swap_blocks";
+  if (num_layers < 0 || num_pairs < 0 || num_host_blocks < 0)
+    return fail(PA_ERR_SHAPE, "%s: negative count", who);
+  if (num_layers == 0 || num_pairs == 0) return ok();
+  if (!layers || !host_k || !host_v || !block_pairs)
+    return fail(PA_ERR_NULL, "%s: NULL layers / host pools / block_pairs", who);
+  for (int32_t l = 0; l < num_layers; ++l) {
+    pa_status st = check_cache(&layers[l], who);
+    if (st != PA_OK) return st;
+    if (layers[l].num_blocks != layers[0].num_blocks ||
+        layers[l].num_kv_heads != layers[0].num_kv_heads ||
+        layers[l].head_dim != layers[0].head_dim || layers[l].cache_dtype != layers[0].cache_dtype)
+      return fail(PA_ERR_SHAPE, "%s: layer %d differs in shape or dtype from layer 0", who, l);
+    if (!host_k[l] || !host_v[l]) return fail(PA_ERR_NULL, "%s: NULL host pool, layer %d", who, l);
+  }
+  const int32_t *pairs = static_cast<const int32_t *>(device_reachable(block_pairs, false));
+  if (!pairs)
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: block_pairs is neither device memory nor pinned host memory", who);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t block_bytes = (int64_t)layers[0].num_kv_heads * PA_BLOCK_SIZE * layers[0].head_dim *
+                              pa::dtype_bytes(layers[0].cache_dtype);
+  for (int32_t l0 = 0; l0 < num_layers; l0 += pa::SwapArgs::kMaxLayers) {
+    pa::SwapArgs a;
+    a.num_layers = num_layers - l0 < pa::SwapArgs::kMaxLayers ? num_layers - l0
+                                                              : pa::SwapArgs::kMaxLayers;
+    for (int32_t l = 0; l < a.num_layers; ++l) {
+      a.dev_k[l] = layers[l0 + l].k_pool;
+      a.dev_v[l] = layers[l0 + l].v_pool;
+      a.host_k[l] = device_reachable(host_k[l0 + l], true);
+      a.host_v[l] = device_reachable(host_v[l0 + l], true);
+      if (!a.host_k[l] || !a.host_v[l])
+        return fail(PA_ERR_UNSUPPORTED,
+                    "%s: host pool of layer %d is not pinned host memory the device can reach", who,
+                    l0 + l);
+    }
+    a.block_bytes = block_bytes;
+    a.num_blocks = layers[0].num_blocks;
+    a.num_host = num_host_blocks;
+    a.pairs = pairs;
+    a.num_pairs = num_pairs;
+    a.to_host = to_host != 0;
+    pa_status st = launch_status(pa::launch_swap_blocks(a, s), who);
+    if (st != PA_OK) return st;
+  }
+  return PA_OK;
+}
+
 const char *pa_status_string(pa_status s) {
   switch (s) {
     case PA_OK: return "ok";

@@ -108,7 +108,23 @@ struct CopyArgs {
   int32_t num_pairs;
 };
 
+struct SwapArgs {
+  static constexpr int kMaxLayers = 32;
+  void *dev_k[kMaxLayers];
+  void *dev_v[kMaxLayers];
+  void *host_k[kMaxLayers];  // device-side addresses of pinned host memory
+  void *host_v[kMaxLayers];
+  int32_t num_layers;
+  int64_t block_bytes;  // bytes of one block in one pool (all KV heads)
+  int32_t num_blocks;
+  int32_t num_host;
+  const int32_t *pairs;  // {device block, host slot}
+  int32_t num_pairs;
+  int32_t to_host;
+};
+
 hipError_t launch_reshape_and_cache(const ReshapeArgs &a, hipStream_t stream);
+hipError_t launch_swap_blocks(const SwapArgs &a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs &a, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);

@@ -355,6 +355,64 @@ def test_stale_workspace_never_leaks():
         assert torch.equal(outs[0], outs[1])
 
 
+def test_swap_out_and_in_round_trip():
+    """Evicting sequences to CPU memory and bringing them back ("PagedAttention, Visualized",
+    Part 3, swapping to disk): only unshared blocks move; the host pools and, after swap-in, the
+    device pools equal the oracle's replay byte for byte; decoding through the new tables gives the
+    same bits as before the swap."""
+    w = wl.WORKLOADS["f16_shared_prefix_batch256"].replace(num_seqs=6, num_blocks=512, prefix_len=64,
+                                                           num_layers=2)
+    lengths = [64 + 5, 64 + 40, 64 + 17, 64 + 100, 64 + 1, 64 + 33]
+    _say("swap out / in, 2 layers")
+    b = DecodeBatch(w, lengths=lengths, pad_block=0)
+    b.use_prefix = False
+    b.run_step(0)
+    torch.cuda.synchronize()
+    st = b.sets[0]
+    caches = [b.caches[l] for l in b.layers]
+    before = [st.out[l].clone() for l in b.layers]
+    nh = 40
+    host = api.HostPools(caches, nh)
+    bb = host.block_bytes
+    bm = b.bm
+    bm.set_host_blocks(nh)
+    prefix_blocks = set(bm.table(st.seqs[0])[:4])
+    victims = [st.seqs[1], st.seqs[3]]
+    pairs_out = np.concatenate([bm.swap_out(s) for s in victims])
+    assert len(pairs_out) > 0 and not set(pairs_out[:, 0].tolist()) & prefix_blocks
+    dev0 = [x for c in caches for x in device_pool_bytes(c)]
+    api.pa_swap_blocks(caches, host, torch.from_numpy(pairs_out).cuda(), True)
+    torch.cuda.synchronize()
+    want_host = [np.zeros(nh * bb, np.uint8) for _ in dev0]
+    oracle.swap_blocks(dev0, want_host, bb, w.num_blocks, nh, pairs_out, True)
+    got_host = [t.numpy() for c in range(len(caches)) for t in (host.k[c], host.v[c])]
+    for gh, wh in zip(got_host, want_host):
+        for h in pairs_out[:, 1]:
+            assert np.array_equal(gh[h * bb:(h + 1) * bb], wh[h * bb:(h + 1) * bb])
+    # the freed device blocks get reused by others in a real run: poison them
+    for c in caches:
+        for d in pairs_out[:, 0]:
+            c.k_pool[d * bb:(d + 1) * bb].fill_(POISON)
+            c.v_pool[d * bb:(d + 1) * bb].fill_(POISON)
+    pairs_in = np.concatenate([bm.swap_in(s) for s in victims])
+    dev1 = [x for c in caches for x in device_pool_bytes(c)]
+    api.pa_swap_blocks(caches, host, torch.from_numpy(pairs_in).cuda(), False)
+    torch.cuda.synchronize()
+    oracle.swap_blocks(dev1, want_host, bb, w.num_blocks, nh, pairs_in, False)
+    for got, want in zip([x for c in caches for x in device_pool_bytes(c)], dev1):
+        assert np.array_equal(got, want)
+    tables, ctx = bm.export(st.seqs, st.tables.shape[1], 0)
+    assert np.array_equal(ctx, st.ctx)
+    d_tables = torch.from_numpy(tables).cuda()
+    for i, l in enumerate(b.layers):
+        out = torch.zeros_like(st.out[l])
+        api.pa_decode_attention(out, st.q[l], b.caches[l], d_tables, st.d_ctx, b.max_context_len,
+                                w.scale, b.partition_size, b.workspace)
+        torch.cuda.synchronize()
+        _say(f"  layer {l}: bitwise equal after swap {torch.equal(out, before[i])}")
+        assert torch.equal(out, before[i])
+
+
 def test_empty_context_and_out_of_range_blocks():
     _say("edge cases")
     w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=3, num_blocks=256)

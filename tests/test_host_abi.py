@@ -259,3 +259,103 @@ def test_per_token_kv_bytes_of_qwen25_7b():
     assert round(447168 / 32768, 2) == 13.65
     # reserving 32,768 slots for a 500-token conversation wastes about 98%
     assert round(1 - 500 / 32768, 2) == 0.98
+
+
+# ------------------------------------------------------------------ swapping to CPU memory
+@pytest.mark.parametrize("seed", range(6))
+def test_block_manager_swapping_matches_model(seed):
+    """pa_bm_swap_out / pa_bm_swap_in against the model on random operation sequences: same pairs,
+    same tables, counts and free lists, and the same refusals."""
+    g = np.random.default_rng(300 + seed)
+    nb, B, nh = 64, int(g.choice([2, 4, 16])), int(g.integers(8, 40))
+    order = g.permutation(nb)
+    prod, model = api.BlockManager(nb, B, order), BlockManagerModel(nb, B, order)
+    prod.set_host_blocks(nh)
+    model.set_host_blocks(nh)
+    live, out = [], set()
+    for _ in range(700):
+        op = int(g.integers(0, 12))
+        if op == 0 or not live:
+            a, b = prod.add_seq(), model.add_seq()
+            assert a == b
+            live.append(a)
+            continue
+        s = live[int(g.integers(len(live)))]
+        if op == 1 and s not in out:
+            a, b = prod.fork(s), model.fork(s)
+            assert a == b
+            live.append(a)
+        elif op == 2 and len(live) > 1:
+            live.remove(s)
+            out.discard(s)
+            prod.free_seq(s)
+            model.free_seq(s)
+        elif op in (3, 4):
+            swap_in = op == 4 and s in out
+            if op == 3 and s in out:
+                continue
+            if op == 4 and not swap_in:
+                continue
+            try:
+                want = model.swap_in(s) if swap_in else model.swap_out(s)
+            except NoBlocks:
+                with pytest.raises(api.PaError) as e:
+                    prod.swap_in(s) if swap_in else prod.swap_out(s)
+                assert e.value.status == -7
+                continue
+            got = prod.swap_in(s) if swap_in else prod.swap_out(s)
+            assert [tuple(p) for p in got.tolist()] == want
+            (out.discard if swap_in else out.add)(s)
+            assert prod.is_swapped(s) == (0 if swap_in else 1)
+        elif s not in out:
+            try:
+                want = model.append(s)
+            except NoBlocks:
+                with pytest.raises(api.PaError):
+                    prod.append(s)
+                continue
+            assert prod.append(s) == want
+        else:  # a swapped-out sequence cannot run
+            with pytest.raises(api.PaError) as e:
+                prod.append(s)
+            assert e.value.status == -8
+        assert prod.num_free() == len(model.free)
+        assert prod.num_free_host() == len(model.host_free)
+    for s in live:
+        assert prod.table(s) == model.table(s)
+    for b in range(nb):
+        assert prod.refcount(b) == model.ref[b]
+    model.check_invariants()
+
+
+def test_swap_blocks_rejections_do_not_launch():
+    c = api.pa_cache(None, None, None, None, 8, 16, 2, 64, api.PA_F16)
+    L = api.lib()
+    arr = (api.pa_cache * 1)(c)
+    hp = (ctypes.c_void_p * 1)(None)
+    pairs = np.zeros((1, 2), np.int32)
+    assert L.pa_swap_blocks(arr, 1, hp, hp, 4, api._ptr(pairs), 0, 1, None) == 0  # nothing to do
+    assert L.pa_swap_blocks(arr, -1, hp, hp, 4, api._ptr(pairs), 1, 1, None) == -2
+    assert L.pa_swap_blocks(None, 1, hp, hp, 4, api._ptr(pairs), 1, 1, None) == -1
+    assert L.pa_swap_blocks(arr, 1, hp, hp, 4, None, 1, 1, None) == -1
+    # a pageable host array of pairs is refused before any launch (the device cannot read it)
+    c2 = api.pa_cache(16, 16, None, None, 8, 16, 2, 64, api.PA_F16)
+    arr2 = (api.pa_cache * 1)(c2)
+    hp2 = (ctypes.c_void_p * 1)(16)
+    st = L.pa_swap_blocks(arr2, 1, hp2, hp2, 4, api._ptr(pairs), 1, 1, None)
+    assert st in (-1, -3)  # NULL pool on a host without a GPU, or unsupported memory
+
+
+def test_set_host_blocks_is_refused_while_a_sequence_is_out():
+    bm = api.BlockManager(8, 4)
+    bm.set_host_blocks(4)
+    s = bm.add_seq()
+    bm.append(s)
+    assert bm.swap_out(s).tolist() == [[0, 0]]  # block 0 (first handed out) to host slot 0
+    assert bm.is_swapped(s) == 1 and bm.num_free_host() == 3 and bm.refcount(0) == 0
+    with pytest.raises(api.PaError) as e:
+        bm.set_host_blocks(8)
+    assert e.value.status == -8
+    assert bm.swap_in(s).tolist() == [[0, 0]]  # block 0 was freed on top, so it comes back
+    bm.set_host_blocks(8)
+    assert bm.num_free_host() == 8
