@@ -185,6 +185,33 @@ def decode_attention(q, q_dtype, k_pool, v_pool, cache_dtype, k_scale, v_scale, 
     return out
 
 
+def prefill_attention(q, q_dtype, k_pool, v_pool, cache_dtype, k_scale, v_scale, num_blocks, H, D,
+                      block_tables, context_lens, query_start, num_q_heads, scale, nthreads=0, B=16):
+    """fp64 attention for a chunk of new tokens per sequence (a prompt, or a chunk of one).  Sequence
+    s has n_s = query_start[s+1] - query_start[s] new tokens at positions L_s - n_s .. L_s - 1
+    (L_s = context_lens[s]); the token at position p attends to positions 0 .. p of its sequence:
+    a prompt passes through the model as one matrix whose tokens look at each other, and a token's
+    K and V serve every token after it ("PagedAttention, Visualized", Parts 1 and 2).  Each token
+    is therefore the decode of its own position, computed here as such.
+    q: raw [num_tokens][Hq*D]; returns [num_tokens][Hq][D]."""
+    block_tables = np.ascontiguousarray(block_tables, np.int32)
+    context_lens = np.asarray(context_lens, np.int64)
+    query_start = np.asarray(query_start, np.int64)
+    S = block_tables.shape[0]
+    rows, ctx = [], []
+    for s in range(S):
+        n = int(query_start[s + 1] - query_start[s])
+        for t in range(n):
+            rows.append(s)
+            ctx.append(int(context_lens[s]) - n + t + 1)
+    T = len(rows)
+    if T == 0:
+        return np.zeros((0, num_q_heads, D), np.float64)
+    return decode_attention(q, q_dtype, k_pool, v_pool, cache_dtype, k_scale, v_scale, num_blocks,
+                            H, D, block_tables[np.asarray(rows)], np.asarray(ctx, np.int32),
+                            num_q_heads, scale, nthreads=nthreads, B=B)
+
+
 def reshape_and_cache(k_pool, v_pool, cache_dtype, k_scale, v_scale, num_blocks, H, D, key, value,
                       in_dtype, slots, B=16, key_stride=None, value_stride=None):
     """In-place replay into host pools (numpy arrays of the cache's raw element type)."""

@@ -513,3 +513,52 @@ def test_swap_replay_copies_whole_blocks_both_ways():
         assert np.array_equal(x[5 * bb:6 * bb], o[4 * bb:5 * bb])
         assert np.array_equal(x[3 * bb:4 * bb], o[0:bb])
         assert not x[:3 * bb].any() and not x[4 * bb:5 * bb].any()
+
+
+# ------------------------------------------------------------------------ prefill (a chunk per sequence)
+def test_prefill_matches_causal_sdpa_on_contiguous_kv():
+    """A chunk of new tokens per sequence against torch's scaled_dot_product_attention with its own
+    causal mask (is_causal) on the de-paged K/V: the last n_s query rows of an L_s x L_s causal
+    attention."""
+    lengths = [7, 16, 40, 3]
+    chunks = [7, 5, 17, 0]  # whole prompt, a chunk ending mid-block, a long chunk, nothing
+    Hq, H, D, nb = 4, 2, 64, 24
+    _, kp, vp, tables, logical = _paged_problem("f32", lengths, Hq, H, D, nb, 500)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = _values((int(qs[-1]), Hq, D), "f32", 501)
+    out = oracle.prefill_attention(raw(q).reshape(int(qs[-1]), -1), "f32", kp, vp, "f32", None,
+                                   None, nb, H, D, tables, np.array(lengths), qs, Hq, 0.125)
+    for s, ((k, v), L, n) in enumerate(zip(logical, lengths, chunks)):
+        if n == 0:
+            continue
+        kk = k.double().repeat_interleave(Hq // H, dim=1).permute(1, 0, 2)  # [Hq, L, D]
+        vv = v.double().repeat_interleave(Hq // H, dim=1).permute(1, 0, 2)
+        # queries for all L positions; only the last n are the chunk's
+        qq = torch.zeros(Hq, L, D, dtype=torch.float64)
+        qq[:, L - n:] = q[qs[s]:qs[s + 1]].double().permute(1, 0, 2)
+        ref = F.scaled_dot_product_attention(qq[None], kk[None], vv[None], is_causal=True,
+                                             scale=0.125)[0]
+        got = torch.from_numpy(out[qs[s]:qs[s + 1]]).permute(1, 0, 2)
+        assert torch.max(torch.abs(got - ref[:, L - n:])) < 1e-12
+
+
+def test_prefill_closed_forms():
+    """The first token of a prompt sees only itself: its output is its own V row.  With every key
+    equal, token p's output is the mean of V[0..p]."""
+    L, Hq, H, D, nb = 20, 2, 1, 64, 8
+    _, kp, vp, tables, logical = _paged_problem("f32", [L], Hq, H, D, nb, 600)
+    qs = np.array([0, L], np.int32)
+    q = _values((L, Hq, D), "f32", 601)
+    out = oracle.prefill_attention(raw(q).reshape(L, -1), "f32", kp, vp, "f32", None, None, nb, H,
+                                   D, tables, np.array([L]), qs, Hq, 0.125)
+    v = logical[0][1].double().numpy()  # [L, H, D]
+    assert np.max(np.abs(out[0, :, :] - v[0, 0])) < 1e-12
+    # equal keys: rewrite every K row of the pool to one vector, then token p averages V[0..p]
+    k_all = np.tile(raw(logical[0][0][:1]), (L, 1, 1))
+    slots = np.array([tables[0, p // 16] * 16 + p % 16 for p in range(L)], np.int64)
+    oracle.reshape_and_cache(kp, vp, "f32", None, None, nb, H, D, k_all, raw(logical[0][1]), "f32",
+                             slots)
+    out = oracle.prefill_attention(raw(q).reshape(L, -1), "f32", kp, vp, "f32", None, None, nb, H,
+                                   D, tables, np.array([L]), qs, Hq, 0.125)
+    for p in range(L):
+        assert np.max(np.abs(out[p, :, :] - v[: p + 1, 0].mean(axis=0))) < 1e-12
