@@ -167,6 +167,53 @@ def swap_bench(args, torch, api, wl, DecodeBatch) -> int:
     return 0
 
 
+def prefill_bench(args, torch, api, wl) -> int:
+    """Prefill of S prompts of P tokens each: every token attends to the positions up to its own,
+    through the block tables (pa_prefill_attention), timed with HIP events on the launch stream.
+    Algorithmic flops = 4 * head_dim * num_q_heads * sum over tokens of the positions attended."""
+    S, P = args.prefill
+    Hq, H, D, B = 28, 4, 128, 16
+    nb = S * (-(-P // B)) + 16
+    w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=S, num_blocks=nb)
+    bm = api.BlockManager(nb, B, wl.free_order(w))
+    seqs = [bm.add_seq() for _ in range(S)]
+    slots = np.concatenate([bm.append_many(s, P) for s in seqs])
+    tables, ctx = bm.export(seqs, -(-P // B), 0)
+    g = wl.torch_generator(w.seed, "cuda")
+    cache = api.KVCache.allocate(nb, H, D, "f16", "cuda")
+    api.pa_reshape_and_cache(cache, wl.normal((S * P, H, D), "f16", g, "cuda"),
+                             wl.normal((S * P, H, D), "f16", g, "cuda"),
+                             torch.from_numpy(slots).cuda())
+    q = wl.normal((S * P, Hq, D), "f16", g, "cuda")
+    out = torch.empty_like(q)
+    qs = torch.arange(0, S * P + 1, P, dtype=torch.int32, device="cuda")
+    call = api.PrefillCall(out, q, cache, torch.from_numpy(tables).cuda(),
+                           torch.from_numpy(ctx).cuda(), qs, P, P, 1.0 / math.sqrt(D))
+    call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, args.steps)
+    ev0.record(stream)
+    for _ in range(reps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    sec = ev0.elapsed_time(ev1) / 1e3 / reps
+    flops = 4.0 * D * Hq * S * (P * (P + 1) / 2)
+    tflops = flops / sec / 1e12
+    kv_bytes = S * P * 2 * H * D * 2
+    print(json.dumps({
+        "metric": "paged prefill attention (pa_prefill_attention)",
+        "workload": f"{S} prompts x {P} tokens, 28 q / 4 KV heads, head_dim 128, f16, causal",
+        "tokens_per_s": round(S * P / sec, 1), "us_per_call": round(sec * 1e6, 2),
+        "calls_timed": reps,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
+                     "flops_per_call": flops, "kv_bytes_written_before": kv_bytes}}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +235,9 @@ def main() -> int:
     ap.add_argument("--swap", action="store_true",
                     help="measure swapping half of the workload's sequences to pinned host memory "
                          "and back (pa_swap_blocks), print that line and exit")
+    ap.add_argument("--prefill", type=int, nargs=2, default=None, metavar=("SEQS", "PROMPT"),
+                    help="measure paged prefill of SEQS prompts of PROMPT tokens each "
+                         "(pa_prefill_attention, Qwen2.5-7B heads, f16), print that line and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB a few times (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -222,6 +272,8 @@ def main() -> int:
     api.lib()
     if args.swap:
         return swap_bench(args, torch, api, wl, DecodeBatch)
+    if args.prefill:
+        return prefill_bench(args, torch, api, wl)
     w = wl.WORKLOADS[args.workload]
     if args.num_blocks:
         w = w.replace(num_blocks=args.num_blocks)

@@ -223,6 +223,35 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_h
                                                int32_t partition_size);
 
 /*
+ * pa_prefill_attention — paged attention for a chunk of new tokens per sequence: a prompt, or a
+ * piece of one.  A prompt goes through the model as one matrix whose tokens look at each other,
+ * and a token's K and V serve every token after it ([Visualized] Parts 1 and 2): sequence s has
+ * n_s = query_start[s+1] - query_start[s] new tokens at positions L_s - n_s .. L_s - 1
+ * (L_s = context_lens[s], the new tokens already written by pa_reshape_and_cache), and the token at
+ * position p attends to positions 0 .. p of its sequence, through its block table.
+ *
+ *   out           device [num_tokens][num_q_heads][head_dim], query dtype, written for every new
+ *                 token of every sequence.
+ *   query         device [num_tokens][num_q_heads][head_dim]; token rows q_stride elements apart
+ *                 (0 = packed).
+ *   query_start   device int32 [num_seqs + 1]: query_start[0] = 0, non-decreasing, the last one
+ *                 num_tokens; n_s <= L_s.
+ *   max_query_len host upper bound of every n_s (sizes the grid; larger n_s are cut to it).
+ *   Other arguments as in pa_decode_attention.  No workspace: each token's rows are computed
+ *   whole by one wavefront.
+ * Supported: the matrix-core configurations of pa_decode_attention (f16 / bf16 caches with the same
+ * query dtype, fp8 caches with f16 queries; head_dim 64 or 128; at most 16 query heads per KV
+ * head; 16-byte aligned query rows and q_stride a multiple of 8; 8-byte aligned output); anything
+ * else is PA_ERR_UNSUPPORTED.
+ */
+pa_status pa_prefill_attention(void *out, const void *query, int32_t q_dtype, int64_t q_stride,
+                               const pa_cache *cache, const int32_t *block_tables,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                               const int32_t *query_start, int32_t num_seqs, int32_t num_tokens,
+                               int32_t num_q_heads, int32_t max_query_len, int32_t max_context_len,
+                               float scale, void *stream);
+
+/*
  * pa_copy_blocks — the clone step of copy-on-write.  When a sequence must write into a block
  * whose reference count is above 1, the engine clones that block, drops the original's count by
  * one and points the writer's table at the clone ([Digest] "Copy-on-write: when two requests share

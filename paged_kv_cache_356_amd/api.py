@@ -32,7 +32,8 @@ EXPORTS = [
     "pa_pool_bytes", "pa_reshape_and_cache", "pa_decode_auto_partition",
     "pa_decode_workspace_bytes", "pa_decode_attention", "pa_decode_attention_shared_prefix",
     "pa_decode_shared_prefix_workspace_bytes", "pa_copy_blocks", "pa_check_copy_pairs",
-    "pa_swap_blocks", "pa_bm_set_host_blocks", "pa_bm_swap_out", "pa_bm_swap_in",
+    "pa_prefill_attention", "pa_swap_blocks", "pa_bm_set_host_blocks", "pa_bm_swap_out",
+    "pa_bm_swap_in",
     "pa_bm_num_free_host", "pa_bm_is_swapped",
     "pa_status_string", "pa_last_error", "pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq",
     "pa_bm_fork", "pa_bm_append", "pa_bm_append_batch", "pa_bm_free_seq", "pa_bm_refcount",
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
             "pa_copy_blocks": (_i32, [_cp, _i32, _vp, _i32, _vp]),
             "pa_check_copy_pairs": (_i32, [_vp, _i32, _i32]),
             "pa_swap_blocks": (_i32, [_cp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp]),
+            "pa_prefill_attention": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _i32, _vp, _vp, _i32,
+                                            _i32, _i32, _i32, _i32, _f32, _vp]),
             "pa_bm_set_host_blocks": (_i32, [_vp, _i32]),
             "pa_bm_swap_out": (_i32, [_vp, _i32, _vp, _i32, _vp]),
             "pa_bm_swap_in": (_i32, [_vp, _i32, _vp, _i32, _vp]),
@@ -284,6 +287,41 @@ def pa_decode_attention_shared_prefix(out: torch.Tensor, query: torch.Tensor, ca
     prefix_table, device int32 [prefix_len / 16])."""
     DecodeCall(out, query, cache, block_tables, context_lens, max_context_len, scale,
                partition_size, workspace, flags, prefix_table, prefix_len)(stream)
+
+
+class PrefillCall:
+    """pa_prefill_attention with every argument but the stream fixed (checks and conversions done
+    once).  out, query: [num_tokens, num_q_heads, head_dim] (query rows may be strided);
+    query_start: device int32 [num_seqs + 1]."""
+
+    def __init__(self, out: torch.Tensor, query: torch.Tensor, cache: KVCache,
+                 block_tables: torch.Tensor, context_lens: torch.Tensor,
+                 query_start: torch.Tensor, max_query_len: int, max_context_len: int,
+                 scale: float):
+        T, Hq, D = query.shape
+        assert out.shape == query.shape and out.dtype == query.dtype and out.is_contiguous()
+        assert query.stride(2) == 1 and query.stride(1) == D
+        assert block_tables.dtype == torch.int32 and block_tables.is_contiguous()
+        assert context_lens.dtype == torch.int32 and context_lens.is_contiguous()
+        assert query_start.dtype == torch.int32 and query_start.is_contiguous()
+        S = block_tables.shape[0]
+        assert query_start.shape[0] == S + 1 and context_lens.shape[0] == S
+        self._keep = (out, query, cache, block_tables, context_lens, query_start)
+        self._args = (_ptr(out), _ptr(query), TORCH_CODES[query.dtype], query.stride(0) if T else 0,
+                      ctypes.byref(cache.struct()), _ptr(block_tables), block_tables.shape[1],
+                      _ptr(context_lens), _ptr(query_start), S, T, Hq, int(max_query_len),
+                      int(max_context_len), float(scale))
+        self._fn = lib().pa_prefill_attention
+
+    def __call__(self, stream=None) -> None:
+        _check(self._fn(*self._args, _stream(stream)))
+
+
+def pa_prefill_attention(out, query, cache, block_tables, context_lens, query_start,
+                         max_query_len: int, max_context_len: int, scale: float,
+                         stream=None) -> None:
+    PrefillCall(out, query, cache, block_tables, context_lens, query_start, max_query_len,
+                max_context_len, scale)(stream)
 
 
 class CopyCall:

@@ -433,47 +433,22 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs &a, int s) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Wavefront item: one wavefront computes KV head h over positions [jb0 * 16, end) of one
-// block-table row, against up to 16 query rows (the 16 columns of the products), and writes the
-// rows' results itself (no merge with other wavefronts, no barrier):
-//  - sequence item (s >= 0): the rows are the g query heads of sequence s, on s's table row.
-//  - prefix tile (s < 0): the rows are flat rows row0 .. row0 + 15 of the batch (flat row r is
-//    query head h*g + r % g of sequence r / g), on the shared prefix's table; each row masks the
-//    positions at or past its own context length.
+// The work of one wavefront: KV head h over blocks [jb0, jb1) of `table`, against up to 16 query
+// rows (the 16 columns of the products).  This lane's column is query row (rs, rhq) (query row rs
+// at q_stride, head rhq; output row rs * Hq + rhq), or padding when !rvalid; positions at or past
+// its `lim` are masked, and V elements of positions at or past `end` (wave-uniform) are zeroed.
 // The result goes to workspace partition `slot`, or straight to the output when slot < 0.
-// Wavefronts of one workgroup run their items independently, so one wavefront's item prologue
-// (query, table fetch, first loads) and epilogue overlap the other wavefronts' block streams.
 // kNT: read K/V with non-temporal loads (each tile is read once per call), or with ordinary loads
-// (prefix tiles, whose blocks the other tiles of the batch read too).  `lens`: the clamped context
-// lengths of the batch (in LDS), read by prefix tiles for their rows' masks.  tbl0: the item's
-// first table entries (first_table_entries of its table row).  settle: a value whose load is in
-// flight (the next item's first table entries), waited for once this item's blocks are done.
+// (tiles that other wavefronts of the call read too).  tbl0: lane i's entry of the first 64
+// blocks (first_table_entries).  settle: a value whose load is in flight (the next item's first
+// table entries), waited for once this item's blocks are done.
 template <class CT, class QT, int D, bool kNT>
-__device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int row0_in, int h_in,
-                                          int jb0_in, int jb1_in, int end_in, int slot_in,
-                                          const int *lens, int tbl0, int &settle) {
-  // The item is the same for the whole wavefront: keep its fields (and so the tile addresses) in
-  // scalar registers.
-  const int s = __builtin_amdgcn_readfirstlane(s_in);
-  const int row0 = __builtin_amdgcn_readfirstlane(row0_in);
-  const int h = __builtin_amdgcn_readfirstlane(h_in);
-  const int jb0 = __builtin_amdgcn_readfirstlane(jb0_in);
-  const int jb1 = __builtin_amdgcn_readfirstlane(jb1_in);
-  const int end = __builtin_amdgcn_readfirstlane(end_in);
-  const int slot = __builtin_amdgcn_readfirstlane(slot_in);
+__device__ __forceinline__ void rows_core(const DecodeArgs &a, const int32_t *table, int h,
+                                          int jb0, int jb1, int end, int slot, int rs, int rhq,
+                                          bool rvalid, int lim, int tbl0, int &settle) {
   constexpr int NT = D / 16;
-  const int H = a.cache.num_kv_heads, Hq = a.num_q_heads, g = Hq / H;
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 15, grp = lane >> 4;
-  const bool tile = s < 0;
-  const int nrows = tile ? min(16, a.num_seqs * g - row0) : g;
-  const bool rvalid = col < nrows;
-  const int rs = tile ? (rvalid ? (row0 + col) / g : 0) : s;
-  const int rhq = h * g + (rvalid ? (tile ? (row0 + col) % g : col) : 0);
-  const int lim = tile && rvalid ? min(end, lens[rs]) : end;
-  const int32_t *table =
-      tile ? a.prefix_table : a.block_tables + (size_t)s * a.max_blocks_per_seq;
-
+  const int Hq = a.num_q_heads;
+  const int grp = (threadIdx.x & 63) >> 4;
   RowState<D> st;
   load_query<CT, D>(a, rs, rhq, rvalid, st);
   float kscale, vscale;
@@ -520,6 +495,39 @@ __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int row
       a.part_ml[row * 2 + 1] = l;
     }
   }
+}
+
+// Wavefront item of the decode: KV head h over positions [jb0 * 16, end) of one block-table row:
+//  - sequence item (s >= 0): the rows are the g query heads of sequence s, on s's table row.
+//  - prefix tile (s < 0): the rows are flat rows row0 .. row0 + 15 of the batch (flat row r is
+//    query head h*g + r % g of sequence r / g), on the shared prefix's table; each row masks the
+//    positions at or past its own context length (`lens`, the clamped lengths in LDS).
+// Wavefronts of one workgroup run their items independently, so one wavefront's item prologue
+// (query, table fetch, first loads) and epilogue overlap the other wavefronts' block streams.
+template <class CT, class QT, int D, bool kNT>
+__device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int row0_in, int h_in,
+                                          int jb0_in, int jb1_in, int end_in, int slot_in,
+                                          const int *lens, int tbl0, int &settle) {
+  // The item is the same for the whole wavefront: keep its fields (and so the tile addresses) in
+  // scalar registers.
+  const int s = __builtin_amdgcn_readfirstlane(s_in);
+  const int row0 = __builtin_amdgcn_readfirstlane(row0_in);
+  const int h = __builtin_amdgcn_readfirstlane(h_in);
+  const int jb0 = __builtin_amdgcn_readfirstlane(jb0_in);
+  const int jb1 = __builtin_amdgcn_readfirstlane(jb1_in);
+  const int end = __builtin_amdgcn_readfirstlane(end_in);
+  const int slot = __builtin_amdgcn_readfirstlane(slot_in);
+  const int H = a.cache.num_kv_heads, Hq = a.num_q_heads, g = Hq / H;
+  const int col = threadIdx.x & 15;
+  const bool tile = s < 0;
+  const int nrows = tile ? min(16, a.num_seqs * g - row0) : g;
+  const bool rvalid = col < nrows;
+  const int rs = tile ? (rvalid ? (row0 + col) / g : 0) : s;
+  const int rhq = h * g + (rvalid ? (tile ? (row0 + col) % g : col) : 0);
+  const int lim = tile && rvalid ? min(end, lens[rs]) : end;
+  const int32_t *table =
+      tile ? a.prefix_table : a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  rows_core<CT, QT, D, kNT>(a, table, h, jb0, jb1, end, slot, rs, rhq, rvalid, lim, tbl0, settle);
 }
 
 // Items of sequence s: plain decode, partitions of its context (an empty context counts one item,
@@ -698,6 +706,59 @@ void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
+// Prefill (a chunk of n new tokens per sequence, positions L - n .. L - 1; the token at position p
+// attends to positions 0 .. p): workgroup (s, h, group) takes 64 rows of sequence s and KV head h
+// (row r is token r / g, query head h*g + r % g), its wavefront w rows 16 w .. 16 w + 15.  Each row
+// masks the positions past its own; the wavefront streams the blocks up to its last row's
+// position.  The four wavefronts of a workgroup walk the same blocks with ordinary loads, and so do
+// the sequence's other workgroups, so the caches serve most of the re-reads.  Rows are complete
+// in one wavefront: the outputs are written directly, no workspace.
+template <class CT, class QT, int D>
+__global__ __launch_bounds__(256)
+#if PA_DECODE_OCC
+__attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
+#endif
+void prefill_mfma_kernel(DecodeArgs a) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = a.cache.num_kv_heads, g = a.num_q_heads / H;
+  const int groups = (a.max_query_len * g + 63) / 64;
+  const int gi = blockIdx.x % groups, sh = blockIdx.x / groups;
+  const int h = sh % H, s = sh / H;
+  const int qs = a.query_start[s];
+  const int n = min(a.query_start[s + 1] - qs, a.max_query_len);
+  const int L = clamp_len(a, s);
+  const int row0 = 64 * gi + 16 * w;
+  if (n <= 0 || row0 >= n * g) return;  // wave-uniform
+  const int last = min(row0 + 15, n * g - 1);
+  const int end = max(0, min(L, L - n + last / g + 1));  // the wavefront's last row's limit
+  const int col = threadIdx.x & 15;
+  const int r = row0 + col;
+  const bool rvalid = r < n * g;
+  const int t = rvalid ? r / g : 0;
+  const int lim = max(0, min(L, L - n + t + 1));
+  const int32_t *table = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  const int jb1 = (end + kBlock - 1) / kBlock;
+  int none = 0;
+  rows_core<CT, QT, D, false>(a, table, h, 0, jb1, end, -1, qs + t, h * g + (rvalid ? r % g : 0),
+                              rvalid, lim, first_table_entries(table, 0, jb1), none);
+}
+
+template <class CT, class QT, int D>
+hipError_t launch_prefill_dd(const DecodeArgs &a, hipStream_t s) {
+  const int g = a.num_q_heads / a.cache.num_kv_heads;
+  const int64_t groups = ((int64_t)a.max_query_len * g + 63) / 64;
+  const int64_t grid = (int64_t)a.num_seqs * a.cache.num_kv_heads * groups;
+  if (grid == 0) return hipSuccess;
+  prefill_mfma_kernel<CT, QT, D><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <class CT, class QT>
+hipError_t launch_prefill_d(const DecodeArgs &a, hipStream_t s) {
+  return a.cache.head_dim == 64 ? launch_prefill_dd<CT, QT, 64>(a, s)
+                                : launch_prefill_dd<CT, QT, 128>(a, s);
+}
+
 // Workgroups of one instantiation that fit on the device at once (occupancy x compute units),
 // looked up once per device.
 template <class CT, class QT, int D>
@@ -758,6 +819,15 @@ bool decode_mfma_supports(const DecodeArgs &a) {
   // an empty pool has no tile for the ring's idle slots to read
   return types && g >= 1 && g <= 16 && (a.cache.head_dim == 64 || a.cache.head_dim == 128) &&
          q_aligned && a.cache.num_blocks > 0;
+}
+
+hipError_t launch_prefill_mfma(const DecodeArgs &a, hipStream_t s) {
+  switch (a.cache.dtype) {
+    case kF16: return launch_prefill_d<f16_t, f16_t>(a, s);
+    case kBF16: return launch_prefill_d<bf16_t, bf16_t>(a, s);
+    case kFP8: return launch_prefill_d<fp8_t, f16_t>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {

@@ -380,6 +380,62 @@ pa_status pa_copy_blocks(const pa_cache *layers, int32_t num_layers, const int32
   return PA_OK;
 }
 
+pa_status pa_prefill_attention(void *out, const void *query, int32_t q_dtype, int64_t q_stride,
+                               const pa_cache *cache, const int32_t *block_tables,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                               const int32_t *query_start, int32_t num_seqs, int32_t num_tokens,
+                               int32_t num_q_heads, int32_t max_query_len, int32_t max_context_len,
+                               float scale, void *stream) {
+  const char *who = "pa_prefill_attention";
+  pa_status st = check_cache(cache, who);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_seqs > 65535)
+    return fail(PA_ERR_SHAPE, "%s: num_seqs %d outside 0..65535", who, num_seqs);
+  if (num_tokens < 0 || max_query_len < 0 || max_context_len < 0)
+    return fail(PA_ERR_SHAPE, "%s: negative num_tokens / max_query_len / max_context_len", who);
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return ok();
+  if (!out || !query || !block_tables || !context_lens || !query_start)
+    return fail(PA_ERR_NULL, "%s: NULL out/query/block_tables/context_lens/query_start", who);
+  const int H = cache->num_kv_heads, D = cache->head_dim;
+  if (num_q_heads < 1 || num_q_heads % H != 0)
+    return fail(PA_ERR_SHAPE, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", who,
+                num_q_heads, H);
+  if (max_blocks_per_seq < 1)
+    return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq %d < 1", who, max_blocks_per_seq);
+  if (q_stride == 0) q_stride = (int64_t)num_q_heads * D;
+  if (q_stride < (int64_t)num_q_heads * D)
+    return fail(PA_ERR_SHAPE, "%s: q_stride %lld below a row", who, (long long)q_stride);
+  const int64_t groups = ((int64_t)max_query_len * (num_q_heads / H) + 63) / 64;
+  if ((int64_t)num_seqs * H * groups > 0x7fffffff)
+    return fail(PA_ERR_SHAPE, "%s: grid of %lld workgroups too large", who,
+                (long long)((int64_t)num_seqs * H * groups));
+  const int64_t cap = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = query;
+  a.q_stride = q_stride;
+  a.q_dtype = q_dtype;
+  a.cache = cache_args(cache);
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.max_context_len = (int32_t)(max_context_len < cap ? max_context_len : cap);
+  a.scale = scale;
+  a.partition_size = 0;
+  a.num_partitions = 1;
+  a.query_start = query_start;
+  a.max_query_len = max_query_len;
+  if (!pa::decode_mfma_supports(a))
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: prefill runs on the matrix cores only (f16 or bf16 cache with the same query "
+                "dtype, or fp8 cache with f16 queries; head_dim 64 or 128; at most 16 query heads "
+                "per KV head; 16-byte aligned query rows, 8-byte aligned output; a non-empty pool)",
+                who);
+  return launch_status(pa::launch_prefill_mfma(a, static_cast<hipStream_t>(stream)), who);
+}
+
 // The device-side address of memory the GPU can reach: device memory, or pinned host memory
 // (hipHostMalloc).  Pageable host memory, or a pointer HIP does not know, gives nullptr.
 static void *device_reachable(const void *p, bool host_only) {

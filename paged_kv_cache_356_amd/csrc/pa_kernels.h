@@ -71,6 +71,10 @@ struct DecodeArgs {
   const int32_t *prefix_table;
   int32_t prefix_len;       // multiple of 16
   int32_t prefix_chunks;    // ceil(prefix_len / kPrefixChunk)
+  // Prefill (a chunk of new tokens per sequence): sequence s's tokens are query rows
+  // query_start[s] .. query_start[s + 1] - 1, at positions context_lens[s] - n_s .. context_lens[s] - 1.
+  const int32_t *query_start;
+  int32_t max_query_len;    // host bound of query_start[s + 1] - query_start[s]
 };
 
 // Partition `part` of positions [base, L) (base a multiple of the block size) cut into
@@ -130,6 +134,7 @@ hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 bool decode_mfma_supports(const DecodeArgs &a);
 bool decode_mfma_supports_prefix(const DecodeArgs &a);
+hipError_t launch_prefill_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_partition_reduce(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace pa
