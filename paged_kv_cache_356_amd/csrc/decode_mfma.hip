@@ -36,12 +36,15 @@
 // (c & 0x80) << 8 | (c & 0x7f) << 7, whose value is exactly decode(c) * 2^-8 (normals and
 // subnormals alike); the 2^8 goes back into the per-head scales.  The NaN code is mapped to a NaN.
 //
-// Workgroup = 4 wavefronts for one (partition, KV head, sequence); wavefront w takes the
-// partition's blocks w, w+4, ... and keeps the loads of its next blocks in flight while it computes
-// the current one.  The four partial states are merged through LDS.
+// Work items: a wavefront takes one (sequence, partition, KV head) at a time and streams the
+// partition's blocks through a ring of register fragments, keeping the loads of its next blocks in
+// flight while it computes the current one; its result goes to the output, or to the workspace as
+// a partial for pa_partition_reduce.  A shared prefix is computed once for the whole batch by
+// workgroup-wide groups of 64 rows that stage each block in LDS.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
+#include <utility>
 
 #include "pa_device.h"
 #include "pa_kernels.h"
@@ -51,6 +54,15 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kMaxScanSeqs = 4096;  // persistent grid: sequences whose item prefix fits in LDS
+// The shared-prefix instantiation also holds the prefix groups' block stages in LDS; its scan
+// arrays are halved so that three workgroups still fit on a compute unit.
+constexpr int kMaxScanSeqsPrefix = 2048;
+#ifndef PA_PREFIX_TILES
+#define PA_PREFIX_TILES 1
+#endif
+// 16-row tiles per wavefront in a prefix group: each block staged in LDS serves 16 kPrefixTiles
+// rows per wavefront, so the group's L2 reads of the prefix fall with the group's size.
+constexpr int kPrefixTiles = PA_PREFIX_TILES;
 #ifndef PA_DECODE_BUFS
 #define PA_DECODE_BUFS 2
 #endif
@@ -237,12 +249,17 @@ __device__ __forceinline__ void load_block(const DecodeArgs &a, int bid, bool ok
     f.v[nt] = load_kv<typename F::VRaw, kNT>(rv, ((16 * nt + col) * kBlock + 4 * grp) * CT::bytes);
 }
 
-// One 16-token block at token tok0 into the state.  Scores of positions at or past `zlim` (per
-// lane) are masked; V elements of positions at or past `vlim` (wave-uniform) are zeroed.  zlim =
-// vlim = tok0 masks the whole block, which leaves the state unchanged.
+// The probabilities of one block for this lane's column, split p = hi + lo in the MFMA input type.
+struct BlockP {
+  uint2 hi, lo;
+};
+
+// First half of a block step: S^T = K Q^T for the block at token tok0, the online-softmax update
+// of the state's maximum and sum (rescaling the accumulator when the maximum moves), and the
+// probabilities.  Scores of positions at or past `zlim` (per lane) are masked.
 template <class CT, int D>
-__device__ __forceinline__ void block_step(const Frag<CT, D> &f, float kscale, int tok0, int zlim,
-                                           int vlim, RowState<D> &rs_) {
+__device__ __forceinline__ BlockP block_scores(const uint4 (&k)[Frag<CT, D>::kKLoads], float kscale,
+                                               int tok0, int zlim, RowState<D> &rs_) {
   constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
   constexpr bool kBF = std::is_same<CT, bf16_t>::value;  // fp8 and f16 caches compute in f16
   constexpr int KK = D / 32;
@@ -253,68 +270,90 @@ __device__ __forceinline__ void block_step(const Frag<CT, D> &f, float kscale, i
   float &m = rs_.m;
   float &l = rs_.l;
   auto &acc = rs_.acc;
-    // ---- S^T = K Q^T: lane holds the scores of tokens tok0 + 4 grp + i for head col
-    f4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (kFP8) {
+  // ---- S^T = K Q^T: lane holds the scores of tokens tok0 + 4 grp + i for head col
+  f4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (kFP8) {
 #pragma unroll
-      for (int i = 0; i < F::kKLoads; ++i) {
-        const uint2 a0 = e4m3x4_to_f16x4(f.k[i].x), a1 = e4m3x4_to_f16x4(f.k[i].y);
-        const uint2 a2 = e4m3x4_to_f16x4(f.k[i].z), a3 = e4m3x4_to_f16x4(f.k[i].w);
-        st = mma_k32<false>(make_uint4(a0.x, a0.y, a1.x, a1.y), qop[2 * i], st);
-        st = mma_k32<false>(make_uint4(a2.x, a2.y, a3.x, a3.y), qop[2 * i + 1], st);
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) st = mma_k32<kBF>(f.k[kk], qop[kk], st);
+    for (int i = 0; i < F::kKLoads; ++i) {
+      const uint2 a0 = e4m3x4_to_f16x4(k[i].x), a1 = e4m3x4_to_f16x4(k[i].y);
+      const uint2 a2 = e4m3x4_to_f16x4(k[i].z), a3 = e4m3x4_to_f16x4(k[i].w);
+      st = mma_k32<false>(make_uint4(a0.x, a0.y, a1.x, a1.y), qop[2 * i], st);
+      st = mma_k32<false>(make_uint4(a2.x, a2.y, a3.x, a3.y), qop[2 * i + 1], st);
     }
-    const int t0 = tok0 + 4 * grp;
-    float z[4];
-    float mx = -INFINITY;
+  } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = t0 + i < zlim ? st[i] * kscale : -INFINITY;  // select: tail slots never leak
-      mx = fmaxf(mx, z[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Lazy rescaling: the running maximum of a head moves only when a block's maximum exceeds it
-    // by more than kSlack (base 2), so probabilities stay below 2^kSlack and the accumulator is
-    // rescaled on a few blocks instead of every one.  The first block always moves it (m = -inf).
-    const bool grow = mx > m + kSlack;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
-      const float mn = grow ? mx : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first block, else <= 1
-      l *= alpha;
+    for (int kk = 0; kk < KK; ++kk) st = mma_k32<kBF>(k[kk], qop[kk], st);
+  }
+  const int t0 = tok0 + 4 * grp;
+  float z[4];
+  float mx = -INFINITY;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
-      m = mn;
-    }
-    float p[4];
+  for (int i = 0; i < 4; ++i) {
+    z[i] = t0 + i < zlim ? st[i] * kscale : -INFINITY;  // select: tail slots never leak
+    mx = fmaxf(mx, z[i]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // Lazy rescaling: the running maximum of a head moves only when a block's maximum exceeds it
+  // by more than kSlack (base 2), so probabilities stay below 2^kSlack and the accumulator is
+  // rescaled on a few blocks instead of every one.  The first block always moves it (m = -inf).
+  const bool grow = mx > m + kSlack;
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
+    const float mn = grow ? mx : m;
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first block, else <= 1
+    l *= alpha;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - m);
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-    uint2 phi, plo;
-    phi.x = pack2<kBF>(p[0], p[1]);
-    phi.y = pack2<kBF>(p[2], p[3]);
-    plo.x = pack2<kBF>(p[0] - unpack_lo<kBF>(phi.x), p[1] - unpack_hi<kBF>(phi.x));
-    plo.y = pack2<kBF>(p[2] - unpack_lo<kBF>(phi.y), p[3] - unpack_hi<kBF>(phi.y));
+    for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
+    m = mn;
+  }
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - m);
+  l += (p[0] + p[1]) + (p[2] + p[3]);
+  BlockP r;
+  r.hi.x = pack2<kBF>(p[0], p[1]);
+  r.hi.y = pack2<kBF>(p[2], p[3]);
+  r.lo.x = pack2<kBF>(p[0] - unpack_lo<kBF>(r.hi.x), p[1] - unpack_hi<kBF>(r.hi.x));
+  r.lo.y = pack2<kBF>(p[2] - unpack_lo<kBF>(r.hi.y), p[3] - unpack_hi<kBF>(r.hi.y));
+  return r;
+}
 
-    // ---- O^T += V^T P^T; V elements of tail tokens are zeroed (select), so NaN there cannot leak
-    const bool tail = tok0 + kBlock > vlim;  // wave-uniform
-    const uint32_t keep0 = (t0 + 0 < vlim ? 0xffffu : 0u) | (t0 + 1 < vlim ? 0xffff0000u : 0u);
-    const uint32_t keep1 = (t0 + 2 < vlim ? 0xffffu : 0u) | (t0 + 3 < vlim ? 0xffff0000u : 0u);
+// Second half: O^T += V^T P^T.  V elements of positions at or past `vlim` (wave-uniform) are
+// zeroed (select), so NaN there cannot leak.
+template <class CT, int D>
+__device__ __forceinline__ void block_values(const typename Frag<CT, D>::VRaw (&v)[Frag<CT, D>::kNT],
+                                             const BlockP &pr, int tok0, int vlim,
+                                             RowState<D> &rs_) {
+  constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
+  constexpr bool kBF = std::is_same<CT, bf16_t>::value;
+  constexpr int NT = Frag<CT, D>::kNT;
+  const int grp = (threadIdx.x & 63) >> 4;
+  const int t0 = tok0 + 4 * grp;
+  const bool tail = tok0 + kBlock > vlim;  // wave-uniform
+  const uint32_t keep0 = (t0 + 0 < vlim ? 0xffffu : 0u) | (t0 + 1 < vlim ? 0xffff0000u : 0u);
+  const uint32_t keep1 = (t0 + 2 < vlim ? 0xffffu : 0u) | (t0 + 3 < vlim ? 0xffff0000u : 0u);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      uint2 vop;
-      if constexpr (kFP8) vop = e4m3x4_to_f16x4(f.v[nt]);
-      else vop = f.v[nt];
-      if (tail) {
-        vop.x &= keep0;
-        vop.y &= keep1;
-      }
-      const f4_t c = mma_k16<kBF>(vop, phi, acc[nt]);
-      acc[nt] = mma_k16<kBF>(vop, plo, c);
+  for (int nt = 0; nt < NT; ++nt) {
+    uint2 vop;
+    if constexpr (kFP8) vop = e4m3x4_to_f16x4(v[nt]);
+    else vop = v[nt];
+    if (tail) {
+      vop.x &= keep0;
+      vop.y &= keep1;
     }
+    const f4_t c = mma_k16<kBF>(vop, pr.hi, rs_.acc[nt]);
+    rs_.acc[nt] = mma_k16<kBF>(vop, pr.lo, c);
+  }
+}
+
+// One 16-token block at token tok0 into the state.  Scores of positions at or past `zlim` (per
+// lane) are masked; V elements of positions at or past `vlim` (wave-uniform) are zeroed.  zlim =
+// vlim = tok0 masks the whole block, which leaves the state unchanged.
+template <class CT, int D>
+__device__ __forceinline__ void block_step(const Frag<CT, D> &f, float kscale, int tok0, int zlim,
+                                           int vlim, RowState<D> &rs_) {
+  const BlockP pr = block_scores<CT, D>(f.k, kscale, tok0, zlim, rs_);
+  block_values<CT, D>(f.v, pr, tok0, vlim, rs_);
 }
 
 // An empty asm that reads and writes every register of a fragment: the compiler must wait for the
@@ -442,13 +481,14 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs &a, int s) {
 // (tiles that other wavefronts of the call read too).  tbl0: lane i's entry of the first 64
 // blocks (first_table_entries).  settle: a value whose load is in flight (the next item's first
 // table entries), waited for once this item's blocks are done.
+template <class QT, int D>
+__device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D> &st, float vscale,
+                                          int slot, int rs, int rhq, bool rvalid);
+
 template <class CT, class QT, int D, bool kNT>
 __device__ __forceinline__ void rows_core(const DecodeArgs &a, const int32_t *table, int h,
                                           int jb0, int jb1, int end, int slot, int rs, int rhq,
                                           bool rvalid, int lim, int tbl0, int &settle) {
-  constexpr int NT = D / 16;
-  const int Hq = a.num_q_heads;
-  const int grp = (threadIdx.x & 63) >> 4;
   RowState<D> st;
   load_query<CT, D>(a, rs, rhq, rvalid, st);
   float kscale, vscale;
@@ -462,7 +502,16 @@ __device__ __forceinline__ void rows_core(const DecodeArgs &a, const int32_t *ta
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk)
     asm volatile("" : "+v"(st.qop[kk].x), "+v"(st.qop[kk].y), "+v"(st.qop[kk].z), "+v"(st.qop[kk].w));
+  emit_rows<QT, D>(a, st, vscale, slot, rs, rhq, rvalid);
+}
 
+// A finished row state to the output (slot < 0) or to workspace partition `slot`.
+template <class QT, int D>
+__device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D> &st, float vscale,
+                                          int slot, int rs, int rhq, bool rvalid) {
+  constexpr int NT = D / 16;
+  const int Hq = a.num_q_heads;
+  const int grp = (threadIdx.x & 63) >> 4;
   // the row's sum over the four lane groups; m is already uniform over them
   float l = st.l;
   l += __shfl_xor(l, 16);
@@ -530,6 +579,189 @@ __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int row
   rows_core<CT, QT, D, kNT>(a, table, h, jb0, jb1, end, slot, rs, rhq, rvalid, lim, tbl0, settle);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Prefix groups through LDS.  The four wavefronts of a workgroup take 64 flat rows of one KV head
+// over the same blocks of the shared prefix, so each block is fetched once per workgroup: every
+// wavefront copies its share of the block's K and V tiles straight into an LDS stage (buffer loads
+// with the LDS destination, no registers), the workgroup meets at a barrier, and each wavefront
+// reads the whole block back from LDS into the fragment layout of the register ring.  kStages
+// stages keep kStages - 1 blocks in flight while one is computed.  Each stage is a variable of its
+// own, so the compiler can tell a read of one stage from the copies still landing in the others.
+
+// f(std::integral_constant<int, i>) for i = I .. N - 1, in order.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+#define PA_LDS __attribute__((address_space(3)))  // LDS pointers
+
+template <class CT, int D>
+struct PrefixStages {
+  static constexpr int kTileBytes = kBlock * D * CT::bytes;
+  static constexpr int kBytes = 2 * kTileBytes;  // K tile, then V tile
+  static constexpr int kChunks = kBytes / 1024;  // 1 KiB copies (64 lanes x 16 bytes) per block
+  static constexpr int kPerWave = (kChunks + kWaves - 1) / kWaves;
+  static constexpr int kStages = kBytes >= 8192 ? 4 : 8;
+  static_assert(kChunks >= 2 && (kChunks % kWaves == 0 || kChunks < kWaves), "stage split");
+};
+
+template <int kBytes, int I>
+__device__ __forceinline__ PA_LDS char *prefix_stage() {
+  __shared__ __attribute__((aligned(16))) char stage[kBytes];
+  return (PA_LDS char *)stage;
+}
+
+// This wavefront's share of the K and V tiles of block bid (KV head h) into stage I; a slot
+// without a block (ok = false) copies through an empty descriptor and touches no memory.
+template <class CT, int D, int I>
+__device__ __forceinline__ void stage_block(const DecodeArgs &a, int bid, bool ok, int h) {
+  using P = PrefixStages<CT, D>;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const size_t tile = ((size_t)(ok ? bid : 0) * a.cache.num_kv_heads + h) * P::kTileBytes;
+  const int n = ok ? P::kTileBytes : 0;
+  const auto rk = tile_rsrc(static_cast<const char *>(a.cache.k_pool) + tile, n);
+  const auto rv = tile_rsrc(static_cast<const char *>(a.cache.v_pool) + tile, n);
+  auto *stage = prefix_stage<P::kBytes, I>();
+#pragma unroll
+  for (int i = 0; i < P::kPerWave; ++i) {
+    const int c = w + kWaves * i;  // 1 KiB chunk of the stage
+    if (P::kChunks % kWaves == 0 || c < P::kChunks) {
+      const bool v = c * 1024 >= P::kTileBytes;
+      const int off = c * 1024 - (v ? P::kTileBytes : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(v ? rv : rk,
+                                               (PA_LDS void *)(stage + c * 1024),
+                                               16, off + 16 * lane, 0, 0, 0);
+    }
+  }
+}
+
+template <class T>
+__device__ __forceinline__ T lds_load(const PA_LDS char *p) {
+  if constexpr (sizeof(T) == 16) return __builtin_bit_cast(T, *(const PA_LDS u32x4_t *)p);
+  else if constexpr (sizeof(T) == 8) return __builtin_bit_cast(T, *(const PA_LDS u32x2_t *)p);
+  else return __builtin_bit_cast(T, *(const PA_LDS uint32_t *)p);
+}
+
+// The K and V tiles of stage I into registers, at the offsets load_block reads them at.
+template <class CT, int D, int I, int N>
+__device__ __forceinline__ void read_stage_k(uint4 (&k)[N]) {
+  static_assert(N == Frag<CT, D>::kKLoads, "K fragment");
+  using P = PrefixStages<CT, D>;
+  const int lane = threadIdx.x & 63;
+  const auto *stage = prefix_stage<P::kBytes, I>();
+#pragma unroll
+  for (int i = 0; i < N; ++i) k[i] = lds_load<uint4>(stage + (lane + 64 * i) * 16);
+}
+
+template <class CT, int D, int I, class VR, int N>
+__device__ __forceinline__ void read_stage_v(VR (&v)[N]) {
+  static_assert(N == Frag<CT, D>::kNT, "V fragment");
+  using P = PrefixStages<CT, D>;
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  const auto *stage = prefix_stage<P::kBytes, I>();
+#pragma unroll
+  for (int nt = 0; nt < N; ++nt)
+    v[nt] = lds_load<VR>(stage + P::kTileBytes + ((16 * nt + col) * kBlock + 4 * grp) * CT::bytes);
+}
+
+// Wait until at most N of this wavefront's memory reads are outstanding (its LDS copies land in
+// order), then for its LDS reads, then meet the workgroup.  The memory clobber keeps the compiler
+// from moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Prefix group: kPrefixTiles tiles of 16 flat rows per wavefront, wavefront w taking rows
+// row0 + 16 kPrefixTiles w .. (flat row r is query head h*g + r % g of sequence r / g; rows past
+// the batch are padding), all over prefix blocks [jb0, jb1), jb1 - jb0 <= 64, whose ids are lane
+// i's `tbl` (first_table_entries).  The whole workgroup calls this with the same arguments; each
+// block read from LDS serves all of the wavefront's tiles.  Each row masks the positions at or
+// past its own context length (`lens`).
+template <class CT, class QT, int D>
+__device__ __forceinline__ void prefix_group(const DecodeArgs &a, const int *lens, int h_in,
+                                             int row0_in, int jb0_in, int jb1_in, int end_in,
+                                             int slot_in, int tbl) {
+  using P = PrefixStages<CT, D>;
+  constexpr int kS = P::kStages;
+  constexpr int kT = kPrefixTiles;
+  const int h = __builtin_amdgcn_readfirstlane(h_in);
+  const int row0 = __builtin_amdgcn_readfirstlane(row0_in);
+  const int jb0 = __builtin_amdgcn_readfirstlane(jb0_in);
+  const int jb1 = __builtin_amdgcn_readfirstlane(jb1_in);
+  const int end = __builtin_amdgcn_readfirstlane(end_in);
+  const int slot = __builtin_amdgcn_readfirstlane(slot_in);
+  const int H = a.cache.num_kv_heads, g = a.num_q_heads / H;
+  const int col = threadIdx.x & 15;
+  RowState<D> st[kT];
+  bool rvalid[kT];
+  int rs[kT], rhq[kT], lim[kT];
+#pragma unroll
+  for (int j = 0; j < kT; ++j) {
+    const int r = row0 + 16 * j + col;  // past the batch: padding (a whole tile may be padding)
+    rvalid[j] = r < a.num_seqs * g;
+    rs[j] = rvalid[j] ? r / g : 0;
+    rhq[j] = h * g + (rvalid[j] ? r % g : 0);
+    lim[j] = rvalid[j] ? min(end, lens[rs[j]]) : end;
+    load_query<CT, D>(a, rs[j], rhq[j], rvalid[j], st[j]);
+  }
+  float kscale, vscale;
+  head_scales<CT>(a, h, kscale, vscale);
+  const int nb = a.cache.num_blocks;
+  const int nk = jb1 - jb0;
+  auto issue = [&](auto I, int k) {  // block k into stage I (past the end: an empty copy)
+    const int bid = k < nk ? __builtin_amdgcn_readlane(tbl, k < 64 ? k : 63) : -1;
+    stage_block<CT, D, decltype(I)::value>(a, bid, (unsigned)bid < (unsigned)nb, h);
+  };
+  auto step = [&](auto I, int k) {  // compute block k from stage I, refill the previous stage
+    constexpr int i = decltype(I)::value;
+    stage_barrier<P::kPerWave * (kS - 2)>();  // block k landed for every wavefront
+    issue(std::integral_constant<int, (i + kS - 1) % kS>{}, k + kS - 1);
+    const int bid = __builtin_amdgcn_readlane(tbl, k < 64 ? k : 63);
+    const bool ok = (unsigned)bid < (unsigned)nb;
+    const int t0 = (jb0 + k) * kBlock;
+    // K for every tile, then V for every tile: one tile's worth of block registers at a time
+    BlockP pr[kT];
+    {
+      uint4 kf[Frag<CT, D>::kKLoads];
+      read_stage_k<CT, D, i>(kf);
+#pragma unroll
+      for (int j = 0; j < kT; ++j) pr[j] = block_scores<CT, D>(kf, kscale, t0, ok ? lim[j] : t0, st[j]);
+    }
+    typename Frag<CT, D>::VRaw vf[Frag<CT, D>::kNT];
+    read_stage_v<CT, D, i>(vf);
+#pragma unroll
+    for (int j = 0; j < kT; ++j) block_values<CT, D>(vf, pr[j], t0, ok ? end : t0, st[j]);
+  };
+  // The block ids and the queries arrive before the first copy is issued: a wait for them after it
+  // would also wait for the copy.  The stages' previous readers (the workgroup's last block) are
+  // done before they are refilled.
+  asm volatile("" : "+v"(tbl));
+#pragma unroll
+  for (int j = 0; j < kT; ++j)
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      asm volatile("" : "+v"(st[j].qop[kk].x), "+v"(st[j].qop[kk].y), "+v"(st[j].qop[kk].z),
+                   "+v"(st[j].qop[kk].w));
+  stage_barrier<63>();
+  static_for<0, kS - 1>([&](auto I) { issue(I, decltype(I)::value); });
+  // Full rounds run every step without a branch, so the compiler knows at each LDS read which
+  // copies are still in flight; the last round (fewer than kS blocks) is guarded.
+  int k0 = 0;
+  for (; k0 + kS <= nk; k0 += kS) static_for<0, kS>([&](auto I) { step(I, k0 + decltype(I)::value); });
+  static_for<0, kS>([&](auto I) {
+    if (k0 + decltype(I)::value < nk) step(I, k0 + decltype(I)::value);
+  });
+#pragma unroll
+  for (int j = 0; j < kT; ++j) emit_rows<QT, D>(a, st[j], vscale, slot, rs[j], rhq[j], rvalid[j]);
+}
+
 // Items of sequence s: plain decode, partitions of its context (an empty context counts one item,
 // which writes its zeros); shared-prefix decode, partitions of the positions after the prefix
 // (possibly none).
@@ -582,12 +814,11 @@ __device__ __forceinline__ void run_sequence_item(const DecodeArgs &a, const Seq
 // of the sequences' item counts that every workgroup computes in LDS.
 // With a shared prefix, the prefix is cut into groups of 64 flat rows (sequence, query head) of
 // one KV head and chunks of up to kPrefixChunk positions; workgroup b takes groups b, b + G, ...
-// (G workgroups), its wavefront w the group's rows 16 w .. 16 w + 15.  The four wavefronts walk
-// the same blocks in the same order with ordinary loads, so the compute unit's cache serves the
-// same tile to all four and each block crosses from L2 about once per group instead of once per
-// 16 rows.  The sequence items go first to the wavefronts of workgroups without prefix work, so
+// (G workgroups), its wavefront w the group's rows 16 w .. 16 w + 15.  The four wavefronts share
+// each block through LDS (prefix_group), so a block crosses from L2 once per group instead of once
+// per 16 rows.  The sequence items go first to the wavefronts of workgroups without prefix work, so
 // the streaming of private blocks from HBM starts at once beside the prefix groups.
-template <class CT, class QT, int D>
+template <class CT, class QT, int D, bool kPre>
 __global__ __launch_bounds__(256)
 #if PA_DECODE_OCC
 __attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
@@ -613,8 +844,9 @@ void decode_mfma_kernel(DecodeArgs a) {
     }
     return;
   }
-  __shared__ int prefix[kMaxScanSeqs + 1];  // items of the sequences before s
-  __shared__ int lens[kMaxScanSeqs];        // clamped context lengths
+  constexpr int kScan = kPre ? kMaxScanSeqsPrefix : kMaxScanSeqs;
+  __shared__ int prefix[kScan + 1];  // items of the sequences before s
+  __shared__ int lens[kScan];        // clamped context lengths
   __shared__ int wave_tot[kWaves];
   // thread t counts the items of sequences [t * per, (t + 1) * per)
   const int per = (S + 255) / 256;
@@ -648,18 +880,18 @@ void decode_mfma_kernel(DecodeArgs a) {
 
   // Prefix groups: list order (chunk, 64-row group, KV head) with the KV head fastest.
   const int G = gridDim.x;
-  const int n_groups = a.prefix_len > 0 ? (S * g + 63) / 64 : 0;
+  constexpr int kGroupRows = 16 * kPrefixTiles * kWaves;
+  const int n_groups = kPre && a.prefix_len > 0 ? (S * g + kGroupRows - 1) / kGroupRows : 0;
   const int n_pre = n_groups * a.prefix_chunks * H;
-  for (int i = blockIdx.x; i < n_pre; i += G) {
-    const int h = i % H, t = (i / H) % n_groups, c = i / (H * n_groups);
-    const int row0 = 64 * t + 16 * w;
-    if (row0 >= S * g) continue;  // the last group's unused tiles
-    const int start = c * kPrefixChunk;
-    const int end = min(a.prefix_len, start + kPrefixChunk);
-    int none = 0;
-    wave_item<CT, QT, D, false>(a, -1, row0, h, start / kBlock, end / kBlock, end, c, lens,
-                                first_table_entries(a.prefix_table, start / kBlock, end / kBlock),
-                                none);
+  if constexpr (kPre) {
+    for (int i = blockIdx.x; i < n_pre; i += G) {
+      const int h = i % H, t = (i / H) % n_groups, c = i / (H * n_groups);
+      const int start = c * kPrefixChunk;
+      const int end = min(a.prefix_len, start + kPrefixChunk);
+      prefix_group<CT, QT, D>(a, lens, h, kGroupRows * t + 16 * kPrefixTiles * w, start / kBlock,
+                              end / kBlock, end, c,
+                              first_table_entries(a.prefix_table, start / kBlock, end / kBlock));
+    }
   }
   // The sequences' items, one per wavefront.  Wavefronts are ranked so that those of workgroups
   // without prefix work come first, each class wavefront-major (wavefront w of every workgroup
@@ -761,7 +993,7 @@ hipError_t launch_prefill_d(const DecodeArgs &a, hipStream_t s) {
 
 // Workgroups of one instantiation that fit on the device at once (occupancy x compute units),
 // looked up once per device.
-template <class CT, class QT, int D>
+template <class CT, class QT, int D, bool kPre>
 int resident_groups() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];
@@ -772,7 +1004,8 @@ int resident_groups() {
     if (c > 0) return c;
   }
   int occ = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_mfma_kernel<CT, QT, D>, 256, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_mfma_kernel<CT, QT, D, kPre>, 256,
+                                                   0) !=
           hipSuccess || occ < 1)
     occ = 1;
   if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
@@ -783,17 +1016,22 @@ int resident_groups() {
   return n;
 }
 
-template <class CT, class QT, int D>
-hipError_t launch_dd(DecodeArgs a, hipStream_t s) {
+template <class CT, class QT, int D, bool kPre>
+hipError_t launch_ddp(DecodeArgs a, hipStream_t s) {
   const int64_t items = (int64_t)a.num_partitions * a.cache.num_kv_heads * a.num_seqs;
   const int64_t direct = (items + kWaves - 1) / kWaves;  // one wavefront per item
-  a.persistent = a.num_seqs <= kMaxScanSeqs;
+  a.persistent = a.num_seqs <= (kPre ? kMaxScanSeqsPrefix : kMaxScanSeqs);
   dim3 grid((unsigned)direct);
   if (a.persistent)
-    grid = dim3((unsigned)(PA_SPREAD ? resident_groups<CT, QT, D>()
-                                     : std::min<int64_t>(direct, resident_groups<CT, QT, D>())));
-  decode_mfma_kernel<CT, QT, D><<<grid, dim3(256), 0, s>>>(a);
+    grid = dim3((unsigned)(PA_SPREAD ? resident_groups<CT, QT, D, kPre>()
+                                     : std::min<int64_t>(direct, resident_groups<CT, QT, D, kPre>())));
+  decode_mfma_kernel<CT, QT, D, kPre><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <class CT, class QT, int D>
+hipError_t launch_dd(const DecodeArgs &a, hipStream_t s) {
+  return a.prefix_len > 0 ? launch_ddp<CT, QT, D, true>(a, s) : launch_ddp<CT, QT, D, false>(a, s);
 }
 
 template <class CT, class QT>
@@ -804,8 +1042,8 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
 }  // namespace
 
 bool decode_mfma_supports_prefix(const DecodeArgs &a) {
-  // the prefix tiles exist only in the persistent grid
-  return decode_mfma_supports(a) && a.num_seqs <= kMaxScanSeqs;
+  // the prefix groups exist only in the persistent grid
+  return decode_mfma_supports(a) && a.num_seqs <= kMaxScanSeqsPrefix;
 }
 
 bool decode_mfma_supports(const DecodeArgs &a) {
