@@ -938,49 +938,322 @@ void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
 // Prefill (a chunk of n new tokens per sequence, positions L - n .. L - 1; the token at position p
-// attends to positions 0 .. p): workgroup (s, h, group) takes 64 rows of sequence s and KV head h
-// (row r is token r / g, query head h*g + r % g), its wavefront w rows 16 w .. 16 w + 15.  Each row
-// masks the positions past its own; the wavefront streams the blocks up to its last row's
-// position.  The four wavefronts of a workgroup walk the same blocks with ordinary loads, and so do
-// the sequence's other workgroups, so the caches serve most of the re-reads.  Rows are complete
-// in one wavefront: the outputs are written directly, no workspace.
+// attends to positions 0 .. p).  Unlike decode, every block serves many rows, so the work is
+// matrix-core bound, not memory bound, and is arranged for the products:
+//  - workgroup (s, h, group) takes kPrefillRows rows of sequence s and KV head h (row r is token
+//    r / g, query head h*g + r % g), its wavefront w kPrefillTiles tiles of 16 rows;
+//  - the blocks go through LDS two at a time (a pair: 32 positions), copied straight from the pool
+//    by the four wavefronts and read back by each, so a block is fetched once per 128 rows;
+//  - the scores of both blocks of a pair are taken together (one maximum update), and P V runs
+//    as one 16x16x32 product per 16 head dims over the pair's 32 positions, the pair's positions
+//    ordered so that each lane's four probabilities of each block (the lane layout the scores come
+//    in) are its eight consecutive reduction indices, and the V^T operand gathers the same four
+//    positions of each block;
+//  - probabilities are rounded once to the input type (no hi + lo split): each output averages
+//    many positions, so the rounding of single probabilities does not accumulate.
+// Each row masks the positions past its own; the workgroup walks the blocks up to its last row's
+// position, in rounds of 64 blocks (one table fetch per round).  Rows are complete in one
+// wavefront: the outputs are written directly, no workspace.
+constexpr int kPrefillTiles = 2;
+constexpr int kXcds = 8;  // accelerator complex dies; workgroups are dealt to them round-robin
+constexpr int kPrefillRows = 16 * kPrefillTiles * kWaves;
+
+template <class CT, int D>
+struct PairStages {
+  static constexpr int kTileBytes = kBlock * D * CT::bytes;
+  static constexpr int kBlockBytes = 2 * kTileBytes;  // K tile, then V tile
+  static constexpr int kBytes = 2 * kBlockBytes;      // block A, then block B
+  static constexpr int kChunks = kBytes / 1024;       // 1 KiB copies per pair
+  static constexpr int kPerWave = kChunks / kWaves;
+  static constexpr int kStages = 4;
+  static_assert(kChunks % kWaves == 0, "pair split");
+};
+
+// This wavefront's share of the pair (blocks ba, bb of KV head h) into stage I.
+template <class CT, int D, int I>
+__device__ __forceinline__ void stage_pair(const DecodeArgs &a, int ba, bool oka, int bb, bool okb,
+                                           int h) {
+  using P = PairStages<CT, D>;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = a.cache.num_kv_heads;
+  const char *kp = static_cast<const char *>(a.cache.k_pool);
+  const char *vp = static_cast<const char *>(a.cache.v_pool);
+  const size_t ta = ((size_t)(oka ? ba : 0) * H + h) * P::kTileBytes;
+  const size_t tb = ((size_t)(okb ? bb : 0) * H + h) * P::kTileBytes;
+  const auto rka = tile_rsrc(kp + ta, oka ? P::kTileBytes : 0);
+  const auto rva = tile_rsrc(vp + ta, oka ? P::kTileBytes : 0);
+  const auto rkb = tile_rsrc(kp + tb, okb ? P::kTileBytes : 0);
+  const auto rvb = tile_rsrc(vp + tb, okb ? P::kTileBytes : 0);
+  auto *stage = prefix_stage<P::kBytes, 16 + I>();
+#pragma unroll
+  for (int i = 0; i < P::kPerWave; ++i) {
+    const int c = w + kWaves * i;  // 1 KiB chunk of the stage
+    const int cb = c * 1024 / P::kBlockBytes, off = c * 1024 - cb * P::kBlockBytes;
+    const bool v = off >= P::kTileBytes;
+    const auto r = cb ? (v ? rvb : rkb) : (v ? rva : rka);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)(stage + c * 1024), 16,
+                                             off - (v ? P::kTileBytes : 0) + 16 * lane, 0, 0, 0);
+  }
+}
+
+template <class CT, int D, int I, int kOff, int N>
+__device__ __forceinline__ void read_pair_k(uint4 (&k)[N]) {
+  using P = PairStages<CT, D>;
+  const int lane = threadIdx.x & 63;
+  const auto *stage = prefix_stage<P::kBytes, 16 + I>() + kOff;
+#pragma unroll
+  for (int i = 0; i < N; ++i) k[i] = lds_load<uint4>(stage + (lane + 64 * i) * 16);
+}
+
+template <class CT, int D, int I, int kOff, class VR, int N>
+__device__ __forceinline__ void read_pair_v(VR (&v)[N]) {
+  using P = PairStages<CT, D>;
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  const auto *stage = prefix_stage<P::kBytes, 16 + I>() + kOff + P::kTileBytes;
+#pragma unroll
+  for (int nt = 0; nt < N; ++nt)
+    v[nt] = lds_load<VR>(stage + ((16 * nt + col) * kBlock + 4 * grp) * CT::bytes);
+}
+
+// S^T of one 16-token block against this wavefront tile's query rows (raw products).
+template <class CT, int D, int N>
+__device__ __forceinline__ f4_t block_qk(const uint4 (&k)[N], const RowState<D> &rs_) {
+  constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
+  constexpr bool kBF = std::is_same<CT, bf16_t>::value;
+  f4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (kFP8) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint2 a0 = e4m3x4_to_f16x4(k[i].x), a1 = e4m3x4_to_f16x4(k[i].y);
+      const uint2 a2 = e4m3x4_to_f16x4(k[i].z), a3 = e4m3x4_to_f16x4(k[i].w);
+      st = mma_k32<false>(make_uint4(a0.x, a0.y, a1.x, a1.y), rs_.qop[2 * i], st);
+      st = mma_k32<false>(make_uint4(a2.x, a2.y, a3.x, a3.y), rs_.qop[2 * i + 1], st);
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < N; ++kk) st = mma_k32<kBF>(k[kk], rs_.qop[kk], st);
+  }
+  return st;
+}
+
+// Maximum over the four 16-lane rows of a wavefront (lanes c, c + 16, c + 32, c + 48), by two
+// lane swaps on the vector ALU (no LDS round trip).
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Softmax update over a pair (block A at tok0, block B at tok0 + 16) from the raw scores sa, sb:
+// positions at or past zla (block A) / zlb (block B) are masked, unless kFull (the caller knows
+// every position of the pair is inside every row's limit).  Returns P^T for the pair's PV
+// product: reduction index 8 grp + i is block A's position 4 grp + i for i < 4, block B's
+// position 4 grp + i - 4 otherwise.
+template <class CT, int D, bool kFull>
+__device__ __forceinline__ uint4 pair_softmax(f4_t sa, f4_t sb, float kscale, int tok0, int zla,
+                                              int zlb, RowState<D> &rs_) {
+  constexpr bool kBF = std::is_same<CT, bf16_t>::value;
+  constexpr int NT = D / 16;
+  const int grp = (threadIdx.x & 63) >> 4;
+  const int t0 = tok0 + 4 * grp;
+  float z[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (kFull) {
+      z[i] = sa[i] * kscale;
+      z[4 + i] = sb[i] * kscale;
+    } else {
+      z[i] = t0 + i < zla ? sa[i] * kscale : -INFINITY;
+      z[4 + i] = t0 + 16 + i < zlb ? sb[i] * kscale : -INFINITY;
+    }
+    mx = fmaxf(mx, fmaxf(z[i], z[4 + i]));
+  }
+  mx = max_over_rows(mx);
+  float &m = rs_.m;
+  const bool grow = mx > m + kSlack;
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const float mn = grow ? mx : m;
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    rs_.l *= alpha;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) rs_.acc[nt] *= alpha;
+    m = mn;
+  }
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - m);
+  rs_.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  return make_uint4(pack2<kBF>(p[0], p[1]), pack2<kBF>(p[2], p[3]), pack2<kBF>(p[4], p[5]),
+                    pack2<kBF>(p[6], p[7]));
+}
+
+// Masks that zero the V elements of positions at or past vla (block A at tok0) / vlb (block B at
+// tok0 + 16) in this lane's four positions of each block.
+__device__ __forceinline__ uint4 pair_keep(int tok0, int vla, int vlb) {
+  const int t0 = tok0 + 4 * ((threadIdx.x & 63) >> 4);
+  return make_uint4((t0 + 0 < vla ? 0xffffu : 0u) | (t0 + 1 < vla ? 0xffff0000u : 0u),
+                    (t0 + 2 < vla ? 0xffffu : 0u) | (t0 + 3 < vla ? 0xffff0000u : 0u),
+                    (t0 + 16 < vlb ? 0xffffu : 0u) | (t0 + 17 < vlb ? 0xffff0000u : 0u),
+                    (t0 + 18 < vlb ? 0xffffu : 0u) | (t0 + 19 < vlb ? 0xffff0000u : 0u));
+}
+
+// V^T operand of the pair for head-dim rows 16 nt + col: block A's 4 positions then block B's,
+// masked by `keep` (a select: NaN in masked positions cannot leak).
+template <class CT, class VR>
+__device__ __forceinline__ uint4 pair_vop(VR va, VR vb, uint4 keep) {
+  constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
+  uint2 x, y;
+  if constexpr (kFP8) {
+    x = e4m3x4_to_f16x4(va);
+    y = e4m3x4_to_f16x4(vb);
+  } else {
+    x = va;
+    y = vb;
+  }
+  return make_uint4(x.x & keep.x, x.y & keep.y, y.x & keep.z, y.y & keep.w);
+}
+
 template <class CT, class QT, int D>
-__global__ __launch_bounds__(256)
-#if PA_DECODE_OCC
-__attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
-#endif
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_mfma_kernel(DecodeArgs a) {
+  using P = PairStages<CT, D>;
+  using F = Frag<CT, D>;
+  constexpr int kS = P::kStages;
+  constexpr int kT = kPrefillTiles;
+  constexpr bool kBF = std::is_same<CT, bf16_t>::value;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.cache.num_kv_heads, g = a.num_q_heads / H;
-  const int groups = (a.max_query_len * g + 63) / 64;
-  const int gi = blockIdx.x % groups, sh = blockIdx.x / groups;
+  const int groups = (a.max_query_len * g + kPrefillRows - 1) / kPrefillRows;
+  // Workgroup b runs on XCD b % 8 (round-robin dispatch); each XCD takes a contiguous range of the
+  // list (sequence, KV head, group), so the groups that re-read one sequence's blocks share an L2.
+  // Within a (sequence, KV head) the longest groups (the last rows of a prompt attend to the most
+  // positions) come first.
+  const int per_xcd = (int)(gridDim.x / kXcds);
+  const int f = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  if (f >= a.num_seqs * H * groups) return;  // the grid's padding to a multiple of kXcds
+  const int gi = groups - 1 - f % groups;
+  const int sh = f / groups;
   const int h = sh % H, s = sh / H;
   const int qs = a.query_start[s];
   const int n = min(a.query_start[s + 1] - qs, a.max_query_len);
   const int L = clamp_len(a, s);
-  const int row0 = 64 * gi + 16 * w;
-  if (n <= 0 || row0 >= n * g) return;  // wave-uniform
-  const int last = min(row0 + 15, n * g - 1);
-  const int end = max(0, min(L, L - n + last / g + 1));  // the wavefront's last row's limit
+  const int nrows = n * g;
+  const int rbase = kPrefillRows * gi;
+  if (n <= 0 || rbase >= nrows) return;  // workgroup-uniform, before any barrier
+  const int last = min(rbase + kPrefillRows - 1, nrows - 1);
+  const int end = max(0, min(L, L - n + last / g + 1));  // the workgroup's last row's limit
   const int col = threadIdx.x & 15;
-  const int r = row0 + col;
-  const bool rvalid = r < n * g;
-  const int t = rvalid ? r / g : 0;
-  const int lim = max(0, min(L, L - n + t + 1));
+  // Positions below this need no mask for any row of the wavefront: its first valid row's limit
+  // (a wavefront of padding rows only: the workgroup's end).
+  const int wrow = rbase + 16 * kT * w;
+  const int wlim = wrow < nrows ? min(end, max(0, min(L, L - n + wrow / g + 1))) : end;
+  RowState<D> st[kT];
+  bool rvalid[kT];
+  int rs[kT], rhq[kT], lim[kT];
+#pragma unroll
+  for (int j = 0; j < kT; ++j) {
+    const int r = rbase + 16 * (kT * w + j) + col;
+    rvalid[j] = r < nrows;
+    const int t = rvalid[j] ? r / g : 0;
+    rs[j] = qs + t;
+    rhq[j] = h * g + (rvalid[j] ? r % g : 0);
+    lim[j] = max(0, min(L, L - n + t + 1));
+    load_query<CT, D>(a, rs[j], rhq[j], rvalid[j], st[j]);
+  }
+  float kscale, vscale;
+  head_scales<CT>(a, h, kscale, vscale);
   const int32_t *table = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  const int nb = a.cache.num_blocks;
   const int jb1 = (end + kBlock - 1) / kBlock;
-  int none = 0;
-  rows_core<CT, QT, D, false>(a, table, h, 0, jb1, end, -1, qs + t, h * g + (rvalid ? r % g : 0),
-                              rvalid, lim, first_table_entries(table, 0, jb1), none);
+  int tbl = first_table_entries(table, 0, jb1);
+#pragma unroll
+  for (int j = 0; j < kT; ++j)
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      asm volatile("" : "+v"(st[j].qop[kk].x), "+v"(st[j].qop[kk].y), "+v"(st[j].qop[kk].z),
+                   "+v"(st[j].qop[kk].w));
+  for (int c0 = 0; c0 < jb1; c0 += 64) {  // rounds of up to 64 blocks
+    const int nk = min(64, jb1 - c0);
+    const int npair = (nk + 1) / 2;
+    // the next round's entries, waited for at its start
+    int tbl_next = c0 + 64 < jb1 ? first_table_entries(table, c0 + 64, jb1) : -1;
+    asm volatile("" : "+v"(tbl));
+    auto id = [&](int b) { return b < nk ? __builtin_amdgcn_readlane(tbl, b) : -1; };
+    auto issue = [&](auto I, int k) {  // pair k into stage I (past the end: empty copies)
+      const int ba = id(2 * k), bb = id(2 * k + 1);
+      stage_pair<CT, D, decltype(I)::value>(a, ba, (unsigned)ba < (unsigned)nb, bb,
+                                            (unsigned)bb < (unsigned)nb, h);
+    };
+    auto step = [&](auto I, int k) {
+      constexpr int i = decltype(I)::value;
+      stage_barrier<P::kPerWave * (kS - 2)>();  // pair k landed for every wavefront
+      issue(std::integral_constant<int, (i + kS - 1) % kS>{}, k + kS - 1);
+      const int ba = id(2 * k), bb = id(2 * k + 1);
+      const bool oka = (unsigned)ba < (unsigned)nb, okb = (unsigned)bb < (unsigned)nb;
+      const int t0 = (c0 + 2 * k) * kBlock;
+      f4_t sa[kT], sb[kT];
+      {
+        uint4 kf[F::kKLoads];
+        read_pair_k<CT, D, i, 0>(kf);
+#pragma unroll
+        for (int j = 0; j < kT; ++j) sa[j] = block_qk<CT, D>(kf, st[j]);
+        read_pair_k<CT, D, i, P::kBlockBytes>(kf);
+#pragma unroll
+        for (int j = 0; j < kT; ++j) sb[j] = block_qk<CT, D>(kf, st[j]);
+      }
+      // a pair wholly inside every row's limit (most of them) skips the masks
+      const bool full = oka && okb && t0 + 2 * kBlock <= wlim;  // wave-uniform
+      uint4 pop[kT];
+      if (full) {
+#pragma unroll
+        for (int j = 0; j < kT; ++j)
+          pop[j] = pair_softmax<CT, D, true>(sa[j], sb[j], kscale, t0, 0, 0, st[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kT; ++j)
+          pop[j] = pair_softmax<CT, D, false>(sa[j], sb[j], kscale, t0, oka ? lim[j] : t0,
+                                              okb ? lim[j] : t0 + kBlock, st[j]);
+      }
+      typename F::VRaw va[F::kNT], vb[F::kNT];
+      read_pair_v<CT, D, i, 0>(va);
+      read_pair_v<CT, D, i, P::kBlockBytes>(vb);
+      const uint4 keep = full ? make_uint4(~0u, ~0u, ~0u, ~0u)
+                              : pair_keep(t0, oka ? end : t0, okb ? end : t0 + kBlock);
+#pragma unroll
+      for (int nt = 0; nt < F::kNT; ++nt) {
+        const uint4 vop = pair_vop<CT>(va[nt], vb[nt], keep);
+#pragma unroll
+        for (int j = 0; j < kT; ++j) st[j].acc[nt] = mma_k32<kBF>(vop, pop[j], st[j].acc[nt]);
+      }
+    };
+    stage_barrier<63>();  // the stages' previous readers are done
+    static_for<0, kS - 1>([&](auto I) { issue(I, decltype(I)::value); });
+    int k0 = 0;
+    for (; k0 + kS <= npair; k0 += kS)
+      static_for<0, kS>([&](auto I) { step(I, k0 + decltype(I)::value); });
+    static_for<0, kS>([&](auto I) {
+      if (k0 + decltype(I)::value < npair) step(I, k0 + decltype(I)::value);
+    });
+    tbl = tbl_next;
+  }
+#pragma unroll
+  for (int j = 0; j < kT; ++j) emit_rows<QT, D>(a, st[j], vscale, -1, rs[j], rhq[j], rvalid[j]);
 }
 
 template <class CT, class QT, int D>
 hipError_t launch_prefill_dd(const DecodeArgs &a, hipStream_t s) {
   const int g = a.num_q_heads / a.cache.num_kv_heads;
-  const int64_t groups = ((int64_t)a.max_query_len * g + 63) / 64;
-  const int64_t grid = (int64_t)a.num_seqs * a.cache.num_kv_heads * groups;
-  if (grid == 0) return hipSuccess;
+  const int64_t groups = ((int64_t)a.max_query_len * g + kPrefillRows - 1) / kPrefillRows;
+  const int64_t items = (int64_t)a.num_seqs * a.cache.num_kv_heads * groups;
+  if (items == 0) return hipSuccess;
+  const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
   prefill_mfma_kernel<CT, QT, D><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
