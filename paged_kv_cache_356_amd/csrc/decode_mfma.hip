@@ -944,34 +944,59 @@ void decode_mfma_kernel(DecodeArgs a) {
 // matrix-core bound, not memory bound, and is arranged for the products:
 //  - workgroup (s, h, group) takes kPrefillRows rows of sequence s and KV head h (row r is token
 //    r / g, query head h*g + r % g), its wavefront w kPrefillTiles tiles of 16 rows;
-//  - the blocks go through LDS two at a time (a pair: 32 positions), copied straight from the pool
-//    by the four wavefronts and read back by each, so a block is fetched once per 128 rows;
-//  - the scores of both blocks of a pair are taken together (one maximum update), and P V runs
-//    as one 16x16x32 product per 16 head dims over the pair's 32 positions, the pair's positions
-//    ordered so that each lane's four probabilities of each block (the lane layout the scores come
-//    in) are its eight consecutive reduction indices, and the V^T operand gathers the same four
-//    positions of each block;
+//  - the blocks go through LDS two at a time (a pair A, B: 32 positions), copied straight from the
+//    pool by the four wavefronts and read back by each, so a block is fetched once per 128 rows;
+//  - P V is one 16x16x32 product per 16 head dims over the pair, reduction index k = position
+//    tok0 + k of the pair: lane group grp (lanes 16 grp ..) holds positions 8 grp .. 8 grp + 7,
+//    i.e. 8 consecutive positions of block grp / 2, so its V^T operand is one 16-byte row piece;
+//  - the scores come from two 16x16x32 products per pair, X on positions 8 q + 0..3 of each
+//    block (q = 0, 1) and Y on 8 q + 4..7, whose result layouts put exactly those 8 positions in
+//    lane group grp (X gives the first four, Y the next four);
+//  - the LDS copy of a block is permuted so that every read of a product operand is a 16-byte
+//    load free of bank conflicts: K vectors of a token row are swizzled (token bit 2 flips with
+//    bit 3, block B also flips bit 3), 16-bit V^T tiles are stored half-row-major;
+//  - the scores of a pair are taken together (one maximum update per pair, the row maximum by
+//    lane swaps rather than LDS shuffles);
 //  - probabilities are rounded once to the input type (no hi + lo split): each output averages
 //    many positions, so the rounding of single probabilities does not accumulate.
 // Each row masks the positions past its own; the workgroup walks the blocks up to its last row's
 // position, in rounds of 64 blocks (one table fetch per round).  Rows are complete in one
 // wavefront: the outputs are written directly, no workspace.
-constexpr int kPrefillTiles = 2;
+#ifndef PA_PREFILL_TILES
+#define PA_PREFILL_TILES 2
+#endif
+#ifndef PA_PREFILL_STAGES
+#define PA_PREFILL_STAGES 4
+#endif
+#ifndef PA_PREFILL_OCC
+#define PA_PREFILL_OCC 2
+#endif
+constexpr int kPrefillTiles = PA_PREFILL_TILES;
 constexpr int kXcds = 8;  // accelerator complex dies; workgroups are dealt to them round-robin
 constexpr int kPrefillRows = 16 * kPrefillTiles * kWaves;
 
 template <class CT, int D>
 struct PairStages {
+  static constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
   static constexpr int kTileBytes = kBlock * D * CT::bytes;
   static constexpr int kBlockBytes = 2 * kTileBytes;  // K tile, then V tile
   static constexpr int kBytes = 2 * kBlockBytes;      // block A, then block B
   static constexpr int kChunks = kBytes / 1024;       // 1 KiB copies per pair
   static constexpr int kPerWave = kChunks / kWaves;
-  static constexpr int kStages = 4;
+  static constexpr int kStages = PA_PREFILL_STAGES;
   static_assert(kChunks % kWaves == 0, "pair split");
 };
 
-// This wavefront's share of the pair (blocks ba, bb of KV head h) into stage I.
+// Token order of a K vector row in LDS: slot k_slot(t, b) (in 16-byte units, within its 16-slot
+// row) holds token t of block b (0: A, 1: B); k_token is its inverse.
+__device__ __forceinline__ int tok_swap(int t) { return t ^ (((t >> 3) & 1) << 2); }  // involution
+__device__ __forceinline__ int k_slot(int t, int b) { return tok_swap(t) ^ (b << 3); }
+__device__ __forceinline__ int k_token(int slot, int b) { return tok_swap(slot ^ (b << 3)); }
+
+// This wavefront's share of the pair (blocks ba, bb of KV head h) into stage I, permuted as the
+// reads expect: LDS slot s of a K tile holds the pool's vector (s / 16, token k_token(s % 16));
+// LDS slot s of a 16-bit V^T tile holds head dim s % D, positions 8 (s / D) .. + 7; fp8 V^T
+// tiles are copied as they are.
 template <class CT, int D, int I>
 __device__ __forceinline__ void stage_pair(const DecodeArgs &a, int ba, bool oka, int bb, bool okb,
                                            int h) {
@@ -993,32 +1018,49 @@ __device__ __forceinline__ void stage_pair(const DecodeArgs &a, int ba, bool oka
     const int c = w + kWaves * i;  // 1 KiB chunk of the stage
     const int cb = c * 1024 / P::kBlockBytes, off = c * 1024 - cb * P::kBlockBytes;
     const bool v = off >= P::kTileBytes;
+    const int slot = (off - (v ? P::kTileBytes : 0)) / 16 + lane;  // LDS slot within the tile
+    int src;                                                       // pool slot within the tile
+    if (!v) src = (slot & ~15) | k_token(slot & 15, cb);
+    else if (P::kFP8) src = slot;
+    else src = 2 * (slot % D) + slot / D;
     const auto r = cb ? (v ? rvb : rkb) : (v ? rva : rka);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)(stage + c * 1024), 16,
-                                             off - (v ? P::kTileBytes : 0) + 16 * lane, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)(stage + c * 1024), 16, 16 * src, 0,
+                                             0, 0);
   }
 }
 
-template <class CT, int D, int I, int kOff, int N>
+// K operand of score product X (which = 0) or Y (which = 1), vector i (16 dims of fp8, 8 of
+// 16-bit): lane (r = lane / 16, c = lane % 16) holds vector 4 i + r of position
+// 8 ((c >> 2) & 1) + 4 which + (c & 3) of block c >> 3.
+template <class CT, int D, int I, int kWhich, int N>
 __device__ __forceinline__ void read_pair_k(uint4 (&k)[N]) {
   using P = PairStages<CT, D>;
-  const int lane = threadIdx.x & 63;
-  const auto *stage = prefix_stage<P::kBytes, 16 + I>() + kOff;
+  const int lane = threadIdx.x & 63, c = lane & 15, r = lane >> 4;
+  const int b = c >> 3;
+  const int t = 8 * ((c >> 2) & 1) + 4 * kWhich + (c & 3);
+  const auto *base = prefix_stage<P::kBytes, 16 + I>() + b * P::kBlockBytes +
+                     (16 * r + k_slot(t, b)) * 16;
 #pragma unroll
-  for (int i = 0; i < N; ++i) k[i] = lds_load<uint4>(stage + (lane + 64 * i) * 16);
+  for (int i = 0; i < N; ++i) k[i] = lds_load<uint4>(base + 64 * 16 * i);
 }
 
-template <class CT, int D, int I, int kOff, class VR, int N>
-__device__ __forceinline__ void read_pair_v(VR (&v)[N]) {
+// V^T operand for head dims 16 nt + c (c = lane % 16) and positions 8 grp .. 8 grp + 7 of the pair
+// (grp = lane / 16: block grp / 2, its positions 8 (grp % 2) ..), as 8 values of the product type.
+template <class CT, int D, int I>
+__device__ __forceinline__ uint4 read_pair_v(int nt) {
   using P = PairStages<CT, D>;
-  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-  const auto *stage = prefix_stage<P::kBytes, 16 + I>() + kOff + P::kTileBytes;
-#pragma unroll
-  for (int nt = 0; nt < N; ++nt)
-    v[nt] = lds_load<VR>(stage + ((16 * nt + col) * kBlock + 4 * grp) * CT::bytes);
+  const int lane = threadIdx.x & 63, c = lane & 15, grp = lane >> 4;
+  const auto *tile = prefix_stage<P::kBytes, 16 + I>() + (grp >> 1) * P::kBlockBytes + P::kTileBytes;
+  if constexpr (P::kFP8) {
+    const uint2 x = lds_load<uint2>(tile + (16 * nt + c) * kBlock + 8 * (grp & 1));
+    const uint2 lo = e4m3x4_to_f16x4(x.x), hi = e4m3x4_to_f16x4(x.y);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  } else {
+    return lds_load<uint4>(tile + ((grp & 1) * D + 16 * nt + c) * 16);
+  }
 }
 
-// S^T of one 16-token block against this wavefront tile's query rows (raw products).
+// S^T of one score product against this wavefront tile's query rows (raw products).
 template <class CT, int D, int N>
 __device__ __forceinline__ f4_t block_qk(const uint4 (&k)[N], const RowState<D> &rs_) {
   constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
@@ -1050,29 +1092,21 @@ __device__ __forceinline__ float max_over_rows(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Softmax update over a pair (block A at tok0, block B at tok0 + 16) from the raw scores sa, sb:
-// positions at or past zla (block A) / zlb (block B) are masked, unless kFull (the caller knows
-// every position of the pair is inside every row's limit).  Returns P^T for the pair's PV
-// product: reduction index 8 grp + i is block A's position 4 grp + i for i < 4, block B's
-// position 4 grp + i - 4 otherwise.
-template <class CT, int D, bool kFull>
-__device__ __forceinline__ uint4 pair_softmax(f4_t sa, f4_t sb, float kscale, int tok0, int zla,
-                                              int zlb, RowState<D> &rs_) {
+// Softmax update over a pair at tok0 from the raw scores sx, sy (products X, Y): this lane's
+// positions are tok0 + 8 grp + i, i < 8 (sx: i < 4, sy: i >= 4); those at or past zl are masked.
+// Returns this lane's P^T operand: the 8 probabilities in position order.
+template <class CT, int D>
+__device__ __forceinline__ uint4 pair_softmax(f4_t sx, f4_t sy, float kscale, int tok0, int zl,
+                                              RowState<D> &rs_) {
   constexpr bool kBF = std::is_same<CT, bf16_t>::value;
   constexpr int NT = D / 16;
-  const int grp = (threadIdx.x & 63) >> 4;
-  const int t0 = tok0 + 4 * grp;
+  const int t0 = tok0 + 8 * ((threadIdx.x & 63) >> 4);
   float z[8];
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if constexpr (kFull) {
-      z[i] = sa[i] * kscale;
-      z[4 + i] = sb[i] * kscale;
-    } else {
-      z[i] = t0 + i < zla ? sa[i] * kscale : -INFINITY;
-      z[4 + i] = t0 + 16 + i < zlb ? sb[i] * kscale : -INFINITY;
-    }
+    z[i] = t0 + i < zl ? sx[i] * kscale : -INFINITY;  // select: masked positions never leak
+    z[4 + i] = t0 + 4 + i < zl ? sy[i] * kscale : -INFINITY;
     mx = fmaxf(mx, fmaxf(z[i], z[4 + i]));
   }
   mx = max_over_rows(mx);
@@ -1094,34 +1128,18 @@ __device__ __forceinline__ uint4 pair_softmax(f4_t sa, f4_t sb, float kscale, in
                     pack2<kBF>(p[6], p[7]));
 }
 
-// Masks that zero the V elements of positions at or past vla (block A at tok0) / vlb (block B at
-// tok0 + 16) in this lane's four positions of each block.
-__device__ __forceinline__ uint4 pair_keep(int tok0, int vla, int vlb) {
-  const int t0 = tok0 + 4 * ((threadIdx.x & 63) >> 4);
-  return make_uint4((t0 + 0 < vla ? 0xffffu : 0u) | (t0 + 1 < vla ? 0xffff0000u : 0u),
-                    (t0 + 2 < vla ? 0xffffu : 0u) | (t0 + 3 < vla ? 0xffff0000u : 0u),
-                    (t0 + 16 < vlb ? 0xffffu : 0u) | (t0 + 17 < vlb ? 0xffff0000u : 0u),
-                    (t0 + 18 < vlb ? 0xffffu : 0u) | (t0 + 19 < vlb ? 0xffff0000u : 0u));
-}
-
-// V^T operand of the pair for head-dim rows 16 nt + col: block A's 4 positions then block B's,
-// masked by `keep` (a select: NaN in masked positions cannot leak).
-template <class CT, class VR>
-__device__ __forceinline__ uint4 pair_vop(VR va, VR vb, uint4 keep) {
-  constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
-  uint2 x, y;
-  if constexpr (kFP8) {
-    x = e4m3x4_to_f16x4(va);
-    y = e4m3x4_to_f16x4(vb);
-  } else {
-    x = va;
-    y = vb;
-  }
-  return make_uint4(x.x & keep.x, x.y & keep.y, y.x & keep.z, y.y & keep.w);
+// Mask words that zero the 16-bit V values of this lane's positions (tok0 + 8 grp + i) at or past
+// vl, two positions per word.
+__device__ __forceinline__ uint4 pair_keep(int tok0, int vl) {
+  const int t0 = tok0 + 8 * ((threadIdx.x & 63) >> 4);
+  auto two = [&](int i) {
+    return (t0 + i < vl ? 0xffffu : 0u) | (t0 + i + 1 < vl ? 0xffff0000u : 0u);
+  };
+  return make_uint4(two(0), two(2), two(4), two(6));
 }
 
 template <class CT, class QT, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PA_PREFILL_OCC)))
 void prefill_mfma_kernel(DecodeArgs a) {
   using P = PairStages<CT, D>;
   using F = Frag<CT, D>;
@@ -1150,10 +1168,7 @@ void prefill_mfma_kernel(DecodeArgs a) {
   const int last = min(rbase + kPrefillRows - 1, nrows - 1);
   const int end = max(0, min(L, L - n + last / g + 1));  // the workgroup's last row's limit
   const int col = threadIdx.x & 15;
-  // Positions below this need no mask for any row of the wavefront: its first valid row's limit
-  // (a wavefront of padding rows only: the workgroup's end).
-  const int wrow = rbase + 16 * kT * w;
-  const int wlim = wrow < nrows ? min(end, max(0, min(L, L - n + wrow / g + 1))) : end;
+  const int grp = (threadIdx.x & 63) >> 4;
   RowState<D> st[kT];
   bool rvalid[kT];
   int rs[kT], rhq[kT], lim[kT];
@@ -1197,38 +1212,30 @@ void prefill_mfma_kernel(DecodeArgs a) {
       issue(std::integral_constant<int, (i + kS - 1) % kS>{}, k + kS - 1);
       const int ba = id(2 * k), bb = id(2 * k + 1);
       const bool oka = (unsigned)ba < (unsigned)nb, okb = (unsigned)bb < (unsigned)nb;
+      const bool okm = (grp >> 1) ? okb : oka;  // this lane's block
       const int t0 = (c0 + 2 * k) * kBlock;
-      f4_t sa[kT], sb[kT];
+      f4_t sx[kT], sy[kT];
       {
         uint4 kf[F::kKLoads];
         read_pair_k<CT, D, i, 0>(kf);
 #pragma unroll
-        for (int j = 0; j < kT; ++j) sa[j] = block_qk<CT, D>(kf, st[j]);
-        read_pair_k<CT, D, i, P::kBlockBytes>(kf);
+        for (int j = 0; j < kT; ++j) sx[j] = block_qk<CT, D>(kf, st[j]);
+        read_pair_k<CT, D, i, 1>(kf);
 #pragma unroll
-        for (int j = 0; j < kT; ++j) sb[j] = block_qk<CT, D>(kf, st[j]);
+        for (int j = 0; j < kT; ++j) sy[j] = block_qk<CT, D>(kf, st[j]);
       }
-      // a pair wholly inside every row's limit (most of them) skips the masks
-      const bool full = oka && okb && t0 + 2 * kBlock <= wlim;  // wave-uniform
       uint4 pop[kT];
-      if (full) {
 #pragma unroll
-        for (int j = 0; j < kT; ++j)
-          pop[j] = pair_softmax<CT, D, true>(sa[j], sb[j], kscale, t0, 0, 0, st[j]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < kT; ++j)
-          pop[j] = pair_softmax<CT, D, false>(sa[j], sb[j], kscale, t0, oka ? lim[j] : t0,
-                                              okb ? lim[j] : t0 + kBlock, st[j]);
-      }
-      typename F::VRaw va[F::kNT], vb[F::kNT];
-      read_pair_v<CT, D, i, 0>(va);
-      read_pair_v<CT, D, i, P::kBlockBytes>(vb);
-      const uint4 keep = full ? make_uint4(~0u, ~0u, ~0u, ~0u)
-                              : pair_keep(t0, oka ? end : t0, okb ? end : t0 + kBlock);
+      for (int j = 0; j < kT; ++j)
+        pop[j] = pair_softmax<CT, D>(sx[j], sy[j], kscale, t0, okm ? lim[j] : 0, st[j]);
+      const uint4 keep = pair_keep(t0, okm ? end : 0);
 #pragma unroll
       for (int nt = 0; nt < F::kNT; ++nt) {
-        const uint4 vop = pair_vop<CT>(va[nt], vb[nt], keep);
+        uint4 vop = read_pair_v<CT, D, i>(nt);
+        vop.x &= keep.x;  // a select: NaN in a masked position cannot leak
+        vop.y &= keep.y;
+        vop.z &= keep.z;
+        vop.w &= keep.w;
 #pragma unroll
         for (int j = 0; j < kT; ++j) st[j].acc[nt] = mma_k32<kBF>(vop, pop[j], st[j].acc[nt]);
       }
