@@ -54,7 +54,7 @@ def algorithmic_bytes(batch, unique: bool) -> int:
     it reads, the queries it reads and the outputs it writes (fp8: plus the per-head scales)."""
     w = batch.w
     kv = batch.kv_bytes_per_layer(unique=unique)
-    tables = int(sum(math.ceil(int(L) / 16) for L in batch.lengths)) * 4
+    tables = int(sum(math.ceil(int(L) / w.block_size) for L in batch.lengths)) * 4
     lens = w.num_seqs * 4
     qe = 4 if w.q_dtype == "f32" else 2
     qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * qe
@@ -128,6 +128,8 @@ def swap_bench(args, torch, api, wl, DecodeBatch) -> int:
     (pa_bm_swap_out / pa_swap_blocks, then pa_bm_swap_in / pa_swap_blocks), timed with HIP events on
     the launch stream.  Bytes = pairs x layers x 2 pools x block bytes."""
     w = wl.WORKLOADS[args.workload]
+    if args.block_size != w.block_size:
+        w = w.replace(block_size=args.block_size, num_blocks=w.num_blocks * 16 // args.block_size)
     if args.num_blocks:
         w = w.replace(num_blocks=args.num_blocks)
     b = DecodeBatch(w, device="cuda", num_sets=1)
@@ -228,6 +230,9 @@ def main() -> int:
     ap.add_argument("--partition", type=int, default=-1, help="partition size (-1 = workload's)")
     ap.add_argument("--num-blocks", type=int, default=0,
                     help="physical blocks per layer pool (0 = the workload's own)")
+    ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
+                    help="token positions per block (pool of the same bytes: num_blocks scaled by "
+                         "16 / block size)")
     ap.add_argument("--no-prefix", action="store_true",
                     help="shared-prefix workload: use the plain decode instead of the shared-prefix one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -275,6 +280,8 @@ def main() -> int:
     if args.prefill:
         return prefill_bench(args, torch, api, wl)
     w = wl.WORKLOADS[args.workload]
+    if args.block_size != w.block_size:
+        w = w.replace(block_size=args.block_size, num_blocks=w.num_blocks * 16 // args.block_size)
     if args.num_blocks:
         w = w.replace(num_blocks=args.num_blocks)
     sets = args.sets or DEFAULT_SETS[w.name]
@@ -386,7 +393,7 @@ def main() -> int:
         "config": {
             "workload": f"{w.name}: {w.description}",
             "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
-            "head_dim": w.head_dim, "block_size": 16, "layers": layers,
+            "head_dim": w.head_dim, "block_size": w.block_size, "layers": layers,
             "num_blocks_per_layer": w.num_blocks, "context_lens": wl.lengths_summary(batch.lengths),
             "partition_size": batch.partition_size or api.pa_decode_auto_partition(
                 w.num_seqs, w.num_kv_heads, batch.max_context_len),
@@ -398,6 +405,11 @@ def main() -> int:
             "kv_bytes_per_layer_unique": batch.kv_bytes_per_layer(unique=True) if unique else
             kv_logical,
             "copy_pairs_per_step": int(batch.sets[0].pairs.shape[0]),
+            # the block-size tradeoff: table entries the kernel reads, and positions allocated but
+            # not (yet) used in each sequence's last block
+            "table_entries_per_layer": int(sum(-(-int(L) // w.block_size) for L in batch.lengths)),
+            "slots_allocated_unused": int(sum(-(-int(L) // w.block_size) * w.block_size - int(L)
+                                              for L in batch.lengths)),
         },
         "hbm_fraction_of_step": round(value / HBM_PEAK_GBPS, 4),
         "seqs_per_s_per_layer": round(seqs_per_s_layer, 1),
@@ -410,7 +422,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(w, args.partition < 0 and not args.valu and
-                                        not args.num_blocks and not args.no_prefix),
+                                        not args.num_blocks and not args.no_prefix and
+                                        args.block_size == 16),
             "traffic_note": "HBM bytes per call from rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE "
                             "(decode + reduce kernels; profiles/traffic.json), null unless this run "
                             "is the measured configuration of unchanged kernels",

@@ -33,7 +33,7 @@ class OracleBatch:
     def __init__(self, batch, pad_block: int, pool_fill: int = 0):
         w = batch.w
         self.w = w
-        self.model = BlockManagerModel(w.num_blocks, 16, batch.free_order)
+        self.model = BlockManagerModel(w.num_blocks, w.block_size, batch.free_order)
         self.sets = []
         for _ in batch.sets:
             seqs, history, twins = wl.build_history(self.model, batch.lengths, w.prefix_len,
@@ -64,7 +64,8 @@ class OracleBatch:
         w = self.w
         H, D = w.num_kv_heads, w.head_dim
         dt = w.cache_dtype
-        n = w.num_blocks * H * 16 * D
+        B = w.block_size
+        n = w.num_blocks * H * B * D
         nbytes = n * np.dtype(RAW_NP[dt]).itemsize
         if self.pool_fill:
             kp = np.full(nbytes, self.pool_fill, np.uint8).view(RAW_NP[dt])
@@ -84,13 +85,13 @@ class OracleBatch:
             if m and (owners is None or owner == "prefix" or owner in owners):
                 oracle.reshape_and_cache(kp, vp, dt, ks, vs, w.num_blocks, H, D,
                                          raw(hk[off:off + m]), raw(hv[off:off + m]), w.kv_dtype,
-                                         np.asarray(slots, np.int64))
+                                         np.asarray(slots, np.int64), B=B)
             off += m
         e = np.dtype(RAW_NP[dt]).itemsize
         if st["pairs"].shape[0]:
-            oracle.copy_blocks([kp], [vp], H * 16 * D * e, w.num_blocks, st["pairs"])
+            oracle.copy_blocks([kp], [vp], H * B * D * e, w.num_blocks, st["pairs"])
         oracle.reshape_and_cache(kp, vp, dt, ks, vs, w.num_blocks, H, D, raw(dst.new_k[layer]),
-                                 raw(dst.new_v[layer]), w.kv_dtype, st["slots"])
+                                 raw(dst.new_v[layer]), w.kv_dtype, st["slots"], B=B)
         self.pools[(layer, set_index)] = (kp, vp, ks, vs)
         return kp, vp
 
@@ -101,7 +102,8 @@ class OracleBatch:
         q = raw(batch.sets[set_index].q[layer]).reshape(w.num_seqs, -1)
         return oracle.decode_attention(q, w.q_dtype, kp, vp, w.cache_dtype, ks, vs, w.num_blocks,
                                        w.num_kv_heads, w.head_dim, st["tables"], st["ctx"],
-                                       w.num_q_heads, w.scale, sel=sel, nthreads=nthreads)
+                                       w.num_q_heads, w.scale, sel=sel, nthreads=nthreads,
+                                       B=w.block_size)
 
 
 def device_pool_bytes(cache) -> tuple[np.ndarray, np.ndarray]:

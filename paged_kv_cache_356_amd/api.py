@@ -155,30 +155,31 @@ class KVCache:
     cache_dtype: int
     k_scale: torch.Tensor | None = None
     v_scale: torch.Tensor | None = None
+    block_size: int = PA_BLOCK_SIZE
 
     @staticmethod
     def allocate(num_blocks, num_kv_heads, head_dim, cache_dtype, device="cuda", k_scale=None,
-                 v_scale=None) -> "KVCache":
+                 v_scale=None, block_size=PA_BLOCK_SIZE) -> "KVCache":
         code = DTYPE_CODES[cache_dtype] if isinstance(cache_dtype, str) else int(cache_dtype)
-        n = pool_bytes(num_blocks, num_kv_heads, head_dim, code)
+        n = pool_bytes(num_blocks, num_kv_heads, head_dim, code, block_size)
         return KVCache(torch.zeros(n, dtype=torch.uint8, device=device),
                        torch.zeros(n, dtype=torch.uint8, device=device), num_blocks, num_kv_heads,
-                       head_dim, code, k_scale, v_scale)
+                       head_dim, code, k_scale, v_scale, block_size)
 
     def struct(self) -> pa_cache:
         """The pa_cache of this layer (built once; rebuilt if a pool tensor was replaced)."""
         key = (_ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.k_scale), _ptr(self.v_scale),
-               self.num_blocks, self.num_kv_heads, self.head_dim, self.cache_dtype)
+               self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim,
+               self.cache_dtype)
         c = self.__dict__.get("_c")
         if c is None or self.__dict__.get("_key") != key:
-            c = pa_cache(key[0], key[1], key[2], key[3], self.num_blocks, PA_BLOCK_SIZE,
-                         self.num_kv_heads, self.head_dim, self.cache_dtype)
+            c = pa_cache(*key)
             self.__dict__["_c"], self.__dict__["_key"] = c, key
         return c
 
 
-def pool_bytes(num_blocks, num_kv_heads, head_dim, cache_dtype) -> int:
-    c = pa_cache(None, None, None, None, num_blocks, PA_BLOCK_SIZE, num_kv_heads, head_dim,
+def pool_bytes(num_blocks, num_kv_heads, head_dim, cache_dtype, block_size=PA_BLOCK_SIZE) -> int:
+    c = pa_cache(None, None, None, None, num_blocks, block_size, num_kv_heads, head_dim,
                  int(cache_dtype))
     n = lib().pa_pool_bytes(ctypes.byref(c))
     if n == 0 and num_blocks > 0:

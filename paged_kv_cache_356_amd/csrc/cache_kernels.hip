@@ -21,9 +21,10 @@ __global__ __launch_bounds__(128) void reshape_and_cache_kernel(ReshapeArgs a) {
   const int t = blockIdx.x;
   const int64_t slot = a.slots[t];
   const CacheArgs &c = a.cache;
-  if (slot < 0 || slot >= (int64_t)c.num_blocks * kBlock) return;  // padding / out of range
-  const int64_t blk = slot / kBlock;
-  const int off = (int)(slot % kBlock);
+  const int B = c.block_size;
+  if (slot < 0 || slot >= (int64_t)c.num_blocks * B) return;  // padding / out of range
+  const int64_t blk = slot / B;
+  const int off = (int)(slot % B);
   const int H = c.num_kv_heads, D = c.head_dim;
   using L = Layout<CT::bytes>;
   constexpr int E = L::E;
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(128) void reshape_and_cache_kernel(ReshapeArgs a) {
   auto *vp = static_cast<typename CT::raw *>(c.v_pool);
   for (int v = threadIdx.x; v < H * vec_per_head; v += blockDim.x) {
     const int h = v / vec_per_head, cv = v % vec_per_head;
-    const size_t tile = L::tile(blk, h, H, D);
+    const size_t tile = L::tile(blk, h, H, D, B);
     const int i0 = cv * E;
     union {
       uint4 v;
@@ -56,11 +57,11 @@ __global__ __launch_bounds__(128) void reshape_and_cache_kernel(ReshapeArgs a) {
       }
     }
     // K: the E elements are one contiguous 16-byte vector of the tile.
-    auto *kdst = kp + tile + L::k_off(off, i0);
+    auto *kdst = kp + tile + L::k_off(off, i0, B);
     *reinterpret_cast<uint4 *>(kdst) = kv.v;
-    // V: transposed tile, element (off, i) at i * 16 + off.
+    // V: transposed tile, element (off, i) at i * B + off.
 #pragma unroll
-    for (int j = 0; j < E; ++j) vp[tile + L::v_off(off, i0 + j)] = vv.e[j];
+    for (int j = 0; j < E; ++j) vp[tile + L::v_off(off, i0 + j, B)] = vv.e[j];
   }
 }
 

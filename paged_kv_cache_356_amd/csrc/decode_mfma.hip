@@ -91,15 +91,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *tile, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(tile), (short)0, bytes, kRsrcWord3);
 }
 
+// off: per-lane byte offset; soff: a wave-uniform byte offset added to it.
 template <class T, bool kNT>
-__device__ __forceinline__ T load_kv(__amdgpu_buffer_rsrc_t r, int off) {
+__device__ __forceinline__ T load_kv(__amdgpu_buffer_rsrc_t r, int off, int soff = 0) {
   constexpr int aux = kNT ? 2 : 0;  // 2: nt
   if constexpr (sizeof(T) == 16)
-    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, aux));
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, aux));
   else if constexpr (sizeof(T) == 8)
-    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, aux));
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, aux));
   else
-    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, aux));
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, aux));
 }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNoMax = -3.0e38f;  // running-maximum floor (finite)
@@ -249,6 +250,84 @@ __device__ __forceinline__ void load_block(const DecodeArgs &a, int bid, bool ok
     f.v[nt] = load_kv<typename F::VRaw, kNT>(rv, ((16 * nt + col) * kBlock + 4 * grp) * CT::bytes);
 }
 
+// Other block sizes.  The ring always advances by one 16-position step (one product's worth);
+// a table entry names a block of kB positions, in the layout of include/pa.h with B = kB.
+//  - kB = 32: a block is two steps; step `sub` of block bid reads positions 16 sub .. 16 sub + 15
+//    of the tile, through the tile's descriptor as for kB = 16.
+//  - kB = 8: a step spans two blocks (b0: positions 0..7 of the step, b1: 8..15).  Lanes of the K
+//    operand rows c < 8 and of the V operand lane groups 0-1 read b0, the others b1, so the loads go
+//    through one descriptor over the whole pool with per-lane offsets; a lane whose block is absent
+//    reads past the descriptor's end (zeros, no memory access), and a step with no block at all
+//    gets an empty descriptor.
+template <int kB>
+struct BlockSteps {
+  static_assert(kB == 8 || kB == 16 || kB == 32, "block size");
+  static constexpr int kChunk = kB == 8 ? 32 : 64;  // ring steps per chunk of table entries
+};
+
+// Lane i's entry of the table entries that ring steps [j0, j0 + kn) read (kB = 8 or 32), -1 past
+// those that positions below vend need: entries past a sequence's blocks are never read.
+template <int kB>
+__device__ __forceinline__ int chunk_table_entries(const int32_t *table, int j0, int kn, int vend) {
+  const int lane = threadIdx.x & 63;
+  const int e0 = kB == 32 ? j0 >> 1 : 2 * j0;
+  const int e1 = min(kB == 32 ? (j0 + kn + 1) >> 1 : 2 * (j0 + kn), (vend + kB - 1) / kB);
+  return lane < e1 - e0 ? table[e0 + lane] : -1;
+}
+
+template <class CT, int D, bool kNT>
+__device__ __forceinline__ void load_block32(const DecodeArgs &a, int bid, bool ok, int sub, int h,
+                                             Frag<CT, D> &f) {
+  using F = Frag<CT, D>;
+  constexpr int kTileBytes = 32 * D * CT::bytes;
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  const size_t tile = ((size_t)(ok ? bid : 0) * a.cache.num_kv_heads + h) * kTileBytes;
+  const int n = ok ? kTileBytes : 0;
+  const auto rk = tile_rsrc(static_cast<const char *>(a.cache.k_pool) + tile, n);
+  const auto rv = tile_rsrc(static_cast<const char *>(a.cache.v_pool) + tile, n);
+  // per-lane parts of the offsets, plus wave-uniform ones (the half, the vector / head-dim rows)
+  const int koff = (grp * 32 + col) * 16, voff = (col * 32 + 4 * grp) * CT::bytes;
+#pragma unroll
+  for (int i = 0; i < F::kKLoads; ++i)
+    f.k[i] = load_kv<uint4, kNT>(rk, koff, (4 * i * 32 + 16 * sub) * 16);
+  // A step reads half of each head dim's 32-position V^T row, so half of every cache line; the
+  // other half belongs to the block's other step, issued next: ordinary loads let it find the
+  // line in L2 instead of fetching it again.
+#pragma unroll
+  for (int nt = 0; nt < F::kNT; ++nt)
+    f.v[nt] = load_kv<typename F::VRaw, false>(rv, voff, (16 * nt * 32 + 16 * sub) * CT::bytes);
+}
+
+// lane_ok: whether this lane's block (of its K row for the scores, of its positions for the
+// probabilities, the same one: lanes 0-31 hold positions of b0, 32-63 of b1) is present.
+template <class CT, int D, bool kNT>
+__device__ __forceinline__ void load_block8(const DecodeArgs &a, int b0, bool ok0, int b1,
+                                            bool ok1, int h, Frag<CT, D> &f) {
+  using F = Frag<CT, D>;
+  constexpr int kTileBytes = 8 * D * CT::bytes;
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  const uint32_t pool = (uint32_t)((size_t)a.cache.num_blocks * a.cache.num_kv_heads * kTileBytes);
+  const uint32_t n = ok0 || ok1 ? pool : 0u;
+  const auto rk = tile_rsrc(static_cast<const char *>(a.cache.k_pool), (int)n);
+  const auto rv = tile_rsrc(static_cast<const char *>(a.cache.v_pool), (int)n);
+  const int H = a.cache.num_kv_heads;
+  // K operand row col: block col >> 3, its position col & 7; an absent block reads past the end
+  const bool kok = col < 8 ? ok0 : ok1;
+  const uint32_t koff =
+      kok ? (uint32_t)((col < 8 ? b0 : b1) * H + h) * kTileBytes + (grp * 8 + (col & 7)) * 16
+          : pool;
+#pragma unroll
+  for (int i = 0; i < F::kKLoads; ++i) f.k[i] = load_kv<uint4, kNT>(rk, (int)koff, i * 4 * 8 * 16);
+  // V operand lane group grp: positions 4 grp .. 4 grp + 3 of the step, block grp >> 1
+  const bool vok = grp < 2 ? ok0 : ok1;
+  const uint32_t voff =
+      vok ? (uint32_t)((grp < 2 ? b0 : b1) * H + h) * kTileBytes + (col * 8 + 4 * (grp & 1)) * CT::bytes
+          : pool;
+#pragma unroll
+  for (int nt = 0; nt < F::kNT; ++nt)
+    f.v[nt] = load_kv<typename F::VRaw, kNT>(rv, (int)voff, 16 * nt * 8 * CT::bytes);
+}
+
 // The probabilities of one block for this lane's column, split p = hi + lo in the MFMA input type.
 struct BlockP {
   uint2 hi, lo;
@@ -386,32 +465,48 @@ __device__ __forceinline__ void settle_frag(Frag<CT, D> &f) {
 // address, and waiting for it would drain every load in flight.  A wavefront with more than 64
 // blocks runs one ring per 64 of them.  The first 64 entries (tbl0, from first_table_entries)
 // come from the caller, which can fetch them while the wavefront's previous item streams.
-template <class CT, int D, bool kNT>
+template <class CT, int D, bool kNT, int kB>
 __device__ __forceinline__ void stream_blocks(const DecodeArgs &a, const int32_t *table, int h,
                                               int jb0, int jb1, int tbl0, int zlim, int vend,
                                               float kscale, RowState<D> &st) {
   using F = Frag<CT, D>;
   // blocks per wavefront in the load ring: fp8 fragments are half the registers of 16-bit ones
   constexpr int kBufs = std::is_same<CT, fp8_t>::value ? PA_FP8_BUFS : PA_DECODE_BUFS;
+  constexpr int kCS = BlockSteps<kB>::kChunk;
   const int nb = a.cache.num_blocks;
   const int lane = threadIdx.x & 63;
-  const int nk = jb1 > jb0 ? jb1 - jb0 : 0;  // this wave's blocks
-  // One ring over the chunk of kn <= 64 blocks starting at block k0, with the chunk's table
+  const int nk = jb1 > jb0 ? jb1 - jb0 : 0;  // this wave's 16-position steps (blocks at kB = 16)
+  // One ring over the chunk of kn <= kCS steps starting at step k0, with the chunk's table
   // entries one per lane in tbl.  The first chunk is run on its own, outside the loop over the
   // others, so that its entries (fetched by the caller) need no wait at a loop header.
   auto chunk = [&](int k0, int kn, int tbl) {
-    // block id of the chunk's k-th block; k < kn is wave-uniform
-    auto entry = [&](int k) { return __builtin_amdgcn_readlane(tbl, k < 64 ? k : 63); };
+    // table entry e of the chunk; the callers keep e < 64 and k < kn wave-uniform
+    auto entry = [&](int e) { return __builtin_amdgcn_readlane(tbl, e < 64 ? e : 63); };
     F buf[kBufs];
-    bool ok[kBufs];
+    bool ok[kBufs];       // the step has a block (kB = 8: at least one of its two)
+    bool lane_ok[kBufs];  // kB = 8: this lane's block of the step is present
     auto load = [&](int b, int k) {
-      const int bid = k < kn ? entry(k) : -1;
-      ok[b] = (unsigned)bid < (unsigned)nb;  // an entry outside the pool is never dereferenced
-      load_block<CT, D, kNT>(a, bid, ok[b], h, buf[b]);
+      if constexpr (kB == 16) {
+        const int bid = k < kn ? entry(k) : -1;
+        ok[b] = (unsigned)bid < (unsigned)nb;  // an entry outside the pool is never dereferenced
+        load_block<CT, D, kNT>(a, bid, ok[b], h, buf[b]);
+      } else if constexpr (kB == 32) {
+        const int j = jb0 + k0 + k;  // absolute step: block j / 2, its half j % 2
+        const int bid = k < kn ? entry((j >> 1) - ((jb0 + k0) >> 1)) : -1;
+        ok[b] = (unsigned)bid < (unsigned)nb;
+        load_block32<CT, D, kNT>(a, bid, ok[b], j & 1, h, buf[b]);
+      } else {
+        const int b0 = k < kn ? entry(2 * k) : -1, b1 = k < kn ? entry(2 * k + 1) : -1;
+        const bool ok0 = (unsigned)b0 < (unsigned)nb, ok1 = (unsigned)b1 < (unsigned)nb;
+        ok[b] = ok0 || ok1;
+        lane_ok[b] = (lane >> 5) ? ok1 : ok0;
+        load_block8<CT, D, kNT>(a, b0, ok0, b1, ok1, h, buf[b]);
+      }
     };
     auto compute = [&](int b, int k) {
       const int t0 = (jb0 + k0 + k) * kBlock;
-      block_step<CT, D>(buf[b], kscale, t0, ok[b] ? zlim : t0, ok[b] ? vend : t0, st);
+      const bool zok = kB == 8 ? lane_ok[b] : ok[b];
+      block_step<CT, D>(buf[b], kscale, t0, zok ? zlim : t0, ok[b] ? vend : t0, st);
     };
 #pragma unroll
     for (int b = 0; b < kBufs; ++b) load(b, b);  // slots past the end: zeros, no memory access
@@ -439,10 +534,11 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs &a, const int32_t
 #pragma unroll
     for (int b = 0; b < kBufs; ++b) settle_frag(buf[b]);
   };
-  if (nk > 0) chunk(0, min(64, nk), tbl0);
-  for (int k0 = 64; k0 < nk; k0 += 64) {
-    const int kn = min(64, nk - k0);
-    chunk(k0, kn, lane < kn ? table[jb0 + k0 + lane] : -1);
+  if (nk > 0) chunk(0, min(kCS, nk), tbl0);
+  for (int k0 = kCS; k0 < nk; k0 += kCS) {
+    const int kn = min(kCS, nk - k0);
+    if constexpr (kB == 16) chunk(k0, kn, lane < kn ? table[jb0 + k0 + lane] : -1);
+    else chunk(k0, kn, chunk_table_entries<kB>(table, jb0 + k0, kn, vend));
   }
 }
 
@@ -485,7 +581,7 @@ template <class QT, int D>
 __device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D> &st, float vscale,
                                           int slot, int rs, int rhq, bool rvalid);
 
-template <class CT, class QT, int D, bool kNT>
+template <class CT, class QT, int D, bool kNT, int kB>
 __device__ __forceinline__ void rows_core(const DecodeArgs &a, const int32_t *table, int h,
                                           int jb0, int jb1, int end, int slot, int rs, int rhq,
                                           bool rvalid, int lim, int tbl0, int &settle) {
@@ -493,7 +589,7 @@ __device__ __forceinline__ void rows_core(const DecodeArgs &a, const int32_t *ta
   load_query<CT, D>(a, rs, rhq, rvalid, st);
   float kscale, vscale;
   head_scales<CT>(a, h, kscale, vscale);
-  stream_blocks<CT, D, kNT>(a, table, h, jb0, jb1, tbl0, lim, end, kscale, st);
+  stream_blocks<CT, D, kNT, kB>(a, table, h, jb0, jb1, tbl0, lim, end, kscale, st);
   // Wait here, where the ring has nothing left in flight, for every load this item started that its
   // blocks may not have consumed (the query and table entries of an item without blocks) and for
   // `settle` (the next item's table entries, fetched before this item started): later, behind this
@@ -546,37 +642,29 @@ __device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D>
   }
 }
 
-// Wavefront item of the decode: KV head h over positions [jb0 * 16, end) of one block-table row:
-//  - sequence item (s >= 0): the rows are the g query heads of sequence s, on s's table row.
-//  - prefix tile (s < 0): the rows are flat rows row0 .. row0 + 15 of the batch (flat row r is
-//    query head h*g + r % g of sequence r / g), on the shared prefix's table; each row masks the
-//    positions at or past its own context length (`lens`, the clamped lengths in LDS).
-// Wavefronts of one workgroup run their items independently, so one wavefront's item prologue
-// (query, table fetch, first loads) and epilogue overlap the other wavefronts' block streams.
-template <class CT, class QT, int D, bool kNT>
-__device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int row0_in, int h_in,
-                                          int jb0_in, int jb1_in, int end_in, int slot_in,
-                                          const int *lens, int tbl0, int &settle) {
+// Wavefront item of the decode: KV head h over positions [jb0 * 16, end) of sequence s's block
+// table row, against the g query heads of s (columns 0 .. g - 1 of the products).  Wavefronts of
+// one workgroup run their items independently, so one wavefront's item prologue (query, table
+// fetch, first loads) and epilogue overlap the other wavefronts' block streams.
+template <class CT, class QT, int D, bool kNT, int kB>
+__device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int h_in, int jb0_in,
+                                          int jb1_in, int end_in, int slot_in, int tbl0,
+                                          int &settle) {
   // The item is the same for the whole wavefront: keep its fields (and so the tile addresses) in
   // scalar registers.
   const int s = __builtin_amdgcn_readfirstlane(s_in);
-  const int row0 = __builtin_amdgcn_readfirstlane(row0_in);
   const int h = __builtin_amdgcn_readfirstlane(h_in);
   const int jb0 = __builtin_amdgcn_readfirstlane(jb0_in);
   const int jb1 = __builtin_amdgcn_readfirstlane(jb1_in);
   const int end = __builtin_amdgcn_readfirstlane(end_in);
   const int slot = __builtin_amdgcn_readfirstlane(slot_in);
-  const int H = a.cache.num_kv_heads, Hq = a.num_q_heads, g = Hq / H;
+  const int g = a.num_q_heads / a.cache.num_kv_heads;
   const int col = threadIdx.x & 15;
-  const bool tile = s < 0;
-  const int nrows = tile ? min(16, a.num_seqs * g - row0) : g;
-  const bool rvalid = col < nrows;
-  const int rs = tile ? (rvalid ? (row0 + col) / g : 0) : s;
-  const int rhq = h * g + (rvalid ? (tile ? (row0 + col) % g : col) : 0);
-  const int lim = tile && rvalid ? min(end, lens[rs]) : end;
-  const int32_t *table =
-      tile ? a.prefix_table : a.block_tables + (size_t)s * a.max_blocks_per_seq;
-  rows_core<CT, QT, D, kNT>(a, table, h, jb0, jb1, end, slot, rs, rhq, rvalid, lim, tbl0, settle);
+  const bool rvalid = col < g;
+  const int rhq = h * g + (rvalid ? col : 0);
+  const int32_t *table = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  rows_core<CT, QT, D, kNT, kB>(a, table, h, jb0, jb1, end, slot, s, rhq, rvalid, end, tbl0,
+                                settle);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -796,15 +884,22 @@ __device__ __forceinline__ SeqItem sequence_item(const DecodeArgs &a, int s, int
   return it;
 }
 
-__device__ __forceinline__ const int32_t *table_row(const DecodeArgs &a, int s) {
-  return a.block_tables + (size_t)s * a.max_blocks_per_seq;
-}
-
-template <class CT, class QT, int D>
+template <class CT, class QT, int D, int kB>
 __device__ __forceinline__ void run_sequence_item(const DecodeArgs &a, const SeqItem &it, int tbl0,
                                                   int &settle) {
-  wave_item<CT, QT, D, PA_DECODE_NT>(a, it.s, 0, it.h, it.jb0, it.jb1, it.end, it.slot, nullptr,
-                                     tbl0, settle);
+  wave_item<CT, QT, D, PA_DECODE_NT, kB>(a, it.s, it.h, it.jb0, it.jb1, it.end, it.slot, tbl0,
+                                         settle);
+}
+
+// Lane i's table entry of the first ring chunk of a sequence item (the table entries of its first
+// 64 blocks at kB = 16).
+template <int kB>
+__device__ __forceinline__ int item_table_entries(const DecodeArgs &a, const SeqItem &it) {
+  const int32_t *row = a.block_tables + (size_t)it.s * a.max_blocks_per_seq;
+  if constexpr (kB == 16) return first_table_entries(row, it.jb0, it.jb1);
+  else
+    return chunk_table_entries<kB>(row, it.jb0, min(BlockSteps<kB>::kChunk, it.jb1 - it.jb0),
+                                   it.end);
 }
 
 // Grid modes.  Direct (plain decode only, more than kMaxScanSeqs sequences): wavefront
@@ -818,12 +913,13 @@ __device__ __forceinline__ void run_sequence_item(const DecodeArgs &a, const Seq
 // each block through LDS (prefix_group), so a block crosses from L2 once per group instead of once
 // per 16 rows.  The sequence items go first to the wavefronts of workgroups without prefix work, so
 // the streaming of private blocks from HBM starts at once beside the prefix groups.
-template <class CT, class QT, int D, bool kPre>
+template <class CT, class QT, int D, bool kPre, int kB>
 __global__ __launch_bounds__(256)
 #if PA_DECODE_OCC
 __attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
 #endif
 void decode_mfma_kernel(DecodeArgs a) {
+  static_assert(!kPre || kB == 16, "the shared prefix runs on 16-position blocks");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = a.num_seqs, H = a.cache.num_kv_heads, g = a.num_q_heads / H;
@@ -839,8 +935,7 @@ void decode_mfma_kernel(DecodeArgs a) {
     if (part < n) {
       const SeqItem it = sequence_item(a, (int)s, L, part, h);
       int none = 0;
-      run_sequence_item<CT, QT, D>(a, it, first_table_entries(table_row(a, it.s), it.jb0, it.jb1),
-                                   none);
+      run_sequence_item<CT, QT, D, kB>(a, it, item_table_entries<kB>(a, it), none);
     }
     return;
   }
@@ -922,16 +1017,16 @@ void decode_mfma_kernel(DecodeArgs a) {
   // instead of three (context length, table, blocks).
   if (rank < total) {
     SeqItem it = item_of(rank);
-    int tbl = first_table_entries(table_row(a, it.s), it.jb0, it.jb1);
+    int tbl = item_table_entries<kB>(a, it);
     asm volatile("" : "+v"(tbl));  // waited for here, once, not at the loop header every item
     for (int f = rank; f < total; f += GW) {
       SeqItem next = it;
       int tbl_next = -1;
       if (f + GW < total) {
         next = item_of(f + GW);
-        tbl_next = first_table_entries(table_row(a, next.s), next.jb0, next.jb1);
+        tbl_next = item_table_entries<kB>(a, next);
       }
-      run_sequence_item<CT, QT, D>(a, it, tbl, tbl_next);
+      run_sequence_item<CT, QT, D, kB>(a, it, tbl, tbl_next);
       it = next;
       tbl = tbl_next;
     }
@@ -1273,7 +1368,7 @@ hipError_t launch_prefill_d(const DecodeArgs &a, hipStream_t s) {
 
 // Workgroups of one instantiation that fit on the device at once (occupancy x compute units),
 // looked up once per device.
-template <class CT, class QT, int D, bool kPre>
+template <class CT, class QT, int D, bool kPre, int kB>
 int resident_groups() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];
@@ -1284,7 +1379,7 @@ int resident_groups() {
     if (c > 0) return c;
   }
   int occ = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_mfma_kernel<CT, QT, D, kPre>, 256,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_mfma_kernel<CT, QT, D, kPre, kB>, 256,
                                                    0) !=
           hipSuccess || occ < 1)
     occ = 1;
@@ -1296,22 +1391,28 @@ int resident_groups() {
   return n;
 }
 
-template <class CT, class QT, int D, bool kPre>
+template <class CT, class QT, int D, bool kPre, int kB>
 hipError_t launch_ddp(DecodeArgs a, hipStream_t s) {
   const int64_t items = (int64_t)a.num_partitions * a.cache.num_kv_heads * a.num_seqs;
   const int64_t direct = (items + kWaves - 1) / kWaves;  // one wavefront per item
   a.persistent = a.num_seqs <= (kPre ? kMaxScanSeqsPrefix : kMaxScanSeqs);
   dim3 grid((unsigned)direct);
-  if (a.persistent)
-    grid = dim3((unsigned)(PA_SPREAD ? resident_groups<CT, QT, D, kPre>()
-                                     : std::min<int64_t>(direct, resident_groups<CT, QT, D, kPre>())));
-  decode_mfma_kernel<CT, QT, D, kPre><<<grid, dim3(256), 0, s>>>(a);
+  if (a.persistent) {
+    const int resident = resident_groups<CT, QT, D, kPre, kB>();
+    grid = dim3((unsigned)(PA_SPREAD ? resident : std::min<int64_t>(direct, resident)));
+  }
+  decode_mfma_kernel<CT, QT, D, kPre, kB><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <class CT, class QT, int D>
 hipError_t launch_dd(const DecodeArgs &a, hipStream_t s) {
-  return a.prefix_len > 0 ? launch_ddp<CT, QT, D, true>(a, s) : launch_ddp<CT, QT, D, false>(a, s);
+  if (a.prefix_len > 0) return launch_ddp<CT, QT, D, true, 16>(a, s);
+  switch (a.cache.block_size) {
+    case 8: return launch_ddp<CT, QT, D, false, 8>(a, s);
+    case 32: return launch_ddp<CT, QT, D, false, 32>(a, s);
+    default: return launch_ddp<CT, QT, D, false, 16>(a, s);
+  }
 }
 
 template <class CT, class QT>

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   for (int j = jb0 + w; j < jb1; j += kWaves) {
     const int bid = table[j];
     if ((unsigned)bid >= (unsigned)a.cache.num_blocks) continue;  // never dereferenced
-    const size_t tile = L::tile(bid, h, H, D);
+    const size_t tile = L::tile(bid, h, H, D, kBlock);  // this kernel runs on 16-position blocks
     const int tok0 = j * kBlock;
 
     // ---- z[i] = scale * log2(e) * <q_i, k_t> for this lane's token t

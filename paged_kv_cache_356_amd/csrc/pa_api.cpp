@@ -28,11 +28,13 @@ pa_status ok() { return PA_OK; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool block_size_ok(int32_t b) { return b == 8 || b == PA_BLOCK_SIZE || b == 32; }
+
 pa_status check_cache(const pa_cache *c, const char *who) {
   if (!c) return fail(PA_ERR_NULL, "%s: cache is NULL", who);
-  if (c->block_size != PA_BLOCK_SIZE)
-    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only %d is supported)", who, c->block_size,
-                PA_BLOCK_SIZE);
+  if (!block_size_ok(c->block_size))
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (8, 16 or 32 supported)", who,
+                c->block_size);
   if (c->num_blocks < 0) return fail(PA_ERR_SHAPE, "%s: num_blocks %d < 0", who, c->num_blocks);
   if (c->num_kv_heads < 1 || c->num_kv_heads > 16)
     return fail(PA_ERR_UNSUPPORTED, "%s: num_kv_heads %d outside 1..16", who, c->num_kv_heads);
@@ -58,6 +60,7 @@ pa::CacheArgs cache_args(const pa_cache *c) {
   a.k_scale = c->k_scale;
   a.v_scale = c->v_scale;
   a.num_blocks = c->num_blocks;
+  a.block_size = c->block_size;
   a.num_kv_heads = c->num_kv_heads;
   a.head_dim = c->head_dim;
   a.dtype = c->cache_dtype;
@@ -105,7 +108,7 @@ size_t ws_bytes_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int
 extern "C" {
 
 size_t pa_pool_bytes(const pa_cache *c) {
-  if (!c || c->block_size != PA_BLOCK_SIZE || c->num_blocks < 0 || c->num_kv_heads < 1 ||
+  if (!c || !block_size_ok(c->block_size) || c->num_blocks < 0 || c->num_kv_heads < 1 ||
       c->head_dim < 1)
     return 0;
   const int e = pa::dtype_bytes(c->cache_dtype);
@@ -212,8 +215,20 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
   if (q_stride < (int64_t)num_q_heads * D)
     return fail(PA_ERR_SHAPE, "%s: q_stride %lld below a row", who, (long long)q_stride);
   if ((flags & ~PA_DECODE_FORCE_VALU) != 0) return fail(PA_ERR_SHAPE, "%s: unknown flags", who);
+  const int B = cache->block_size;
+  if (B != PA_BLOCK_SIZE) {
+    if (prefix_len > 0)
+      return fail(PA_ERR_UNSUPPORTED, "%s: a shared prefix needs block_size %d", who,
+                  PA_BLOCK_SIZE);
+    if (flags & PA_DECODE_FORCE_VALU)
+      return fail(PA_ERR_UNSUPPORTED, "%s: the vector-ALU kernel needs block_size %d", who,
+                  PA_BLOCK_SIZE);
+    // 8-position blocks are read through one buffer descriptor per pool: 32-bit offsets
+    if (B == 8 && pa_pool_bytes(cache) > (size_t)0xffff0000u)
+      return fail(PA_ERR_UNSUPPORTED, "%s: block_size 8 needs a pool below 4 GiB", who);
+  }
 
-  const int64_t cap = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
+  const int64_t cap = (int64_t)max_blocks_per_seq * B;
   const int32_t max_len = (int32_t)(max_context_len < cap ? max_context_len : cap);
   pa::DecodeArgs a;
   a.out = out;
@@ -269,6 +284,12 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool use_mfma = use_prefix || (!force_valu && pa::decode_mfma_supports(a));
+  if (!use_mfma && B != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: block_size %d runs on the matrix cores only (f16 or bf16 cache with the same "
+                "query dtype, or fp8 cache with f16 queries; 16-byte aligned query rows, 8-byte "
+                "aligned output)",
+                who, B);
   hipError_t e = use_mfma ? pa::launch_decode_mfma(a, s) : pa::launch_decode_valu(a, s);
   if (e == hipSuccess) e = pa::launch_partition_reduce(a, s);
   return launch_status(e, who);
@@ -355,13 +376,14 @@ pa_status pa_copy_blocks(const pa_cache *layers, int32_t num_layers, const int32
     pa_status st = check_cache(&layers[l], who);
     if (st != PA_OK) return st;
     if (layers[l].num_blocks != layers[0].num_blocks ||
+        layers[l].block_size != layers[0].block_size ||
         layers[l].num_kv_heads != layers[0].num_kv_heads ||
         layers[l].head_dim != layers[0].head_dim || layers[l].cache_dtype != layers[0].cache_dtype)
       return fail(PA_ERR_SHAPE, "%s: layer %d differs in shape or dtype from layer 0", who, l);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t block_bytes = (int64_t)layers[0].num_kv_heads * PA_BLOCK_SIZE * layers[0].head_dim *
-                              pa::dtype_bytes(layers[0].cache_dtype);
+  const int64_t block_bytes = (int64_t)layers[0].num_kv_heads * layers[0].block_size *
+                              layers[0].head_dim * pa::dtype_bytes(layers[0].cache_dtype);
   for (int32_t l0 = 0; l0 < num_layers; l0 += pa::CopyArgs::kMaxLayers) {
     pa::CopyArgs a;
     a.num_layers = num_layers - l0 < pa::CopyArgs::kMaxLayers ? num_layers - l0
@@ -409,6 +431,8 @@ pa_status pa_prefill_attention(void *out, const void *query, int32_t q_dtype, in
   if ((int64_t)num_seqs * H * groups > 0x7fffffff)
     return fail(PA_ERR_SHAPE, "%s: grid of %lld workgroups too large", who,
                 (long long)((int64_t)num_seqs * H * groups));
+  if (cache->block_size != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED, "%s: prefill needs block_size %d", who, PA_BLOCK_SIZE);
   const int64_t cap = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
   pa::DecodeArgs a{};
   a.out = out;
@@ -462,6 +486,7 @@ pa_status pa_swap_blocks(const pa_cache *layers, int32_t num_layers, void *const
     pa_status st = check_cache(&layers[l], who);
     if (st != PA_OK) return st;
     if (layers[l].num_blocks != layers[0].num_blocks ||
+        layers[l].block_size != layers[0].block_size ||
         layers[l].num_kv_heads != layers[0].num_kv_heads ||
         layers[l].head_dim != layers[0].head_dim || layers[l].cache_dtype != layers[0].cache_dtype)
       return fail(PA_ERR_SHAPE, "%s: layer %d differs in shape or dtype from layer 0", who, l);
@@ -472,8 +497,8 @@ pa_status pa_swap_blocks(const pa_cache *layers, int32_t num_layers, void *const
     return fail(PA_ERR_UNSUPPORTED,
                 "%s: block_pairs is neither device memory nor pinned host memory", who);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t block_bytes = (int64_t)layers[0].num_kv_heads * PA_BLOCK_SIZE * layers[0].head_dim *
-                              pa::dtype_bytes(layers[0].cache_dtype);
+  const int64_t block_bytes = (int64_t)layers[0].num_kv_heads * layers[0].block_size *
+                              layers[0].head_dim * pa::dtype_bytes(layers[0].cache_dtype);
   for (int32_t l0 = 0; l0 < num_layers; l0 += pa::SwapArgs::kMaxLayers) {
     pa::SwapArgs a;
     a.num_layers = num_layers - l0 < pa::SwapArgs::kMaxLayers ? num_layers - l0

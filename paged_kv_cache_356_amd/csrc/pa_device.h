@@ -90,16 +90,18 @@ template <> __device__ __forceinline__ float cache_to_f32<bf16_t>(uint16_t v) {
 }
 template <> __device__ __forceinline__ float cache_to_f32<fp8_t>(uint8_t v) { return e4m3_to_f32(v); }
 
-// Pool layout (include/pa.h).  E = 16 / bytes elements per 16-byte vector.
-// K tile: element (t, i) at ((i / E) * 16 + t) * E + i % E;  V tile: element (t, i) at i * 16 + t.
+// Pool layout (include/pa.h), B positions per block.  E = 16 / bytes elements per 16-byte vector.
+// K tile: element (t, i) at ((i / E) * B + t) * E + i % E;  V tile: element (t, i) at i * B + t.
 template <int BYTES>
 struct Layout {
   static constexpr int E = 16 / BYTES;
-  __device__ __forceinline__ static size_t tile(int64_t block, int h, int H, int D) {
-    return ((size_t)block * H + h) * (size_t)kBlock * D;
+  __device__ __forceinline__ static size_t tile(int64_t block, int h, int H, int D, int B) {
+    return ((size_t)block * H + h) * (size_t)B * D;
   }
-  __device__ __forceinline__ static int k_off(int t, int i) { return ((i / E) * kBlock + t) * E + (i % E); }
-  __device__ __forceinline__ static int v_off(int t, int i) { return i * kBlock + t; }
+  __device__ __forceinline__ static int k_off(int t, int i, int B) {
+    return ((i / E) * B + t) * E + (i % E);
+  }
+  __device__ __forceinline__ static int v_off(int t, int i, int B) { return i * B + t; }
 };
 
 }  // namespace pa

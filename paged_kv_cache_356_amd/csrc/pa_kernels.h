@@ -10,7 +10,7 @@ namespace pa {
 
 enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };
 
-constexpr int kBlock = 16;  // token positions per KV block
+constexpr int kBlock = 16;  // token positions per KV block by default, and per ring step
 
 // Shared-prefix decode: prefix positions per prefix work item (and per workspace partition slot).
 #ifndef PA_PREFIX_CHUNK
@@ -28,6 +28,7 @@ struct CacheArgs {
   const float *k_scale;
   const float *v_scale;
   int32_t num_blocks;
+  int32_t block_size;  // token positions per block: 8, 16 or 32 (16 unless stated otherwise)
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t dtype;

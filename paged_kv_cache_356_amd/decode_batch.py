@@ -69,7 +69,9 @@ class DecodeBatch:
         self.free_order = wl.free_order(w)
         self.layers = list(range(w.num_layers)) if layers is None else list(layers)
         self.partition_size = w.partition_size if partition_size is None else partition_size
-        self.bm = api.BlockManager(w.num_blocks, api.PA_BLOCK_SIZE, self.free_order)
+        B = w.block_size
+        assert B == api.PA_BLOCK_SIZE or not w.prefix_len, "a shared prefix needs 16-position blocks"
+        self.bm = api.BlockManager(w.num_blocks, B, self.free_order)
 
         # (2) the workload's recipe on the block manager, then (4) this step's appends
         self.sets = []
@@ -83,7 +85,7 @@ class DecodeBatch:
         for st in self.sets:
             st.slots, st.pairs = self.bm.append_batch(st.seqs)
         self.max_context_len = int(self.lengths.max()) if S else 0
-        self.max_blocks = max(1, math.ceil(self.max_context_len / api.PA_BLOCK_SIZE))
+        self.max_blocks = max(1, math.ceil(self.max_context_len / B))
         for st in self.sets:
             st.tables, st.ctx = self.bm.export(st.seqs, self.max_blocks, pad_block)
             st.d_slots = torch.from_numpy(st.slots).to(device)
@@ -94,7 +96,7 @@ class DecodeBatch:
         # (3) pools and history
         self.caches = {}
         for l in self.layers:
-            cache = api.KVCache.allocate(w.num_blocks, H, D, w.cache_dtype, device)
+            cache = api.KVCache.allocate(w.num_blocks, H, D, w.cache_dtype, device, block_size=B)
             if pool_fill:
                 cache.k_pool.fill_(pool_fill)
                 cache.v_pool.fill_(pool_fill)
@@ -203,13 +205,14 @@ class DecodeBatch:
         if not unique:
             return int(self.lengths.astype(np.int64).sum()) * row
         st = self.sets[0]
+        B = w.block_size
         slots = set()
         for s in range(w.num_seqs):
             L = int(st.ctx[s])
-            for j in range(math.ceil(L / 16)):
+            for j in range(math.ceil(L / B)):
                 b = int(st.tables[s, j])
-                n = min(16, L - 16 * j)
-                slots.update(b * 16 + t for t in range(n))
+                n = min(B, L - B * j)
+                slots.update(b * B + t for t in range(n))
         return len(slots) * row
 
 

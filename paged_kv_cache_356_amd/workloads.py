@@ -52,6 +52,7 @@ class Workload:
     partition_size: int = 0  # 0 = library default
     prefix_len: int = 0      # shared prefix tokens
     description: str = ""
+    block_size: int = BLOCK_SIZE  # token positions per block
 
     @property
     def seed(self) -> int:

@@ -231,6 +231,61 @@ def test_many_sequences_direct_grid():
     _check_batch(b, ob, 0, TOL["f16"], sel=sel)
 
 
+@pytest.mark.parametrize("B", [8, 32])
+@pytest.mark.parametrize("name", ["f16_batch32", "bf16_32k_batch8", "fp8_28layer_batch512"])
+def test_block_sizes_match_oracle(name, B):
+    """Pools of 8- and 32-position blocks: the same reduced workloads against the oracle run with
+    that block size, the step's cache writes bit-exact, partitions that start inside a block."""
+    kw = dict(SMALL[name])
+    kw["num_blocks"] = kw["num_blocks"] * 16 // B
+    w = wl.WORKLOADS[name].replace(block_size=B, **kw)
+    pad = _pad_block(w)
+    for ps in (0, 48):
+        _say(f"{name} reduced, block size {B}, partition {ps}")
+        b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON,
+                        lengths=SMALL_LENGTHS[name], partition_size=ps)
+        ob = OracleBatch(b, pad, pool_fill=POISON)
+        ob.metadata_matches(b)
+        for l in b.layers:
+            _check_batch(b, ob, l, TOL[w.cache_dtype])
+            kp, vp, _, _ = ob.pools[(l, 0)]
+            dk, dv = device_pool_bytes(b.caches[l])
+            assert np.array_equal(dk, kp.view(np.uint8)) and np.array_equal(dv, vp.view(np.uint8))
+
+
+@pytest.mark.parametrize("B", [8, 32])
+def test_block_sizes_out_of_range_entry(B):
+    """A table entry outside the pool leaves its B positions out, also when it is one of the two
+    blocks of a 16-position step (B = 8) or one step of two (B = 32)."""
+    w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=2, num_blocks=4096 // B, block_size=B)
+    _say(f"out-of-range entry, block size {B}")
+    pad = _pad_block(w)
+    b = DecodeBatch(w, keep_values=True, lengths=[100, 77], pad_block=pad, pool_fill=POISON)
+    b.run_step(0)
+    st = b.sets[0]
+    tables = st.d_tables.clone()
+    j = 3 if B == 8 else 1  # positions 24..31, or 32..63
+    tables[0, j] = w.num_blocks + 5
+    out = torch.full_like(st.out[0], 7.0)
+    api.pa_decode_attention(out, st.q[0], b.caches[0], tables, st.d_ctx, b.max_context_len,
+                            w.scale, 0, b.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(out[1], st.out[0][1])
+    ob = OracleBatch(b, pad, pool_fill=POISON)
+    ob.build_pools(b, 0)
+    kp, vp, _, _ = ob.pools[(0, 0)]
+    t0 = ob.sets[0]["tables"][0]
+    H, D = w.num_kv_heads, w.head_dim
+    q = raw(st.q[0][0]).reshape(-1)
+    keep = np.r_[0:j * B, (j + 1) * B:100]
+    ref = np.zeros((w.num_q_heads, D))
+    for hq in range(w.num_q_heads):
+        kc, vc = oracle.gather(kp, vp, "f16", None, None, w.num_blocks, H, D, t0, 100, hq // 7, B=B)
+        qd = oracle.f16_to_f64(q[hq * D:(hq + 1) * D])
+        ref[hq] = oracle.attend_contiguous(qd, kc[keep], vc[keep], w.scale)
+    assert max_abs_err(as_f64(out[0]), ref) <= TOL["f16"]
+
+
 # --------------------------------------------------------------------------- invariances
 def test_permutation_of_physical_blocks_is_bitwise_invisible():
     _say("permutation invariance")

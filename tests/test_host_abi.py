@@ -58,7 +58,7 @@ def _decode(cache, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(block_size=8), -3), (dict(head_dim=96), -3), (dict(num_kv_heads=0), -3),
+    (dict(block_size=12), -3), (dict(head_dim=96), -3), (dict(num_kv_heads=0), -3),
     (dict(cache_dtype=9), -3), (dict(k_pool=None), -1), (dict(k_pool=17), -2),
     (dict(cache_dtype=api.PA_FP8_E4M3), -1), (dict(k_scale=64), -2),
 ])
@@ -95,6 +95,34 @@ def _decode_prefix(cache, prefix_table=1024, prefix_len=64, **kw):
 def test_shared_prefix_decode_validation(kw, status):
     assert _decode_prefix(_cache(), **kw) == status
     assert api.lib().pa_last_error()
+
+
+def test_block_sizes_8_and_32():
+    """Pools of 8- and 32-position blocks are sized by the same layout; the paths that run only on
+    16-position blocks refuse them before any launch."""
+    for B in (8, 16, 32):
+        c = _cache(block_size=B)
+        assert api.lib().pa_pool_bytes(ctypes.byref(c)) == 8 * 4 * B * 128 * 2
+    assert api.lib().pa_pool_bytes(ctypes.byref(_cache(block_size=12))) == 0
+    # the vector-ALU kernel (fp32 caches, or forced) and the shared prefix need B = 16
+    f32 = _cache(block_size=8, cache_dtype=api.PA_F32)
+    assert _decode(f32, q_dtype=api.PA_F32) == -3
+    assert _decode(_cache(block_size=32), flags=api.PA_DECODE_FORCE_VALU) == -3
+    assert _decode_prefix(_cache(block_size=32)) == -3
+    # 8-position blocks are addressed with 32-bit offsets into one pool
+    assert _decode(_cache(block_size=8, num_blocks=1 << 21)) == -3
+    assert _prefill(_cache(block_size=8)) == -3
+    assert api.lib().pa_last_error()
+
+
+def _prefill(cache, **kw):
+    a = dict(out=64, query=128, q_dtype=api.PA_F16, q_stride=0, tables=256, max_blocks=8, ctx=512,
+             qstart=1024, S=2, T=8, Hq=28, max_q=4, max_ctx=128, scale=0.1)
+    a.update(kw)
+    return api.lib().pa_prefill_attention(
+        a["out"], a["query"], a["q_dtype"], a["q_stride"], ctypes.byref(cache), a["tables"],
+        a["max_blocks"], a["ctx"], a["qstart"], a["S"], a["T"], a["Hq"], a["max_q"], a["max_ctx"],
+        a["scale"], None)
 
 
 def test_shared_prefix_workspace_sizing():
@@ -157,7 +185,7 @@ def test_copy_pair_checks():
 @pytest.mark.parametrize("seed", range(8))
 def test_block_manager_matches_model(seed):
     g = np.random.default_rng(100 + seed)
-    nb, B = 96, int(g.choice([1, 4, 16]))
+    nb, B = 96, int(g.choice([1, 4, 8, 16, 32]))
     order = g.permutation(nb)
     prod = api.BlockManager(nb, B, order)
     model = BlockManagerModel(nb, B, order)

@@ -562,3 +562,60 @@ def test_prefill_closed_forms():
                                    D, tables, np.array([L]), qs, Hq, 0.125)
     for p in range(L):
         assert np.max(np.abs(out[p, :, :] - v[: p + 1, 0].mean(axis=0))) < 1e-12
+
+
+# ------------------------------------------------------------------------ block size
+@pytest.mark.parametrize("dtype", ["f16", "fp8"])
+def test_block_size_changes_the_layout_not_the_result(dtype):
+    """The block size only decides where positions land ("PagedAttention" (devoured.fyi), "Why the
+    attention kernel works at all": the math is untouched by the layout): the same sequences
+    written into pools of 8-, 16- and 32-position blocks, through tables from a block manager of
+    that size, give bitwise the same oracle output, which matches SDPA on the rows."""
+    from oracle.bm_model import BlockManagerModel
+    H, Hq, D = 2, 6, 64
+    lengths = [5, 16, 17, 40, 33, 8]
+    kd = "f16"
+    k = [_values((L, H, D), kd, 40 + i) for i, L in enumerate(lengths)]
+    v = [_values((L, H, D), kd, 60 + i) for i, L in enumerate(lengths)]
+    q = _values((len(lengths), Hq, D), kd, 80)
+    ks = vs = None
+    if dtype == "fp8":  # amax / 448 per head: every value is inside the E4M3 range
+        ks = (torch.cat(k).float().abs().amax(dim=(0, 2)) / 448).numpy().astype(np.float32)
+        vs = (torch.cat(v).float().abs().amax(dim=(0, 2)) / 448).numpy().astype(np.float32)
+    outs = {}
+    for B in (8, 16, 32):
+        nb = 256 // B
+        bm = BlockManagerModel(nb, B, np.random.default_rng(B).permutation(nb))
+        seqs = [bm.add_seq() for _ in lengths]
+        slots = [[bm.append(s)[0] for _ in range(L)] for s, L in zip(seqs, lengths)]
+        M = max(-(-L // B) for L in lengths)
+        rows, ctx = bm.export(seqs, M, 0)
+        kp = host_pool(nb, H, D, dtype, B=B, fill=nan_bits(dtype))
+        vp = host_pool(nb, H, D, dtype, B=B, fill=nan_bits(dtype))
+        oracle.reshape_and_cache(kp, vp, dtype, ks, vs, nb, H, D, raw(torch.cat(k)), raw(torch.cat(v)),
+                                 kd, np.concatenate(slots).astype(np.int64), B=B)
+        outs[B] = oracle.decode_attention(raw(q).reshape(len(lengths), -1), kd, kp, vp, dtype, ks,
+                                          vs, nb, H, D, np.array(rows, np.int32),
+                                          np.array(ctx, np.int32), Hq, 0.125, B=B)
+    assert np.array_equal(outs[8], outs[16]) and np.array_equal(outs[32], outs[16])
+    for s, L in enumerate(lengths):
+        for hq in range(Hq):
+            h = hq // (Hq // H)
+            kk, vv = k[s][:, h].double(), v[s][:, h].double()
+            if dtype == "fp8":
+                kk = (k[s][:, h].float() / float(ks[h])).to(torch.float8_e4m3fn).double() * float(ks[h])
+                vv = (v[s][:, h].float() / float(vs[h])).to(torch.float8_e4m3fn).double() * float(vs[h])
+            ref = _sdpa(q[s, hq].double().numpy(), kk.numpy(), vv.numpy(), 0.125)
+            assert np.max(np.abs(outs[16][s, hq] - ref)) < 1e-12
+
+
+def test_layout_indices_of_an_8_position_block():
+    """Worked by hand from the layout description with B = 8 (H = 2 KV heads, D = 64, f16 so 8
+    elements per 16-byte vector): K element (t, i) of tile (b, h) sits at
+    (b*H + h)*B*D + ((i // 8)*B + t)*8 + i % 8; V element (t, i) at (b*H + h)*B*D + i*B + t."""
+    H, D, B = 2, 64, 8
+    # block 3, head 1, position 5, dim 19: tile 7*512 = 3584; K ((2*8 + 5)*8 + 3) = 171; V 19*8 + 5
+    assert oracle.k_index(3, 1, 5, 19, H, D, B, "f16") == 3584 + 171
+    assert oracle.v_index(3, 1, 5, 19, H, D, B) == 3584 + 157
+    # block 0, head 0, position 7, dim 63: K (7*8 + 7)*8 + 7 = 511 (the tile's last element)
+    assert oracle.k_index(0, 0, 7, 63, H, D, B, "f16") == 511
