@@ -58,8 +58,11 @@ typedef enum pa_dtype {
                       cache storage only, always with one fp32 scale per KV head             */
 } pa_dtype;
 
-/* The only block size this build supports: 16 token positions per block, the default the pages
- * give ([Digest] "PagedAttention in one picture" and "Misconceptions"). */
+/* The default block size: 16 token positions per block, the default the pages give ([Digest]
+ * "PagedAttention in one picture" and "Misconceptions").  Pools of 8 or 32 positions per block are
+ * accepted where a function says so: the pages describe the block size as a tradeoff between the
+ * padding in each sequence's last block and the table size and per-block overhead ([Digest]
+ * "Misconceptions"). */
 #define PA_BLOCK_SIZE 16
 
 /*
@@ -67,7 +70,8 @@ typedef enum pa_dtype {
  *
  * Pool layout (owned by the library; described here so that independent code can read it).
  * Let e be the element size of cache_dtype in bytes (f32 4, f16 2, bf16 2, fp8 1), E = 16 / e the
- * number of elements in one 16-byte vector, B = block_size = 16, D = head_dim, H = num_kv_heads.
+ * number of elements in one 16-byte vector, B = block_size (8, 16 or 32), D = head_dim,
+ * H = num_kv_heads.
  * Both pools are block-major and then head-major: block b holds H consecutive tiles, one per KV
  * head, each of B*D elements (B*D*e bytes: 4 KiB for f16/bf16 at D = 128, always a whole number
  * of 128-byte lines).  Tile (b, h) starts at element (b*H + h) * B*D.  Inside a tile:
@@ -75,7 +79,7 @@ typedef enum pa_dtype {
  *   K tile: the head dimension is cut into D/E vectors of E elements (16 bytes).  Vector c of token
  *           slot t is stored at vector index c*B + t, so element (t, i) sits at element offset
  *           ((i / E) * B + t) * E + (i % E) within the tile.  One 16-byte vector per token, for all
- *           16 tokens, forms 256 contiguous bytes.
+ *           B tokens, forms 16 * B contiguous bytes.
  *   V tile: stored transposed: the B values of head-dimension index i are contiguous, so element
  *           (t, i) sits at element offset i * B + t within the tile.
  *
@@ -93,7 +97,7 @@ typedef struct pa_cache {
   const float *k_scale;    /* device [num_kv_heads] fp32, fp8 only, else NULL      */
   const float *v_scale;    /* device [num_kv_heads] fp32, fp8 only, else NULL      */
   int32_t num_blocks;      /* physical blocks in this pool                        */
-  int32_t block_size;      /* must be PA_BLOCK_SIZE                               */
+  int32_t block_size;      /* 8, 16 (PA_BLOCK_SIZE) or 32, see each function       */
   int32_t num_kv_heads;    /* 1 .. 16                                             */
   int32_t head_dim;        /* 64 or 128                                           */
   int32_t cache_dtype;     /* a pa_dtype                                          */
@@ -113,9 +117,9 @@ size_t pa_pool_bytes(const pa_cache *cache);
  *   key, value    device [num_tokens] rows; row t holds num_kv_heads * head_dim elements of
  *                 `in_dtype` laid out [kv_head][head_dim]; consecutive rows are key_stride /
  *                 value_stride ELEMENTS apart (>= num_kv_heads * head_dim).
- *   slot_mapping  device int64 [num_tokens]: token t goes to block slot_mapping[t] / 16, slot
- *                 slot_mapping[t] % 16.  A negative value skips the token (padding); a value
- *                 >= num_blocks * 16 is also skipped and never written.
+ *   slot_mapping  device int64 [num_tokens]: token t goes to block slot_mapping[t] / B, slot
+ *                 slot_mapping[t] % B (B = block_size: 8, 16 or 32).  A negative value skips the
+ *                 token (padding); a value >= num_blocks * B is also skipped and never written.
  *   in_dtype      f32/f16/bf16.  For an f32/f16/bf16 cache it must equal cache_dtype and the
  *                 element is copied bit for bit.  For an fp8 cache each element x becomes
  *                 E4M3FN(round-to-nearest-even, saturating at +-448)(float(x) / scale[h]), the
@@ -150,29 +154,34 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   for sequence s with L = context_lens[s] and query head q (KV head h = q / (num_q_heads /
  *   num_kv_heads)):  z_p = scale * <query[s][q], K_s[p][h]> for p in [0, L);
  *   out[s][q] = sum_p exp(z_p - max z) * V_s[p][h] / sum_p exp(z_p - max z);   out = 0 when L == 0,
- *   where K_s[p][h] is element (slot p % 16) of tile (block_tables[s][p / 16], h) of the K pool.
+ *   where K_s[p][h] is element (slot p % B) of tile (block_tables[s][p / B], h) of the K pool,
+ *   B = block_size.
  *
  *   out           device [num_seqs][num_q_heads][head_dim] in q_dtype, written in full.
  *   query         device rows of num_q_heads * head_dim elements of q_dtype; sequence s starts at
  *                 element s * q_stride (q_stride 0 means num_q_heads * head_dim).
  *   q_dtype       f32 with an f32 cache; f16 with an f16 cache; bf16 with a bf16 cache; f16 or
  *                 bf16 with an fp8 cache.
- *   block_tables  device int32 [num_seqs][max_blocks_per_seq].  Only the first ceil(L / 16)
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq].  Only the first ceil(L / B)
  *                 entries of row s are read; the rest may hold anything.  An entry outside
- *                 [0, num_blocks) is never dereferenced: the 16 positions it covers are left out.
+ *                 [0, num_blocks) is never dereferenced: the B positions it covers are left out.
  *   context_lens  device int32 [num_seqs]; L includes the token written this step.  Values are
- *                 clamped to [0, min(max_context_len, 16 * max_blocks_per_seq)].
+ *                 clamped to [0, min(max_context_len, B * max_blocks_per_seq)].
  *   max_context_len  host upper bound of context_lens, used to size the launch without reading
  *                 the device.
  *   scale         softmax scale, normally 1 / sqrt(head_dim).
  *   partition_size  most tokens per split-K partition: 0 = pa_decode_auto_partition(),
  *                 otherwise a positive multiple of 16.  A context of L tokens is cut into
- *                 ceil(L / partition_size) partitions of whole blocks, as equal as whole blocks
- *                 allow; when there are several they are computed independently (running max,
+ *                 ceil(L / partition_size) partitions of whole 16-position steps, as equal as
+ *                 those allow (a partition may start inside a 32-position block); when there are
+ *                 several they are computed independently (running max,
  *                 running sum, unnormalised output) and merged by a second kernel.
  *   workspace     device scratch of at least pa_decode_workspace_bytes() bytes (NULL if 0).
- * Supported: block_size 16, head_dim 64 or 128, num_q_heads a multiple of num_kv_heads with at
- * most 16 query heads per KV head.
+ * Supported: head_dim 64 or 128, num_q_heads a multiple of num_kv_heads with at most 16 query
+ * heads per KV head; block_size 16 for every dtype, 8 or 32 for the matrix-core configurations
+ * (f16 / bf16 caches with the same query dtype, fp8 caches with f16 queries, 16-byte aligned query
+ * rows, 8-byte aligned output), 8 only for pools below 4 GiB.  Anything else is
+ * PA_ERR_UNSUPPORTED.
  */
 pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int64_t q_stride,
                               const pa_cache *cache, const int32_t *block_tables,
@@ -189,8 +198,8 @@ pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int
  * prefix" and "Misconceptions", on system prompts shared by many users).  The result is the same
  * attention as pa_decode_attention over each sequence's whole context (within floating-point
  * rounding: the summation order differs); only the reading changes: each block of the prefix is
- * read once for all sequences, with up to 16 (sequence, query head) rows per matrix-core product,
- * instead of once per sequence.
+ * read for groups of 64 (sequence, query head) rows at a time, staged once per group in on-chip
+ * memory, instead of once per sequence.
  *
  *   prefix_table  device int32 [prefix_len / 16]: the prefix's physical block ids.  The first
  *                 prefix_len / 16 entries of every block_tables row must hold the same ids (the
@@ -201,9 +210,9 @@ pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int
  *   workspace     at least pa_decode_shared_prefix_workspace_bytes() bytes.
  * The prefix is computed in chunks of 512 positions; the positions after it are cut into
  * partitions as in pa_decode_attention (ceil((L - prefix_len) / partition_size) of them).
- * All other arguments and rules are those of pa_decode_attention.  Batches the prefix path does not
- * cover (more than 4096 sequences, the vector-ALU dtype pairs, PA_DECODE_FORCE_VALU) are computed
- * by the plain decode, with the same result.
+ * All other arguments and rules are those of pa_decode_attention; block_size must be 16.  Batches
+ * the prefix path does not cover (more than 2048 sequences, the vector-ALU dtype pairs,
+ * PA_DECODE_FORCE_VALU) are computed by the plain decode, with the same result.
  */
 pa_status pa_decode_attention_shared_prefix(void *out, const void *query, int32_t q_dtype,
                                             int64_t q_stride, const pa_cache *cache,
@@ -239,10 +248,10 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_h
  *   max_query_len host upper bound of every n_s (sizes the grid; larger n_s are cut to it).
  *   Other arguments as in pa_decode_attention.  No workspace: each token's rows are computed
  *   whole by one wavefront.
- * Supported: the matrix-core configurations of pa_decode_attention (f16 / bf16 caches with the same
- * query dtype, fp8 caches with f16 queries; head_dim 64 or 128; at most 16 query heads per KV
- * head; 16-byte aligned query rows and q_stride a multiple of 8; 8-byte aligned output); anything
- * else is PA_ERR_UNSUPPORTED.
+ * Supported: block_size 16 and the matrix-core configurations of pa_decode_attention (f16 / bf16
+ * caches with the same query dtype, fp8 caches with f16 queries; head_dim 64 or 128; at most 16
+ * query heads per KV head; 16-byte aligned query rows and q_stride a multiple of 8; 8-byte aligned
+ * output); anything else is PA_ERR_UNSUPPORTED.
  */
 pa_status pa_prefill_attention(void *out, const void *query, int32_t q_dtype, int64_t q_stride,
                                const pa_cache *cache, const int32_t *block_tables,
