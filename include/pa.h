@@ -131,8 +131,9 @@ pa_status pa_reshape_and_cache(const pa_cache *cache, const void *key, const voi
                                const int64_t *slot_mapping, int32_t num_tokens, void *stream);
 
 /* Partition size used when pa_decode_attention is given partition_size = 0 for these sizes:
- * 1,024 positions for at most 64 (sequence, KV head) rows with contexts of 4,096 or more, else 256
- * halved (down to 64) while that leaves fewer than 512 partitions in all. */
+ * 1,024 positions for at most 64 (sequence, KV head) rows with contexts of 4,096 or more; 512 for
+ * 2,048 rows or more with contexts of 8,192 or more; else 256 halved (down to 64) while that
+ * leaves fewer than 512 partitions in all. */
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len);
 
 /* Device workspace bytes pa_decode_attention needs for these sizes (0 is a valid answer when the

@@ -150,11 +150,14 @@ pa_status pa_reshape_and_cache(const pa_cache *cache, const void *key, const voi
 
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
   // Measured on MI355X: a few long (sequence, KV head) rows run best with 1,024-position
-  // partitions (rare item prologues, still enough items to spread); everything else with 256,
-  // halved (down to 64) while that leaves fewer than 512 items to spread over the device.
+  // partitions (rare item prologues, still enough items to spread); many rows with long contexts
+  // (two or more items per wavefront at any size) with 512 (fewer item boundaries per wavefront,
+  // fewer partials); everything else with 256, halved (down to 64) while that leaves fewer than
+  // 512 items to spread over the device.
   const int64_t rows = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
   const int32_t L = max_context_len > 0 ? max_context_len : 1;
   if (rows <= 64 && L >= 4096) return 1024;
+  if (rows >= 2048 && L >= 8192) return 512;
   int32_t pt = 256;
   while (pt > 64 && rows * ceil_div(L, pt) < 512) pt /= 2;
   return pt;

@@ -152,7 +152,8 @@ def test_workspace_sizing():
     assert need >= rows * 128 * 4 + rows * 2 * 4
     assert api.pa_decode_auto_partition(8, 4, 32768) == 1024    # few long rows
     assert api.pa_decode_auto_partition(32, 4, 2048) == 256
-    assert api.pa_decode_auto_partition(512, 4, 13708) == 256
+    assert api.pa_decode_auto_partition(512, 4, 13708) == 512   # many long rows
+    assert api.pa_decode_auto_partition(256, 4, 13708) == 256
     assert api.pa_decode_auto_partition(2, 2, 1000) == 64       # tiny batch: more, smaller items
     assert api.pa_decode_auto_partition(1, 1, 100) == 64
 
