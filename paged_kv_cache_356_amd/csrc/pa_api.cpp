@@ -233,7 +233,7 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
 
   const int64_t cap = (int64_t)max_blocks_per_seq * B;
   const int32_t max_len = (int32_t)(max_context_len < cap ? max_context_len : cap);
-  pa::DecodeArgs a;
+  pa::DecodeArgs a{};
   a.out = out;
   a.q = query;
   a.q_stride = q_stride;
