@@ -235,6 +235,9 @@ def main() -> int:
                          "16 / block size)")
     ap.add_argument("--no-prefix", action="store_true",
                     help="shared-prefix workload: use the plain decode instead of the shared-prefix one")
+    ap.add_argument("--fused", action="store_true",
+                    help="step through pa_decode_attention_append (the cache write inside the "
+                         "decode kernel) instead of reshape_and_cache + decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--swap", action="store_true",
@@ -300,18 +303,22 @@ def main() -> int:
 
     # Every library call enqueues on torch's current stream: the default stream when run eagerly,
     # the capture stream while a graph is being captured.
+    fused = args.fused
+
     def step(r: int):
         """One step of set r: the copy-on-write clone, then per layer the new token's K/V write and
-        the decode attention."""
+        the decode attention (one fused call with --fused, else reshape_and_cache + decode)."""
         batch.copy(r)
         for l in layers:
-            batch.reshape(r, l)
-            batch.decode(r, l, flags=flags)
+            if not fused:
+                batch.reshape(r, l)
+            batch.decode(r, l, flags=flags, append=fused)
 
     def decodes(n: int):
-        """n decode calls back to back, rotating over sets and layers (fresh KV for each)."""
+        """n decode calls back to back, rotating over sets and layers (fresh KV for each); the
+        fused calls rewrite the step's token, the same bytes to the same slot each time."""
         for k in range(n):
-            batch.decode(k % sets, layers[(k // sets) % len(layers)], flags=flags)
+            batch.decode(k % sets, layers[(k // sets) % len(layers)], flags=flags, append=fused)
 
     n_dec = max(8, min(64, sets * len(layers)))
     # Set-up: one pass over every set (the first write into a set's clone targets costs
@@ -373,6 +380,10 @@ def main() -> int:
     kv_logical = batch.kv_bytes_per_layer(unique=False)
     unique = w.prefix_len > 0
     alg = algorithmic_bytes(batch, unique=unique)
+    if fused:  # the call also reads each new token's K/V row and writes it into the cache
+        e_in = 4 if w.q_dtype == "f32" else 2
+        e_c = 1 if w.cache_dtype == "fp8" else (4 if w.cache_dtype == "f32" else 2)
+        alg += w.num_seqs * (2 * w.num_kv_heads * w.head_dim * (e_in + e_c) + 8)
     achieved = alg / dec_mean_s / 1e9
     value = kv_logical * layers / (ms_per_step / 1e3) / 1e9
     seqs_per_s_layer = w.num_seqs / (ms_per_step / 1e3 / layers)
@@ -399,6 +410,9 @@ def main() -> int:
                 w.num_seqs, w.num_kv_heads, batch.max_context_len),
             "kernel": "valu" if args.valu else "default",
             "shared_prefix_decode": bool(batch.use_prefix),
+            "step_calls": "copy_blocks (when the step clones) + per layer " +
+                          ("pa_decode_attention_append (cache write fused into the decode kernel)"
+                           if fused else "pa_reshape_and_cache + decode"),
             "sets_rotated": sets,
             "launch": "hip graph replay" if args.graph else "eager (GPU-bound)",
             "kv_bytes_per_step_logical": kv_logical * layers,
@@ -421,13 +435,14 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(w, args.partition < 0 and not args.valu and
+            "traffic": measured_traffic(w, args.partition < 0 and not args.valu and not fused and
                                         not args.num_blocks and not args.no_prefix and
                                         args.block_size == 16),
             "traffic_note": "HBM bytes per call from rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE "
                             "(decode + reduce kernels; profiles/traffic.json), null unless this run "
                             "is the measured configuration of unchanged kernels",
-            "kernel": ("pa_decode_attention_shared_prefix" if batch.use_prefix else
+            "kernel": ("pa_decode_attention_append" + (" (shared prefix)" if batch.use_prefix else "")
+                       if fused else "pa_decode_attention_shared_prefix" if batch.use_prefix else
                        "pa_decode_attention") + " (split-K decode + partition reduce)",
             "bytes_per_call": alg,
             "bytes_kind": "unique physical KV slots" if unique else "logical KV",

@@ -226,6 +226,44 @@ pa_status pa_decode_attention_shared_prefix(void *out, const void *query, int32_
                                             void *workspace, size_t workspace_bytes,
                                             uint32_t flags, void *stream);
 
+/*
+ * pa_decode_attention_append — one decode step with its cache write: pa_reshape_and_cache of each
+ * sequence's new token followed by pa_decode_attention (prefix_len = 0) or
+ * pa_decode_attention_shared_prefix (prefix_len > 0), in one call.  Each generated token appends
+ * one K/V entry to its sequence's current block ([Lesson06] "How paging grows") and is attended
+ * to in the same step, as position context_lens[s] - 1 ([Visualized] Parts 1 and 2).
+ *
+ *   key, value    device rows of num_kv_heads * head_dim elements of q_dtype, one per sequence;
+ *                 sequence s's row starts at element s * key_stride (value_stride); a stride of
+ *                 0 means num_kv_heads * head_dim.  Written into the cache as
+ *                 pa_reshape_and_cache writes rows of that dtype (a bit copy, or E4M3FN with the
+ *                 per-head scales for an fp8 cache).
+ *   slot_mapping  device int64 [num_seqs]: the slot of position context_lens[s] - 1 of sequence s
+ *                 (its block table's entry for that position times block_size, plus the offset),
+ *                 or negative for no write.  With a shared prefix the position must lie after it
+ *                 (context_lens[s] > prefix_len); a slot given for a shorter context is not
+ *                 written.  Two sequences must not share a slot.
+ *   prefix_table, prefix_len  as in pa_decode_attention_shared_prefix (NULL / 0: plain decode).
+ *   workspace     at least pa_decode_workspace_bytes() (pa_decode_shared_prefix_workspace_bytes()
+ *                 with a prefix) bytes.
+ * All other arguments and rules are those of pa_decode_attention.  The pools end byte for byte as
+ * pa_reshape_and_cache leaves them.  On the matrix-core kernel the wavefront that walks the last
+ * positions of each (sequence, KV head) writes that head's part of the token and takes the token
+ * from registers instead of reading it back, so one kernel does both; the attention equals that of
+ * the two calls within floating-point rounding (the new position is summed last).  Configurations
+ * of the vector-ALU kernel, and key/value rows that are not 4-byte aligned, run the two calls.
+ */
+pa_status pa_decode_attention_append(void *out, const void *query, int32_t q_dtype,
+                                     int64_t q_stride, const pa_cache *cache, const void *key,
+                                     const void *value, int64_t key_stride, int64_t value_stride,
+                                     const int64_t *slot_mapping, const int32_t *block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                     int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t max_context_len, float scale,
+                                     const int32_t *prefix_table, int32_t prefix_len,
+                                     int32_t partition_size, void *workspace,
+                                     size_t workspace_bytes, uint32_t flags, void *stream);
+
 /* Device workspace bytes pa_decode_attention_shared_prefix needs for these sizes. */
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                                int32_t num_kv_heads, int32_t head_dim,

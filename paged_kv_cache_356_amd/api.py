@@ -31,6 +31,7 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPO
 EXPORTS = [
     "pa_pool_bytes", "pa_reshape_and_cache", "pa_decode_auto_partition",
     "pa_decode_workspace_bytes", "pa_decode_attention", "pa_decode_attention_shared_prefix",
+    "pa_decode_attention_append",
     "pa_decode_shared_prefix_workspace_bytes", "pa_copy_blocks", "pa_check_copy_pairs",
     "pa_prefill_attention", "pa_swap_blocks", "pa_bm_set_host_blocks", "pa_bm_swap_out",
     "pa_bm_swap_in",
@@ -78,6 +79,9 @@ def lib() -> ctypes.CDLL:
             "pa_decode_attention_shared_prefix": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _i32, _vp,
                                                           _i32, _i32, _i32, _f32, _vp, _i32, _i32,
                                                           _vp, _sz, _u32, _vp]),
+            "pa_decode_attention_append": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _vp, _i64, _i64,
+                                                   _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp,
+                                                   _i32, _i32, _vp, _sz, _u32, _vp]),
             "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32,
                                                               _i32]),
             "pa_copy_blocks": (_i32, [_cp, _i32, _vp, _i32, _vp]),
@@ -226,15 +230,18 @@ def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max
 
 
 class DecodeCall:
-    """pa_decode_attention, or pa_decode_attention_shared_prefix when prefix_table is given, with
-    every argument but the stream fixed: the checks and conversions are done once, when the call is
-    made, for loops that repeat it (a decode step per layer)."""
+    """pa_decode_attention, or pa_decode_attention_shared_prefix when prefix_table is given, or
+    pa_decode_attention_append when the new tokens (key, value: [S, num_kv_heads, head_dim], rows
+    strided along S; slot_mapping int64 [S]) are given, with every argument but the stream fixed:
+    the checks and conversions are done once, when the call is made, for loops that repeat it (a
+    decode step per layer)."""
 
     def __init__(self, out: torch.Tensor, query: torch.Tensor, cache: KVCache,
                  block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
                  scale: float, partition_size: int = 0, workspace: torch.Tensor | None = None,
                  flags: int = PA_DECODE_DEFAULT, prefix_table: torch.Tensor | None = None,
-                 prefix_len: int = 0):
+                 prefix_len: int = 0, key: torch.Tensor | None = None,
+                 value: torch.Tensor | None = None, slot_mapping: torch.Tensor | None = None):
         S, Hq, D = query.shape
         assert out.shape == query.shape and out.dtype == query.dtype and out.is_contiguous()
         assert query.stride(2) == 1 and query.stride(1) == D  # rows contiguous, strided along S
@@ -245,8 +252,22 @@ class DecodeCall:
                 ctypes.byref(cache.struct()), _ptr(block_tables), block_tables.shape[1],
                 _ptr(context_lens), S, Hq, int(max_context_len), float(scale))
         tail = (int(partition_size), _ptr(workspace), ws_bytes, int(flags))
-        self._keep = (out, query, cache, block_tables, context_lens, workspace, prefix_table)
-        if prefix_table is None:
+        self._keep = (out, query, cache, block_tables, context_lens, workspace, prefix_table, key,
+                      value, slot_mapping)
+        if key is not None:
+            assert value is not None and slot_mapping is not None
+            assert key.dtype == query.dtype and value.dtype == query.dtype
+            assert key.shape[0] == S and value.shape[0] == S and slot_mapping.shape[0] == S
+            for t in (key, value):
+                assert t.stride(-1) == 1 and t[0].is_contiguous()
+            assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
+            if prefix_table is not None:
+                assert prefix_table.dtype == torch.int32 and prefix_table.is_contiguous()
+            self._fn = lib().pa_decode_attention_append
+            self._args = head[:5] + (_ptr(key), _ptr(value), key.stride(0) if S else 0,
+                                     value.stride(0) if S else 0, _ptr(slot_mapping)) + head[5:] + \
+                (_ptr(prefix_table), int(prefix_len) if prefix_table is not None else 0) + tail
+        elif prefix_table is None:
             self._fn = lib().pa_decode_attention
             self._args = head + tail
         else:
@@ -267,6 +288,21 @@ def pa_decode_attention(out: torch.Tensor, query: torch.Tensor, cache: KVCache,
     block_tables int32 [S, max_blocks_per_seq]; context_lens int32 [S]."""
     DecodeCall(out, query, cache, block_tables, context_lens, max_context_len, scale,
                partition_size, workspace, flags)(stream)
+
+
+def pa_decode_attention_append(out: torch.Tensor, query: torch.Tensor, cache: KVCache,
+                               key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
+                               block_tables: torch.Tensor, context_lens: torch.Tensor,
+                               max_context_len: int, scale: float,
+                               prefix_table: torch.Tensor | None = None, prefix_len: int = 0,
+                               partition_size: int = 0, workspace: torch.Tensor | None = None,
+                               flags: int = PA_DECODE_DEFAULT, stream=None) -> None:
+    """pa_reshape_and_cache of each sequence's new token (key, value [S, num_kv_heads, head_dim] in
+    the query dtype, slot_mapping int64 [S]: the slot of position context_lens[s] - 1) followed by
+    the decode (plain, or shared-prefix when prefix_table is given), in one call."""
+    DecodeCall(out, query, cache, block_tables, context_lens, max_context_len, scale,
+               partition_size, workspace, flags, prefix_table, prefix_len, key, value,
+               slot_mapping)(stream)
 
 
 def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,

@@ -53,6 +53,7 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
+#define PA_LDS __attribute__((address_space(3)))  // LDS pointers
 constexpr int kMaxScanSeqs = 4096;  // persistent grid: sequences whose item prefix fits in LDS
 // The shared-prefix instantiation also holds the prefix groups' block stages in LDS; its scan
 // arrays are halved so that three workgroups still fit on a compute unit.
@@ -581,15 +582,272 @@ template <class QT, int D>
 __device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D> &st, float vscale,
                                           int slot, int rs, int rhq, bool rvalid);
 
+// A 4-, 8- or 16-byte LDS read.
+template <class T>
+__device__ __forceinline__ T lds_load(const PA_LDS char *p) {
+  if constexpr (sizeof(T) == 16) return __builtin_bit_cast(T, *(const PA_LDS u32x4_t *)p);
+  else if constexpr (sizeof(T) == 8) return __builtin_bit_cast(T, *(const PA_LDS u32x2_t *)p);
+  else return __builtin_bit_cast(T, *(const PA_LDS uint32_t *)p);
+}
+
+// The appended token of sequence s for KV head h (fused append): lane l holds elements 2 l and
+// 2 l + 1 of its K and V rows (two 16-bit values in one word; zeros past D / 2), and every lane the
+// token's slot.
+struct NewToken {
+  uint32_t k, v;
+  int64_t slot;
+};
+
+// The token is copied from memory straight into this wavefront's part of LDS when the item
+// starts (buffer loads with the LDS destination: no register holds it while the blocks stream)
+// and read back once the ring is done, long after it has landed.
+struct NewTokenStage {
+  uint32_t k[64], v[64], slot[64];
+};
+
+__device__ __forceinline__ PA_LDS NewTokenStage *new_token_stage() {
+  __shared__ __attribute__((aligned(16))) NewTokenStage stage[kWaves];
+  return (PA_LDS NewTokenStage *)&stage[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
+}
+
+template <int D>
+__device__ __forceinline__ void stage_new_token(const DecodeArgs &a, int s, int h) {
+  const int lane = threadIdx.x & 63;
+  PA_LDS NewTokenStage *st = new_token_stage();
+  const size_t e = (size_t)h * D;
+  const auto rk = tile_rsrc(reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.append_k) +
+                                                           (size_t)s * a.append_k_stride + e),
+                            2 * D);
+  const auto rv = tile_rsrc(reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.append_v) +
+                                                           (size_t)s * a.append_v_stride + e),
+                            2 * D);
+  const auto rs = tile_rsrc(reinterpret_cast<const char *>(a.append_slots + s), 8);
+  // lanes past the row (D = 64) or past the slot's two words read zeros through the bounds
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (PA_LDS void *)st->k, 4, 4 * lane, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (PA_LDS void *)st->v, 4, 4 * lane, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (PA_LDS void *)st->slot, 4, 4 * lane, 0, 0, 0);
+}
+
+__device__ __forceinline__ NewToken read_new_token() {
+  const int lane = threadIdx.x & 63;
+  const PA_LDS NewTokenStage *st = new_token_stage();
+  NewToken t;
+  t.k = st->k[lane];
+  t.v = st->v[lane];
+  t.slot = (int64_t)(((uint64_t)st->slot[1] << 32) | st->slot[0]);
+  return t;
+}
+
+// A new token's pair of 16-bit input values in the cache's encoding, as stored by
+// reshape_and_cache: a bit copy for 16-bit caches; for fp8, E4M3FN(float(x) / scale) of each, the
+// two bytes in the low half.
+template <class CT, class QT>
+__device__ __forceinline__ uint32_t encode_pair(uint32_t w, float scale) {
+  if constexpr (std::is_same<CT, fp8_t>::value) {
+    auto widen = [](uint32_t b) {
+      if constexpr (std::is_same<QT, bf16_t>::value) return bf16_bits_to_f32((uint16_t)b);
+      else return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+    };
+    const uint32_t lo = f32_to_e4m3(__fdiv_rn(widen(w & 0xffffu), scale));
+    const uint32_t hi = f32_to_e4m3(__fdiv_rn(widen(w >> 16), scale));
+    return lo | (hi << 8);
+  } else {
+    return w;
+  }
+}
+
+// Where the fused append reads and writes the pools: the fields it needs, loaded after the ring.
+struct AppendPools {
+  char *k_pool, *v_pool;
+  int num_blocks, block_size, num_kv_heads;
+};
+
+// The encoded new token into its slot of both pools, as reshape_and_cache writes it: lane l the
+// elements 2 l and 2 l + 1 (adjacent in a K vector; two V^T rows).  Bit copies of the encoded
+// width, never value conversions.
+template <class CT, int D>
+__device__ __forceinline__ void store_new_token(const AppendPools &c, int64_t slot, int h,
+                                                uint32_t kenc, uint32_t venc) {
+  const int lane = threadIdx.x & 63;
+  const int B = c.block_size;
+  if (2 * lane >= D || slot < 0 || slot >= (int64_t)c.num_blocks * B) return;
+  using Lt = Layout<CT::bytes>;
+  using U = typename std::conditional<CT::bytes == 1, uint8_t, uint16_t>::type;
+  constexpr int kBits = 8 * CT::bytes;
+  const int64_t blk = slot / B;
+  const int off = (int)(slot % B);
+  const size_t tile = Lt::tile(blk, h, c.num_kv_heads, D, B);
+  const int i0 = 2 * lane;
+  U *kp = reinterpret_cast<U *>(c.k_pool) + tile;
+  U *vp = reinterpret_cast<U *>(c.v_pool) + tile;
+  if constexpr (CT::bytes == 1) *reinterpret_cast<uint16_t *>(kp + Lt::k_off(off, i0, B)) = (uint16_t)kenc;
+  else *reinterpret_cast<uint32_t *>(kp + Lt::k_off(off, i0, B)) = kenc;
+  vp[Lt::v_off(off, i0, B)] = (U)venc;
+  vp[Lt::v_off(off, i0 + 1, B)] = (U)(venc >> kBits);
+}
+
+// Position `off` of block b, KV head h, as the pool holds it, in the word layout of the new token
+// (lane l: elements 2 l and 2 l + 1 of K and of V).
+template <class CT, int D>
+__device__ __forceinline__ void pool_position(const AppendPools &c, int b, int off, int h,
+                                              uint32_t &kw, uint32_t &vw) {
+  const int lane = threadIdx.x & 63;
+  const int B = c.block_size;
+  using Lt = Layout<CT::bytes>;
+  using U = typename std::conditional<CT::bytes == 1, uint8_t, uint16_t>::type;
+  constexpr int kBits = 8 * CT::bytes;
+  kw = vw = 0u;
+  if (2 * lane >= D) return;
+  const size_t tile = Lt::tile(b, h, c.num_kv_heads, D, B);
+  const int i0 = 2 * lane;
+  const U *kp = reinterpret_cast<const U *>(c.k_pool) + tile;
+  const U *vp = reinterpret_cast<const U *>(c.v_pool) + tile;
+  if constexpr (CT::bytes == 1) kw = *reinterpret_cast<const uint16_t *>(kp + Lt::k_off(off, i0, B));
+  else kw = *reinterpret_cast<const uint32_t *>(kp + Lt::k_off(off, i0, B));
+  vw = (uint32_t)vp[Lt::v_off(off, i0, B)] | ((uint32_t)vp[Lt::v_off(off, i0 + 1, B)] << kBits);
+}
+
+// The kernel's argument struct read through the kernel-argument segment, its address passed
+// through an empty asm: the compiler cannot reuse values loaded before, so the fields the append
+// needs after the ring are loaded then, instead of being held in scalar registers while the
+// blocks stream.  The struct is the decode kernel's only parameter, at offset 0.
+__device__ __forceinline__ const __attribute__((address_space(4))) DecodeArgs *fresh_args() {
+  auto *p = (const __attribute__((address_space(4))) DecodeArgs *)
+      __builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
+// 16-bit floats (f16, or bf16 when kBF) to fp32.
+template <bool kBF>
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  if constexpr (kBF) return __uint_as_float(w << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)w);
+}
+template <bool kBF>
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  if constexpr (kBF) return __uint_as_float(w & 0xffff0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// The fused append's tail, after the ring: position L - 1 is the new token when its slot is in the
+// pool (written there now), else what the pool holds at L - 1 (no write).  The position's K and V,
+// in the cache's encoding, go back to this wavefront's LDS stage, from which each lane reads the
+// dims of its query operand (score) and of its accumulator rows (value); the position enters the
+// online softmax in fp32 vector arithmetic, with the ring's lazy-rescaling rule.
+template <class CT, class QT, int D>
+__device__ __forceinline__ void append_tail(int rs, int h, int L, float kscale, RowState<D> &st) {
+  constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
+  constexpr bool kBF = std::is_same<CT, bf16_t>::value;  // fp8 caches compute in f16
+  const int lane = threadIdx.x & 63, grp = lane >> 4;
+  // The compiler does not order the copies into LDS before these reads: wait for them here, where
+  // the ring has drained (an item without blocks waits for the copies themselves).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const auto *ka = fresh_args();
+  AppendPools c;
+  c.k_pool = static_cast<char *>(ka->cache.k_pool);
+  c.v_pool = static_cast<char *>(ka->cache.v_pool);
+  c.num_blocks = ka->cache.num_blocks;
+  c.block_size = ka->cache.block_size;
+  c.num_kv_heads = ka->cache.num_kv_heads;
+  PA_LDS NewTokenStage *sg = new_token_stage();
+  const NewToken nt = read_new_token();
+  const int64_t aslot =
+      (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(nt.slot >> 32)) << 32) |
+                (uint32_t)__builtin_amdgcn_readfirstlane((int)nt.slot));
+  const bool write = aslot >= 0 && aslot < (int64_t)c.num_blocks * c.block_size;
+  uint32_t kenc = 0u, venc = 0u;
+  bool have = write;
+  if (write) {
+    float ks = 1.0f, vs = 1.0f;
+    if constexpr (kFP8) {
+      using cfloat = const __attribute__((address_space(4))) float;
+      ks = ((cfloat *)(uintptr_t)ka->cache.k_scale)[h];
+      vs = ((cfloat *)(uintptr_t)ka->cache.v_scale)[h];
+    }
+    kenc = encode_pair<CT, QT>(nt.k, ks);
+    venc = encode_pair<CT, QT>(nt.v, vs);
+  } else if (L > 0) {
+    const int p = L - 1, B = c.block_size;
+    const int32_t *table = ka->block_tables + (size_t)rs * ka->max_blocks_per_seq;
+    const int b = __builtin_amdgcn_readfirstlane(table[p / B]);
+    have = (unsigned)b < (unsigned)c.num_blocks;  // an entry outside the pool: left out
+    if (have) pool_position<CT, D>(c, b, p % B, h, kenc, venc);
+  }
+  if (have && L > 0) {
+    // the encoded position, dims contiguous (lanes past D / 2 hold zeros)
+    if constexpr (kFP8) {
+      ((PA_LDS uint16_t *)sg->k)[lane] = (uint16_t)kenc;
+      ((PA_LDS uint16_t *)sg->v)[lane] = (uint16_t)venc;
+    } else {
+      sg->k[lane] = kenc;
+      sg->v[lane] = venc;
+    }
+    const PA_LDS char *kb = (const PA_LDS char *)sg->k;
+    const PA_LDS char *vb = (const PA_LDS char *)sg->v;
+    // score: this lane's 8 query dims per product kk, summed over the four lane groups
+    float z = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const int d0 = kFP8 ? 16 * grp + 64 * (kk >> 1) + 8 * (kk & 1) : 8 * grp + 32 * kk;
+      uint4 kv;
+      if constexpr (kFP8) {
+        const uint2 b8 = lds_load<uint2>(kb + d0);
+        const uint2 a = e4m3x4_to_f16x4(b8.x), b = e4m3x4_to_f16x4(b8.y);
+        kv = make_uint4(a.x, a.y, b.x, b.y);
+      } else {
+        kv = lds_load<uint4>(kb + 2 * d0);
+      }
+      const uint4 q = st.qop[kk];
+      z += half_lo<kBF>(q.x) * half_lo<kBF>(kv.x) + half_hi<kBF>(q.x) * half_hi<kBF>(kv.x);
+      z += half_lo<kBF>(q.y) * half_lo<kBF>(kv.y) + half_hi<kBF>(q.y) * half_hi<kBF>(kv.y);
+      z += half_lo<kBF>(q.z) * half_lo<kBF>(kv.z) + half_hi<kBF>(q.z) * half_hi<kBF>(kv.z);
+      z += half_lo<kBF>(q.w) * half_lo<kBF>(kv.w) + half_hi<kBF>(q.w) * half_hi<kBF>(kv.w);
+    }
+    z += __shfl_xor(z, 16);
+    z += __shfl_xor(z, 32);
+    z *= kscale;
+    const bool grow = z > st.m + kSlack;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
+      const float mn = grow ? z : st.m;
+      const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+      st.l *= alpha;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) st.acc[t] *= alpha;
+      st.m = mn;
+    }
+    const float pr = __builtin_amdgcn_exp2f(z - st.m);
+    if (grp == 0) st.l += pr;  // the row's sum adds the four lane groups at the end
+    // value: accumulator rows 16 t + 4 grp + i of this lane's column
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      const int d = 16 * t + 4 * grp;
+      uint2 vv;
+      if constexpr (kFP8) vv = e4m3x4_to_f16x4(lds_load<uint32_t>(vb + d));
+      else vv = lds_load<uint2>(vb + 2 * d);
+      st.acc[t][0] += pr * half_lo<kBF>(vv.x);
+      st.acc[t][1] += pr * half_hi<kBF>(vv.x);
+      st.acc[t][2] += pr * half_lo<kBF>(vv.y);
+      st.acc[t][3] += pr * half_hi<kBF>(vv.y);
+    }
+  }
+  if (write) store_new_token<CT, D>(c, aslot, h, kenc, venc);
+}
+
 template <class CT, class QT, int D, bool kNT, int kB>
 __device__ __forceinline__ void rows_core(const DecodeArgs &a, const int32_t *table, int h,
                                           int jb0, int jb1, int end, int slot, int rs, int rhq,
-                                          bool rvalid, int lim, int tbl0, int &settle) {
+                                          bool rvalid, int lim, int tbl0, int &settle, bool append,
+                                          int L) {
   RowState<D> st;
   load_query<CT, D>(a, rs, rhq, rvalid, st);
+  if (append) stage_new_token<D>(a, rs, h);
   float kscale, vscale;
   head_scales<CT>(a, h, kscale, vscale);
   stream_blocks<CT, D, kNT, kB>(a, table, h, jb0, jb1, tbl0, lim, end, kscale, st);
+  // Fused append (wave-uniform): position L - 1 was left out of the ring; it is the new token when
+  // the slot is in the pool, else what the pool holds there (no write).
+  if (append) append_tail<CT, QT, D>(rs, h, L, kscale, st);
   // Wait here, where the ring has nothing left in flight, for every load this item started that its
   // blocks may not have consumed (the query and table entries of an item without blocks) and for
   // `settle` (the next item's table entries, fetched before this item started): later, behind this
@@ -646,9 +904,9 @@ __device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D>
 // table row, against the g query heads of s (columns 0 .. g - 1 of the products).  Wavefronts of
 // one workgroup run their items independently, so one wavefront's item prologue (query, table
 // fetch, first loads) and epilogue overlap the other wavefronts' block streams.
-template <class CT, class QT, int D, bool kNT, int kB>
+template <class CT, class QT, int D, bool kNT, int kB, bool kApp>
 __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int h_in, int jb0_in,
-                                          int jb1_in, int end_in, int slot_in, int tbl0,
+                                          int jb1_in, int end_in, int slot_in, int L_in, int tbl0,
                                           int &settle) {
   // The item is the same for the whole wavefront: keep its fields (and so the tile addresses) in
   // scalar registers.
@@ -663,8 +921,13 @@ __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int h_i
   const bool rvalid = col < g;
   const int rhq = h * g + (rvalid ? col : 0);
   const int32_t *table = a.block_tables + (size_t)s * a.max_blocks_per_seq;
-  rows_core<CT, QT, D, kNT, kB>(a, table, h, jb0, jb1, end, slot, s, rhq, rvalid, end, tbl0,
-                                settle);
+  // Fused append: the row's last item (the one whose positions end at the context length) writes
+  // the new token and takes position L - 1 from registers; its pool walk stops before it.
+  const int L = __builtin_amdgcn_readfirstlane(L_in);
+  const bool append = kApp && end == L;
+  const int e = append && L > 0 ? L - 1 : end;
+  rows_core<CT, QT, D, kNT, kB>(a, table, h, jb0, append ? min(jb1, (e + kBlock - 1) / kBlock) : jb1,
+                                e, slot, s, rhq, rvalid, e, tbl0, settle, append, L);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -685,7 +948,6 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
-#define PA_LDS __attribute__((address_space(3)))  // LDS pointers
 
 template <class CT, int D>
 struct PrefixStages {
@@ -728,12 +990,6 @@ __device__ __forceinline__ void stage_block(const DecodeArgs &a, int bid, bool o
   }
 }
 
-template <class T>
-__device__ __forceinline__ T lds_load(const PA_LDS char *p) {
-  if constexpr (sizeof(T) == 16) return __builtin_bit_cast(T, *(const PA_LDS u32x4_t *)p);
-  else if constexpr (sizeof(T) == 8) return __builtin_bit_cast(T, *(const PA_LDS u32x2_t *)p);
-  else return __builtin_bit_cast(T, *(const PA_LDS uint32_t *)p);
-}
 
 // The K and V tiles of stage I into registers, at the offsets load_block reads them at.
 template <class CT, int D, int I, int N>
@@ -861,13 +1117,13 @@ __device__ __forceinline__ int seq_items(const DecodeArgs &a, int L) {
 // Sequence item `part` of sequence s (context length L), KV head h: its blocks [jb0, jb1), the end
 // of its positions and its workspace slot (-1: the output itself).
 struct SeqItem {
-  int s, h, jb0, jb1, end, slot;
+  int s, h, jb0, jb1, end, slot, L;
 };
 
 __device__ __forceinline__ SeqItem sequence_item(const DecodeArgs &a, int s, int L, int part,
                                                  int h) {
   const int PT = a.partition_size;
-  SeqItem it{s, h, 0, 0, 0, -1};
+  SeqItem it{s, h, 0, 0, 0, -1, L};
   int start, end;
   if (a.prefix_len > 0) {
     partition_range(a.prefix_len, L, PT, part, &start, &end);
@@ -884,11 +1140,11 @@ __device__ __forceinline__ SeqItem sequence_item(const DecodeArgs &a, int s, int
   return it;
 }
 
-template <class CT, class QT, int D, int kB>
+template <class CT, class QT, int D, int kB, bool kApp>
 __device__ __forceinline__ void run_sequence_item(const DecodeArgs &a, const SeqItem &it, int tbl0,
                                                   int &settle) {
-  wave_item<CT, QT, D, PA_DECODE_NT, kB>(a, it.s, it.h, it.jb0, it.jb1, it.end, it.slot, tbl0,
-                                         settle);
+  wave_item<CT, QT, D, PA_DECODE_NT, kB, kApp>(a, it.s, it.h, it.jb0, it.jb1, it.end, it.slot, it.L,
+                                         tbl0, settle);
 }
 
 // Lane i's table entry of the first ring chunk of a sequence item (the table entries of its first
@@ -913,7 +1169,7 @@ __device__ __forceinline__ int item_table_entries(const DecodeArgs &a, const Seq
 // each block through LDS (prefix_group), so a block crosses from L2 once per group instead of once
 // per 16 rows.  The sequence items go first to the wavefronts of workgroups without prefix work, so
 // the streaming of private blocks from HBM starts at once beside the prefix groups.
-template <class CT, class QT, int D, bool kPre, int kB>
+template <class CT, class QT, int D, bool kPre, int kB, bool kApp>
 __global__ __launch_bounds__(256)
 #if PA_DECODE_OCC
 __attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
@@ -935,7 +1191,7 @@ void decode_mfma_kernel(DecodeArgs a) {
     if (part < n) {
       const SeqItem it = sequence_item(a, (int)s, L, part, h);
       int none = 0;
-      run_sequence_item<CT, QT, D, kB>(a, it, item_table_entries<kB>(a, it), none);
+      run_sequence_item<CT, QT, D, kB, kApp>(a, it, item_table_entries<kB>(a, it), none);
     }
     return;
   }
@@ -1026,7 +1282,7 @@ void decode_mfma_kernel(DecodeArgs a) {
         next = item_of(f + GW);
         tbl_next = item_table_entries<kB>(a, next);
       }
-      run_sequence_item<CT, QT, D, kB>(a, it, tbl, tbl_next);
+      run_sequence_item<CT, QT, D, kB, kApp>(a, it, tbl, tbl_next);
       it = next;
       tbl = tbl_next;
     }
@@ -1368,7 +1624,7 @@ hipError_t launch_prefill_d(const DecodeArgs &a, hipStream_t s) {
 
 // Workgroups of one instantiation that fit on the device at once (occupancy x compute units),
 // looked up once per device.
-template <class CT, class QT, int D, bool kPre, int kB>
+template <class CT, class QT, int D, bool kPre, int kB, bool kApp>
 int resident_groups() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];
@@ -1379,7 +1635,7 @@ int resident_groups() {
     if (c > 0) return c;
   }
   int occ = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_mfma_kernel<CT, QT, D, kPre, kB>, 256,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_mfma_kernel<CT, QT, D, kPre, kB, kApp>, 256,
                                                    0) !=
           hipSuccess || occ < 1)
     occ = 1;
@@ -1391,18 +1647,25 @@ int resident_groups() {
   return n;
 }
 
-template <class CT, class QT, int D, bool kPre, int kB>
-hipError_t launch_ddp(DecodeArgs a, hipStream_t s) {
+template <class CT, class QT, int D, bool kPre, int kB, bool kApp>
+hipError_t launch_ddpa(DecodeArgs a, hipStream_t s) {
   const int64_t items = (int64_t)a.num_partitions * a.cache.num_kv_heads * a.num_seqs;
   const int64_t direct = (items + kWaves - 1) / kWaves;  // one wavefront per item
   a.persistent = a.num_seqs <= (kPre ? kMaxScanSeqsPrefix : kMaxScanSeqs);
   dim3 grid((unsigned)direct);
   if (a.persistent) {
-    const int resident = resident_groups<CT, QT, D, kPre, kB>();
+    const int resident = resident_groups<CT, QT, D, kPre, kB, kApp>();
     grid = dim3((unsigned)(PA_SPREAD ? resident : std::min<int64_t>(direct, resident)));
   }
-  decode_mfma_kernel<CT, QT, D, kPre, kB><<<grid, dim3(256), 0, s>>>(a);
+  decode_mfma_kernel<CT, QT, D, kPre, kB, kApp><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
+}
+
+// The fused append is an instantiation of its own, so that the plain decode keeps its registers.
+template <class CT, class QT, int D, bool kPre, int kB>
+hipError_t launch_ddp(const DecodeArgs &a, hipStream_t s) {
+  return a.append_slots ? launch_ddpa<CT, QT, D, kPre, kB, true>(a, s)
+                        : launch_ddpa<CT, QT, D, kPre, kB, false>(a, s);
 }
 
 template <class CT, class QT, int D>

@@ -178,13 +178,24 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 
 namespace {
 
-// Validation and dispatch shared by the plain and the shared-prefix decode.
+// The appended tokens of pa_decode_attention_append: one row per sequence.
+struct AppendIn {
+  const void *key;
+  const void *value;
+  int64_t key_stride;
+  int64_t value_stride;
+  const int64_t *slots;
+};
+
+// Validation and dispatch shared by the plain and the shared-prefix decode, with or without the
+// fused append.
 pa_status decode_common(const char *who, void *out, const void *query, int32_t q_dtype,
                         int64_t q_stride, const pa_cache *cache, const int32_t *block_tables,
                         int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
                         int32_t num_q_heads, int32_t max_context_len, float scale,
                         const int32_t *prefix_table, int32_t prefix_len, int32_t partition_size,
-                        void *workspace, size_t workspace_bytes, uint32_t flags, void *stream) {
+                        void *workspace, size_t workspace_bytes, uint32_t flags, void *stream,
+                        const AppendIn *app = nullptr) {
   pa_status st = check_cache(cache, who);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_seqs > 65535)
@@ -218,6 +229,18 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
   if (q_stride < (int64_t)num_q_heads * D)
     return fail(PA_ERR_SHAPE, "%s: q_stride %lld below a row", who, (long long)q_stride);
   if ((flags & ~PA_DECODE_FORCE_VALU) != 0) return fail(PA_ERR_SHAPE, "%s: unknown flags", who);
+  AppendIn ap{};
+  if (app) {
+    ap = *app;
+    if (!ap.key || !ap.value || !ap.slots)
+      return fail(PA_ERR_NULL, "%s: NULL key/value/slot_mapping", who);
+    const int64_t row = (int64_t)H * D;
+    if (ap.key_stride == 0) ap.key_stride = row;
+    if (ap.value_stride == 0) ap.value_stride = row;
+    if (ap.key_stride < row || ap.value_stride < row)
+      return fail(PA_ERR_SHAPE, "%s: key/value strides %lld/%lld below a row of %lld elements",
+                  who, (long long)ap.key_stride, (long long)ap.value_stride, (long long)row);
+  }
   const int B = cache->block_size;
   if (B != PA_BLOCK_SIZE) {
     if (prefix_len > 0)
@@ -287,6 +310,32 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool use_mfma = use_prefix || (!force_valu && pa::decode_mfma_supports(a));
+  if (app) {
+    // The matrix-core kernel writes the new tokens itself (16-bit rows read in pairs); elsewhere
+    // reshape_and_cache runs first, with the same result.
+    const bool fused = use_mfma && (reinterpret_cast<uintptr_t>(ap.key) & 3u) == 0 &&
+                       (reinterpret_cast<uintptr_t>(ap.value) & 3u) == 0 &&
+                       ap.key_stride % 2 == 0 && ap.value_stride % 2 == 0;
+    if (fused) {
+      a.append_slots = ap.slots;
+      a.append_k = ap.key;
+      a.append_v = ap.value;
+      a.append_k_stride = ap.key_stride;
+      a.append_v_stride = ap.value_stride;
+    } else {
+      pa::ReshapeArgs r;
+      r.cache = a.cache;
+      r.key = ap.key;
+      r.value = ap.value;
+      r.in_dtype = q_dtype;
+      r.key_stride = ap.key_stride;
+      r.value_stride = ap.value_stride;
+      r.slots = ap.slots;
+      r.num_tokens = num_seqs;
+      const hipError_t er = pa::launch_reshape_and_cache(r, s);
+      if (er != hipSuccess) return launch_status(er, who);
+    }
+  }
   if (!use_mfma && B != PA_BLOCK_SIZE)
     return fail(PA_ERR_UNSUPPORTED,
                 "%s: block_size %d runs on the matrix cores only (f16 or bf16 cache with the same "
@@ -328,6 +377,23 @@ pa_status pa_decode_attention_shared_prefix(void *out, const void *query, int32_
                        block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
                        max_context_len, scale, prefix_table, prefix_len, partition_size,
                        workspace, workspace_bytes, flags, stream);
+}
+
+pa_status pa_decode_attention_append(void *out, const void *query, int32_t q_dtype,
+                                     int64_t q_stride, const pa_cache *cache, const void *key,
+                                     const void *value, int64_t key_stride, int64_t value_stride,
+                                     const int64_t *slot_mapping, const int32_t *block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                     int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t max_context_len, float scale,
+                                     const int32_t *prefix_table, int32_t prefix_len,
+                                     int32_t partition_size, void *workspace,
+                                     size_t workspace_bytes, uint32_t flags, void *stream) {
+  const AppendIn app{key, value, key_stride, value_stride, slot_mapping};
+  return decode_common("pa_decode_attention_append", out, query, q_dtype, q_stride, cache,
+                       block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                       max_context_len, scale, prefix_table, prefix_len, partition_size,
+                       workspace, workspace_bytes, flags, stream, &app);
 }
 
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

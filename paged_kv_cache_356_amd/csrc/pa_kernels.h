@@ -66,6 +66,15 @@ struct DecodeArgs {
   float *part_out;          // NULL when num_partitions == 1
   float *part_ml;
   int32_t persistent;       // grid mode of the matrix-core kernel (set by its launcher)
+  // Fused append (NULL append_slots: none): sequence s's new token, rows append_k/v + s * stride
+  // (num_kv_heads * head_dim elements of q_dtype), goes to slot append_slots[s] (< 0: none), which
+  // is the slot of position context_lens[s] - 1; the wavefront of each (s, KV head) row's last
+  // item writes that head's part and takes the position from registers instead of the pool.
+  const int64_t *append_slots;
+  const void *append_k;
+  const void *append_v;
+  int64_t append_k_stride;
+  int64_t append_v_stride;
   // Shared-prefix decode (0 / NULL for the plain decode): every sequence's first prefix_len
   // positions live in the blocks prefix_table[0 .. prefix_len / 16).  Workspace partition slots
   // 0 .. prefix_chunks - 1 of every row hold the prefix's chunks, the suffix partitions follow.

@@ -138,6 +138,7 @@ class DecodeBatch:
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
         # use the shared-prefix decode where the workload has a prefix (run_step / run_layer)
         self.use_prefix = self.prefix_len > 0
+        self.fused = False  # run_layer: one pa_decode_attention_append call instead of two
 
     # ------------------------------------------------------------------ the step
     # The library calls of a step are prepared once per (set, layer) and replayed (api.*Call): the
@@ -172,27 +173,36 @@ class DecodeBatch:
 
     def run_layer(self, set_index: int, layer: int, flags: int = api.PA_DECODE_DEFAULT,
                   stream=None, copy: bool = True, reshape: bool = True):
+        """One layer of the step: copy-on-write clones, then the cache write and the attention,
+        as two calls (reshape_and_cache, decode) or, when `fused` is set, as one
+        (pa_decode_attention_append)."""
         if copy:
             self.copy(set_index, [layer], stream)
+        if self.fused and reshape:
+            self.decode(set_index, layer, flags=flags, stream=stream, append=True)
+            return
         if reshape:
             self.reshape(set_index, layer, stream)
         self.decode(set_index, layer, flags=flags, stream=stream)
 
     def decode(self, set_index: int, layer: int, flags: int = api.PA_DECODE_DEFAULT, stream=None,
-               out: torch.Tensor | None = None):
-        """The step's attention call for one layer (shared-prefix decode when use_prefix)."""
+               out: torch.Tensor | None = None, append: bool = False):
+        """The step's attention call for one layer (shared-prefix decode when use_prefix); with
+        `append`, the fused call that also writes the step's new token."""
         st = self.sets[set_index]
 
         def make(o):
             pre = dict(prefix_table=self.prefix_tables[set_index], prefix_len=self.prefix_len) \
                 if self.use_prefix else {}
+            if append:
+                pre.update(key=st.new_k[layer], value=st.new_v[layer], slot_mapping=st.d_slots)
             return api.DecodeCall(o, st.q[layer], self.caches[layer], st.d_tables, st.d_ctx,
                                   self.max_context_len, self.w.scale, self.partition_size,
                                   self.workspace, flags, **pre)
         if out is not None:
             make(out)(stream)
             return
-        key = ("decode", set_index, layer, flags, self.use_prefix, self.partition_size)
+        key = ("decode", set_index, layer, flags, self.use_prefix, self.partition_size, append)
         self._call(key, lambda: make(st.out[layer]))(stream)
 
     # ------------------------------------------------------------------ accounting

@@ -592,6 +592,101 @@ def test_rejections_do_not_launch():
     assert e.value.status == -4
 
 
+# --------------------------------------------------------------------------- fused append
+FUSED = ["tiny_f32", "f16_batch32", "bf16_32k_batch8", "f16_shared_prefix_batch256",
+         "fp8_28layer_batch512"]
+
+
+def _reduced(name, **kw):
+    w = wl.WORKLOADS[name]
+    if name in SMALL:
+        w = w.replace(**SMALL[name])
+    return w.replace(**kw) if kw else w
+
+
+@pytest.mark.parametrize("name", FUSED)
+@pytest.mark.parametrize("flags", [api.PA_DECODE_DEFAULT, api.PA_DECODE_FORCE_VALU])
+def test_fused_append_matches_oracle(name, flags):
+    """pa_decode_attention_append (the new token written and attended to in one call) against the
+    oracle: attention within the dtype's tolerance, every pool byte equal to the oracle's replay of
+    reshape_and_cache; the vector-ALU configurations run the two calls behind the same entry."""
+    w = _reduced(name)
+    _say(f"fused append, {name} reduced, flags {flags}")
+    pad = _pad_block(w)
+    b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON,
+                    lengths=SMALL_LENGTHS.get(name), partition_size=0 if name != "bf16_32k_batch8" else 512)
+    b.fused = True
+    ob = OracleBatch(b, pad, pool_fill=POISON)
+    ob.metadata_matches(b)
+    for l in b.layers:
+        _check_batch(b, ob, l, TOL[w.cache_dtype], flags=flags)
+        kp, vp, _, _ = ob.pools[(l, 0)]
+        dk, dv = device_pool_bytes(b.caches[l])
+        assert np.array_equal(dk, kp.view(np.uint8)) and np.array_equal(dv, vp.view(np.uint8))
+
+
+@pytest.mark.parametrize("B", [8, 16, 32])
+@pytest.mark.parametrize("name", ["f16_batch32", "fp8_28layer_batch512", "f16_shared_prefix_batch256"])
+def test_fused_append_equals_two_calls(name, B):
+    """The fused call leaves the pools byte for byte as reshape_and_cache + decode do, and its
+    attention agrees with theirs within the tolerance (only the new position's place in the
+    summation differs); repeating the call gives the same bits (the write is idempotent)."""
+    if B != 16 and name == "f16_shared_prefix_batch256":
+        pytest.skip("the shared prefix runs on 16-position blocks")
+    kw = {}
+    if B != 16:
+        kw = dict(block_size=B, num_blocks=SMALL[name]["num_blocks"] * 16 // B)
+    w = _reduced(name, **kw)
+    _say(f"fused vs two calls, {name} reduced, block size {B}")
+    runs = []
+    for fused in (False, True):
+        b = DecodeBatch(w, pad_block=0, lengths=SMALL_LENGTHS[name])
+        b.fused = fused
+        b.run_step(0)
+        torch.cuda.synchronize()
+        runs.append((b, [b.sets[0].out[l].clone() for l in b.layers],
+                     [device_pool_bytes(b.caches[l]) for l in b.layers]))
+    (b2, outs2, pools2), (b1, outs1, pools1) = runs[0], runs[1]
+    for l, (o1, o2, p1, p2) in enumerate(zip(outs1, outs2, pools1, pools2)):
+        assert np.array_equal(p1[0], p2[0]) and np.array_equal(p1[1], p2[1])
+        err = float((o1.double() - o2.double()).abs().max())
+        _say(f"  layer {l}: fused vs two calls max-abs {err:.3e}")
+        assert err <= TOL[w.cache_dtype]
+    # again: the same token to the same slot, the same result
+    b1.run_step(0)
+    torch.cuda.synchronize()
+    for l, o1 in zip(b1.layers, outs1):
+        assert torch.equal(b1.sets[0].out[l], o1)
+
+
+def test_fused_append_skips_slots_outside_the_pool():
+    """A negative slot (padding) or one past the pool is not written, and position L - 1 is then
+    what the pool holds, as with reshape_and_cache + decode; an empty context with a slot is written
+    and attends to nothing."""
+    for name in ("f16_batch32", "fp8_28layer_batch512"):
+        w = _reduced(name, num_layers=1)
+        lengths = [int(x) for x in SMALL_LENGTHS[name]]
+        _say(f"fused append, slots outside the pool, {name}")
+        outs, pools = [], []
+        for fused in (False, True):
+            b = DecodeBatch(w, pad_block=0, lengths=lengths)
+            st = b.sets[0]
+            slots = st.d_slots.clone()
+            slots[0] = -1
+            slots[2] = w.num_blocks * w.block_size + 5
+            st.d_slots.copy_(slots)
+            b.fused = fused
+            b.run_step(0)
+            torch.cuda.synchronize()
+            outs.append(st.out[0].clone())
+            pools.append(device_pool_bytes(b.caches[0]))
+        assert np.array_equal(pools[0][0], pools[1][0]) and np.array_equal(pools[0][1], pools[1][1])
+        err = float((outs[0].double() - outs[1].double()).abs().max())
+        _say(f"  max-abs {err:.3e}")
+        assert torch.isfinite(outs[1].float()).all()
+        assert err <= TOL[w.cache_dtype]
+
+
 # --------------------------------------------------------------------------- full sizes, sampled
 @pytest.mark.parametrize("name", ["f16_batch32", "bf16_32k_batch8", "f16_shared_prefix_batch256", "fp8_28layer_batch512"])
 def test_full_size_workloads_sampled(name):
