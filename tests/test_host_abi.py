@@ -77,6 +77,30 @@ def test_decode_validation(kw, status):
     assert _decode(_cache(), **kw) == status
 
 
+def _decode_append(cache, **kw):
+    a = dict(out=64, query=128, q_dtype=api.PA_F16, q_stride=0, key=2048, value=4096, ks=0, vs=0,
+             slots=8192, tables=256, max_blocks=4, ctx=512, S=2, Hq=28, max_ctx=64, scale=0.1,
+             prefix_table=None, prefix_len=0, ps=0, ws=None, ws_bytes=0, flags=0)
+    a.update(kw)
+    return api.lib().pa_decode_attention_append(
+        a["out"], a["query"], a["q_dtype"], a["q_stride"], ctypes.byref(cache), a["key"],
+        a["value"], a["ks"], a["vs"], a["slots"], a["tables"], a["max_blocks"], a["ctx"], a["S"],
+        a["Hq"], a["max_ctx"], a["scale"], a["prefix_table"], a["prefix_len"], a["ps"], a["ws"],
+        a["ws_bytes"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(key=None), -1), (dict(value=None), -1), (dict(slots=None), -1),
+    (dict(ks=100), -2), (dict(vs=511), -2), (dict(out=None), -1), (dict(Hq=30), -2),
+    (dict(prefix_len=64), -1), (dict(prefix_len=8, prefix_table=1024), -2),
+    (dict(max_ctx=4096, ps=16), -4), (dict(S=0, key=None), 0),
+])
+def test_decode_append_validation(kw, status):
+    """pa_decode_attention_append checks its own arguments (the new rows, their strides, the slots)
+    and the decode's, before any launch; no call reaches the GPU here."""
+    assert _decode_append(_cache(), **kw) == status
+
+
 def _decode_prefix(cache, prefix_table=1024, prefix_len=64, **kw):
     a = dict(out=64, query=128, q_dtype=api.PA_F16, q_stride=0, tables=256, max_blocks=8, ctx=512,
              S=2, Hq=28, max_ctx=128, scale=0.1, ps=0, ws=None, ws_bytes=0, flags=0)
