@@ -1252,8 +1252,19 @@ void decode_mfma_kernel(DecodeArgs a) {
   // wavefronts running at the same time cover the H tiles (b, 0..H-1) of the same blocks, next to
   // each other in the pool.
   const int busy = min(n_pre, G);  // workgroups 0 .. busy - 1 have prefix work
-  const int rank = blockIdx.x < busy ? (G - busy) * kWaves + w * busy + blockIdx.x
-                                     : w * (G - busy) + (blockIdx.x - busy);
+  // Workgroup b runs on compute unit b mod N (N = num_cus) when the grid is a whole number of
+  // workgroups per unit.  With prefix work on units 0 .. busy - 1 only, the other units would hold
+  // one more item workgroup each; that last one (b >= G - N + busy) is ranked after all other item
+  // workgroups, so the wavefronts left without an item are there, and every unit streams about the
+  // same number of items.
+  const int N = a.num_cus;
+  const bool spread = kPre && busy > 0 && N > 0 && busy < N && G % N == 0 && G >= 2 * N;
+  const int nA = spread ? G - N : G - busy;  // item workgroups ranked first
+  const int cb = G - N + busy;               // first of the late item workgroups (spread)
+  const int b = blockIdx.x;
+  const int rank = b < busy ? (G - busy) * kWaves + w * busy + b
+                   : (!spread || b < cb) ? w * nA + (b - busy)
+                                         : nA * kWaves + w * (N - busy) + (b - cb);
   const int total = __builtin_amdgcn_readfirstlane(prefix[S]) * H;
   const int GW = G * kWaves;
   auto item_of = [&](int f) {
@@ -1624,6 +1635,22 @@ hipError_t launch_prefill_d(const DecodeArgs &a, hipStream_t s) {
 
 // Workgroups of one instantiation that fit on the device at once (occupancy x compute units),
 // looked up once per device.
+// Compute units of the current device, looked up once per device.
+int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  const int c = cache[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return 0;
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 template <class CT, class QT, int D, bool kPre, int kB, bool kApp>
 int resident_groups() {
   constexpr int kMaxDev = 64;
@@ -1653,6 +1680,7 @@ hipError_t launch_ddpa(DecodeArgs a, hipStream_t s) {
   const int64_t direct = (items + kWaves - 1) / kWaves;  // one wavefront per item
   a.persistent = a.num_seqs <= (kPre ? kMaxScanSeqsPrefix : kMaxScanSeqs);
   dim3 grid((unsigned)direct);
+  a.num_cus = device_cus();
   if (a.persistent) {
     const int resident = resident_groups<CT, QT, D, kPre, kB, kApp>();
     grid = dim3((unsigned)(PA_SPREAD ? resident : std::min<int64_t>(direct, resident)));
