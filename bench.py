@@ -235,6 +235,9 @@ def main() -> int:
                          "16 / block size)")
     ap.add_argument("--no-prefix", action="store_true",
                     help="shared-prefix workload: use the plain decode instead of the shared-prefix one")
+    ap.add_argument("--contiguous", action="store_true",
+                    help="control: physical blocks handed out in pool order, so that every "
+                         "sequence's blocks are adjacent (the indirection-overhead baseline)")
     ap.add_argument("--fused", action="store_true",
                     help="step through pa_decode_attention_append (the cache write inside the "
                          "decode kernel) instead of reshape_and_cache + decode")
@@ -293,6 +296,7 @@ def main() -> int:
     batch = DecodeBatch(w, device="cuda", num_sets=sets,
                         keep_values=not args.no_cpu_baseline,
                         partition_size=None if args.partition < 0 else args.partition,
+                        contiguous=args.contiguous,
                         keep_layers=[0])
     batch.use_prefix = batch.use_prefix and not args.no_prefix
     torch.cuda.synchronize()
@@ -410,6 +414,8 @@ def main() -> int:
                 w.num_seqs, w.num_kv_heads, batch.max_context_len),
             "kernel": "valu" if args.valu else "default",
             "shared_prefix_decode": bool(batch.use_prefix),
+            "block_placement": "contiguous (free list in pool order)" if args.contiguous else
+                               "scattered (seeded permutation of the pool)",
             "step_calls": "copy_blocks (when the step clones) + per layer " +
                           ("pa_decode_attention_append (cache write fused into the decode kernel)"
                            if fused else "pa_reshape_and_cache + decode"),
@@ -436,6 +442,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(w, args.partition < 0 and not args.valu and not fused and
+                                        not args.contiguous and
                                         not args.num_blocks and not args.no_prefix and
                                         args.block_size == 16),
             "traffic_note": "HBM bytes per call from rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE "

@@ -60,13 +60,16 @@ def value_seed(w: wl.Workload, set_index: int, layer: int) -> int:
 class DecodeBatch:
     def __init__(self, w: wl.Workload, device="cuda", num_sets: int = 1, layers=None,
                  pad_block: int = 0, keep_values: bool = False, pool_fill: int = 0,
-                 lengths=None, partition_size: int | None = None, keep_layers=None):
+                 lengths=None, partition_size: int | None = None, keep_layers=None,
+                 contiguous: bool = False):
         self.w = w
         self.device = device
         H, D, S = w.num_kv_heads, w.head_dim, w.num_seqs
         self.lengths = wl.context_lengths(w) if lengths is None else np.asarray(lengths, np.int32)
         assert len(self.lengths) == S
-        self.free_order = wl.free_order(w)
+        # contiguous: the free list in pool order, so that each sequence's blocks sit next to each
+        # other (the control against which the block table's indirection is measured)
+        self.free_order = np.arange(w.num_blocks, dtype=np.int32) if contiguous else wl.free_order(w)
         self.layers = list(range(w.num_layers)) if layers is None else list(layers)
         self.partition_size = w.partition_size if partition_size is None else partition_size
         B = w.block_size
