@@ -11,7 +11,10 @@ Prints ONE JSON line:
   roofline     for pa_decode_attention (the dominant call: split-K kernel + partition reduce):
                algorithmic bytes per call (unique physical KV slots + tables + lengths + Q + out)
                / its mean duration from HIP events on the launch stream, against 8 TB/s;
-  cpu_baseline the CPU oracle (fp64) timed on the host's cores on a bounded sample of set 0.
+  cpu_baseline the CPU oracle (fp64) timed on the host's cores on a bounded sample of set 0;
+  decode_call_us, reshape_call_us, copy_call_us
+               p10 / p50 / p90 / mean of single calls (an event between consecutive eager calls),
+               and seqs_per_s_per_layer_calls = S / (decode + reshape + copy / layers), medians.
 
 Timing loops rotate between `--sets` independent batches of the workload placed in the same pool
 (distinct blocks and values), so each step reads KV that the 256 MB MALL and the L2s do not already
@@ -377,8 +380,33 @@ def main() -> int:
         run_decodes()
     ev1.record(stream)
     torch.cuda.synchronize()
-    gc.enable()
     dec_mean_s = ev0.elapsed_time(ev1) / 1e3 / (reps * n_dec)
+
+    # Per-call distributions (eager calls, an event recorded between consecutive calls on the
+    # launch stream): the decode call, and the step's other calls, reshape_and_cache (per layer)
+    # and copy_blocks (all layers at once, when the step clones).
+    lay = list(batch.layers)
+
+    def per_call(fn, n: int):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        evs[0].record(stream)
+        for k in range(n):
+            fn(k)
+            evs[k + 1].record(stream)
+        torch.cuda.synchronize()
+        us = np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(n)])
+        return {"p10": round(float(np.percentile(us, 10)), 3), "p50": round(float(np.median(us)), 3),
+                "p90": round(float(np.percentile(us, 90)), 3), "mean": round(float(us.mean()), 3),
+                "calls": n}
+
+    n_pc = max(20, min(200, sets * len(lay) * 4))
+    dec_pc = per_call(lambda k: batch.decode(k % sets, lay[(k // sets) % len(lay)], flags=flags,
+                                             append=fused), n_pc)
+    resh_pc = None if fused else per_call(
+        lambda k: batch.reshape(k % sets, lay[(k // sets) % len(lay)]), n_pc)
+    copy_pc = per_call(lambda k: batch.copy(k % sets), max(20, sets * 4)) \
+        if batch.sets[0].pairs.shape[0] else None
+    gc.enable()
     ms_per_step = elapsed * 1e3 / args.steps
     layers = len(batch.layers)
     kv_logical = batch.kv_bytes_per_layer(unique=False)
@@ -434,6 +462,12 @@ def main() -> int:
         "hbm_fraction_of_step": round(value / HBM_PEAK_GBPS, 4),
         "seqs_per_s_per_layer": round(seqs_per_s_layer, 1),
         "decode_call_us_mean": round(dec_mean_s * 1e6, 3),
+        "decode_call_us": dec_pc,
+        "reshape_call_us": resh_pc,
+        "copy_call_us": copy_pc,
+        "seqs_per_s_per_layer_calls": round(w.num_seqs / (
+            (dec_pc["p50"] + (resh_pc["p50"] if resh_pc else 0.0) +
+             (copy_pc["p50"] / len(lay) if copy_pc else 0.0)) * 1e-6), 1),
         "decode_calls_timed": reps * n_dec,
         "roofline": {
             "bound": "hbm",
