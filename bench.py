@@ -13,7 +13,7 @@ Prints ONE JSON line:
                / its mean duration from HIP events on the launch stream, against 8 TB/s;
   cpu_baseline the CPU oracle (fp64) timed on the host's cores on a bounded sample of set 0;
   decode_call_us, reshape_call_us, copy_call_us
-               p10 / p50 / p90 / mean of single calls (an event between consecutive eager calls),
+               p10 / p50 / p90 / mean per call over 20 batches of back-to-back eager calls,
                and seqs_per_s_per_layer_calls = S / (decode + reshape + copy / layers), medians.
 
 Timing loops rotate between `--sets` independent batches of the workload placed in the same pool
@@ -382,29 +382,32 @@ def main() -> int:
     torch.cuda.synchronize()
     dec_mean_s = ev0.elapsed_time(ev1) / 1e3 / (reps * n_dec)
 
-    # Per-call distributions (eager calls, an event recorded between consecutive calls on the
-    # launch stream): the decode call, and the step's other calls, reshape_and_cache (per layer)
-    # and copy_blocks (all layers at once, when the step clones).
+    # Per-call distributions: 20 repetitions of a batch of back-to-back eager calls, an event on
+    # the launch stream around each batch (an event between single calls would add its own
+    # ~2 us); p10 / p50 / p90 over the batches' per-call times.  The decode call, and the step's
+    # other calls: reshape_and_cache (per layer) and copy_blocks (all layers at once, when the
+    # step clones).
     lay = list(batch.layers)
 
-    def per_call(fn, n: int):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    def per_call(fn, n: int, reps: int = 20):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         evs[0].record(stream)
-        for k in range(n):
-            fn(k)
-            evs[k + 1].record(stream)
+        for r in range(reps):
+            for k in range(n):
+                fn(r * n + k)
+            evs[r + 1].record(stream)
         torch.cuda.synchronize()
-        us = np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(n)])
+        us = np.array([evs[r].elapsed_time(evs[r + 1]) * 1e3 / n for r in range(reps)])
         return {"p10": round(float(np.percentile(us, 10)), 3), "p50": round(float(np.median(us)), 3),
                 "p90": round(float(np.percentile(us, 90)), 3), "mean": round(float(us.mean()), 3),
-                "calls": n}
+                "calls": n * reps}
 
-    n_pc = max(20, min(200, sets * len(lay) * 4))
+    n_pc = max(4, min(16, sets * len(lay)))
     dec_pc = per_call(lambda k: batch.decode(k % sets, lay[(k // sets) % len(lay)], flags=flags,
                                              append=fused), n_pc)
     resh_pc = None if fused else per_call(
         lambda k: batch.reshape(k % sets, lay[(k // sets) % len(lay)]), n_pc)
-    copy_pc = per_call(lambda k: batch.copy(k % sets), max(20, sets * 4)) \
+    copy_pc = per_call(lambda k: batch.copy(k % sets), max(4, sets)) \
         if batch.sets[0].pairs.shape[0] else None
     gc.enable()
     ms_per_step = elapsed * 1e3 / args.steps

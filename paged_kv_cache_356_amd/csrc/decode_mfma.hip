@@ -831,7 +831,48 @@ __device__ __forceinline__ void append_tail(int rs, int h, int L, float kscale, 
       st.acc[t][3] += pr * half_hi<kBF>(vv.y);
     }
   }
-  if (write) store_new_token<CT, D>(c, aslot, h, kenc, venc);
+  // the persistent grid leaves the writes to write_token_rows
+  if (write && !ka->persistent) store_new_token<CT, D>(c, aslot, h, kenc, venc);
+}
+
+// Fused append on the persistent grid: the new tokens' writes into the pools, row (s, h) by the
+// wavefront of rank GW - 1 - (s H + h) mod GW once its items are done.  The high ranks are those
+// with fewest or no items, so the stores (2- and 4-byte pieces over ~80 cache lines per row) stay
+// off the item streams; the rows' last items attend to the token from their own copy, and their
+// walk never reads its position, so nothing waits for these writes.
+template <class CT, class QT, int D>
+__device__ __forceinline__ void write_token_rows(const DecodeArgs &a, int rank, int GW) {
+  const int lane = threadIdx.x & 63;
+  const int H = a.cache.num_kv_heads, rows = a.num_seqs * H;
+  AppendPools c;
+  c.k_pool = static_cast<char *>(a.cache.k_pool);
+  c.v_pool = static_cast<char *>(a.cache.v_pool);
+  c.num_blocks = a.cache.num_blocks;
+  c.block_size = a.cache.block_size;
+  c.num_kv_heads = H;
+  for (int r = GW - 1 - rank; r < rows; r += GW) {
+    const int s = r / H, h = r - (r / H) * H;
+    const int64_t slot = a.append_slots[s];
+    const int64_t sl =
+        (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(slot >> 32)) << 32) |
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)slot));
+    if (sl < 0 || sl >= (int64_t)c.num_blocks * c.block_size) continue;
+    uint32_t kw = 0u, vw = 0u;
+    if (2 * lane < D) {
+      const size_t e = (size_t)h * D + 2 * lane;
+      kw = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(a.append_k) +
+                                               (size_t)s * a.append_k_stride + e);
+      vw = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(a.append_v) +
+                                               (size_t)s * a.append_v_stride + e);
+    }
+    float ks = 1.0f, vs = 1.0f;
+    if constexpr (std::is_same<CT, fp8_t>::value) {
+      using cfloat = const __attribute__((address_space(4))) float;
+      ks = ((cfloat *)(uintptr_t)a.cache.k_scale)[h];
+      vs = ((cfloat *)(uintptr_t)a.cache.v_scale)[h];
+    }
+    store_new_token<CT, D>(c, sl, h, encode_pair<CT, QT>(kw, ks), encode_pair<CT, QT>(vw, vs));
+  }
 }
 
 template <class CT, class QT, int D, bool kNT, int kB>
@@ -1298,6 +1339,7 @@ void decode_mfma_kernel(DecodeArgs a) {
       tbl = tbl_next;
     }
   }
+  if constexpr (kApp) write_token_rows<CT, QT, D>(a, rank, GW);
 }
 
 // ---------------------------------------------------------------------------------------------
