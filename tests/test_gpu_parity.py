@@ -223,12 +223,26 @@ def test_many_sequences_direct_grid():
     w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=S, num_blocks=16384)
     _say(f"direct grid, {S} sequences")
     pad = _pad_block(w)
-    b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON, lengths=lengths,
-                    partition_size=16)
-    ob = OracleBatch(b, pad, pool_fill=POISON)
     sel_s = np.r_[0:8, S - 8:S]
     sel = (np.repeat(sel_s, w.num_q_heads), np.tile(np.arange(w.num_q_heads), len(sel_s)))
-    _check_batch(b, ob, 0, TOL["f16"], sel=sel)
+    for fused in (False, True):  # the fused append stores the token from the last item's tail here
+        _say(f"  fused {fused}")
+        b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON, lengths=lengths,
+                        partition_size=16)
+        b.fused = fused
+        ob = OracleBatch(b, pad, pool_fill=POISON)
+        _check_batch(b, ob, 0, TOL["f16"], sel=sel, owners=set(sel_s.tolist()))
+        kp, vp, _, _ = ob.pools[(0, 0)]
+        dk, dv = device_pool_bytes(b.caches[0])
+        span = w.num_kv_heads * 16 * w.head_dim * 2
+        for s_ in sel_s:  # the sampled sequences' blocks, the new tokens' slots included
+            for j in range(math.ceil(int(lengths[s_]) / 16)):
+                blk = int(ob.sets[0]["tables"][s_, j])
+                sl = slice(blk * span, (blk + 1) * span)
+                assert np.array_equal(dk[sl], kp.view(np.uint8)[sl])
+                assert np.array_equal(dv[sl], vp.view(np.uint8)[sl])
+        del b, ob
+        torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("B", [8, 32])
