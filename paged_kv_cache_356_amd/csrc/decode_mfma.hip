@@ -76,6 +76,12 @@ constexpr int kPrefixTiles = PA_PREFIX_TILES;
 #ifndef PA_SPREAD
 #define PA_SPREAD 0
 #endif
+// The plain decode's fused-append instantiation runs at two wavefronts per SIMD (256 registers,
+// no spills): measured level with the plain decode on the 32K batch and faster than three per
+// SIMD on the others; the shared-prefix one keeps three (its grid needs three workgroups per CU).
+#ifndef PA_APPEND_OCC
+#define PA_APPEND_OCC 2
+#endif
 #ifndef PA_DECODE_OCC
 #define PA_DECODE_OCC 3  // at least this many wavefronts per SIMD (caps registers at 168)
 #endif
@@ -1213,7 +1219,7 @@ __device__ __forceinline__ int item_table_entries(const DecodeArgs &a, const Seq
 template <class CT, class QT, int D, bool kPre, int kB, bool kApp>
 __global__ __launch_bounds__(256)
 #if PA_DECODE_OCC
-__attribute__((amdgpu_waves_per_eu(PA_DECODE_OCC)))
+__attribute__((amdgpu_waves_per_eu(kApp && !kPre ? PA_APPEND_OCC : PA_DECODE_OCC)))
 #endif
 void decode_mfma_kernel(DecodeArgs a) {
   static_assert(!kPre || kB == 16, "the shared prefix runs on 16-position blocks");
