@@ -92,9 +92,13 @@ def cpu_baseline(batch, budget_s: float) -> dict:
 
     w = batch.w
     L = batch.lengths.astype(np.int64)
-    # estimate: ~4 ns per (position, head-dim, query head) on one core for de-page + dot products
+    # estimate: ~4 ns per (position, head-dim, query head) on one core for de-page + dot products,
+    # plus rebuilding the sequence's history in the oracle's pool first (one thread): ~1.2 us per
+    # element for the fp8 encoder (an exact search over the codes), ~5 ns for bit copies
     threads = oracle.max_threads()
-    per_seq = L * w.num_q_heads * w.head_dim * 4e-9 * 2 / max(threads, 1)
+    enc = 1.2e-6 if w.cache_dtype == "fp8" else 5e-9
+    per_seq = L * w.num_q_heads * w.head_dim * 4e-9 * 2 / max(threads, 1) + \
+        L * 2 * w.num_kv_heads * w.head_dim * enc
     take, acc = [], 0.0
     for s in range(w.num_seqs):
         if take and acc + per_seq[s] > budget_s:
