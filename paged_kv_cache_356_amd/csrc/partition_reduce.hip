@@ -26,6 +26,12 @@ namespace pa {
 namespace {
 
 constexpr int kRowsPerGroup = 4;
+// Split variant: wavefronts per row, and the most rows it is used for.
+#ifndef PA_REDUCE_SPLIT
+#define PA_REDUCE_SPLIT 1
+#endif
+constexpr int kWavesSplit = 4;
+constexpr int kSplitRows = 1024;
 
 // kPer: float4 loads in flight per lane (a sub-chunk of G * kPer partitions).  A few keep the
 // registers low, so that many rows are in flight, for batches of many rows; 32 takes 64
@@ -110,11 +116,92 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void partition_reduce_kernel(De
   }
 }
 
+// Few rows with many partitions: one workgroup per row, its four wavefronts each merging a quarter
+// of the head dims, so that the same bytes are read by four times as many wavefronts.  In a
+// wavefront, lane (group pg, column c) owns float4 column c of the quarter and the partitions
+// pg, pg + 8, ... (up to 8 of them per pass, all loaded before any is used); the eight groups are
+// combined with shuffles at the end.
+template <class QT, int D>
+__global__ __launch_bounds__(256) void partition_reduce_split_kernel(DecodeArgs a) {
+  constexpr int C = D / 4 / kWavesSplit;  // float4 columns per wavefront
+  constexpr int PG = 64 / C;              // partition groups per wavefront
+  constexpr int kPer = 64 / PG;           // partitions per lane in one pass of 64
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row = blockIdx.x;  // s * Hq + hq
+  const int s = row / a.num_q_heads;
+  const int NP = a.num_partitions;
+  const size_t row0 = (size_t)row * NP;
+  const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml) + row0;
+  const float4 *po = reinterpret_cast<const float4 *>(a.part_out) + row0 * (D / 4);
+  const int c = lane % C, pg = lane / C;
+  const int col = w * C + c;  // float4 column of the row
+
+  int Ls = a.context_lens[s];
+  Ls = Ls < 0 ? 0 : (Ls > a.max_context_len ? a.max_context_len : Ls);
+  const int np = row_partitions(a, Ls);
+  if (np <= 1 && a.prefix_len == 0) return;  // finished by the decode kernel
+  const float2 v0 = lane < np ? ml[lane] : make_float2(-INFINITY, 0.0f);
+  float4 x[kPer];
+  auto load_pass = [&](int base, int n) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int q = pg + k * PG;
+      x[k] = q < n ? po[(size_t)(base + q) * (D / 4) + col] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+  };
+  load_pass(0, min(64, np));
+  float M = v0.x;
+  for (int p = lane + 64; p < np; p += 64) M = fmaxf(M, ml[p].x);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float wsum = 0.0f;
+  for (int base = 0; base < np; base += 64) {
+    const int n = min(64, np - base);
+    if (base > 0) load_pass(base, n);
+    const float2 v = base == 0 ? v0 : (lane < n ? ml[base + lane] : make_float2(-INFINITY, 0.0f));
+    const float wl = v.x == -INFINITY ? 0.0f : v.y * __builtin_amdgcn_exp2f(v.x - M);
+    wsum += wl;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const float wq = __shfl(wl, (pg + k * PG) & 63);  // 0 for q >= n
+      acc.x += wq * x[k].x;
+      acc.y += wq * x[k].y;
+      acc.z += wq * x[k].z;
+      acc.w += wq * x[k].w;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o);
+#pragma unroll
+  for (int o = C; o < 64; o <<= 1) {
+    acc.x += __shfl_xor(acc.x, o);
+    acc.y += __shfl_xor(acc.y, o);
+    acc.z += __shfl_xor(acc.z, o);
+    acc.w += __shfl_xor(acc.w, o);
+  }
+  if (pg == 0) {
+    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    auto *out = static_cast<typename QT::raw *>(a.out) + (size_t)row * D + 4 * col;
+    out[0] = from_f32<QT>(acc.x * inv);
+    out[1] = from_f32<QT>(acc.y * inv);
+    out[2] = from_f32<QT>(acc.z * inv);
+    out[3] = from_f32<QT>(acc.w * inv);
+  }
+}
+
 template <class QT>
 hipError_t launch_q(const DecodeArgs &a, hipStream_t s) {
   const int rows = a.num_seqs * a.num_q_heads;
   dim3 grid((rows + kRowsPerGroup - 1) / kRowsPerGroup), block(64 * kRowsPerGroup);
   const bool wide = PA_REDUCE_WIDE && rows <= 2048 && a.num_partitions > 16;
+  if (PA_REDUCE_SPLIT && wide && rows <= kSplitRows) {
+    if (a.cache.head_dim == 64)
+      partition_reduce_split_kernel<QT, 64><<<dim3(rows), dim3(64 * kWavesSplit), 0, s>>>(a);
+    else
+      partition_reduce_split_kernel<QT, 128><<<dim3(rows), dim3(64 * kWavesSplit), 0, s>>>(a);
+    return hipGetLastError();
+  }
   if (a.cache.head_dim == 64) {
     if (wide) partition_reduce_kernel<QT, 64, 16><<<grid, block, 0, s>>>(a);
     else partition_reduce_kernel<QT, 64, 2><<<grid, block, 0, s>>>(a);
