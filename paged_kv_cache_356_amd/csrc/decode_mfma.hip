@@ -858,6 +858,9 @@ __device__ __forceinline__ void write_token_rows(const DecodeArgs &a, int rank, 
   c.num_kv_heads = H;
   for (int r = GW - 1 - rank; r < rows; r += GW) {
     const int s = r / H, h = r - (r / H) * H;
+    // with a shared prefix, a context that does not extend past it takes no write (its position
+    // would lie in the prefix's blocks, which the prefix groups are reading)
+    if (a.prefix_len > 0 && __builtin_amdgcn_readfirstlane(clamp_len(a, s)) <= a.prefix_len) continue;
     const int64_t slot = a.append_slots[s];
     const int64_t sl =
         (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(slot >> 32)) << 32) |

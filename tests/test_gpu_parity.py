@@ -673,6 +673,50 @@ def test_fused_append_equals_two_calls(name, B):
         assert torch.equal(b1.sets[0].out[l], o1)
 
 
+def test_fused_append_shared_prefix_short_context_not_written():
+    """With a shared prefix, a sequence whose context does not extend past the prefix takes no
+    write (its slot would lie in the shared blocks): the pools keep their bytes there and its
+    attention is that of the unchanged pool."""
+    w = _reduced("f16_shared_prefix_batch256", num_layers=1)
+    lengths = SMALL_LENGTHS["f16_shared_prefix_batch256"]
+    _say("fused append, shared prefix, a context inside the prefix")
+    pad = _pad_block(w)
+    b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON, lengths=lengths)
+    st = b.sets[0]
+    ob = OracleBatch(b, pad, pool_fill=POISON)
+    b.copy(0)
+    b.reshape(0, 0)  # every token written as the two-call step does
+    torch.cuda.synchronize()
+    before_k, before_v = device_pool_bytes(b.caches[0])
+    ctx = st.ctx.copy()
+    ctx[1] = 40  # inside the 64-position prefix
+    d_ctx = torch.from_numpy(ctx).cuda()
+    prefix_slot = int(ob.sets[0]["tables"][1, 0]) * w.block_size + 39  # position 39 of the prefix
+    slots = st.d_slots.clone()
+    slots[1] = prefix_slot
+    new_k = st.new_k[0].clone()
+    new_k[1].fill_(7.0)  # a value that would show if it were written
+    new_v = st.new_v[0].clone()
+    new_v[1].fill_(7.0)
+    out = torch.empty_like(st.out[0])
+    api.pa_decode_attention_append(out, st.q[0], b.caches[0], new_k, new_v, slots, st.d_tables,
+                                   d_ctx, b.max_context_len, w.scale, b.prefix_tables[0],
+                                   b.prefix_len, 0, b.workspace)
+    torch.cuda.synchronize()
+    after_k, after_v = device_pool_bytes(b.caches[0])
+    # the other sequences rewrote their own tokens (same bytes); nothing else changed
+    assert np.array_equal(before_k, after_k) and np.array_equal(before_v, after_v)
+    ob.build_pools(b, 0)
+    kp, vp, _, _ = ob.pools[(0, 0)]
+    q = raw(st.q[0]).reshape(w.num_seqs, -1)
+    ref = oracle.decode_attention(q, w.q_dtype, kp, vp, w.cache_dtype, None, None, w.num_blocks,
+                                  w.num_kv_heads, w.head_dim, ob.sets[0]["tables"], ctx,
+                                  w.num_q_heads, w.scale)
+    err = max_abs_err(as_f64(out), ref)
+    _say(f"  max-abs err {err:.3e}")
+    assert err <= TOL["f16"]
+
+
 def test_fused_append_skips_slots_outside_the_pool():
     """A negative slot (padding) or one past the pool is not written, and position L - 1 is then
     what the pool holds, as with reshape_and_cache + decode; an empty context with a slot is written
