@@ -251,7 +251,8 @@ pa_status pa_decode_attention_shared_prefix(void *out, const void *query, int32_
  * positions of each (sequence, KV head) writes that head's part of the token and takes the token
  * from registers instead of reading it back, so one kernel does both; the attention equals that of
  * the two calls within floating-point rounding (the new position is summed last).  Configurations
- * of the vector-ALU kernel, and key/value rows that are not 4-byte aligned, run the two calls.
+ * of the vector-ALU kernel, and key/value rows that are not 4-byte aligned, run the two calls;
+ * with a shared prefix, rows that are not 4-byte aligned (or odd strides) are PA_ERR_SHAPE.
  */
 pa_status pa_decode_attention_append(void *out, const void *query, int32_t q_dtype,
                                      int64_t q_stride, const pa_cache *cache, const void *key,

@@ -285,6 +285,15 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
     t.prefix_len = prefix_len;
     use_prefix = !force_valu && pa::decode_mfma_supports_prefix(t);
   }
+  // With a shared prefix only the kernel's own write keeps a context that ends inside the prefix
+  // from being written (reshape_and_cache would write every slot): it needs 16-bit rows it can
+  // read in pairs.
+  if (app && use_prefix &&
+      ((reinterpret_cast<uintptr_t>(ap.key) & 3u) != 0 ||
+       (reinterpret_cast<uintptr_t>(ap.value) & 3u) != 0 || ap.key_stride % 2 != 0 ||
+       ap.value_stride % 2 != 0))
+    return fail(PA_ERR_SHAPE, "%s: with a shared prefix, key/value rows must be 4-byte aligned "
+                "with even strides", who);
   const int32_t pt = resolve_partition(num_seqs, H, use_prefix ? max_len - prefix_len : max_len,
                                        partition_size);
   const int64_t slots = decode_slots(max_len, pt, use_prefix ? prefix_len : 0);

@@ -94,6 +94,8 @@ def _decode_append(cache, **kw):
     (dict(ks=100), -2), (dict(vs=511), -2), (dict(out=None), -1), (dict(Hq=30), -2),
     (dict(prefix_len=64), -1), (dict(prefix_len=8, prefix_table=1024), -2),
     (dict(max_ctx=4096, ps=16), -4), (dict(S=0, key=None), 0),
+    (dict(prefix_table=1024, prefix_len=64, key=2050), -2),
+    (dict(prefix_table=1024, prefix_len=64, ks=513), -2),
 ])
 def test_decode_append_validation(kw, status):
     """pa_decode_attention_append checks its own arguments (the new rows, their strides, the slots)
