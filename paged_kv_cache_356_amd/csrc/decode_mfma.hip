@@ -934,14 +934,35 @@ __device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D>
     }
   } else {
     const size_t row = orow * a.num_partitions + slot;
+    if constexpr (std::is_same<QT, f16_t>::value) {
+      // f16 queries: the partial output in fp16 (half the workspace traffic; it is a normalised
+      // average of V rows, rounded once more before the merge), stored lane-contiguous: the
+      // quads of head dims 16 nt + 4 grp .. + 3 at quad grp * NT + nt of the row, so each lane
+      // writes NT * 8 contiguous bytes and a row's four lane groups one contiguous span
+      typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+      uint32_t hw[2 * NT];  // round to nearest even
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float4 v;
-      v.x = st.acc[nt][0] * inv;
-      v.y = st.acc[nt][1] * inv;
-      v.z = st.acc[nt][2] * inv;
-      v.w = st.acc[nt][3] * inv;
-      *reinterpret_cast<float4 *>(a.part_out + row * D + 16 * nt + 4 * grp) = v;
+      for (int nt = 0; nt < NT; ++nt) {
+        hw[2 * nt] = __builtin_bit_cast(
+            uint32_t, h2_t{(_Float16)(st.acc[nt][0] * inv), (_Float16)(st.acc[nt][1] * inv)});
+        hw[2 * nt + 1] = __builtin_bit_cast(
+            uint32_t, h2_t{(_Float16)(st.acc[nt][2] * inv), (_Float16)(st.acc[nt][3] * inv)});
+      }
+      uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<_Float16 *>(a.part_out) + row * D +
+                                             (size_t)grp * NT * 4);
+#pragma unroll
+      for (int k = 0; k < NT / 2; ++k)
+        dst[k] = make_uint4(hw[4 * k], hw[4 * k + 1], hw[4 * k + 2], hw[4 * k + 3]);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float4 v;
+        v.x = st.acc[nt][0] * inv;
+        v.y = st.acc[nt][1] * inv;
+        v.z = st.acc[nt][2] * inv;
+        v.w = st.acc[nt][3] * inv;
+        *reinterpret_cast<float4 *>(a.part_out + row * D + 16 * nt + 4 * grp) = v;
+      }
     }
     if (grp == 0) {
       a.part_ml[row * 2] = st.m;

@@ -19,6 +19,8 @@
 // row's partition count is known: the outputs do not wait for the maximum, so a row with few
 // partitions makes two round trips to memory (context length, then its partials), not three.
 // Slots past the row's partitions hold whatever earlier calls left there and are never read.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -26,6 +28,22 @@ namespace pa {
 namespace {
 
 constexpr int kRowsPerGroup = 4;
+
+// Head dims 4 c .. 4 c + 3 of partial output p of a row (its first quad at q0), fp32 or fp16
+// (kHalf).  fp16 partials are stored lane-contiguous by the decode kernel: the quad of dims
+// 16 nt + 4 grp .. sits at quad grp * (D / 16) + nt.
+template <bool kHalf, int D>
+__device__ __forceinline__ float4 load_part4(const float *part_out, size_t q0, int p, int c) {
+  constexpr int C = D / 4;
+  if constexpr (kHalf) {
+    const int q = (c & 3) * (D / 16) + (c >> 2);
+    const uint2 u = reinterpret_cast<const uint2 *>(part_out)[q0 + (size_t)p * C + q];
+    const _Float16 *h = reinterpret_cast<const _Float16 *>(&u);
+    return make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+  } else {
+    return reinterpret_cast<const float4 *>(part_out)[q0 + (size_t)p * C + c];
+  }
+}
 // Split variant: wavefronts per row, and the most rows it is used for.
 #ifndef PA_REDUCE_SPLIT
 #define PA_REDUCE_SPLIT 1
@@ -42,7 +60,7 @@ constexpr int kSplitRows = 1024;
 #ifndef PA_REDUCE_PER
 #define PA_REDUCE_PER 4
 #endif
-template <class QT, int D, int kPer>
+template <class QT, int D, int kPer, bool kHalf>
 __global__ __launch_bounds__(64 * kRowsPerGroup) void partition_reduce_kernel(DecodeArgs a) {
   constexpr int C = D / 4;   // float4 columns of a partial output
   constexpr int G = 64 / C;  // partitions handled side by side in a wavefront
@@ -54,7 +72,7 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void partition_reduce_kernel(De
   const int NP = a.num_partitions;
   const size_t row0 = (size_t)row * NP;
   const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml) + row0;
-  const float4 *po = reinterpret_cast<const float4 *>(a.part_out) + row0 * C;
+  const size_t po0 = row0 * C;  // float4 index of the row's first partial
   const int c = lane % C, grp = lane / C;
 
   int Ls = a.context_lens[s];
@@ -67,7 +85,8 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void partition_reduce_kernel(De
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int q = sub + grp + k * G;
-      x[k] = q < n ? po[(size_t)(base + q) * C + c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      x[k] = q < n ? load_part4<kHalf, D>(a.part_out, po0, base + q, c)
+                   : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
   };
   load_sub(0, 0, min(64, np));
@@ -121,7 +140,7 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void partition_reduce_kernel(De
 // wavefront, lane (group pg, column c) owns float4 column c of the quarter and the partitions
 // pg, pg + 8, ... (up to 8 of them per pass, all loaded before any is used); the eight groups are
 // combined with shuffles at the end.
-template <class QT, int D>
+template <class QT, int D, bool kHalf>
 __global__ __launch_bounds__(256) void partition_reduce_split_kernel(DecodeArgs a) {
   constexpr int C = D / 4 / kWavesSplit;  // float4 columns per wavefront
   constexpr int PG = 64 / C;              // partition groups per wavefront
@@ -132,7 +151,7 @@ __global__ __launch_bounds__(256) void partition_reduce_split_kernel(DecodeArgs 
   const int NP = a.num_partitions;
   const size_t row0 = (size_t)row * NP;
   const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml) + row0;
-  const float4 *po = reinterpret_cast<const float4 *>(a.part_out) + row0 * (D / 4);
+  const size_t po0 = row0 * (D / 4);  // float4 index of the row's first partial
   const int c = lane % C, pg = lane / C;
   const int col = w * C + c;  // float4 column of the row
 
@@ -146,7 +165,8 @@ __global__ __launch_bounds__(256) void partition_reduce_split_kernel(DecodeArgs 
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int q = pg + k * PG;
-      x[k] = q < n ? po[(size_t)(base + q) * (D / 4) + col] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      x[k] = q < n ? load_part4<kHalf, D>(a.part_out, po0, base + q, col)
+                   : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
   };
   load_pass(0, min(64, np));
@@ -190,26 +210,34 @@ __global__ __launch_bounds__(256) void partition_reduce_split_kernel(DecodeArgs 
   }
 }
 
-template <class QT>
-hipError_t launch_q(const DecodeArgs &a, hipStream_t s) {
+template <class QT, bool kHalf>
+hipError_t launch_qh(const DecodeArgs &a, hipStream_t s) {
   const int rows = a.num_seqs * a.num_q_heads;
   dim3 grid((rows + kRowsPerGroup - 1) / kRowsPerGroup), block(64 * kRowsPerGroup);
   const bool wide = PA_REDUCE_WIDE && rows <= 2048 && a.num_partitions > 16;
   if (PA_REDUCE_SPLIT && wide && rows <= kSplitRows) {
     if (a.cache.head_dim == 64)
-      partition_reduce_split_kernel<QT, 64><<<dim3(rows), dim3(64 * kWavesSplit), 0, s>>>(a);
+      partition_reduce_split_kernel<QT, 64, kHalf><<<dim3(rows), dim3(64 * kWavesSplit), 0, s>>>(a);
     else
-      partition_reduce_split_kernel<QT, 128><<<dim3(rows), dim3(64 * kWavesSplit), 0, s>>>(a);
+      partition_reduce_split_kernel<QT, 128, kHalf><<<dim3(rows), dim3(64 * kWavesSplit), 0, s>>>(a);
     return hipGetLastError();
   }
   if (a.cache.head_dim == 64) {
-    if (wide) partition_reduce_kernel<QT, 64, 16><<<grid, block, 0, s>>>(a);
-    else partition_reduce_kernel<QT, 64, 2><<<grid, block, 0, s>>>(a);
+    if (wide) partition_reduce_kernel<QT, 64, 16, kHalf><<<grid, block, 0, s>>>(a);
+    else partition_reduce_kernel<QT, 64, 2, kHalf><<<grid, block, 0, s>>>(a);
   } else {
-    if (wide) partition_reduce_kernel<QT, 128, 32><<<grid, block, 0, s>>>(a);
-    else partition_reduce_kernel<QT, 128, PA_REDUCE_PER><<<grid, block, 0, s>>>(a);
+    if (wide) partition_reduce_kernel<QT, 128, 32, kHalf><<<grid, block, 0, s>>>(a);
+    else partition_reduce_kernel<QT, 128, PA_REDUCE_PER, kHalf><<<grid, block, 0, s>>>(a);
   }
   return hipGetLastError();
+}
+
+// fp16 partials come only from the matrix-core kernel with f16 queries (part_f16).
+template <class QT>
+hipError_t launch_q(const DecodeArgs &a, hipStream_t s) {
+  if constexpr (std::is_same<QT, f16_t>::value)
+    if (a.part_f16) return launch_qh<QT, true>(a, s);
+  return launch_qh<QT, false>(a, s);
 }
 
 }  // namespace
