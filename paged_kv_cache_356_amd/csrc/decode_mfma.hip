@@ -569,6 +569,16 @@ __device__ __forceinline__ void head_scales(const DecodeArgs &a, int h, float &k
   }
 }
 
+// Scale of a row's partial outputs in the workspace.  With an fp8 cache the f16-query partials
+// stay in units of the cache codes (|x| <= 448, so inside fp16's range whatever the head's scale),
+// and the partition reduce applies the head's v_scale; otherwise they carry the full scale.
+template <class CT, class QT>
+__device__ __forceinline__ float partial_vscale(float vscale) {
+  if constexpr (std::is_same<CT, fp8_t>::value && std::is_same<QT, f16_t>::value)
+    return kFp8Unscale;
+  return vscale;
+}
+
 __device__ __forceinline__ int clamp_len(const DecodeArgs &a, int s) {
   int L = a.context_lens[s];
   return L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
@@ -906,13 +916,14 @@ __device__ __forceinline__ void rows_core(const DecodeArgs &a, const int32_t *ta
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk)
     asm volatile("" : "+v"(st.qop[kk].x), "+v"(st.qop[kk].y), "+v"(st.qop[kk].z), "+v"(st.qop[kk].w));
-  emit_rows<QT, D>(a, st, vscale, slot, rs, rhq, rvalid);
+  emit_rows<QT, D>(a, st, vscale, partial_vscale<CT, QT>(vscale), slot, rs, rhq, rvalid);
 }
 
-// A finished row state to the output (slot < 0) or to workspace partition `slot`.
+// A finished row state to the output (slot < 0, scaled by vscale) or to workspace partition
+// `slot` (scaled by pvscale).
 template <class QT, int D>
 __device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D> &st, float vscale,
-                                          int slot, int rs, int rhq, bool rvalid) {
+                                          float pvscale, int slot, int rs, int rhq, bool rvalid) {
   constexpr int NT = D / 16;
   const int Hq = a.num_q_heads;
   const int grp = (threadIdx.x & 63) >> 4;
@@ -922,7 +933,7 @@ __device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D>
   l += __shfl_xor(l, 32);
   if (!rvalid) return;
   const size_t orow = (size_t)rs * Hq + rhq;
-  const float inv = l > 0.0f ? vscale / l : 0.0f;  // no position at all: zero
+  const float inv = l > 0.0f ? (slot < 0 ? vscale : pvscale) / l : 0.0f;  // no position: zero
   if (slot < 0) {
     auto *out = static_cast<typename QT::raw *>(a.out) + orow * D;
 #pragma unroll
@@ -1174,7 +1185,9 @@ __device__ __forceinline__ void prefix_group(const DecodeArgs &a, const int *len
     if (k0 + decltype(I)::value < nk) step(I, k0 + decltype(I)::value);
   });
 #pragma unroll
-  for (int j = 0; j < kT; ++j) emit_rows<QT, D>(a, st[j], vscale, slot, rs[j], rhq[j], rvalid[j]);
+  for (int j = 0; j < kT; ++j)
+    emit_rows<QT, D>(a, st[j], vscale, partial_vscale<CT, QT>(vscale), slot, rs[j], rhq[j],
+                     rvalid[j]);
 }
 
 // Items of sequence s: plain decode, partitions of its context (an empty context counts one item,
@@ -1685,7 +1698,8 @@ void prefill_mfma_kernel(DecodeArgs a) {
     tbl = tbl_next;
   }
 #pragma unroll
-  for (int j = 0; j < kT; ++j) emit_rows<QT, D>(a, st[j], vscale, -1, rs[j], rhq[j], rvalid[j]);
+  for (int j = 0; j < kT; ++j)
+    emit_rows<QT, D>(a, st[j], vscale, vscale, -1, rs[j], rhq[j], rvalid[j]);
 }
 
 template <class CT, class QT, int D>

@@ -351,8 +351,10 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
                 "query dtype, or fp8 cache with f16 queries; 16-byte aligned query rows, 8-byte "
                 "aligned output)",
                 who, B);
-  // the matrix-core kernel keeps the partials of f16-query rows in fp16
+  // the matrix-core kernel keeps the partials of f16-query rows in fp16, with an fp8 cache in
+  // units of the codes (the reduce applies the head's v_scale)
   a.part_f16 = use_mfma && q_dtype == PA_F16 ? 1 : 0;
+  a.part_vscale = a.part_f16 && cdt == PA_FP8_E4M3 ? 1 : 0;
   hipError_t e = use_mfma ? pa::launch_decode_mfma(a, s) : pa::launch_decode_valu(a, s);
   if (e == hipSuccess) e = pa::launch_partition_reduce(a, s);
   return launch_status(e, who);

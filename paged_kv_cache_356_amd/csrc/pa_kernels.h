@@ -65,6 +65,7 @@ struct DecodeArgs {
   int32_t num_partitions;   // ceil(max_context_len / partition_size)
   float *part_out;          // NULL when num_partitions == 1
   int32_t part_f16;         // 1: part_out holds fp16 values (matrix-core kernel, f16 queries)
+  int32_t part_vscale;      // 1: those values are in fp8 code units; the reduce applies v_scale
   float *part_ml;
   int32_t persistent;       // grid mode of the matrix-core kernel (set by its launcher)
   int32_t num_cus;          // compute units of the device (set by the launcher; 0: unknown)

@@ -57,6 +57,18 @@ constexpr int kSplitRows = 1024;
 #ifndef PA_REDUCE_WIDE
 #define PA_REDUCE_WIDE 1
 #endif
+// Scale of the merged row: 1, or the KV head's v_scale where the partials are in units of fp8
+// cache codes (part_vscale).
+template <bool kHalf>
+__device__ __forceinline__ float out_scale(const DecodeArgs &a, int row) {
+  if constexpr (kHalf)
+    if (a.part_vscale) {
+      const int hq = row % a.num_q_heads;
+      return a.cache.v_scale[hq / (a.num_q_heads / a.cache.num_kv_heads)];
+    }
+  return 1.0f;
+}
+
 #ifndef PA_REDUCE_PER
 #define PA_REDUCE_PER 4
 #endif
@@ -126,7 +138,7 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void partition_reduce_kernel(De
     acc.w += __shfl_xor(acc.w, o);
   }
   if (lane < C) {
-    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    const float inv = wsum > 0.0f ? out_scale<kHalf>(a, row) / wsum : 0.0f;
     auto *out = static_cast<typename QT::raw *>(a.out) + (size_t)row * D + 4 * lane;
     out[0] = from_f32<QT>(acc.x * inv);
     out[1] = from_f32<QT>(acc.y * inv);
@@ -201,7 +213,7 @@ __global__ __launch_bounds__(256) void partition_reduce_split_kernel(DecodeArgs 
     acc.w += __shfl_xor(acc.w, o);
   }
   if (pg == 0) {
-    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    const float inv = wsum > 0.0f ? out_scale<kHalf>(a, row) / wsum : 0.0f;
     auto *out = static_cast<typename QT::raw *>(a.out) + (size_t)row * D + 4 * col;
     out[0] = from_f32<QT>(acc.x * inv);
     out[1] = from_f32<QT>(acc.y * inv);

@@ -399,6 +399,67 @@ def test_poison_outside_the_context_never_leaks():
     assert torch.equal(clean.sets[0].out[0], dirty.sets[0].out[0])
 
 
+@pytest.mark.parametrize("flags", [api.PA_DECODE_DEFAULT, api.PA_DECODE_FORCE_VALU])
+def test_fp8_cache_values_beyond_f16_range(flags):
+    """An fp8 cache whose dequantised values pass f16's largest finite value (written from f32 rows
+    with v_scale up to 500), decoded with f16 queries over several partitions.  The first partition
+    of sequence 0 holds values of 448 * 500 under keys that leave it no weight: its own average is
+    not representable in f16, the merged output is, and must match the oracle.  Error bound: the
+    f16 output and an fp16 partial each round once (2^-11 relative), so 2^-8 of the largest weighted
+    |V| of the head leaves a margin of two."""
+    _say(f"fp8 cache beyond f16 range, flags {flags}")
+    H, Hq, D, S, ps = 4, 28, 128, 3, 64
+    lens = [200, 77, 130]
+    ks = np.array([0.05, 0.05, 0.05, 0.05], np.float32)
+    vs = np.array([500.0, 0.01, 300.0, 1.0], np.float32)
+    g = np.random.default_rng(17)
+    nbs = [math.ceil(L / 16) for L in lens]
+    nb = sum(nbs) + 3
+    perm = g.permutation(nb)
+    tables = np.zeros((S, max(nbs)), np.int32)
+    o = 0
+    for s, n in enumerate(nbs):
+        tables[s, :n] = perm[o:o + n]
+        o += n
+    slots = np.concatenate([tables[s, np.arange(L) // 16].astype(np.int64) * 16 + np.arange(L) % 16
+                            for s, L in enumerate(lens)])
+    T = len(slots)
+    key = (g.standard_normal((T, H, D)) * 0.4).astype(np.float32)
+    val = (g.uniform(-4, 4, (T, H, D)) * vs[None, :, None]).astype(np.float32)
+    key[:64, 0, :] = -448 * ks[0]  # sequence 0, head 0, partition 0: scores near -190
+    val[:64, 0, :] = 448 * vs[0]   # 224,000: past f16's range
+    q = g.standard_normal((S, Hq, D)).astype(np.float32)
+    q[:, :7, :] = g.uniform(0.5, 1.0, (S, 7, D))
+    qt = torch.from_numpy(q).to(torch.float16).cuda()
+    cache = api.KVCache.allocate(nb, H, D, "fp8", "cuda", torch.from_numpy(ks).cuda(),
+                                 torch.from_numpy(vs).cuda())
+    api.pa_reshape_and_cache(cache, torch.from_numpy(key).cuda(), torch.from_numpy(val).cuda(),
+                             torch.from_numpy(slots).cuda())
+    kp = host_pool(nb, H, D, "fp8")
+    vp = host_pool(nb, H, D, "fp8")
+    oracle.reshape_and_cache(kp, vp, "fp8", ks, vs, nb, H, D, key, val, "f32", slots)
+    scale = 1.0 / math.sqrt(D)
+    ws = torch.empty(api.pa_decode_workspace_bytes(S, Hq, H, D, max(lens), ps), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(qt)
+    api.pa_decode_attention(out, qt, cache, torch.from_numpy(tables).cuda(),
+                            torch.tensor(lens, dtype=torch.int32, device="cuda"), max(lens), scale,
+                            ps, ws, flags)
+    torch.cuda.synchronize()
+    dk, dv = device_pool_bytes(cache)
+    assert np.array_equal(dk, kp) and np.array_equal(dv, vp)
+    got = as_f64(out)
+    assert np.all(np.isfinite(got))
+    qd = qt.cpu().double().numpy()
+    for s, L in enumerate(lens):
+        for hq in range(Hq):
+            h = hq // (Hq // H)
+            kc, vc = oracle.gather(kp, vp, "fp8", ks, vs, nb, H, D, tables[s], L, h)
+            ref = oracle.attend_contiguous(qd[s, hq], kc, vc, scale)
+            tol = 2.0 ** -8 * 4 * float(vs[h])  # weighted |V| <= 4 * v_scale (partition 0 weighs 0)
+            assert max_abs_err(got[s, hq], ref) <= tol, (s, hq)
+
+
 def test_stale_workspace_never_leaks():
     """Workspace slots past a row's own partitions hold whatever earlier calls left there and must
     never be read: a workspace full of NaN bytes gives the same bits as a zeroed one, for the plain
