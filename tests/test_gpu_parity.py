@@ -349,29 +349,32 @@ def test_shared_prefix_equals_duplicated_prefix_bitwise():
     assert torch.equal(out2, st.out[0])
 
 
+@pytest.mark.parametrize("cache_dtype", ["f16", "fp8"])
 @pytest.mark.parametrize("ps", [0, 32])
-def test_shared_prefix_decode_matches_oracle(ps):
+def test_shared_prefix_decode_matches_oracle(ps, cache_dtype):
     """pa_decode_attention_shared_prefix against the oracle: the recipe's batch, then the same
     pool with some contexts cut below the prefix or to exactly the prefix (no suffix at all), and
-    the vector-ALU fallback; prefix chunks of 32 positions exercise several prefix partitions."""
+    the vector-ALU fallback; prefix chunks of 32 positions exercise several prefix partitions.
+    The fp8 case (E4M3 cache, f16 queries) runs the prefix groups on 2 KiB tiles."""
     w = wl.WORKLOADS["f16_shared_prefix_batch256"].replace(num_seqs=7, num_blocks=1024,
-                                                           prefix_len=64)
+                                                           prefix_len=64, cache_dtype=cache_dtype)
+    tol = TOL[cache_dtype]
     lengths = [64 + 1, 64 + 16, 64 + 17, 64 + 300, 64 + 2, 64 + 511, 64 + 40]
-    _say(f"shared-prefix decode, partition {ps}")
+    _say(f"shared-prefix decode, {cache_dtype} cache, partition {ps}")
     pad = _pad_block(w)
     b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON, lengths=lengths,
                     partition_size=ps)
     assert b.use_prefix
     ob = OracleBatch(b, pad, pool_fill=POISON)
     ob.metadata_matches(b)
-    _check_batch(b, ob, 0, TOL["f16"])
+    _check_batch(b, ob, 0, tol)
     st = b.sets[0]
-    kp, vp, _, _ = ob.pools[(0, 0)]
+    kp, vp, ks, vs = ob.pools[(0, 0)]
     ctx = st.ctx.copy()
     ctx[[0, 3]] = [20, 64]  # below the prefix; exactly the prefix
     d_ctx = torch.from_numpy(ctx).cuda()
     q = raw(st.q[0]).reshape(w.num_seqs, -1)
-    ref = oracle.decode_attention(q, w.q_dtype, kp, vp, w.cache_dtype, None, None, w.num_blocks,
+    ref = oracle.decode_attention(q, w.q_dtype, kp, vp, w.cache_dtype, ks, vs, w.num_blocks,
                                   w.num_kv_heads, w.head_dim, ob.sets[0]["tables"], ctx,
                                   w.num_q_heads, w.scale)
     for flags in (api.PA_DECODE_DEFAULT, api.PA_DECODE_FORCE_VALU):
@@ -382,7 +385,7 @@ def test_shared_prefix_decode_matches_oracle(ps):
         torch.cuda.synchronize()
         err = max_abs_err(as_f64(out), ref)
         _say(f"  cut contexts, flags {flags}: max-abs err {err:.3e}")
-        assert err <= TOL["f16"]
+        assert err <= tol
 
 
 def test_poison_outside_the_context_never_leaks():
