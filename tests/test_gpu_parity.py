@@ -184,11 +184,14 @@ SMALL_LENGTHS = {
 }
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("name", ["f16_batch32", "bf16_32k_batch8", "f16_shared_prefix_batch256", "fp8_28layer_batch512"])
 @pytest.mark.parametrize("flags", [api.PA_DECODE_DEFAULT, api.PA_DECODE_FORCE_VALU])
-def test_small_workloads_match_oracle(name, flags):
-    w = wl.WORKLOADS[name].replace(**SMALL[name])
-    _say(f"{name} reduced, flags {flags}")
+def test_small_workloads_match_oracle(name, flags, D):
+    """The reduced workloads at their own head_dim (128) and at 64, the other head size both
+    decode kernels take (on the matrix cores: 4 column tiles per head instead of 8)."""
+    w = wl.WORKLOADS[name].replace(**SMALL[name], head_dim=D)
+    _say(f"{name} reduced, head_dim {D}, flags {flags}")
     pad = _pad_block(w)
     b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON,
                     lengths=SMALL_LENGTHS[name], partition_size=0 if name != "bf16_32k_batch8" else 512)
