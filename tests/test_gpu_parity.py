@@ -685,14 +685,16 @@ def _reduced(name, **kw):
     return w.replace(**kw) if kw else w
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("name", FUSED)
 @pytest.mark.parametrize("flags", [api.PA_DECODE_DEFAULT, api.PA_DECODE_FORCE_VALU])
-def test_fused_append_matches_oracle(name, flags):
+def test_fused_append_matches_oracle(name, flags, D):
     """pa_decode_attention_append (the new token written and attended to in one call) against the
     oracle: attention within the dtype's tolerance, every pool byte equal to the oracle's replay of
-    reshape_and_cache; the vector-ALU configurations run the two calls behind the same entry."""
-    w = _reduced(name)
-    _say(f"fused append, {name} reduced, flags {flags}")
+    reshape_and_cache; the vector-ALU configurations run the two calls behind the same entry.  At
+    head_dim 64 the lanes past the head's 32 element pairs stage zeros and store nothing."""
+    w = _reduced(name, head_dim=D)
+    _say(f"fused append, {name} reduced, head_dim {D}, flags {flags}")
     pad = _pad_block(w)
     b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON,
                     lengths=SMALL_LENGTHS.get(name), partition_size=0 if name != "bf16_32k_batch8" else 512)
