@@ -549,16 +549,17 @@ def test_swap_out_and_in_round_trip():
         assert torch.equal(out, before[i])
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("cache_dtype", ["f16", "bf16", "fp8"])
-def test_prefill_matches_oracle(cache_dtype):
+def test_prefill_matches_oracle(cache_dtype, D):
     """pa_prefill_attention against the oracle: sequences with a history and a chunk of new tokens
     (a whole prompt, a chunk inside one block, one across blocks, a long one, none, one over a
-    history of more than 64 blocks), NaN in every pool byte no sequence owns."""
+    history of more than 64 blocks), NaN in every pool byte no sequence owns; head_dim 128 and 64."""
     q_dtype = "f16" if cache_dtype == "fp8" else cache_dtype
-    Hq, H, D, nb, B = 28, 4, 128, 512, 16
+    Hq, H, nb, B = 28, 4, 512, 16
     lengths = [37, 200, 18, 700, 9, 64, 1500]
     chunks = [37, 5, 13, 300, 0, 64, 130]
-    _say(f"prefill, {cache_dtype} cache")
+    _say(f"prefill, {cache_dtype} cache, head_dim {D}")
     g = torch.Generator().manual_seed(4242)
     bm = api.BlockManager(nb, B, wl.free_order(wl.WORKLOADS["f16_batch32"].replace(num_blocks=nb)))
     seqs = [bm.add_seq() for _ in lengths]
