@@ -248,17 +248,19 @@ def test_many_sequences_direct_grid():
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("B", [8, 32])
 @pytest.mark.parametrize("name", ["f16_batch32", "bf16_32k_batch8", "fp8_28layer_batch512"])
-def test_block_sizes_match_oracle(name, B):
+def test_block_sizes_match_oracle(name, B, D):
     """Pools of 8- and 32-position blocks: the same reduced workloads against the oracle run with
-    that block size, the step's cache writes bit-exact, partitions that start inside a block."""
+    that block size, the step's cache writes bit-exact, partitions that start inside a block;
+    head_dim 128 and 64."""
     kw = dict(SMALL[name])
     kw["num_blocks"] = kw["num_blocks"] * 16 // B
-    w = wl.WORKLOADS[name].replace(block_size=B, **kw)
+    w = wl.WORKLOADS[name].replace(block_size=B, head_dim=D, **kw)
     pad = _pad_block(w)
     for ps in (0, 48):
-        _say(f"{name} reduced, block size {B}, partition {ps}")
+        _say(f"{name} reduced, block size {B}, head_dim {D}, partition {ps}")
         b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON,
                         lengths=SMALL_LENGTHS[name], partition_size=ps)
         ob = OracleBatch(b, pad, pool_fill=POISON)
