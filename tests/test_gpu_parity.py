@@ -354,18 +354,21 @@ def test_shared_prefix_equals_duplicated_prefix_bitwise():
     assert torch.equal(out2, st.out[0])
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("cache_dtype", ["f16", "fp8"])
 @pytest.mark.parametrize("ps", [0, 32])
-def test_shared_prefix_decode_matches_oracle(ps, cache_dtype):
+def test_shared_prefix_decode_matches_oracle(ps, cache_dtype, D):
     """pa_decode_attention_shared_prefix against the oracle: the recipe's batch, then the same
     pool with some contexts cut below the prefix or to exactly the prefix (no suffix at all), and
     the vector-ALU fallback; prefix chunks of 32 positions exercise several prefix partitions.
-    The fp8 case (E4M3 cache, f16 queries) runs the prefix groups on 2 KiB tiles."""
+    The fp8 case (E4M3 cache, f16 queries) runs the prefix groups on 2 KiB tiles (1 KiB at
+    head_dim 64)."""
     w = wl.WORKLOADS["f16_shared_prefix_batch256"].replace(num_seqs=7, num_blocks=1024,
-                                                           prefix_len=64, cache_dtype=cache_dtype)
+                                                           prefix_len=64, cache_dtype=cache_dtype,
+                                                           head_dim=D)
     tol = TOL[cache_dtype]
     lengths = [64 + 1, 64 + 16, 64 + 17, 64 + 300, 64 + 2, 64 + 511, 64 + 40]
-    _say(f"shared-prefix decode, {cache_dtype} cache, partition {ps}")
+    _say(f"shared-prefix decode, {cache_dtype} cache, head_dim {D}, partition {ps}")
     pad = _pad_block(w)
     b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON, lengths=lengths,
                     partition_size=ps)
