@@ -175,9 +175,15 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                 otherwise a positive multiple of 16.  A context of L tokens is cut into
  *                 ceil(L / partition_size) partitions of whole 16-position steps, as equal as
  *                 those allow (a partition may start inside a 32-position block); when there are
- *                 several they are computed independently (running max,
- *                 running sum, unnormalised output) and merged by a second kernel.
+ *                 several they are computed independently (each keeps its running max, running
+ *                 sum and output, and stores the max, the sum and its normalised output) and
+ *                 merged by a second kernel.
  *   workspace     device scratch of at least pa_decode_workspace_bytes() bytes (NULL if 0).
+ * Arithmetic: products, exponentials and sums in fp32 (the matrix cores take f16 / bf16 operands,
+ * fp8 codes widened to f16); the result rounds once to q_dtype.  With f16 queries on the matrix
+ * cores each partition's normalised output is kept in fp16 (round to nearest even) until the
+ * merge, adding at most 2^-11 of its magnitude; with an fp8 cache it is kept in units of the codes
+ * (|x| <= 448) and the head's v_scale is applied after the merge, so no partial overflows.
  * Supported: head_dim 64 or 128, num_q_heads a multiple of num_kv_heads with at most 16 query
  * heads per KV head; block_size 16 for every dtype, 8 or 32 for the matrix-core configurations
  * (f16 / bf16 caches with the same query dtype, fp8 caches with f16 queries, 16-byte aligned query
