@@ -6,12 +6,18 @@ pairs), then for every layer reshape_and_cache of the new token and the split-K 
 partition reduce.  The step's metadata (slots, tables, lengths, copy pairs) comes from the host
 block manager before timing and is resident in HBM when the timed region starts.
 
-Prints ONE JSON line:
-  value        KV GB/s of the step: algorithmic (logical) KV bytes read per step / step time;
+Prints ONE JSON line (default workload: the shared-prefix batch of 256 sequences):
+  value        KV GB/s of the step: algorithmic KV bytes read per step / step time, the median of
+               several passes of the timed loop (unique physical slots for the shared-prefix
+               workload, whose logical bytes count the prefix once per sequence; logical otherwise);
   roofline     for pa_decode_attention (the dominant call: split-K kernel + partition reduce):
                algorithmic bytes per call (unique physical KV slots + tables + lengths + Q + out)
                / its mean duration from HIP events on the launch stream, against 8 TB/s;
-  cpu_baseline the CPU oracle (fp64) timed on the host's cores on a bounded sample of set 0;
+  cpu_baseline the CPU oracle (fp64) timed on the host's cores on a bounded sample of set 0, and on
+               one core;
+  calibration  the read-bandwidth reference (pa_calibrate_read): a plain read of exactly the tiles
+               a decode call reads, and a sequential read of 2 GiB, on the same device;
+  targets      the 32K-context bf16 batch's decode call measured in the same run (default run);
   decode_call_us, reshape_call_us, copy_call_us
                p10 / p50 / p90 / mean per call over 20 batches of back-to-back eager calls,
                and seqs_per_s_per_layer_calls = S / (decode + reshape + copy / layers), medians.
@@ -43,6 +49,7 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "paged decode attention KV GB/s (% of HBM peak) + sequences/s per layer"
 # independent batches rotated by the timing loop, so that successive steps read KV that no cache
 # holds (the 256 MB MALL included); the 28-layer step reads ~14.5 GB by itself
+DEFAULT_WORKLOAD = "f16_shared_prefix_batch256"
 DEFAULT_SETS = {"tiny_f32": 1, "f16_batch32": 16, "bf16_32k_batch8": 3,
                 "f16_shared_prefix_batch256": 4, "fp8_28layer_batch512": 1}
 
@@ -63,6 +70,83 @@ def algorithmic_bytes(batch, unique: bool) -> int:
     qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * qe
     sc = 2 * w.num_kv_heads * 4 if w.cache_dtype == "fp8" else 0
     return kv + tables + lens + qo + sc
+
+
+def tile_list(batch, r: int) -> np.ndarray:
+    """Tile indices (block * num_kv_heads + head) that a decode call of set r reads: every
+    sequence's blocks up to its context length, for every KV head, each distinct tile once (a shared
+    prefix's blocks count once), in (sequence, block, head) order."""
+    w = batch.w
+    st = batch.sets[r]
+    B, H = w.block_size, w.num_kv_heads
+    seen, out = set(), []
+    for s in range(w.num_seqs):
+        for j in range(-(-int(st.ctx[s]) // B)):
+            b = int(st.tables[s, j])
+            if b in seen or not 0 <= b < w.num_blocks:
+                continue
+            seen.add(b)
+            out.extend(b * H + h for h in range(H))
+    return np.asarray(out, np.int32)
+
+
+def calibration(batch, torch, api, sets: int) -> dict:
+    """pa_calibrate_read on this device: the tiles the decode reads (rotating over the sets and
+    layers as the decode timing does, so no cache holds them), and a sequential read of up to 1 GiB
+    per pool; both with 8 wavefronts per compute unit, all resident at once."""
+    w = batch.w
+    e = 1 if w.cache_dtype == "fp8" else (4 if w.cache_dtype == "f32" else 2)
+    tb = w.block_size * w.head_dim * e
+    if tb % 1024:
+        return None
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    waves = 8 * cus
+    sink = torch.empty(waves, dtype=torch.int32, device="cuda")
+    lists = [torch.from_numpy(tile_list(batch, r)).cuda() for r in range(sets)]
+    lay = list(batch.layers)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n, reps=10):
+        for k in range(n):
+            fn(k)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for k in range(n * reps):
+            fn(k)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / 1e3 / (n * reps)
+
+    def gather(k):
+        c = batch.caches[lay[(k // sets) % len(lay)]]
+        t = lists[k % sets]
+        api.pa_calibrate_read(c.k_pool, c.v_pool, tb, t, t.numel(), sink, waves)
+
+    n = max(4, sets * len(lay))
+    sec_g = timed(gather, n)
+    g_bytes = 2 * lists[0].numel() * tb
+    c0 = batch.caches[lay[0]]
+    n_seq = min(c0.k_pool.numel(), 1 << 30) // tb
+    sec_s = timed(lambda k: api.pa_calibrate_read(c0.k_pool, c0.v_pool, tb, None, n_seq, sink,
+                                                  waves), 2)
+    s_bytes = 2 * n_seq * tb
+    return {"kernel": "pa_calibrate_read", "waves": waves,
+            "gather_GBps": round(g_bytes / sec_g / 1e9, 1), "gather_bytes": g_bytes,
+            "gather_us": round(sec_g * 1e6, 2),
+            "sequential_GBps": round(s_bytes / sec_s / 1e9, 1), "sequential_bytes": s_bytes,
+            "note": "plain reads of the decode call's own tiles (each distinct tile once) and of a "
+                    "contiguous range; the achievable rate on this device for those bytes"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def measured_traffic(w, default_run: bool):
@@ -114,20 +198,33 @@ def cpu_baseline(batch, budget_s: float) -> dict:
     row = 2 * w.num_kv_heads * w.head_dim * e
     # per query head the oracle de-pages its KV head's rows: count the logical bytes of the sample
     sample_bytes = int(L[take].sum()) * row
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        ob.attention(batch, layer, sel=sel, nthreads=threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 1000:
-            break
+    def run(nthreads, budget, sel):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            ob.attention(batch, layer, sel=sel, nthreads=nthreads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or reps >= 1000:
+                return reps, el
+
+    reps, el = run(threads, budget_s, sel)
     gbps = sample_bytes * reps / el / 1e9
+    # one core: the first sequences of the same sample, bounded to a fifth of the budget
+    frac = (budget_s / 5) / max(acc * max(threads, 1), 1e-9)
+    one = take[:max(1, min(len(take), int(len(take) * frac)))]
+    sel1 = (np.repeat(one, w.num_q_heads), np.tile(np.arange(w.num_q_heads), len(one)))
+    reps1, el1 = run(1, budget_s / 5, sel1)
+    bytes1 = int(L[one].sum()) * row
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"layer {layer}, set 0: {len(take)} of {w.num_seqs} sequences x all "
                       f"{w.num_q_heads} query heads ({int(L[take].sum())} positions), fp64, "
                       f"{reps} pass(es) in {el:.2f} s; seqs/s = "
-                      f"{len(take) * reps / el:.3f}"}
+                      f"{len(take) * reps / el:.3f}",
+            "one_core": {"value": round(bytes1 * reps1 / el1 / 1e9, 4), "unit": "GB/s",
+                         "sample": f"{len(one)} sequence(s) of the same sample, {reps1} pass(es) "
+                                   f"in {el1:.2f} s on 1 thread"}}
 
 
 def swap_bench(args, torch, api, wl, DecodeBatch) -> int:
@@ -223,12 +320,69 @@ def prefill_bench(args, torch, api, wl) -> int:
     return 0
 
 
+def decode_call_mean(batch, torch, sets: int, n: int, flags: int = 0, fused: bool = False,
+                     budget_s: float = 2e-3, first_reps: int = 3) -> float:
+    """Mean duration of one decode call: n calls back to back (rotating over sets and layers), a
+    few times over, between two HIP events on the stream they run on."""
+    lay = list(batch.layers)
+
+    def calls():
+        for k in range(n):
+            batch.decode(k % sets, lay[(k // sets) % len(lay)], flags=flags, append=fused)
+
+    for _ in range(first_reps):
+        calls()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    calls()
+    torch.cuda.synchronize()
+    est = (time.perf_counter() - t0) / n
+    reps = max(1, min(20, int(budget_s / max(est, 1e-6))))
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(reps):
+        calls()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / 1e3 / (reps * n)
+
+
+def target_call(name: str, torch, api, wl, DecodeBatch) -> dict:
+    """The decode call of another workload, measured in the same run: its roofline fraction."""
+    w = wl.WORKLOADS[name]
+    sets = DEFAULT_SETS[name]
+    b = DecodeBatch(w, device="cuda", num_sets=sets)
+    for r in range(sets):
+        b.run_step(r)
+    torch.cuda.synchronize()
+    sec = decode_call_mean(b, torch, sets, max(8, min(64, sets * len(b.layers))))
+    unique = w.prefix_len > 0
+    alg = algorithmic_bytes(b, unique=unique)
+    ach = alg / sec / 1e9
+    out = {"workload": f"{w.name}: {w.description}", "decode_call_us": round(sec * 1e6, 3),
+           "bytes_per_call": alg, "bytes_kind": "unique physical KV slots" if unique else
+           "logical KV", "achieved": round(ach, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+           "frac": round(ach / HBM_PEAK_GBPS, 4)}
+    del b
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="f16_batch32", choices=list(DEFAULT_SETS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(DEFAULT_SETS))
+    ap.add_argument("--passes", type=int, default=5,
+                    help="passes of the timed loop (each times exactly --steps steps); value and "
+                         "ms_per_step come from the median pass")
+    ap.add_argument("--targets", default=None,
+                    help="comma-separated workloads whose decode call is measured in the same run "
+                         "(roofline only); default: the 32K-context batch beside the default "
+                         "workload, none otherwise; '' for none")
+    ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--sets", type=int, default=0, help="independent batches rotated (0 = default)")
     ap.add_argument("--valu", action="store_true", help="force the vector-ALU decode kernel")
     ap.add_argument("--graph", action="store_true",
@@ -367,12 +521,16 @@ def main() -> int:
     # timeit does): a full collection takes tens of milliseconds, longer than many steps.
     gc.collect()
     gc.disable()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        run_step(k)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    log(f"[bench] timed {args.steps} step(s) in {elapsed * 1e3:.2f} ms")
+    pass_s = []
+    for p in range(max(1, args.passes)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            run_step(k)
+        torch.cuda.synchronize()
+        pass_s.append(time.perf_counter() - t0)
+        log(f"[bench] pass {p}: timed {args.steps} step(s) in {pass_s[-1] * 1e3:.2f} ms")
+    elapsed = float(np.median(pass_s))
 
     # Decode-call duration for the roofline: n_dec calls back to back between two HIP events on the
     # stream they run on, a few times over.
@@ -424,7 +582,8 @@ def main() -> int:
         e_c = 1 if w.cache_dtype == "fp8" else (4 if w.cache_dtype == "f32" else 2)
         alg += w.num_seqs * (2 * w.num_kv_heads * w.head_dim * (e_in + e_c) + 8)
     achieved = alg / dec_mean_s / 1e9
-    value = kv_logical * layers / (ms_per_step / 1e3) / 1e9
+    kv_step = (batch.kv_bytes_per_layer(unique=True) if unique else kv_logical) * layers
+    value = kv_step / (ms_per_step / 1e3) / 1e9
     seqs_per_s_layer = w.num_seqs / (ms_per_step / 1e3 / layers)
 
     res = {
@@ -435,6 +594,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "passes_ms_per_step": [round(t * 1e3 / args.steps, 5) for t in pass_s],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -456,6 +616,8 @@ def main() -> int:
                            if fused else "pa_reshape_and_cache + decode"),
             "sets_rotated": sets,
             "launch": "hip graph replay" if args.graph else "eager (GPU-bound)",
+            "value_bytes": "unique physical KV slots per step (the shared prefix once)" if unique
+                           else "logical KV bytes per step",
             "kv_bytes_per_step_logical": kv_logical * layers,
             "kv_bytes_per_layer_unique": batch.kv_bytes_per_layer(unique=True) if unique else
             kv_logical,
@@ -496,6 +658,19 @@ def main() -> int:
             "bytes_kind": "unique physical KV slots" if unique else "logical KV",
         },
     }
+    if not args.no_calibration:
+        res["calibration"] = calibration(batch, torch, api, sets)
+        log(f"[bench] calibration {res['calibration']}")
+    default_run = (args.workload == DEFAULT_WORKLOAD and not fused and not args.valu and
+                   args.partition < 0 and args.block_size == 16 and not args.contiguous and
+                   not args.no_prefix and not args.num_blocks)
+    targets = args.targets if args.targets is not None else \
+        ("bf16_32k_batch8" if default_run else "")
+    if targets:
+        res["targets"] = {}
+        for name in [t for t in targets.split(",") if t]:
+            res["targets"][name] = target_call(name, torch, api, wl, DecodeBatch)
+            log(f"[bench] target {name}: {res['targets'][name]}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(batch, args.cpu_budget)

@@ -111,8 +111,8 @@ size_t pa_pool_bytes(const pa_cache *cache);
 
 /*
  * pa_reshape_and_cache — write each new token's K and V into its slot.
- * Each new token appends one KV entry inside the current logical block of its sequence
- * ([Lesson06] "How paging grows"); K and V are kept for every later token ([Visualized] Part 2).
+ * A new token's K and V go to the next unused slot of its sequence's last block ([Lesson06] "How
+ * paging grows"), where every later token reads them ([Visualized] Part 2).
  *
  *   key, value    device [num_tokens] rows; row t holds num_kv_heads * head_dim elements of
  *                 `in_dtype` laid out [kv_head][head_dim]; consecutive rows are key_stride /
@@ -248,7 +248,10 @@ pa_status pa_decode_attention_shared_prefix(void *out, const void *query, int32_
  *                 (its block table's entry for that position times block_size, plus the offset),
  *                 or negative for no write.  With a shared prefix the position must lie after it
  *                 (context_lens[s] > prefix_len); a slot given for a shorter context is not
- *                 written.  Two sequences must not share a slot.
+ *                 written.  Two sequences must not share a slot.  With prefix_len > 0 the call
+ *                 needs the prefix path (the batches pa_decode_attention_shared_prefix computes
+ *                 with its prefix groups): anything else is PA_ERR_UNSUPPORTED, and nothing is
+ *                 written.
  *   prefix_table, prefix_len  as in pa_decode_attention_shared_prefix (NULL / 0: plain decode).
  *   workspace     at least pa_decode_workspace_bytes() (pa_decode_shared_prefix_workspace_bytes()
  *                 with a prefix) bytes.

@@ -5,8 +5,8 @@ It follows the pages step by step:
     to the pool when a sequence finishes ("PagedAttention" (devoured.fyi), "PagedAttention in one
     picture");
   * a per-sequence block table mapping logical block index to physical block id (same section);
-  * a new block is mapped only when the previous one is full; every token appends one entry in the
-    current block ("LLM Inference Visualizer, Lesson 06", "How paging grows");
+  * a new block is mapped only when the previous one is full; each token takes the next slot of
+    the sequence's last block ("LLM Inference Visualizer, Lesson 06", "How paging grows");
   * shared blocks carry a reference count; fork shares every block ("PagedAttention, Visualized",
     Part 3, copy-on-write after fork / shared prefix blocks);
   * a write into a block whose count is above 1 clones it, decrements the original and retargets the

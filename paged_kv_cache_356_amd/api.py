@@ -27,8 +27,9 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPO
           -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_ALIAS", -6: "PA_ERR_LAUNCH", -7: "PA_ERR_NO_BLOCKS",
           -8: "PA_ERR_STATE"}
 
-# Every symbol include/pa.h declares.
+# Every symbol include/*.h declares.
 EXPORTS = [
+    "pa_calibrate_read",
     "pa_pool_bytes", "pa_reshape_and_cache", "pa_decode_auto_partition",
     "pa_decode_workspace_bytes", "pa_decode_attention", "pa_decode_attention_shared_prefix",
     "pa_decode_attention_append",
@@ -71,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         sig = {
             "pa_pool_bytes": (_sz, [_cp]),
+            "pa_calibrate_read": (_i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i32, _vp]),
             "pa_reshape_and_cache": (_i32, [_cp, _vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp]),
             "pa_decode_auto_partition": (_i32, [_i32, _i32, _i32]),
             "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -192,6 +194,14 @@ def pool_bytes(num_blocks, num_kv_heads, head_dim, cache_dtype, block_size=PA_BL
 
 
 # --------------------------------------------------------------------------- kernels
+def pa_calibrate_read(k_pool: torch.Tensor, v_pool: torch.Tensor, tile_bytes: int,
+                      tiles: torch.Tensor | None, num_tiles: int, sink: torch.Tensor,
+                      num_waves: int, stream=None) -> None:
+    """The read-bandwidth reference (include/pa_calibrate.h): read the listed tiles of both pools."""
+    _check(lib().pa_calibrate_read(_ptr(k_pool), _ptr(v_pool), int(tile_bytes), _ptr(tiles),
+                                   int(num_tiles), _ptr(sink), int(num_waves), _stream(stream)))
+
+
 class ReshapeCall:
     """pa_reshape_and_cache with every argument but the stream fixed: the checks and conversions
     are done once, when the call is made, for loops that repeat it."""

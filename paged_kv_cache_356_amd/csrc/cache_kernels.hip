@@ -1,9 +1,9 @@
 // cache_kernels.hip — reshape_and_cache (write each new token's K/V into its slot) and
 // copy_blocks (the clone step of copy-on-write) for gfx950.
 //
-// reshape_and_cache: each generated token appends one K/V entry inside the current block of its
-// sequence ("LLM Inference Visualizer, Lesson 06", "How paging grows"); K and V are what every
-// later token reads ("PagedAttention, Visualized", Part 2).
+// reshape_and_cache: a generated token's K and V land in the next unused slot of its sequence's
+// last block ("LLM Inference Visualizer, Lesson 06", "How paging grows"), where every later token
+// reads them ("PagedAttention, Visualized", Part 2).
 // copy_blocks: a writer into a shared block gets a clone of that one block ("PagedAttention"
 // (devoured.fyi), "Copy-on-write: when two requests share a prefix").
 #include <type_traits>

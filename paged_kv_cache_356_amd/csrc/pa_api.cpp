@@ -294,8 +294,10 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
        ap.value_stride % 2 != 0))
     return fail(PA_ERR_SHAPE, "%s: with a shared prefix, key/value rows must be 4-byte aligned "
                 "with even strides", who);
-  const int32_t pt = resolve_partition(num_seqs, H, use_prefix ? max_len - prefix_len : max_len,
-                                       partition_size);
+  // The automatic partition size follows the caller's max_context_len, as the workspace-size
+  // functions do (the clamped max_len only bounds the number of partition slots).
+  const int32_t pt = resolve_partition(
+      num_seqs, H, use_prefix ? max_context_len - prefix_len : max_context_len, partition_size);
   const int64_t slots = decode_slots(max_len, pt, use_prefix ? prefix_len : 0);
   const bool partials = use_prefix || slots > 1;
   const size_t need = ws_bytes_for(num_seqs, num_q_heads, D, slots, partials);
@@ -319,6 +321,23 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool use_mfma = use_prefix || (!force_valu && pa::decode_mfma_supports(a));
+  // Every check runs before the first launch: a failed call enqueues nothing.
+  if (!use_mfma && B != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: block_size %d runs on the matrix cores only (f16 or bf16 cache with the same "
+                "query dtype, or fp8 cache with f16 queries; 16-byte aligned query rows, 8-byte "
+                "aligned output)",
+                who, B);
+  // With a shared prefix, only the prefix kernel keeps a context that ends inside the prefix from
+  // writing its token into the shared blocks; batches it does not cover are refused rather than
+  // appended by a path without that guard.
+  if (app && prefix_len > 0 && !use_prefix)
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: the append with a shared prefix needs the prefix path (f16 / bf16 cache with "
+                "the same query dtype or fp8 cache with f16 queries, at most 2048 sequences, no "
+                "PA_DECODE_FORCE_VALU); call pa_reshape_and_cache and "
+                "pa_decode_attention_shared_prefix instead",
+                who);
   if (app) {
     // The matrix-core kernel writes the new tokens itself (16-bit rows read in pairs); elsewhere
     // reshape_and_cache runs first, with the same result.
@@ -345,12 +364,6 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
       if (er != hipSuccess) return launch_status(er, who);
     }
   }
-  if (!use_mfma && B != PA_BLOCK_SIZE)
-    return fail(PA_ERR_UNSUPPORTED,
-                "%s: block_size %d runs on the matrix cores only (f16 or bf16 cache with the same "
-                "query dtype, or fp8 cache with f16 queries; 16-byte aligned query rows, 8-byte "
-                "aligned output)",
-                who, B);
   // the matrix-core kernel keeps the partials of f16-query rows in fp16, with an fp8 cache in
   // units of the codes (the reduce applies the head's v_scale)
   a.part_f16 = use_mfma && q_dtype == PA_F16 ? 1 : 0;

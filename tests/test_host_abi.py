@@ -1,10 +1,11 @@
-"""CPU tests of the product's host side: libpa.so loads and exports every symbol include/pa.h
+"""CPU tests of the product's host side: libpa.so loads and exports every symbol include/*.h
 declares, argument validation rejects bad calls before any launch, the C++ block manager agrees
 bit for bit with the oracle's model, and the pages' per-token KV arithmetic holds for
 pa_pool_bytes.  No kernel is launched here."""
 from __future__ import annotations
 
 import ctypes
+import glob
 import os
 import re
 
@@ -19,9 +20,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _header_functions():
-    text = open(os.path.join(ROOT, "include", "pa.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -101,6 +104,32 @@ def test_decode_append_validation(kw, status):
     """pa_decode_attention_append checks its own arguments (the new rows, their strides, the slots)
     and the decode's, before any launch; no call reaches the GPU here."""
     assert _decode_append(_cache(), **kw) == status
+
+
+def test_append_rejections_come_before_any_launch():
+    """A configuration the append cannot run is refused before the cache write is enqueued: an f32
+    cache at block size 8 (no matrix-core kernel for it), and a shared prefix on a batch the prefix
+    path does not cover (here PA_DECODE_FORCE_VALU).  Without a GPU a launch would report
+    PA_ERR_LAUNCH (-6), so PA_ERR_UNSUPPORTED (-3) shows that nothing was launched first."""
+    f32 = _cache(cache_dtype=api.PA_F32, block_size=8)
+    assert _decode_append(f32, q_dtype=api.PA_F32, ws=4096, ws_bytes=1 << 20) == -3
+    assert "block_size 8" in api.lib().pa_last_error().decode()
+    st = _decode_append(_cache(), prefix_table=1024, prefix_len=64, ws=4096, ws_bytes=1 << 30,
+                        flags=api.PA_DECODE_FORCE_VALU)
+    assert st == -3
+    assert "prefix path" in api.lib().pa_last_error().decode()
+
+
+def test_workspace_size_follows_the_callers_max_context_len():
+    """The automatic partition size is chosen from the caller's max_context_len in both the size
+    function and the call, even when the table's capacity is smaller: a workspace of exactly
+    pa_decode_workspace_bytes() passes the size check (the misaligned workspace pointer then stops
+    the call before any launch, with PA_ERR_SHAPE rather than PA_ERR_WORKSPACE)."""
+    need = api.pa_decode_workspace_bytes(1, 28, 4, 128, 4096, 0)
+    assert need > 0
+    st = _decode(_cache(), S=1, max_blocks=250, max_ctx=4096, ws=4097, ws_bytes=need)
+    assert st == -2, api.lib().pa_last_error().decode()
+    assert "aligned" in api.lib().pa_last_error().decode()
 
 
 def _decode_prefix(cache, prefix_table=1024, prefix_len=64, **kw):
