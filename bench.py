@@ -93,17 +93,17 @@ def tile_list(batch, r: int) -> np.ndarray:
 def calibration(batch, torch, api, sets: int) -> dict:
     """pa_calibrate_read on this device: the tiles the decode reads (rotating over the sets and
     layers as the decode timing does, so no cache holds them), and a sequential read of up to 1 GiB
-    per pool; both with 8 wavefronts per compute unit, all resident at once."""
+    per pool."""
     w = batch.w
     e = 1 if w.cache_dtype == "fp8" else (4 if w.cache_dtype == "f32" else 2)
     tb = w.block_size * w.head_dim * e
     if tb % 1024:
         return None
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    waves = 8 * cus
-    sink = torch.empty(waves, dtype=torch.int32, device="cuda")
     lists = [torch.from_numpy(tile_list(batch, r)).cuda() for r in range(sets)]
     lay = list(batch.layers)
+    n_seq0 = min(batch.caches[lay[0]].k_pool.numel(), 1 << 30) // tb
+    sink = torch.empty((max(n_seq0, max(t.numel() for t in lists)) + 3) // 4, dtype=torch.int32,
+                       device="cuda")
     stream = torch.cuda.current_stream()
 
     def timed(fn, n, reps=10):
@@ -121,17 +121,16 @@ def calibration(batch, torch, api, sets: int) -> dict:
     def gather(k):
         c = batch.caches[lay[(k // sets) % len(lay)]]
         t = lists[k % sets]
-        api.pa_calibrate_read(c.k_pool, c.v_pool, tb, t, t.numel(), sink, waves)
+        api.pa_calibrate_read(c.k_pool, c.v_pool, tb, t, t.numel(), sink)
 
     n = max(4, sets * len(lay))
     sec_g = timed(gather, n)
     g_bytes = 2 * lists[0].numel() * tb
     c0 = batch.caches[lay[0]]
     n_seq = min(c0.k_pool.numel(), 1 << 30) // tb
-    sec_s = timed(lambda k: api.pa_calibrate_read(c0.k_pool, c0.v_pool, tb, None, n_seq, sink,
-                                                  waves), 2)
+    sec_s = timed(lambda k: api.pa_calibrate_read(c0.k_pool, c0.v_pool, tb, None, n_seq, sink), 2)
     s_bytes = 2 * n_seq * tb
-    return {"kernel": "pa_calibrate_read", "waves": waves,
+    return {"kernel": "pa_calibrate_read", "waves": "one per tile",
             "gather_GBps": round(g_bytes / sec_g / 1e9, 1), "gather_bytes": g_bytes,
             "gather_us": round(sec_g * 1e6, 2),
             "sequential_GBps": round(s_bytes / sec_s / 1e9, 1), "sequential_bytes": s_bytes,
@@ -385,6 +384,9 @@ def main() -> int:
     ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--sets", type=int, default=0, help="independent batches rotated (0 = default)")
     ap.add_argument("--valu", action="store_true", help="force the vector-ALU decode kernel")
+    ap.add_argument("--separate-reduce", action="store_true",
+                    help="merge partitions with the separate reduce kernel instead of inside the "
+                         "decode kernel (PA_DECODE_SEPARATE_REDUCE)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as a captured HIP graph instead of launching every call "
                          "from Python")
@@ -452,7 +454,8 @@ def main() -> int:
     if args.num_blocks:
         w = w.replace(num_blocks=args.num_blocks)
     sets = args.sets or DEFAULT_SETS[w.name]
-    flags = api.PA_DECODE_FORCE_VALU if args.valu else api.PA_DECODE_DEFAULT
+    flags = (api.PA_DECODE_FORCE_VALU if args.valu else api.PA_DECODE_DEFAULT) | \
+        (api.PA_DECODE_SEPARATE_REDUCE if args.separate_reduce else 0)
     t_build = time.perf_counter()
     batch = DecodeBatch(w, device="cuda", num_sets=sets,
                         keep_values=not args.no_cpu_baseline,
@@ -608,6 +611,8 @@ def main() -> int:
             "partition_size": batch.partition_size or api.pa_decode_auto_partition(
                 w.num_seqs, w.num_kv_heads, batch.max_context_len),
             "kernel": "valu" if args.valu else "default",
+            "partition_merge": "partition-reduce kernel" if args.separate_reduce or args.valu
+                               else "in the decode kernel where it applies",
             "shared_prefix_decode": bool(batch.use_prefix),
             "block_placement": "contiguous (free list in pool order)" if args.contiguous else
                                "scattered (seeded permutation of the pool)",
@@ -662,6 +667,7 @@ def main() -> int:
         res["calibration"] = calibration(batch, torch, api, sets)
         log(f"[bench] calibration {res['calibration']}")
     default_run = (args.workload == DEFAULT_WORKLOAD and not fused and not args.valu and
+                   not args.separate_reduce and
                    args.partition < 0 and args.block_size == 16 and not args.contiguous and
                    not args.no_prefix and not args.num_blocks)
     targets = args.targets if args.targets is not None else \

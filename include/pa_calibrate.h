@@ -25,17 +25,17 @@ extern "C" {
  *   tiles          device int32 [num_tiles] tile indices (any order; each is read once per call,
  *                  in both pools).  NULL reads tiles 0 .. num_tiles - 1 in order (a sequential
  *                  read of num_tiles * tile_bytes bytes per pool).
- *   sink           device uint32 [num_waves]: one word per wavefront (an XOR of what it read), so
- *                  that the loads are not dead code; its value means nothing.
- *   num_waves      wavefronts of the launch (four per workgroup); the list is cut into num_waves
- *                  equal contiguous ranges, each wavefront keeping 16 loads of 16 bytes per lane in
- *                  flight (16 KiB per wavefront), with the non-temporal hint the decode kernels use.
+ *   sink           device uint32 [ceil(num_tiles / 4)]: one word per workgroup of four
+ *                  wavefronts (an XOR of what they read), so that the loads are not dead code; its
+ *                  value means nothing.
+ * One wavefront per list entry issues all of the entry's 16-byte loads at once (tile_bytes / 512
+ * per lane, each wave-wide load a whole 1 KiB, with the non-temporal hint the decode kernels use);
+ * the hardware keeps as many wavefronts in flight as fit on the device.
  * Returns PA_ERR_NULL / PA_ERR_SHAPE for bad arguments (nothing enqueued), PA_ERR_LAUNCH if the
  * launch fails.  Bytes read per call: 2 * num_tiles * tile_bytes.
  */
 pa_status pa_calibrate_read(const void *k_pool, const void *v_pool, int64_t tile_bytes,
-                            const int32_t *tiles, int64_t num_tiles, uint32_t *sink,
-                            int32_t num_waves, void *stream);
+                            const int32_t *tiles, int64_t num_tiles, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,8 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_BLOCK_SIZE = 16
 PA_DECODE_DEFAULT = 0
 PA_DECODE_FORCE_VALU = 1
+PA_DECODE_SEPARATE_REDUCE = 2
+PA_DECODE_COUNTER_BYTES = 262144  # the workspace's leading arrival counters: zero between calls
 DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
 TORCH_CODES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 ELEM_BYTES = {PA_F32: 4, PA_F16: 2, PA_BF16: 2, PA_FP8_E4M3: 1}
@@ -72,7 +74,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         sig = {
             "pa_pool_bytes": (_sz, [_cp]),
-            "pa_calibrate_read": (_i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i32, _vp]),
+            "pa_calibrate_read": (_i32, [_vp, _vp, _i64, _vp, _i64, _vp, _vp]),
             "pa_reshape_and_cache": (_i32, [_cp, _vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp]),
             "pa_decode_auto_partition": (_i32, [_i32, _i32, _i32]),
             "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -196,10 +198,11 @@ def pool_bytes(num_blocks, num_kv_heads, head_dim, cache_dtype, block_size=PA_BL
 # --------------------------------------------------------------------------- kernels
 def pa_calibrate_read(k_pool: torch.Tensor, v_pool: torch.Tensor, tile_bytes: int,
                       tiles: torch.Tensor | None, num_tiles: int, sink: torch.Tensor,
-                      num_waves: int, stream=None) -> None:
-    """The read-bandwidth reference (include/pa_calibrate.h): read the listed tiles of both pools."""
+                      stream=None) -> None:
+    """The read-bandwidth reference (include/pa_calibrate.h): read the listed tiles of both pools;
+    sink holds at least ceil(num_tiles / 4) words."""
     _check(lib().pa_calibrate_read(_ptr(k_pool), _ptr(v_pool), int(tile_bytes), _ptr(tiles),
-                                   int(num_tiles), _ptr(sink), int(num_waves), _stream(stream)))
+                                   int(num_tiles), _ptr(sink), _stream(stream)))
 
 
 class ReshapeCall:
