@@ -1044,8 +1044,7 @@ template <class QT, int D>
 __device__ __forceinline__ void merge_unit(const DecodeArgs &a, int s, int h, int n) {
   constexpr int NT = D / 16;
   constexpr int DPL = D / 16;  // head dims per lane
-  constexpr int HV = DPL / 8;  // 16-byte loads per fp16 partial and lane (D = 128: 1)
-  constexpr int FV = DPL / 4;  // 16-byte loads per fp32 partial and lane
+  constexpr int FV = DPL / 4;  // 16-byte loads per fp32 partial and lane (fp16: half of them)
   const int lane = threadIdx.x & 63, k = lane & 15, rq = lane >> 4;
   const int Hq = a.num_q_heads, g = Hq / a.cache.num_kv_heads;
   const bool half = a.part_f16 != 0;
@@ -1070,11 +1069,14 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs &a, int s, int h, in
     // lane's part of partial p (a slot past n reads slot n - 1 again; its weight is 0)
     auto load = [&](int p, u32x4_t (&x)[FV]) {
       const int q = rr * NP + min(p, n - 1);
-      if (half) {
-#pragma unroll
-        for (int i = 0; i < HV; ++i)
-          x[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, (q * D + DPL * k) * 2 + 16 * i, 0,
-                                                       kCoherent);
+      if (half) {  // DPL halves: 16 bytes (D = 128) or 8 bytes (D = 64)
+        if constexpr (DPL == 8) {
+          x[0] = __builtin_amdgcn_raw_buffer_load_b128(rp, (q * D + DPL * k) * 2, 0, kCoherent);
+        } else {
+          const u32x2_t y =
+              __builtin_amdgcn_raw_buffer_load_b64(rp, (q * D + DPL * k) * 2, 0, kCoherent);
+          x[0] = u32x4_t{y[0], y[1], 0u, 0u};
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < FV; ++i)
@@ -1084,12 +1086,9 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs &a, int s, int h, in
     };
     auto add = [&](const u32x4_t (&x)[FV], float w, facc_t &acc) {
       if (half) {
+        const _Float16 *e = reinterpret_cast<const _Float16 *>(&x[0]);
 #pragma unroll
-        for (int i = 0; i < HV; ++i) {
-          const _Float16 *e = reinterpret_cast<const _Float16 *>(&x[i]);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[8 * i + j] += w * (float)e[j];
-        }
+        for (int j = 0; j < DPL; ++j) acc[j] += w * (float)e[j];
       } else {
 #pragma unroll
         for (int i = 0; i < FV; ++i)
