@@ -384,9 +384,6 @@ def main() -> int:
     ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--sets", type=int, default=0, help="independent batches rotated (0 = default)")
     ap.add_argument("--valu", action="store_true", help="force the vector-ALU decode kernel")
-    ap.add_argument("--separate-reduce", action="store_true",
-                    help="merge partitions with the separate reduce kernel instead of inside the "
-                         "decode kernel (PA_DECODE_SEPARATE_REDUCE)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as a captured HIP graph instead of launching every call "
                          "from Python")
@@ -454,8 +451,7 @@ def main() -> int:
     if args.num_blocks:
         w = w.replace(num_blocks=args.num_blocks)
     sets = args.sets or DEFAULT_SETS[w.name]
-    flags = (api.PA_DECODE_FORCE_VALU if args.valu else api.PA_DECODE_DEFAULT) | \
-        (api.PA_DECODE_SEPARATE_REDUCE if args.separate_reduce else 0)
+    flags = api.PA_DECODE_FORCE_VALU if args.valu else api.PA_DECODE_DEFAULT
     t_build = time.perf_counter()
     batch = DecodeBatch(w, device="cuda", num_sets=sets,
                         keep_values=not args.no_cpu_baseline,
@@ -611,8 +607,6 @@ def main() -> int:
             "partition_size": batch.partition_size or api.pa_decode_auto_partition(
                 w.num_seqs, w.num_kv_heads, batch.max_context_len),
             "kernel": "valu" if args.valu else "default",
-            "partition_merge": "partition-reduce kernel" if args.separate_reduce or args.valu
-                               else "in the decode kernel where it applies",
             "shared_prefix_decode": bool(batch.use_prefix),
             "block_placement": "contiguous (free list in pool order)" if args.contiguous else
                                "scattered (seeded permutation of the pool)",
@@ -667,7 +661,6 @@ def main() -> int:
         res["calibration"] = calibration(batch, torch, api, sets)
         log(f"[bench] calibration {res['calibration']}")
     default_run = (args.workload == DEFAULT_WORKLOAD and not fused and not args.valu and
-                   not args.separate_reduce and
                    args.partition < 0 and args.block_size == 16 and not args.contiguous and
                    not args.no_prefix and not args.num_blocks)
     targets = args.targets if args.targets is not None else \

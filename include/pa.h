@@ -137,13 +137,7 @@ pa_status pa_reshape_and_cache(const pa_cache *cache, const void *key, const voi
 int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len);
 
 /* Device workspace bytes pa_decode_attention needs for these sizes (0 is a valid answer when the
- * work fits one partition per sequence).  partition_size = 0 means the automatic choice.
- * A non-empty workspace starts with PA_DECODE_COUNTER_BYTES of arrival counters (one 32-bit word
- * per (sequence, KV head) row, used when the decode kernel merges a row's partitions itself): they
- * must be zero before the first call that uses the workspace (torch.zeros, hipMemset), and every
- * call leaves them zero.  The rest holds the partitions' results and may contain anything between
- * calls.  With PA_DECODE_SEPARATE_REDUCE the counters are never read or written. */
-#define PA_DECODE_COUNTER_BYTES 262144u
+ * work fits one partition per sequence).  partition_size = 0 means the automatic choice. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size);
@@ -151,8 +145,6 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 /* Flags for pa_decode_attention. */
 #define PA_DECODE_DEFAULT 0u
 #define PA_DECODE_FORCE_VALU 1u  /* use the vector-ALU kernel even where the matrix-core one applies */
-#define PA_DECODE_SEPARATE_REDUCE 2u /* merge partitions with the separate reduce kernel (leaves the
-                                        workspace's counters untouched)                          */
 
 /*
  * pa_decode_attention — one decode step of paged attention for a batch of sequences.

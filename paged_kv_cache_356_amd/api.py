@@ -19,8 +19,6 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_BLOCK_SIZE = 16
 PA_DECODE_DEFAULT = 0
 PA_DECODE_FORCE_VALU = 1
-PA_DECODE_SEPARATE_REDUCE = 2
-PA_DECODE_COUNTER_BYTES = 262144  # the workspace's leading arrival counters: zero between calls
 DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
 TORCH_CODES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 ELEM_BYTES = {PA_F32: 4, PA_F16: 2, PA_BF16: 2, PA_FP8_E4M3: 1}

@@ -93,9 +93,6 @@ constexpr int kPrefixTiles = PA_PREFIX_TILES;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, the value raw loads use on gfx9
-// Cache-policy operand of the raw buffer builtins: sc1, the device-scope (coherent across the
-// XCDs' L2 caches) bit that relaxed agent-scope atomic loads and stores carry on gfx950.
-constexpr int kCoherent = 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *tile, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(tile), (short)0, bytes, kRsrcWord3);
@@ -599,8 +596,7 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs &a, int s) {
 // table entries), waited for once this item's blocks are done.
 template <class QT, int D>
 __device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D> &st, float vscale,
-                                          float pvscale, int slot, int rs, int rhq, bool rvalid,
-                                          size_t base_row = 0);
+                                          int slot, int rs, int rhq, bool rvalid);
 
 // A 4-, 8- or 16-byte LDS read.
 template <class T>
@@ -898,15 +894,8 @@ __device__ __forceinline__ void write_token_rows(const DecodeArgs &a, int rank, 
   }
 }
 
-template <class QT, int D>
-__device__ __forceinline__ void merge_unit(const DecodeArgs &a, int s, int h, int n);
-__device__ __forceinline__ bool arrive(const DecodeArgs &a, int unit, int n);
-
-// Returns true when the in-kernel merge is on and this item's partition completed its row: the
-// caller then merges row (rs, h) (merge_unit), after its own items, where the ring's registers are
-// free.
 template <class CT, class QT, int D, bool kNT, int kB>
-__device__ __forceinline__ bool rows_core(const DecodeArgs &a, const int32_t *table, int h,
+__device__ __forceinline__ void rows_core(const DecodeArgs &a, const int32_t *table, int h,
                                           int jb0, int jb1, int end, int slot, int rs, int rhq,
                                           bool rvalid, int lim, int tbl0, int &settle, bool append,
                                           int L) {
@@ -927,23 +916,14 @@ __device__ __forceinline__ bool rows_core(const DecodeArgs &a, const int32_t *ta
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk)
     asm volatile("" : "+v"(st.qop[kk].x), "+v"(st.qop[kk].y), "+v"(st.qop[kk].z), "+v"(st.qop[kk].w));
-  const int g = a.num_q_heads / a.cache.num_kv_heads;
-  emit_rows<QT, D>(a, st, vscale, partial_vscale<CT, QT>(vscale), slot, rs, rhq, rvalid,
-                   (size_t)rs * a.num_q_heads + h * g);
-  // In-kernel merge: this partition is one arrival of row (rs, h), whose partitions (and prefix
-  // chunks) number row_partitions(L).
-  return a.merge && slot >= 0 &&
-         arrive(a, rs * a.cache.num_kv_heads + h, row_partitions(a, L));
+  emit_rows<QT, D>(a, st, vscale, partial_vscale<CT, QT>(vscale), slot, rs, rhq, rvalid);
 }
 
 // A finished row state to the output (slot < 0, scaled by vscale) or to workspace partition
-// `slot` (scaled by pvscale).  base_row: a wave-uniform output row at or below every valid lane's
-// (rs Hq + rhq), within 4,096 rows of them: the device-coherent stores of the in-kernel merge go
-// through one buffer descriptor based there.
+// `slot` (scaled by pvscale).
 template <class QT, int D>
 __device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D> &st, float vscale,
-                                          float pvscale, int slot, int rs, int rhq, bool rvalid,
-                                          size_t base_row) {
+                                          float pvscale, int slot, int rs, int rhq, bool rvalid) {
   constexpr int NT = D / 16;
   const int Hq = a.num_q_heads;
   const int grp = (threadIdx.x & 63) >> 4;
@@ -979,190 +959,25 @@ __device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D>
         hw[2 * nt + 1] = __builtin_bit_cast(
             uint32_t, h2_t{(_Float16)(st.acc[nt][2] * inv), (_Float16)(st.acc[nt][3] * inv)});
       }
-      // device-coherent stores (a row's in-kernel merge may run on another XCD), through a
-      // descriptor based at the wave-uniform base row's first slot
-      const size_t b0 = base_row * a.num_partitions;
-      const auto r = tile_rsrc(reinterpret_cast<const char *>(a.part_out) + b0 * D * 2,
-                               0x7fffffff);
-      const int off = (int)(row - b0) * D * 2 + grp * NT * 8;
+      uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<_Float16 *>(a.part_out) + row * D +
+                                             (size_t)grp * NT * 4);
 #pragma unroll
       for (int k = 0; k < NT / 2; ++k)
-        __builtin_amdgcn_raw_buffer_store_b128(
-            u32x4_t{hw[4 * k], hw[4 * k + 1], hw[4 * k + 2], hw[4 * k + 3]}, r, off + 16 * k, 0,
-            kCoherent);
+        dst[k] = make_uint4(hw[4 * k], hw[4 * k + 1], hw[4 * k + 2], hw[4 * k + 3]);
     } else {
-      const size_t b0 = base_row * a.num_partitions;
-      const auto r = tile_rsrc(reinterpret_cast<const char *>(a.part_out) + b0 * D * 4,
-                               0x7fffffff);
-      const int off = (int)(row - b0) * D * 4 + grp * 16;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        __builtin_amdgcn_raw_buffer_store_b128(
-            u32x4_t{__float_as_uint(st.acc[nt][0] * inv), __float_as_uint(st.acc[nt][1] * inv),
-                    __float_as_uint(st.acc[nt][2] * inv), __float_as_uint(st.acc[nt][3] * inv)},
-            r, off + 64 * nt, 0, kCoherent);
+      for (int nt = 0; nt < NT; ++nt) {
+        float4 v;
+        v.x = st.acc[nt][0] * inv;
+        v.y = st.acc[nt][1] * inv;
+        v.z = st.acc[nt][2] * inv;
+        v.w = st.acc[nt][3] * inv;
+        *reinterpret_cast<float4 *>(a.part_out + row * D + 16 * nt + 4 * grp) = v;
+      }
     }
     if (grp == 0) {
-      const size_t b0 = base_row * a.num_partitions;
-      const auto r = tile_rsrc(reinterpret_cast<const char *>(a.part_ml) + b0 * 8, 0x7fffffff);
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(st.m), __float_as_uint(l)}, r,
-                                            (int)(row - b0) * 8, 0, kCoherent);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------------------------
-// In-kernel merge.  Each arrival of a (sequence, KV head) row (a partition of its positions, or a
-// chunk of the shared prefix) stores its partials with device-coherent stores, waits until they are
-// complete, and counts itself on the row's counter with an atomic increment that wraps to zero at
-// the row's number of arrivals n: the arrival that reads n - 1 is the last, merges the row, and
-// leaves the counter at zero for the next call.  The merger reads the partials with
-// device-coherent loads, so no cache of its own XCD can hand it stale lines.
-
-// Counts this wavefront's arrival on `unit` (lane 0 does the atomic); true on the last one.
-__device__ __forceinline__ bool arrive(const DecodeArgs &a, int unit, int n) {
-  // the partial stores are complete before the count moves; the clobber keeps the compiler from
-  // moving memory accesses across
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  uint32_t old = 0u;
-  if ((threadIdx.x & 63) == 0)
-    old = __builtin_amdgcn_atomic_inc32(a.counters + unit, (uint32_t)(n - 1), __ATOMIC_RELAXED,
-                                        "agent");
-  old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
-  asm volatile("" ::: "memory");
-  return old == (uint32_t)(n - 1);
-}
-
-// The merge of row (s, h): its g query rows' n partials, M = max m_p, w_p = l_p 2^(m_p - M),
-// out = sum w_p o_p / sum w_p (times the head's v_scale where the partials are in fp8 code units),
-// the same merge the partition-reduce kernel does.  Four query rows at a time, 16 lanes per row,
-// each lane D / 16 head dims of every partial (16 bytes of fp16 partials, stored quad-permuted:
-// quads (D / 64) k .. of the row; or fp32 dims (D / 16) k ..).  Up to 64 partials: their (m, l)
-// pairs stay in registers, one per lane and 16 of them per row.  The first four partials are
-// requested with the pairs, the next four while the current four are summed.
-template <class QT, int D>
-__device__ __forceinline__ void merge_unit(const DecodeArgs &a, int s, int h, int n) {
-  constexpr int NT = D / 16;
-  constexpr int DPL = D / 16;  // head dims per lane
-  constexpr int FV = DPL / 4;  // 16-byte loads per fp32 partial and lane (fp16: half of them)
-  const int lane = threadIdx.x & 63, k = lane & 15, rq = lane >> 4;
-  const int Hq = a.num_q_heads, g = Hq / a.cache.num_kv_heads;
-  const bool half = a.part_f16 != 0;
-  const int NP = a.num_partitions;
-  float oscale = 1.0f;
-  if (half && a.part_vscale) {
-    using cfloat = const __attribute__((address_space(4))) float;
-    oscale = ((cfloat *)(uintptr_t)a.cache.v_scale)[h];
-  }
-  // one descriptor over the row's g query rows (wave-uniform), per-lane offsets inside it
-  const size_t row0 = (size_t)s * Hq + h * g;
-  const int esz = half ? 2 : 4;
-  const auto rml =
-      tile_rsrc(reinterpret_cast<const char *>(a.part_ml) + row0 * NP * 8, g * NP * 8);
-  const auto rp = tile_rsrc(reinterpret_cast<const char *>(a.part_out) + row0 * NP * D * esz,
-                            g * NP * D * esz);
-  typedef float facc_t __attribute__((ext_vector_type(DPL)));
-  for (int r0 = 0; r0 < g; r0 += 4) {
-    const int r = r0 + rq;
-    const bool rv = r < g;
-    const int rr = rv ? r : 0;
-    // lane's part of partial p (a slot past n reads slot n - 1 again; its weight is 0)
-    auto load = [&](int p, u32x4_t (&x)[FV]) {
-      const int q = rr * NP + min(p, n - 1);
-      if (half) {  // DPL halves: 16 bytes (D = 128) or 8 bytes (D = 64)
-        if constexpr (DPL == 8) {
-          x[0] = __builtin_amdgcn_raw_buffer_load_b128(rp, (q * D + DPL * k) * 2, 0, kCoherent);
-        } else {
-          const u32x2_t y =
-              __builtin_amdgcn_raw_buffer_load_b64(rp, (q * D + DPL * k) * 2, 0, kCoherent);
-          x[0] = u32x4_t{y[0], y[1], 0u, 0u};
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < FV; ++i)
-          x[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, (q * D + DPL * k) * 4 + 16 * i, 0,
-                                                       kCoherent);
-      }
-    };
-    auto add = [&](const u32x4_t (&x)[FV], float w, facc_t &acc) {
-      if (half) {
-        const _Float16 *e = reinterpret_cast<const _Float16 *>(&x[0]);
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) acc[j] += w * (float)e[j];
-      } else {
-#pragma unroll
-        for (int i = 0; i < FV; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[4 * i + j] += w * __uint_as_float(x[i][j]);
-      }
-    };
-    // (m, l) of partials k, k + 16, k + 32, k + 48 (past n: masked below)
-    float2 v[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int p = min(k + 16 * c, n - 1);
-      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(rml, (rr * NP + p) * 8, 0, kCoherent);
-      v[c] = make_float2(__uint_as_float(x[0]), __uint_as_float(x[1]));
-    }
-    u32x4_t cur[4][FV], nxt[4][FV];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) load(j, cur[j]);
-    float M = kNoMax;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (k + 16 * c < n) M = fmaxf(M, v[c].x);
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float wl[4], W = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      wl[c] = k + 16 * c < n ? v[c].y * __builtin_amdgcn_exp2f(v[c].x - M) : 0.0f;
-      W += wl[c];
-    }
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) W += __shfl_xor(W, o);
-    facc_t acc = {};
-    for (int p0 = 0; p0 < n; p0 += 4) {
-      if (p0 + 4 < n) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) load(p0 + 4 + j, nxt[j]);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int p = p0 + j;  // wave-uniform
-        const float wc = p < 16 ? wl[0] : p < 32 ? wl[1] : p < 48 ? wl[2] : wl[3];
-        add(cur[j], __shfl(wc, (lane & 48) | (p & 15)), acc);  // weight 0 past n
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < FV; ++i) cur[j][i] = nxt[j][i];
-    }
-    if (!rv) continue;
-    const float inv = W > 0.0f ? oscale / W : 0.0f;
-    auto *out = static_cast<typename QT::raw *>(a.out) + (row0 + r) * D;
-    if (half) {
-      // quad q of the stored order holds dims 16 (q % NT) + 4 (q / NT) .. + 3
-#pragma unroll
-      for (int j = 0; j < DPL / 4; ++j) {
-        const int q = (DPL / 4) * k + j;
-        const int d0 = 16 * (q % NT) + 4 * (q / NT);
-        typename QT::raw o4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] = from_f32<QT>(acc[4 * j + i] * inv);
-        *reinterpret_cast<uint2 *>(out + d0) = *reinterpret_cast<const uint2 *>(o4);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < DPL / 4; ++j) {
-        typename QT::raw o4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] = from_f32<QT>(acc[4 * j + i] * inv);
-        if constexpr (sizeof(typename QT::raw) == 4)
-          *reinterpret_cast<uint4 *>(out + DPL * k + 4 * j) = *reinterpret_cast<const uint4 *>(o4);
-        else
-          *reinterpret_cast<uint2 *>(out + DPL * k + 4 * j) = *reinterpret_cast<const uint2 *>(o4);
-      }
+      a.part_ml[row * 2] = st.m;
+      a.part_ml[row * 2 + 1] = l;
     }
   }
 }
@@ -1172,7 +987,7 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs &a, int s, int h, in
 // one workgroup run their items independently, so one wavefront's item prologue (query, table
 // fetch, first loads) and epilogue overlap the other wavefronts' block streams.
 template <class CT, class QT, int D, bool kNT, int kB, bool kApp>
-__device__ __forceinline__ bool wave_item(const DecodeArgs &a, int s_in, int h_in, int jb0_in,
+__device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int h_in, int jb0_in,
                                           int jb1_in, int end_in, int slot_in, int L_in, int tbl0,
                                           int &settle) {
   // The item is the same for the whole wavefront: keep its fields (and so the tile addresses) in
@@ -1193,9 +1008,8 @@ __device__ __forceinline__ bool wave_item(const DecodeArgs &a, int s_in, int h_i
   const int L = __builtin_amdgcn_readfirstlane(L_in);
   const bool append = kApp && end == L;
   const int e = append && L > 0 ? L - 1 : end;
-  return rows_core<CT, QT, D, kNT, kB>(a, table, h, jb0,
-                                       append ? min(jb1, (e + kBlock - 1) / kBlock) : jb1, e,
-                                       slot, s, rhq, rvalid, e, tbl0, settle, append, L);
+  rows_core<CT, QT, D, kNT, kB>(a, table, h, jb0, append ? min(jb1, (e + kBlock - 1) / kBlock) : jb1,
+                                e, slot, s, rhq, rvalid, e, tbl0, settle, append, L);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1290,39 +1104,36 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Prefix group: kPrefixTiles tiles per wavefront, each of 16 / g whole (sequence, KV head h) rows
-// (g query heads each; the tile's last 16 mod g columns are padding): tile j of the wavefront
-// holds sequences seq0 + (16 / g) j .., column c query head h*g + c % g of sequence
-// seq0 + (16 / g) j + c / g (past the batch: padding), all over prefix blocks [jb0, jb1),
-// jb1 - jb0 <= 64, whose ids are lane i's `tbl` (first_table_entries).  The whole workgroup calls
-// this with the same arguments; each block read from LDS serves all of the wavefront's tiles.
-// Each row masks the positions at or past its own context length (`lens`).  With the in-kernel
-// merge, each tile's sequences then count this chunk as one arrival.
+// Prefix group: kPrefixTiles tiles of 16 flat rows per wavefront, wavefront w taking rows
+// row0 + 16 kPrefixTiles w .. (flat row r is query head h*g + r % g of sequence r / g; rows past
+// the batch are padding), all over prefix blocks [jb0, jb1), jb1 - jb0 <= 64, whose ids are lane
+// i's `tbl` (first_table_entries).  The whole workgroup calls this with the same arguments; each
+// block read from LDS serves all of the wavefront's tiles.  Each row masks the positions at or
+// past its own context length (`lens`).
 template <class CT, class QT, int D>
-__device__ __forceinline__ uint64_t prefix_group(const DecodeArgs &a, const int *lens, int h_in,
-                                                 int seq0_in, int jb0_in, int jb1_in, int end_in,
-                                                 int slot_in, int tbl) {
+__device__ __forceinline__ void prefix_group(const DecodeArgs &a, const int *lens, int h_in,
+                                             int row0_in, int jb0_in, int jb1_in, int end_in,
+                                             int slot_in, int tbl) {
   using P = PrefixStages<CT, D>;
   constexpr int kS = P::kStages;
   constexpr int kT = kPrefixTiles;
   const int h = __builtin_amdgcn_readfirstlane(h_in);
-  const int seq0 = __builtin_amdgcn_readfirstlane(seq0_in);
+  const int row0 = __builtin_amdgcn_readfirstlane(row0_in);
   const int jb0 = __builtin_amdgcn_readfirstlane(jb0_in);
   const int jb1 = __builtin_amdgcn_readfirstlane(jb1_in);
   const int end = __builtin_amdgcn_readfirstlane(end_in);
   const int slot = __builtin_amdgcn_readfirstlane(slot_in);
   const int H = a.cache.num_kv_heads, g = a.num_q_heads / H;
-  const int upt = 16 / g;  // whole rows (sequences) per tile
   const int col = threadIdx.x & 15;
   RowState<D> st[kT];
   bool rvalid[kT];
   int rs[kT], rhq[kT], lim[kT];
 #pragma unroll
   for (int j = 0; j < kT; ++j) {
-    const int sq = seq0 + upt * j + col / g;  // past the batch: padding (a whole tile may be)
-    rvalid[j] = col < upt * g && sq < a.num_seqs;
-    rs[j] = rvalid[j] ? sq : 0;
-    rhq[j] = h * g + (rvalid[j] ? col % g : 0);
+    const int r = row0 + 16 * j + col;  // past the batch: padding (a whole tile may be padding)
+    rvalid[j] = r < a.num_seqs * g;
+    rs[j] = rvalid[j] ? r / g : 0;
+    rhq[j] = h * g + (rvalid[j] ? r % g : 0);
     lim[j] = rvalid[j] ? min(end, lens[rs[j]]) : end;
     load_query<CT, D>(a, rs[j], rhq[j], rvalid[j], st[j]);
   }
@@ -1376,23 +1187,7 @@ __device__ __forceinline__ uint64_t prefix_group(const DecodeArgs &a, const int 
 #pragma unroll
   for (int j = 0; j < kT; ++j)
     emit_rows<QT, D>(a, st[j], vscale, partial_vscale<CT, QT>(vscale), slot, rs[j], rhq[j],
-                     rvalid[j], (size_t)min(seq0 + upt * j, a.num_seqs - 1) * a.num_q_heads + h * g);
-  // In-kernel merge: one arrival per sequence of the wavefront's tiles, lane u counting sequence
-  // seq0 + u; bit u of the result: this chunk completed that sequence's row (the caller merges it).
-  if (!a.merge) return 0;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  const int lane = threadIdx.x & 63;
-  const int nu = min(kT * upt, a.num_seqs - seq0);
-  bool last = false;
-  if (lane < nu) {
-    const int n = row_partitions(a, lens[seq0 + lane]);
-    const uint32_t old = __builtin_amdgcn_atomic_inc32(a.counters + (seq0 + lane) * H + h,
-                                                       (uint32_t)(n - 1), __ATOMIC_RELAXED, "agent");
-    last = old == (uint32_t)(n - 1);
-  }
-  const uint64_t mine = __builtin_amdgcn_ballot_w64(last);
-  asm volatile("" ::: "memory");
-  return mine;
+                     rvalid[j]);
 }
 
 // Items of sequence s: plain decode, partitions of its context (an empty context counts one item,
@@ -1430,10 +1225,10 @@ __device__ __forceinline__ SeqItem sequence_item(const DecodeArgs &a, int s, int
 }
 
 template <class CT, class QT, int D, int kB, bool kApp>
-__device__ __forceinline__ bool run_sequence_item(const DecodeArgs &a, const SeqItem &it, int tbl0,
+__device__ __forceinline__ void run_sequence_item(const DecodeArgs &a, const SeqItem &it, int tbl0,
                                                   int &settle) {
-  return wave_item<CT, QT, D, PA_DECODE_NT, kB, kApp>(a, it.s, it.h, it.jb0, it.jb1, it.end,
-                                                      it.slot, it.L, tbl0, settle);
+  wave_item<CT, QT, D, PA_DECODE_NT, kB, kApp>(a, it.s, it.h, it.jb0, it.jb1, it.end, it.slot, it.L,
+                                         tbl0, settle);
 }
 
 // Lane i's table entry of the first ring chunk of a sequence item (the table entries of its first
@@ -1518,31 +1313,19 @@ void decode_mfma_kernel(DecodeArgs a) {
   if (tid == 255) prefix[S] = run;  // thread 255 holds the grand total (its chunk ends at S or later)
   __syncthreads();
 
-  // Prefix groups: list order (chunk, group, KV head) with the KV head fastest; a group is the
-  // kWaves kPrefixTiles (16 / g) sequences whose rows of one KV head fill its wavefronts' tiles.
+  // Prefix groups: list order (chunk, 64-row group, KV head) with the KV head fastest.
   const int G = gridDim.x;
-  const int upg = kWaves * kPrefixTiles * (16 / g);  // sequences per group
-  const int n_groups = kPre && a.prefix_len > 0 ? (S + upg - 1) / upg : 0;
+  constexpr int kGroupRows = 16 * kPrefixTiles * kWaves;
+  const int n_groups = kPre && a.prefix_len > 0 ? (S * g + kGroupRows - 1) / kGroupRows : 0;
   const int n_pre = n_groups * a.prefix_chunks * H;
-  // Rows this wavefront completed (in-kernel merge), merged once all its work is done, where the
-  // ring's registers are free: lane i of `pend` holds the i-th such row (s H + h).  The host turns
-  // the merge on only where no wavefront can complete more than 64 rows (decode_mfma_merge_fits).
-  int pend = 0, npend = 0;
   if constexpr (kPre) {
     for (int i = blockIdx.x; i < n_pre; i += G) {
       const int h = i % H, t = (i / H) % n_groups, c = i / (H * n_groups);
       const int start = c * kPrefixChunk;
       const int end = min(a.prefix_len, start + kPrefixChunk);
-      const int seq0 = upg * t + kPrefixTiles * (16 / g) * w;
-      uint64_t done = prefix_group<CT, QT, D>(
-          a, lens, h, seq0, start / kBlock, end / kBlock, end, c,
-          first_table_entries(a.prefix_table, start / kBlock, end / kBlock));
-      while (done) {  // at most 16 rows per group
-        const int u = __builtin_ctzll(done);
-        done &= done - 1;
-        pend = lane == npend ? (seq0 + u) * H + h : pend;
-        ++npend;
-      }
+      prefix_group<CT, QT, D>(a, lens, h, kGroupRows * t + 16 * kPrefixTiles * w, start / kBlock,
+                              end / kBlock, end, c,
+                              first_table_entries(a.prefix_table, start / kBlock, end / kBlock));
     }
   }
   // The sequences' items, one per wavefront.  Wavefronts are ranked so that those of workgroups
@@ -1594,18 +1377,10 @@ void decode_mfma_kernel(DecodeArgs a) {
         next = item_of(f + GW);
         tbl_next = item_table_entries<kB>(a, next);
       }
-      if (run_sequence_item<CT, QT, D, kB, kApp>(a, it, tbl, tbl_next)) {
-        pend = lane == npend ? it.s * H + it.h : pend;
-        ++npend;
-      }
+      run_sequence_item<CT, QT, D, kB, kApp>(a, it, tbl, tbl_next);
       it = next;
       tbl = tbl_next;
     }
-  }
-  for (int i = 0; i < npend; ++i) {
-    const int u = __builtin_amdgcn_readlane(pend, i);
-    const int s = u / H;
-    merge_unit<QT, D>(a, s, u - s * H, row_partitions(a, __builtin_amdgcn_readfirstlane(lens[s])));
   }
   if constexpr (kApp) write_token_rows<CT, QT, D>(a, rank, GW);
 }
@@ -2023,66 +1798,6 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
 }
 
 }  // namespace
-
-bool decode_mfma_persistent(const DecodeArgs &a) {
-  return a.num_seqs <= (a.prefix_len > 0 ? kMaxScanSeqsPrefix : kMaxScanSeqs);
-}
-
-namespace {
-template <class CT, class QT, int D, bool kPre, int kB, bool kApp>
-bool merge_fits_t(const DecodeArgs &a) {
-  // most rows one wavefront can complete: its items (at most ceil(items / GW), items bounded by
-  // every row having the longest context), plus 16 per prefix group its workgroup computes
-  const int64_t G = resident_groups<CT, QT, D, kPre, kB, kApp>();
-  const int64_t GW = G * kWaves;
-  const int64_t H = a.cache.num_kv_heads, g = a.num_q_heads / H;
-  const int64_t L = a.max_context_len;
-  const int64_t per_row =
-      a.prefix_len > 0 ? (L > a.prefix_len ? (L - a.prefix_len + a.partition_size - 1) /
-                                                 a.partition_size : 0)
-                       : (L > 0 ? (L + a.partition_size - 1) / a.partition_size : 1);
-  const int64_t items = (int64_t)a.num_seqs * H * per_row;
-  int64_t worst = (items + GW - 1) / GW;
-  if (a.prefix_len > 0) {
-    const int64_t upg = kWaves * kPrefixTiles * (16 / g);
-    const int64_t n_pre = (a.num_seqs + upg - 1) / upg * a.prefix_chunks * H;
-    worst += 16 * ((n_pre + G - 1) / G);
-  }
-  return worst <= 64;
-}
-
-template <class CT, class QT, int D>
-bool merge_fits_dd(const DecodeArgs &a) {
-  const bool app = a.append_slots != nullptr;
-  if (a.prefix_len > 0)
-    return app ? merge_fits_t<CT, QT, D, true, 16, true>(a) : merge_fits_t<CT, QT, D, true, 16, false>(a);
-  switch (a.cache.block_size) {
-    case 8:
-      return app ? merge_fits_t<CT, QT, D, false, 8, true>(a) : merge_fits_t<CT, QT, D, false, 8, false>(a);
-    case 32:
-      return app ? merge_fits_t<CT, QT, D, false, 32, true>(a)
-                 : merge_fits_t<CT, QT, D, false, 32, false>(a);
-    default:
-      return app ? merge_fits_t<CT, QT, D, false, 16, true>(a)
-                 : merge_fits_t<CT, QT, D, false, 16, false>(a);
-  }
-}
-
-template <class CT, class QT>
-bool merge_fits_d(const DecodeArgs &a) {
-  return a.cache.head_dim == 64 ? merge_fits_dd<CT, QT, 64>(a) : merge_fits_dd<CT, QT, 128>(a);
-}
-}  // namespace
-
-bool decode_mfma_merge_fits(const DecodeArgs &a) {
-  if (!decode_mfma_persistent(a)) return false;
-  switch (a.cache.dtype) {
-    case kF16: return merge_fits_d<f16_t, f16_t>(a);
-    case kBF16: return merge_fits_d<bf16_t, bf16_t>(a);
-    case kFP8: return merge_fits_d<fp8_t, f16_t>(a);
-    default: return false;
-  }
-}
 
 bool decode_mfma_supports_prefix(const DecodeArgs &a) {
   // the prefix groups exist only in the persistent grid

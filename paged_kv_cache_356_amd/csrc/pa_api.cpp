@@ -12,8 +12,6 @@
 
 namespace {
 
-static_assert(PA_DECODE_COUNTER_BYTES == pa::kCounterBytes, "counter region of the workspace");
-
 thread_local std::string g_last_error;
 
 pa_status fail(pa_status st, const char *fmt, ...) {
@@ -92,13 +90,11 @@ int64_t decode_slots(int32_t max_len, int32_t pt, int32_t prefix_len) {
          (max_len > prefix_len ? ceil_div(max_len - prefix_len, pt) : 0);
 }
 
-// Workspace: with more than one partition slot per row, or a shared prefix, the in-kernel
-// merge's counters (kCounterBytes), then the partials [S][Hq][slots][D] and their (m, l)
-// [S][Hq][slots][2], fp32; none otherwise.
+// Workspace: with more than one partition slot per row, or a shared prefix, the partials
+// [S][Hq][slots][D] and their (m, l) [S][Hq][slots][2], fp32; none otherwise.
 size_t partials_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int64_t slots) {
   const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)slots;
-  return pa::kCounterBytes + align256(rows * head_dim * sizeof(float)) +
-         align256(rows * 2 * sizeof(float));
+  return align256(rows * head_dim * sizeof(float)) + align256(rows * 2 * sizeof(float));
 }
 
 size_t ws_bytes_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int64_t slots,
@@ -232,8 +228,7 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
   if (q_stride == 0) q_stride = (int64_t)num_q_heads * D;
   if (q_stride < (int64_t)num_q_heads * D)
     return fail(PA_ERR_SHAPE, "%s: q_stride %lld below a row", who, (long long)q_stride);
-  if ((flags & ~(PA_DECODE_FORCE_VALU | PA_DECODE_SEPARATE_REDUCE)) != 0)
-    return fail(PA_ERR_SHAPE, "%s: unknown flags", who);
+  if ((flags & ~PA_DECODE_FORCE_VALU) != 0) return fail(PA_ERR_SHAPE, "%s: unknown flags", who);
   AppendIn ap{};
   if (app) {
     ap = *app;
@@ -321,10 +316,8 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
   if (partials) {
     char *ws = static_cast<char *>(workspace);
     const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)slots;
-    a.counters = reinterpret_cast<uint32_t *>(ws);
-    a.part_out = reinterpret_cast<float *>(ws + pa::kCounterBytes);
-    a.part_ml =
-        reinterpret_cast<float *>(ws + pa::kCounterBytes + align256(rows * D * sizeof(float)));
+    a.part_out = reinterpret_cast<float *>(ws);
+    a.part_ml = reinterpret_cast<float *>(ws + align256(rows * D * sizeof(float)));
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool use_mfma = use_prefix || (!force_valu && pa::decode_mfma_supports(a));
@@ -375,12 +368,8 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
   // units of the codes (the reduce applies the head's v_scale)
   a.part_f16 = use_mfma && q_dtype == PA_F16 ? 1 : 0;
   a.part_vscale = a.part_f16 && cdt == PA_FP8_E4M3 ? 1 : 0;
-  // The matrix-core kernel on its persistent grid merges each row's partitions itself (its last
-  // arrival does), unless the caller asks for the separate reduce kernel.
-  a.merge = partials && use_mfma && slots <= pa::kMergeMaxSlots &&
-            !(flags & PA_DECODE_SEPARATE_REDUCE) && pa::decode_mfma_merge_fits(a);
   hipError_t e = use_mfma ? pa::launch_decode_mfma(a, s) : pa::launch_decode_valu(a, s);
-  if (e == hipSuccess && !a.merge) e = pa::launch_partition_reduce(a, s);
+  if (e == hipSuccess) e = pa::launch_partition_reduce(a, s);
   return launch_status(e, who);
 }
 

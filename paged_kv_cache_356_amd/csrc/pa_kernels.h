@@ -68,12 +68,6 @@ struct DecodeArgs {
   int32_t part_vscale;      // 1: those values are in fp8 code units; the reduce applies v_scale
   float *part_ml;
   int32_t persistent;       // grid mode of the matrix-core kernel (set by its launcher)
-  // In-kernel merge (matrix-core kernel, persistent grid): every partial of a (sequence, KV head)
-  // row is stored device-coherent, then the row's counter counts it; the arrival that completes
-  // the count merges the row's partials into the output and leaves the counter at zero.  No
-  // partition-reduce launch follows.
-  int32_t merge;
-  uint32_t *counters;       // [num_seqs * num_kv_heads], zero between calls
   int32_t num_cus;          // compute units of the device (set by the launcher; 0: unknown)
   // Fused append (NULL append_slots: none): sequence s's new token, rows append_k/v + s * stride
   // (num_kv_heads * head_dim elements of q_dtype), goes to slot append_slots[s] (< 0: none), which
@@ -153,15 +147,6 @@ hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 bool decode_mfma_supports(const DecodeArgs &a);
 bool decode_mfma_supports_prefix(const DecodeArgs &a);
-bool decode_mfma_persistent(const DecodeArgs &a);  // the persistent grid (else one item per wave)
-// Whether the persistent grid can merge rows in the kernel for these arguments (no wavefront
-// completes more rows than it can hold pending); needs partition_size, prefix and append set.
-bool decode_mfma_merge_fits(const DecodeArgs &a);
-// Arrival counters of the in-kernel merge: the first kCounterBytes of a decode workspace, one per
-// (sequence, KV head) row of a persistent grid (at most 4,096 sequences x 16 KV heads).
-constexpr size_t kCounterBytes = 4096 * 16 * 4;
-// Partials per row that the in-kernel merge takes (their (m, l) pairs stay in registers).
-constexpr int kMergeMaxSlots = 64;
 hipError_t launch_prefill_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_partition_reduce(const DecodeArgs &a, hipStream_t stream);
 

@@ -138,8 +138,7 @@ class DecodeBatch:
             ws = max(ws, api.pa_decode_shared_prefix_workspace_bytes(
                 S, w.num_q_heads, H, D, self.max_context_len, self.prefix_len,
                 self.partition_size))
-        # zero-filled: its leading arrival counters must start at zero (every call leaves them so)
-        self.workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
         # use the shared-prefix decode where the workload has a prefix (run_step / run_layer)
         self.use_prefix = self.prefix_len > 0
         self.fused = False  # run_layer: one pa_decode_attention_append call instead of two

@@ -450,7 +450,7 @@ def test_fp8_cache_values_beyond_f16_range(flags):
     vp = host_pool(nb, H, D, "fp8")
     oracle.reshape_and_cache(kp, vp, "fp8", ks, vs, nb, H, D, key, val, "f32", slots)
     scale = 1.0 / math.sqrt(D)
-    ws = torch.zeros(api.pa_decode_workspace_bytes(S, Hq, H, D, max(lens), ps), dtype=torch.uint8,
+    ws = torch.empty(api.pa_decode_workspace_bytes(S, Hq, H, D, max(lens), ps), dtype=torch.uint8,
                      device="cuda")
     out = torch.empty_like(qt)
     api.pa_decode_attention(out, qt, cache, torch.from_numpy(tables).cuda(),
@@ -473,10 +473,8 @@ def test_fp8_cache_values_beyond_f16_range(flags):
 
 def test_stale_workspace_never_leaks():
     """Workspace slots past a row's own partitions hold whatever earlier calls left there and must
-    never be read: a workspace whose partials region is full of NaN bytes gives the same bits as a
-    zeroed one, for the plain and the shared-prefix decode, with rows of 1, several and all the
-    partitions, merged in the decode kernel and by the separate reduce; the leading counters are
-    zero after every call."""
+    never be read: a workspace full of NaN bytes gives the same bits as a zeroed one, for the plain
+    and the shared-prefix decode, with rows of 1, several and all the partitions."""
     _say("NaN-filled workspace")
     for name, lengths, ps in (("f16_batch32", [1000, 17, 513, 64, 250], 64),
                               ("f16_shared_prefix_batch256", [64 + 1, 64 + 300, 64 + 17, 64 + 2],
@@ -486,19 +484,16 @@ def test_stale_workspace_never_leaks():
             kw["prefix_len"] = 64
         w = wl.WORKLOADS[name].replace(**kw)
         b = DecodeBatch(w, lengths=lengths, pad_block=0, partition_size=ps)
-        C = api.PA_DECODE_COUNTER_BYTES
-        for flags in (api.PA_DECODE_DEFAULT, api.PA_DECODE_SEPARATE_REDUCE):
-            outs = []
-            for fill in (0, POISON):
-                b.workspace[C:].fill_(fill)
-                b.sets[0].out[0].fill_(0)
-                b.decode(0, 0, flags=flags)
-                torch.cuda.synchronize()
-                outs.append(b.sets[0].out[0].clone())
-                assert int(b.workspace[:C].count_nonzero()) == 0
-            _say(f"  {name}, flags {flags}: equal {torch.equal(outs[0], outs[1])}")
-            assert torch.isfinite(outs[1].float()).all()
-            assert torch.equal(outs[0], outs[1])
+        outs = []
+        for fill in (0, POISON):
+            b.workspace.fill_(fill)
+            b.sets[0].out[0].fill_(0)
+            b.decode(0, 0)
+            torch.cuda.synchronize()
+            outs.append(b.sets[0].out[0].clone())
+        _say(f"  {name}: equal {torch.equal(outs[0], outs[1])}")
+        assert torch.isfinite(outs[1].float()).all()
+        assert torch.equal(outs[0], outs[1])
 
 
 def test_swap_out_and_in_round_trip():
@@ -710,9 +705,6 @@ def test_fused_append_matches_oracle(name, flags, D):
     b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON,
                     lengths=SMALL_LENGTHS.get(name), partition_size=0 if name != "bf16_32k_batch8" else 512)
     b.fused = True
-    if w.prefix_len and flags == api.PA_DECODE_FORCE_VALU:
-        _refused_append_writes_nothing(b)
-        return
     ob = OracleBatch(b, pad, pool_fill=POISON)
     ob.metadata_matches(b)
     for l in b.layers:
@@ -720,37 +712,6 @@ def test_fused_append_matches_oracle(name, flags, D):
         kp, vp, _, _ = ob.pools[(l, 0)]
         dk, dv = device_pool_bytes(b.caches[l])
         assert np.array_equal(dk, kp.view(np.uint8)) and np.array_equal(dv, vp.view(np.uint8))
-
-
-def _refused_append_writes_nothing(b, flags=api.PA_DECODE_FORCE_VALU):
-    """A shared-prefix append off the prefix path (vector-ALU kernel, or more sequences than the
-    prefix groups take) is refused with PA_ERR_UNSUPPORTED before anything is enqueued: the pools
-    keep every byte."""
-    b.copy(0)
-    torch.cuda.synchronize()
-    before = [device_pool_bytes(b.caches[l]) for l in b.layers]
-    for l in b.layers:
-        with pytest.raises(api.PaError) as e:
-            b.decode(0, l, flags=flags, append=True)
-        assert e.value.status == -3
-    torch.cuda.synchronize()
-    for l, (k0, v0) in zip(b.layers, before):
-        k1, v1 = device_pool_bytes(b.caches[l])
-        assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
-
-
-def test_fused_append_shared_prefix_refused_beyond_the_prefix_groups():
-    """More sequences than the prefix groups' scan takes (2,048): the shared-prefix append has no
-    path that keeps a context ending inside the prefix from writing into it, so it is refused and
-    nothing is written; the two calls (reshape_and_cache + the shared-prefix decode, which falls back
-    to the plain decode) remain available."""
-    S = 2050
-    lengths = np.full(S, 64 + 3, np.int32)
-    w = _reduced("f16_shared_prefix_batch256", num_seqs=S, num_blocks=8192, num_layers=1)
-    _say(f"fused append refused, shared prefix, {S} sequences")
-    b = DecodeBatch(w, pad_block=0, lengths=lengths)
-    b.fused = True
-    _refused_append_writes_nothing(b, flags=api.PA_DECODE_DEFAULT)
 
 
 @pytest.mark.parametrize("B", [8, 16, 32])
