@@ -705,6 +705,9 @@ def test_fused_append_matches_oracle(name, flags, D):
     b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON,
                     lengths=SMALL_LENGTHS.get(name), partition_size=0 if name != "bf16_32k_batch8" else 512)
     b.fused = True
+    if w.prefix_len and flags == api.PA_DECODE_FORCE_VALU:
+        _refused_append_writes_nothing(b)
+        return
     ob = OracleBatch(b, pad, pool_fill=POISON)
     ob.metadata_matches(b)
     for l in b.layers:
@@ -712,6 +715,37 @@ def test_fused_append_matches_oracle(name, flags, D):
         kp, vp, _, _ = ob.pools[(l, 0)]
         dk, dv = device_pool_bytes(b.caches[l])
         assert np.array_equal(dk, kp.view(np.uint8)) and np.array_equal(dv, vp.view(np.uint8))
+
+
+def _refused_append_writes_nothing(b, flags=api.PA_DECODE_FORCE_VALU):
+    """A shared-prefix append off the prefix path (vector-ALU kernel, or more sequences than the
+    prefix groups take) is refused with PA_ERR_UNSUPPORTED before anything is enqueued: the pools
+    keep every byte."""
+    b.copy(0)
+    torch.cuda.synchronize()
+    before = [device_pool_bytes(b.caches[l]) for l in b.layers]
+    for l in b.layers:
+        with pytest.raises(api.PaError) as e:
+            b.decode(0, l, flags=flags, append=True)
+        assert e.value.status == -3
+    torch.cuda.synchronize()
+    for l, (k0, v0) in zip(b.layers, before):
+        k1, v1 = device_pool_bytes(b.caches[l])
+        assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+
+
+def test_fused_append_shared_prefix_refused_beyond_the_prefix_groups():
+    """More sequences than the prefix groups' scan takes (2,048): the shared-prefix append has no
+    path that keeps a context ending inside the prefix from writing into it, so it is refused and
+    nothing is written; the two calls (reshape_and_cache + the shared-prefix decode, which falls back
+    to the plain decode) remain available."""
+    S = 2050
+    lengths = np.full(S, 64 + 3, np.int32)
+    w = _reduced("f16_shared_prefix_batch256", num_seqs=S, num_blocks=8192, num_layers=1)
+    _say(f"fused append refused, shared prefix, {S} sequences")
+    b = DecodeBatch(w, pad_block=0, lengths=lengths)
+    b.fused = True
+    _refused_append_writes_nothing(b, flags=api.PA_DECODE_DEFAULT)
 
 
 @pytest.mark.parametrize("B", [8, 16, 32])
