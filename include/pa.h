@@ -198,6 +198,30 @@ pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int
                               size_t workspace_bytes, uint32_t flags, void *stream);
 
 /*
+ * pa_decode_attention_noalloc — pa_decode_attention without a workspace argument, for callers that
+ * cannot allocate device memory around the call: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The split-K partials go to a fixed scratch array of
+ * PA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on each GPU it runs on until the
+ * process ends; the call itself allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine) and its first call on a device looks up that device's copy of the array.
+ *   All arguments and results are those of pa_decode_attention (same kernels, same partition
+ *   sizes, bit-identical output).
+ *   A call whose partials need more than PA_NOALLOC_SCRATCH_BYTES (the need is at most
+ *   pa_decode_workspace_bytes() for the same sizes) returns PA_ERR_WORKSPACE before touching the
+ *   device; so do all the argument errors of pa_decode_attention.
+ *   Every call on one GPU shares that GPU's scratch, and nothing in it needs to start at zero
+ *   (each call reads only the partials it wrote): calls that overlap on one GPU (different streams
+ *   or threads without ordering) race; order them yourself.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pa_status pa_decode_attention_noalloc(void *out, const void *query, int32_t q_dtype,
+                                      int64_t q_stride, const pa_cache *cache,
+                                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t *context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_context_len, float scale,
+                                      int32_t partition_size, uint32_t flags, void *stream);
+
+/*
  * pa_decode_attention_shared_prefix — pa_decode_attention for a batch whose sequences all begin
  * with the same prefix_len positions stored in the same physical blocks: several requests share a
  * prompt prefix and their block tables point at one copy of it ([Visualized] Part 3, shared

@@ -19,6 +19,7 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_BLOCK_SIZE = 16
 PA_DECODE_DEFAULT = 0
 PA_DECODE_FORCE_VALU = 1
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20  # the fixed device scratch of pa_decode_attention_noalloc
 DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
 TORCH_CODES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 ELEM_BYTES = {PA_F32: 4, PA_F16: 2, PA_BF16: 2, PA_FP8_E4M3: 1}
@@ -32,7 +33,7 @@ EXPORTS = [
     "pa_calibrate_read",
     "pa_pool_bytes", "pa_reshape_and_cache", "pa_decode_auto_partition",
     "pa_decode_workspace_bytes", "pa_decode_attention", "pa_decode_attention_shared_prefix",
-    "pa_decode_attention_append",
+    "pa_decode_attention_append", "pa_decode_attention_noalloc",
     "pa_decode_shared_prefix_workspace_bytes", "pa_copy_blocks", "pa_check_copy_pairs",
     "pa_prefill_attention", "pa_swap_blocks", "pa_bm_set_host_blocks", "pa_bm_swap_out",
     "pa_bm_swap_in",
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
             "pa_decode_attention_append": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _vp, _i64, _i64,
                                                    _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp,
                                                    _i32, _i32, _vp, _sz, _u32, _vp]),
+            "pa_decode_attention_noalloc": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _i32, _vp,
+                                                    _i32, _i32, _i32, _f32, _i32, _u32, _vp]),
             "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32,
                                                               _i32]),
             "pa_copy_blocks": (_i32, [_cp, _i32, _vp, _i32, _vp]),
@@ -299,6 +302,24 @@ def pa_decode_attention(out: torch.Tensor, query: torch.Tensor, cache: KVCache,
     block_tables int32 [S, max_blocks_per_seq]; context_lens int32 [S]."""
     DecodeCall(out, query, cache, block_tables, context_lens, max_context_len, scale,
                partition_size, workspace, flags)(stream)
+
+
+def pa_decode_attention_noalloc(out: torch.Tensor, query: torch.Tensor, cache: KVCache,
+                                block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                max_context_len: int, scale: float, partition_size: int = 0,
+                                flags: int = PA_DECODE_DEFAULT, stream=None) -> None:
+    """pa_decode_attention with the partials in the library's fixed device scratch (no workspace
+    argument, nothing allocated by the call)."""
+    S, Hq, D = query.shape
+    assert out.shape == query.shape and out.dtype == query.dtype and out.is_contiguous()
+    assert query.stride(2) == 1 and query.stride(1) == D
+    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous()
+    assert context_lens.dtype == torch.int32 and context_lens.is_contiguous()
+    _check(lib().pa_decode_attention_noalloc(
+        _ptr(out), _ptr(query), TORCH_CODES[query.dtype], query.stride(0) if S else 0,
+        ctypes.byref(cache.struct()), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        S, Hq, int(max_context_len), float(scale), int(partition_size), int(flags),
+        _stream(stream)))
 
 
 def pa_decode_attention_append(out: torch.Tensor, query: torch.Tensor, cache: KVCache,

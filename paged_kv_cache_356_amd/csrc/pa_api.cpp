@@ -12,6 +12,8 @@
 
 namespace {
 
+static_assert(PA_NOALLOC_SCRATCH_BYTES == pa::kNoAllocScratchBytes, "no-alloc scratch size");
+
 thread_local std::string g_last_error;
 
 pa_status fail(pa_status st, const char *fmt, ...) {
@@ -189,13 +191,15 @@ struct AppendIn {
 
 // Validation and dispatch shared by the plain and the shared-prefix decode, with or without the
 // fused append.
+// noalloc: the partials go to the library's fixed device scratch (pa_decode_attention_noalloc);
+// workspace / workspace_bytes are then ignored.
 pa_status decode_common(const char *who, void *out, const void *query, int32_t q_dtype,
                         int64_t q_stride, const pa_cache *cache, const int32_t *block_tables,
                         int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
                         int32_t num_q_heads, int32_t max_context_len, float scale,
                         const int32_t *prefix_table, int32_t prefix_len, int32_t partition_size,
                         void *workspace, size_t workspace_bytes, uint32_t flags, void *stream,
-                        const AppendIn *app = nullptr) {
+                        const AppendIn *app = nullptr, bool noalloc = false) {
   pa_status st = check_cache(cache, who);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_seqs > 65535)
@@ -301,6 +305,23 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
   const int64_t slots = decode_slots(max_len, pt, use_prefix ? prefix_len : 0);
   const bool partials = use_prefix || slots > 1;
   const size_t need = ws_bytes_for(num_seqs, num_q_heads, D, slots, partials);
+  if (noalloc) {
+    if (need > pa::kNoAllocScratchBytes)
+      return fail(PA_ERR_WORKSPACE,
+                  "%s: the call needs %zu bytes of scratch, above the fixed %zu (use "
+                  "pa_decode_attention with a workspace, or fewer sequences or a larger "
+                  "partition_size)",
+                  who, need, pa::kNoAllocScratchBytes);
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      const hipError_t e = pa::noalloc_scratch(&workspace);
+      if (e != hipSuccess)
+        return fail(PA_ERR_LAUNCH, "%s: device scratch lookup failed: %s", who,
+                    hipGetErrorString(e));
+      workspace_bytes = pa::kNoAllocScratchBytes;
+    }
+  }
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
                 need);
@@ -387,6 +408,18 @@ pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int
                        max_blocks_per_seq, context_lens, num_seqs, num_q_heads, max_context_len,
                        scale, nullptr, 0, partition_size, workspace, workspace_bytes, flags,
                        stream);
+}
+
+pa_status pa_decode_attention_noalloc(void *out, const void *query, int32_t q_dtype,
+                                      int64_t q_stride, const pa_cache *cache,
+                                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t *context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_context_len, float scale,
+                                      int32_t partition_size, uint32_t flags, void *stream) {
+  return decode_common("pa_decode_attention_noalloc", out, query, q_dtype, q_stride, cache,
+                       block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                       max_context_len, scale, nullptr, 0, partition_size, nullptr, 0, flags,
+                       stream, nullptr, true);
 }
 
 pa_status pa_decode_attention_shared_prefix(void *out, const void *query, int32_t q_dtype,

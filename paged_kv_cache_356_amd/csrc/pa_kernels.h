@@ -140,6 +140,11 @@ struct SwapArgs {
   int32_t to_host;
 };
 
+// Fixed device scratch of pa_decode_attention_noalloc (scratch.hip): its size, and the current
+// device's address of it (looked up once per device; no allocation).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 hipError_t launch_reshape_and_cache(const ReshapeArgs &a, hipStream_t stream);
 hipError_t launch_swap_blocks(const SwapArgs &a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs &a, hipStream_t stream);
