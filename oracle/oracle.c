@@ -77,8 +77,9 @@ double orc_e4m3_to_f64(uint8_t c) {
 
 /* Encode a binary32 value as E4M3FN: nearest representable value, ties to the even code (even
  * fraction), magnitudes at or above the largest finite value 448 saturate to 448, NaN -> 0x7F with
- * the sign bit of the input.  Done by scanning the 127 non-negative finite codes, whose values
- * increase with the code. */
+ * the sign bit of the input.  The 127 non-negative finite codes 0x00 .. 0x7E have values that
+ * increase with the code, so the largest code whose value does not exceed |x| is found by bisection
+ * over them (the decoder above gives each code's value). */
 uint8_t orc_e4m3_from_f32(float x) {
   uint32_t bits;
   memcpy(&bits, &x, sizeof bits);
@@ -86,9 +87,12 @@ uint8_t orc_e4m3_from_f32(float x) {
   if (isnan(x)) return (uint8_t)(sign | 0x7F);
   double a = fabs((double)x);
   if (a >= 448.0) return (uint8_t)(sign | 0x7E);
-  int lo = 0; /* largest code with value <= a */
-  for (int c = 0; c <= 0x7E; ++c) {
-    if (orc_e4m3_to_f64((uint8_t)c) <= a) lo = c;
+  /* largest code with value <= a: value(lo) <= a < value(hi) holds throughout (value(0) = 0) */
+  int lo = 0, hi = 0x7F;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (orc_e4m3_to_f64((uint8_t)mid) <= a) lo = mid;
+    else hi = mid;
   }
   int code = lo;
   if (lo < 0x7E) {
