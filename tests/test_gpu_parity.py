@@ -854,11 +854,37 @@ def test_fused_append_skips_slots_outside_the_pool():
         assert err <= TOL[w.cache_dtype]
 
 
-# --------------------------------------------------------------------------- full sizes, sampled
-@pytest.mark.parametrize("name", ["f16_batch32", "bf16_32k_batch8", "f16_shared_prefix_batch256", "fp8_28layer_batch512"])
-def test_full_size_workloads_sampled(name):
+# --------------------------------------------------------------------------- full sizes
+FULL = ["f16_batch32", "bf16_32k_batch8", "f16_shared_prefix_batch256"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workloads_every_row(name):
+    """The workload at its full size, in the launch configuration the benchmark times (automatic
+    partition size or the workload's own, the shared-prefix decode for the prefix batch): every
+    (sequence, query head) output against the oracle, and both pools byte for byte."""
     w = wl.WORKLOADS[name]
-    layers = [0, w.num_layers - 1] if w.num_layers > 1 else [0]
+    _say(f"{name} full size, every row")
+    pad = _pad_block(w)
+    b = DecodeBatch(w, keep_values=True, pad_block=pad)
+    ob = OracleBatch(b, pad)
+    ob.metadata_matches(b)
+    _check_batch(b, ob, 0, TOL[w.cache_dtype])
+    kp, vp, _, _ = ob.pools[(0, 0)]
+    dk, dv = device_pool_bytes(b.caches[0])
+    assert np.array_equal(dk, kp.view(np.uint8)) and np.array_equal(dv, vp.view(np.uint8))
+    ob.pools.clear()
+    del b
+    torch.cuda.empty_cache()
+
+
+def test_full_size_fp8_28_layers_sampled():
+    """The 28-layer fp8 batch at full size (about 200 GB of pools), layers 0 and 27: 64 sampled
+    sequences (the longest and the shortest among them) x every query head against the oracle,
+    and the cache bytes of every block those sequences reference."""
+    name = "fp8_28layer_batch512"
+    w = wl.WORKLOADS[name]
+    layers = [0, w.num_layers - 1]
     _say(f"{name} full size, layers {layers}")
     pad = _pad_block(w)
     b = DecodeBatch(w, keep_values=True, pad_block=pad, layers=layers)
@@ -866,17 +892,17 @@ def test_full_size_workloads_sampled(name):
     ob.metadata_matches(b)
     L = b.lengths
     g = np.random.default_rng(17)
-    seqs = sorted({int(np.argmax(L)), int(np.argmin(L)), *g.choice(len(L), 4, replace=False).tolist()})
-    heads = [0, w.num_q_heads - 1, int(g.integers(w.num_q_heads))]
+    seqs = sorted({int(np.argmax(L)), int(np.argmin(L)),
+                   *g.choice(len(L), 62, replace=False).tolist()})
+    assert len(seqs) >= 63
+    heads = list(range(w.num_q_heads))
     sel = (np.repeat(seqs, len(heads)), np.tile(heads, len(seqs)))
     for l in layers:
         _check_batch(b, ob, l, TOL[w.cache_dtype], sel=sel, owners=set(seqs))
-        # bit-exact cache contents on every block the sampled sequences reference
         kp, vp, _, _ = ob.pools[(l, 0)]
         dk, dv = device_pool_bytes(b.caches[l])
         H, D = w.num_kv_heads, w.head_dim
-        e = {"f16": 2, "bf16": 2, "fp8": 1, "f32": 4}[w.cache_dtype]
-        span = H * 16 * D * e
+        span = H * 16 * D  # fp8: one byte per element
         for s in seqs:
             for j in range(math.ceil(int(L[s]) / 16)):
                 blk = int(ob.sets[0]["tables"][s, j])
@@ -886,3 +912,40 @@ def test_full_size_workloads_sampled(name):
         ob.pools.clear()
     del b
     torch.cuda.empty_cache()
+
+
+def test_wide_partition_reduce_every_row():
+    """A batch whose partition merge takes the reduce's wide variant (1,025 to 2,048 query rows with
+    more than 16 partitions: 40 sequences of up to 8,192 positions in 256-position partitions, 1,120
+    rows): every row against the oracle."""
+    lengths = [8192, 8191, 4097, 6000, 7777, 8000] + [4000 + 97 * i for i in range(34)]
+    S = len(lengths)
+    w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=S, num_blocks=S * 512 + 64)
+    assert api.pa_decode_auto_partition(S, w.num_kv_heads, max(lengths)) == 256
+    assert 1024 < S * w.num_q_heads <= 2048 and math.ceil(max(lengths) / 256) > 16
+    _say(f"wide partition reduce: {S} sequences, {S * w.num_q_heads} rows")
+    pad = _pad_block(w)
+    b = DecodeBatch(w, keep_values=True, pad_block=pad, lengths=lengths)
+    ob = OracleBatch(b, pad)
+    _check_batch(b, ob, 0, TOL["f16"])
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("flags", [api.PA_DECODE_DEFAULT, api.PA_DECODE_FORCE_VALU])
+def test_fp8_cache_with_bf16_queries(flags, D):
+    """An fp8 cache read by bf16 queries (the vector-ALU kernel takes that pair), two layers of the
+    reduced 28-layer batch with several partitions per row: attention within the fp8 tolerance, the
+    cache writes bit-exact over the whole pools."""
+    w = wl.WORKLOADS["fp8_28layer_batch512"].replace(**SMALL["fp8_28layer_batch512"],
+                                                      q_dtype="bf16", head_dim=D)
+    _say(f"fp8 cache, bf16 queries, head_dim {D}, flags {flags}")
+    pad = _pad_block(w)
+    b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON,
+                    lengths=SMALL_LENGTHS["fp8_28layer_batch512"])
+    ob = OracleBatch(b, pad, pool_fill=POISON)
+    ob.metadata_matches(b)
+    for l in b.layers:
+        _check_batch(b, ob, l, TOL["fp8"], flags=flags)
+        kp, vp, _, _ = ob.pools[(l, 0)]
+        dk, dv = device_pool_bytes(b.caches[l])
+        assert np.array_equal(dk, kp.view(np.uint8)) and np.array_equal(dv, vp.view(np.uint8))
