@@ -353,6 +353,34 @@ pa_status pa_copy_blocks(const pa_cache *layers, int32_t num_layers, const int32
 pa_status pa_check_copy_pairs(const int32_t *block_pairs_host, int32_t num_pairs,
                               int32_t num_blocks);
 
+/* Host-side check of a HOST copy of a slot_mapping: PA_ERR_ALIAS when two tokens name the same
+ * slot (a race in pa_reshape_and_cache); slots that are negative or past the pool are skipped, as
+ * the kernels skip them. */
+pa_status pa_check_slots(const int64_t *slots_host, int32_t num_tokens, int32_t num_blocks,
+                         int32_t block_size);
+
+/* Host-side check of a HOST copy of context_lens: PA_ERR_SHAPE when a length is negative or above
+ * max_context_len (the host bound that sizes the decode's launch). */
+pa_status pa_check_context_lens(const int32_t *context_lens_host, int32_t num_seqs,
+                                int32_t max_context_len);
+
+/*
+ * Debug checks (PA_DEBUG).  Off by default; on when the environment variable PA_DEBUG is set to a
+ * non-zero value at the library's first use, or after pa_set_debug(1).  With them on, before
+ * anything is enqueued:
+ *   pa_reshape_and_cache and pa_decode_attention_append copy slot_mapping to the host and run
+ *     pa_check_slots (repeated slots: PA_ERR_ALIAS);
+ *   pa_copy_blocks copies block_pairs to the host and runs pa_check_copy_pairs (PA_ERR_ALIAS,
+ *     PA_ERR_SHAPE);
+ *   every decode entry point copies context_lens to the host and runs pa_check_context_lens
+ *     (PA_ERR_SHAPE).
+ * The copies wait for the stream to reach the call (hipStreamSynchronize), so debug mode gives up
+ * the library's rule of never synchronising; a failed check enqueues nothing.  The switch is
+ * process-wide.
+ */
+void pa_set_debug(int on);
+int pa_debug_enabled(void);
+
 /*
  * pa_swap_blocks — evicting blocks to CPU memory and bringing them back, the KV cache's swapping
  * to disk ([Visualized] Part 3, the OS-to-PagedAttention table and the paragraph after it).  For

@@ -35,6 +35,7 @@ EXPORTS = [
     "pa_decode_workspace_bytes", "pa_decode_attention", "pa_decode_attention_shared_prefix",
     "pa_decode_attention_append", "pa_decode_attention_noalloc",
     "pa_decode_shared_prefix_workspace_bytes", "pa_copy_blocks", "pa_check_copy_pairs",
+    "pa_check_slots", "pa_check_context_lens", "pa_set_debug", "pa_debug_enabled",
     "pa_prefill_attention", "pa_swap_blocks", "pa_bm_set_host_blocks", "pa_bm_swap_out",
     "pa_bm_swap_in",
     "pa_bm_num_free_host", "pa_bm_is_swapped",
@@ -91,6 +92,10 @@ def lib() -> ctypes.CDLL:
                                                               _i32]),
             "pa_copy_blocks": (_i32, [_cp, _i32, _vp, _i32, _vp]),
             "pa_check_copy_pairs": (_i32, [_vp, _i32, _i32]),
+            "pa_check_slots": (_i32, [_vp, _i32, _i32, _i32]),
+            "pa_check_context_lens": (_i32, [_vp, _i32, _i32]),
+            "pa_set_debug": (None, [ctypes.c_int]),
+            "pa_debug_enabled": (ctypes.c_int, []),
             "pa_swap_blocks": (_i32, [_cp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp]),
             "pa_prefill_attention": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _i32, _vp, _vp, _i32,
                                             _i32, _i32, _i32, _i32, _f32, _vp]),
@@ -450,6 +455,25 @@ def pa_swap_blocks(caches: list[KVCache], host: HostPools, block_pairs: torch.Te
     """block_pairs: int32 [P, 2] of (device block, host slot) in device or pinned host memory; every
     layer in `caches` is copied to its host pools (to_host) or back."""
     SwapCall(caches, host, block_pairs, to_host)(stream)
+
+
+def pa_check_slots(slots: np.ndarray, num_blocks: int, block_size: int = PA_BLOCK_SIZE) -> None:
+    slots = np.ascontiguousarray(slots, np.int64)
+    _check(lib().pa_check_slots(_ptr(slots), slots.shape[0], num_blocks, block_size))
+
+
+def pa_check_context_lens(context_lens: np.ndarray, max_context_len: int) -> None:
+    lens = np.ascontiguousarray(context_lens, np.int32)
+    _check(lib().pa_check_context_lens(_ptr(lens), lens.shape[0], int(max_context_len)))
+
+
+def pa_set_debug(on: bool) -> None:
+    """The library's PA_DEBUG checks on or off, process-wide."""
+    lib().pa_set_debug(1 if on else 0)
+
+
+def pa_debug_enabled() -> bool:
+    return bool(lib().pa_debug_enabled())
 
 
 def pa_check_copy_pairs(pairs: np.ndarray, num_blocks: int) -> None:

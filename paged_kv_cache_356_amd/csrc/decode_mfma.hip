@@ -30,11 +30,12 @@
 //
 // Probabilities are split p = hi + lo with hi, lo in the MFMA input type, and both parts go through
 // the PV product: the result then carries p to ~2^-16 (bf16) or ~2^-22 (f16) relative accuracy, not
-// the 2^-8 / 2^-11 of a single rounding.
+// the 2^-8 / 2^-11 of a single rounding.  (Measured on MI355X: a single rounding is not faster on
+// any workload, the fp8 28-layer batch 2% slower, and its errors are several times larger.)
 //
-// fp8 (E4M3FN) caches compute in f16: byte c becomes the binary16 with bits
-// (c & 0x80) << 8 | (c & 0x7f) << 7, whose value is exactly decode(c) * 2^-8 (normals and
-// subnormals alike); the 2^8 goes back into the per-head scales.  The NaN code is mapped to a NaN.
+// fp8 (E4M3FN) caches compute in f16: the hardware conversion widens four codes to their exact
+// binary16 values (every E4M3FN value is one), the per-head scales multiplying the logits (K) and
+// the output (V).
 //
 // Work items: a wavefront takes one (sequence, partition, KV head) at a time and streams the
 // partition's blocks through a ring of register fragments, keeping the loads of its next blocks in
@@ -58,33 +59,21 @@ constexpr int kMaxScanSeqs = 4096;  // persistent grid: sequences whose item pre
 // The shared-prefix instantiation also holds the prefix groups' block stages in LDS; its scan
 // arrays are halved so that three workgroups still fit on a compute unit.
 constexpr int kMaxScanSeqsPrefix = 2048;
-#ifndef PA_PREFIX_TILES
-#define PA_PREFIX_TILES 1
-#endif
 // 16-row tiles per wavefront in a prefix group: each block staged in LDS serves 16 kPrefixTiles
-// rows per wavefront, so the group's L2 reads of the prefix fall with the group's size.
-constexpr int kPrefixTiles = PA_PREFIX_TILES;
-#ifndef PA_DECODE_BUFS
-#define PA_DECODE_BUFS 2
-#endif
-#ifndef PA_FP8_BUFS
-#define PA_FP8_BUFS 3
-#endif
-#ifndef PA_DECODE_NT
-#define PA_DECODE_NT 1
-#endif
-#ifndef PA_SPREAD
-#define PA_SPREAD 0
-#endif
-// The plain decode's fused-append instantiation runs at two wavefronts per SIMD (256 registers,
-// no spills): measured level with the plain decode on the 32K batch and faster than three per
-// SIMD on the others; the shared-prefix one keeps three (its grid needs three workgroups per CU).
-#ifndef PA_APPEND_OCC
-#define PA_APPEND_OCC 2
-#endif
-#ifndef PA_DECODE_OCC
-#define PA_DECODE_OCC 3  // at least this many wavefronts per SIMD (caps registers at 168)
-#endif
+// rows per wavefront (two tiles spill registers at three workgroups per compute unit).
+constexpr int kPrefixTiles = 1;
+// Blocks in flight per wavefront in the ring: two 16-bit fragments, or three fp8 ones (half the
+// registers each).  Deeper rings at fewer wavefronts per SIMD measured slower.
+constexpr int kDecodeBufs = 2;
+constexpr int kFp8Bufs = 3;
+// K/V tiles of the sequences' own blocks are read once per call: non-temporal loads.
+constexpr bool kDecodeNT = true;
+// Wavefronts per SIMD the instantiations are built for (registers capped at 512 / occupancy): three
+// (168 registers); the plain decode's fused-append instantiation two (256 registers, no spills),
+// measured level with the plain decode on the 32K batch and faster than three on the others; the
+// shared-prefix one keeps three (its grid needs three workgroups per compute unit).
+constexpr int kDecodeOcc = 3;
+constexpr int kAppendOcc = 2;
 
 // K/V tiles are read with raw buffer loads through a descriptor per tile: a slot with no block
 // gets a descriptor of length 0, whose loads return zeros without touching memory (and still count
@@ -162,37 +151,14 @@ __device__ __forceinline__ float unpack_hi(uint32_t v) {
   else return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
-#ifndef PA_FP8_HWCVT
-#define PA_FP8_HWCVT 1
-#endif
-// Scale that the f16 values produced from fp8 codes carry: 2^-8 for the bit mapping below, 1 for
-// the hardware conversion.
-constexpr float kFp8Unscale = PA_FP8_HWCVT ? 1.0f : 256.0f;
-
-// Four E4M3FN bytes (byte 0 first) -> four binary16 values equal to decode(byte) * 2^-8, or, with
-// the hardware conversion (v_cvt_scalef32_pk_f16_fp8 at scale 1), equal to decode(byte).
+// Four E4M3FN bytes (byte 0 first) -> four binary16 values equal to decode(byte), by the hardware
+// conversion v_cvt_scalef32_pk_f16_fp8 at scale 1 (exact for all 256 codes, checked on the GPU;
+// the NaN code gives a NaN).
 __device__ __forceinline__ uint2 e4m3x4_to_f16x4(uint32_t x) {
-#if PA_FP8_HWCVT
   uint2 r;
   r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
   r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true));
   return r;
-#else
-  const uint32_t t01 = ((x & 0xffu) << 8) | ((x & 0xff00u) << 16);
-  const uint32_t t23 = ((x >> 8) & 0xff00u) | (x & 0xff000000u);
-  uint2 r;
-  r.x = (t01 & 0x80008000u) | ((t01 >> 1) & 0x3f803f80u);
-  r.y = (t23 & 0x80008000u) | ((t23 >> 1) & 0x3f803f80u);
-  // A byte whose low 7 bits are all ones is the NaN code: give it a binary16 NaN.
-  const uint32_t y = x & 0x7f7f7f7fu;
-  if (__builtin_expect(((y + 0x01010101u) & 0x80808080u) != 0u, 0)) {
-    if ((y & 0x7fu) == 0x7fu) r.x |= 0x7e00u;
-    if ((y & 0x7f00u) == 0x7f00u) r.x |= 0x7e000000u;
-    if ((y & 0x7f0000u) == 0x7f0000u) r.y |= 0x7e00u;
-    if ((y & 0x7f000000u) == 0x7f000000u) r.y |= 0x7e000000u;
-  }
-  return r;
-#endif
 }
 
 template <class CT, int D>
@@ -478,7 +444,7 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs &a, const int32_t
                                               float kscale, RowState<D> &st) {
   using F = Frag<CT, D>;
   // blocks per wavefront in the load ring: fp8 fragments are half the registers of 16-bit ones
-  constexpr int kBufs = std::is_same<CT, fp8_t>::value ? PA_FP8_BUFS : PA_DECODE_BUFS;
+  constexpr int kBufs = std::is_same<CT, fp8_t>::value ? kFp8Bufs : kDecodeBufs;
   constexpr int kCS = BlockSteps<kB>::kChunk;
   const int nb = a.cache.num_blocks;
   const int lane = threadIdx.x & 63;
@@ -564,8 +530,8 @@ __device__ __forceinline__ void head_scales(const DecodeArgs &a, int h, float &k
   vscale = 1.0f;
   if constexpr (std::is_same<CT, fp8_t>::value) {
     using cfloat = const __attribute__((address_space(4))) float;
-    kscale *= ((cfloat *)(uintptr_t)a.cache.k_scale)[h] * kFp8Unscale;
-    vscale = ((cfloat *)(uintptr_t)a.cache.v_scale)[h] * kFp8Unscale;
+    kscale *= ((cfloat *)(uintptr_t)a.cache.k_scale)[h];
+    vscale = ((cfloat *)(uintptr_t)a.cache.v_scale)[h];
   }
 }
 
@@ -575,7 +541,7 @@ __device__ __forceinline__ void head_scales(const DecodeArgs &a, int h, float &k
 template <class CT, class QT>
 __device__ __forceinline__ float partial_vscale(float vscale) {
   if constexpr (std::is_same<CT, fp8_t>::value && std::is_same<QT, f16_t>::value)
-    return kFp8Unscale;
+    return 1.0f;
   return vscale;
 }
 
@@ -1227,7 +1193,7 @@ __device__ __forceinline__ SeqItem sequence_item(const DecodeArgs &a, int s, int
 template <class CT, class QT, int D, int kB, bool kApp>
 __device__ __forceinline__ void run_sequence_item(const DecodeArgs &a, const SeqItem &it, int tbl0,
                                                   int &settle) {
-  wave_item<CT, QT, D, PA_DECODE_NT, kB, kApp>(a, it.s, it.h, it.jb0, it.jb1, it.end, it.slot, it.L,
+  wave_item<CT, QT, D, kDecodeNT, kB, kApp>(a, it.s, it.h, it.jb0, it.jb1, it.end, it.slot, it.L,
                                          tbl0, settle);
 }
 
@@ -1255,9 +1221,7 @@ __device__ __forceinline__ int item_table_entries(const DecodeArgs &a, const Seq
 // the streaming of private blocks from HBM starts at once beside the prefix groups.
 template <class CT, class QT, int D, bool kPre, int kB, bool kApp>
 __global__ __launch_bounds__(256)
-#if PA_DECODE_OCC
-__attribute__((amdgpu_waves_per_eu(kApp && !kPre ? PA_APPEND_OCC : PA_DECODE_OCC)))
-#endif
+__attribute__((amdgpu_waves_per_eu(kApp && !kPre ? kAppendOcc : kDecodeOcc)))
 void decode_mfma_kernel(DecodeArgs a) {
   static_assert(!kPre || kB == 16, "the shared prefix runs on 16-position blocks");
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1409,16 +1373,11 @@ void decode_mfma_kernel(DecodeArgs a) {
 // Each row masks the positions past its own; the workgroup walks the blocks up to its last row's
 // position, in rounds of 64 blocks (one table fetch per round).  Rows are complete in one
 // wavefront: the outputs are written directly, no workspace.
-#ifndef PA_PREFILL_TILES
-#define PA_PREFILL_TILES 2
-#endif
-#ifndef PA_PREFILL_STAGES
-#define PA_PREFILL_STAGES 4
-#endif
-#ifndef PA_PREFILL_OCC
-#define PA_PREFILL_OCC 2
-#endif
-constexpr int kPrefillTiles = PA_PREFILL_TILES;
+// Two 16-row tiles per wavefront, four pair stages in LDS, two wavefronts per SIMD (one tile at
+// three per SIMD and three or six stages measured slower).
+constexpr int kPrefillTiles = 2;
+constexpr int kPrefillStages = 4;
+constexpr int kPrefillOcc = 2;
 constexpr int kXcds = 8;  // accelerator complex dies; workgroups are dealt to them round-robin
 constexpr int kPrefillRows = 16 * kPrefillTiles * kWaves;
 
@@ -1430,7 +1389,7 @@ struct PairStages {
   static constexpr int kBytes = 2 * kBlockBytes;      // block A, then block B
   static constexpr int kChunks = kBytes / 1024;       // 1 KiB copies per pair
   static constexpr int kPerWave = kChunks / kWaves;
-  static constexpr int kStages = PA_PREFILL_STAGES;
+  static constexpr int kStages = kPrefillStages;
   static_assert(kChunks % kWaves == 0, "pair split");
 };
 
@@ -1586,7 +1545,7 @@ __device__ __forceinline__ uint4 pair_keep(int tok0, int vl) {
 }
 
 template <class CT, class QT, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PA_PREFILL_OCC)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrefillOcc)))
 void prefill_mfma_kernel(DecodeArgs a) {
   using P = PairStages<CT, D>;
   using F = Frag<CT, D>;
@@ -1769,7 +1728,7 @@ hipError_t launch_ddpa(DecodeArgs a, hipStream_t s) {
   a.num_cus = device_cus();
   if (a.persistent) {
     const int resident = resident_groups<CT, QT, D, kPre, kB, kApp>();
-    grid = dim3((unsigned)(PA_SPREAD ? resident : std::min<int64_t>(direct, resident)));
+    grid = dim3((unsigned)std::min<int64_t>(direct, resident));
   }
   decode_mfma_kernel<CT, QT, D, kPre, kB, kApp><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();

@@ -2,8 +2,11 @@
 // dispatch to the gfx950 kernels.  Nothing here allocates or synchronises device memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 #include <vector>
 
@@ -76,6 +79,38 @@ pa_status launch_status(hipError_t e, const char *who) {
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
+// Debug checks (PA_DEBUG): off unless the environment variable PA_DEBUG is set to a non-zero value
+// when the library is first used, or pa_set_debug() turns them on.
+std::atomic<int> g_debug{-1};
+
+bool debug_on() {
+  int d = g_debug.load(std::memory_order_relaxed);
+  if (d < 0) {
+    const char *e = std::getenv("PA_DEBUG");
+    d = (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
+    int expected = -1;
+    g_debug.compare_exchange_strong(expected, d, std::memory_order_relaxed);
+    d = g_debug.load(std::memory_order_relaxed);
+  }
+  return d > 0;
+}
+
+// Debug mode only: n elements of a device (or pinned host) array, copied to the host once the
+// stream has reached this point.
+template <class T>
+pa_status debug_fetch(const T *src, int64_t n, void *stream, std::vector<T> &dst, const char *who,
+                      const char *what) {
+  dst.assign((size_t)n, T());
+  if (n == 0) return PA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(dst.data(), src, (size_t)n * sizeof(T), hipMemcpyDefault, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess)
+    return fail(PA_ERR_LAUNCH, "%s: PA_DEBUG copy of %s failed: %s", who, what,
+                hipGetErrorString(e));
+  return PA_OK;
+}
+
 int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                           int32_t partition_size) {
   return partition_size > 0 ? partition_size
@@ -138,6 +173,13 @@ pa_status pa_reshape_and_cache(const pa_cache *cache, const void *key, const voi
   if (key_stride < row || value_stride < row)
     return fail(PA_ERR_SHAPE, "%s: strides %lld/%lld below a row of %lld elements", who,
                 (long long)key_stride, (long long)value_stride, (long long)row);
+  if (debug_on()) {
+    std::vector<int64_t> h;
+    st = debug_fetch(slot_mapping, num_tokens, stream, h, who, "slot_mapping");
+    if (st != PA_OK) return st;
+    st = pa_check_slots(h.data(), num_tokens, cache->num_blocks, cache->block_size);
+    if (st != PA_OK) return fail(st, "%s: %s", who, g_last_error.c_str());
+  }
   pa::ReshapeArgs a;
   a.cache = cache_args(cache);
   a.key = key;
@@ -258,6 +300,20 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
       return fail(PA_ERR_UNSUPPORTED, "%s: block_size 8 needs a pool below 4 GiB", who);
   }
 
+  if (debug_on()) {
+    std::vector<int32_t> lens;
+    st = debug_fetch(context_lens, num_seqs, stream, lens, who, "context_lens");
+    if (st != PA_OK) return st;
+    st = pa_check_context_lens(lens.data(), num_seqs, max_context_len);
+    if (st != PA_OK) return fail(st, "%s: %s", who, g_last_error.c_str());
+    if (app) {
+      std::vector<int64_t> sl;
+      st = debug_fetch(ap.slots, num_seqs, stream, sl, who, "slot_mapping");
+      if (st != PA_OK) return st;
+      st = pa_check_slots(sl.data(), num_seqs, cache->num_blocks, B);
+      if (st != PA_OK) return fail(st, "%s: %s", who, g_last_error.c_str());
+    }
+  }
   const int64_t cap = (int64_t)max_blocks_per_seq * B;
   const int32_t max_len = (int32_t)(max_context_len < cap ? max_context_len : cap);
   pa::DecodeArgs a{};
@@ -494,6 +550,43 @@ pa_status pa_check_copy_pairs(const int32_t *pairs, int32_t num_pairs, int32_t n
   return PA_OK;
 }
 
+pa_status pa_check_slots(const int64_t *slots, int32_t num_tokens, int32_t num_blocks,
+                         int32_t block_size) {
+  const char *who = "pa_check_slots";
+  if (num_tokens < 0 || num_blocks < 0 || block_size < 1)
+    return fail(PA_ERR_SHAPE, "%s: negative count or block size", who);
+  if (num_tokens > 0 && !slots) return fail(PA_ERR_NULL, "%s: slots is NULL", who);
+  const int64_t n = (int64_t)num_blocks * block_size;
+  std::vector<char> seen((size_t)n, 0);
+  for (int32_t t = 0; t < num_tokens; ++t) {
+    const int64_t s = slots[t];
+    if (s < 0 || s >= n) continue;  // skipped by the kernels
+    if (seen[(size_t)s]) return fail(PA_ERR_ALIAS, "%s: slot %lld repeats (token %d)", who,
+                                     (long long)s, t);
+    seen[(size_t)s] = 1;
+  }
+  return PA_OK;
+}
+
+pa_status pa_check_context_lens(const int32_t *context_lens, int32_t num_seqs,
+                                int32_t max_context_len) {
+  const char *who = "pa_check_context_lens";
+  if (num_seqs < 0) return fail(PA_ERR_SHAPE, "%s: num_seqs < 0", who);
+  if (num_seqs > 0 && !context_lens) return fail(PA_ERR_NULL, "%s: context_lens is NULL", who);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (context_lens[s] < 0)
+      return fail(PA_ERR_SHAPE, "%s: context_lens[%d] = %d < 0", who, s, context_lens[s]);
+    if (context_lens[s] > max_context_len)
+      return fail(PA_ERR_SHAPE, "%s: context_lens[%d] = %d above max_context_len %d", who, s,
+                  context_lens[s], max_context_len);
+  }
+  return PA_OK;
+}
+
+void pa_set_debug(int on) { g_debug.store(on ? 1 : 0, std::memory_order_relaxed); }
+
+int pa_debug_enabled(void) { return debug_on() ? 1 : 0; }
+
 pa_status pa_copy_blocks(const pa_cache *layers, int32_t num_layers, const int32_t *block_pairs,
                          int32_t num_pairs, void *stream) {
   const char *who = "pa_copy_blocks";
@@ -508,6 +601,13 @@ pa_status pa_copy_blocks(const pa_cache *layers, int32_t num_layers, const int32
         layers[l].num_kv_heads != layers[0].num_kv_heads ||
         layers[l].head_dim != layers[0].head_dim || layers[l].cache_dtype != layers[0].cache_dtype)
       return fail(PA_ERR_SHAPE, "%s: layer %d differs in shape or dtype from layer 0", who, l);
+  }
+  if (debug_on()) {
+    std::vector<int32_t> h;
+    pa_status st = debug_fetch(block_pairs, 2 * (int64_t)num_pairs, stream, h, who, "block_pairs");
+    if (st != PA_OK) return st;
+    st = pa_check_copy_pairs(h.data(), num_pairs, layers[0].num_blocks);
+    if (st != PA_OK) return fail(st, "%s: %s", who, g_last_error.c_str());
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t block_bytes = (int64_t)layers[0].num_kv_heads * layers[0].block_size *

@@ -45,18 +45,14 @@ __device__ __forceinline__ float4 load_part4(const float *part_out, size_t q0, i
   }
 }
 // Split variant: wavefronts per row, and the most rows it is used for.
-#ifndef PA_REDUCE_SPLIT
-#define PA_REDUCE_SPLIT 1
-#endif
 constexpr int kWavesSplit = 4;
 constexpr int kSplitRows = 1024;
 
 // kPer: float4 loads in flight per lane (a sub-chunk of G * kPer partitions).  A few keep the
-// registers low, so that many rows are in flight, for batches of many rows; 32 takes 64
-// partitions of a row in one round trip when rows are few (then occupancy does not matter).
-#ifndef PA_REDUCE_WIDE
-#define PA_REDUCE_WIDE 1
-#endif
+// registers low, so that many rows are in flight, for batches of many rows (4: 8 and 16 measured
+// no better); 32 takes 64 partitions of a row in one round trip when rows are few (the wide
+// variant: then occupancy does not matter).
+constexpr int kPerNarrow = 4;
 // Scale of the merged row: 1, or the KV head's v_scale where the partials are in units of fp8
 // cache codes (part_vscale).
 template <bool kHalf>
@@ -69,9 +65,6 @@ __device__ __forceinline__ float out_scale(const DecodeArgs &a, int row) {
   return 1.0f;
 }
 
-#ifndef PA_REDUCE_PER
-#define PA_REDUCE_PER 4
-#endif
 template <class QT, int D, int kPer, bool kHalf>
 __global__ __launch_bounds__(64 * kRowsPerGroup) void partition_reduce_kernel(DecodeArgs a) {
   constexpr int C = D / 4;   // float4 columns of a partial output
@@ -226,8 +219,8 @@ template <class QT, bool kHalf>
 hipError_t launch_qh(const DecodeArgs &a, hipStream_t s) {
   const int rows = a.num_seqs * a.num_q_heads;
   dim3 grid((rows + kRowsPerGroup - 1) / kRowsPerGroup), block(64 * kRowsPerGroup);
-  const bool wide = PA_REDUCE_WIDE && rows <= 2048 && a.num_partitions > 16;
-  if (PA_REDUCE_SPLIT && wide && rows <= kSplitRows) {
+  const bool wide = rows <= 2048 && a.num_partitions > 16;
+  if (wide && rows <= kSplitRows) {
     if (a.cache.head_dim == 64)
       partition_reduce_split_kernel<QT, 64, kHalf><<<dim3(rows), dim3(64 * kWavesSplit), 0, s>>>(a);
     else
@@ -239,7 +232,7 @@ hipError_t launch_qh(const DecodeArgs &a, hipStream_t s) {
     else partition_reduce_kernel<QT, 64, 2, kHalf><<<grid, block, 0, s>>>(a);
   } else {
     if (wide) partition_reduce_kernel<QT, 128, 32, kHalf><<<grid, block, 0, s>>>(a);
-    else partition_reduce_kernel<QT, 128, PA_REDUCE_PER, kHalf><<<grid, block, 0, s>>>(a);
+    else partition_reduce_kernel<QT, 128, kPerNarrow, kHalf><<<grid, block, 0, s>>>(a);
   }
   return hipGetLastError();
 }

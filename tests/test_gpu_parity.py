@@ -854,6 +854,47 @@ def test_fused_append_skips_slots_outside_the_pool():
         assert err <= TOL[w.cache_dtype]
 
 
+# --------------------------------------------------------------------------- debug checks
+def test_debug_checks_refuse_before_launch():
+    """With the PA_DEBUG checks on: repeated slots in reshape_and_cache and in the fused append,
+    aliasing copy pairs, and a context length above max_context_len are refused before anything is
+    enqueued (the pools and the output keep their bytes); valid calls still run."""
+    w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=4, num_blocks=256)
+    b = DecodeBatch(w, pad_block=0, lengths=[40, 300, 17, 129])
+    st = b.sets[0]
+    cache = b.caches[0]
+    api.pa_set_debug(True)
+    try:
+        b.run_step(0)  # a valid step passes the checks
+        torch.cuda.synchronize()
+        before = device_pool_bytes(cache)
+        dup = st.d_slots.clone()
+        dup[2] = dup[0]
+        with pytest.raises(api.PaError) as e:
+            api.pa_reshape_and_cache(cache, st.new_k[0], st.new_v[0], dup)
+        assert e.value.status == -5
+        out = torch.full_like(st.out[0], 3.0)
+        with pytest.raises(api.PaError) as e:
+            api.pa_decode_attention_append(out, st.q[0], cache, st.new_k[0], st.new_v[0], dup,
+                                           st.d_tables, st.d_ctx, b.max_context_len, w.scale,
+                                           workspace=b.workspace)
+        assert e.value.status == -5
+        with pytest.raises(api.PaError) as e:
+            api.pa_decode_attention(out, st.q[0], cache, st.d_tables, st.d_ctx,
+                                    b.max_context_len - 1, w.scale, workspace=b.workspace)
+        assert e.value.status == -2
+        pairs = torch.tensor([[1, 2], [2, 3]], dtype=torch.int32, device="cuda")
+        with pytest.raises(api.PaError) as e:
+            api.pa_copy_blocks([cache], pairs)
+        assert e.value.status == -5
+        torch.cuda.synchronize()
+        after = device_pool_bytes(cache)
+        assert np.array_equal(before[0], after[0]) and np.array_equal(before[1], after[1])
+        assert bool((out == 3.0).all())
+    finally:
+        api.pa_set_debug(False)
+
+
 # --------------------------------------------------------------------------- full sizes
 FULL = ["f16_batch32", "bf16_32k_batch8", "f16_shared_prefix_batch256"]
 

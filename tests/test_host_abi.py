@@ -443,3 +443,34 @@ def test_set_host_blocks_is_refused_while_a_sequence_is_out():
     assert bm.swap_in(s).tolist() == [[0, 0]]  # block 0 was freed on top, so it comes back
     bm.set_host_blocks(8)
     assert bm.num_free_host() == 8
+
+
+def test_slot_checks():
+    """pa_check_slots: a repeated in-pool slot is an alias; negative and past-the-pool slots are
+    skipped, as the kernels skip them."""
+    api.pa_check_slots(np.array([0, 5, 17, -1, -1, 8 * 16, 8 * 16]), 8)
+    with pytest.raises(api.PaError) as e:
+        api.pa_check_slots(np.array([3, 9, 3]), 8)
+    assert e.value.status == -5 and "repeats" in str(e.value)
+    api.pa_check_slots(np.array([0, 8, 31]), 4, block_size=8)
+    with pytest.raises(api.PaError):
+        api.pa_check_slots(np.array([31, 31]), 4, block_size=8)
+    api.pa_check_slots(np.zeros(0, np.int64), 8)
+
+
+def test_context_length_checks():
+    api.pa_check_context_lens(np.array([0, 5, 64]), 64)
+    with pytest.raises(api.PaError) as e:
+        api.pa_check_context_lens(np.array([0, 65]), 64)
+    assert e.value.status == -2 and "above max_context_len" in str(e.value)
+    with pytest.raises(api.PaError):
+        api.pa_check_context_lens(np.array([-1]), 64)
+
+
+def test_debug_switch():
+    was = api.pa_debug_enabled()
+    api.pa_set_debug(True)
+    assert api.pa_debug_enabled()
+    api.pa_set_debug(False)
+    assert not api.pa_debug_enabled()
+    api.pa_set_debug(was)
