@@ -1499,23 +1499,36 @@ __device__ __forceinline__ float max_over_rows(float x) {
 }
 
 // Softmax update over a pair at tok0 from the raw scores sx, sy (products X, Y): this lane's
-// positions are tok0 + 8 grp + i, i < 8 (sx: i < 4, sy: i >= 4); those at or past zl are masked.
+// positions are tok0 + 8 grp + i, i < 8 (sx: i < 4, sy: i >= 4); with `masked` (wave-uniform:
+// some row's limit falls inside the pair, or a block of the pair is absent) those at or past zl
+// are excluded.  With a positive scale (the usual case) the row maximum is taken over the raw
+// scores and scaled once, and each probability is 2^(s * kscale - m) in one fused multiply-add.
 // Returns this lane's P^T operand: the 8 probabilities in position order.
 template <class CT, int D>
 __device__ __forceinline__ uint4 pair_softmax(f4_t sx, f4_t sy, float kscale, int tok0, int zl,
-                                              RowState<D> &rs_) {
+                                              bool masked, RowState<D> &rs_) {
   constexpr bool kBF = std::is_same<CT, bf16_t>::value;
   constexpr int NT = D / 16;
   const int t0 = tok0 + 8 * ((threadIdx.x & 63) >> 4);
   float z[8];
-  float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    z[i] = t0 + i < zl ? sx[i] * kscale : -INFINITY;  // select: masked positions never leak
-    z[4 + i] = t0 + 4 + i < zl ? sy[i] * kscale : -INFINITY;
-    mx = fmaxf(mx, fmaxf(z[i], z[4 + i]));
+    z[i] = sx[i];
+    z[4 + i] = sy[i];
   }
-  mx = max_over_rows(mx);
+  const bool fast = kscale > 0.0f;  // wave-uniform
+  if (!fast) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] *= kscale;
+  }
+  if (masked) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = t0 + i < zl ? z[i] : -INFINITY;  // never leaks NaN
+  }
+  const float ks = fast ? kscale : 1.0f;
+  float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                   fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+  mx = max_over_rows(mx) * ks;  // -inf stays -inf (ks > 0)
   float &m = rs_.m;
   const bool grow = mx > m + kSlack;
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -1528,7 +1541,7 @@ __device__ __forceinline__ uint4 pair_softmax(f4_t sx, f4_t sy, float kscale, in
   }
   float p[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - m);
+  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[i], ks, -m));
   rs_.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   return make_uint4(pack2<kBF>(p[0], p[1]), pack2<kBF>(p[2], p[3]), pack2<kBF>(p[4], p[5]),
                     pack2<kBF>(p[6], p[7]));
@@ -1590,6 +1603,13 @@ void prefill_mfma_kernel(DecodeArgs a) {
   }
   float kscale, vscale;
   head_scales<CT>(a, h, kscale, vscale);
+  // the smallest limit of this wavefront's rows (wave-uniform): pairs below it need no score mask
+  int lmin = 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < kT; ++j) lmin = min(lmin, rvalid[j] ? lim[j] : 0x7fffffff);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) lmin = min(lmin, __shfl_xor(lmin, o));
+  lmin = __builtin_amdgcn_readfirstlane(lmin);
   const int32_t *table = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   const int nb = a.cache.num_blocks;
   const int jb1 = (end + kBlock - 1) / kBlock;
@@ -1630,18 +1650,27 @@ void prefill_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < kT; ++j) sy[j] = block_qk<CT, D>(kf, st[j]);
       }
+      // Masks only where they change something (wave-uniform tests): the scores where some row's
+      // limit falls inside the pair, the V values where the pair reaches the workgroup's end
+      // (positions past it may hold anything, NaN included); an absent block masks both.
+      const bool both = oka && okb;
+      const bool zmask = !both || t0 + 2 * kBlock > lmin;
+      const bool vmask = !both || t0 + 2 * kBlock > end;
       uint4 pop[kT];
 #pragma unroll
       for (int j = 0; j < kT; ++j)
-        pop[j] = pair_softmax<CT, D>(sx[j], sy[j], kscale, t0, okm ? lim[j] : 0, st[j]);
-      const uint4 keep = pair_keep(t0, okm ? end : 0);
+        pop[j] = pair_softmax<CT, D>(sx[j], sy[j], kscale, t0, okm ? lim[j] : 0, zmask, st[j]);
+      uint4 keep = make_uint4(~0u, ~0u, ~0u, ~0u);
+      if (vmask) keep = pair_keep(t0, okm ? end : 0);
 #pragma unroll
       for (int nt = 0; nt < F::kNT; ++nt) {
         uint4 vop = read_pair_v<CT, D, i>(nt);
-        vop.x &= keep.x;  // a select: NaN in a masked position cannot leak
-        vop.y &= keep.y;
-        vop.z &= keep.z;
-        vop.w &= keep.w;
+        if (vmask) {  // a select: NaN in a masked position cannot leak
+          vop.x &= keep.x;
+          vop.y &= keep.y;
+          vop.z &= keep.z;
+          vop.w &= keep.w;
+        }
 #pragma unroll
         for (int j = 0; j < kT; ++j) st[j].acc[nt] = mma_k32<kBF>(vop, pop[j], st[j].acc[nt]);
       }
