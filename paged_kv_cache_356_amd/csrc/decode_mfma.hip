@@ -140,6 +140,19 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
   }
 }
 
+// The same rounding in one packed conversion (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32).
+template <bool BF>
+__device__ __forceinline__ uint32_t pack2_pk(float x, float y) {
+  typedef float fl2_t __attribute__((ext_vector_type(2)));
+  if constexpr (BF) {
+    typedef __bf16 bh2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((fl2_t){x, y}, bh2_t));
+  } else {
+    typedef _Float16 hh2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((fl2_t){x, y}, hh2_t));
+  }
+}
+
 template <bool BF>
 __device__ __forceinline__ float unpack_lo(uint32_t v) {
   if constexpr (BF) return __uint_as_float(v << 16);
@@ -1399,40 +1412,59 @@ __device__ __forceinline__ int tok_swap(int t) { return t ^ (((t >> 3) & 1) << 2
 __device__ __forceinline__ int k_slot(int t, int b) { return tok_swap(t) ^ (b << 3); }
 __device__ __forceinline__ int k_token(int slot, int b) { return tok_swap(slot ^ (b << 3)); }
 
-// This wavefront's share of the pair (blocks ba, bb of KV head h) into stage I, permuted as the
+// Wavefront w copies tile w of every pair: the K tile (w = 0) or V tile (w = 1) of block A, or
+// those of block B (w = 2, 3), in 1 KiB pieces j = 0 .. kTileBytes / 1024 - 1, permuted as the
 // reads expect: LDS slot s of a K tile holds the pool's vector (s / 16, token k_token(s % 16));
 // LDS slot s of a 16-bit V^T tile holds head dim s % D, positions 8 (s / D) .. + 7; fp8 V^T
-// tiles are copied as they are.
-template <class CT, int D, int I>
-__device__ __forceinline__ void stage_pair(const DecodeArgs &a, int ba, bool oka, int bb, bool okb,
-                                           int h) {
+// tiles are copied as they are.  Piece j's source offset is a per-lane part that does not depend
+// on j (`voff`) plus a wave-uniform part (`piece_soff`), both fixed for the whole call.
+struct PairCopy {
+  const char *base;  // pool of this wavefront's tile, advanced to KV head h
+  size_t stride;     // bytes between blocks in that pool (num_kv_heads tiles)
+  int voff;          // per-lane source byte offset of every piece
+  int blk;           // block of the pair this wavefront copies (0: A, 1: B)
+  bool is_v;
+};
+
+template <class CT, int D>
+__device__ __forceinline__ PairCopy pair_copy_setup(const DecodeArgs &a, int h) {
   using P = PairStages<CT, D>;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int H = a.cache.num_kv_heads;
-  const char *kp = static_cast<const char *>(a.cache.k_pool);
-  const char *vp = static_cast<const char *>(a.cache.v_pool);
-  const size_t ta = ((size_t)(oka ? ba : 0) * H + h) * P::kTileBytes;
-  const size_t tb = ((size_t)(okb ? bb : 0) * H + h) * P::kTileBytes;
-  const auto rka = tile_rsrc(kp + ta, oka ? P::kTileBytes : 0);
-  const auto rva = tile_rsrc(vp + ta, oka ? P::kTileBytes : 0);
-  const auto rkb = tile_rsrc(kp + tb, okb ? P::kTileBytes : 0);
-  const auto rvb = tile_rsrc(vp + tb, okb ? P::kTileBytes : 0);
-  auto *stage = prefix_stage<P::kBytes, 16 + I>();
+  PairCopy c;
+  c.blk = w >> 1;
+  c.is_v = (w & 1) != 0;
+  c.stride = (size_t)a.cache.num_kv_heads * P::kTileBytes;
+  c.base = static_cast<const char *>(c.is_v ? a.cache.v_pool : a.cache.k_pool) +
+           (size_t)h * P::kTileBytes;
+  if (!c.is_v) c.voff = 16 * ((lane & ~15) | k_token(lane & 15, c.blk));
+  else c.voff = P::kFP8 ? 16 * lane : 32 * lane;
+  return c;
+}
+
+// Wave-uniform source offset of piece j (LDS slots 64 j .. 64 j + 63 of the tile).
+template <class CT, int D>
+__device__ __forceinline__ int piece_soff(const PairCopy &c, int j) {
+  using P = PairStages<CT, D>;
+  if (P::kFP8 || !c.is_v) return 1024 * j;
+  return 16 * (2 * ((64 * j) % D) + (64 * j) / D);  // slot 64 j + lane -> 2 (slot % D) + slot / D
+}
+
+// This wavefront's tile of the pair (blocks ba, bb of KV head h) into stage I; an absent block
+// copies through an empty descriptor and touches no memory.
+template <class CT, int D, int I>
+__device__ __forceinline__ void stage_pair(const PairCopy &c, int ba, bool oka, int bb, bool okb) {
+  using P = PairStages<CT, D>;
+  constexpr int kPieces = P::kTileBytes / 1024;
+  static_assert(kPieces * kWaves == P::kChunks, "one tile per wavefront");
+  const int b = c.blk ? bb : ba;
+  const bool ok = c.blk ? okb : oka;
+  const auto r = tile_rsrc(c.base + (size_t)(ok ? b : 0) * c.stride, ok ? P::kTileBytes : 0);
+  auto *dst = prefix_stage<P::kBytes, 16 + I>() + (2 * c.blk + (c.is_v ? 1 : 0)) * P::kTileBytes;
 #pragma unroll
-  for (int i = 0; i < P::kPerWave; ++i) {
-    const int c = w + kWaves * i;  // 1 KiB chunk of the stage
-    const int cb = c * 1024 / P::kBlockBytes, off = c * 1024 - cb * P::kBlockBytes;
-    const bool v = off >= P::kTileBytes;
-    const int slot = (off - (v ? P::kTileBytes : 0)) / 16 + lane;  // LDS slot within the tile
-    int src;                                                       // pool slot within the tile
-    if (!v) src = (slot & ~15) | k_token(slot & 15, cb);
-    else if (P::kFP8) src = slot;
-    else src = 2 * (slot % D) + slot / D;
-    const auto r = cb ? (v ? rvb : rkb) : (v ? rva : rka);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)(stage + c * 1024), 16, 16 * src, 0,
-                                             0, 0);
-  }
+  for (int j = 0; j < kPieces; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)(dst + 1024 * j), 16, c.voff,
+                                             piece_soff<CT, D>(c, j), 0, 0);
 }
 
 // K operand of score product X (which = 0) or Y (which = 1), vector i (16 dims of fp8, 8 of
@@ -1498,18 +1530,18 @@ __device__ __forceinline__ float max_over_rows(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Softmax update over a pair at tok0 from the raw scores sx, sy (products X, Y): this lane's
-// positions are tok0 + 8 grp + i, i < 8 (sx: i < 4, sy: i >= 4); with `masked` (wave-uniform:
-// some row's limit falls inside the pair, or a block of the pair is absent) those at or past zl
-// are excluded.  With a positive scale (the usual case) the row maximum is taken over the raw
-// scores and scaled once, and each probability is 2^(s * kscale - m) in one fused multiply-add.
-// Returns this lane's P^T operand: the 8 probabilities in position order.
+// Softmax update over a pair from the raw scores sx, sy (products X, Y): this lane's positions are
+// the pair's 8 grp + i, i < 8 (sx: i < 4, sy: i >= 4).  With `masked` (wave-uniform: some row's
+// limit falls inside the pair, or a block of the pair is absent) those at or past `rel` (this
+// lane's limit minus the pair's first position 8 grp) are excluded.  With a positive scale (the
+// usual case) the row maximum is taken over the raw scores and scaled once, and each probability
+// is 2^(s * kscale - m) in one fused multiply-add.  Returns this lane's P^T operand: the 8
+// probabilities in position order.
 template <class CT, int D>
-__device__ __forceinline__ uint4 pair_softmax(f4_t sx, f4_t sy, float kscale, int tok0, int zl,
-                                              bool masked, RowState<D> &rs_) {
+__device__ __forceinline__ uint4 pair_softmax(f4_t sx, f4_t sy, float kscale, int rel, bool masked,
+                                              RowState<D> &rs_) {
   constexpr bool kBF = std::is_same<CT, bf16_t>::value;
   constexpr int NT = D / 16;
-  const int t0 = tok0 + 8 * ((threadIdx.x & 63) >> 4);
   float z[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1523,7 +1555,7 @@ __device__ __forceinline__ uint4 pair_softmax(f4_t sx, f4_t sy, float kscale, in
   }
   if (masked) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = t0 + i < zl ? z[i] : -INFINITY;  // never leaks NaN
+    for (int i = 0; i < 8; ++i) z[i] = i < rel ? z[i] : -INFINITY;  // never leaks NaN
   }
   const float ks = fast ? kscale : 1.0f;
   float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
@@ -1543,17 +1575,14 @@ __device__ __forceinline__ uint4 pair_softmax(f4_t sx, f4_t sy, float kscale, in
 #pragma unroll
   for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[i], ks, -m));
   rs_.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-  return make_uint4(pack2<kBF>(p[0], p[1]), pack2<kBF>(p[2], p[3]), pack2<kBF>(p[4], p[5]),
-                    pack2<kBF>(p[6], p[7]));
+  return make_uint4(pack2_pk<kBF>(p[0], p[1]), pack2_pk<kBF>(p[2], p[3]),
+                    pack2_pk<kBF>(p[4], p[5]), pack2_pk<kBF>(p[6], p[7]));
 }
 
-// Mask words that zero the 16-bit V values of this lane's positions (tok0 + 8 grp + i) at or past
-// vl, two positions per word.
-__device__ __forceinline__ uint4 pair_keep(int tok0, int vl) {
-  const int t0 = tok0 + 8 * ((threadIdx.x & 63) >> 4);
-  auto two = [&](int i) {
-    return (t0 + i < vl ? 0xffffu : 0u) | (t0 + i + 1 < vl ? 0xffff0000u : 0u);
-  };
+// Mask words that zero the 16-bit V values of this lane's positions 8 grp + i of the pair at or
+// past rel (this lane's limit minus 8 grp), two positions per word.
+__device__ __forceinline__ uint4 pair_keep(int rel) {
+  auto two = [&](int i) { return (i < rel ? 0xffffu : 0u) | (i + 1 < rel ? 0xffff0000u : 0u); };
   return make_uint4(two(0), two(2), two(4), two(6));
 }
 
@@ -1613,6 +1642,7 @@ void prefill_mfma_kernel(DecodeArgs a) {
   const int32_t *table = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   const int nb = a.cache.num_blocks;
   const int jb1 = (end + kBlock - 1) / kBlock;
+  const PairCopy pc = pair_copy_setup<CT, D>(a, h);
   int tbl = first_table_entries(table, 0, jb1);
 #pragma unroll
   for (int j = 0; j < kT; ++j)
@@ -1629,8 +1659,8 @@ void prefill_mfma_kernel(DecodeArgs a) {
     auto id = [&](int b) { return b < nk ? __builtin_amdgcn_readlane(tbl, b) : -1; };
     auto issue = [&](auto I, int k) {  // pair k into stage I (past the end: empty copies)
       const int ba = id(2 * k), bb = id(2 * k + 1);
-      stage_pair<CT, D, decltype(I)::value>(a, ba, (unsigned)ba < (unsigned)nb, bb,
-                                            (unsigned)bb < (unsigned)nb, h);
+      stage_pair<CT, D, decltype(I)::value>(pc, ba, (unsigned)ba < (unsigned)nb, bb,
+                                            (unsigned)bb < (unsigned)nb);
     };
     auto step = [&](auto I, int k) {
       constexpr int i = decltype(I)::value;
@@ -1656,23 +1686,30 @@ void prefill_mfma_kernel(DecodeArgs a) {
       const bool both = oka && okb;
       const bool zmask = !both || t0 + 2 * kBlock > lmin;
       const bool vmask = !both || t0 + 2 * kBlock > end;
+      const int tl = t0 + 8 * grp;  // this lane's first position of the pair
       uint4 pop[kT];
 #pragma unroll
       for (int j = 0; j < kT; ++j)
-        pop[j] = pair_softmax<CT, D>(sx[j], sy[j], kscale, t0, okm ? lim[j] : 0, zmask, st[j]);
-      uint4 keep = make_uint4(~0u, ~0u, ~0u, ~0u);
-      if (vmask) keep = pair_keep(t0, okm ? end : 0);
+        pop[j] = pair_softmax<CT, D>(sx[j], sy[j], kscale, (okm ? lim[j] : 0) - tl, zmask, st[j]);
+      if (!vmask) {
 #pragma unroll
-      for (int nt = 0; nt < F::kNT; ++nt) {
-        uint4 vop = read_pair_v<CT, D, i>(nt);
-        if (vmask) {  // a select: NaN in a masked position cannot leak
-          vop.x &= keep.x;
+        for (int nt = 0; nt < F::kNT; ++nt) {
+          const uint4 vop = read_pair_v<CT, D, i>(nt);
+#pragma unroll
+          for (int j = 0; j < kT; ++j) st[j].acc[nt] = mma_k32<kBF>(vop, pop[j], st[j].acc[nt]);
+        }
+      } else {
+        const uint4 keep = pair_keep((okm ? end : 0) - tl);
+#pragma unroll
+        for (int nt = 0; nt < F::kNT; ++nt) {
+          uint4 vop = read_pair_v<CT, D, i>(nt);
+          vop.x &= keep.x;  // a select: NaN in a masked position cannot leak
           vop.y &= keep.y;
           vop.z &= keep.z;
           vop.w &= keep.w;
-        }
 #pragma unroll
-        for (int j = 0; j < kT; ++j) st[j].acc[nt] = mma_k32<kBF>(vop, pop[j], st[j].acc[nt]);
+          for (int j = 0; j < kT; ++j) st[j].acc[nt] = mma_k32<kBF>(vop, pop[j], st[j].acc[nt]);
+        }
       }
     };
     stage_barrier<63>();  // the stages' previous readers are done
