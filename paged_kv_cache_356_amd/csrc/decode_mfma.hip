@@ -1530,50 +1530,39 @@ __device__ __forceinline__ float max_over_rows(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Softmax update over a pair from the raw scores sx, sy (products X, Y): this lane's positions are
-// the pair's 8 grp + i, i < 8 (sx: i < 4, sy: i >= 4).  With `masked` (wave-uniform: some row's
-// limit falls inside the pair, or a block of the pair is absent) those at or past `rel` (this
-// lane's limit minus the pair's first position 8 grp) are excluded.  With a positive scale (the
-// usual case) the row maximum is taken over the raw scores and scaled once, and each probability
-// is 2^(s * kscale - m) in one fused multiply-add.  Returns this lane's P^T operand: the 8
-// probabilities in position order.
+// Softmax over a pair, in two parts, so that the next pair's score products can be issued beside
+// each.  z holds this lane's raw scores of the pair, positions 8 grp + i, i < 8 (product X gives
+// i < 4, product Y the rest); ks > 0 is the logit scale (a negative scale is folded into the
+// query's sign, a zero one replaced by the smallest normal float, which leaves every probability
+// at exactly 1 as a zero scale does).
+// Part 1: the pair's row maximum, scaled once; returns whether it exceeds the running maximum by
+// more than kSlack (base 2), when the running state must be rescaled.
+__device__ __forceinline__ bool pair_max(const float (&z)[8], float ks, float m, float &mx) {
+  float x = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                  fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+  mx = max_over_rows(x) * ks;  // -inf stays -inf
+  return mx > m + kSlack;
+}
+
+// Rescale this lane's running state to the new maximum mx when `grow` (per lane).
+template <int D>
+__device__ __forceinline__ void pair_rescale(bool grow, float mx, RowState<D> &rs_) {
+  const float mn = grow ? mx : rs_.m;
+  const float alpha = __builtin_amdgcn_exp2f(rs_.m - mn);
+  rs_.l *= alpha;
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) rs_.acc[nt] *= alpha;
+  rs_.m = mn;
+}
+
+// Part 2: each probability 2^(s * ks - m) in one fused multiply-add, their sum added to l; returns
+// this lane's P^T operand, the 8 probabilities in position order rounded to the input type.
 template <class CT, int D>
-__device__ __forceinline__ uint4 pair_softmax(f4_t sx, f4_t sy, float kscale, int rel, bool masked,
-                                              RowState<D> &rs_) {
+__device__ __forceinline__ uint4 pair_probs(const float (&z)[8], float ks, RowState<D> &rs_) {
   constexpr bool kBF = std::is_same<CT, bf16_t>::value;
-  constexpr int NT = D / 16;
-  float z[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    z[i] = sx[i];
-    z[4 + i] = sy[i];
-  }
-  const bool fast = kscale > 0.0f;  // wave-uniform
-  if (!fast) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] *= kscale;
-  }
-  if (masked) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = i < rel ? z[i] : -INFINITY;  // never leaks NaN
-  }
-  const float ks = fast ? kscale : 1.0f;
-  float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                   fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-  mx = max_over_rows(mx) * ks;  // -inf stays -inf (ks > 0)
-  float &m = rs_.m;
-  const bool grow = mx > m + kSlack;
-  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-    const float mn = grow ? mx : m;
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    rs_.l *= alpha;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) rs_.acc[nt] *= alpha;
-    m = mn;
-  }
   float p[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[i], ks, -m));
+  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[i], ks, -rs_.m));
   rs_.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   return make_uint4(pack2_pk<kBF>(p[0], p[1]), pack2_pk<kBF>(p[2], p[3]),
                     pack2_pk<kBF>(p[4], p[5]), pack2_pk<kBF>(p[6], p[7]));
@@ -1632,6 +1621,20 @@ void prefill_mfma_kernel(DecodeArgs a) {
   }
   float kscale, vscale;
   head_scales<CT>(a, h, kscale, vscale);
+  // The logit scale enters as ks > 0: a negative scale flips the sign of the query operand (the
+  // products then come out exactly negated), a zero scale becomes the smallest normal float.
+  const float ks = fabsf(kscale) == 0.0f ? 1.17549435e-38f : fabsf(kscale);
+  if (kscale < 0.0f) {
+#pragma unroll
+    for (int j = 0; j < kT; ++j)
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        st[j].qop[kk].x ^= 0x80008000u;
+        st[j].qop[kk].y ^= 0x80008000u;
+        st[j].qop[kk].z ^= 0x80008000u;
+        st[j].qop[kk].w ^= 0x80008000u;
+      }
+  }
   // the smallest limit of this wavefront's rows (wave-uniform): pairs below it need no score mask
   int lmin = 0x7fffffff;
 #pragma unroll
@@ -1650,6 +1653,9 @@ void prefill_mfma_kernel(DecodeArgs a) {
     for (int kk = 0; kk < D / 32; ++kk)
       asm volatile("" : "+v"(st[j].qop[kk].x), "+v"(st[j].qop[kk].y), "+v"(st[j].qop[kk].z),
                    "+v"(st[j].qop[kk].w));
+  // The pairs of a round go through the stages in order; step k computes the softmax and P V of
+  // pair k and, beside that softmax, the score products of pair k + 1 (its K tiles are in LDS by
+  // then), so the matrix cores have work while the vector ALUs do the softmax.
   for (int c0 = 0; c0 < jb1; c0 += 64) {  // rounds of up to 64 blocks
     const int nk = min(64, jb1 - c0);
     const int npair = (nk + 1) / 2;
@@ -1662,35 +1668,73 @@ void prefill_mfma_kernel(DecodeArgs a) {
       stage_pair<CT, D, decltype(I)::value>(pc, ba, (unsigned)ba < (unsigned)nb, bb,
                                             (unsigned)bb < (unsigned)nb);
     };
+    // Raw scores of the pair in stage I, this lane's 8 positions per tile (X then Y products).
+    auto scores_x = [&](auto I, float (&z)[kT][8]) {
+      uint4 kf[F::kKLoads];
+      read_pair_k<CT, D, decltype(I)::value, 0>(kf);
+#pragma unroll
+      for (int j = 0; j < kT; ++j) {
+        const f4_t x = block_qk<CT, D>(kf, st[j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[j][i] = x[i];
+      }
+    };
+    auto scores_y = [&](auto I, float (&z)[kT][8]) {
+      uint4 kf[F::kKLoads];
+      read_pair_k<CT, D, decltype(I)::value, 1>(kf);
+#pragma unroll
+      for (int j = 0; j < kT; ++j) {
+        const f4_t y = block_qk<CT, D>(kf, st[j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[j][4 + i] = y[i];
+      }
+    };
+    float zc[kT][8];  // scores of the current pair
     auto step = [&](auto I, int k) {
       constexpr int i = decltype(I)::value;
-      stage_barrier<P::kPerWave * (kS - 2)>();  // pair k landed for every wavefront
+      constexpr int inext = (i + 1) % kS;
+      // pair k + 1 landed for every wavefront, and every wavefront is done with pair k - 1's stage
+      stage_barrier<P::kPerWave * (kS - 3)>();
       issue(std::integral_constant<int, (i + kS - 1) % kS>{}, k + kS - 1);
       const int ba = id(2 * k), bb = id(2 * k + 1);
       const bool oka = (unsigned)ba < (unsigned)nb, okb = (unsigned)bb < (unsigned)nb;
       const bool okm = (grp >> 1) ? okb : oka;  // this lane's block
       const int t0 = (c0 + 2 * k) * kBlock;
-      f4_t sx[kT], sy[kT];
-      {
-        uint4 kf[F::kKLoads];
-        read_pair_k<CT, D, i, 0>(kf);
-#pragma unroll
-        for (int j = 0; j < kT; ++j) sx[j] = block_qk<CT, D>(kf, st[j]);
-        read_pair_k<CT, D, i, 1>(kf);
-#pragma unroll
-        for (int j = 0; j < kT; ++j) sy[j] = block_qk<CT, D>(kf, st[j]);
-      }
+      const int tl = t0 + 8 * grp;  // this lane's first position of the pair
       // Masks only where they change something (wave-uniform tests): the scores where some row's
       // limit falls inside the pair, the V values where the pair reaches the workgroup's end
       // (positions past it may hold anything, NaN included); an absent block masks both.
       const bool both = oka && okb;
       const bool zmask = !both || t0 + 2 * kBlock > lmin;
       const bool vmask = !both || t0 + 2 * kBlock > end;
-      const int tl = t0 + 8 * grp;  // this lane's first position of the pair
+      if (zmask) {
+#pragma unroll
+        for (int j = 0; j < kT; ++j) {
+          const int rel = (okm ? lim[j] : 0) - tl;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) zc[j][q] = q < rel ? zc[j][q] : -INFINITY;  // never NaN
+        }
+      }
+      // Pair k + 1's X products beside pair k's maxima.  Past the round's last pair the stage
+      // holds an empty copy (zeros); those scores are not used.
+      float zn[kT][8];
+      scores_x(std::integral_constant<int, inext>{}, zn);
+      float mx[kT];
+      bool grow[kT], any = false;
+#pragma unroll
+      for (int j = 0; j < kT; ++j) {
+        grow[j] = pair_max(zc[j], ks, st[j].m, mx[j]);
+        any = any || grow[j];
+      }
+      if (__builtin_amdgcn_ballot_w64(any) != 0) {
+#pragma unroll
+        for (int j = 0; j < kT; ++j) pair_rescale(grow[j], mx[j], st[j]);
+      }
+      // Pair k + 1's Y products beside pair k's probabilities.
+      scores_y(std::integral_constant<int, inext>{}, zn);
       uint4 pop[kT];
 #pragma unroll
-      for (int j = 0; j < kT; ++j)
-        pop[j] = pair_softmax<CT, D>(sx[j], sy[j], kscale, (okm ? lim[j] : 0) - tl, zmask, st[j]);
+      for (int j = 0; j < kT; ++j) pop[j] = pair_probs<CT, D>(zc[j], ks, st[j]);
       if (!vmask) {
 #pragma unroll
         for (int nt = 0; nt < F::kNT; ++nt) {
@@ -1711,9 +1755,16 @@ void prefill_mfma_kernel(DecodeArgs a) {
           for (int j = 0; j < kT; ++j) st[j].acc[nt] = mma_k32<kBF>(vop, pop[j], st[j].acc[nt]);
         }
       }
+#pragma unroll
+      for (int j = 0; j < kT; ++j)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) zc[j][q] = zn[j][q];
     };
     stage_barrier<63>();  // the stages' previous readers are done
     static_for<0, kS - 1>([&](auto I) { issue(I, decltype(I)::value); });
+    stage_barrier<P::kPerWave * (kS - 2)>();  // pair 0 landed for every wavefront
+    scores_x(std::integral_constant<int, 0>{}, zc);
+    scores_y(std::integral_constant<int, 0>{}, zc);
     int k0 = 0;
     for (; k0 + kS <= npair; k0 += kS)
       static_for<0, kS>([&](auto I) { step(I, k0 + decltype(I)::value); });

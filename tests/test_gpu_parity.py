@@ -560,11 +560,23 @@ def test_prefill_matches_oracle(cache_dtype, D):
     """pa_prefill_attention against the oracle: sequences with a history and a chunk of new tokens
     (a whole prompt, a chunk inside one block, one across blocks, a long one, none, one over a
     history of more than 64 blocks), NaN in every pool byte no sequence owns; head_dim 128 and 64."""
+    _prefill_case(cache_dtype, D, 1.0 / math.sqrt(D))
+
+
+@pytest.mark.parametrize("cache_dtype", ["f16", "fp8"])
+@pytest.mark.parametrize("scale", [-0.125, 0.0])
+def test_prefill_negative_and_zero_scale(cache_dtype, scale):
+    """The same batch with a negative softmax scale (the largest logits are those of the most
+    negative products) and a zero one (every position of a row weighs the same)."""
+    _prefill_case(cache_dtype, 128, scale)
+
+
+def _prefill_case(cache_dtype, D, scale):
     q_dtype = "f16" if cache_dtype == "fp8" else cache_dtype
     Hq, H, nb, B = 28, 4, 512, 16
     lengths = [37, 200, 18, 700, 9, 64, 1500]
     chunks = [37, 5, 13, 300, 0, 64, 130]
-    _say(f"prefill, {cache_dtype} cache, head_dim {D}")
+    _say(f"prefill, {cache_dtype} cache, head_dim {D}, scale {scale}")
     g = torch.Generator().manual_seed(4242)
     bm = api.BlockManager(nb, B, wl.free_order(wl.WORKLOADS["f16_batch32"].replace(num_blocks=nb)))
     seqs = [bm.add_seq() for _ in lengths]
@@ -589,7 +601,7 @@ def test_prefill_matches_oracle(cache_dtype, D):
     out = torch.full_like(q, 7.0)
     api.pa_prefill_attention(out, q, cache, torch.from_numpy(tables).cuda(),
                              torch.from_numpy(ctx).cuda(), torch.from_numpy(qs).cuda(),
-                             max(chunks), max(lengths), 1.0 / math.sqrt(D))
+                             max(chunks), max(lengths), scale)
     torch.cuda.synchronize()
     kp, vp = device_pool_bytes(cache)
     kp = kp.view(RAW_NP[cache_dtype])
@@ -598,7 +610,7 @@ def test_prefill_matches_oracle(cache_dtype, D):
     vs_np = None if vscale is None else vscale.cpu().numpy()
     ref = oracle.prefill_attention(raw(q).reshape(T, -1), q_dtype, kp, vp, cache_dtype, ks_np,
                                    vs_np, nb, H, D, tables, ctx, qs, Hq,
-                                   float(np.float32(1.0 / math.sqrt(D))))
+                                   float(np.float32(scale)))
     got = as_f64(out)
     err = max_abs_err(got, ref)
     _say(f"  max-abs err {err:.3e} over {T} tokens")
