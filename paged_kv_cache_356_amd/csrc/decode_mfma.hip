@@ -1795,8 +1795,6 @@ hipError_t launch_prefill_d(const DecodeArgs &a, hipStream_t s) {
                                 : launch_prefill_dd<CT, QT, 128>(a, s);
 }
 
-// Workgroups of one instantiation that fit on the device at once (occupancy x compute units),
-// looked up once per device.
 // Compute units of the current device, looked up once per device.
 int device_cus() {
   constexpr int kMaxDev = 64;
