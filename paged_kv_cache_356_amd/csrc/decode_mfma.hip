@@ -1369,7 +1369,8 @@ void decode_mfma_kernel(DecodeArgs a) {
 //  - workgroup (s, h, group) takes kPrefillRows rows of sequence s and KV head h (row r is token
 //    r / g, query head h*g + r % g), its wavefront w kPrefillTiles tiles of 16 rows;
 //  - the blocks go through LDS two at a time (a pair A, B: 32 positions), copied straight from the
-//    pool by the four wavefronts and read back by each, so a block is fetched once per 128 rows;
+//    pool (wavefront w copies tile w of the pair: K or V of block A or B) and read back by each
+//    wavefront, so a block is fetched once per 128 rows;
 //  - P V is one 16x16x32 product per 16 head dims over the pair, reduction index k = position
 //    tok0 + k of the pair: lane group grp (lanes 16 grp ..) holds positions 8 grp .. 8 grp + 7,
 //    i.e. 8 consecutive positions of block grp / 2, so its V^T operand is one 16-byte row piece;
@@ -1382,12 +1383,14 @@ void decode_mfma_kernel(DecodeArgs a) {
 //  - the scores of a pair are taken together (one maximum update per pair, the row maximum by
 //    lane swaps rather than LDS shuffles);
 //  - probabilities are rounded once to the input type (no hi + lo split): each output averages
-//    many positions, so the rounding of single probabilities does not accumulate.
+//    many positions, so the rounding of single probabilities does not accumulate;
+//  - step k of a round computes pair k's softmax and P V and, beside that softmax, the score
+//    products of pair k + 1, so the matrix pipe has work while the vector ALUs do the softmax.
 // Each row masks the positions past its own; the workgroup walks the blocks up to its last row's
 // position, in rounds of 64 blocks (one table fetch per round).  Rows are complete in one
 // wavefront: the outputs are written directly, no workspace.
 // Two 16-row tiles per wavefront, four pair stages in LDS, two wavefronts per SIMD (one tile at
-// three per SIMD and three or six stages measured slower).
+// three per SIMD, and three, five or six stages, measured slower).
 constexpr int kPrefillTiles = 2;
 constexpr int kPrefillStages = 4;
 constexpr int kPrefillOcc = 2;
