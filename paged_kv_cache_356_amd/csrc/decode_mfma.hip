@@ -47,14 +47,13 @@
 #include <type_traits>
 #include <utility>
 
+#include "mfma_common.h"
 #include "pa_device.h"
 #include "pa_kernels.h"
 
 namespace pa {
 namespace {
 
-constexpr int kWaves = 4;
-#define PA_LDS __attribute__((address_space(3)))  // LDS pointers
 constexpr int kMaxScanSeqs = 4096;  // persistent grid: sequences whose item prefix fits in LDS
 // The shared-prefix instantiation also holds the prefix groups' block stages in LDS; its scan
 // arrays are halved so that three workgroups still fit on a compute unit.
@@ -75,18 +74,6 @@ constexpr bool kDecodeNT = true;
 constexpr int kDecodeOcc = 3;
 constexpr int kAppendOcc = 2;
 
-// K/V tiles are read with raw buffer loads through a descriptor per tile: a slot with no block
-// gets a descriptor of length 0, whose loads return zeros without touching memory (and still count
-// in vmcnt, so the ring's waits stay partial).  kNT adds the non-temporal hint (each tile is read
-// once per call).
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, the value raw loads use on gfx9
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *tile, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(tile), (short)0, bytes, kRsrcWord3);
-}
-
 // off: per-lane byte offset; soff: a wave-uniform byte offset added to it.
 template <class T, bool kNT>
 __device__ __forceinline__ T load_kv(__amdgpu_buffer_rsrc_t r, int off, int soff = 0) {
@@ -97,124 +84,6 @@ __device__ __forceinline__ T load_kv(__amdgpu_buffer_rsrc_t r, int off, int soff
     return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, aux));
   else
     return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, aux));
-}
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNoMax = -3.0e38f;  // running-maximum floor (finite)
-constexpr float kSlack = 8.0f;  // base-2 headroom of the lazily rescaled running maximum
-
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
-typedef short s4_t __attribute__((ext_vector_type(4)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
-
-template <bool BF>
-__device__ __forceinline__ f4_t mma_k32(uint4 a, uint4 b, f4_t c) {
-  if constexpr (BF)
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, a),
-                                                   __builtin_bit_cast(b8_t, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a),
-                                                  __builtin_bit_cast(h8_t, b), c, 0, 0, 0);
-}
-
-template <bool BF>
-__device__ __forceinline__ f4_t mma_k16(uint2 a, uint2 b, f4_t c) {
-  if constexpr (BF)
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, a),
-                                                     __builtin_bit_cast(s4_t, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, a),
-                                                 __builtin_bit_cast(h4_t, b), c, 0, 0, 0);
-}
-
-// Two floats -> two 16-bit values of the MFMA input type (round to nearest even), packed.
-template <bool BF>
-__device__ __forceinline__ uint32_t pack2(float x, float y) {
-  if constexpr (BF) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y) << 16);
-  } else {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y) << 16);
-  }
-}
-
-// The same rounding in one packed conversion (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32).
-template <bool BF>
-__device__ __forceinline__ uint32_t pack2_pk(float x, float y) {
-  typedef float fl2_t __attribute__((ext_vector_type(2)));
-  if constexpr (BF) {
-    typedef __bf16 bh2_t __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((fl2_t){x, y}, bh2_t));
-  } else {
-    typedef _Float16 hh2_t __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((fl2_t){x, y}, hh2_t));
-  }
-}
-
-template <bool BF>
-__device__ __forceinline__ float unpack_lo(uint32_t v) {
-  if constexpr (BF) return __uint_as_float(v << 16);
-  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
-}
-template <bool BF>
-__device__ __forceinline__ float unpack_hi(uint32_t v) {
-  if constexpr (BF) return __uint_as_float(v & 0xffff0000u);
-  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
-}
-
-// Four E4M3FN bytes (byte 0 first) -> four binary16 values equal to decode(byte), by the hardware
-// conversion v_cvt_scalef32_pk_f16_fp8 at scale 1 (exact for all 256 codes, checked on the GPU;
-// the NaN code gives a NaN).
-__device__ __forceinline__ uint2 e4m3x4_to_f16x4(uint32_t x) {
-  uint2 r;
-  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
-  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true));
-  return r;
-}
-
-template <class CT, int D>
-struct Frag {
-  static constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
-  static constexpr int kKLoads = kFP8 ? D / 64 : D / 32;  // 16-byte K loads per lane
-  static constexpr int kNT = D / 16;                      // PV products (16 head-dim rows each)
-  using VRaw = typename std::conditional<kFP8, uint32_t, uint2>::type;
-  uint4 k[kKLoads];
-  VRaw v[kNT];
-};
-
-
-// ---------------------------------------------------------------------------------------------
-// Per-wavefront pieces.  Lane l = 16 * grp + col: column col of the products is one query row.
-
-template <int D>
-struct RowState {
-  uint4 qop[D / 32];  // Q^T operand of this lane's query row
-  float m, l;         // running maximum (base-2 logits) and running sum of this lane's column
-  f4_t acc[D / 16];   // O^T accumulator: head-dim rows 16 nt + 4 grp + i of this lane's column
-};
-
-// Q^T operand: lane l holds query row (rs, rhq), 8 dims per product kk, zeros for a padding
-// column.  The dims follow the K operand: f16/bf16 tiles give lane group grp dims 8 grp + 32 kk;
-// fp8 tiles give 16-byte vectors of 16 dims, split in two products, so 16 grp + 64 (kk/2) +
-// 8 (kk%2).
-template <class CT, int D>
-__device__ __forceinline__ void load_query(const DecodeArgs &a, int rs, int rhq, bool rvalid,
-                                           RowState<D> &st) {
-  constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
-  const int grp = (threadIdx.x & 63) >> 4;
-  const auto *q =
-      reinterpret_cast<const uint16_t *>(a.q) + (size_t)rs * a.q_stride + (size_t)rhq * D;
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) {
-    const int d0 = kFP8 ? 16 * grp + 64 * (kk >> 1) + 8 * (kk & 1) : 8 * grp + 32 * kk;
-    st.qop[kk] = rvalid ? *reinterpret_cast<const uint4 *>(q + d0) : make_uint4(0, 0, 0, 0);
-  }
-  st.m = kNoMax;  // a finite floor: a fully masked block gives exp2(-inf - m) = 0, not NaN
-  st.l = 0.0f;
-#pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) st.acc[nt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
 // The K and V tiles of block bid, KV head h, into f; ok = false (no block in this slot) loads zeros
@@ -528,26 +397,6 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs &a, const int32_t
   }
 }
 
-// Lane i's entry of the first 64 blocks [jb0, jb1) of a table row (-1 past the range).
-__device__ __forceinline__ int first_table_entries(const int32_t *table, int jb0, int jb1) {
-  const int lane = threadIdx.x & 63;
-  return lane < min(64, jb1 - jb0) ? table[jb0 + lane] : -1;
-}
-
-// The per-head scales are read through the constant address space: the kernel never writes them,
-// and scalar loads keep them out of the vector memory counter the block ring waits on.
-template <class CT>
-__device__ __forceinline__ void head_scales(const DecodeArgs &a, int h, float &kscale,
-                                            float &vscale) {
-  kscale = a.scale * kLog2e;
-  vscale = 1.0f;
-  if constexpr (std::is_same<CT, fp8_t>::value) {
-    using cfloat = const __attribute__((address_space(4))) float;
-    kscale *= ((cfloat *)(uintptr_t)a.cache.k_scale)[h];
-    vscale = ((cfloat *)(uintptr_t)a.cache.v_scale)[h];
-  }
-}
-
 // Scale of a row's partial outputs in the workspace.  With an fp8 cache the f16-query partials
 // stay in units of the cache codes (|x| <= 448, so inside fp16's range whatever the head's scale),
 // and the partition reduce applies the head's v_scale; otherwise they carry the full scale.
@@ -556,33 +405,6 @@ __device__ __forceinline__ float partial_vscale(float vscale) {
   if constexpr (std::is_same<CT, fp8_t>::value && std::is_same<QT, f16_t>::value)
     return 1.0f;
   return vscale;
-}
-
-__device__ __forceinline__ int clamp_len(const DecodeArgs &a, int s) {
-  int L = a.context_lens[s];
-  return L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
-}
-
-// ---------------------------------------------------------------------------------------------
-// The work of one wavefront: KV head h over blocks [jb0, jb1) of `table`, against up to 16 query
-// rows (the 16 columns of the products).  This lane's column is query row (rs, rhq) (query row rs
-// at q_stride, head rhq; output row rs * Hq + rhq), or padding when !rvalid; positions at or past
-// its `lim` are masked, and V elements of positions at or past `end` (wave-uniform) are zeroed.
-// The result goes to workspace partition `slot`, or straight to the output when slot < 0.
-// kNT: read K/V with non-temporal loads (each tile is read once per call), or with ordinary loads
-// (tiles that other wavefronts of the call read too).  tbl0: lane i's entry of the first 64
-// blocks (first_table_entries).  settle: a value whose load is in flight (the next item's first
-// table entries), waited for once this item's blocks are done.
-template <class QT, int D>
-__device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D> &st, float vscale,
-                                          int slot, int rs, int rhq, bool rvalid);
-
-// A 4-, 8- or 16-byte LDS read.
-template <class T>
-__device__ __forceinline__ T lds_load(const PA_LDS char *p) {
-  if constexpr (sizeof(T) == 16) return __builtin_bit_cast(T, *(const PA_LDS u32x4_t *)p);
-  else if constexpr (sizeof(T) == 8) return __builtin_bit_cast(T, *(const PA_LDS u32x2_t *)p);
-  else return __builtin_bit_cast(T, *(const PA_LDS uint32_t *)p);
 }
 
 // The appended token of sequence s for KV head h (fused append): lane l holds elements 2 l and
@@ -873,6 +695,16 @@ __device__ __forceinline__ void write_token_rows(const DecodeArgs &a, int rank, 
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// The work of one wavefront: KV head h over blocks [jb0, jb1) of `table`, against up to 16 query
+// rows (the 16 columns of the products).  This lane's column is query row (rs, rhq) (query row rs
+// at q_stride, head rhq; output row rs * Hq + rhq), or padding when !rvalid; positions at or past
+// its `lim` are masked, and V elements of positions at or past `end` (wave-uniform) are zeroed.
+// The result goes to workspace partition `slot`, or straight to the output when slot < 0.
+// kNT: read K/V with non-temporal loads (each tile is read once per call), or with ordinary loads
+// (tiles that other wavefronts of the call read too).  tbl0: lane i's entry of the first 64
+// blocks (first_table_entries).  settle: a value whose load is in flight (the next item's first
+// table entries), waited for once this item's blocks are done.
 template <class CT, class QT, int D, bool kNT, int kB>
 __device__ __forceinline__ void rows_core(const DecodeArgs &a, const int32_t *table, int h,
                                           int jb0, int jb1, int end, int slot, int rs, int rhq,
@@ -896,69 +728,6 @@ __device__ __forceinline__ void rows_core(const DecodeArgs &a, const int32_t *ta
   for (int kk = 0; kk < D / 32; ++kk)
     asm volatile("" : "+v"(st.qop[kk].x), "+v"(st.qop[kk].y), "+v"(st.qop[kk].z), "+v"(st.qop[kk].w));
   emit_rows<QT, D>(a, st, vscale, partial_vscale<CT, QT>(vscale), slot, rs, rhq, rvalid);
-}
-
-// A finished row state to the output (slot < 0, scaled by vscale) or to workspace partition
-// `slot` (scaled by pvscale).
-template <class QT, int D>
-__device__ __forceinline__ void emit_rows(const DecodeArgs &a, const RowState<D> &st, float vscale,
-                                          float pvscale, int slot, int rs, int rhq, bool rvalid) {
-  constexpr int NT = D / 16;
-  const int Hq = a.num_q_heads;
-  const int grp = (threadIdx.x & 63) >> 4;
-  // the row's sum over the four lane groups; m is already uniform over them
-  float l = st.l;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (!rvalid) return;
-  const size_t orow = (size_t)rs * Hq + rhq;
-  const float inv = l > 0.0f ? (slot < 0 ? vscale : pvscale) / l : 0.0f;  // no position: zero
-  if (slot < 0) {
-    auto *out = static_cast<typename QT::raw *>(a.out) + orow * D;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      typename QT::raw v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = from_f32<QT>(st.acc[nt][i] * inv);
-      *reinterpret_cast<uint2 *>(out + 16 * nt + 4 * grp) = *reinterpret_cast<const uint2 *>(v);
-    }
-  } else {
-    const size_t row = orow * a.num_partitions + slot;
-    if constexpr (std::is_same<QT, f16_t>::value) {
-      // f16 queries: the partial output in fp16 (half the workspace traffic; it is a normalised
-      // average of V rows, rounded once more before the merge), stored lane-contiguous: the
-      // quads of head dims 16 nt + 4 grp .. + 3 at quad grp * NT + nt of the row, so each lane
-      // writes NT * 8 contiguous bytes and a row's four lane groups one contiguous span
-      typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-      uint32_t hw[2 * NT];  // round to nearest even
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        hw[2 * nt] = __builtin_bit_cast(
-            uint32_t, h2_t{(_Float16)(st.acc[nt][0] * inv), (_Float16)(st.acc[nt][1] * inv)});
-        hw[2 * nt + 1] = __builtin_bit_cast(
-            uint32_t, h2_t{(_Float16)(st.acc[nt][2] * inv), (_Float16)(st.acc[nt][3] * inv)});
-      }
-      uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<_Float16 *>(a.part_out) + row * D +
-                                             (size_t)grp * NT * 4);
-#pragma unroll
-      for (int k = 0; k < NT / 2; ++k)
-        dst[k] = make_uint4(hw[4 * k], hw[4 * k + 1], hw[4 * k + 2], hw[4 * k + 3]);
-    } else {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float4 v;
-        v.x = st.acc[nt][0] * inv;
-        v.y = st.acc[nt][1] * inv;
-        v.z = st.acc[nt][2] * inv;
-        v.w = st.acc[nt][3] * inv;
-        *reinterpret_cast<float4 *>(a.part_out + row * D + 16 * nt + 4 * grp) = v;
-      }
-    }
-    if (grp == 0) {
-      a.part_ml[row * 2] = st.m;
-      a.part_ml[row * 2 + 1] = l;
-    }
-  }
 }
 
 // Wavefront item of the decode: KV head h over positions [jb0 * 16, end) of sequence s's block
@@ -1000,16 +769,6 @@ __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int h_i
 // stages keep kStages - 1 blocks in flight while one is computed.  Each stage is a variable of its
 // own, so the compiler can tell a read of one stage from the copies still landing in the others.
 
-// f(std::integral_constant<int, i>) for i = I .. N - 1, in order.
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-
 template <class CT, int D>
 struct PrefixStages {
   static constexpr int kTileBytes = kBlock * D * CT::bytes;
@@ -1019,12 +778,6 @@ struct PrefixStages {
   static constexpr int kStages = kBytes >= 8192 ? 4 : 8;
   static_assert(kChunks >= 2 && (kChunks % kWaves == 0 || kChunks < kWaves), "stage split");
 };
-
-template <int kBytes, int I>
-__device__ __forceinline__ PA_LDS char *prefix_stage() {
-  __shared__ __attribute__((aligned(16))) char stage[kBytes];
-  return (PA_LDS char *)stage;
-}
 
 // This wavefront's share of the K and V tiles of block bid (KV head h) into stage I; a slot
 // without a block (ok = false) copies through an empty descriptor and touches no memory.
@@ -1051,7 +804,6 @@ __device__ __forceinline__ void stage_block(const DecodeArgs &a, int bid, bool o
   }
 }
 
-
 // The K and V tiles of stage I into registers, at the offsets load_block reads them at.
 template <class CT, int D, int I, int N>
 __device__ __forceinline__ void read_stage_k(uint4 (&k)[N]) {
@@ -1072,15 +824,6 @@ __device__ __forceinline__ void read_stage_v(VR (&v)[N]) {
 #pragma unroll
   for (int nt = 0; nt < N; ++nt)
     v[nt] = lds_load<VR>(stage + P::kTileBytes + ((16 * nt + col) * kBlock + 4 * grp) * CT::bytes);
-}
-
-// Wait until at most N of this wavefront's memory reads are outstanding (its LDS copies land in
-// order), then for its LDS reads, then meet the workgroup.  The memory clobber keeps the compiler
-// from moving LDS accesses across the barrier.
-template <int N>
-__device__ __forceinline__ void stage_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // Prefix group: kPrefixTiles tiles of 16 flat rows per wavefront, wavefront w taking rows
@@ -1363,440 +1106,6 @@ void decode_mfma_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Prefill (a chunk of n new tokens per sequence, positions L - n .. L - 1; the token at position p
-// attends to positions 0 .. p).  Unlike decode, every block serves many rows, so the work is
-// matrix-core bound, not memory bound, and is arranged for the products:
-//  - workgroup (s, h, group) takes kPrefillRows rows of sequence s and KV head h (row r is token
-//    r / g, query head h*g + r % g), its wavefront w kPrefillTiles tiles of 16 rows;
-//  - the blocks go through LDS two at a time (a pair A, B: 32 positions), copied straight from the
-//    pool (wavefront w copies tile w of the pair: K or V of block A or B) and read back by each
-//    wavefront, so a block is fetched once per 128 rows;
-//  - P V is one 16x16x32 product per 16 head dims over the pair, reduction index k = position
-//    tok0 + k of the pair: lane group grp (lanes 16 grp ..) holds positions 8 grp .. 8 grp + 7,
-//    i.e. 8 consecutive positions of block grp / 2, so its V^T operand is one 16-byte row piece;
-//  - the scores come from two 16x16x32 products per pair, X on positions 8 q + 0..3 of each
-//    block (q = 0, 1) and Y on 8 q + 4..7, whose result layouts put exactly those 8 positions in
-//    lane group grp (X gives the first four, Y the next four);
-//  - the LDS copy of a block is permuted so that every read of a product operand is a 16-byte
-//    load free of bank conflicts: K vectors of a token row are swizzled (token bit 2 flips with
-//    bit 3, block B also flips bit 3), 16-bit V^T tiles are stored half-row-major;
-//  - the scores of a pair are taken together (one maximum update per pair, the row maximum by
-//    lane swaps rather than LDS shuffles);
-//  - probabilities are rounded once to the input type (no hi + lo split): each output averages
-//    many positions, so the rounding of single probabilities does not accumulate;
-//  - step k of a round computes pair k's softmax and P V and, beside that softmax, the score
-//    products of pair k + 1, so the matrix pipe has work while the vector ALUs do the softmax.
-// Each row masks the positions past its own; the workgroup walks the blocks up to its last row's
-// position, in rounds of 64 blocks (one table fetch per round).  Rows are complete in one
-// wavefront: the outputs are written directly, no workspace.
-// Two 16-row tiles per wavefront, four pair stages in LDS, two wavefronts per SIMD (one tile at
-// three per SIMD, and three, five or six stages, measured slower).
-constexpr int kPrefillTiles = 2;
-constexpr int kPrefillStages = 4;
-constexpr int kPrefillOcc = 2;
-constexpr int kXcds = 8;  // accelerator complex dies; workgroups are dealt to them round-robin
-constexpr int kPrefillRows = 16 * kPrefillTiles * kWaves;
-
-template <class CT, int D>
-struct PairStages {
-  static constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
-  static constexpr int kTileBytes = kBlock * D * CT::bytes;
-  static constexpr int kBlockBytes = 2 * kTileBytes;  // K tile, then V tile
-  static constexpr int kBytes = 2 * kBlockBytes;      // block A, then block B
-  static constexpr int kChunks = kBytes / 1024;       // 1 KiB copies per pair
-  static constexpr int kPerWave = kChunks / kWaves;
-  static constexpr int kStages = kPrefillStages;
-  static_assert(kChunks % kWaves == 0, "pair split");
-};
-
-// Token order of a K vector row in LDS: slot k_slot(t, b) (in 16-byte units, within its 16-slot
-// row) holds token t of block b (0: A, 1: B); k_token is its inverse.
-__device__ __forceinline__ int tok_swap(int t) { return t ^ (((t >> 3) & 1) << 2); }  // involution
-__device__ __forceinline__ int k_slot(int t, int b) { return tok_swap(t) ^ (b << 3); }
-__device__ __forceinline__ int k_token(int slot, int b) { return tok_swap(slot ^ (b << 3)); }
-
-// Wavefront w copies tile w of every pair: the K tile (w = 0) or V tile (w = 1) of block A, or
-// those of block B (w = 2, 3), in 1 KiB pieces j = 0 .. kTileBytes / 1024 - 1, permuted as the
-// reads expect: LDS slot s of a K tile holds the pool's vector (s / 16, token k_token(s % 16));
-// LDS slot s of a 16-bit V^T tile holds head dim s % D, positions 8 (s / D) .. + 7; fp8 V^T
-// tiles are copied as they are.  Piece j's source offset is a per-lane part that does not depend
-// on j (`voff`) plus a wave-uniform part (`piece_soff`), both fixed for the whole call.
-struct PairCopy {
-  const char *base;  // pool of this wavefront's tile, advanced to KV head h
-  size_t stride;     // bytes between blocks in that pool (num_kv_heads tiles)
-  int voff;          // per-lane source byte offset of every piece
-  int blk;           // block of the pair this wavefront copies (0: A, 1: B)
-  bool is_v;
-};
-
-template <class CT, int D>
-__device__ __forceinline__ PairCopy pair_copy_setup(const DecodeArgs &a, int h) {
-  using P = PairStages<CT, D>;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  PairCopy c;
-  c.blk = w >> 1;
-  c.is_v = (w & 1) != 0;
-  c.stride = (size_t)a.cache.num_kv_heads * P::kTileBytes;
-  c.base = static_cast<const char *>(c.is_v ? a.cache.v_pool : a.cache.k_pool) +
-           (size_t)h * P::kTileBytes;
-  if (!c.is_v) c.voff = 16 * ((lane & ~15) | k_token(lane & 15, c.blk));
-  else c.voff = P::kFP8 ? 16 * lane : 32 * lane;
-  return c;
-}
-
-// Wave-uniform source offset of piece j (LDS slots 64 j .. 64 j + 63 of the tile).
-template <class CT, int D>
-__device__ __forceinline__ int piece_soff(const PairCopy &c, int j) {
-  using P = PairStages<CT, D>;
-  if (P::kFP8 || !c.is_v) return 1024 * j;
-  return 16 * (2 * ((64 * j) % D) + (64 * j) / D);  // slot 64 j + lane -> 2 (slot % D) + slot / D
-}
-
-// This wavefront's tile of the pair (blocks ba, bb of KV head h) into stage I; an absent block
-// copies through an empty descriptor and touches no memory.
-template <class CT, int D, int I>
-__device__ __forceinline__ void stage_pair(const PairCopy &c, int ba, bool oka, int bb, bool okb) {
-  using P = PairStages<CT, D>;
-  constexpr int kPieces = P::kTileBytes / 1024;
-  static_assert(kPieces * kWaves == P::kChunks, "one tile per wavefront");
-  const int b = c.blk ? bb : ba;
-  const bool ok = c.blk ? okb : oka;
-  const auto r = tile_rsrc(c.base + (size_t)(ok ? b : 0) * c.stride, ok ? P::kTileBytes : 0);
-  auto *dst = prefix_stage<P::kBytes, 16 + I>() + (2 * c.blk + (c.is_v ? 1 : 0)) * P::kTileBytes;
-#pragma unroll
-  for (int j = 0; j < kPieces; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PA_LDS void *)(dst + 1024 * j), 16, c.voff,
-                                             piece_soff<CT, D>(c, j), 0, 0);
-}
-
-// K operand of score product X (which = 0) or Y (which = 1), vector i (16 dims of fp8, 8 of
-// 16-bit): lane (r = lane / 16, c = lane % 16) holds vector 4 i + r of position
-// 8 ((c >> 2) & 1) + 4 which + (c & 3) of block c >> 3.
-template <class CT, int D, int I, int kWhich, int N>
-__device__ __forceinline__ void read_pair_k(uint4 (&k)[N]) {
-  using P = PairStages<CT, D>;
-  const int lane = threadIdx.x & 63, c = lane & 15, r = lane >> 4;
-  const int b = c >> 3;
-  const int t = 8 * ((c >> 2) & 1) + 4 * kWhich + (c & 3);
-  const auto *base = prefix_stage<P::kBytes, 16 + I>() + b * P::kBlockBytes +
-                     (16 * r + k_slot(t, b)) * 16;
-#pragma unroll
-  for (int i = 0; i < N; ++i) k[i] = lds_load<uint4>(base + 64 * 16 * i);
-}
-
-// V^T operand for head dims 16 nt + c (c = lane % 16) and positions 8 grp .. 8 grp + 7 of the pair
-// (grp = lane / 16: block grp / 2, its positions 8 (grp % 2) ..), as 8 values of the product type.
-template <class CT, int D, int I>
-__device__ __forceinline__ uint4 read_pair_v(int nt) {
-  using P = PairStages<CT, D>;
-  const int lane = threadIdx.x & 63, c = lane & 15, grp = lane >> 4;
-  const auto *tile = prefix_stage<P::kBytes, 16 + I>() + (grp >> 1) * P::kBlockBytes + P::kTileBytes;
-  if constexpr (P::kFP8) {
-    const uint2 x = lds_load<uint2>(tile + (16 * nt + c) * kBlock + 8 * (grp & 1));
-    const uint2 lo = e4m3x4_to_f16x4(x.x), hi = e4m3x4_to_f16x4(x.y);
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
-  } else {
-    return lds_load<uint4>(tile + ((grp & 1) * D + 16 * nt + c) * 16);
-  }
-}
-
-// S^T of one score product against this wavefront tile's query rows (raw products).
-template <class CT, int D, int N>
-__device__ __forceinline__ f4_t block_qk(const uint4 (&k)[N], const RowState<D> &rs_) {
-  constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
-  constexpr bool kBF = std::is_same<CT, bf16_t>::value;
-  f4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
-  if constexpr (kFP8) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const uint2 a0 = e4m3x4_to_f16x4(k[i].x), a1 = e4m3x4_to_f16x4(k[i].y);
-      const uint2 a2 = e4m3x4_to_f16x4(k[i].z), a3 = e4m3x4_to_f16x4(k[i].w);
-      st = mma_k32<false>(make_uint4(a0.x, a0.y, a1.x, a1.y), rs_.qop[2 * i], st);
-      st = mma_k32<false>(make_uint4(a2.x, a2.y, a3.x, a3.y), rs_.qop[2 * i + 1], st);
-    }
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < N; ++kk) st = mma_k32<kBF>(k[kk], rs_.qop[kk], st);
-  }
-  return st;
-}
-
-// Maximum over the four 16-lane rows of a wavefront (lanes c, c + 16, c + 32, c + 48), by two
-// lane swaps on the vector ALU (no LDS round trip).
-__device__ __forceinline__ float max_over_rows(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-// Softmax over a pair, in two parts, so that the next pair's score products can be issued beside
-// each.  z holds this lane's raw scores of the pair, positions 8 grp + i, i < 8 (product X gives
-// i < 4, product Y the rest); ks > 0 is the logit scale (a negative scale is folded into the
-// query's sign, a zero one replaced by the smallest normal float, which leaves every probability
-// at exactly 1 as a zero scale does).
-// Part 1: the pair's row maximum, scaled once; returns whether it exceeds the running maximum by
-// more than kSlack (base 2), when the running state must be rescaled.
-__device__ __forceinline__ bool pair_max(const float (&z)[8], float ks, float m, float &mx) {
-  float x = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                  fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-  mx = max_over_rows(x) * ks;  // -inf stays -inf
-  return mx > m + kSlack;
-}
-
-// Rescale this lane's running state to the new maximum mx when `grow` (per lane).
-template <int D>
-__device__ __forceinline__ void pair_rescale(bool grow, float mx, RowState<D> &rs_) {
-  const float mn = grow ? mx : rs_.m;
-  const float alpha = __builtin_amdgcn_exp2f(rs_.m - mn);
-  rs_.l *= alpha;
-#pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) rs_.acc[nt] *= alpha;
-  rs_.m = mn;
-}
-
-// Part 2: each probability 2^(s * ks - m) in one fused multiply-add, their sum added to l; returns
-// this lane's P^T operand, the 8 probabilities in position order rounded to the input type.
-template <class CT, int D>
-__device__ __forceinline__ uint4 pair_probs(const float (&z)[8], float ks, RowState<D> &rs_) {
-  constexpr bool kBF = std::is_same<CT, bf16_t>::value;
-  float p[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[i], ks, -rs_.m));
-  rs_.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-  return make_uint4(pack2_pk<kBF>(p[0], p[1]), pack2_pk<kBF>(p[2], p[3]),
-                    pack2_pk<kBF>(p[4], p[5]), pack2_pk<kBF>(p[6], p[7]));
-}
-
-// Mask words that zero the 16-bit V values of this lane's positions 8 grp + i of the pair at or
-// past rel (this lane's limit minus 8 grp), two positions per word.
-__device__ __forceinline__ uint4 pair_keep(int rel) {
-  auto two = [&](int i) { return (i < rel ? 0xffffu : 0u) | (i + 1 < rel ? 0xffff0000u : 0u); };
-  return make_uint4(two(0), two(2), two(4), two(6));
-}
-
-template <class CT, class QT, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrefillOcc)))
-void prefill_mfma_kernel(DecodeArgs a) {
-  using P = PairStages<CT, D>;
-  using F = Frag<CT, D>;
-  constexpr int kS = P::kStages;
-  constexpr int kT = kPrefillTiles;
-  constexpr bool kBF = std::is_same<CT, bf16_t>::value;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int H = a.cache.num_kv_heads, g = a.num_q_heads / H;
-  const int groups = (a.max_query_len * g + kPrefillRows - 1) / kPrefillRows;
-  // Workgroup b runs on XCD b % 8 (round-robin dispatch); each XCD takes a contiguous range of the
-  // list (sequence, KV head, group), so the groups that re-read one sequence's blocks share an L2.
-  // Within a (sequence, KV head) the longest groups (the last rows of a prompt attend to the most
-  // positions) come first.
-  const int per_xcd = (int)(gridDim.x / kXcds);
-  const int f = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-  if (f >= a.num_seqs * H * groups) return;  // the grid's padding to a multiple of kXcds
-  const int gi = groups - 1 - f % groups;
-  const int sh = f / groups;
-  const int h = sh % H, s = sh / H;
-  const int qs = a.query_start[s];
-  const int n = min(a.query_start[s + 1] - qs, a.max_query_len);
-  const int L = clamp_len(a, s);
-  const int nrows = n * g;
-  const int rbase = kPrefillRows * gi;
-  if (n <= 0 || rbase >= nrows) return;  // workgroup-uniform, before any barrier
-  const int last = min(rbase + kPrefillRows - 1, nrows - 1);
-  const int end = max(0, min(L, L - n + last / g + 1));  // the workgroup's last row's limit
-  const int col = threadIdx.x & 15;
-  const int grp = (threadIdx.x & 63) >> 4;
-  RowState<D> st[kT];
-  bool rvalid[kT];
-  int rs[kT], rhq[kT], lim[kT];
-#pragma unroll
-  for (int j = 0; j < kT; ++j) {
-    const int r = rbase + 16 * (kT * w + j) + col;
-    rvalid[j] = r < nrows;
-    const int t = rvalid[j] ? r / g : 0;
-    rs[j] = qs + t;
-    rhq[j] = h * g + (rvalid[j] ? r % g : 0);
-    lim[j] = max(0, min(L, L - n + t + 1));
-    load_query<CT, D>(a, rs[j], rhq[j], rvalid[j], st[j]);
-  }
-  float kscale, vscale;
-  head_scales<CT>(a, h, kscale, vscale);
-  // The logit scale enters as ks > 0: a negative scale flips the sign of the query operand (the
-  // products then come out exactly negated), a zero scale becomes the smallest normal float.
-  const float ks = fabsf(kscale) == 0.0f ? 1.17549435e-38f : fabsf(kscale);
-  if (kscale < 0.0f) {
-#pragma unroll
-    for (int j = 0; j < kT; ++j)
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) {
-        st[j].qop[kk].x ^= 0x80008000u;
-        st[j].qop[kk].y ^= 0x80008000u;
-        st[j].qop[kk].z ^= 0x80008000u;
-        st[j].qop[kk].w ^= 0x80008000u;
-      }
-  }
-  // the smallest limit of this wavefront's rows (wave-uniform): pairs below it need no score mask
-  int lmin = 0x7fffffff;
-#pragma unroll
-  for (int j = 0; j < kT; ++j) lmin = min(lmin, rvalid[j] ? lim[j] : 0x7fffffff);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) lmin = min(lmin, __shfl_xor(lmin, o));
-  lmin = __builtin_amdgcn_readfirstlane(lmin);
-  const int32_t *table = a.block_tables + (size_t)s * a.max_blocks_per_seq;
-  const int nb = a.cache.num_blocks;
-  const int jb1 = (end + kBlock - 1) / kBlock;
-  const PairCopy pc = pair_copy_setup<CT, D>(a, h);
-  int tbl = first_table_entries(table, 0, jb1);
-#pragma unroll
-  for (int j = 0; j < kT; ++j)
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-      asm volatile("" : "+v"(st[j].qop[kk].x), "+v"(st[j].qop[kk].y), "+v"(st[j].qop[kk].z),
-                   "+v"(st[j].qop[kk].w));
-  // The pairs of a round go through the stages in order; step k computes the softmax and P V of
-  // pair k and, beside that softmax, the score products of pair k + 1 (its K tiles are in LDS by
-  // then), so the matrix cores have work while the vector ALUs do the softmax.
-  for (int c0 = 0; c0 < jb1; c0 += 64) {  // rounds of up to 64 blocks
-    const int nk = min(64, jb1 - c0);
-    const int npair = (nk + 1) / 2;
-    // the next round's entries, waited for at its start
-    int tbl_next = c0 + 64 < jb1 ? first_table_entries(table, c0 + 64, jb1) : -1;
-    asm volatile("" : "+v"(tbl));
-    auto id = [&](int b) { return b < nk ? __builtin_amdgcn_readlane(tbl, b) : -1; };
-    auto issue = [&](auto I, int k) {  // pair k into stage I (past the end: empty copies)
-      const int ba = id(2 * k), bb = id(2 * k + 1);
-      stage_pair<CT, D, decltype(I)::value>(pc, ba, (unsigned)ba < (unsigned)nb, bb,
-                                            (unsigned)bb < (unsigned)nb);
-    };
-    // Raw scores of the pair in stage I, this lane's 8 positions per tile (X then Y products).
-    auto scores_x = [&](auto I, float (&z)[kT][8]) {
-      uint4 kf[F::kKLoads];
-      read_pair_k<CT, D, decltype(I)::value, 0>(kf);
-#pragma unroll
-      for (int j = 0; j < kT; ++j) {
-        const f4_t x = block_qk<CT, D>(kf, st[j]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[j][i] = x[i];
-      }
-    };
-    auto scores_y = [&](auto I, float (&z)[kT][8]) {
-      uint4 kf[F::kKLoads];
-      read_pair_k<CT, D, decltype(I)::value, 1>(kf);
-#pragma unroll
-      for (int j = 0; j < kT; ++j) {
-        const f4_t y = block_qk<CT, D>(kf, st[j]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[j][4 + i] = y[i];
-      }
-    };
-    float zc[kT][8];  // scores of the current pair
-    auto step = [&](auto I, int k) {
-      constexpr int i = decltype(I)::value;
-      constexpr int inext = (i + 1) % kS;
-      // pair k + 1 landed for every wavefront, and every wavefront is done with pair k - 1's stage
-      stage_barrier<P::kPerWave * (kS - 3)>();
-      issue(std::integral_constant<int, (i + kS - 1) % kS>{}, k + kS - 1);
-      const int ba = id(2 * k), bb = id(2 * k + 1);
-      const bool oka = (unsigned)ba < (unsigned)nb, okb = (unsigned)bb < (unsigned)nb;
-      const bool okm = (grp >> 1) ? okb : oka;  // this lane's block
-      const int t0 = (c0 + 2 * k) * kBlock;
-      const int tl = t0 + 8 * grp;  // this lane's first position of the pair
-      // Masks only where they change something (wave-uniform tests): the scores where some row's
-      // limit falls inside the pair, the V values where the pair reaches the workgroup's end
-      // (positions past it may hold anything, NaN included); an absent block masks both.
-      const bool both = oka && okb;
-      const bool zmask = !both || t0 + 2 * kBlock > lmin;
-      const bool vmask = !both || t0 + 2 * kBlock > end;
-      if (zmask) {
-#pragma unroll
-        for (int j = 0; j < kT; ++j) {
-          const int rel = (okm ? lim[j] : 0) - tl;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) zc[j][q] = q < rel ? zc[j][q] : -INFINITY;  // never NaN
-        }
-      }
-      // Pair k + 1's X products beside pair k's maxima.  Past the round's last pair the stage
-      // holds an empty copy (zeros); those scores are not used.
-      float zn[kT][8];
-      scores_x(std::integral_constant<int, inext>{}, zn);
-      float mx[kT];
-      bool grow[kT], any = false;
-#pragma unroll
-      for (int j = 0; j < kT; ++j) {
-        grow[j] = pair_max(zc[j], ks, st[j].m, mx[j]);
-        any = any || grow[j];
-      }
-      if (__builtin_amdgcn_ballot_w64(any) != 0) {
-#pragma unroll
-        for (int j = 0; j < kT; ++j) pair_rescale(grow[j], mx[j], st[j]);
-      }
-      // Pair k + 1's Y products beside pair k's probabilities.
-      scores_y(std::integral_constant<int, inext>{}, zn);
-      uint4 pop[kT];
-#pragma unroll
-      for (int j = 0; j < kT; ++j) pop[j] = pair_probs<CT, D>(zc[j], ks, st[j]);
-      if (!vmask) {
-#pragma unroll
-        for (int nt = 0; nt < F::kNT; ++nt) {
-          const uint4 vop = read_pair_v<CT, D, i>(nt);
-#pragma unroll
-          for (int j = 0; j < kT; ++j) st[j].acc[nt] = mma_k32<kBF>(vop, pop[j], st[j].acc[nt]);
-        }
-      } else {
-        const uint4 keep = pair_keep((okm ? end : 0) - tl);
-#pragma unroll
-        for (int nt = 0; nt < F::kNT; ++nt) {
-          uint4 vop = read_pair_v<CT, D, i>(nt);
-          vop.x &= keep.x;  // a select: NaN in a masked position cannot leak
-          vop.y &= keep.y;
-          vop.z &= keep.z;
-          vop.w &= keep.w;
-#pragma unroll
-          for (int j = 0; j < kT; ++j) st[j].acc[nt] = mma_k32<kBF>(vop, pop[j], st[j].acc[nt]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kT; ++j)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) zc[j][q] = zn[j][q];
-    };
-    stage_barrier<63>();  // the stages' previous readers are done
-    static_for<0, kS - 1>([&](auto I) { issue(I, decltype(I)::value); });
-    stage_barrier<P::kPerWave * (kS - 2)>();  // pair 0 landed for every wavefront
-    scores_x(std::integral_constant<int, 0>{}, zc);
-    scores_y(std::integral_constant<int, 0>{}, zc);
-    int k0 = 0;
-    for (; k0 + kS <= npair; k0 += kS)
-      static_for<0, kS>([&](auto I) { step(I, k0 + decltype(I)::value); });
-    static_for<0, kS>([&](auto I) {
-      if (k0 + decltype(I)::value < npair) step(I, k0 + decltype(I)::value);
-    });
-    tbl = tbl_next;
-  }
-#pragma unroll
-  for (int j = 0; j < kT; ++j)
-    emit_rows<QT, D>(a, st[j], vscale, vscale, -1, rs[j], rhq[j], rvalid[j]);
-}
-
-template <class CT, class QT, int D>
-hipError_t launch_prefill_dd(const DecodeArgs &a, hipStream_t s) {
-  const int g = a.num_q_heads / a.cache.num_kv_heads;
-  const int64_t groups = ((int64_t)a.max_query_len * g + kPrefillRows - 1) / kPrefillRows;
-  const int64_t items = (int64_t)a.num_seqs * a.cache.num_kv_heads * groups;
-  if (items == 0) return hipSuccess;
-  const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
-  prefill_mfma_kernel<CT, QT, D><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
-  return hipGetLastError();
-}
-
-template <class CT, class QT>
-hipError_t launch_prefill_d(const DecodeArgs &a, hipStream_t s) {
-  return a.cache.head_dim == 64 ? launch_prefill_dd<CT, QT, 64>(a, s)
-                                : launch_prefill_dd<CT, QT, 128>(a, s);
-}
 
 // Compute units of the current device, looked up once per device.
 int device_cus() {
@@ -1892,15 +1201,6 @@ bool decode_mfma_supports(const DecodeArgs &a) {
   // an empty pool has no tile for the ring's idle slots to read
   return types && g >= 1 && g <= 16 && (a.cache.head_dim == 64 || a.cache.head_dim == 128) &&
          q_aligned && a.cache.num_blocks > 0;
-}
-
-hipError_t launch_prefill_mfma(const DecodeArgs &a, hipStream_t s) {
-  switch (a.cache.dtype) {
-    case kF16: return launch_prefill_d<f16_t, f16_t>(a, s);
-    case kBF16: return launch_prefill_d<bf16_t, bf16_t>(a, s);
-    case kFP8: return launch_prefill_d<fp8_t, f16_t>(a, s);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
