@@ -324,10 +324,13 @@ void prefill_mfma_kernel(DecodeArgs a) {
     int tbl_next = c0 + 64 < jb1 ? first_table_entries(table, c0 + 64, jb1) : -1;
     asm volatile("" : "+v"(tbl));
     auto id = [&](int b) { return b < nk ? __builtin_amdgcn_readlane(tbl, b) : -1; };
+    int pid[kS][2];  // block ids of the pair in each stage, kept from its copy to its step
     auto issue = [&](auto I, int k) {  // pair k into stage I (past the end: empty copies)
-      const int ba = id(2 * k), bb = id(2 * k + 1);
-      stage_pair<CT, D, decltype(I)::value>(pc, ba, (unsigned)ba < (unsigned)nb, bb,
-                                            (unsigned)bb < (unsigned)nb);
+      constexpr int i = decltype(I)::value;
+      pid[i][0] = id(2 * k);
+      pid[i][1] = id(2 * k + 1);
+      stage_pair<CT, D, i>(pc, pid[i][0], (unsigned)pid[i][0] < (unsigned)nb, pid[i][1],
+                           (unsigned)pid[i][1] < (unsigned)nb);
     };
     // Raw scores of the pair in stage I, this lane's 8 positions per tile (X then Y products).
     auto scores_x = [&](auto I, float (&z)[kT][8]) {
@@ -357,9 +360,9 @@ void prefill_mfma_kernel(DecodeArgs a) {
       // pair k + 1 landed for every wavefront, and every wavefront is done with pair k - 1's stage
       stage_barrier<P::kPerWave * (kS - 3)>();
       issue(std::integral_constant<int, (i + kS - 1) % kS>{}, k + kS - 1);
-      const int ba = id(2 * k), bb = id(2 * k + 1);
-      const bool oka = (unsigned)ba < (unsigned)nb, okb = (unsigned)bb < (unsigned)nb;
-      const bool okm = (grp >> 1) ? okb : oka;  // this lane's block
+      const bool oka = (unsigned)pid[i][0] < (unsigned)nb, okb = (unsigned)pid[i][1] < (unsigned)nb;
+      // this lane's block is present (read only inside the masked branches)
+      auto okm = [&]() { return (grp >> 1) ? okb : oka; };
       const int t0 = (c0 + 2 * k) * kBlock;
       const int tl = t0 + 8 * grp;  // this lane's first position of the pair
       // Masks only where they change something (wave-uniform tests): the scores where some row's
@@ -371,7 +374,7 @@ void prefill_mfma_kernel(DecodeArgs a) {
       if (zmask) {
 #pragma unroll
         for (int j = 0; j < kT; ++j) {
-          const int rel = (okm ? lim[j] : 0) - tl;
+          const int rel = (okm() ? lim[j] : 0) - tl;
 #pragma unroll
           for (int q = 0; q < 8; ++q) zc[j][q] = q < rel ? zc[j][q] : -INFINITY;  // never NaN
         }
@@ -404,7 +407,7 @@ void prefill_mfma_kernel(DecodeArgs a) {
           for (int j = 0; j < kT; ++j) st[j].acc[nt] = mma_k32<kBF>(vop, pop[j], st[j].acc[nt]);
         }
       } else {
-        const uint4 keep = pair_keep((okm ? end : 0) - tl);
+        const uint4 keep = pair_keep((okm() ? end : 0) - tl);
 #pragma unroll
         for (int nt = 0; nt < F::kNT; ++nt) {
           uint4 vop = read_pair_v<CT, D, i>(nt);
