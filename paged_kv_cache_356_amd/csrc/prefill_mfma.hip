@@ -400,12 +400,16 @@ void prefill_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < kT; ++j) pop[j] = pair_probs<CT, D>(zc[j], ks, st[j]);
       if (!vmask) {
+        // every V^T read issued before the products, so the LDS latency is paid once per pair
+        uint4 vop[F::kNT];
 #pragma unroll
-        for (int nt = 0; nt < F::kNT; ++nt) {
-          const uint4 vop = read_pair_v<CT, D, i>(nt);
+        for (int nt = 0; nt < F::kNT; ++nt) vop[nt] = read_pair_v<CT, D, i>(nt);
 #pragma unroll
-          for (int j = 0; j < kT; ++j) st[j].acc[nt] = mma_k32<kBF>(vop, pop[j], st[j].acc[nt]);
-        }
+        for (int nt = 0; nt < F::kNT; ++nt)
+#pragma unroll
+          for (int j = 0; j < kT; ++j) st[j].acc[nt] = mma_k32<kBF>(vop[nt], pop[j], st[j].acc[nt]);
+        __builtin_amdgcn_sched_group_barrier(0x100, F::kNT, 0);       // the LDS reads first,
+        __builtin_amdgcn_sched_group_barrier(0x8, F::kNT * kT, 0);    // then the products
       } else {
         const uint4 keep = pair_keep((okm() ? end : 0) - tl);
 #pragma unroll
