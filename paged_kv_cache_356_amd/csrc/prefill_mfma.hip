@@ -180,15 +180,22 @@ __device__ __forceinline__ f4_t block_qk(const uint4 (&k)[N], const RowState<D> 
   return st;
 }
 
-// Maximum over the four 16-lane rows of a wavefront (lanes c, c + 16, c + 32, c + 48), by two
-// lane swaps on the vector ALU (no LDS round trip).
-__device__ __forceinline__ float max_over_rows(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+// Maxima over the four 16-lane rows of a wavefront (lanes c, c + 16, c + 32, c + 48) of two values
+// at once, t and u (the two tiles' pair maxima), by three lane swaps on the vector ALU: the first
+// swap pairs row 1 of t with row 0 of u (and row 3 with row 2), so one maximum leaves t's rows
+// {0, 1} and {2, 3} reduced in rows 0 and 2 and u's in rows 1 and 3; swapping the halves reduces
+// over all four rows; a last swap of rows hands every lane both results.
+__device__ __forceinline__ void max_over_rows2(float &t, float &u) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(u), false,
                                                   false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+  const float m1 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false,
                                                   false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  const float m2 = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(m2), __float_as_uint(m2), false,
+                                                  false);
+  t = __uint_as_float(c[0]);
+  u = __uint_as_float(c[1]);
 }
 
 // Softmax over a pair, in two parts, so that the next pair's score products can be issued beside
@@ -196,13 +203,21 @@ __device__ __forceinline__ float max_over_rows(float x) {
 // i < 4, product Y the rest); ks > 0 is the logit scale (a negative scale is folded into the
 // query's sign, a zero one replaced by the smallest normal float, which leaves every probability
 // at exactly 1 as a zero scale does).
-// Part 1: the pair's row maximum, scaled once; returns whether it exceeds the running maximum by
-// more than kSlack (base 2), when the running state must be rescaled.
-__device__ __forceinline__ bool pair_max(const float (&z)[8], float ks, float m, float &mx) {
-  float x = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                  fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-  mx = max_over_rows(x) * ks;  // -inf stays -inf
-  return mx > m + kSlack;
+// Part 1: the pair's row maxima of both tiles, scaled once; grow[j] says whether tile j's exceeds
+// its running maximum by more than kSlack (base 2), when its running state must be rescaled.
+template <int D>
+__device__ __forceinline__ void pair_max2(const float (&z)[2][8], float ks, const RowState<D> (&rs)[2],
+                                          float (&mx)[2], bool (&grow)[2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    mx[j] = fmaxf(fmaxf(fmaxf(z[j][0], z[j][1]), fmaxf(z[j][2], z[j][3])),
+                  fmaxf(fmaxf(z[j][4], z[j][5]), fmaxf(z[j][6], z[j][7])));
+  max_over_rows2(mx[0], mx[1]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    mx[j] *= ks;  // -inf stays -inf
+    grow[j] = mx[j] > rs[j].m + kSlack;
+  }
 }
 
 // Rescale this lane's running state to the new maximum mx when `grow` (per lane).
@@ -384,13 +399,10 @@ void prefill_mfma_kernel(DecodeArgs a) {
       float zn[kT][8];
       scores_x(std::integral_constant<int, inext>{}, zn);
       float mx[kT];
-      bool grow[kT], any = false;
-#pragma unroll
-      for (int j = 0; j < kT; ++j) {
-        grow[j] = pair_max(zc[j], ks, st[j].m, mx[j]);
-        any = any || grow[j];
-      }
-      if (__builtin_amdgcn_ballot_w64(any) != 0) {
+      bool grow[kT];
+      static_assert(kT == 2, "the row maxima are reduced two tiles at a time");
+      pair_max2<D>(zc, ks, st, mx, grow);
+      if ((__builtin_amdgcn_ballot_w64(grow[0]) | __builtin_amdgcn_ballot_w64(grow[1])) != 0) {
 #pragma unroll
         for (int j = 0; j < kT; ++j) pair_rescale(grow[j], mx[j], st[j]);
       }

@@ -571,7 +571,17 @@ def test_prefill_negative_and_zero_scale(cache_dtype, scale):
     _prefill_case(cache_dtype, 128, scale)
 
 
-def _prefill_case(cache_dtype, D, scale):
+@pytest.mark.parametrize("cache_dtype", ["f16", "fp8"])
+def test_prefill_rows_of_very_different_scales(cache_dtype):
+    """Query rows scaled by 1 to 64 (a factor per token and query head), so that the logits of rows
+    sharing a wavefront, and of its two 16-row tiles, differ by far more than the running maximum's
+    headroom: a row maximum taken over the wrong lanes would overflow the 16-bit probabilities.
+    (f16 probabilities: with bf16 ones the rounding of a nearly one-hot row's two or three largest
+    probabilities, 2^-9 each, alone reaches the bf16 tolerance.)"""
+    _prefill_case(cache_dtype, 128, 1.0 / math.sqrt(128), row_scales=True)
+
+
+def _prefill_case(cache_dtype, D, scale, row_scales=False):
     q_dtype = "f16" if cache_dtype == "fp8" else cache_dtype
     Hq, H, nb, B = 28, 4, 512, 16
     lengths = [37, 200, 18, 700, 9, 64, 1500]
@@ -597,7 +607,11 @@ def _prefill_case(cache_dtype, D, scale):
                              torch.from_numpy(np.concatenate(slots)).cuda())
     qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
     T = int(qs[-1])
-    q = torch.randn(T, Hq, D, generator=g).to(wl.TORCH_DTYPES[q_dtype]).cuda()
+    q = torch.randn(T, Hq, D, generator=g)
+    if row_scales:  # 2^0 .. 2^6 by token and query head
+        e = (torch.arange(T).view(T, 1) * 3 + torch.arange(Hq).view(1, Hq) * 5) % 7
+        q = q * torch.pow(2.0, e.to(torch.float32)).unsqueeze(-1)
+    q = q.to(wl.TORCH_DTYPES[q_dtype]).cuda()
     out = torch.full_like(q, 7.0)
     api.pa_prefill_attention(out, q, cache, torch.from_numpy(tables).cuda(),
                              torch.from_numpy(ctx).cuda(), torch.from_numpy(qs).cuda(),
