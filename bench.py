@@ -401,6 +401,8 @@ def main() -> int:
     ap.add_argument("--fused", action="store_true",
                     help="step through pa_decode_attention_append (the cache write inside the "
                          "decode kernel) instead of reshape_and_cache + decode")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="deal the decode's work in batch order instead of pa_decode_plan's order")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--swap", action="store_true",
@@ -457,13 +459,25 @@ def main() -> int:
                         keep_values=not args.no_cpu_baseline,
                         partition_size=None if args.partition < 0 else args.partition,
                         contiguous=args.contiguous,
-                        keep_layers=[0])
+                        keep_layers=[0], plan=not args.no_plan)
     batch.use_prefix = batch.use_prefix and not args.no_prefix
     torch.cuda.synchronize()
     log(f"[bench] {w.name}: built {sets} set(s), {len(batch.layers)} layer(s) in "
         f"{time.perf_counter() - t_build:.1f} s; lengths {wl.lengths_summary(batch.lengths)}")
 
     layers = batch.layers
+    # the planner's host time for one set (step metadata, computed beside the block tables)
+    plan_us = None
+    if not args.no_plan:
+        st0 = batch.sets[0]
+        t0 = time.perf_counter()
+        for _ in range(20):
+            api.pa_decode_plan(batch.caches[layers[0]], st0.q[layers[0]].dtype, st0.ctx,
+                               w.num_q_heads, batch.max_blocks, batch.max_context_len,
+                               batch.prefix_len if batch.use_prefix else 0, batch.partition_size,
+                               (api.PA_DECODE_FORCE_VALU if args.valu else 0) |
+                               (api.PA_DECODE_PLAN_APPEND if args.fused else 0))
+        plan_us = round((time.perf_counter() - t0) / 20 * 1e6, 1)
 
     # Every library call enqueues on torch's current stream: the default stream when run eagerly,
     # the capture stream while a graph is being captured.
@@ -608,6 +622,11 @@ def main() -> int:
                 w.num_seqs, w.num_kv_heads, batch.max_context_len),
             "kernel": "valu" if args.valu else "default",
             "shared_prefix_decode": bool(batch.use_prefix),
+            "dealing_order": "batch order" if args.no_plan else
+                             "pa_decode_plan (host, from each set's context lengths)" if
+                             batch.order(0, flags, fused) is not None else
+                             "pa_decode_plan: the batch order itself for these lengths",
+            "plan_host_us": plan_us,
             "block_placement": "contiguous (free list in pool order)" if args.contiguous else
                                "scattered (seeded permutation of the pool)",
             "step_calls": "copy_blocks (when the step clones) + per layer " +
@@ -644,7 +663,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(w, args.partition < 0 and not args.valu and not fused and
-                                        not args.contiguous and
+                                        not args.contiguous and not args.no_plan and
                                         not args.num_blocks and not args.no_prefix and
                                         args.block_size == 16),
             "traffic_note": "HBM bytes per call from rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE "
@@ -662,7 +681,7 @@ def main() -> int:
         log(f"[bench] calibration {res['calibration']}")
     default_run = (args.workload == DEFAULT_WORKLOAD and not fused and not args.valu and
                    args.partition < 0 and args.block_size == 16 and not args.contiguous and
-                   not args.no_prefix and not args.num_blocks)
+                   not args.no_prefix and not args.num_blocks and not args.no_plan)
     targets = args.targets if args.targets is not None else \
         ("bf16_32k_batch8" if default_run else "")
     if targets:

@@ -145,6 +145,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 /* Flags for pa_decode_attention. */
 #define PA_DECODE_DEFAULT 0u
 #define PA_DECODE_FORCE_VALU 1u  /* use the vector-ALU kernel even where the matrix-core one applies */
+#define PA_DECODE_PLAN_APPEND 2u /* pa_decode_plan only: plan for pa_decode_attention_append's grid */
 
 /*
  * pa_decode_attention — one decode step of paged attention for a batch of sequences.
@@ -168,6 +169,16 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                 [0, num_blocks) is never dereferenced: the B positions it covers are left out.
  *   context_lens  device int32 [num_seqs]; L includes the token written this step.  Values are
  *                 clamped to [0, min(max_context_len, B * max_blocks_per_seq)].
+ *   seq_order     NULL, or device int32 [num_seqs] holding each of 0 .. num_seqs - 1 once: the
+ *                 order in which the sequences' work is dealt to the device's wavefronts
+ *                 (pa_decode_plan computes a balanced one from the host's copy of the context
+ *                 lengths).  It changes the time of the call, never its result: the output is the
+ *                 same bit for bit with any permutation.  An entry outside 0 .. num_seqs - 1 is
+ *                 skipped, and a sequence that no entry names gets undefined output (PA_DEBUG
+ *                 checks that the array is a permutation).  Used by the matrix-core kernel's
+ *                 persistent grid (at most 4,096 sequences; 2,048 with a shared prefix) while
+ *                 num_seqs times the partitions of the longest row stays below 2^20; ignored
+ *                 elsewhere.
  *   max_context_len  host upper bound of context_lens, used to size the launch without reading
  *                 the device.
  *   scale         softmax scale, normally 1 / sqrt(head_dim).
@@ -193,9 +204,38 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int64_t q_stride,
                               const pa_cache *cache, const int32_t *block_tables,
                               int32_t max_blocks_per_seq, const int32_t *context_lens,
-                              int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
-                              float scale, int32_t partition_size, void *workspace,
-                              size_t workspace_bytes, uint32_t flags, void *stream);
+                              const int32_t *seq_order, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t max_context_len, float scale, int32_t partition_size,
+                              void *workspace, size_t workspace_bytes, uint32_t flags,
+                              void *stream);
+
+/*
+ * pa_decode_plan — a dealing order for pa_decode_attention's seq_order, computed on the host
+ * from a HOST copy of the step's context lengths: step metadata that the scheduler holds beside
+ * the block tables the kernel walks ([Digest] "PagedAttention in one picture"), while the order
+ * only changes how the kernel fetches, not the attention it computes ([Digest] "Misconceptions").  Every sequence's positions are cut into partitions (work items) as the call
+ * cuts them; the sequences are taken by the size of their largest item, largest first, and put
+ * into rounds of as many items as the call's grid has wavefronts for them, the rounds filled
+ * alternately from the largest and from the smallest sequences left, so that a wavefront dealt a
+ * large item in one round gets a small one in the next and the wavefronts end close together.
+ *   cache, q_dtype, num_q_heads, max_blocks_per_seq, max_context_len, prefix_len,
+ *   partition_size  those of the decode call the order is for (prefix_len 0: pa_decode_attention;
+ *                 > 0: pa_decode_attention_shared_prefix).
+ *   context_lens  HOST int32 [num_seqs], clamped as the call clamps them.
+ *   flags         PA_DECODE_FORCE_VALU as in the call; PA_DECODE_PLAN_APPEND for the grid of
+ *                 pa_decode_attention_append.
+ *   seq_order     HOST int32 [num_seqs], written: a permutation of 0 .. num_seqs - 1 (the identity
+ *                 where the call would not deal a list or ignores the order: the vector-ALU
+ *                 kernel, the direct grid, 2^20 or more partition slots in all).
+ *   round_items   optional (NULL): the items per round, the grid's wavefronts that take sequence
+ *                 items on the current device (0 with the identity).
+ * The grid depends on the current device (its compute units); an order planned for another
+ * device, or for other lengths, is still a valid seq_order, only less balanced.
+ */
+pa_status pa_decode_plan(const pa_cache *cache, int32_t q_dtype, const int32_t *context_lens,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                         int32_t max_context_len, int32_t prefix_len, int32_t partition_size,
+                         uint32_t flags, int32_t *seq_order, int32_t *round_items);
 
 /*
  * pa_decode_attention_noalloc — pa_decode_attention without a workspace argument, for callers that
@@ -204,8 +244,8 @@ pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int
  * PA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on each GPU it runs on until the
  * process ends; the call itself allocates nothing (no hipMalloc, hipFree or allocating library
  * routine) and its first call on a device looks up that device's copy of the array.
- *   All arguments and results are those of pa_decode_attention (same kernels, same partition
- *   sizes, bit-identical output).
+ *   All arguments and results are those of pa_decode_attention with seq_order NULL (same
+ *   kernels, same partition sizes, bit-identical output).
  *   A call whose partials need more than PA_NOALLOC_SCRATCH_BYTES (the need is at most
  *   pa_decode_workspace_bytes() for the same sizes) returns PA_ERR_WORKSPACE before touching the
  *   device; so do all the argument errors of pa_decode_attention.
@@ -249,7 +289,8 @@ pa_status pa_decode_attention_shared_prefix(void *out, const void *query, int32_
                                             int64_t q_stride, const pa_cache *cache,
                                             const int32_t *block_tables,
                                             int32_t max_blocks_per_seq,
-                                            const int32_t *context_lens, int32_t num_seqs,
+                                            const int32_t *context_lens,
+                                            const int32_t *seq_order, int32_t num_seqs,
                                             int32_t num_q_heads, int32_t max_context_len,
                                             float scale, const int32_t *prefix_table,
                                             int32_t prefix_len, int32_t partition_size,
@@ -292,8 +333,8 @@ pa_status pa_decode_attention_append(void *out, const void *query, int32_t q_dty
                                      const void *value, int64_t key_stride, int64_t value_stride,
                                      const int64_t *slot_mapping, const int32_t *block_tables,
                                      int32_t max_blocks_per_seq, const int32_t *context_lens,
-                                     int32_t num_seqs, int32_t num_q_heads,
-                                     int32_t max_context_len, float scale,
+                                     const int32_t *seq_order, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t max_context_len, float scale,
                                      const int32_t *prefix_table, int32_t prefix_len,
                                      int32_t partition_size, void *workspace,
                                      size_t workspace_bytes, uint32_t flags, void *stream);
@@ -364,6 +405,10 @@ pa_status pa_check_slots(const int64_t *slots_host, int32_t num_tokens, int32_t 
 pa_status pa_check_context_lens(const int32_t *context_lens_host, int32_t num_seqs,
                                 int32_t max_context_len);
 
+/* Host-side check of a HOST copy of a seq_order: PA_ERR_SHAPE unless it holds each of
+ * 0 .. num_seqs - 1 exactly once. */
+pa_status pa_check_seq_order(const int32_t *seq_order_host, int32_t num_seqs);
+
 /*
  * Debug checks (PA_DEBUG).  Off by default; on when the environment variable PA_DEBUG is set to a
  * non-zero value at the library's first use, or after pa_set_debug(1).  With them on, before
@@ -373,7 +418,7 @@ pa_status pa_check_context_lens(const int32_t *context_lens_host, int32_t num_se
  *   pa_copy_blocks copies block_pairs to the host and runs pa_check_copy_pairs (PA_ERR_ALIAS,
  *     PA_ERR_SHAPE);
  *   every decode entry point copies context_lens to the host and runs pa_check_context_lens
- *     (PA_ERR_SHAPE).
+ *     (PA_ERR_SHAPE), and a seq_order, when given, with pa_check_seq_order (PA_ERR_SHAPE).
  * The copies wait for the stream to reach the call (hipStreamSynchronize), so debug mode gives up
  * the library's rule of never synchronising; a failed check enqueues nothing.  The switch is
  * process-wide.

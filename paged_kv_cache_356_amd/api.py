@@ -19,6 +19,7 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_BLOCK_SIZE = 16
 PA_DECODE_DEFAULT = 0
 PA_DECODE_FORCE_VALU = 1
+PA_DECODE_PLAN_APPEND = 2  # pa_decode_plan only: plan for pa_decode_attention_append
 PA_NOALLOC_SCRATCH_BYTES = 64 << 20  # the fixed device scratch of pa_decode_attention_noalloc
 DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
 TORCH_CODES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
@@ -35,7 +36,8 @@ EXPORTS = [
     "pa_decode_workspace_bytes", "pa_decode_attention", "pa_decode_attention_shared_prefix",
     "pa_decode_attention_append", "pa_decode_attention_noalloc",
     "pa_decode_shared_prefix_workspace_bytes", "pa_copy_blocks", "pa_check_copy_pairs",
-    "pa_check_slots", "pa_check_context_lens", "pa_set_debug", "pa_debug_enabled",
+    "pa_check_slots", "pa_check_context_lens", "pa_check_seq_order", "pa_decode_plan",
+    "pa_set_debug", "pa_debug_enabled",
     "pa_prefill_attention", "pa_swap_blocks", "pa_bm_set_host_blocks", "pa_bm_swap_out",
     "pa_bm_swap_in",
     "pa_bm_num_free_host", "pa_bm_is_swapped",
@@ -78,14 +80,17 @@ def lib() -> ctypes.CDLL:
             "pa_reshape_and_cache": (_i32, [_cp, _vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp]),
             "pa_decode_auto_partition": (_i32, [_i32, _i32, _i32]),
             "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
-            "pa_decode_attention": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _i32, _vp, _i32, _i32,
-                                           _i32, _f32, _i32, _vp, _sz, _u32, _vp]),
+            "pa_decode_attention": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _i32, _vp, _vp, _i32,
+                                           _i32, _i32, _f32, _i32, _vp, _sz, _u32, _vp]),
             "pa_decode_attention_shared_prefix": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _i32, _vp,
-                                                          _i32, _i32, _i32, _f32, _vp, _i32, _i32,
-                                                          _vp, _sz, _u32, _vp]),
+                                                          _vp, _i32, _i32, _i32, _f32, _vp, _i32,
+                                                          _i32, _vp, _sz, _u32, _vp]),
             "pa_decode_attention_append": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _vp, _i64, _i64,
-                                                   _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp,
-                                                   _i32, _i32, _vp, _sz, _u32, _vp]),
+                                                   _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
+                                                   _vp, _i32, _i32, _vp, _sz, _u32, _vp]),
+            "pa_decode_plan": (_i32, [_cp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _u32,
+                                      _vp, _vp]),
+            "pa_check_seq_order": (_i32, [_vp, _i32]),
             "pa_decode_attention_noalloc": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _i32, _vp,
                                                     _i32, _i32, _i32, _f32, _i32, _u32, _vp]),
             "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32,
@@ -260,19 +265,23 @@ class DecodeCall:
                  scale: float, partition_size: int = 0, workspace: torch.Tensor | None = None,
                  flags: int = PA_DECODE_DEFAULT, prefix_table: torch.Tensor | None = None,
                  prefix_len: int = 0, key: torch.Tensor | None = None,
-                 value: torch.Tensor | None = None, slot_mapping: torch.Tensor | None = None):
+                 value: torch.Tensor | None = None, slot_mapping: torch.Tensor | None = None,
+                 seq_order: torch.Tensor | None = None):
         S, Hq, D = query.shape
         assert out.shape == query.shape and out.dtype == query.dtype and out.is_contiguous()
         assert query.stride(2) == 1 and query.stride(1) == D  # rows contiguous, strided along S
         assert block_tables.dtype == torch.int32 and block_tables.is_contiguous()
         assert context_lens.dtype == torch.int32 and context_lens.is_contiguous()
+        if seq_order is not None:
+            assert seq_order.dtype == torch.int32 and seq_order.is_contiguous()
+            assert seq_order.shape == (S,)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         head = (_ptr(out), _ptr(query), TORCH_CODES[query.dtype], query.stride(0) if S else 0,
                 ctypes.byref(cache.struct()), _ptr(block_tables), block_tables.shape[1],
-                _ptr(context_lens), S, Hq, int(max_context_len), float(scale))
+                _ptr(context_lens), _ptr(seq_order), S, Hq, int(max_context_len), float(scale))
         tail = (int(partition_size), _ptr(workspace), ws_bytes, int(flags))
         self._keep = (out, query, cache, block_tables, context_lens, workspace, prefix_table, key,
-                      value, slot_mapping)
+                      value, slot_mapping, seq_order)
         if key is not None:
             assert value is not None and slot_mapping is not None
             assert key.dtype == query.dtype and value.dtype == query.dtype
@@ -302,11 +311,29 @@ def pa_decode_attention(out: torch.Tensor, query: torch.Tensor, cache: KVCache,
                         block_tables: torch.Tensor, context_lens: torch.Tensor,
                         max_context_len: int, scale: float, partition_size: int = 0,
                         workspace: torch.Tensor | None = None, flags: int = PA_DECODE_DEFAULT,
-                        stream=None) -> None:
+                        stream=None, seq_order: torch.Tensor | None = None) -> None:
     """out, query: [S, num_q_heads, head_dim] (query rows may be strided along S);
-    block_tables int32 [S, max_blocks_per_seq]; context_lens int32 [S]."""
+    block_tables int32 [S, max_blocks_per_seq]; context_lens int32 [S]; seq_order: None or device
+    int32 [S], a permutation of the sequences (the dealing order, pa_decode_plan)."""
     DecodeCall(out, query, cache, block_tables, context_lens, max_context_len, scale,
-               partition_size, workspace, flags)(stream)
+               partition_size, workspace, flags, seq_order=seq_order)(stream)
+
+
+def pa_decode_plan(cache: KVCache, q_dtype: torch.dtype, context_lens, num_q_heads: int,
+                   max_blocks_per_seq: int, max_context_len: int, prefix_len: int = 0,
+                   partition_size: int = 0, flags: int = PA_DECODE_DEFAULT,
+                   with_round: bool = False):
+    """The dealing order pa_decode_plan computes from the host's context lengths (a sequence of
+    ints): an int32 numpy array [S]; with_round also returns the items per round."""
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    S = int(lens.shape[0])
+    order = np.empty(S, np.int32)
+    rnd = ctypes.c_int32(0)
+    _check(lib().pa_decode_plan(ctypes.byref(cache.struct()), TORCH_CODES[q_dtype], _ptr(lens), S,
+                                int(num_q_heads), int(max_blocks_per_seq), int(max_context_len),
+                                int(prefix_len), int(partition_size), int(flags), _ptr(order),
+                                ctypes.byref(rnd)))
+    return (order, rnd.value) if with_round else order
 
 
 def pa_decode_attention_noalloc(out: torch.Tensor, query: torch.Tensor, cache: KVCache,
@@ -333,13 +360,14 @@ def pa_decode_attention_append(out: torch.Tensor, query: torch.Tensor, cache: KV
                                max_context_len: int, scale: float,
                                prefix_table: torch.Tensor | None = None, prefix_len: int = 0,
                                partition_size: int = 0, workspace: torch.Tensor | None = None,
-                               flags: int = PA_DECODE_DEFAULT, stream=None) -> None:
+                               flags: int = PA_DECODE_DEFAULT, stream=None,
+                               seq_order: torch.Tensor | None = None) -> None:
     """pa_reshape_and_cache of each sequence's new token (key, value [S, num_kv_heads, head_dim] in
     the query dtype, slot_mapping int64 [S]: the slot of position context_lens[s] - 1) followed by
     the decode (plain, or shared-prefix when prefix_table is given), in one call."""
     DecodeCall(out, query, cache, block_tables, context_lens, max_context_len, scale,
                partition_size, workspace, flags, prefix_table, prefix_len, key, value,
-               slot_mapping)(stream)
+               slot_mapping, seq_order)(stream)
 
 
 def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
@@ -356,11 +384,13 @@ def pa_decode_attention_shared_prefix(out: torch.Tensor, query: torch.Tensor, ca
                                       prefix_table: torch.Tensor, prefix_len: int,
                                       partition_size: int = 0,
                                       workspace: torch.Tensor | None = None,
-                                      flags: int = PA_DECODE_DEFAULT, stream=None) -> None:
+                                      flags: int = PA_DECODE_DEFAULT, stream=None,
+                                      seq_order: torch.Tensor | None = None) -> None:
     """pa_decode_attention for a batch sharing its first prefix_len positions (the blocks in
     prefix_table, device int32 [prefix_len / 16])."""
     DecodeCall(out, query, cache, block_tables, context_lens, max_context_len, scale,
-               partition_size, workspace, flags, prefix_table, prefix_len)(stream)
+               partition_size, workspace, flags, prefix_table, prefix_len,
+               seq_order=seq_order)(stream)
 
 
 class PrefillCall:
@@ -465,6 +495,11 @@ def pa_check_slots(slots: np.ndarray, num_blocks: int, block_size: int = PA_BLOC
 def pa_check_context_lens(context_lens: np.ndarray, max_context_len: int) -> None:
     lens = np.ascontiguousarray(context_lens, np.int32)
     _check(lib().pa_check_context_lens(_ptr(lens), lens.shape[0], int(max_context_len)))
+
+
+def pa_check_seq_order(seq_order: np.ndarray) -> None:
+    order = np.ascontiguousarray(seq_order, np.int32)
+    _check(lib().pa_check_seq_order(_ptr(order), order.shape[0]))
 
 
 def pa_set_debug(on: bool) -> None:

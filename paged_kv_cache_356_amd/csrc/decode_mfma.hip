@@ -1000,19 +1000,40 @@ void decode_mfma_kernel(DecodeArgs a) {
     return;
   }
   constexpr int kScan = kPre ? kMaxScanSeqsPrefix : kMaxScanSeqs;
-  __shared__ int prefix[kScan + 1];  // items of the sequences before s
-  __shared__ int lens[kScan];        // clamped context lengths
+  static_assert(kScan <= (1 << (32 - kOrderCountBits)), "sequence ids must fit beside the counts");
+  // prefix[i]: items of the list entries before entry i; with a dealing order the entry's sequence
+  // sits above the count, in bits kOrderCountBits and up (the launcher passes an order only when
+  // every count fits below them).
+  __shared__ int prefix[kScan + 1];
+  __shared__ int lens[kScan];  // clamped context lengths, by sequence
   __shared__ int wave_tot[kWaves];
-  // thread t counts the items of sequences [t * per, (t + 1) * per)
+  // The item list runs over the sequences in batch order, or in the caller's seq_order; an entry
+  // of seq_order outside [0, S) contributes no item.  Thread t counts the items of list entries
+  // [t * per, (t + 1) * per).
+  const int32_t *ord = a.seq_order;
   const int per = (S + 255) / 256;
   const int s0 = tid * per;
   int mine = 0;
-  for (int i = 0; i < per; ++i)
-    if (s0 + i < S) {
-      const int L = clamp_len(a, s0 + i);
-      lens[s0 + i] = L;
-      mine += seq_items(a, L);
-    }
+  if (ord) {
+    for (int i = 0; i < per; ++i)
+      if (s0 + i < S) {
+        lens[s0 + i] = clamp_len(a, s0 + i);
+        prefix[s0 + i] = ord[s0 + i];  // this thread's entries, until their counts replace them
+      }
+    __syncthreads();
+    for (int i = 0; i < per; ++i)
+      if (s0 + i < S) {
+        const int s = prefix[s0 + i];
+        mine += (unsigned)s < (unsigned)S ? seq_items(a, lens[s]) : 0;
+      }
+  } else {
+    for (int i = 0; i < per; ++i)
+      if (s0 + i < S) {
+        const int L = clamp_len(a, s0 + i);
+        lens[s0 + i] = L;
+        mine += seq_items(a, L);
+      }
+  }
   int incl = mine;  // inclusive scan over the wavefront
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -1024,10 +1045,17 @@ void decode_mfma_kernel(DecodeArgs a) {
   int run = incl - mine;
   for (int v = 0; v < w; ++v) run += wave_tot[v];
   for (int i = 0; i < per; ++i) {
-    const int s = s0 + i;
-    if (s < S) {
-      prefix[s] = run;
-      run += seq_items(a, lens[s]);
+    const int j = s0 + i;
+    if (j < S) {
+      if (ord) {
+        const int s = prefix[j];
+        const bool valid = (unsigned)s < (unsigned)S;
+        prefix[j] = run | (int)((unsigned)(valid ? s : 0) << kOrderCountBits);
+        run += valid ? seq_items(a, lens[s]) : 0;
+      } else {
+        prefix[j] = run;
+        run += seq_items(a, lens[j]);
+      }
     }
   }
   if (tid == 255) prefix[S] = run;  // thread 255 holds the grand total (its chunk ends at S or later)
@@ -1074,14 +1102,16 @@ void decode_mfma_kernel(DecodeArgs a) {
   auto item_of = [&](int f) {
     const int pf = f / H;
     const int h = f - pf * H;
-    int lo = 0, hi = S - 1;  // largest s with prefix[s] <= pf (LDS values, made uniform)
+    const int cmask = ord ? (1 << kOrderCountBits) - 1 : -1;
+    int lo = 0, hi = S - 1;  // largest entry whose count is <= pf (LDS values, made uniform)
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (__builtin_amdgcn_readfirstlane(prefix[mid]) <= pf) lo = mid;
+      if ((__builtin_amdgcn_readfirstlane(prefix[mid]) & cmask) <= pf) lo = mid;
       else hi = mid - 1;
     }
-    return sequence_item(a, lo, __builtin_amdgcn_readfirstlane(lens[lo]),
-                         pf - __builtin_amdgcn_readfirstlane(prefix[lo]), h);
+    const int e = __builtin_amdgcn_readfirstlane(prefix[lo]);
+    const int s = ord ? (int)((unsigned)e >> kOrderCountBits) : lo;
+    return sequence_item(a, s, __builtin_amdgcn_readfirstlane(lens[s]), pf - (e & cmask), h);
   };
   // The next item's coordinates and first table entries are fetched before the current item
   // streams, so an item starts with one round trip to memory (its first blocks, with its query)
@@ -1146,41 +1176,84 @@ int resident_groups() {
   return n;
 }
 
-template <class CT, class QT, int D, bool kPre, int kB, bool kApp>
-hipError_t launch_ddpa(DecodeArgs a, hipStream_t s) {
-  const int64_t items = (int64_t)a.num_partitions * a.cache.num_kv_heads * a.num_seqs;
-  const int64_t direct = (items + kWaves - 1) / kWaves;  // one wavefront per item
-  a.persistent = a.num_seqs <= (kPre ? kMaxScanSeqsPrefix : kMaxScanSeqs);
-  dim3 grid((unsigned)direct);
-  a.num_cus = device_cus();
-  if (a.persistent) {
-    const int resident = resident_groups<CT, QT, D, kPre, kB, kApp>();
-    grid = dim3((unsigned)std::min<int64_t>(direct, resident));
+// The instantiation a call runs on, as a tag type for with_kernel's visitor.
+template <class CT_, class QT_, int D_, bool kPre_, int kB_, bool kApp_>
+struct KernelCfg {
+  using CT = CT_;
+  using QT = QT_;
+  static constexpr int D = D_, kB = kB_;
+  static constexpr bool kPre = kPre_, kApp = kApp_;
+};
+
+// Calls f(KernelCfg<...>{}) for the instantiation that computes `a`: cache dtype, head_dim, shared
+// prefix, block size, and the fused append (an instantiation of its own, so that the plain decode
+// keeps its registers).
+template <class CT, class QT, int D, bool kPre, int kB, class F>
+auto with_app(const DecodeArgs &a, F &&f) {
+  return a.append_slots ? f(KernelCfg<CT, QT, D, kPre, kB, true>{})
+                        : f(KernelCfg<CT, QT, D, kPre, kB, false>{});
+}
+
+template <class CT, class QT, int D, class F>
+auto with_blocks(const DecodeArgs &a, F &&f) {
+  if (a.prefix_len > 0) return with_app<CT, QT, D, true, 16>(a, f);
+  switch (a.cache.block_size) {
+    case 8: return with_app<CT, QT, D, false, 8>(a, f);
+    case 32: return with_app<CT, QT, D, false, 32>(a, f);
+    default: return with_app<CT, QT, D, false, 16>(a, f);
   }
-  decode_mfma_kernel<CT, QT, D, kPre, kB, kApp><<<grid, dim3(256), 0, s>>>(a);
+}
+
+template <class CT, class QT, class F>
+auto with_dim(const DecodeArgs &a, F &&f) {
+  return a.cache.head_dim == 64 ? with_blocks<CT, QT, 64>(a, f) : with_blocks<CT, QT, 128>(a, f);
+}
+
+// Grid of a call on the current device: direct (one wavefront per item, rounded up to whole
+// workgroups) or persistent (every workgroup that fits at once, at most the direct count).
+template <class C>
+dim3 decode_grid(DecodeArgs &a) {
+  const int64_t items = (int64_t)a.num_partitions * a.cache.num_kv_heads * a.num_seqs;
+  const int64_t direct = (items + kWaves - 1) / kWaves;
+  a.persistent = a.num_seqs <= (C::kPre ? kMaxScanSeqsPrefix : kMaxScanSeqs);
+  if (!a.persistent) return dim3((unsigned)direct);
+  const int resident = resident_groups<typename C::CT, typename C::QT, C::D, C::kPre, C::kB,
+                                       C::kApp>();
+  return dim3((unsigned)std::min<int64_t>(direct, resident));
+}
+
+template <class C>
+hipError_t launch_cfg(DecodeArgs a, hipStream_t s) {
+  const dim3 grid = decode_grid<C>(a);
+  a.num_cus = device_cus();
+  decode_mfma_kernel<typename C::CT, typename C::QT, C::D, C::kPre, C::kB, C::kApp>
+      <<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
-// The fused append is an instantiation of its own, so that the plain decode keeps its registers.
-template <class CT, class QT, int D, bool kPre, int kB>
-hipError_t launch_ddp(const DecodeArgs &a, hipStream_t s) {
-  return a.append_slots ? launch_ddpa<CT, QT, D, kPre, kB, true>(a, s)
-                        : launch_ddpa<CT, QT, D, kPre, kB, false>(a, s);
-}
-
-template <class CT, class QT, int D>
-hipError_t launch_dd(const DecodeArgs &a, hipStream_t s) {
-  if (a.prefix_len > 0) return launch_ddp<CT, QT, D, true, 16>(a, s);
-  switch (a.cache.block_size) {
-    case 8: return launch_ddp<CT, QT, D, false, 8>(a, s);
-    case 32: return launch_ddp<CT, QT, D, false, 32>(a, s);
-    default: return launch_ddp<CT, QT, D, false, 16>(a, s);
+// Wavefronts of the persistent grid that take sequence items (those of workgroups without prefix
+// groups); 0 for the direct grid.
+template <class C>
+int item_waves_cfg(DecodeArgs a) {
+  const int G = (int)decode_grid<C>(a).x;
+  if (!a.persistent) return 0;
+  int busy = 0;
+  if (C::kPre && a.prefix_len > 0) {
+    constexpr int kGroupRows = 16 * kPrefixTiles * kWaves;
+    const int64_t n_groups = ((int64_t)a.num_seqs * (a.num_q_heads / a.cache.num_kv_heads) +
+                              kGroupRows - 1) / kGroupRows;
+    busy = (int)std::min<int64_t>(n_groups * a.prefix_chunks * a.cache.num_kv_heads, G);
   }
+  return (G - busy) * kWaves;
 }
 
-template <class CT, class QT>
-hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
-  return a.cache.head_dim == 64 ? launch_dd<CT, QT, 64>(a, s) : launch_dd<CT, QT, 128>(a, s);
+template <class F>
+auto with_kernel(const DecodeArgs &a, F &&f) {
+  switch (a.cache.dtype) {
+    case kBF16: return with_dim<bf16_t, bf16_t>(a, f);
+    case kFP8: return with_dim<fp8_t, f16_t>(a, f);
+    default: return with_dim<f16_t, f16_t>(a, f);
+  }
 }
 
 }  // namespace
@@ -1204,12 +1277,14 @@ bool decode_mfma_supports(const DecodeArgs &a) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
-  switch (a.cache.dtype) {
-    case kF16: return launch_d<f16_t, f16_t>(a, s);
-    case kBF16: return launch_d<bf16_t, bf16_t>(a, s);
-    case kFP8: return launch_d<fp8_t, f16_t>(a, s);
-    default: return hipErrorInvalidValue;
-  }
+  if (a.cache.dtype != kF16 && a.cache.dtype != kBF16 && a.cache.dtype != kFP8)
+    return hipErrorInvalidValue;
+  return with_kernel(a, [&](auto c) { return launch_cfg<decltype(c)>(a, s); });
+}
+
+int decode_mfma_item_waves(const DecodeArgs &a) {
+  if (a.cache.dtype != kF16 && a.cache.dtype != kBF16 && a.cache.dtype != kFP8) return 0;
+  return with_kernel(a, [&](auto c) { return item_waves_cfg<decltype(c)>(a); });
 }
 
 }  // namespace pa

@@ -2,6 +2,7 @@
 // dispatch to the gfx950 kernels.  Nothing here allocates or synchronises device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -237,10 +238,11 @@ struct AppendIn {
 // workspace / workspace_bytes are then ignored.
 pa_status decode_common(const char *who, void *out, const void *query, int32_t q_dtype,
                         int64_t q_stride, const pa_cache *cache, const int32_t *block_tables,
-                        int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
-                        int32_t num_q_heads, int32_t max_context_len, float scale,
-                        const int32_t *prefix_table, int32_t prefix_len, int32_t partition_size,
-                        void *workspace, size_t workspace_bytes, uint32_t flags, void *stream,
+                        int32_t max_blocks_per_seq, const int32_t *context_lens,
+                        const int32_t *seq_order, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t max_context_len, float scale, const int32_t *prefix_table,
+                        int32_t prefix_len, int32_t partition_size, void *workspace,
+                        size_t workspace_bytes, uint32_t flags, void *stream,
                         const AppendIn *app = nullptr, bool noalloc = false) {
   pa_status st = check_cache(cache, who);
   if (st != PA_OK) return st;
@@ -313,6 +315,13 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
       st = pa_check_slots(sl.data(), num_seqs, cache->num_blocks, B);
       if (st != PA_OK) return fail(st, "%s: %s", who, g_last_error.c_str());
     }
+    if (seq_order) {
+      std::vector<int32_t> ord;
+      st = debug_fetch(seq_order, num_seqs, stream, ord, who, "seq_order");
+      if (st != PA_OK) return st;
+      st = pa_check_seq_order(ord.data(), num_seqs);
+      if (st != PA_OK) return fail(st, "%s: %s", who, g_last_error.c_str());
+    }
   }
   const int64_t cap = (int64_t)max_blocks_per_seq * B;
   const int32_t max_len = (int32_t)(max_context_len < cap ? max_context_len : cap);
@@ -337,6 +346,7 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
   a.num_partitions = 1;
   a.part_out = nullptr;
   a.part_ml = nullptr;
+  a.seq_order = seq_order;
   const bool force_valu = (flags & PA_DECODE_FORCE_VALU) != 0;
   // The prefix's tiles need the matrix-core kernel; elsewhere the plain decode gives the same result.
   bool use_prefix = prefix_len > 0;
@@ -385,6 +395,7 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
     return fail(PA_ERR_SHAPE, "%s: workspace must be 16-byte aligned", who);
   a.partition_size = pt;
   a.num_partitions = (int32_t)slots;
+  if (!pa::order_fits(num_seqs, slots)) a.seq_order = nullptr;
   if (use_prefix) {
     a.prefix_table = prefix_table;
     a.prefix_len = prefix_len;
@@ -457,13 +468,14 @@ extern "C" {
 pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int64_t q_stride,
                               const pa_cache *cache, const int32_t *block_tables,
                               int32_t max_blocks_per_seq, const int32_t *context_lens,
-                              int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
-                              float scale, int32_t partition_size, void *workspace,
-                              size_t workspace_bytes, uint32_t flags, void *stream) {
+                              const int32_t *seq_order, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t max_context_len, float scale, int32_t partition_size,
+                              void *workspace, size_t workspace_bytes, uint32_t flags,
+                              void *stream) {
   return decode_common("pa_decode_attention", out, query, q_dtype, q_stride, cache, block_tables,
-                       max_blocks_per_seq, context_lens, num_seqs, num_q_heads, max_context_len,
-                       scale, nullptr, 0, partition_size, workspace, workspace_bytes, flags,
-                       stream);
+                       max_blocks_per_seq, context_lens, seq_order, num_seqs, num_q_heads,
+                       max_context_len, scale, nullptr, 0, partition_size, workspace,
+                       workspace_bytes, flags, stream);
 }
 
 pa_status pa_decode_attention_noalloc(void *out, const void *query, int32_t q_dtype,
@@ -473,25 +485,26 @@ pa_status pa_decode_attention_noalloc(void *out, const void *query, int32_t q_dt
                                       int32_t num_q_heads, int32_t max_context_len, float scale,
                                       int32_t partition_size, uint32_t flags, void *stream) {
   return decode_common("pa_decode_attention_noalloc", out, query, q_dtype, q_stride, cache,
-                       block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
-                       max_context_len, scale, nullptr, 0, partition_size, nullptr, 0, flags,
-                       stream, nullptr, true);
+                       block_tables, max_blocks_per_seq, context_lens, nullptr, num_seqs,
+                       num_q_heads, max_context_len, scale, nullptr, 0, partition_size, nullptr,
+                       0, flags, stream, nullptr, true);
 }
 
 pa_status pa_decode_attention_shared_prefix(void *out, const void *query, int32_t q_dtype,
                                             int64_t q_stride, const pa_cache *cache,
                                             const int32_t *block_tables,
                                             int32_t max_blocks_per_seq,
-                                            const int32_t *context_lens, int32_t num_seqs,
+                                            const int32_t *context_lens,
+                                            const int32_t *seq_order, int32_t num_seqs,
                                             int32_t num_q_heads, int32_t max_context_len,
                                             float scale, const int32_t *prefix_table,
                                             int32_t prefix_len, int32_t partition_size,
                                             void *workspace, size_t workspace_bytes,
                                             uint32_t flags, void *stream) {
   return decode_common("pa_decode_attention_shared_prefix", out, query, q_dtype, q_stride, cache,
-                       block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
-                       max_context_len, scale, prefix_table, prefix_len, partition_size,
-                       workspace, workspace_bytes, flags, stream);
+                       block_tables, max_blocks_per_seq, context_lens, seq_order, num_seqs,
+                       num_q_heads, max_context_len, scale, prefix_table, prefix_len,
+                       partition_size, workspace, workspace_bytes, flags, stream);
 }
 
 pa_status pa_decode_attention_append(void *out, const void *query, int32_t q_dtype,
@@ -499,16 +512,16 @@ pa_status pa_decode_attention_append(void *out, const void *query, int32_t q_dty
                                      const void *value, int64_t key_stride, int64_t value_stride,
                                      const int64_t *slot_mapping, const int32_t *block_tables,
                                      int32_t max_blocks_per_seq, const int32_t *context_lens,
-                                     int32_t num_seqs, int32_t num_q_heads,
-                                     int32_t max_context_len, float scale,
+                                     const int32_t *seq_order, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t max_context_len, float scale,
                                      const int32_t *prefix_table, int32_t prefix_len,
                                      int32_t partition_size, void *workspace,
                                      size_t workspace_bytes, uint32_t flags, void *stream) {
   const AppendIn app{key, value, key_stride, value_stride, slot_mapping};
   return decode_common("pa_decode_attention_append", out, query, q_dtype, q_stride, cache,
-                       block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
-                       max_context_len, scale, prefix_table, prefix_len, partition_size,
-                       workspace, workspace_bytes, flags, stream, &app);
+                       block_tables, max_blocks_per_seq, context_lens, seq_order, num_seqs,
+                       num_q_heads, max_context_len, scale, prefix_table, prefix_len,
+                       partition_size, workspace, workspace_bytes, flags, stream, &app);
 }
 
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
@@ -581,6 +594,106 @@ pa_status pa_check_context_lens(const int32_t *context_lens, int32_t num_seqs,
                   context_lens[s], max_context_len);
   }
   return PA_OK;
+}
+
+pa_status pa_check_seq_order(const int32_t *seq_order, int32_t num_seqs) {
+  const char *who = "pa_check_seq_order";
+  if (num_seqs < 0) return fail(PA_ERR_SHAPE, "%s: num_seqs < 0", who);
+  if (num_seqs > 0 && !seq_order) return fail(PA_ERR_NULL, "%s: seq_order is NULL", who);
+  std::vector<char> seen((size_t)num_seqs, 0);
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t s = seq_order[i];
+    if (s < 0 || s >= num_seqs)
+      return fail(PA_ERR_SHAPE, "%s: seq_order[%d] = %d outside 0..%d", who, i, s, num_seqs - 1);
+    if (seen[(size_t)s])
+      return fail(PA_ERR_SHAPE, "%s: sequence %d appears twice (entry %d)", who, s, i);
+    seen[(size_t)s] = 1;
+  }
+  return PA_OK;
+}
+
+pa_status pa_decode_plan(const pa_cache *cache, int32_t q_dtype, const int32_t *context_lens,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                         int32_t max_context_len, int32_t prefix_len, int32_t partition_size,
+                         uint32_t flags, int32_t *seq_order, int32_t *round_items) {
+  const char *who = "pa_decode_plan";
+  pa_status st = check_cache(cache, who);
+  if (st != PA_OK) return st;
+  if (round_items) *round_items = 0;
+  if (num_seqs < 0 || num_seqs > 65535)
+    return fail(PA_ERR_SHAPE, "%s: num_seqs %d outside 0..65535", who, num_seqs);
+  if (num_seqs == 0) return ok();
+  if (!context_lens || !seq_order) return fail(PA_ERR_NULL, "%s: NULL context_lens/seq_order", who);
+  const int H = cache->num_kv_heads, B = cache->block_size;
+  if (num_q_heads < 1 || num_q_heads % H != 0)
+    return fail(PA_ERR_SHAPE, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", who,
+                num_q_heads, H);
+  if (max_blocks_per_seq < 1 || max_context_len < 0 || prefix_len < 0 ||
+      prefix_len % PA_BLOCK_SIZE != 0 || partition_size < 0 || partition_size % PA_BLOCK_SIZE != 0)
+    return fail(PA_ERR_SHAPE, "%s: bad max_blocks_per_seq / max_context_len / prefix_len / "
+                "partition_size", who);
+  if ((flags & ~(PA_DECODE_FORCE_VALU | PA_DECODE_PLAN_APPEND)) != 0)
+    return fail(PA_ERR_SHAPE, "%s: unknown flags", who);
+  for (int32_t s = 0; s < num_seqs; ++s) seq_order[s] = s;
+
+  // The kernel and grid the decode call would use (the checks of decode_common that choose them).
+  const int64_t cap = (int64_t)max_blocks_per_seq * B;
+  const int32_t max_len = (int32_t)(max_context_len < cap ? max_context_len : cap);
+  const bool force_valu = (flags & PA_DECODE_FORCE_VALU) != 0;
+  static const int64_t kAnySlot = 0;
+  pa::DecodeArgs a{};
+  a.q_dtype = q_dtype;
+  a.cache = cache_args(cache);
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.max_context_len = max_len;
+  a.append_slots = (flags & PA_DECODE_PLAN_APPEND) ? &kAnySlot : nullptr;
+  bool use_prefix = prefix_len > 0 && B == PA_BLOCK_SIZE;
+  if (use_prefix) {
+    pa::DecodeArgs t = a;
+    t.prefix_len = prefix_len;
+    use_prefix = !force_valu && pa::decode_mfma_supports_prefix(t);
+  }
+  const bool use_mfma = use_prefix || (!force_valu && pa::decode_mfma_supports(a));
+  if (!use_mfma) return ok();  // the vector-ALU kernel deals no list
+  const int32_t pt = resolve_partition(
+      num_seqs, H, use_prefix ? max_context_len - prefix_len : max_context_len, partition_size);
+  a.partition_size = pt;
+  a.num_partitions = (int32_t)decode_slots(max_len, pt, use_prefix ? prefix_len : 0);
+  if (use_prefix) {
+    a.prefix_len = prefix_len;
+    a.prefix_chunks = ceil_div(prefix_len, pa::kPrefixChunk);
+  }
+  if (!pa::order_fits(num_seqs, a.num_partitions)) return ok();  // the call ignores an order
+  const int waves = pa::decode_mfma_item_waves(a);
+  if (waves <= 0) return ok();  // the direct grid: one wavefront per item, no list to deal
+
+  // Items of each sequence and the 16-position steps of its largest item, as the kernel cuts them.
+  const int32_t base = use_prefix ? prefix_len : 0;
+  std::vector<int32_t> items((size_t)num_seqs), steps((size_t)num_seqs);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t L = std::min(std::max(context_lens[s], 0), max_len);
+    const int32_t n = L > base ? ceil_div(L - base, pt) : (use_prefix ? 0 : 1);
+    items[(size_t)s] = n * H;
+    steps[(size_t)s] = L > base ? ceil_div(ceil_div(L - base, pa::kBlock), n) : 0;
+  }
+  std::vector<int32_t> by_size((size_t)num_seqs);
+  for (int32_t s = 0; s < num_seqs; ++s) by_size[(size_t)s] = s;
+  std::stable_sort(by_size.begin(), by_size.end(),
+                   [&](int32_t x, int32_t y) { return steps[(size_t)x] > steps[(size_t)y]; });
+  // Rounds of `waves` items, filled alternately with the largest and the smallest items left, so
+  // that a wavefront given a large item in one round is given a small one in the next.
+  int32_t lo = 0, hi = num_seqs - 1, k = 0;
+  for (int round = 0; lo <= hi; ++round) {
+    int64_t n = 0;
+    while (lo <= hi && n < waves) {
+      const int32_t s = (round % 2 == 0) ? by_size[(size_t)lo++] : by_size[(size_t)hi--];
+      seq_order[k++] = s;
+      n += items[(size_t)s];
+    }
+  }
+  if (round_items) *round_items = waves;
+  return ok();
 }
 
 void pa_set_debug(int on) { g_debug.store(on ? 1 : 0, std::memory_order_relaxed); }

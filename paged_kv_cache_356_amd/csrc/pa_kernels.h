@@ -86,7 +86,19 @@ struct DecodeArgs {
   // query_start[s] .. query_start[s + 1] - 1, at positions context_lens[s] - n_s .. context_lens[s] - 1.
   const int32_t *query_start;
   int32_t max_query_len;    // host bound of query_start[s + 1] - query_start[s]
+  // Dealing order of the persistent matrix-core grid (NULL: batch order): its item list runs over
+  // sequences seq_order[0], seq_order[1], ...; an entry outside [0, num_seqs) is skipped.  Given
+  // only while every per-sequence item count of the list stays below 2^kOrderCountBits.
+  const int32_t *seq_order;
 };
+
+// The persistent grid keeps an ordered list's sequence ids beside the item counts in one LDS word.
+constexpr int kOrderCountBits = 20;
+
+// Whether a dealing order fits the list (at most `slots` items per sequence).
+inline bool order_fits(int32_t num_seqs, int64_t slots) {
+  return (int64_t)num_seqs * slots < ((int64_t)1 << kOrderCountBits);
+}
 
 // Partition `part` of positions [base, L) (base a multiple of the block size) cut into
 // n = ceil((L - base) / PT) partitions: the range's nb blocks are shared out as evenly as whole
@@ -150,6 +162,9 @@ hipError_t launch_decode_valu(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 bool decode_mfma_supports(const DecodeArgs &a);
 bool decode_mfma_supports_prefix(const DecodeArgs &a);
+// Wavefronts that take sequence items when the matrix-core kernel runs `a` on the current device
+// (0: the direct grid, which deals no list).
+int decode_mfma_item_waves(const DecodeArgs &a);
 hipError_t launch_prefill_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_partition_reduce(const DecodeArgs &a, hipStream_t stream);
 

@@ -61,7 +61,7 @@ class DecodeBatch:
     def __init__(self, w: wl.Workload, device="cuda", num_sets: int = 1, layers=None,
                  pad_block: int = 0, keep_values: bool = False, pool_fill: int = 0,
                  lengths=None, partition_size: int | None = None, keep_layers=None,
-                 contiguous: bool = False):
+                 contiguous: bool = False, plan: bool = True):
         self.w = w
         self.device = device
         H, D, S = w.num_kv_heads, w.head_dim, w.num_seqs
@@ -142,6 +142,10 @@ class DecodeBatch:
         # use the shared-prefix decode where the workload has a prefix (run_step / run_layer)
         self.use_prefix = self.prefix_len > 0
         self.fused = False  # run_layer: one pa_decode_attention_append call instead of two
+        # the decode calls take the dealing order pa_decode_plan computes from each set's lengths
+        # (step metadata, like the block tables); plan=False keeps the batch order
+        self.plan = plan
+        self._orders = {}
 
     # ------------------------------------------------------------------ the step
     # The library calls of a step are prepared once per (set, layer) and replayed (api.*Call): the
@@ -188,6 +192,27 @@ class DecodeBatch:
             self.reshape(set_index, layer, stream)
         self.decode(set_index, layer, flags=flags, stream=stream)
 
+    def order(self, set_index: int, flags: int = api.PA_DECODE_DEFAULT, append: bool = False):
+        """The set's dealing order for its decode calls (a device int32 [S]; None with plan off or
+        where the plan is the batch order itself, which the call then deals without the order's
+        extra scan): pa_decode_plan on the host copy of the set's context lengths, computed once
+        per set and call kind."""
+        if not self.plan:
+            return None
+        key = (set_index, flags, append, self.use_prefix, self.partition_size)
+        if key not in self._orders:
+            st = self.sets[set_index]
+            w = self.w
+            cache = self.caches[self.layers[0]]
+            q_dtype = st.q[self.layers[0]].dtype
+            order = api.pa_decode_plan(
+                cache, q_dtype, st.ctx, w.num_q_heads, self.max_blocks, self.max_context_len,
+                self.prefix_len if self.use_prefix else 0, self.partition_size,
+                flags | (api.PA_DECODE_PLAN_APPEND if append else 0))
+            identity = bool((order == np.arange(order.shape[0])).all())
+            self._orders[key] = None if identity else torch.from_numpy(order).to(self.device)
+        return self._orders[key]
+
     def decode(self, set_index: int, layer: int, flags: int = api.PA_DECODE_DEFAULT, stream=None,
                out: torch.Tensor | None = None, append: bool = False):
         """The step's attention call for one layer (shared-prefix decode when use_prefix); with
@@ -201,11 +226,13 @@ class DecodeBatch:
                 pre.update(key=st.new_k[layer], value=st.new_v[layer], slot_mapping=st.d_slots)
             return api.DecodeCall(o, st.q[layer], self.caches[layer], st.d_tables, st.d_ctx,
                                   self.max_context_len, self.w.scale, self.partition_size,
-                                  self.workspace, flags, **pre)
+                                  self.workspace, flags,
+                                  seq_order=self.order(set_index, flags, append), **pre)
         if out is not None:
             make(out)(stream)
             return
-        key = ("decode", set_index, layer, flags, self.use_prefix, self.partition_size, append)
+        key = ("decode", set_index, layer, flags, self.use_prefix, self.partition_size, append,
+               self.plan)
         self._call(key, lambda: make(st.out[layer]))(stream)
 
     # ------------------------------------------------------------------ accounting

@@ -921,6 +921,106 @@ def test_debug_checks_refuse_before_launch():
         api.pa_set_debug(False)
 
 
+# --------------------------------------------------------------------------- dealing order
+ORDER_CASES = {
+    # (workload, its changes, fused append): 200 sequences at partition 64 give more items than
+    # the persistent grid has wavefronts, so the dealing order spans several rounds
+    "f16": ("f16_batch32", {}, False),
+    "f16_d64": ("f16_batch32", dict(head_dim=64), False),
+    "f16_b8": ("f16_batch32", dict(block_size=8, num_blocks=16384), False),
+    "f16_b32": ("f16_batch32", dict(block_size=32, num_blocks=4096), False),
+    "bf16": ("bf16_32k_batch8", {}, False),
+    "fp8": ("fp8_28layer_batch512", dict(num_layers=1), False),
+    "prefix_f16": ("f16_shared_prefix_batch256", dict(prefix_len=128), False),
+    "prefix_fp8": ("f16_shared_prefix_batch256", dict(prefix_len=128, cache_dtype="fp8"), False),
+    "fused_f16": ("f16_batch32", {}, True),
+    "fused_prefix": ("f16_shared_prefix_batch256", dict(prefix_len=128), True),
+}
+
+
+def _decode_ordered(b, out, order, append=False):
+    st, l = b.sets[0], b.layers[0]
+    pre = dict(prefix_table=b.prefix_tables[0], prefix_len=b.prefix_len) if b.use_prefix else {}
+    if append:
+        pre.update(key=st.new_k[l], value=st.new_v[l], slot_mapping=st.d_slots)
+    api.DecodeCall(out, st.q[l], b.caches[l], st.d_tables, st.d_ctx, b.max_context_len, b.w.scale,
+                   b.partition_size, b.workspace, api.PA_DECODE_DEFAULT, seq_order=order, **pre)()
+
+
+@pytest.mark.parametrize("case", list(ORDER_CASES))
+def test_dealing_order_is_bitwise_invisible(case):
+    """The order in which the sequences' items are dealt (seq_order) changes which wavefront
+    computes an item, never what it computes: the planner's order, a random permutation and the
+    reversed batch give the batch order's output bit for bit, and an entry outside the batch is
+    skipped without touching the other sequences' rows."""
+    name, kw, append = ORDER_CASES[case]
+    w = wl.WORKLOADS[name].replace(**{"num_seqs": 200, "num_blocks": 8192, **kw})
+    rng = np.random.default_rng(11)
+    base = w.prefix_len
+    lengths = (base + rng.integers(1, 700, size=200)).tolist()
+    _say(f"dealing order, {case}")
+    b = DecodeBatch(w, pad_block=0, lengths=lengths, partition_size=64, layers=[0], plan=False)
+    b.run_step(0)
+    st, l = b.sets[0], 0
+    ref = torch.full_like(st.out[l], 7.0)
+    _decode_ordered(b, ref, None, append)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(ref.float()).all())
+    plan, rnd = api.pa_decode_plan(b.caches[l], st.q[l].dtype, st.ctx, w.num_q_heads,
+                                   b.max_blocks, b.max_context_len, base, 64,
+                                   api.PA_DECODE_PLAN_APPEND if append else 0, with_round=True)
+    items = int(sum(-(-(L - base) // 64) for L in lengths)) * w.num_kv_heads
+    _say(f"  {items} items, {rnd} per round")
+    assert sorted(plan.tolist()) == list(range(200)) and 0 < rnd < items
+    assert plan.tolist() != list(range(200))
+    perm = rng.permutation(200).astype(np.int32)
+    for oname, order in (("plan", plan), ("random", perm), ("reversed", np.arange(199, -1, -1))):
+        out = torch.full_like(ref, 3.0)
+        _decode_ordered(b, out, torch.from_numpy(np.ascontiguousarray(order, np.int32)).cuda(),
+                        append)
+        torch.cuda.synchronize()
+        same = torch.equal(out, ref)
+        _say(f"  {oname}: bitwise equal {same}")
+        assert same
+    # sequence perm[5] named by no entry: every other row as before
+    holed = perm.copy()
+    gone = int(holed[5])
+    holed[5] = -1
+    out = torch.full_like(ref, 3.0)
+    _decode_ordered(b, out, torch.from_numpy(holed).cuda(), append)
+    torch.cuda.synchronize()
+    keep = torch.ones(200, dtype=torch.bool)
+    keep[gone] = False
+    assert torch.equal(out[keep.cuda()], ref[keep.cuda()])
+
+
+def test_debug_checks_refuse_a_dealing_order_that_is_not_a_permutation():
+    w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=4, num_blocks=256)
+    b = DecodeBatch(w, pad_block=0, lengths=[40, 300, 17, 129])
+    b.run_step(0)
+    st = b.sets[0]
+    api.pa_set_debug(True)
+    try:
+        out = torch.full_like(st.out[0], 3.0)
+        good = torch.tensor([3, 1, 0, 2], dtype=torch.int32, device="cuda")
+        api.pa_decode_attention(out, st.q[0], b.caches[0], st.d_tables, st.d_ctx,
+                                b.max_context_len, w.scale, workspace=b.workspace, seq_order=good)
+        torch.cuda.synchronize()
+        assert torch.equal(out, st.out[0])
+        for bad in ([3, 1, 1, 2], [0, 1, 2, 4]):
+            out = torch.full_like(st.out[0], 3.0)
+            with pytest.raises(api.PaError) as e:
+                api.pa_decode_attention(out, st.q[0], b.caches[0], st.d_tables, st.d_ctx,
+                                        b.max_context_len, w.scale, workspace=b.workspace,
+                                        seq_order=torch.tensor(bad, dtype=torch.int32,
+                                                               device="cuda"))
+            assert e.value.status == -2
+            torch.cuda.synchronize()
+            assert bool((out == 3.0).all())
+    finally:
+        api.pa_set_debug(False)
+
+
 # --------------------------------------------------------------------------- full sizes
 FULL = ["f16_batch32", "bf16_32k_batch8", "f16_shared_prefix_batch256"]
 

@@ -52,12 +52,12 @@ def _cache(**kw):
 
 def _decode(cache, **kw):
     a = dict(out=64, query=128, q_dtype=api.PA_F16, q_stride=0, tables=256, max_blocks=4, ctx=512,
-             S=2, Hq=28, max_ctx=64, scale=0.1, ps=0, ws=None, ws_bytes=0, flags=0)
+             order=None, S=2, Hq=28, max_ctx=64, scale=0.1, ps=0, ws=None, ws_bytes=0, flags=0)
     a.update(kw)
     return api.lib().pa_decode_attention(a["out"], a["query"], a["q_dtype"], a["q_stride"],
                                          ctypes.byref(cache), a["tables"], a["max_blocks"], a["ctx"],
-                                         a["S"], a["Hq"], a["max_ctx"], a["scale"], a["ps"], a["ws"],
-                                         a["ws_bytes"], a["flags"], None)
+                                         a["order"], a["S"], a["Hq"], a["max_ctx"], a["scale"],
+                                         a["ps"], a["ws"], a["ws_bytes"], a["flags"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -82,14 +82,14 @@ def test_decode_validation(kw, status):
 
 def _decode_append(cache, **kw):
     a = dict(out=64, query=128, q_dtype=api.PA_F16, q_stride=0, key=2048, value=4096, ks=0, vs=0,
-             slots=8192, tables=256, max_blocks=4, ctx=512, S=2, Hq=28, max_ctx=64, scale=0.1,
-             prefix_table=None, prefix_len=0, ps=0, ws=None, ws_bytes=0, flags=0)
+             slots=8192, tables=256, max_blocks=4, ctx=512, order=None, S=2, Hq=28, max_ctx=64,
+             scale=0.1, prefix_table=None, prefix_len=0, ps=0, ws=None, ws_bytes=0, flags=0)
     a.update(kw)
     return api.lib().pa_decode_attention_append(
         a["out"], a["query"], a["q_dtype"], a["q_stride"], ctypes.byref(cache), a["key"],
-        a["value"], a["ks"], a["vs"], a["slots"], a["tables"], a["max_blocks"], a["ctx"], a["S"],
-        a["Hq"], a["max_ctx"], a["scale"], a["prefix_table"], a["prefix_len"], a["ps"], a["ws"],
-        a["ws_bytes"], a["flags"], None)
+        a["value"], a["ks"], a["vs"], a["slots"], a["tables"], a["max_blocks"], a["ctx"],
+        a["order"], a["S"], a["Hq"], a["max_ctx"], a["scale"], a["prefix_table"], a["prefix_len"],
+        a["ps"], a["ws"], a["ws_bytes"], a["flags"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -134,12 +134,12 @@ def test_workspace_size_follows_the_callers_max_context_len():
 
 def _decode_prefix(cache, prefix_table=1024, prefix_len=64, **kw):
     a = dict(out=64, query=128, q_dtype=api.PA_F16, q_stride=0, tables=256, max_blocks=8, ctx=512,
-             S=2, Hq=28, max_ctx=128, scale=0.1, ps=0, ws=None, ws_bytes=0, flags=0)
+             order=None, S=2, Hq=28, max_ctx=128, scale=0.1, ps=0, ws=None, ws_bytes=0, flags=0)
     a.update(kw)
     return api.lib().pa_decode_attention_shared_prefix(
         a["out"], a["query"], a["q_dtype"], a["q_stride"], ctypes.byref(cache), a["tables"],
-        a["max_blocks"], a["ctx"], a["S"], a["Hq"], a["max_ctx"], a["scale"], prefix_table,
-        prefix_len, a["ps"], a["ws"], a["ws_bytes"], a["flags"], None)
+        a["max_blocks"], a["ctx"], a["order"], a["S"], a["Hq"], a["max_ctx"], a["scale"],
+        prefix_table, prefix_len, a["ps"], a["ws"], a["ws_bytes"], a["flags"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -474,3 +474,98 @@ def test_debug_switch():
     api.pa_set_debug(False)
     assert not api.pa_debug_enabled()
     api.pa_set_debug(was)
+
+
+def test_seq_order_checks():
+    api.pa_check_seq_order(np.array([2, 0, 1]))
+    api.pa_check_seq_order(np.zeros(0, np.int32))
+    for bad in ([0, 0, 1], [0, 3, 1], [-1, 0, 1]):
+        with pytest.raises(api.PaError) as e:
+            api.pa_check_seq_order(np.array(bad))
+        assert e.value.status == -2
+
+
+def _plan(cache, lens, Hq=28, max_blocks=None, max_ctx=None, prefix_len=0, ps=0, flags=0,
+          q_dtype=api.PA_F16):
+    lens = np.ascontiguousarray(lens, np.int32)
+    S = lens.shape[0]
+    B = cache.block_size
+    max_ctx = int(lens.max()) if max_ctx is None else max_ctx
+    max_blocks = max(1, -(-max_ctx // B)) if max_blocks is None else max_blocks
+    order = np.full(S, -7, np.int32)
+    rnd = ctypes.c_int32(-1)
+    st = api.lib().pa_decode_plan(ctypes.byref(cache), q_dtype, lens.ctypes.data, S, Hq,
+                                  max_blocks, max_ctx, prefix_len, ps, flags, order.ctypes.data,
+                                  ctypes.byref(rnd))
+    return st, order, rnd.value
+
+
+def _snake_model(lens, pt, H, base, prefix, round_items, max_len):
+    """The dealing order written out: sequences by the 16-position steps of their largest
+    partition, largest first (ties in batch order), rounds of round_items items filled alternately
+    from the largest and the smallest left."""
+    items, steps = [], []
+    for L in np.clip(lens, 0, max_len):
+        L = int(L)
+        n = -(-(L - base) // pt) if L > base else (0 if prefix else 1)
+        items.append(n * H)
+        steps.append(-(-(-(-(L - base) // 16)) // n) if L > base else 0)
+    rest = sorted(range(len(lens)), key=lambda s: -steps[s])  # stable
+    out, rnd = [], 0
+    while rest:
+        n = 0
+        while rest and n < round_items:
+            s = rest.pop(0) if rnd % 2 == 0 else rest.pop()
+            out.append(s)
+            n += items[s]
+        rnd += 1
+    return out
+
+
+def test_decode_plan_is_the_snake_order():
+    """pa_decode_plan deals the sequences by the size of their largest item in rounds of the
+    grid's item wavefronts.  Without a GPU the grid is a single workgroup, so the round is 4 items
+    (one per wavefront) and the order is checked against the model at that size."""
+    rng = np.random.default_rng(5)
+    lens = rng.integers(0, 3000, size=61).astype(np.int32)
+    lens[[3, 9]] = 0
+    st, order, rnd = _plan(_cache(), lens, ps=256)
+    assert st == 0, api.lib().pa_last_error()
+    assert rnd > 0 and sorted(order.tolist()) == list(range(61))
+    assert order.tolist() == _snake_model(lens, 256, 4, 0, False, rnd, int(lens.max()))
+    # the automatic partition size, and lengths above max_context_len clamped as the call does
+    st, order, rnd = _plan(_cache(), lens, max_ctx=2000)
+    pt = api.pa_decode_auto_partition(61, 4, 2000)
+    assert order.tolist() == _snake_model(lens, pt, 4, 0, False, rnd, 2000)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(flags=api.PA_DECODE_FORCE_VALU),            # the vector-ALU kernel deals no list
+    dict(cache_dtype=api.PA_F32, q_dtype=api.PA_F32),
+    dict(S=4097),                                    # the direct grid (one wavefront per item)
+    dict(S=4096, ps=16, max_ctx=4096),               # 2^20 partition slots: the order is ignored
+])
+def test_decode_plan_identity_where_the_call_ignores_it(kw):
+    kw = dict(kw)
+    S = kw.pop("S", 40)
+    q_dtype = kw.pop("q_dtype", api.PA_F16)
+    cache = _cache(**{k: kw.pop(k) for k in ("cache_dtype",) if k in kw})
+    lens = np.random.default_rng(1).integers(1, 4096, size=S)
+    st, order, rnd = _plan(cache, lens, q_dtype=q_dtype, **kw)
+    assert st == 0, api.lib().pa_last_error()
+    assert order.tolist() == list(range(S)) and rnd == 0
+
+
+def test_decode_plan_rejections():
+    lens = np.array([5, 9], np.int32)
+    assert _plan(_cache(), lens, flags=8)[0] == -2
+    assert _plan(_cache(), lens, prefix_len=8)[0] == -2
+    assert _plan(_cache(), lens, Hq=30)[0] == -2
+    assert _plan(_cache(block_size=12), lens)[0] == -3
+    rnd = ctypes.c_int32(0)
+    assert api.lib().pa_decode_plan(ctypes.byref(_cache()), api.PA_F16, lens.ctypes.data, 2, 28,
+                                    1, 16, 0, 0, 0, None, ctypes.byref(rnd)) == -1
+    # an empty batch plans nothing; round_items may be NULL
+    assert api.lib().pa_decode_plan(ctypes.byref(_cache()), api.PA_F16, None, 0, 28, 1, 16, 0, 0,
+                                    0, None, None) == 0
+
