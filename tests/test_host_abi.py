@@ -544,14 +544,16 @@ def test_decode_plan_is_the_snake_order():
     dict(cache_dtype=api.PA_F32, q_dtype=api.PA_F32),
     dict(S=4097),                                    # the direct grid (one wavefront per item)
     dict(S=4096, ps=16, max_ctx=4096),               # 2^20 partition slots: the order is ignored
+    dict(S=1, ps=4096, num_kv_heads=2),              # 2 items, a round of 4: nothing to balance
 ])
 def test_decode_plan_identity_where_the_call_ignores_it(kw):
     kw = dict(kw)
     S = kw.pop("S", 40)
     q_dtype = kw.pop("q_dtype", api.PA_F16)
-    cache = _cache(**{k: kw.pop(k) for k in ("cache_dtype",) if k in kw})
+    cache = _cache(**{k: kw.pop(k) for k in ("cache_dtype", "num_kv_heads") if k in kw})
     lens = np.random.default_rng(1).integers(1, 4096, size=S)
     st, order, rnd = _plan(cache, lens, q_dtype=q_dtype, **kw)
+    assert st == 0, api.lib().pa_last_error()
     assert st == 0, api.lib().pa_last_error()
     assert order.tolist() == list(range(S)) and rnd == 0
 
