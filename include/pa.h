@@ -301,9 +301,10 @@ pa_status pa_decode_attention_shared_prefix(void *out, const void *query, int32_
 /*
  * pa_decode_attention_append — one decode step with its cache write: pa_reshape_and_cache of each
  * sequence's new token followed by pa_decode_attention (prefix_len = 0) or
- * pa_decode_attention_shared_prefix (prefix_len > 0), in one call.  Each generated token appends
- * one K/V entry to its sequence's current block ([Lesson06] "How paging grows") and is attended
- * to in the same step, as position context_lens[s] - 1 ([Visualized] Parts 1 and 2).
+ * pa_decode_attention_shared_prefix (prefix_len > 0), in one call.  The step's new K and V land
+ * in the next free slot of the sequence's last block ([Lesson06] "How paging grows"), and the
+ * same step's query already attends to them, as position context_lens[s] - 1 ([Visualized]
+ * Parts 1 and 2).
  *
  *   key, value    device rows of num_kv_heads * head_dim elements of q_dtype, one per sequence;
  *                 sequence s's row starts at element s * key_stride (value_stride); a stride of
