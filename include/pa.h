@@ -226,8 +226,9 @@ pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int
  *                 pa_decode_attention_append.
  *   seq_order     HOST int32 [num_seqs], written: a permutation of 0 .. num_seqs - 1 (the identity
  *                 where the call would not deal a list or ignores the order: the vector-ALU
- *                 kernel, the direct grid, 2^20 or more partition slots in all; and where the
- *                 items fill at most half of one round, so that no order balances anything).
+ *                 kernel, the direct grid, 2^20 or more partition slots in all; and where no
+ *                 order balances anything: the items fill at most half of one round, or, without
+ *                 a shared prefix, at most one round).
  *   round_items   optional (NULL): the items per round, the grid's wavefronts that take sequence
  *                 items on the current device (0 with the identity).
  * The grid depends on the current device (its compute units); an order planned for another

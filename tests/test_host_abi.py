@@ -545,6 +545,7 @@ def test_decode_plan_is_the_snake_order():
     dict(S=4097),                                    # the direct grid (one wavefront per item)
     dict(S=4096, ps=16, max_ctx=4096),               # 2^20 partition slots: the order is ignored
     dict(S=1, ps=4096, num_kv_heads=2),              # 2 items, a round of 4: nothing to balance
+    dict(S=1, ps=4096),                              # 4 items in one round of 4, no prefix
 ])
 def test_decode_plan_identity_where_the_call_ignores_it(kw):
     kw = dict(kw)
