@@ -14,8 +14,10 @@
 namespace pa {
 namespace {
 
-// One workgroup per token.  Thread v handles K vector c (E elements of head h) of that token:
-// it writes the 16-byte K vector in one store and the E transposed V elements one by one.
+// One workgroup per token.  16-bit caches: thread v handles K vector c (E elements of head h) of
+// that token, writing the 16-byte K vector in one store and the E transposed V elements one by one.
+// fp8 caches: thread v handles 4 elements (one 4-byte word of a K vector), so that all 128 threads
+// share the token's divisions and encodings instead of 32 of them doing 16 each.
 template <class CT, class IT>
 __global__ __launch_bounds__(128) void reshape_and_cache_kernel(ReshapeArgs a) {
   const int t = blockIdx.x;
@@ -27,41 +29,50 @@ __global__ __launch_bounds__(128) void reshape_and_cache_kernel(ReshapeArgs a) {
   const int off = (int)(slot % B);
   const int H = c.num_kv_heads, D = c.head_dim;
   using L = Layout<CT::bytes>;
+  constexpr bool kFP8 = std::is_same<CT, fp8_t>::value;
   constexpr int E = L::E;
-  const int vec_per_head = D / E;
+  constexpr int P = kFP8 ? 4 : E;  // elements per thread
+  const int per_head = D / P;
   const auto *key = static_cast<const typename IT::raw *>(a.key) + (size_t)t * a.key_stride;
   const auto *val = static_cast<const typename IT::raw *>(a.value) + (size_t)t * a.value_stride;
   auto *kp = static_cast<typename CT::raw *>(c.k_pool);
   auto *vp = static_cast<typename CT::raw *>(c.v_pool);
-  for (int v = threadIdx.x; v < H * vec_per_head; v += blockDim.x) {
-    const int h = v / vec_per_head, cv = v % vec_per_head;
+  for (int v = threadIdx.x; v < H * per_head; v += blockDim.x) {
+    const int h = v / per_head;
+    const int i0 = (v % per_head) * P;
     const size_t tile = L::tile(blk, h, H, D, B);
-    const int i0 = cv * E;
-    union {
-      uint4 v;
-      typename CT::raw e[E];
-    } kv, vv;
-    if constexpr (std::is_same<CT, fp8_t>::value) {
+    if constexpr (kFP8) {
       const float ks = c.k_scale[h], vs = c.v_scale[h];
+      uint32_t kw = 0;
+      uint8_t ve[P];
 #pragma unroll
-      for (int j = 0; j < E; ++j) {
-        kv.e[j] = f32_to_e4m3(__fdiv_rn(load_f32<IT>(key, (size_t)h * D + i0 + j), ks));
-        vv.e[j] = f32_to_e4m3(__fdiv_rn(load_f32<IT>(val, (size_t)h * D + i0 + j), vs));
+      for (int j = 0; j < P; ++j) {
+        kw |= (uint32_t)f32_to_e4m3(__fdiv_rn(load_f32<IT>(key, (size_t)h * D + i0 + j), ks))
+              << (8 * j);
+        ve[j] = f32_to_e4m3(__fdiv_rn(load_f32<IT>(val, (size_t)h * D + i0 + j), vs));
       }
+      // K: the 4 elements are one aligned word of a 16-byte vector of the tile.
+      *reinterpret_cast<uint32_t *>(kp + tile + L::k_off(off, i0, B)) = kw;
+      // V: transposed tile, element (off, i) at i * B + off.
+#pragma unroll
+      for (int j = 0; j < P; ++j) vp[tile + L::v_off(off, i0 + j, B)] = ve[j];
     } else {
       static_assert(std::is_same<CT, IT>::value, "non-fp8 caches take rows of their own dtype");
+      union {
+        uint4 v;
+        typename CT::raw e[E];
+      } kv, vv;
 #pragma unroll
       for (int j = 0; j < E; ++j) {  // same dtype: bit copy
         kv.e[j] = key[(size_t)h * D + i0 + j];
         vv.e[j] = val[(size_t)h * D + i0 + j];
       }
-    }
-    // K: the E elements are one contiguous 16-byte vector of the tile.
-    auto *kdst = kp + tile + L::k_off(off, i0, B);
-    *reinterpret_cast<uint4 *>(kdst) = kv.v;
-    // V: transposed tile, element (off, i) at i * B + off.
+      // K: the E elements are one contiguous 16-byte vector of the tile.
+      *reinterpret_cast<uint4 *>(kp + tile + L::k_off(off, i0, B)) = kv.v;
+      // V: transposed tile, element (off, i) at i * B + off.
 #pragma unroll
-    for (int j = 0; j < E; ++j) vp[tile + L::v_off(off, i0 + j, B)] = vv.e[j];
+      for (int j = 0; j < E; ++j) vp[tile + L::v_off(off, i0 + j, B)] = vv.e[j];
+    }
   }
 }
 
