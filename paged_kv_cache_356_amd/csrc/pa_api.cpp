@@ -680,7 +680,8 @@ pa_status pa_decode_plan(const pa_cache *cache, int32_t q_dtype, const int32_t *
   // Where no wavefront gets a second item and no prefix workgroups share the compute units
   // (whose third, late-starting workgroups the order feeds the small items), or where the list
   // fills at most half of one round, the order has nothing to balance and the ordered scan only
-  // costs time (measured: f16_batch32, 608 items on 1,024 wavefronts, +0.3 us).
+  // costs time (measured: 32 fp16 sequences of up to 2,048 positions, 608 items on 1,024
+  // wavefronts, +0.3 us).
   int64_t total = 0;
   for (int32_t s = 0; s < num_seqs; ++s) total += items[(size_t)s];
   if (2 * total <= waves || (total <= waves && !use_prefix)) return ok();
