@@ -25,7 +25,9 @@
  *  - Host-side validation runs before any launch; on failure nothing is enqueued and the call
  *    returns a negative pa_status; pa_last_error() then holds a thread-local description.
  *  - After a launch, a HIP launch error is returned as PA_ERR_LAUNCH.
- *  - Functions are re-entrant; the only global state is the thread-local error text.
+ *  - Functions are re-entrant.  Global state: the thread-local error text, the process-wide
+ *    PA_DEBUG switch, per-device values looked up once (compute units, the kernels' occupancy,
+ *    the address of pa_decode_attention_noalloc's scratch) and that scratch itself.
  *  - Calls that touch the same device buffers on different streams race; order them yourself.
  */
 #ifndef PA_H
