@@ -215,11 +215,15 @@ pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int
  * pa_decode_plan — a dealing order for pa_decode_attention's seq_order, computed on the host
  * from a HOST copy of the step's context lengths: step metadata that the scheduler holds beside
  * the block tables the kernel walks ([Digest] "PagedAttention in one picture"), while the order
- * only changes how the kernel fetches, not the attention it computes ([Digest] "Misconceptions").  Every sequence's positions are cut into partitions (work items) as the call
- * cuts them; the sequences are taken by the size of their largest item, largest first, and put
- * into rounds of as many items as the call's grid has wavefronts for them, the rounds filled
- * alternately from the largest and from the smallest sequences left, so that a wavefront dealt a
- * large item in one round gets a small one in the next and the wavefronts end close together.
+ * only changes how the kernel fetches, not the attention it computes ([Digest] "Misconceptions").
+ * Every sequence's positions are cut into partitions (work items) as the call cuts them; the
+ * sequences are taken by the size of their largest item, largest first, and put into rounds of as
+ * many items as the call's grid has wavefronts for them, the rounds filled alternately from the
+ * largest and from the smallest sequences left, so that a wavefront dealt a large item in one round
+ * gets a small one in the next and the wavefronts end close together (with at most two rounds:
+ * the largest sequences on the wavefronts that take one item, the next largest in the first round
+ * of the others, the rest smallest first).  The call's partition reduce merges rows in the same
+ * order.
  *   cache, q_dtype, num_q_heads, max_blocks_per_seq, max_context_len, prefix_len,
  *   partition_size  those of the decode call the order is for (prefix_len 0: pa_decode_attention;
  *                 > 0: pa_decode_attention_shared_prefix).

@@ -689,15 +689,42 @@ pa_status pa_decode_plan(const pa_cache *cache, int32_t q_dtype, const int32_t *
   for (int32_t s = 0; s < num_seqs; ++s) by_size[(size_t)s] = s;
   std::stable_sort(by_size.begin(), by_size.end(),
                    [&](int32_t x, int32_t y) { return steps[(size_t)x] > steps[(size_t)y]; });
-  // Rounds of `waves` items, filled alternately with the largest and the smallest items left, so
-  // that a wavefront given a large item in one round is given a small one in the next.
-  int32_t lo = 0, hi = num_seqs - 1, k = 0;
-  for (int round = 0; lo <= hi; ++round) {
-    int64_t n = 0;
-    while (lo <= hi && n < waves) {
-      const int32_t s = (round % 2 == 0) ? by_size[(size_t)lo++] : by_size[(size_t)hi--];
-      seq_order[k++] = s;
-      n += items[(size_t)s];
+  int32_t k = 0;
+  if (total > waves && total <= 2 * (int64_t)waves) {
+    // Two rounds: total - waves wavefronts take two items, the others one.  The largest
+    // sequences go to the one-item wavefronts (the last entries of the first round), the next
+    // largest to the two-item wavefronts' first round, and the rest follow smallest first, so that
+    // the second round gives the largest first-round items the smallest second ones.  A sequence
+    // that does not fit a region goes to the next.
+    const int64_t pairs = total - waves, singles = waves - pairs;
+    std::vector<int32_t> first, single, second;
+    int64_t nf = 0, ns = 0;
+    for (int32_t s : by_size) {
+      const int64_t n = items[(size_t)s];
+      if (ns + n <= singles) {
+        single.push_back(s);
+        ns += n;
+      } else if (nf + n <= pairs) {
+        first.push_back(s);
+        nf += n;
+      } else {
+        second.push_back(s);
+      }
+    }
+    for (int32_t s : first) seq_order[k++] = s;
+    for (int32_t s : single) seq_order[k++] = s;
+    for (auto it = second.rbegin(); it != second.rend(); ++it) seq_order[k++] = *it;
+  } else {
+    // Rounds of `waves` items, filled alternately with the largest and the smallest items left,
+    // so that a wavefront given a large item in one round is given a small one in the next.
+    int32_t lo = 0, hi = num_seqs - 1;
+    for (int round = 0; lo <= hi; ++round) {
+      int64_t n = 0;
+      while (lo <= hi && n < waves) {
+        const int32_t s = (round % 2 == 0) ? by_size[(size_t)lo++] : by_size[(size_t)hi--];
+        seq_order[k++] = s;
+        n += items[(size_t)s];
+      }
     }
   }
   if (round_items) *round_items = waves;

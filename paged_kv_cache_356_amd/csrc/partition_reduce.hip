@@ -65,14 +65,28 @@ __device__ __forceinline__ float out_scale(const DecodeArgs &a, int row) {
   return 1.0f;
 }
 
+// Output row (s * Hq + hq) of grid row r: with a dealing order, grid rows run over the sequences
+// in that order (the decode's largest items first, so that the rows with the most partitions are
+// merged first), else in batch order; -1 for an order entry outside the batch.  The entry is the
+// same for the whole wavefront, so the order is read with a scalar load.
+__device__ __forceinline__ int reduce_row(const DecodeArgs &a, int r) {
+  if (!a.seq_order) return r;
+  const int Hq = a.num_q_heads;
+  const int e = __builtin_amdgcn_readfirstlane(r / Hq);
+  const int s = a.seq_order[e];
+  return (unsigned)s < (unsigned)a.num_seqs ? s * Hq + (r - e * Hq) : -1;
+}
+
 template <class QT, int D, int kPer, bool kHalf>
 __global__ __launch_bounds__(64 * kRowsPerGroup) void partition_reduce_kernel(DecodeArgs a) {
   constexpr int C = D / 4;   // float4 columns of a partial output
   constexpr int G = 64 / C;  // partitions handled side by side in a wavefront
   constexpr int SUB = G * kPer;
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kRowsPerGroup + (threadIdx.x >> 6);  // s * Hq + hq
-  if (row >= a.num_seqs * a.num_q_heads) return;
+  const int r = blockIdx.x * kRowsPerGroup + (threadIdx.x >> 6);
+  if (r >= a.num_seqs * a.num_q_heads) return;
+  const int row = reduce_row(a, r);  // s * Hq + hq
+  if (row < 0) return;
   const int s = row / a.num_q_heads;
   const int NP = a.num_partitions;
   const size_t row0 = (size_t)row * NP;
@@ -151,7 +165,8 @@ __global__ __launch_bounds__(256) void partition_reduce_split_kernel(DecodeArgs 
   constexpr int PG = 64 / C;              // partition groups per wavefront
   constexpr int kPer = 64 / PG;           // partitions per lane in one pass of 64
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int row = blockIdx.x;  // s * Hq + hq
+  const int row = reduce_row(a, blockIdx.x);  // s * Hq + hq
+  if (row < 0) return;
   const int s = row / a.num_q_heads;
   const int NP = a.num_partitions;
   const size_t row0 = (size_t)row * NP;

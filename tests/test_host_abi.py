@@ -511,6 +511,22 @@ def _snake_model(lens, pt, H, base, prefix, round_items, max_len):
         items.append(n * H)
         steps.append(-(-(-(-(L - base) // 16)) // n) if L > base else 0)
     rest = sorted(range(len(lens)), key=lambda s: -steps[s])  # stable
+    total = sum(items)
+    if round_items < total <= 2 * round_items:
+        # two rounds: the largest sequences on the one-item wavefronts, the next largest in the
+        # two-item wavefronts' first round, the rest smallest first
+        pairs, singles = total - round_items, 2 * round_items - total
+        first, single, second, nf, ns = [], [], [], 0, 0
+        for s in rest:
+            if ns + items[s] <= singles:
+                single.append(s)
+                ns += items[s]
+            elif nf + items[s] <= pairs:
+                first.append(s)
+                nf += items[s]
+            else:
+                second.append(s)
+        return first + single + second[::-1]
     out, rnd = [], 0
     while rest:
         n = 0
@@ -537,6 +553,26 @@ def test_decode_plan_is_the_snake_order():
     st, order, rnd = _plan(_cache(), lens, max_ctx=2000)
     pt = api.pa_decode_auto_partition(61, 4, 2000)
     assert order.tolist() == _snake_model(lens, pt, 4, 0, False, rnd, 2000)
+
+
+def test_decode_plan_two_rounds():
+    """Lists of more than one and at most two rounds take the two-round arrangement: one KV head,
+    so a sequence of n partitions is n items, and rounds of 4 items (one workgroup without a
+    GPU); every list of 5 to 8 items is checked against the model."""
+    c = _cache(num_kv_heads=1)
+    rng = np.random.default_rng(3)
+    seen = 0
+    for _ in range(200):
+        S = int(rng.integers(2, 7))
+        lens = rng.integers(1, 3 * 256, size=S).astype(np.int32)
+        st, order, rnd = _plan(c, lens, Hq=16, ps=256)
+        assert st == 0, api.lib().pa_last_error()
+        total = int(sum(-(-int(L) // 256) for L in lens))
+        if not (rnd < total <= 2 * rnd):
+            continue
+        seen += 1
+        assert order.tolist() == _snake_model(lens, 256, 1, 0, False, rnd, int(lens.max()))
+    assert seen >= 20
 
 
 @pytest.mark.parametrize("kw", [
