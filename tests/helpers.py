@@ -47,3 +47,44 @@ def max_abs_err(a, b) -> float:
 
 
 TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2, "fp8": 3e-2}
+
+
+def plan_order_model(lens, pt, H, base, prefix, round_items, max_len):
+    """pa_decode_plan's dealing order written out: sequences by the 16-position steps of their
+    largest partition, largest first (ties in batch order); with more than one and at most two
+    rounds of round_items items, the largest on the one-item wavefronts, the next largest in the
+    two-item wavefronts' first round and the rest smallest first; otherwise rounds filled
+    alternately from the largest and the smallest left.  Partitions of pt positions after `base`
+    (a shared prefix of that length when `prefix`), H items per partition."""
+    items, steps = [], []
+    for L in np.clip(lens, 0, max_len):
+        L = int(L)
+        n = -(-(L - base) // pt) if L > base else (0 if prefix else 1)
+        items.append(n * H)
+        steps.append(-(-(-(-(L - base) // 16)) // n) if L > base else 0)
+    rest = sorted(range(len(lens)), key=lambda s: -steps[s])  # stable
+    total = sum(items)
+    if round_items < total <= 2 * round_items:
+        # two rounds: the largest sequences on the one-item wavefronts, the next largest in the
+        # two-item wavefronts' first round, the rest smallest first
+        pairs, singles = total - round_items, 2 * round_items - total
+        first, single, second, nf, ns = [], [], [], 0, 0
+        for s in rest:
+            if ns + items[s] <= singles:
+                single.append(s)
+                ns += items[s]
+            elif nf + items[s] <= pairs:
+                first.append(s)
+                nf += items[s]
+            else:
+                second.append(s)
+        return first + single + second[::-1]
+    out, rnd = [], 0
+    while rest:
+        n = 0
+        while rest and n < round_items:
+            s = rest.pop(0) if rnd % 2 == 0 else rest.pop()
+            out.append(s)
+            n += items[s]
+        rnd += 1
+    return out

@@ -15,7 +15,7 @@ import oracle
 from paged_kv_cache_356_amd import api
 from paged_kv_cache_356_amd import workloads as wl
 from paged_kv_cache_356_amd.decode_batch import DecodeBatch
-from tests.helpers import RAW_NP, TOL, host_pool, max_abs_err, raw
+from tests.helpers import RAW_NP, TOL, host_pool, max_abs_err, plan_order_model, raw
 from oracle.batch import OracleBatch, as_f64, device_pool_bytes
 
 pytestmark = pytest.mark.gpu
@@ -973,6 +973,9 @@ def test_dealing_order_is_bitwise_invisible(case):
     _say(f"  {items} items, {rnd} per round")
     assert sorted(plan.tolist()) == list(range(200)) and 0 < rnd < items
     assert plan.tolist() != list(range(200))
+    # the arrangement at the device's own round size (one or two rounds, or more)
+    assert plan.tolist() == plan_order_model(st.ctx, 64, w.num_kv_heads, base, base > 0, rnd,
+                                             b.max_context_len)
     perm = rng.permutation(200).astype(np.int32)
     for oname, order in (("plan", plan), ("random", perm), ("reversed", np.arange(199, -1, -1))):
         out = torch.full_like(ref, 3.0)
