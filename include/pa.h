@@ -289,9 +289,11 @@ pa_status pa_decode_attention_noalloc(void *out, const void *query, int32_t q_dt
  *   workspace     at least pa_decode_shared_prefix_workspace_bytes() bytes.
  * The prefix is computed in chunks of 512 positions; the positions after it are cut into
  * partitions as in pa_decode_attention (ceil((L - prefix_len) / partition_size) of them).
- * All other arguments and rules are those of pa_decode_attention; block_size must be 16.  Batches
- * the prefix path does not cover (more than 2048 sequences, the vector-ALU dtype pairs,
- * PA_DECODE_FORCE_VALU) are computed by the plain decode, with the same result.
+ * All other arguments and rules are those of pa_decode_attention.  The prefix path runs on
+ * 16-position blocks; batches it does not cover (8- or 32-position blocks, more than 2048
+ * sequences, the vector-ALU dtype pairs, PA_DECODE_FORCE_VALU) are computed by the plain decode,
+ * with the same result: each sequence then reads the prefix through its own table, and
+ * prefix_table is checked but not read.
  */
 pa_status pa_decode_attention_shared_prefix(void *out, const void *query, int32_t q_dtype,
                                             int64_t q_stride, const pa_cache *cache,
@@ -322,10 +324,11 @@ pa_status pa_decode_attention_shared_prefix(void *out, const void *query, int32_
  *                 (its block table's entry for that position times block_size, plus the offset),
  *                 or negative for no write.  With a shared prefix the position must lie after it
  *                 (context_lens[s] > prefix_len); a slot given for a shorter context is not
- *                 written.  Two sequences must not share a slot.  With prefix_len > 0 the call
- *                 needs the prefix path (the batches pa_decode_attention_shared_prefix computes
- *                 with its prefix groups): anything else is PA_ERR_UNSUPPORTED, and nothing is
- *                 written.
+ *                 written (and its attention reads position context_lens[s] - 1 from the pool).
+ *                 Two sequences must not share a slot.  With prefix_len > 0 the call needs the
+ *                 matrix-core kernel (the prefix path, or the plain decode for the batches the
+ *                 prefix path does not cover): the vector-ALU configurations are
+ *                 PA_ERR_UNSUPPORTED, and nothing is written.
  *   prefix_table, prefix_len  as in pa_decode_attention_shared_prefix (NULL / 0: plain decode).
  *   workspace     at least pa_decode_workspace_bytes() (pa_decode_shared_prefix_workspace_bytes()
  *                 with a prefix) bytes.

@@ -131,8 +131,19 @@ def pool_elems(num_blocks: int, H: int, D: int, B: int = 16) -> int:
     return num_blocks * H * B * D
 
 
+def _check_pools(k_pool, v_pool, cache_dtype, num_blocks, H, D, B):
+    """The C routines index the pools by (block, head, slot, dim); refuse arrays smaller than the
+    geometry they are told (a wrong block size would read past their end)."""
+    need = pool_elems(num_blocks, H, D, B) * ELEM_BYTES[_code(cache_dtype)]
+    for name, pool in (("k_pool", k_pool), ("v_pool", v_pool)):
+        if np.asarray(pool).nbytes < need:
+            raise ValueError(f"{name} holds {np.asarray(pool).nbytes} bytes, fewer than "
+                             f"{num_blocks} blocks of {B} positions x {H} heads x {D} need ({need})")
+
+
 def gather(k_pool, v_pool, cache_dtype, k_scale, v_scale, num_blocks, H, D, table, L, h, B=16):
     """De-page positions [0, L) of one sequence's KV head h into fp64 [L][D] arrays."""
+    _check_pools(k_pool, v_pool, cache_dtype, num_blocks, H, D, B)
     kc = np.zeros((max(L, 1), D), np.float64)
     vc = np.zeros((max(L, 1), D), np.float64)
     table = np.ascontiguousarray(table, np.int32)
@@ -160,6 +171,7 @@ def decode_attention(q, q_dtype, k_pool, v_pool, cache_dtype, k_scale, v_scale, 
                      q_stride=0):
     """fp64 decode attention.  q: raw [S][Hq*D] array (f32 values, or uint16 bits for f16/bf16).
     sel: optional (seq_idx, head_idx) int arrays; returns [len(sel)][D], else [S][Hq][D]."""
+    _check_pools(k_pool, v_pool, cache_dtype, num_blocks, H, D, B)
     block_tables = np.ascontiguousarray(block_tables, np.int32)
     context_lens = np.ascontiguousarray(context_lens, np.int32)
     S, M = block_tables.shape
@@ -215,6 +227,7 @@ def prefill_attention(q, q_dtype, k_pool, v_pool, cache_dtype, k_scale, v_scale,
 def reshape_and_cache(k_pool, v_pool, cache_dtype, k_scale, v_scale, num_blocks, H, D, key, value,
                       in_dtype, slots, B=16, key_stride=None, value_stride=None):
     """In-place replay into host pools (numpy arrays of the cache's raw element type)."""
+    _check_pools(k_pool, v_pool, cache_dtype, num_blocks, H, D, B)
     key = np.ascontiguousarray(key)
     value = np.ascontiguousarray(value)
     slots = np.ascontiguousarray(slots, np.int64)

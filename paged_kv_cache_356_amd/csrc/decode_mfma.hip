@@ -670,8 +670,9 @@ __device__ __forceinline__ void write_token_rows(const DecodeArgs &a, int rank, 
   for (int r = GW - 1 - rank; r < rows; r += GW) {
     const int s = r / H, h = r - (r / H) * H;
     // with a shared prefix, a context that does not extend past it takes no write (its position
-    // would lie in the prefix's blocks, which the prefix groups are reading)
-    if (a.prefix_len > 0 && __builtin_amdgcn_readfirstlane(clamp_len(a, s)) <= a.prefix_len) continue;
+    // would lie in the prefix's blocks, which every sequence of the batch reads)
+    if (a.append_from > 0 && __builtin_amdgcn_readfirstlane(clamp_len(a, s)) <= a.append_from)
+      continue;
     const int64_t slot = a.append_slots[s];
     const int64_t sl =
         (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(slot >> 32)) << 32) |
@@ -754,7 +755,7 @@ __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int h_i
   // Fused append: the row's last item (the one whose positions end at the context length) writes
   // the new token and takes position L - 1 from registers; its pool walk stops before it.
   const int L = __builtin_amdgcn_readfirstlane(L_in);
-  const bool append = kApp && end == L;
+  const bool append = kApp && end == L && !(a.append_from > 0 && L <= a.append_from);
   const int e = append && L > 0 ? L - 1 : end;
   rows_core<CT, QT, D, kNT, kB>(a, table, h, jb0, append ? min(jb1, (e + kBlock - 1) / kBlock) : jb1,
                                 e, slot, s, rhq, rvalid, e, tbl0, settle, append, L);

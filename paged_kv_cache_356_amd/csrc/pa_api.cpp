@@ -291,9 +291,6 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
   }
   const int B = cache->block_size;
   if (B != PA_BLOCK_SIZE) {
-    if (prefix_len > 0)
-      return fail(PA_ERR_UNSUPPORTED, "%s: a shared prefix needs block_size %d", who,
-                  PA_BLOCK_SIZE);
     if (flags & PA_DECODE_FORCE_VALU)
       return fail(PA_ERR_UNSUPPORTED, "%s: the vector-ALU kernel needs block_size %d", who,
                   PA_BLOCK_SIZE);
@@ -348,8 +345,9 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
   a.part_ml = nullptr;
   a.seq_order = seq_order;
   const bool force_valu = (flags & PA_DECODE_FORCE_VALU) != 0;
-  // The prefix's tiles need the matrix-core kernel; elsewhere the plain decode gives the same result.
-  bool use_prefix = prefix_len > 0;
+  // The prefix's tiles need the matrix-core kernel on 16-position blocks; elsewhere the plain
+  // decode gives the same result, each sequence reading the prefix through its own table.
+  bool use_prefix = prefix_len > 0 && B == PA_BLOCK_SIZE;
   if (use_prefix) {
     pa::DecodeArgs t = a;
     t.prefix_len = prefix_len;
@@ -358,7 +356,7 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
   // With a shared prefix only the kernel's own write keeps a context that ends inside the prefix
   // from being written (reshape_and_cache would write every slot): it needs 16-bit rows it can
   // read in pairs.
-  if (app && use_prefix &&
+  if (app && prefix_len > 0 &&
       ((reinterpret_cast<uintptr_t>(ap.key) & 3u) != 0 ||
        (reinterpret_cast<uintptr_t>(ap.value) & 3u) != 0 || ap.key_stride % 2 != 0 ||
        ap.value_stride % 2 != 0))
@@ -416,13 +414,14 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
                 "query dtype, or fp8 cache with f16 queries; 16-byte aligned query rows, 8-byte "
                 "aligned output)",
                 who, B);
-  // With a shared prefix, only the prefix kernel keeps a context that ends inside the prefix from
-  // writing its token into the shared blocks; batches it does not cover are refused rather than
-  // appended by a path without that guard.
-  if (app && prefix_len > 0 && !use_prefix)
+  // With a shared prefix, only the matrix-core kernel's own write keeps a context that ends inside
+  // the prefix from writing its token into the shared blocks (the prefix kernel, or the plain
+  // decode with append_from); the vector-ALU configurations are refused rather than appended by a
+  // path without that guard.
+  if (app && prefix_len > 0 && !use_mfma)
     return fail(PA_ERR_UNSUPPORTED,
-                "%s: the append with a shared prefix needs the prefix path (f16 / bf16 cache with "
-                "the same query dtype or fp8 cache with f16 queries, at most 2048 sequences, no "
+                "%s: the append with a shared prefix needs the matrix-core kernel (f16 / bf16 cache "
+                "with the same query dtype or fp8 cache with f16 queries, no "
                 "PA_DECODE_FORCE_VALU); call pa_reshape_and_cache and "
                 "pa_decode_attention_shared_prefix instead",
                 who);
@@ -434,6 +433,7 @@ pa_status decode_common(const char *who, void *out, const void *query, int32_t q
                        ap.key_stride % 2 == 0 && ap.value_stride % 2 == 0;
     if (fused) {
       a.append_slots = ap.slots;
+      a.append_from = prefix_len;
       a.append_k = ap.key;
       a.append_v = ap.value;
       a.append_k_stride = ap.key_stride;

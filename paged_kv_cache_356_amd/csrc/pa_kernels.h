@@ -72,6 +72,10 @@ struct DecodeArgs {
   // is the slot of position context_lens[s] - 1; the wavefront of each (s, KV head) row's last
   // item writes that head's part and takes the position from registers instead of the pool.
   const int64_t *append_slots;
+  // With a shared prefix of append_from positions (0: none), a context of at most append_from
+  // positions takes no write: its position lies in the shared blocks, which keep their bytes, and
+  // the attention reads it from the pool.
+  int32_t append_from;
   const void *append_k;
   const void *append_v;
   int64_t append_k_stride;

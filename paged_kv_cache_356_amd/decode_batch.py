@@ -73,7 +73,6 @@ class DecodeBatch:
         self.layers = list(range(w.num_layers)) if layers is None else list(layers)
         self.partition_size = w.partition_size if partition_size is None else partition_size
         B = w.block_size
-        assert B == api.PA_BLOCK_SIZE or not w.prefix_len, "a shared prefix needs 16-position blocks"
         self.bm = api.BlockManager(w.num_blocks, B, self.free_order)
 
         # (2) the workload's recipe on the block manager, then (4) this step's appends
@@ -123,11 +122,11 @@ class DecodeBatch:
                     # set 0's history rows, kept for checks on the host
                     st.hist_k[l], st.hist_v[l] = hk, hv
                 del hk, hv
-        # the shared prefix's blocks: the first prefix_len / 16 entries of every table (all equal)
+        # the shared prefix's blocks: the first prefix_len / B entries of every table (all equal)
         self.prefix_len = w.prefix_len
         self.prefix_tables = []
         if self.prefix_len:
-            nb = self.prefix_len // api.PA_BLOCK_SIZE
+            nb = self.prefix_len // B
             for st in self.sets:
                 first = st.tables[:, :nb]
                 assert (first == first[0]).all(), "the batch's tables do not share the prefix blocks"

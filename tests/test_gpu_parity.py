@@ -396,6 +396,44 @@ def test_shared_prefix_decode_matches_oracle(ps, cache_dtype, D):
         assert err <= tol
 
 
+@pytest.mark.parametrize("cache_dtype", ["f16", "fp8"])
+@pytest.mark.parametrize("B", [8, 32])
+def test_shared_prefix_other_block_sizes_match_oracle(B, cache_dtype):
+    """pa_decode_attention_shared_prefix on 8- and 32-position blocks (computed by the plain
+    decode, every sequence reading the prefix through its own table) against the oracle: the
+    recipe's batch with its copy-on-write step, then contexts cut below and to exactly the
+    prefix.  The fused append at these sizes is covered beside the plain append."""
+    w = wl.WORKLOADS["f16_shared_prefix_batch256"].replace(num_seqs=7, num_blocks=1024 * 16 // B,
+                                                           prefix_len=64, cache_dtype=cache_dtype,
+                                                           block_size=B)
+    tol = TOL[cache_dtype]
+    lengths = [64 + 1, 64 + 16, 64 + 17, 64 + 300, 64 + 2, 64 + 511, 64 + 40]
+    _say(f"shared-prefix decode, {cache_dtype} cache, block size {B}")
+    pad = _pad_block(w)
+    b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON, lengths=lengths)
+    assert b.use_prefix
+    ob = OracleBatch(b, pad, pool_fill=POISON)
+    ob.metadata_matches(b)
+    _check_batch(b, ob, 0, tol)
+    st = b.sets[0]
+    kp, vp, ks, vs = ob.pools[(0, 0)]
+    ctx = st.ctx.copy()
+    ctx[[0, 3]] = [20, 64]  # below the prefix; exactly the prefix
+    d_ctx = torch.from_numpy(ctx).cuda()
+    q = raw(st.q[0]).reshape(w.num_seqs, -1)
+    ref = oracle.decode_attention(q, w.q_dtype, kp, vp, w.cache_dtype, ks, vs, w.num_blocks,
+                                  w.num_kv_heads, w.head_dim, ob.sets[0]["tables"], ctx,
+                                  w.num_q_heads, w.scale, B=B)
+    out = torch.full_like(st.out[0], 5.0)
+    api.pa_decode_attention_shared_prefix(out, st.q[0], b.caches[0], st.d_tables, d_ctx,
+                                          b.max_context_len, w.scale, b.prefix_tables[0],
+                                          b.prefix_len, 0, b.workspace)
+    torch.cuda.synchronize()
+    err = max_abs_err(as_f64(out), ref)
+    _say(f"  cut contexts: max-abs err {err:.3e}")
+    assert err <= tol
+
+
 def test_poison_outside_the_context_never_leaks():
     _say("NaN poison")
     w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=5, num_blocks=512)
@@ -744,9 +782,9 @@ def test_fused_append_matches_oracle(name, flags, D):
 
 
 def _refused_append_writes_nothing(b, flags=api.PA_DECODE_FORCE_VALU):
-    """A shared-prefix append off the prefix path (vector-ALU kernel, or more sequences than the
-    prefix groups take) is refused with PA_ERR_UNSUPPORTED before anything is enqueued: the pools
-    keep every byte."""
+    """A shared-prefix append on the vector-ALU kernel (which has no guard for contexts inside the
+    prefix) is refused with PA_ERR_UNSUPPORTED before anything is enqueued: the pools keep every
+    byte."""
     b.copy(0)
     torch.cuda.synchronize()
     before = [device_pool_bytes(b.caches[l]) for l in b.layers]
@@ -760,28 +798,12 @@ def _refused_append_writes_nothing(b, flags=api.PA_DECODE_FORCE_VALU):
         assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
 
 
-def test_fused_append_shared_prefix_refused_beyond_the_prefix_groups():
-    """More sequences than the prefix groups' scan takes (2,048): the shared-prefix append has no
-    path that keeps a context ending inside the prefix from writing into it, so it is refused and
-    nothing is written; the two calls (reshape_and_cache + the shared-prefix decode, which falls back
-    to the plain decode) remain available."""
-    S = 2050
-    lengths = np.full(S, 64 + 3, np.int32)
-    w = _reduced("f16_shared_prefix_batch256", num_seqs=S, num_blocks=8192, num_layers=1)
-    _say(f"fused append refused, shared prefix, {S} sequences")
-    b = DecodeBatch(w, pad_block=0, lengths=lengths)
-    b.fused = True
-    _refused_append_writes_nothing(b, flags=api.PA_DECODE_DEFAULT)
-
-
 @pytest.mark.parametrize("B", [8, 16, 32])
 @pytest.mark.parametrize("name", ["f16_batch32", "fp8_28layer_batch512", "f16_shared_prefix_batch256"])
 def test_fused_append_equals_two_calls(name, B):
     """The fused call leaves the pools byte for byte as reshape_and_cache + decode do, and its
     attention agrees with theirs within the tolerance (only the new position's place in the
     summation differs); repeating the call gives the same bits (the write is idempotent)."""
-    if B != 16 and name == "f16_shared_prefix_batch256":
-        pytest.skip("the shared prefix runs on 16-position blocks")
     kw = {}
     if B != 16:
         kw = dict(block_size=B, num_blocks=SMALL[name]["num_blocks"] * 16 // B)
@@ -808,13 +830,22 @@ def test_fused_append_equals_two_calls(name, B):
         assert torch.equal(b1.sets[0].out[l], o1)
 
 
-def test_fused_append_shared_prefix_short_context_not_written():
+@pytest.mark.parametrize("B,S", [(16, None), (8, None), (32, None), (16, 2050)])
+def test_fused_append_shared_prefix_short_context_not_written(B, S):
     """With a shared prefix, a sequence whose context does not extend past the prefix takes no
     write (its slot would lie in the shared blocks): the pools keep their bytes there and its
-    attention is that of the unchanged pool."""
-    w = _reduced("f16_shared_prefix_batch256", num_layers=1)
-    lengths = SMALL_LENGTHS["f16_shared_prefix_batch256"]
-    _say("fused append, shared prefix, a context inside the prefix")
+    attention is that of the unchanged pool.  At 8- and 32-position blocks, and with more
+    sequences (2,050) than the prefix groups take, the plain decode runs the call and keeps the
+    same rule."""
+    name = "f16_shared_prefix_batch256"
+    kw = {} if B == 16 else dict(block_size=B, num_blocks=SMALL[name]["num_blocks"] * 16 // B)
+    lengths = SMALL_LENGTHS[name]
+    if S is not None:
+        kw.update(num_seqs=S, num_blocks=8192)
+        lengths = 64 + 1 + np.arange(S, dtype=np.int32) % 37
+    w = _reduced(name, num_layers=1, **kw)
+    _say(f"fused append, shared prefix, a context inside the prefix, block size {B}, "
+         f"{w.num_seqs} sequences")
     pad = _pad_block(w)
     b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON, lengths=lengths)
     st = b.sets[0]
@@ -826,7 +857,8 @@ def test_fused_append_shared_prefix_short_context_not_written():
     ctx = st.ctx.copy()
     ctx[1] = 40  # inside the 64-position prefix
     d_ctx = torch.from_numpy(ctx).cuda()
-    prefix_slot = int(ob.sets[0]["tables"][1, 0]) * w.block_size + 39  # position 39 of the prefix
+    # position 39 of the prefix
+    prefix_slot = int(ob.sets[0]["tables"][1, 39 // B]) * w.block_size + 39 % B
     slots = st.d_slots.clone()
     slots[1] = prefix_slot
     new_k = st.new_k[0].clone()
@@ -846,7 +878,7 @@ def test_fused_append_shared_prefix_short_context_not_written():
     q = raw(st.q[0]).reshape(w.num_seqs, -1)
     ref = oracle.decode_attention(q, w.q_dtype, kp, vp, w.cache_dtype, None, None, w.num_blocks,
                                   w.num_kv_heads, w.head_dim, ob.sets[0]["tables"], ctx,
-                                  w.num_q_heads, w.scale)
+                                  w.num_q_heads, w.scale, B=B)
     err = max_abs_err(as_f64(out), ref)
     _say(f"  max-abs err {err:.3e}")
     assert err <= TOL["f16"]

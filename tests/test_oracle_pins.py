@@ -619,3 +619,19 @@ def test_layout_indices_of_an_8_position_block():
     assert oracle.v_index(3, 1, 5, 19, H, D, B) == 3584 + 157
     # block 0, head 0, position 7, dim 63: K (7*8 + 7)*8 + 7 = 511 (the tile's last element)
     assert oracle.k_index(0, 0, 7, 63, H, D, B, "f16") == 511
+
+
+def test_oracle_refuses_pools_smaller_than_their_geometry():
+    """A pool of 8-position blocks read as 16-position blocks would be indexed past its end: the
+    oracle's wrappers refuse it before the C routines run."""
+    nb, H, D = 4, 1, 8
+    kp = np.zeros(oracle.pool_elems(nb, H, D, 8), np.float32)
+    vp = np.zeros_like(kp)
+    q = np.zeros((1, D), np.float32)
+    table = np.array([[3, 2, 1, 0]], np.int32)
+    ctx = np.array([20], np.int32)
+    oracle.decode_attention(q, "f32", kp, vp, "f32", None, None, nb, H, D, table, ctx, 1, 1.0, B=8)
+    with pytest.raises(ValueError, match="fewer than"):
+        oracle.decode_attention(q, "f32", kp, vp, "f32", None, None, nb, H, D, table, ctx, 1, 1.0)
+    with pytest.raises(ValueError, match="fewer than"):
+        oracle.gather(kp, vp, "f32", None, None, nb, H, D, table[0], 20, 0)
