@@ -148,10 +148,11 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def measured_traffic(w, default_run: bool):
+def measured_traffic(w, default_run: bool, partition_size: int):
     """HBM bytes per decode call from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs summarised in
     profiles/traffic.json (scaled by the reference copy), or None when this run is not the measured
-    configuration or the kernel sources have changed since the counters were taken."""
+    configuration (the same workload and call partition size) or the kernel sources have changed
+    since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not default_run or not os.path.exists(path):
@@ -163,7 +164,10 @@ def measured_traffic(w, default_run: bool):
             h.update(fh.read())
     if h.hexdigest() != t["sha256"] or w.name not in t["workloads"]:
         return None
-    return int(t["workloads"][w.name]["bytes_per_call"])
+    rec = t["workloads"][w.name]
+    if rec.get("partition_size") != partition_size:
+        return None
+    return int(rec["bytes_per_call"])
 
 
 def cpu_baseline(batch, budget_s: float) -> dict:
@@ -586,6 +590,9 @@ def main() -> int:
         if batch.sets[0].pairs.shape[0] else None
     gc.enable()
     ms_per_step = elapsed * 1e3 / args.steps
+    # the partition size the decode calls were made with (the planner's, where it picked one)
+    call_partition = batch.call_partition(0, flags, fused) or batch.partition_size or \
+        api.pa_decode_auto_partition(w.num_seqs, w.num_kv_heads, batch.max_context_len)
     layers = len(batch.layers)
     kv_logical = batch.kv_bytes_per_layer(unique=False)
     unique = w.prefix_len > 0
@@ -618,8 +625,9 @@ def main() -> int:
             "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "layers": layers,
             "num_blocks_per_layer": w.num_blocks, "context_lens": wl.lengths_summary(batch.lengths),
-            "partition_size": batch.partition_size or api.pa_decode_auto_partition(
-                w.num_seqs, w.num_kv_heads, batch.max_context_len),
+            "partition_size": call_partition,
+            "partition_planned": bool(not batch.partition_size and
+                                      batch.call_partition(0, flags, fused)),
             "kernel": "valu" if args.valu else "default",
             "shared_prefix_decode": bool(batch.use_prefix),
             "dealing_order": "batch order" if args.no_plan else
@@ -665,7 +673,7 @@ def main() -> int:
             "traffic": measured_traffic(w, args.partition < 0 and not args.valu and not fused and
                                         not args.contiguous and not args.no_plan and
                                         not args.num_blocks and not args.no_prefix and
-                                        args.block_size == 16),
+                                        args.block_size == 16, call_partition),
             "traffic_note": "HBM bytes per call from rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE "
                             "(decode + reduce kernels; profiles/traffic.json), null unless this run "
                             "is the measured configuration of unchanged kernels",

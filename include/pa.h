@@ -237,13 +237,24 @@ pa_status pa_decode_attention(void *out, const void *query, int32_t q_dtype, int
  *                 a shared prefix, at most one round).
  *   round_items   optional (NULL): the items per round, the grid's wavefronts that take sequence
  *                 items on the current device (0 with the identity).
+ *   partition_size_out  optional (NULL): the partition_size to make the call with, for which the
+ *                 order was planned.  The caller's own partition_size, except where it is 0
+ *                 (automatic) for a call without a shared prefix whose list takes more than one
+ *                 round: then the planner also tries larger partitions (multiples of 64 positions
+ *                 above the automatic size, up to 2,048, while the list keeps more than one round)
+ *                 and returns the one whose planned deal has the least busiest-wavefront KV bytes
+ *                 plus 240 KiB per round of items (fewer items: fewer ring fills, partials and
+ *                 merges; a measured trade-off), or 0 where the automatic size wins.  A size the
+ *                 planner returns is never below the automatic one, so a workspace sized for
+ *                 partition_size 0 still suffices.
  * The grid depends on the current device (its compute units); an order planned for another
  * device, or for other lengths, is still a valid seq_order, only less balanced.
  */
 pa_status pa_decode_plan(const pa_cache *cache, int32_t q_dtype, const int32_t *context_lens,
                          int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                          int32_t max_context_len, int32_t prefix_len, int32_t partition_size,
-                         uint32_t flags, int32_t *seq_order, int32_t *round_items);
+                         uint32_t flags, int32_t *seq_order, int32_t *round_items,
+                         int32_t *partition_size_out);
 
 /*
  * pa_decode_attention_noalloc — pa_decode_attention without a workspace argument, for callers that

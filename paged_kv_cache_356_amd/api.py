@@ -89,7 +89,7 @@ def lib() -> ctypes.CDLL:
                                                    _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
                                                    _vp, _i32, _i32, _vp, _sz, _u32, _vp]),
             "pa_decode_plan": (_i32, [_cp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _u32,
-                                      _vp, _vp]),
+                                      _vp, _vp, _vp]),
             "pa_check_seq_order": (_i32, [_vp, _i32]),
             "pa_decode_attention_noalloc": (_i32, [_vp, _vp, _i32, _i64, _cp, _vp, _i32, _vp,
                                                     _i32, _i32, _i32, _f32, _i32, _u32, _vp]),
@@ -322,18 +322,21 @@ def pa_decode_attention(out: torch.Tensor, query: torch.Tensor, cache: KVCache,
 def pa_decode_plan(cache: KVCache, q_dtype: torch.dtype, context_lens, num_q_heads: int,
                    max_blocks_per_seq: int, max_context_len: int, prefix_len: int = 0,
                    partition_size: int = 0, flags: int = PA_DECODE_DEFAULT,
-                   with_round: bool = False):
+                   with_round: bool = False, with_partition: bool = False):
     """The dealing order pa_decode_plan computes from the host's context lengths (a sequence of
-    ints): an int32 numpy array [S]; with_round also returns the items per round."""
+    ints): an int32 numpy array [S]; with_round also returns the items per round, with_partition
+    the partition size to make the call with (order, [round], [partition])."""
     lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
     S = int(lens.shape[0])
     order = np.empty(S, np.int32)
     rnd = ctypes.c_int32(0)
+    pt = ctypes.c_int32(0)
     _check(lib().pa_decode_plan(ctypes.byref(cache.struct()), TORCH_CODES[q_dtype], _ptr(lens), S,
                                 int(num_q_heads), int(max_blocks_per_seq), int(max_context_len),
                                 int(prefix_len), int(partition_size), int(flags), _ptr(order),
-                                ctypes.byref(rnd)))
-    return (order, rnd.value) if with_round else order
+                                ctypes.byref(rnd), ctypes.byref(pt)))
+    out = (order,) + ((rnd.value,) if with_round else ()) + ((pt.value,) if with_partition else ())
+    return out if len(out) > 1 else order
 
 
 def pa_decode_attention_noalloc(out: torch.Tensor, query: torch.Tensor, cache: KVCache,

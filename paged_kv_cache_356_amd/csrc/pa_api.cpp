@@ -612,14 +612,135 @@ pa_status pa_check_seq_order(const int32_t *seq_order, int32_t num_seqs) {
   return PA_OK;
 }
 
+namespace {
+
+// Items of each sequence (partitions of pt positions after `base`, times the KV heads) and the
+// 16-position steps of its largest item, as the kernel cuts them; returns the list's item count.
+int64_t plan_items(const int32_t *context_lens, int32_t num_seqs, int32_t max_len, int32_t base,
+                   bool use_prefix, int32_t pt, int H, std::vector<int32_t> &items,
+                   std::vector<int32_t> &steps) {
+  items.assign((size_t)num_seqs, 0);
+  steps.assign((size_t)num_seqs, 0);
+  int64_t total = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t L = std::min(std::max(context_lens[s], 0), max_len);
+    const int32_t n = L > base ? ceil_div(L - base, pt) : (use_prefix ? 0 : 1);
+    items[(size_t)s] = n * H;
+    steps[(size_t)s] = L > base ? ceil_div(ceil_div(L - base, pa::kBlock), n) : 0;
+    total += items[(size_t)s];
+  }
+  return total;
+}
+
+// The dealing order of those items on `waves` item wavefronts (item f of the list goes to
+// wavefront f mod waves), written to order[0 .. num_seqs); false, with the order untouched, where
+// it has nothing to balance.
+bool plan_arrange(const std::vector<int32_t> &items, const std::vector<int32_t> &steps,
+                  int64_t total, int waves, bool use_prefix, int32_t *order) {
+  const int32_t num_seqs = (int32_t)items.size();
+  // Where no wavefront gets a second item and no prefix workgroups share the compute units
+  // (whose third, late-starting workgroups the order feeds the small items), or where the list
+  // fills at most half of one round, the order has nothing to balance and the ordered scan only
+  // costs time (measured: 32 fp16 sequences of up to 2,048 positions, 608 items on 1,024
+  // wavefronts, +0.3 us).
+  if (2 * total <= waves || (total <= waves && !use_prefix)) return false;
+  std::vector<int32_t> by_size((size_t)num_seqs);
+  for (int32_t s = 0; s < num_seqs; ++s) by_size[(size_t)s] = s;
+  std::stable_sort(by_size.begin(), by_size.end(),
+                   [&](int32_t x, int32_t y) { return steps[(size_t)x] > steps[(size_t)y]; });
+  int32_t k = 0;
+  if (total > waves && total <= 2 * (int64_t)waves) {
+    // Two rounds: total - waves wavefronts take two items, the others one.  The largest
+    // sequences go to the one-item wavefronts (the last entries of the first round), the next
+    // largest to the two-item wavefronts' first round, and the rest follow smallest first, so that
+    // the second round gives the largest first-round items the smallest second ones.  A sequence
+    // that does not fit a region goes to the next.
+    const int64_t pairs = total - waves, singles = waves - pairs;
+    std::vector<int32_t> first, single, second;
+    int64_t nf = 0, ns = 0;
+    for (int32_t s : by_size) {
+      const int64_t n = items[(size_t)s];
+      if (ns + n <= singles) {
+        single.push_back(s);
+        ns += n;
+      } else if (nf + n <= pairs) {
+        first.push_back(s);
+        nf += n;
+      } else {
+        second.push_back(s);
+      }
+    }
+    for (int32_t s : first) order[k++] = s;
+    for (int32_t s : single) order[k++] = s;
+    for (auto it = second.rbegin(); it != second.rend(); ++it) order[k++] = *it;
+  } else {
+    // Rounds of `waves` items, filled alternately with the largest and the smallest items left,
+    // so that a wavefront given a large item in one round is given a small one in the next.
+    int32_t lo = 0, hi = num_seqs - 1;
+    for (int round = 0; lo <= hi; ++round) {
+      int64_t n = 0;
+      while (lo <= hi && n < waves) {
+        const int32_t s = (round % 2 == 0) ? by_size[(size_t)lo++] : by_size[(size_t)hi--];
+        order[k++] = s;
+        n += items[(size_t)s];
+      }
+    }
+  }
+  return true;
+}
+
+// 16-position steps of the busiest wavefront when order's list is dealt item f -> wavefront
+// f mod waves, every item of a sequence counted at its largest item's steps.  A sequence's items
+// are a run of the list, so each adds its steps to a cyclic range of wavefronts (a difference
+// array: O(num_seqs + waves)).
+int64_t busiest_steps(const int32_t *order, const std::vector<int32_t> &items,
+                      const std::vector<int32_t> &steps, int waves) {
+  std::vector<int64_t> diff((size_t)waves + 1, 0);
+  int64_t every = 0, f = 0;
+  for (size_t k = 0; k < items.size(); ++k) {
+    const int32_t s = order[k];
+    const int64_t n = items[(size_t)s], v = steps[(size_t)s];
+    if (n == 0) continue;
+    every += (n / waves) * v;
+    const int64_t r = n % waves, w0 = f % waves;
+    if (r > 0) {
+      diff[(size_t)w0] += v;
+      if (w0 + r <= waves) {
+        diff[(size_t)(w0 + r)] -= v;
+      } else {
+        diff[(size_t)waves] -= v;
+        diff[0] += v;
+        diff[(size_t)(w0 + r - waves)] -= v;
+      }
+    }
+    f += n;
+  }
+  int64_t run = 0, best = 0;
+  for (int w = 0; w < waves; ++w) {
+    run += diff[(size_t)w];
+    best = std::max(best, run);
+  }
+  return every + best;
+}
+
+// Planned partition sizes: multiples of this step above the automatic size, up to the last.
+constexpr int32_t kPlanPartitionStep = 64;
+constexpr int32_t kPlanPartitionMax = 2048;
+// What one more round of items costs, in bytes of the busiest wavefront's KV stream.
+constexpr double kPlanRoundBytes = 240.0 * 1024.0;
+
+}  // namespace
+
 pa_status pa_decode_plan(const pa_cache *cache, int32_t q_dtype, const int32_t *context_lens,
                          int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                          int32_t max_context_len, int32_t prefix_len, int32_t partition_size,
-                         uint32_t flags, int32_t *seq_order, int32_t *round_items) {
+                         uint32_t flags, int32_t *seq_order, int32_t *round_items,
+                         int32_t *partition_size_out) {
   const char *who = "pa_decode_plan";
   pa_status st = check_cache(cache, who);
   if (st != PA_OK) return st;
   if (round_items) *round_items = 0;
+  if (partition_size_out) *partition_size_out = partition_size;
   if (num_seqs < 0 || num_seqs > 65535)
     return fail(PA_ERR_SHAPE, "%s: num_seqs %d outside 0..65535", who, num_seqs);
   if (num_seqs == 0) return ok();
@@ -656,77 +777,58 @@ pa_status pa_decode_plan(const pa_cache *cache, int32_t q_dtype, const int32_t *
   }
   const bool use_mfma = use_prefix || (!force_valu && pa::decode_mfma_supports(a));
   if (!use_mfma) return ok();  // the vector-ALU kernel deals no list
-  const int32_t pt = resolve_partition(
-      num_seqs, H, use_prefix ? max_context_len - prefix_len : max_context_len, partition_size);
-  a.partition_size = pt;
-  a.num_partitions = (int32_t)decode_slots(max_len, pt, use_prefix ? prefix_len : 0);
-  if (use_prefix) {
-    a.prefix_len = prefix_len;
-    a.prefix_chunks = ceil_div(prefix_len, pa::kPrefixChunk);
-  }
-  if (!pa::order_fits(num_seqs, a.num_partitions)) return ok();  // the call ignores an order
-  const int waves = pa::decode_mfma_item_waves(a);
-  if (waves <= 0) return ok();  // the direct grid: one wavefront per item, no list to deal
-
-  // Items of each sequence and the 16-position steps of its largest item, as the kernel cuts them.
   const int32_t base = use_prefix ? prefix_len : 0;
-  std::vector<int32_t> items((size_t)num_seqs), steps((size_t)num_seqs);
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    const int32_t L = std::min(std::max(context_lens[s], 0), max_len);
-    const int32_t n = L > base ? ceil_div(L - base, pt) : (use_prefix ? 0 : 1);
-    items[(size_t)s] = n * H;
-    steps[(size_t)s] = L > base ? ceil_div(ceil_div(L - base, pa::kBlock), n) : 0;
-  }
-  // Where no wavefront gets a second item and no prefix workgroups share the compute units
-  // (whose third, late-starting workgroups the order feeds the small items), or where the list
-  // fills at most half of one round, the order has nothing to balance and the ordered scan only
-  // costs time (measured: 32 fp16 sequences of up to 2,048 positions, 608 items on 1,024
-  // wavefronts, +0.3 us).
+  // The list and grid at partition size pt: the call's partition slots, its item wavefronts (0:
+  // the direct grid, or an order the call would ignore) and the items.
+  std::vector<int32_t> items, steps;
+  auto setup = [&](int32_t pt, int64_t *total) {
+    a.partition_size = pt;
+    a.num_partitions = (int32_t)decode_slots(max_len, pt, base);
+    if (use_prefix) {
+      a.prefix_len = prefix_len;
+      a.prefix_chunks = ceil_div(prefix_len, pa::kPrefixChunk);
+    }
+    if (!pa::order_fits(num_seqs, a.num_partitions)) return 0;
+    const int waves = pa::decode_mfma_item_waves(a);
+    if (waves > 0)
+      *total = plan_items(context_lens, num_seqs, max_len, base, use_prefix, pt, H, items, steps);
+    return waves;
+  };
+  const int32_t pt0 = resolve_partition(num_seqs, H, max_context_len - base, partition_size);
+  int32_t pt = pt0;
   int64_t total = 0;
-  for (int32_t s = 0; s < num_seqs; ++s) total += items[(size_t)s];
-  if (2 * total <= waves || (total <= waves && !use_prefix)) return ok();
-  std::vector<int32_t> by_size((size_t)num_seqs);
-  for (int32_t s = 0; s < num_seqs; ++s) by_size[(size_t)s] = s;
-  std::stable_sort(by_size.begin(), by_size.end(),
-                   [&](int32_t x, int32_t y) { return steps[(size_t)x] > steps[(size_t)y]; });
-  int32_t k = 0;
-  if (total > waves && total <= 2 * (int64_t)waves) {
-    // Two rounds: total - waves wavefronts take two items, the others one.  The largest
-    // sequences go to the one-item wavefronts (the last entries of the first round), the next
-    // largest to the two-item wavefronts' first round, and the rest follow smallest first, so that
-    // the second round gives the largest first-round items the smallest second ones.  A sequence
-    // that does not fit a region goes to the next.
-    const int64_t pairs = total - waves, singles = waves - pairs;
-    std::vector<int32_t> first, single, second;
-    int64_t nf = 0, ns = 0;
-    for (int32_t s : by_size) {
-      const int64_t n = items[(size_t)s];
-      if (ns + n <= singles) {
-        single.push_back(s);
-        ns += n;
-      } else if (nf + n <= pairs) {
-        first.push_back(s);
-        nf += n;
-      } else {
-        second.push_back(s);
+  int waves = setup(pt0, &total);
+  if (waves <= 0) return ok();
+  // Automatic partitions of a plain decode whose list takes more than one round: larger
+  // partitions mean fewer items, each of which costs its wavefront a ring fill and drain, a
+  // partial and a merge, but a longer busiest wavefront.  Each candidate size's list is arranged
+  // and dealt as below, and the size with the least (busiest wavefront's KV bytes + one round's
+  // cost per round of items) is kept; sizes whose list fits one round are not taken (the deal then
+  // has nothing to balance: the fp8 batch of 512 sequences took 129 us on 3,008 items against
+  // 107 us on 3,720).  Only sizes above the automatic one are tried, so a workspace sized for it
+  // still serves the call.
+  if (partition_size == 0 && !use_prefix && total > waves) {
+    const int eb = a.cache.dtype == pa::kFP8 ? 1 : (a.cache.dtype == pa::kF32 ? 4 : 2);
+    const double step_bytes = 2.0 * pa::kBlock * a.cache.head_dim * eb;
+    std::vector<int32_t> trial((size_t)num_seqs);
+    double best = -1.0;
+    for (int32_t c = pt0; c <= std::max(pt0, kPlanPartitionMax); c += kPlanPartitionStep) {
+      int64_t tc = 0;
+      const int wc = setup(c, &tc);
+      if (wc <= 0 || tc <= wc) break;
+      for (int32_t s = 0; s < num_seqs; ++s) trial[(size_t)s] = s;
+      plan_arrange(items, steps, tc, wc, false, trial.data());
+      const double cost = (double)busiest_steps(trial.data(), items, steps, wc) * step_bytes +
+                          kPlanRoundBytes * (double)tc / wc;
+      if (best < 0.0 || cost < best) {
+        best = cost;
+        pt = c;
       }
     }
-    for (int32_t s : first) seq_order[k++] = s;
-    for (int32_t s : single) seq_order[k++] = s;
-    for (auto it = second.rbegin(); it != second.rend(); ++it) seq_order[k++] = *it;
-  } else {
-    // Rounds of `waves` items, filled alternately with the largest and the smallest items left,
-    // so that a wavefront given a large item in one round is given a small one in the next.
-    int32_t lo = 0, hi = num_seqs - 1;
-    for (int round = 0; lo <= hi; ++round) {
-      int64_t n = 0;
-      while (lo <= hi && n < waves) {
-        const int32_t s = (round % 2 == 0) ? by_size[(size_t)lo++] : by_size[(size_t)hi--];
-        seq_order[k++] = s;
-        n += items[(size_t)s];
-      }
-    }
+    waves = setup(pt, &total);
+    if (pt != pt0 && partition_size_out) *partition_size_out = pt;
   }
+  if (!plan_arrange(items, steps, total, waves, use_prefix, seq_order)) return ok();
   if (round_items) *round_items = waves;
   return ok();
 }

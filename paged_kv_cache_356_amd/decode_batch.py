@@ -191,26 +191,36 @@ class DecodeBatch:
             self.reshape(set_index, layer, stream)
         self.decode(set_index, layer, flags=flags, stream=stream)
 
-    def order(self, set_index: int, flags: int = api.PA_DECODE_DEFAULT, append: bool = False):
-        """The set's dealing order for its decode calls (a device int32 [S]; None with plan off or
-        where the plan is the batch order itself, which the call then deals without the order's
-        extra scan): pa_decode_plan on the host copy of the set's context lengths, computed once
-        per set and call kind."""
+    def plan_for(self, set_index: int, flags: int = api.PA_DECODE_DEFAULT, append: bool = False):
+        """The set's dealing order and partition size for its decode calls: pa_decode_plan on the
+        host copy of the set's context lengths, computed once per set and call kind.  The order
+        is a device int32 [S], None with plan off or where the plan is the batch order itself
+        (which the call then deals without the order's extra scan); the partition size is the
+        batch's own unless that is automatic and the planner picked a larger one."""
         if not self.plan:
-            return None
+            return None, self.partition_size
         key = (set_index, flags, append, self.use_prefix, self.partition_size)
         if key not in self._orders:
             st = self.sets[set_index]
             w = self.w
             cache = self.caches[self.layers[0]]
             q_dtype = st.q[self.layers[0]].dtype
-            order = api.pa_decode_plan(
+            order, pt = api.pa_decode_plan(
                 cache, q_dtype, st.ctx, w.num_q_heads, self.max_blocks, self.max_context_len,
                 self.prefix_len if self.use_prefix else 0, self.partition_size,
-                flags | (api.PA_DECODE_PLAN_APPEND if append else 0))
+                flags | (api.PA_DECODE_PLAN_APPEND if append else 0), with_partition=True)
             identity = bool((order == np.arange(order.shape[0])).all())
-            self._orders[key] = None if identity else torch.from_numpy(order).to(self.device)
+            self._orders[key] = (None if identity else torch.from_numpy(order).to(self.device), pt)
         return self._orders[key]
+
+    def order(self, set_index: int, flags: int = api.PA_DECODE_DEFAULT, append: bool = False):
+        """The set's dealing order (plan_for)."""
+        return self.plan_for(set_index, flags, append)[0]
+
+    def call_partition(self, set_index: int = 0, flags: int = api.PA_DECODE_DEFAULT,
+                       append: bool = False) -> int:
+        """The partition size the set's decode calls are made with (plan_for; 0: automatic)."""
+        return self.plan_for(set_index, flags, append)[1]
 
     def decode(self, set_index: int, layer: int, flags: int = api.PA_DECODE_DEFAULT, stream=None,
                out: torch.Tensor | None = None, append: bool = False):
@@ -223,10 +233,10 @@ class DecodeBatch:
                 if self.use_prefix else {}
             if append:
                 pre.update(key=st.new_k[layer], value=st.new_v[layer], slot_mapping=st.d_slots)
+            order, pt = self.plan_for(set_index, flags, append)
             return api.DecodeCall(o, st.q[layer], self.caches[layer], st.d_tables, st.d_ctx,
-                                  self.max_context_len, self.w.scale, self.partition_size,
-                                  self.workspace, flags,
-                                  seq_order=self.order(set_index, flags, append), **pre)
+                                  self.max_context_len, self.w.scale, pt, self.workspace, flags,
+                                  seq_order=order, **pre)
         if out is not None:
             make(out)(stream)
             return

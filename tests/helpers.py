@@ -88,3 +88,37 @@ def plan_order_model(lens, pt, H, base, prefix, round_items, max_len):
             n += items[s]
         rnd += 1
     return out
+
+
+def plan_busiest_steps(lens, pt, H, order, round_items, max_len):
+    """16-position steps of the busiest wavefront when the items of `order` (each sequence's
+    partitions times H, every one at its largest partition's steps) are dealt item f -> wavefront
+    f mod round_items, one by one."""
+    load = np.zeros(round_items, np.int64)
+    f = 0
+    for s in order:
+        L = int(min(max(int(lens[s]), 0), max_len))
+        n = -(-L // pt) if L > 0 else 1
+        steps = -(-(-(-L // 16)) // n) if L > 0 else 0
+        for _ in range(n * H):
+            load[f % round_items] += steps
+            f += 1
+    return int(load.max())
+
+
+def plan_partition_model(lens, auto, H, round_items, step_bytes, max_len, round_bytes=240 * 1024):
+    """pa_decode_plan's partition size for an automatic call without a prefix: the sizes auto,
+    auto + 64, ... up to 2,048 while the list keeps more than one round, each costed as the busiest
+    wavefront's KV bytes under the planned deal plus round_bytes per round of items; the cheapest
+    (the first of equals), or 0 where that is auto itself."""
+    best, pick = None, auto
+    for c in range(auto, max(auto, 2048) + 1, 64):
+        total = sum((-(-int(min(max(L, 0), max_len)) // c) if L > 0 else 1) * H for L in lens)
+        if total <= round_items:
+            break
+        order = plan_order_model(lens, c, H, 0, False, round_items, max_len)
+        cost = plan_busiest_steps(lens, c, H, order, round_items, max_len) * step_bytes + \
+            round_bytes * total / round_items
+        if best is None or cost < best:
+            best, pick = cost, c
+    return 0 if pick == auto else pick

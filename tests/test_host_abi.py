@@ -16,6 +16,7 @@ from oracle.bm_model import BlockManagerModel, NoBlocks
 from paged_kv_cache_356_amd import api
 from paged_kv_cache_356_amd import workloads as wl
 from tests.helpers import plan_order_model as _snake_model
+from tests.helpers import plan_partition_model as _partition_model
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -488,7 +489,7 @@ def test_seq_order_checks():
 
 
 def _plan(cache, lens, Hq=28, max_blocks=None, max_ctx=None, prefix_len=0, ps=0, flags=0,
-          q_dtype=api.PA_F16):
+          q_dtype=api.PA_F16, with_partition=False):
     lens = np.ascontiguousarray(lens, np.int32)
     S = lens.shape[0]
     B = cache.block_size
@@ -496,9 +497,12 @@ def _plan(cache, lens, Hq=28, max_blocks=None, max_ctx=None, prefix_len=0, ps=0,
     max_blocks = max(1, -(-max_ctx // B)) if max_blocks is None else max_blocks
     order = np.full(S, -7, np.int32)
     rnd = ctypes.c_int32(-1)
+    pt = ctypes.c_int32(-1)
     st = api.lib().pa_decode_plan(ctypes.byref(cache), q_dtype, lens.ctypes.data, S, Hq,
                                   max_blocks, max_ctx, prefix_len, ps, flags, order.ctypes.data,
-                                  ctypes.byref(rnd))
+                                  ctypes.byref(rnd), ctypes.byref(pt))
+    if with_partition:
+        return st, order, rnd.value, pt.value
     return st, order, rnd.value
 
 
@@ -513,10 +517,48 @@ def test_decode_plan_is_the_snake_order():
     assert st == 0, api.lib().pa_last_error()
     assert rnd > 0 and sorted(order.tolist()) == list(range(61))
     assert order.tolist() == _snake_model(lens, 256, 4, 0, False, rnd, int(lens.max()))
-    # the automatic partition size, and lengths above max_context_len clamped as the call does
-    st, order, rnd = _plan(_cache(), lens, max_ctx=2000)
-    pt = api.pa_decode_auto_partition(61, 4, 2000)
-    assert order.tolist() == _snake_model(lens, pt, 4, 0, False, rnd, 2000)
+    # the automatic partition size, and lengths above max_context_len clamped as the call does:
+    # the order is planned for the partition size the planner returns
+    st, order, rnd, pt = _plan(_cache(), lens, max_ctx=2000, with_partition=True)
+    auto = api.pa_decode_auto_partition(61, 4, 2000)
+    assert pt == _partition_model(lens, auto, 4, rnd, 2 * 16 * 128 * 2, 2000)
+    assert order.tolist() == _snake_model(lens, pt or auto, 4, 0, False, rnd, 2000)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_plan_partition_size(seed):
+    """With an automatic partition size and a list of more than one round, pa_decode_plan also
+    picks the partition size (never below the automatic one) by the cost of its own planned deal:
+    checked against the model on random batches (rounds of 4 items without a GPU), the order then
+    being the one planned for that size; an explicit size, or a shared prefix, is kept."""
+    rng = np.random.default_rng(100 + seed)
+    S = int(rng.integers(2, 40))
+    H = int(rng.choice([1, 2, 4]))
+    D = int(rng.choice([64, 128]))
+    dt = [api.PA_F16, api.PA_BF16, api.PA_FP8_E4M3][seed % 3]
+    lens = np.clip(np.rint(rng.lognormal(np.log(int(rng.integers(100, 3000))), 1.0, S)), 1,
+                   20000).astype(np.int32)
+    if seed == 0:
+        lens[:3] = 0
+    scales = dict(k_scale=64, v_scale=128) if dt == api.PA_FP8_E4M3 else {}
+    cache = _cache(cache_dtype=dt, num_kv_heads=H, head_dim=D, **scales)
+    max_ctx = int(lens.max())
+    st, order, rnd, pt = _plan(cache, lens, Hq=4 * H, with_partition=True,
+                               q_dtype=api.PA_F16 if dt == api.PA_FP8_E4M3 else dt)
+    assert st == 0, api.lib().pa_last_error()
+    auto = api.pa_decode_auto_partition(S, H, max_ctx)
+    step_bytes = 2 * 16 * D * (1 if dt == api.PA_FP8_E4M3 else 2)
+    want = _partition_model(lens, auto, H, rnd, step_bytes, max_ctx)
+    assert pt == want and (pt == 0 or auto < pt <= 2048) and pt % 16 == 0
+    assert order.tolist() == _snake_model(lens, pt or auto, H, 0, False, rnd, max_ctx)
+    # an explicit partition size is the caller's to keep
+    st, _, _, pt2 = _plan(cache, lens, Hq=4 * H, ps=auto, with_partition=True,
+                          q_dtype=api.PA_F16 if dt == api.PA_FP8_E4M3 else dt)
+    assert st == 0 and pt2 == auto
+    # the shared-prefix decode keeps its automatic size
+    st, _, _, pt3 = _plan(cache, lens + 64, Hq=4 * H, prefix_len=64, with_partition=True,
+                          q_dtype=api.PA_F16 if dt == api.PA_FP8_E4M3 else dt)
+    assert st == 0 and pt3 == 0
 
 
 def test_decode_plan_two_rounds():
@@ -567,8 +609,8 @@ def test_decode_plan_rejections():
     assert _plan(_cache(block_size=12), lens)[0] == -3
     rnd = ctypes.c_int32(0)
     assert api.lib().pa_decode_plan(ctypes.byref(_cache()), api.PA_F16, lens.ctypes.data, 2, 28,
-                                    1, 16, 0, 0, 0, None, ctypes.byref(rnd)) == -1
-    # an empty batch plans nothing; round_items may be NULL
+                                    1, 16, 0, 0, 0, None, ctypes.byref(rnd), None) == -1
+    # an empty batch plans nothing; round_items and partition_size_out may be NULL
     assert api.lib().pa_decode_plan(ctypes.byref(_cache()), api.PA_F16, None, 0, 28, 1, 16, 0, 0,
-                                    0, None, None) == 0
+                                    0, None, None, None) == 0
 
