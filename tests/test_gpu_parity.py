@@ -15,7 +15,8 @@ import oracle
 from paged_kv_cache_356_amd import api
 from paged_kv_cache_356_amd import workloads as wl
 from paged_kv_cache_356_amd.decode_batch import DecodeBatch
-from tests.helpers import RAW_NP, TOL, host_pool, max_abs_err, plan_order_model, raw
+from tests.helpers import (RAW_NP, TOL, host_pool, max_abs_err, plan_order_model,
+                           plan_partition_model, raw)
 from oracle.batch import OracleBatch, as_f64, device_pool_bytes
 
 pytestmark = pytest.mark.gpu
@@ -977,6 +978,32 @@ def _decode_ordered(b, out, order, append=False):
         pre.update(key=st.new_k[l], value=st.new_v[l], slot_mapping=st.d_slots)
     api.DecodeCall(out, st.q[l], b.caches[l], st.d_tables, st.d_ctx, b.max_context_len, b.w.scale,
                    b.partition_size, b.workspace, api.PA_DECODE_DEFAULT, seq_order=order, **pre)()
+
+
+@pytest.mark.parametrize("cache_dtype", ["fp8", "f16"])
+def test_planned_partition_size_on_the_device(cache_dtype):
+    """On the device's own grid, pa_decode_plan's partition size for the fp8 28-layer batch's
+    lengths (512 sequences, an automatic call of more than one round) equals the model of its
+    search, the order is the one planned for that size, and a call made with it is accepted by a
+    workspace sized for the automatic size."""
+    w = wl.WORKLOADS["fp8_28layer_batch512"]
+    lens = wl.context_lengths(w)
+    H, D = w.num_kv_heads, w.head_dim
+    scales = {} if cache_dtype != "fp8" else dict(
+        k_scale=torch.ones(H, device="cuda"), v_scale=torch.ones(H, device="cuda"))
+    cache = api.KVCache.allocate(16, H, D, cache_dtype, "cuda", **scales)
+    max_ctx = int(lens.max())
+    max_blocks = -(-max_ctx // 16)
+    order, rnd, pt = api.pa_decode_plan(cache, torch.float16, lens, w.num_q_heads, max_blocks,
+                                        max_ctx, 0, 0, 0, with_round=True, with_partition=True)
+    auto = api.pa_decode_auto_partition(w.num_seqs, H, max_ctx)
+    step_bytes = 2 * 16 * D * (1 if cache_dtype == "fp8" else 2)
+    _say(f"  {cache_dtype}: automatic {auto}, planned {pt}, {rnd} items per round")
+    assert rnd > 0 and pt == plan_partition_model(lens, auto, H, rnd, step_bytes, max_ctx)
+    assert pt > auto  # this batch gains from larger partitions
+    assert order.tolist() == plan_order_model(lens, pt, H, 0, False, rnd, max_ctx)
+    ws = api.pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, H, D, max_ctx, 0)
+    assert ws >= api.pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, H, D, max_ctx, pt)
 
 
 @pytest.mark.parametrize("case", list(ORDER_CASES))
