@@ -73,6 +73,9 @@ constexpr bool kDecodeNT = true;
 // shared-prefix one keeps three (its grid needs three workgroups per compute unit).
 constexpr int kDecodeOcc = 3;
 constexpr int kAppendOcc = 2;
+// Paired items run one wavefront per SIMD (pair_items), so their instantiation can take 256
+// registers: the ring's boundary emit stays out of scratch.
+constexpr int kPairOcc = 2;
 
 // off: per-lane byte offset; soff: a wave-uniform byte offset added to it.
 template <class T, bool kNT>
@@ -320,10 +323,18 @@ __device__ __forceinline__ void settle_frag(Frag<CT, D> &f) {
 // address, and waiting for it would drain every load in flight.  A wavefront with more than 64
 // blocks runs one ring per 64 of them.  The first 64 entries (tbl0, from first_table_entries)
 // come from the caller, which can fetch them while the wavefront's previous item streams.
-template <class CT, int D, bool kNT, int kB>
+// kPair: after step mid - 1 (mid > 0) the ring calls at_mid(st), which sets the first partition of
+// a paired item aside and resets the row state, and streams on without draining.
+struct NoMid {
+  template <class T>
+  __device__ void operator()(T &) const {}
+};
+
+template <class CT, int D, bool kNT, int kB, bool kPair = false, class Mid = NoMid>
 __device__ __forceinline__ void stream_blocks(const DecodeArgs &a, const int32_t *table, int h,
                                               int jb0, int jb1, int tbl0, int zlim, int vend,
-                                              float kscale, RowState<D> &st) {
+                                              float kscale, RowState<D> &st, int mid = -1,
+                                              Mid &&at_mid = Mid{}) {
   using F = Frag<CT, D>;
   // blocks per wavefront in the load ring: fp8 fragments are half the registers of 16-bit ones
   constexpr int kBufs = std::is_same<CT, fp8_t>::value ? kFp8Bufs : kDecodeBufs;
@@ -362,6 +373,9 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs &a, const int32_t
       const int t0 = (jb0 + k0 + k) * kBlock;
       const bool zok = kB == 8 ? lane_ok[b] : ok[b];
       block_step<CT, D>(buf[b], kscale, t0, zok ? zlim : t0, ok[b] ? vend : t0, st);
+      if constexpr (kPair) {
+        if (k0 + k + 1 == mid) at_mid(st);  // wave-uniform
+      }
     };
 #pragma unroll
     for (int b = 0; b < kBufs; ++b) load(b, b);  // slots past the end: zeros, no memory access
@@ -706,17 +720,41 @@ __device__ __forceinline__ void write_token_rows(const DecodeArgs &a, int rank, 
 // (tiles that other wavefronts of the call read too).  tbl0: lane i's entry of the first 64
 // blocks (first_table_entries).  settle: a value whose load is in flight (the next item's first
 // table entries), waited for once this item's blocks are done.
-template <class CT, class QT, int D, bool kNT, int kB>
+// kPair: the blocks are two partitions, the first mid steps long (mid > 0); its state is set aside
+// when the ring passes into the second, and its partial goes to workspace slot mid_slot after.
+template <class CT, class QT, int D, bool kNT, int kB, bool kPair = false>
 __device__ __forceinline__ void rows_core(const DecodeArgs &a, const int32_t *table, int h,
                                           int jb0, int jb1, int end, int slot, int rs, int rhq,
                                           bool rvalid, int lim, int tbl0, int &settle, bool append,
-                                          int L) {
+                                          int L, int mid = -1, int mid_slot = -1) {
   RowState<D> st;
   load_query<CT, D>(a, rs, rhq, rvalid, st);
   if (append) stage_new_token<D>(a, rs, h);
   float kscale, vscale;
   head_scales<CT>(a, h, kscale, vscale);
-  stream_blocks<CT, D, kNT, kB>(a, table, h, jb0, jb1, tbl0, lim, end, kscale, st);
+  // Paired items: at the boundary the first partition's state moves to `first` (its partial is
+  // stored after the ring: a store inside it measured 5 us slower on the 32K batch) and the row
+  // state starts over.
+  RowState<D> first;
+  if constexpr (kPair) {
+    first.m = kNoMax;
+    first.l = 0.0f;
+    auto at_mid = [&](RowState<D> &r) {
+      first.m = r.m;
+      first.l = r.l;
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt) {
+        first.acc[nt] = r.acc[nt];
+        r.acc[nt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+      r.m = kNoMax;
+      r.l = 0.0f;
+    };
+    stream_blocks<CT, D, kNT, kB, true>(a, table, h, jb0, jb1, tbl0, lim, end, kscale, st, mid,
+                                        at_mid);
+  } else {
+    stream_blocks<CT, D, kNT, kB>(a, table, h, jb0, jb1, tbl0, lim, end, kscale, st);
+  }
   // Fused append (wave-uniform): position L - 1 was left out of the ring; it is the new token when
   // the slot is in the pool, else what the pool holds there (no write).
   if (append) append_tail<CT, QT, D>(rs, h, L, kscale, st);
@@ -729,16 +767,19 @@ __device__ __forceinline__ void rows_core(const DecodeArgs &a, const int32_t *ta
   for (int kk = 0; kk < D / 32; ++kk)
     asm volatile("" : "+v"(st.qop[kk].x), "+v"(st.qop[kk].y), "+v"(st.qop[kk].z), "+v"(st.qop[kk].w));
   emit_rows<QT, D>(a, st, vscale, partial_vscale<CT, QT>(vscale), slot, rs, rhq, rvalid);
+  if constexpr (kPair)
+    if (mid > 0)
+      emit_rows<QT, D>(a, first, vscale, partial_vscale<CT, QT>(vscale), mid_slot, rs, rhq, rvalid);
 }
 
 // Wavefront item of the decode: KV head h over positions [jb0 * 16, end) of sequence s's block
 // table row, against the g query heads of s (columns 0 .. g - 1 of the products).  Wavefronts of
 // one workgroup run their items independently, so one wavefront's item prologue (query, table
 // fetch, first loads) and epilogue overlap the other wavefronts' block streams.
-template <class CT, class QT, int D, bool kNT, int kB, bool kApp>
+template <class CT, class QT, int D, bool kNT, int kB, bool kApp, bool kPair = false>
 __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int h_in, int jb0_in,
                                           int jb1_in, int end_in, int slot_in, int L_in, int tbl0,
-                                          int &settle) {
+                                          int &settle, int mid_in = -1, int mid_slot_in = -1) {
   // The item is the same for the whole wavefront: keep its fields (and so the tile addresses) in
   // scalar registers.
   const int s = __builtin_amdgcn_readfirstlane(s_in);
@@ -757,8 +798,10 @@ __device__ __forceinline__ void wave_item(const DecodeArgs &a, int s_in, int h_i
   const int L = __builtin_amdgcn_readfirstlane(L_in);
   const bool append = kApp && end == L && !(a.append_from > 0 && L <= a.append_from);
   const int e = append && L > 0 ? L - 1 : end;
-  rows_core<CT, QT, D, kNT, kB>(a, table, h, jb0, append ? min(jb1, (e + kBlock - 1) / kBlock) : jb1,
-                                e, slot, s, rhq, rvalid, e, tbl0, settle, append, L);
+  rows_core<CT, QT, D, kNT, kB, kPair>(
+      a, table, h, jb0, append ? min(jb1, (e + kBlock - 1) / kBlock) : jb1, e, slot, s, rhq,
+      rvalid, e, tbl0, settle, append, L, __builtin_amdgcn_readfirstlane(mid_in),
+      __builtin_amdgcn_readfirstlane(mid_slot_in));
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -916,25 +959,40 @@ __device__ __forceinline__ void prefix_group(const DecodeArgs &a, const int *len
 // Items of sequence s: plain decode, partitions of its context (an empty context counts one item,
 // which writes its zeros); shared-prefix decode, partitions of the positions after the prefix
 // (possibly none).
+// With paired items, a row's partitions are taken two at a time (the last one alone when odd).
 __device__ __forceinline__ int seq_items(const DecodeArgs &a, int L) {
   if (a.prefix_len > 0) return row_partitions(a, L) - a.prefix_chunks;
-  return L > 0 ? row_partitions(a, L) : 1;
+  if (L <= 0) return 1;
+  return a.pair_items ? (row_partitions(a, L) + 1) / 2 : row_partitions(a, L);
 }
 
 // Sequence item `part` of sequence s (context length L), KV head h: its blocks [jb0, jb1), the end
-// of its positions and its workspace slot (-1: the output itself).
+// of its positions and its workspace slot (-1: the output itself).  A paired item covers
+// partitions 2 part and 2 part + 1: slot is the second's, and the first, mid steps long, goes to
+// mid_slot (mid = -1: a single partition).
 struct SeqItem {
-  int s, h, jb0, jb1, end, slot, L;
+  int s, h, jb0, jb1, end, slot, L, mid, mid_slot;
 };
 
 __device__ __forceinline__ SeqItem sequence_item(const DecodeArgs &a, int s, int L, int part,
                                                  int h) {
   const int PT = a.partition_size;
-  SeqItem it{s, h, 0, 0, 0, -1, L};
+  SeqItem it{s, h, 0, 0, 0, -1, L, -1, -1};
   int start, end;
   if (a.prefix_len > 0) {
     partition_range(a.prefix_len, L, PT, part, &start, &end);
     it.slot = a.prefix_chunks + part;
+  } else if (L > 0 && a.pair_items) {
+    const int n = (L + PT - 1) / PT;
+    const int p0 = 2 * part, p1 = min(n, p0 + 2);
+    int s1, e0;
+    partition_range(0, L, PT, p0, &start, &e0);
+    partition_range(0, L, PT, p1 - 1, &s1, &end);
+    it.slot = L > PT ? p1 - 1 : -1;
+    if (p1 - p0 == 2) {
+      it.mid = (e0 - start) / kBlock;
+      it.mid_slot = p0;
+    }
   } else if (L > 0) {
     partition_range(0, L, PT, part, &start, &end);
     it.slot = L > PT ? part : -1;
@@ -947,11 +1005,11 @@ __device__ __forceinline__ SeqItem sequence_item(const DecodeArgs &a, int s, int
   return it;
 }
 
-template <class CT, class QT, int D, int kB, bool kApp>
+template <class CT, class QT, int D, int kB, bool kApp, bool kPair = false>
 __device__ __forceinline__ void run_sequence_item(const DecodeArgs &a, const SeqItem &it, int tbl0,
                                                   int &settle) {
-  wave_item<CT, QT, D, kDecodeNT, kB, kApp>(a, it.s, it.h, it.jb0, it.jb1, it.end, it.slot, it.L,
-                                         tbl0, settle);
+  wave_item<CT, QT, D, kDecodeNT, kB, kApp, kPair>(a, it.s, it.h, it.jb0, it.jb1, it.end, it.slot,
+                                                   it.L, tbl0, settle, it.mid, it.mid_slot);
 }
 
 // Lane i's table entry of the first ring chunk of a sequence item (the table entries of its first
@@ -976,16 +1034,18 @@ __device__ __forceinline__ int item_table_entries(const DecodeArgs &a, const Seq
 // each block through LDS (prefix_group), so a block crosses from L2 once per group instead of once
 // per 16 rows.  The sequence items go first to the wavefronts of workgroups without prefix work, so
 // the streaming of private blocks from HBM starts at once beside the prefix groups.
-template <class CT, class QT, int D, bool kPre, int kB, bool kApp>
+template <class CT, class QT, int D, bool kPre, int kB, bool kApp, bool kPair = false>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(kApp && !kPre ? kAppendOcc : kDecodeOcc)))
+__attribute__((amdgpu_waves_per_eu(kPair ? kPairOcc : kApp && !kPre ? kAppendOcc : kDecodeOcc)))
 void decode_mfma_kernel(DecodeArgs a) {
   static_assert(!kPre || kB == 16, "the shared prefix runs on 16-position blocks");
+  static_assert(!kPair || (!kPre && !kApp && kB == 16), "paired items: plain decode, 16 positions");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = a.num_seqs, H = a.cache.num_kv_heads, g = a.num_q_heads / H;
   const int PT = a.partition_size;
   if (!a.persistent) {
+    if constexpr (kPair) return;  // the launcher pairs items only on the persistent grid
     const int64_t f = (int64_t)blockIdx.x * kWaves + w;
     const int part = (int)(f % a.num_partitions);
     const int h = (int)((f / a.num_partitions) % H);
@@ -1128,7 +1188,7 @@ void decode_mfma_kernel(DecodeArgs a) {
         next = item_of(f + GW);
         tbl_next = item_table_entries<kB>(a, next);
       }
-      run_sequence_item<CT, QT, D, kB, kApp>(a, it, tbl, tbl_next);
+      run_sequence_item<CT, QT, D, kB, kApp, kPair>(a, it, tbl, tbl_next);
       it = next;
       tbl = tbl_next;
     }
@@ -1154,7 +1214,24 @@ int device_cus() {
   return cus;
 }
 
-template <class CT, class QT, int D, bool kPre, int kB, bool kApp>
+// Whether a plain decode takes its partitions two to a wavefront item (pair_items).  One wavefront
+// streaming a row's blocks in one long run outpaces two wavefronts of a SIMD streaming them as two
+// items, and the boundary between the two partitions costs the ring nothing.  Pairs are taken where
+// the list at one partition per item holds between one and two items per SIMD: one round either
+// way, and the pairs still give every SIMD a wavefront.  The count takes every row at the call's
+// largest partition count (the host does not see the context lengths).
+bool pair_items(const DecodeArgs &a) {
+  if (a.prefix_len > 0 || a.append_slots || a.cache.block_size != kBlock ||
+      a.num_seqs > kMaxScanSeqs || a.num_partitions < 2)
+    return false;
+  const int cus = device_cus();
+  if (cus <= 0) return false;
+  const int64_t simds = (int64_t)cus * 4;
+  const int64_t items = (int64_t)a.num_seqs * a.cache.num_kv_heads * a.num_partitions;
+  return items > simds && items <= 2 * simds;
+}
+
+template <class CT, class QT, int D, bool kPre, int kB, bool kApp, bool kPair>
 int resident_groups() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];
@@ -1165,8 +1242,8 @@ int resident_groups() {
     if (c > 0) return c;
   }
   int occ = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_mfma_kernel<CT, QT, D, kPre, kB, kApp>, 256,
-                                                   0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &occ, decode_mfma_kernel<CT, QT, D, kPre, kB, kApp, kPair>, 256, 0) !=
           hipSuccess || occ < 1)
     occ = 1;
   if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
@@ -1178,12 +1255,12 @@ int resident_groups() {
 }
 
 // The instantiation a call runs on, as a tag type for with_kernel's visitor.
-template <class CT_, class QT_, int D_, bool kPre_, int kB_, bool kApp_>
+template <class CT_, class QT_, int D_, bool kPre_, int kB_, bool kApp_, bool kPair_ = false>
 struct KernelCfg {
   using CT = CT_;
   using QT = QT_;
   static constexpr int D = D_, kB = kB_;
-  static constexpr bool kPre = kPre_, kApp = kApp_;
+  static constexpr bool kPre = kPre_, kApp = kApp_, kPair = kPair_;
 };
 
 // Calls f(KernelCfg<...>{}) for the instantiation that computes `a`: cache dtype, head_dim, shared
@@ -1191,6 +1268,8 @@ struct KernelCfg {
 // keeps its registers).
 template <class CT, class QT, int D, bool kPre, int kB, class F>
 auto with_app(const DecodeArgs &a, F &&f) {
+  if constexpr (!kPre && kB == 16)
+    if (a.pair_items) return f(KernelCfg<CT, QT, D, false, 16, false, true>{});
   return a.append_slots ? f(KernelCfg<CT, QT, D, kPre, kB, true>{})
                         : f(KernelCfg<CT, QT, D, kPre, kB, false>{});
 }
@@ -1214,12 +1293,13 @@ auto with_dim(const DecodeArgs &a, F &&f) {
 // workgroups) or persistent (every workgroup that fits at once, at most the direct count).
 template <class C>
 dim3 decode_grid(DecodeArgs &a) {
-  const int64_t items = (int64_t)a.num_partitions * a.cache.num_kv_heads * a.num_seqs;
+  const int64_t parts = C::kPair ? (a.num_partitions + 1) / 2 : a.num_partitions;
+  const int64_t items = parts * a.cache.num_kv_heads * a.num_seqs;
   const int64_t direct = (items + kWaves - 1) / kWaves;
   a.persistent = a.num_seqs <= (C::kPre ? kMaxScanSeqsPrefix : kMaxScanSeqs);
   if (!a.persistent) return dim3((unsigned)direct);
   const int resident = resident_groups<typename C::CT, typename C::QT, C::D, C::kPre, C::kB,
-                                       C::kApp>();
+                                       C::kApp, C::kPair>();
   return dim3((unsigned)std::min<int64_t>(direct, resident));
 }
 
@@ -1227,7 +1307,7 @@ template <class C>
 hipError_t launch_cfg(DecodeArgs a, hipStream_t s) {
   const dim3 grid = decode_grid<C>(a);
   a.num_cus = device_cus();
-  decode_mfma_kernel<typename C::CT, typename C::QT, C::D, C::kPre, C::kB, C::kApp>
+  decode_mfma_kernel<typename C::CT, typename C::QT, C::D, C::kPre, C::kB, C::kApp, C::kPair>
       <<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
@@ -1280,7 +1360,9 @@ bool decode_mfma_supports(const DecodeArgs &a) {
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
   if (a.cache.dtype != kF16 && a.cache.dtype != kBF16 && a.cache.dtype != kFP8)
     return hipErrorInvalidValue;
-  return with_kernel(a, [&](auto c) { return launch_cfg<decltype(c)>(a, s); });
+  DecodeArgs b = a;
+  b.pair_items = pair_items(a) ? 1 : 0;
+  return with_kernel(b, [&](auto c) { return launch_cfg<decltype(c)>(b, s); });
 }
 
 int decode_mfma_item_waves(const DecodeArgs &a) {

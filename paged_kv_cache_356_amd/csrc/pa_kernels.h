@@ -67,6 +67,10 @@ struct DecodeArgs {
   float *part_ml;
   int32_t persistent;       // grid mode of the matrix-core kernel (set by its launcher)
   int32_t num_cus;          // compute units of the device (set by the launcher; 0: unknown)
+  // Paired items (set by the matrix-core launcher; plain decode only): a wavefront's item is two
+  // consecutive partitions of one (sequence, KV head) row, streamed as one run of blocks, the first
+  // partition's partial emitted where the second begins.
+  int32_t pair_items;
   // Fused append (NULL append_slots: none): sequence s's new token, rows append_k/v + s * stride
   // (num_kv_heads * head_dim elements of q_dtype), goes to slot append_slots[s] (< 0: none), which
   // is the slot of position context_lens[s] - 1; the wavefront of each (s, KV head) row's last

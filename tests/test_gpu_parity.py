@@ -435,6 +435,56 @@ def test_shared_prefix_other_block_sizes_match_oracle(B, cache_dtype):
     assert err <= tol
 
 
+def _pairs_taken(S, H, num_partitions):
+    """The matrix-core launcher's rule for paired items: between one and two items per SIMD at the
+    call's largest partition count."""
+    simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    return simds < S * H * num_partitions <= 2 * simds
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("cache_dtype", ["f16", "bf16", "fp8"])
+def test_paired_items_match_oracle(cache_dtype, D):
+    """Batches whose items the kernel takes two partitions at a time (a wavefront streams both as
+    one run of blocks and emits the first's partial where the second begins): against the oracle,
+    with rows of an odd number of partitions, of one partition (written straight to the output),
+    empty rows, a NaN-poisoned pool and workspace, a dealing order, and the batch permuted."""
+    q = "bf16" if cache_dtype == "bf16" else "f16"
+    w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=40, num_blocks=8192, cache_dtype=cache_dtype,
+                                            q_dtype=q, head_dim=D)
+    rng = np.random.default_rng(11)
+    lengths = rng.integers(1, 2600, size=40).astype(np.int32)
+    lengths[:10] = [1, 2, 16, 256, 257, 512, 513, 768, 2600, 2599]
+    npart = -(-int(lengths.max()) // 256)
+    assert _pairs_taken(40, w.num_kv_heads, npart), "the batch must take paired items"
+    _say(f"paired items, {cache_dtype} cache, head_dim {D}, {npart} partitions of 256")
+    pad = _pad_block(w)
+    b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON, lengths=lengths,
+                    partition_size=256)
+    b.workspace.fill_(0xFF)  # NaN in every fp16 / fp32 slot the kernel does not write
+    ob = OracleBatch(b, pad, pool_fill=POISON)
+    ob.metadata_matches(b)
+    tol = TOL[cache_dtype]
+    _check_batch(b, ob, 0, tol)
+    st = b.sets[0]
+    kp, vp, ks, vs = ob.pools[(0, 0)]
+    ctx = st.ctx.copy()
+    ctx[1] = 0  # an empty row: zeros
+    d_ctx = torch.from_numpy(ctx).cuda()
+    ref = oracle.decode_attention(raw(st.q[0]).reshape(w.num_seqs, -1), w.q_dtype, kp, vp,
+                                  w.cache_dtype, ks, vs, w.num_blocks, w.num_kv_heads, w.head_dim,
+                                  ob.sets[0]["tables"], ctx, w.num_q_heads, w.scale)
+    for name, order in (("reversed", np.arange(39, -1, -1)), ("random", rng.permutation(40))):
+        out = torch.full_like(st.out[0], 3.0)
+        api.pa_decode_attention(out, st.q[0], b.caches[0], st.d_tables, d_ctx,
+                                b.max_context_len, w.scale, 256, b.workspace,
+                                seq_order=torch.from_numpy(order.astype(np.int32)).cuda())
+        torch.cuda.synchronize()
+        err = max_abs_err(as_f64(out), ref)
+        _say(f"  {name} order: max-abs err {err:.3e}")
+        assert err <= tol
+
+
 def test_poison_outside_the_context_never_leaks():
     _say("NaN poison")
     w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=5, num_blocks=512)
