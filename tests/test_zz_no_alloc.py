@@ -29,7 +29,11 @@ def test_no_alloc_oversized_call_is_refused_before_any_device_work():
 @pytest.mark.gpu
 def test_no_alloc_matches_the_workspace_decode_on_two_calls():
     torch.cuda.set_device(0)
+    paired = [2600, 1, 257, 512, 513, 2599] + [100 + 83 * i for i in range(24)]
     cases = [
+        # a batch whose items the kernel pairs (30 x 4 rows of up to 11 partitions: between one
+        # and two items per SIMD on 256 compute units), then smaller ones
+        ("f16_batch32", dict(num_seqs=30, num_blocks=8192), paired, 256),
         # several partitions per row (the partials live in the scratch), then a smaller batch
         ("f16_batch32", dict(num_seqs=12, num_blocks=2048), [2048, 1500, 700, 1, 17, 129, 256,
                                                             257, 1999, 64, 640, 1024], 128),
