@@ -485,6 +485,54 @@ def test_paired_items_match_oracle(cache_dtype, D):
         assert err <= tol
 
 
+# Seeded batches of mixed shapes through the whole step (clones, cache writes, the planned order and
+# partition size, the decode): each with the work-distribution mode it reaches on 256 compute units.
+RANDOM_BATCHES = [
+    # (seed, name, cache dtype, head_dim, sequences, length mix, partition size, mode)
+    (1, "f16_batch32", "f16", 128, 64, ("uniform", 16, 1300), 256, "paired"),
+    (2, "f16_batch32", "bf16", 64, 48, ("uniform", 300, 2500), 256, "paired"),
+    (3, "f16_batch32", "f16", 128, 512, ("lognormal", 600, 1.0), 0, "planned partition"),
+    (4, "f16_batch32", "bf16", 64, 400, ("lognormal", 500, 1.0), 0, "planned partition"),
+    (5, "f16_batch32", "bf16", 128, 20, ("uniform", 1, 600), 64, "single items"),
+    (6, "fp8_28layer_batch512", "fp8", 64, 40, ("uniform", 1, 3000), 256, "paired"),
+]
+
+
+@pytest.mark.parametrize("case", RANDOM_BATCHES, ids=[f"seed{c[0]}-{c[7]}" for c in RANDOM_BATCHES])
+def test_random_batches_match_oracle(case):
+    """Every row of seeded batches against the oracle, each batch chosen to reach one mode of the
+    matrix-core decode's work distribution: paired items, a partition size the planner picked for a
+    multi-round list, or single items."""
+    seed, name, cdt, D, S, mix, ps, mode = case
+    rng = np.random.default_rng(1000 + seed)
+    if mix[0] == "uniform":
+        lengths = rng.integers(mix[1], mix[2], size=S, endpoint=True)
+    else:
+        lengths = np.clip(np.rint(rng.lognormal(np.log(mix[1]), mix[2], size=S)), 1, 8000)
+    lengths = lengths.astype(np.int32)
+    q = "bf16" if cdt == "bf16" else "f16"
+    base = wl.WORKLOADS[name]
+    w = base.replace(num_seqs=S, num_layers=1, cache_dtype=cdt, q_dtype=q, head_dim=D,
+                     num_blocks=int(lengths.sum() // 16 + 2 * S + 1024))
+    _say(f"random batch {seed}: {S} x {cdt} head_dim {D}, lengths {mix}, partition {ps}, {mode}")
+    pad = _pad_block(w)
+    b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON, lengths=lengths,
+                    partition_size=ps)
+    H = w.num_kv_heads
+    pt = b.call_partition(0) or ps or api.pa_decode_auto_partition(S, H, b.max_context_len)
+    npart = -(-b.max_context_len // pt)
+    if mode == "paired":
+        assert _pairs_taken(S, H, npart)
+    elif mode == "planned partition":
+        assert b.call_partition(0) > api.pa_decode_auto_partition(S, H, b.max_context_len)
+    else:
+        assert not _pairs_taken(S, H, npart) and b.call_partition(0) == ps
+    _say(f"  partition {pt} ({npart} per row)")
+    ob = OracleBatch(b, pad, pool_fill=POISON)
+    ob.metadata_matches(b)
+    _check_batch(b, ob, 0, TOL[cdt])
+
+
 def test_poison_outside_the_context_never_leaks():
     _say("NaN poison")
     w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=5, num_blocks=512)
