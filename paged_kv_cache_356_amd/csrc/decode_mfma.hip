@@ -74,7 +74,7 @@ constexpr bool kDecodeNT = true;
 constexpr int kDecodeOcc = 3;
 constexpr int kAppendOcc = 2;
 // Paired items run one wavefront per SIMD (pair_items), so their instantiation can take 256
-// registers: the ring's boundary emit stays out of scratch.
+// registers: the first partition's row state, held until the ring ends, fits without scratch.
 constexpr int kPairOcc = 2;
 
 // off: per-lane byte offset; soff: a wave-uniform byte offset added to it.
