@@ -1039,7 +1039,7 @@ __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(kPair ? kPairOcc : kApp && !kPre ? kAppendOcc : kDecodeOcc)))
 void decode_mfma_kernel(DecodeArgs a) {
   static_assert(!kPre || kB == 16, "the shared prefix runs on 16-position blocks");
-  static_assert(!kPair || (!kPre && !kApp && kB == 16), "paired items: plain decode, 16 positions");
+  static_assert(!kPair || (!kPre && kB == 16), "paired items: plain decode, 16 positions");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = a.num_seqs, H = a.cache.num_kv_heads, g = a.num_q_heads / H;
@@ -1221,7 +1221,7 @@ int device_cus() {
 // way, and the pairs still give every SIMD a wavefront.  The count takes every row at the call's
 // largest partition count (the host does not see the context lengths).
 bool pair_items(const DecodeArgs &a) {
-  if (a.prefix_len > 0 || a.append_slots || a.cache.block_size != kBlock ||
+  if (a.prefix_len > 0 || a.cache.block_size != kBlock ||
       a.num_seqs > kMaxScanSeqs || a.num_partitions < 2)
     return false;
   const int cus = device_cus();
@@ -1269,7 +1269,9 @@ struct KernelCfg {
 template <class CT, class QT, int D, bool kPre, int kB, class F>
 auto with_app(const DecodeArgs &a, F &&f) {
   if constexpr (!kPre && kB == 16)
-    if (a.pair_items) return f(KernelCfg<CT, QT, D, false, 16, false, true>{});
+    if (a.pair_items)
+      return a.append_slots ? f(KernelCfg<CT, QT, D, false, 16, true, true>{})
+                            : f(KernelCfg<CT, QT, D, false, 16, false, true>{});
   return a.append_slots ? f(KernelCfg<CT, QT, D, kPre, kB, true>{})
                         : f(KernelCfg<CT, QT, D, kPre, kB, false>{});
 }

@@ -485,6 +485,41 @@ def test_paired_items_match_oracle(cache_dtype, D):
         assert err <= tol
 
 
+@pytest.mark.parametrize("cache_dtype", ["f16", "fp8"])
+def test_paired_items_fused_append(cache_dtype):
+    """The fused append on a batch whose items the kernel pairs: pools byte for byte as the oracle's
+    replay of reshape_and_cache leaves them, attention against the oracle, and the same pools and
+    attention (within tolerance) as reshape_and_cache + decode."""
+    q = "f16"
+    w = wl.WORKLOADS["f16_batch32"].replace(num_seqs=40, num_blocks=8192, cache_dtype=cache_dtype,
+                                            q_dtype=q)
+    rng = np.random.default_rng(12)
+    lengths = rng.integers(1, 2600, size=40).astype(np.int32)
+    lengths[:8] = [1, 2, 256, 257, 512, 513, 2600, 2599]
+    assert _pairs_taken(40, w.num_kv_heads, -(-int(lengths.max()) // 256))
+    _say(f"paired items, fused append, {cache_dtype} cache")
+    tol = TOL[cache_dtype]
+    pad = _pad_block(w)
+    b = DecodeBatch(w, keep_values=True, pad_block=pad, pool_fill=POISON, lengths=lengths,
+                    partition_size=256)
+    b.fused = True
+    ob = OracleBatch(b, pad, pool_fill=POISON)
+    ob.metadata_matches(b)
+    _check_batch(b, ob, 0, tol)
+    kp, vp, _, _ = ob.pools[(0, 0)]
+    dk, dv = device_pool_bytes(b.caches[0])
+    assert np.array_equal(dk, kp.view(np.uint8)) and np.array_equal(dv, vp.view(np.uint8))
+    fused_out = b.sets[0].out[0].clone()
+    b2 = DecodeBatch(w, pad_block=pad, pool_fill=POISON, lengths=lengths, partition_size=256)
+    b2.run_step(0)
+    torch.cuda.synchronize()
+    dk2, dv2 = device_pool_bytes(b2.caches[0])
+    assert np.array_equal(dk, dk2) and np.array_equal(dv, dv2)
+    err = float((fused_out.double() - b2.sets[0].out[0].double()).abs().max())
+    _say(f"  fused vs two calls max-abs {err:.3e}")
+    assert err <= tol
+
+
 # Seeded batches of mixed shapes through the whole step (clones, cache writes, the planned order and
 # partition size, the decode): each with the work-distribution mode it reaches on 256 compute units.
 RANDOM_BATCHES = [
