@@ -644,10 +644,26 @@ bool plan_arrange(const std::vector<int32_t> &items, const std::vector<int32_t> 
   // costs time (measured: 32 fp16 sequences of up to 2,048 positions, 608 items on 1,024
   // wavefronts, +0.3 us).
   if (2 * total <= waves || (total <= waves && !use_prefix)) return false;
+  // The sequences by the steps of their largest item, largest first, ties in batch order: a
+  // counting sort over the step counts (a stable comparison sort where they run very large).
   std::vector<int32_t> by_size((size_t)num_seqs);
-  for (int32_t s = 0; s < num_seqs; ++s) by_size[(size_t)s] = s;
-  std::stable_sort(by_size.begin(), by_size.end(),
-                   [&](int32_t x, int32_t y) { return steps[(size_t)x] > steps[(size_t)y]; });
+  int32_t max_step = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) max_step = std::max(max_step, steps[(size_t)s]);
+  if (max_step <= 8192) {
+    std::vector<int32_t> start((size_t)max_step + 1, 0);
+    for (int32_t s = 0; s < num_seqs; ++s) ++start[(size_t)steps[(size_t)s]];
+    int32_t pos = 0;
+    for (int32_t v = max_step; v >= 0; --v) {
+      const int32_t c = start[(size_t)v];
+      start[(size_t)v] = pos;
+      pos += c;
+    }
+    for (int32_t s = 0; s < num_seqs; ++s) by_size[(size_t)start[(size_t)steps[(size_t)s]]++] = s;
+  } else {
+    for (int32_t s = 0; s < num_seqs; ++s) by_size[(size_t)s] = s;
+    std::stable_sort(by_size.begin(), by_size.end(),
+                     [&](int32_t x, int32_t y) { return steps[(size_t)x] > steps[(size_t)y]; });
+  }
   int32_t k = 0;
   if (total > waves && total <= 2 * (int64_t)waves) {
     // Two rounds: total - waves wavefronts take two items, the others one.  The largest
