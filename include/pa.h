@@ -190,7 +190,10 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                 those allow (a partition may start inside a 32-position block); when there are
  *                 several they are computed independently (each keeps its running max, running
  *                 sum and output, and stores the max, the sum and its normalised output) and
- *                 merged by a second kernel.
+ *                 merged by a second kernel.  Where the call's rows hold between one and two
+ *                 partitions per SIMD of the device, one wavefront computes two consecutive
+ *                 partitions of a row in one pass over their blocks; each still stores its own
+ *                 partial.  pa_decode_plan can pick a larger size for automatic calls.
  *   workspace     device scratch of at least pa_decode_workspace_bytes() bytes (NULL if 0).
  * Arithmetic: products, exponentials and sums in fp32 (the matrix cores take f16 / bf16 operands,
  * fp8 codes widened to f16); the result rounds once to q_dtype.  With f16 queries on the matrix
